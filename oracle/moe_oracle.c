@@ -1,0 +1,182 @@
+/*
+ * CPU oracle for MoE token dispatch and combine. TEST INFRASTRUCTURE ONLY:
+ * see moe_oracle.h for who may call it, the pages it follows and the shapes.
+ * Plain loops in token order, single-threaded, no blocking or reordering.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int id_is_expert(int32_t e, int32_t E) { return e >= 0 && e < E; }
+
+/* Widen a bf16 bit pattern to float: the 16 bits are the top half of a float. */
+static float widen_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Round a float to bf16, to nearest, ties to even; NaN stays NaN (quiet bit set). */
+static uint16_t narrow_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  const uint32_t lower = u & 0xFFFFu;
+  uint32_t upper = u >> 16;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* topk_ids,
+                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
+                  int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row) {
+  const int32_t m = E / R; /* experts per rank; expert e is on rank e / m */
+  int err = 0;
+  unsigned char* on_rank = (unsigned char*)malloc((size_t)R);
+  int32_t* next_rank = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+  int32_t* next_expert = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+
+  /* Counts: a token adds one row to every distinct rank among its experts,
+   * and one pair to the expert of every valid slot. */
+  for (int32_t r = 0; r < R; ++r) rank_counts[r] = 0;
+  for (int32_t e = 0; e < E; ++e) expert_counts[e] = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    memset(on_rank, 0, (size_t)R);
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = topk_ids[(int64_t)t * k + j];
+      if (!id_is_expert(e, E)) {
+        if (e != -1) err |= ORACLE_ERR_BAD_ID;
+        continue;
+      }
+      expert_counts[e] += 1;
+      on_rank[e / m] = 1;
+    }
+    for (int32_t r = 0; r < R; ++r) rank_counts[r] += on_rank[r];
+  }
+
+  /* Exclusive prefix sums: where each rank's segment and each expert's run begins. */
+  rank_offsets[0] = 0;
+  for (int32_t r = 0; r < R; ++r) rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];
+  expert_offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) expert_offsets[e + 1] = expert_offsets[e] + expert_counts[e];
+
+  /* Positions: walk the tokens in order and hand out the next free row of the
+   * segment (rank) or run (expert), so rows ascend with the token index. */
+  for (int32_t r = 0; r < R; ++r) next_rank[r] = rank_offsets[r];
+  for (int32_t e = 0; e < E; ++e) next_expert[e] = expert_offsets[e];
+  for (int32_t t = 0; t < T; ++t) {
+    memset(on_rank, 0, (size_t)R);
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = topk_ids[(int64_t)t * k + j];
+      if (!id_is_expert(e, E)) {
+        pair_row[(int64_t)t * k + j] = -1;
+        continue;
+      }
+      pair_row[(int64_t)t * k + j] = next_expert[e]++;
+      on_rank[e / m] = 1;
+    }
+    for (int32_t r = 0; r < R; ++r)
+      token_rank_slot[(int64_t)t * R + r] = on_rank[r] ? next_rank[r]++ : -1;
+  }
+
+  free(on_rank);
+  free(next_rank);
+  free(next_expert);
+  return err;
+}
+
+int oracle_pack(int32_t T, int32_t H, int32_t R, const uint16_t* hidden,
+                const int32_t* token_rank_slot, uint16_t* rank_buf, int32_t* rank_src_token,
+                int64_t cap_rank) {
+  int err = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t r = 0; r < R; ++r) {
+      const int64_t row = token_rank_slot[(int64_t)t * R + r];
+      if (row < 0) continue;
+      if (row >= cap_rank) {
+        err |= ORACLE_ERR_RANK_CAP;
+        continue;
+      }
+      memcpy(rank_buf + row * H, hidden + (int64_t)t * H, sizeof(uint16_t) * (size_t)H);
+      rank_src_token[row] = t;
+    }
+  }
+  return err;
+}
+
+int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+                   const uint16_t* rank_buf, const int32_t* rank_src_token,
+                   const int32_t* rank_offsets, const int32_t* topk_ids,
+                   const int32_t* pair_row, int64_t cap_rank, uint16_t* expert_buf,
+                   int32_t* expert_src_pair, int64_t cap_expert) {
+  (void)T;
+  const int32_t m = E / R;
+  int err = 0;
+  int64_t rows = rank_offsets[R];
+  if (rows > cap_rank) rows = cap_rank;
+  int32_t r = 0;
+  for (int64_t i = 0; i < rows; ++i) {
+    while (i >= rank_offsets[r + 1]) ++r; /* the segment that holds row i */
+    const int32_t t = rank_src_token[i];
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = topk_ids[(int64_t)t * k + j];
+      if (!id_is_expert(e, E) || e / m != r) continue;
+      const int64_t dst = pair_row[(int64_t)t * k + j];
+      if (dst >= cap_expert) {
+        err |= ORACLE_ERR_EXPERT_CAP;
+        continue;
+      }
+      memcpy(expert_buf + dst * H, rank_buf + i * H, sizeof(uint16_t) * (size_t)H);
+      expert_src_pair[dst] = t * k + j;
+    }
+  }
+  return err;
+}
+
+int oracle_combine(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
+                   const int32_t* pair_row, const float* topk_weights, int64_t cap_expert,
+                   uint16_t* out, float* out_f32) {
+  int err = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      for (int32_t j = 0; j < k; ++j) {
+        const int64_t row = pair_row[(int64_t)t * k + j];
+        if (row < 0) continue;
+        if (row >= cap_expert) {
+          err |= ORACLE_ERR_EXPERT_CAP;
+          continue;
+        }
+        acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);
+      }
+      out[(int64_t)t * H + h] = narrow_bf16_rne(acc);
+      if (out_f32) out_f32[(int64_t)t * H + h] = acc;
+    }
+  }
+  return err;
+}
+
+int oracle_combine_f64(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
+                       const int32_t* pair_row, const float* topk_weights, int64_t cap_expert,
+                       double* out_f64) {
+  int err = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < k; ++j) {
+        const int64_t row = pair_row[(int64_t)t * k + j];
+        if (row < 0) continue;
+        if (row >= cap_expert) {
+          err |= ORACLE_ERR_EXPERT_CAP;
+          continue;
+        }
+        acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);
+      }
+      out_f64[(int64_t)t * H + h] = acc;
+    }
+  }
+  return err;
+}

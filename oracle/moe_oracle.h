@@ -1,0 +1,102 @@
+/*
+ * CPU oracle for MoE token dispatch and combine (one GPU's share of an
+ * expert-parallel layer, the R destination ranks being logical buffers).
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the plain, slow, single-threaded
+ * definition that the GPU library is checked against. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load or call it;
+ * the product path never does. It shares no code with the GPU library.
+ *
+ * Source pages (cited by title and section):
+ *  [A2A]  "A2A backends" page, vincentzed.com/writing/a2a-backends
+ *  [GPUs] "How GPUs Talk to Each Other During LLM Inference", how-gpus-talk.vercel.app
+ *  [EP]   "Beyond One GPU: Tensor, Pipeline and Expert Parallelism, and Split
+ *         Prefill and Decode", ishwarj.com
+ *
+ * Shapes: T tokens, H hidden (bf16 elements), E experts, R ranks, k slots per
+ * token. Expert e lives on rank e / (E/R) (contiguous placement: [A2A] sec 1.1
+ * gives 48 of 384 experts per GPU, sec 2.1 gives each GPU the id range
+ * [first_local, first_local + num_local); [EP] places experts in order, E/G per GPU).
+ *
+ * Id convention: -1 means "no expert in this slot" and is skipped silently
+ * ([A2A] sec 2.1 marks non-local experts with -1; sec 6.3 marks empty slots
+ * with an invalid id). Any other id outside [0, E) is skipped and reported
+ * with ORACLE_ERR_BAD_ID.
+ *
+ * Parity status: every function below is pinned by the CPU tests (stable-sort
+ * and brute-force equivalence, closed-form copy count, prose examples,
+ * identity and one-hot combine, exact-rational error bound); none is unpinned.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_ERR_BAD_ID 1        /* an id outside [-1, E) was skipped */
+#define ORACLE_ERR_RANK_CAP 2      /* a rank-buffer row at or past cap_rank was dropped */
+#define ORACLE_ERR_EXPERT_CAP 4    /* an expert row at or past cap_expert was dropped/ignored */
+
+/*
+ * Layout ([A2A] sec 3.2 first step; sec 5.1). Counts rows per destination rank
+ * (one per token per distinct rank holding one of its experts, [A2A] sec 1.1
+ * Figure 1 and sec 1.3 third answer) and pairs per expert, takes exclusive
+ * prefix sums, and numbers every (token, rank) copy and every (token, slot)
+ * pair in ascending token order inside its segment.
+ *   rank_counts[R], rank_offsets[R+1], expert_counts[E], expert_offsets[E+1]
+ *   token_rank_slot[T*R]: row of token t in rank r's segment, or -1
+ *   pair_row[T*k]: row of pair (t, j) in the expert-grouped buffer, or -1
+ * Returns the OR of ORACLE_ERR_* bits.
+ */
+int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* topk_ids,
+                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
+                  int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row);
+
+/*
+ * Pack ([A2A] sec 1.3 third answer, sec 3.2 first step): copy token t's hidden
+ * row once into every rank segment row token_rank_slot[t*R + r] >= 0, and
+ * record the source token of that row. Rows at or past cap_rank are dropped.
+ */
+int oracle_pack(int32_t T, int32_t H, int32_t R, const uint16_t* hidden,
+                const int32_t* token_rank_slot, uint16_t* rank_buf, int32_t* rank_src_token,
+                int64_t cap_rank);
+
+/*
+ * Permute by expert, on the receiving side ([A2A] sec 3.3 regroup; sec 5.1
+ * copy epilogue with do_expand): every rank-buffer row i below
+ * min(rank_offsets[R], cap_rank), sitting in the segment of rank r and holding
+ * token t = rank_src_token[i], is copied once for each slot j of t whose expert
+ * lives on r, to row pair_row[t*k + j]; expert_src_pair of that row is t*k + j.
+ */
+int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+                   const uint16_t* rank_buf, const int32_t* rank_src_token,
+                   const int32_t* rank_offsets, const int32_t* topk_ids,
+                   const int32_t* pair_row, int64_t cap_rank, uint16_t* expert_buf,
+                   int32_t* expert_src_pair, int64_t cap_expert);
+
+/*
+ * Combine ([A2A] sec 1.1: the MoE output is the sum of the chosen experts'
+ * outputs, each multiplied by its weight; sec 7.1: the sum is taken in 32-bit
+ * floats; [GPUs] sec 3.3: a fixed addition order gives identical results).
+ * acc = +0.0f; for j = 0..k-1 with pair_row[t*k+j] valid:
+ *   acc = fmaf(w[t*k+j], float(expert_out[row][h]), acc)
+ * out[t][h] = bf16 round-to-nearest-even of acc; out_f32 (if not NULL) = acc.
+ */
+int oracle_combine(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
+                   const int32_t* pair_row, const float* topk_weights, int64_t cap_expert,
+                   uint16_t* out, float* out_f32);
+
+/* The same weighted sum in double precision (each product of a float weight and
+ * a bf16 value is exact in double), used as the reference value of the fp32
+ * tolerance check. */
+int oracle_combine_f64(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
+                       const int32_t* pair_row, const float* topk_weights, int64_t cap_expert,
+                       double* out_f64);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

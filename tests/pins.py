@@ -1,0 +1,552 @@
+"""Pins that tie the oracle to something other than itself.
+
+Each pin is a plain function that raises AssertionError when the oracle
+disagrees with what the pages or the mathematics fix:
+  * library routines the definition reduces to (stable sort, bincount, cumsum),
+  * brute force on tiny inputs,
+  * the closed-form copy count of the "A2A backends" page, section 1.3, exact
+    over every k-subset and statistically over the seeded workloads,
+  * prose examples of that page (sections 1.1, 3.3 and 4.1, constructed
+    instances under tests/golden/),
+  * combine special cases (identity experts, one-hot weights, k = 1, exact
+    doubling, round-to-nearest-even ties) and the exact rational result within
+    the standard error bound of a fused multiply-add chain.
+
+The pins are collected by test_oracle_pins.py and replayed against
+deliberately broken copies of the oracle by test_oracle_mutants.py.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+# ----------------------------------------------------------------------------
+# helpers (test side; none of them is the oracle's arithmetic)
+
+def bf16_bits_to_float(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def closed_form_copies(E: int, R: int, k: int) -> Fraction:
+    """Expected distinct ranks per token, uniform router ("A2A backends" page,
+    section 1.3): R * (1 - C(E - E/R, k) / C(E, k)), as an exact fraction."""
+    return R * (1 - Fraction(math.comb(E - E // R, k), math.comb(E, k)))
+
+
+def rand_ids(rng, T, E, k, p_neg=0.0, p_dup=0.0, p_bad=0.0):
+    """Random top-k ids: distinct experts per token, then some slots set to -1,
+    some duplicated from slot 0, some set to out-of-range ids."""
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) \
+        if T else np.zeros((0, k), np.int32)
+    if T and k > 1 and p_dup:
+        dup = rng.random((T, k)) < p_dup
+        dup[:, 0] = False
+        ids = np.where(dup, ids[:, :1], ids)
+    if T and p_neg:
+        ids = np.where(rng.random((T, k)) < p_neg, -1, ids)
+    if T and p_bad:
+        bad = rng.random((T, k)) < p_bad
+        ids = np.where(bad, rng.choice([-7, -2, E, E + 5], size=(T, k)), ids)
+    return np.ascontiguousarray(ids, dtype=np.int32)
+
+
+def valid_mask(ids, E):
+    return (ids >= 0) & (ids < E)
+
+
+def read_golden(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def expected_layout_by_sorting(ids: np.ndarray, E: int, R: int) -> dict:
+    """The layout the definition reduces to, built from library routines only:
+    stable argsort by key (expert; rank), bincount and cumsum."""
+    T, k = ids.shape
+    m = E // R
+    flat = ids.reshape(-1)
+    ok = valid_mask(flat, E)
+    idx = np.nonzero(ok)[0]
+    order = idx[np.argsort(flat[idx], kind="stable")]
+    pair_row = np.full(T * k, -1, np.int64)
+    pair_row[order] = np.arange(order.size)
+    expert_counts = np.bincount(flat[idx], minlength=E)
+
+    present = np.zeros((T, R), bool)
+    tt = np.repeat(np.arange(T), k)[ok]
+    present[tt, flat[ok] // m] = True
+    t_of, r_of = np.nonzero(present)  # row-major: ascending t, then r
+    order_r = np.argsort(r_of, kind="stable")
+    slot = np.full((T, R), -1, np.int64)
+    slot[t_of[order_r], r_of[order_r]] = np.arange(order_r.size)
+    rank_counts = present.sum(0)
+    return dict(
+        rank_counts=rank_counts,
+        rank_offsets=np.concatenate([[0], np.cumsum(rank_counts)]),
+        expert_counts=expert_counts,
+        expert_offsets=np.concatenate([[0], np.cumsum(expert_counts)]),
+        token_rank_slot=slot,
+        pair_row=pair_row.reshape(T, k),
+    )
+
+
+LAYOUT_KEYS = ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
+               "token_rank_slot", "pair_row")
+
+
+def assert_layout_equal(got: dict, want: dict, what: str):
+    for key in LAYOUT_KEYS:
+        a = np.asarray(got[key]).astype(np.int64)
+        b = np.asarray(want[key]).astype(np.int64)
+        assert a.shape == b.shape and np.array_equal(a, b), f"{what}: {key} differs"
+
+
+# ----------------------------------------------------------------------------
+# layout pins
+
+LAYOUT_CASES = [
+    # (T, E, R, k, p_neg, p_dup, seed)
+    (1, 4, 2, 2, 0.0, 0.0, 1),
+    (7, 8, 4, 3, 0.2, 0.0, 2),
+    (64, 16, 4, 2, 0.0, 0.0, 3),
+    (100, 16, 16, 4, 0.1, 0.2, 4),
+    (333, 384, 8, 6, 0.05, 0.05, 5),
+    (257, 256, 8, 8, 0.0, 0.1, 6),
+    (50, 12, 1, 5, 0.1, 0.0, 7),
+    (129, 64, 64, 1, 0.3, 0.0, 8),
+]
+
+
+def pin_layout_stable_sort():
+    """Rows of a rank segment / expert run ascend with the token index, which
+    is exactly a stable sort of the (token, rank) copies by rank and of the
+    (token, slot) pairs by expert; offsets are exclusive prefix sums of the
+    counts ("A2A backends" page, sections 3.2 and 5.1)."""
+    for T, E, R, k, pn, pd, seed in LAYOUT_CASES:
+        ids = rand_ids(np.random.default_rng(seed), T, E, k, pn, pd)
+        got = oracle.layout(ids, E, R)
+        assert got["err"] == 0, "no bad ids in these cases"
+        assert_layout_equal(got, expected_layout_by_sorting(ids, E, R),
+                            f"stable-sort T={T} E={E} R={R} k={k}")
+
+
+def pin_layout_brute_force():
+    """Every position counted directly from its definition, O(T^2), tiny inputs."""
+    rng = np.random.default_rng(11)
+    for T, E, R, k in [(1, 2, 1, 1), (3, 4, 2, 2), (5, 6, 3, 2), (8, 8, 4, 4), (8, 8, 8, 3),
+                       (6, 8, 2, 4)]:
+        for rep in range(3):
+            ids = rand_ids(rng, T, E, k, p_neg=0.15, p_dup=0.15)
+            got = oracle.layout(ids, E, R)
+            m = E // R
+            pairs = [(t, j, int(ids[t, j])) for t in range(T) for j in range(k)
+                     if 0 <= ids[t, j] < E]
+            ranks_of = [sorted({int(e) // m for e in ids[t] if 0 <= e < E}) for t in range(T)]
+            for t in range(T):
+                for j in range(k):
+                    e = int(ids[t, j])
+                    if not 0 <= e < E:
+                        assert got["pair_row"][t, j] == -1
+                        continue
+                    before = sum(1 for (_, _, e2) in pairs if e2 < e)
+                    earlier = sum(1 for (t2, j2, e2) in pairs if e2 == e and (t2, j2) < (t, j))
+                    assert got["pair_row"][t, j] == before + earlier, ("pair_row", T, E, R, k, t, j)
+                for r in range(R):
+                    if r not in ranks_of[t]:
+                        assert got["token_rank_slot"][t, r] == -1
+                        continue
+                    before = sum(1 for t2 in range(T) for r2 in ranks_of[t2] if r2 < r)
+                    earlier = sum(1 for t2 in range(t) if r in ranks_of[t2])
+                    assert got["token_rank_slot"][t, r] == before + earlier, ("slot", t, r)
+            for r in range(R):
+                assert got["rank_counts"][r] == sum(r in rs for rs in ranks_of)
+            for e in range(E):
+                assert got["expert_counts"][e] == sum(1 for p in pairs if p[2] == e)
+
+
+def pin_layout_invariants():
+    """Counts and positions agree with each other on the seeded workloads."""
+    for name in ("tiny", "decode", "prefill", "skew"):
+        w = synth.WORKLOADS[name]
+        ids, _ = synth.routing(w)
+        lay = oracle.layout(ids, w.E, w.R)
+        assert lay["err"] == 0
+        D = np.array([len({int(e) // w.m for e in row}) for row in ids])
+        C = int(D.sum())
+        slots = lay["token_rank_slot"]
+        assert int(lay["rank_counts"].sum()) == C == int(lay["rank_offsets"][-1])
+        assert np.array_equal((slots >= 0).sum(1), D), "copies per token != distinct ranks"
+        assert int(lay["expert_counts"].sum()) == w.T * w.k == int(lay["expert_offsets"][-1])
+        s = np.sort(slots[slots >= 0])
+        assert np.array_equal(s, np.arange(C)), "slots are not a bijection onto [0, C)"
+        p = np.sort(lay["pair_row"].reshape(-1))
+        assert np.array_equal(p, np.arange(w.T * w.k)), "pair rows not a bijection onto [0, P)"
+        for r in range(w.R):
+            col = slots[:, r]
+            col = col[col >= 0]
+            assert np.all(np.diff(col) == 1), "rank segment rows not ascending in t"
+            assert col.size == 0 or col[0] == lay["rank_offsets"][r]
+
+
+def pin_closed_form_exhaustive():
+    """Over every k-subset of experts (one token each), the mean number of
+    copies equals the closed form of the "A2A backends" page, section 1.3,
+    exactly."""
+    for E, R, k in [(8, 4, 3), (12, 4, 3), (12, 3, 5), (16, 8, 2), (10, 5, 4)]:
+        ids = np.array(list(itertools.combinations(range(E), k)), dtype=np.int32)
+        lay = oracle.layout(ids, E, R)
+        got = Fraction(int(lay["rank_counts"].sum()), ids.shape[0])
+        assert got == closed_form_copies(E, R, k), (E, R, k, got)
+        assert int(lay["expert_counts"].sum()) == ids.size
+
+
+def pin_closed_form_workloads():
+    """Seeded uniform-router workloads: mean copies within 4 sigma of the closed
+    form (the page's 4.43 for 384 experts, 8 GPUs, top-6)."""
+    for name in ("tiny", "decode", "prefill"):
+        w = synth.WORKLOADS[name]
+        ids, _ = synth.routing(w)
+        lay = oracle.layout(ids, w.E, w.R)
+        D = (lay["token_rank_slot"] >= 0).sum(1)
+        mu = float(closed_form_copies(w.E, w.R, w.k))
+        sigma = float(D.std()) / math.sqrt(w.T)
+        assert abs(D.mean() - mu) <= 4 * max(sigma, 1e-9), (name, D.mean(), mu, sigma)
+
+
+def pin_page_bytes():
+    """Bytes per GPU per layer at the prefill workload: the oracle's copy count
+    times the 10,240-byte row lands on the page's 177 MB (per distinct GPU),
+    well below 240 MB (per expert) and 320 MB (every GPU)."""
+    w = synth.WORKLOADS["prefill"]
+    ids, _ = synth.routing(w)
+    lay = oracle.layout(ids, w.E, w.R)
+    row = w.H * 2
+    mib_gpu = int(lay["rank_offsets"][-1]) * row / 2 ** 20
+    mib_expert = int(lay["expert_offsets"][-1]) * row / 2 ** 20
+    assert abs(mib_gpu - 177) < 2.5, mib_gpu
+    assert mib_expert == 240.0
+
+
+def pin_figure1():
+    rows = {r[0]: r[1:] for r in read_golden("figure1_token.txt")}
+    E, R = int(rows["E"][0]), int(rows["R"][0])
+    ids = np.array([[int(x) for x in rows["ids"]]], np.int32)
+    lay = oracle.layout(ids, E, R)
+    assert int((lay["token_rank_slot"] >= 0).sum()) == int(rows["copies"][0])
+    hid = np.arange(16, dtype=np.uint16).reshape(1, 16)
+    rank_buf, _, err = oracle.pack(hid, lay["token_rank_slot"], cap_rank=3)
+    assert err == 0 and int(lay["rank_offsets"][-1]) == 2
+
+
+def pin_figure4():
+    """Five rows arrive at rank 1 and become seven expert rows."""
+    rows = read_golden("figure4_regroup.txt")
+    kv = {r[0]: r[1:] for r in rows if r[0] != "token"}
+    E, R, rank = int(kv["E"][0]), int(kv["R"][0]), int(kv["rank"][0])
+    ids = np.array([[int(x) for x in r[2:]] for r in rows if r[0] == "token"], np.int32)
+    T, k = ids.shape
+    H = 8
+    hid = (np.arange(T * H, dtype=np.uint16) + 1).reshape(T, H)
+    lay = oracle.layout(ids, E, R)
+    assert int(lay["rank_counts"][rank]) == int(kv["arrived_rows"][0])
+    m = E // R
+    local = range(rank * m, (rank + 1) * m)
+    assert int(sum(lay["expert_counts"][e] for e in local)) == int(kv["expert_rows"][0])
+    rank_buf, src, _ = oracle.pack(hid, lay["token_rank_slot"], cap_rank=T * min(k, R))
+    ebuf, esrc, err = oracle.permute(rank_buf, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+                                     cap_expert=T * k)
+    assert err == 0
+    lo, hi = lay["expert_offsets"][rank * m], lay["expert_offsets"][(rank + 1) * m]
+    assert hi - lo == 7
+    seg = slice(lay["rank_offsets"][rank], lay["rank_offsets"][rank + 1])
+    assert list(src[seg]) == [0, 1, 2, 3, 4], "rows arrive in token order a..e"
+    # token a needs E2 and E3: it shows up in both runs
+    for e in (2, 3):
+        run = esrc[lay["expert_offsets"][e]:lay["expert_offsets"][e + 1]] // k
+        assert 0 in run
+    for row in range(lo, hi):
+        assert np.array_equal(ebuf[row], hid[esrc[row] // k])
+
+
+def pin_bad_ids():
+    """Out-of-range ids are reported and then treated like -1."""
+    rng = np.random.default_rng(21)
+    for T, E, R, k in [(40, 16, 4, 3), (90, 64, 8, 6)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1, p_bad=0.15)
+        bad = (ids != -1) & ~valid_mask(ids, E)
+        assert bad.any()
+        got = oracle.layout(ids, E, R)
+        assert got["err"] & oracle.ERR_BAD_ID
+        clean = np.where(bad, -1, ids)
+        ref = oracle.layout(clean, E, R)
+        assert ref["err"] == 0
+        assert_layout_equal(got, ref, "bad ids vs -1")
+
+
+# ----------------------------------------------------------------------------
+# pack / permute pins
+
+def pin_pack_permute_rows():
+    """Every packed row is its source token's row, placed where the stable sort
+    puts it; every expert row is the token row of its pair; rows past the
+    counts are left alone (canaries)."""
+    for T, E, R, k, pn, pd, seed in LAYOUT_CASES:
+        rng = np.random.default_rng(100 + seed)
+        ids = rand_ids(rng, T, E, k, pn, pd)
+        H = 24
+        hid = rng.integers(0, 65536, size=(T, H), dtype=np.uint16)
+        lay = oracle.layout(ids, E, R)
+        want = expected_layout_by_sorting(ids, E, R)
+        cap_rank, cap_expert = T * min(k, R) + 3, T * k + 3
+        canary = np.uint16(0xBEEF)
+        rb = np.full((cap_rank, H), canary, np.uint16)
+        src = np.full(cap_rank, -5, np.int32)
+        rb, src, e1 = oracle.pack(hid, lay["token_rank_slot"], cap_rank, rb, src)
+        C = int(want["rank_offsets"][-1])
+        assert e1 == 0
+        t_of = np.full(C, -1)
+        ts, rs = np.nonzero(want["token_rank_slot"] >= 0)
+        t_of[want["token_rank_slot"][ts, rs]] = ts
+        assert np.array_equal(src[:C], t_of)
+        assert np.array_equal(rb[:C], hid[t_of])
+        assert np.all(rb[C:] == canary) and np.all(src[C:] == -5)
+
+        eb = np.full((cap_expert, H), canary, np.uint16)
+        es = np.full(cap_expert, -5, np.int32)
+        eb, es, e2 = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+                                    cap_expert, eb, es)
+        assert e2 == 0
+        P = int(want["expert_offsets"][-1])
+        pr = want["pair_row"].reshape(-1)
+        pair_of = np.full(P, -1)
+        ok = pr >= 0
+        pair_of[pr[ok]] = np.nonzero(ok)[0]
+        assert np.array_equal(es[:P], pair_of)
+        assert np.array_equal(eb[:P], hid[pair_of // k])
+        assert np.all(eb[P:] == canary) and np.all(es[P:] == -5)
+
+
+def pin_permute_reads_own_segment():
+    """The permute of a rank segment reads only the rows that arrived in that
+    segment: with every rank-buffer row made distinguishable, expert row
+    pair_row[t, j] holds the copy of token t from the segment of rank(e_tj)."""
+    rng = np.random.default_rng(27)
+    for T, E, R, k in [(60, 16, 4, 4), (128, 384, 8, 6)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1)
+        lay = oracle.layout(ids, E, R)
+        C = int(lay["rank_offsets"][-1])
+        H = 4
+        rb = np.repeat(np.arange(C, dtype=np.uint16)[:, None], H, 1)  # row i holds i
+        src = np.full(C, -1, np.int32)
+        ts, rs = np.nonzero(lay["token_rank_slot"] >= 0)
+        src[lay["token_rank_slot"][ts, rs]] = ts
+        eb, es, err = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+                                     T * k)
+        assert err == 0
+        m = E // R
+        for t in range(T):
+            for j in range(k):
+                e = int(ids[t, j])
+                if e < 0:
+                    continue
+                want = lay["token_rank_slot"][t, e // m]
+                assert np.all(eb[lay["pair_row"][t, j]] == want), (t, j)
+
+
+def pin_caps():
+    """Undersized buffers: rows past the cap are dropped, never written out of
+    bounds, and reported."""
+    rng = np.random.default_rng(31)
+    T, E, R, k, H = 50, 16, 4, 3, 8
+    ids = rand_ids(rng, T, E, k)
+    hid = rng.integers(0, 65536, size=(T, H), dtype=np.uint16)
+    lay = oracle.layout(ids, E, R)
+    C = int(lay["rank_offsets"][-1])
+    cap = C - 7
+    rb = np.zeros((cap, H), np.uint16)
+    src = np.full(cap, -1, np.int32)
+    rb, src, err = oracle.pack(hid, lay["token_rank_slot"], cap, rb, src)
+    assert err == oracle.ERR_RANK_CAP
+    assert np.all(src >= 0)
+    P = int(lay["expert_offsets"][-1])
+    eb = np.zeros((P - 5, H), np.uint16)
+    es = np.full(P - 5, -1, np.int32)
+    eb, es, err2 = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E, P - 5,
+                                  eb, es)
+    assert err2 & oracle.ERR_EXPERT_CAP
+    out, _, err3 = oracle.combine(eb, lay["pair_row"], np.ones((T, k), np.float32))
+    assert err3 & oracle.ERR_EXPERT_CAP
+
+
+# ----------------------------------------------------------------------------
+# combine pins
+
+def _renormalised_weights(rng, T, k):
+    w = rng.random((T, k)) + 0.05
+    return (w / w.sum(1, keepdims=True)).astype(np.float32)
+
+
+def pin_roundtrip_identity():
+    """Identity experts and renormalised weights give back the hidden state
+    bit for bit (the weights sum to 1 within a few float32 ulps, far below
+    half a bf16 ulp): dispatch followed by combine is the identity."""
+    for name in ("tiny", "decode"):
+        w = synth.WORKLOADS[name]
+        hid = synth.hidden(w)
+        ids, wts = synth.routing(w)
+        res = oracle.dispatch_combine(hid, ids, wts, w.E, w.R)
+        assert res["err"] == 0
+        a, b = res["out"], hid
+        zero = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+        assert np.all((a == b) | zero), f"{name}: identity round trip differs"
+    rng = np.random.default_rng(41)
+    T, E, R, k, H = 77, 32, 4, 5, 40
+    ids = rand_ids(rng, T, E, k, p_neg=0.2)
+    ids[:, 0] = rng.integers(0, E, T)  # keep one valid slot per token
+    wts = np.where(ids >= 0, rng.random((T, k)) + 0.05, 0.0)
+    wts = (wts / wts.sum(1, keepdims=True)).astype(np.float32)
+    hid = synth.normal_bf16(5, 0, T * H).reshape(T, H)
+    res = oracle.dispatch_combine(hid, ids, wts, E, R)
+    a, b = res["out"], hid
+    assert np.all((a == b) | (((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)))
+
+
+def pin_combine_one_hot():
+    """A one-hot weight row selects exactly one expert output: the combine of
+    token t is then y[t, j0] bit for bit, so every (token, slot) -> row link
+    and every weight index is exercised."""
+    rng = np.random.default_rng(51)
+    for T, E, R, k, H in [(64, 16, 4, 4, 16), (200, 384, 8, 6, 24), (33, 8, 8, 8, 8)]:
+        ids = rand_ids(rng, T, E, k)
+        y = synth.normal_bf16(7, 2, T * k * H).reshape(T, k, H)
+        lay = oracle.layout(ids, E, R)
+        eo = oracle.place_slots(y, lay["pair_row"], T * k)
+        for j0 in range(k):
+            w = np.zeros((T, k), np.float32)
+            w[:, j0] = 1.0
+            out, out32, err = oracle.combine(eo, lay["pair_row"], w)
+            assert err == 0
+            assert np.array_equal(out, y[:, j0, :]), (T, E, k, j0)
+        j0 = rng.integers(0, k, T)
+        w = np.zeros((T, k), np.float32)
+        w[np.arange(T), j0] = 1.0
+        out, _, _ = oracle.combine(eo, lay["pair_row"], w)
+        assert np.array_equal(out, y[np.arange(T), j0, :])
+
+
+def pin_combine_scaling_and_skip():
+    """Doubling every weight doubles the float32 sum exactly; slots whose id is
+    -1 contribute nothing whatever their weight."""
+    rng = np.random.default_rng(61)
+    T, E, R, k, H = 90, 32, 8, 4, 32
+    ids = rand_ids(rng, T, E, k, p_neg=0.25)
+    y = synth.normal_bf16(9, 2, T * k * H).reshape(T, k, H)
+    lay = oracle.layout(ids, E, R)
+    eo = oracle.place_slots(y, lay["pair_row"], T * k)
+    w = rng.random((T, k)).astype(np.float32)
+    _, a32, _ = oracle.combine(eo, lay["pair_row"], w)
+    _, b32, _ = oracle.combine(eo, lay["pair_row"], w * np.float32(2))
+    assert np.array_equal(b32, a32 * np.float32(2))
+    w2 = np.where(ids < 0, np.float32(1e30), w).astype(np.float32)
+    _, c32, _ = oracle.combine(eo, lay["pair_row"], w2)
+    assert np.array_equal(c32, a32)
+
+
+def pin_combine_k1():
+    rng = np.random.default_rng(71)
+    T, E, R, H = 50, 8, 2, 16
+    ids = rng.integers(0, E, (T, 1)).astype(np.int32)
+    y = synth.normal_bf16(3, 2, T * H).reshape(T, 1, H)
+    lay = oracle.layout(ids, E, R)
+    eo = oracle.place_slots(y, lay["pair_row"], T)
+    out, _, _ = oracle.combine(eo, lay["pair_row"], np.ones((T, 1), np.float32))
+    assert np.array_equal(out, y[:, 0, :])
+
+
+def pin_combine_exact_bound():
+    """Against the exact rational sum: the float32 result of a chain of k fused
+    multiply-adds is within gamma_k * sum|w*y| (gamma_k = k*u / (1 - k*u),
+    u = 2^-24), the bf16 output is a nearest bf16 of the float32 result, and
+    the double-precision variant is within 2^-50 of exact."""
+    rng = np.random.default_rng(81)
+    for T, E, R, k, H in [(24, 16, 4, 6, 8), (16, 64, 8, 8, 12), (20, 8, 2, 2, 8)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1)
+        y = synth.normal_bf16(11, 2, T * k * H).reshape(T, k, H)
+        w = (rng.standard_normal((T, k)) * 3).astype(np.float32)
+        lay = oracle.layout(ids, E, R)
+        eo = oracle.place_slots(y, lay["pair_row"], T * k)
+        out, out32, _ = oracle.combine(eo, lay["pair_row"], w)
+        out64, _ = oracle.combine_f64(eo, lay["pair_row"], w)
+        yf = bf16_bits_to_float(y)
+        gamma = k * U32 / (1 - k * U32)
+        for t in range(T):
+            for h in range(H):
+                terms = [Fraction(float(w[t, j])) * Fraction(float(yf[t, j, h]))
+                         for j in range(k) if ids[t, j] >= 0]
+                exact = sum(terms, Fraction(0))
+                mag = sum((abs(x) for x in terms), Fraction(0))
+                err32 = abs(Fraction(float(out32[t, h])) - exact)
+                assert err32 <= gamma * mag, (t, h, float(err32), float(mag))
+                assert abs(Fraction(float(out64[t, h])) - exact) <= Fraction(2) ** -50 * mag
+                # nearest bf16: no other bf16 is strictly closer to the float32 value
+                o = int(out[t, h])
+                acc = Fraction(float(out32[t, h]))
+                mine = abs(Fraction(float(bf16_bits_to_float(o))) - acc)
+                for nb in (o - 1, o + 1):
+                    if 0 <= nb < 65536 and (nb & 0x7F80) != 0x7F80:
+                        assert abs(Fraction(float(bf16_bits_to_float(nb))) - acc) >= mine
+
+
+def pin_combine_rounding_ties():
+    """Round to nearest, ties to even, on float32 sums that fall exactly
+    halfway between two bf16 values (1 + 2^-8 lies halfway between 1 and
+    1 + 2^-7; 1 + 3*2^-8 halfway between 1 + 2^-7 and 1 + 2^-6)."""
+    E, R, H = 4, 2, 8
+    ids = np.array([[0], [1], [2], [3]], np.int32)
+    one = np.full((4, 1, H), 0x3F80, np.uint16)  # bf16 1.0
+    lay = oracle.layout(ids, E, R)
+    eo = oracle.place_slots(one, lay["pair_row"], 4)
+    w = np.array([[1 + 2 ** -8], [1 + 3 * 2 ** -8], [-(1 + 2 ** -8)], [1 + 2 ** -7]],
+                 np.float32)
+    out, out32, _ = oracle.combine(eo, lay["pair_row"], w)
+    # 1+2^-8 -> 1.0 (even mantissa 0x00); 1+3*2^-8 -> 1+2^-6 (0x3F82, even);
+    # negative tie -> -1.0; 1+2^-7 is exact (0x3F81).
+    assert list(out[:, 0]) == [0x3F80, 0x3F82, 0xBF80, 0x3F81], [hex(v) for v in out[:, 0]]
+
+
+PINS = [
+    pin_layout_stable_sort,
+    pin_layout_brute_force,
+    pin_layout_invariants,
+    pin_closed_form_exhaustive,
+    pin_closed_form_workloads,
+    pin_page_bytes,
+    pin_figure1,
+    pin_figure4,
+    pin_bad_ids,
+    pin_pack_permute_rows,
+    pin_permute_reads_own_segment,
+    pin_caps,
+    pin_roundtrip_identity,
+    pin_combine_one_hot,
+    pin_combine_scaling_and_skip,
+    pin_combine_k1,
+    pin_combine_exact_bound,
+    pin_combine_rounding_ties,
+]

@@ -1,0 +1,105 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of moe_oracle.c (on the CPU, in a
+temporary directory), builds it, and replays every pin against it: at least one
+pin must fail. This shows the pins constrain each part of the oracle: the
+placement of experts on ranks, the per-rank dedupe, the scan offsets, the
+token order, the permute's rank test and bookkeeping, the combine's slots,
+weights and rounding.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")
+TESTS = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(TESTS)
+
+MUTANTS = {
+    "round-robin placement": (
+        "on_rank[e / m] = 1;\n    }\n    for (int32_t r = 0; r < R; ++r) rank_counts[r] += on_rank[r];",
+        "on_rank[e % R] = 1;\n    }\n    for (int32_t r = 0; r < R; ++r) rank_counts[r] += on_rank[r];"),
+    "one copy per expert": (
+        "      expert_counts[e] += 1;\n      on_rank[e / m] = 1;",
+        "      expert_counts[e] += 1;\n      on_rank[e / m] += 1;"),
+    "inclusive rank scan": (
+        "for (int32_t r = 0; r < R; ++r) next_rank[r] = rank_offsets[r];",
+        "for (int32_t r = 0; r < R; ++r) next_rank[r] = rank_offsets[r + 1];"),
+    "expert runs start one late": (
+        "for (int32_t e = 0; e < E; ++e) next_expert[e] = expert_offsets[e];",
+        "for (int32_t e = 0; e < E; ++e) next_expert[e] = expert_offsets[e] + (e > 0);"),
+    "tokens walked backwards": (
+        "  for (int32_t t = 0; t < T; ++t) {\n    memset(on_rank, 0, (size_t)R);\n    for (int32_t j = 0; j < k; ++j) {\n      const int32_t e = topk_ids[(int64_t)t * k + j];\n      if (!id_is_expert(e, E)) {\n        pair_row",
+        "  for (int32_t t = T - 1; t >= 0; --t) {\n    memset(on_rank, 0, (size_t)R);\n    for (int32_t j = 0; j < k; ++j) {\n      const int32_t e = topk_ids[(int64_t)t * k + j];\n      if (!id_is_expert(e, E)) {\n        pair_row"),
+    "-1 reported as bad": (
+        "if (e != -1) err |= ORACLE_ERR_BAD_ID;",
+        "err |= ORACLE_ERR_BAD_ID;"),
+    "pack records wrong token": (
+        "rank_src_token[row] = t;",
+        "rank_src_token[row] = t + (r > 0);"),
+    "permute wrong rank test": (
+        "if (!id_is_expert(e, E) || e / m != r) continue;",
+        "if (!id_is_expert(e, E)) continue;"),
+    "permute wrong pair id": (
+        "expert_src_pair[dst] = t * k + j;",
+        "expert_src_pair[dst] = t * k;"),
+    "combine reversed weights": (
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);",
+        "acc = fmaf(topk_weights[(int64_t)t * k + (k - 1 - j)], widen_bf16(expert_out[row * H + h]), acc);"),
+    "combine drops last slot": (
+        "      float acc = 0.0f;\n      for (int32_t j = 0; j < k; ++j) {",
+        "      float acc = 0.0f;\n      for (int32_t j = 0; j < k - 1; ++j) {"),
+    "combine truncates": (
+        "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;",
+        "if (lower > 0xFFFFu) upper += 1u;"),
+    "combine ties round down": (
+        "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;",
+        "if (lower > 0x8000u) upper += 1u;"),
+    "combine ties away from zero": (
+        "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;",
+        "if (lower >= 0x8000u) upper += 1u;"),
+    "combine squares weight": (
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);",
+        "acc = fmaf(topk_weights[(int64_t)t * k + j] * topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);"),
+    "f64 combine rounds products to float": (
+        "acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);",
+        "acc += (double)(topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]));"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    find, repl = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site for {name!r} not found exactly once"
+    mutated = tmp_path / "moe_oracle.c"
+    mutated.write_text(src.replace(find, repl))
+    hdr = os.path.join(os.path.dirname(SRC), "moe_oracle.h")
+    (tmp_path / "moe_oracle.h").write_text(open(hdr).read())
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    str(mutated), "-o", str(lib), "-lm"], check=True)
+    # Run the pins in a child process: a broken oracle may write out of bounds.
+    script = (
+        "import sys; sys.path[:0] = [%r, %r]\n"
+        "import oracle, pins\n"
+        "failed = []\n"
+        "with oracle.use_library(%r):\n"
+        "    for pin in pins.PINS:\n"
+        "        try:\n"
+        "            pin()\n"
+        "        except (AssertionError, IndexError, ValueError):\n"
+        "            failed.append(pin.__name__)\n"
+        "print('FAILED_PINS', ' '.join(failed))\n"
+    ) % (ROOT, TESTS, str(lib))
+    proc = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True,
+                          timeout=300)
+    if proc.returncode != 0:
+        return  # the broken oracle crashed the pin run: caught
+    line = [x for x in proc.stdout.splitlines() if x.startswith("FAILED_PINS")][-1]
+    assert line.split()[1:], f"no pin caught the mutant {name!r}"
