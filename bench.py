@@ -1,0 +1,229 @@
+"""Benchmark: one step = one pass of the whole hot path (layout, pack,
+permute, combine) over one batch of seeded synthetic input already resident in
+HBM, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+Prints ONE JSON line: dispatch+combine throughput in GB/s of algorithmic bytes
+(what the method must move, with the measured copy count C and pair count P),
+its fraction of the 8 TB/s HBM peak, per-call times, the roofline of the
+dominant kernel (permute) measured with HIP events on the stream it runs on,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "dispatch+combine GB/s and % HBM peak, T=4096 H=5120 E=384 top-6 R=8"
+KERNEL_SOURCE = os.path.join(ROOT, "combine_topk_ids_02_amd", "csrc", "moe_dispatch.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(T, H, E, R, k, C, P):
+    """Bytes each call must move at least (each row read once, each copy
+    written once, plus the index arrays it reads and writes)."""
+    row = 2 * H
+    return {
+        "layout": 4 * T * k + 4 * T * R + 4 * T * k + 8 * (E + R + 1),
+        "pack": T * row + C * row + 4 * T * R + 4 * C,
+        "permute": C * row + P * row + 4 * C + 8 * T * k + 4 * P,
+        "combine": P * row + T * row + 8 * T * k,
+    }
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, only if the kernel source has not changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_sha256_16") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, hid, ids, wts, y, budget_s: float):
+    """The oracle as it stands, single-threaded, on the same workload: whole
+    steps (layout, pack, permute, combine) repeated until `budget_s` is used."""
+    import numpy as np
+
+    import oracle
+
+    T, k = ids.shape
+    cap_rank, cap_expert = T * min(k, w.R), T * k
+    lay = oracle.layout(ids, w.E, w.R)
+    eo = oracle.place_slots(y, lay["pair_row"], cap_expert)
+    reps, t_total = 0, 0.0
+    C = P = 0
+    while t_total < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        lay = oracle.layout(ids, w.E, w.R)
+        rb, src, _ = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
+        oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], w.E, cap_expert)
+        oracle.combine(eo, lay["pair_row"], wts, want_f32=False)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
+    nbytes = sum(algorithmic_bytes(T, w.H, w.E, w.R, k, C, P).values())
+    del np
+    return {
+        "value": round(nbytes * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
+        "kind": "oracle", "ms_per_step": round(1e3 * t_total / reps, 2),
+        "sample": f"{reps} whole {w.name} steps (layout+pack+permute+combine), "
+                  f"single thread, {t_total:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this path runs one GPU's share "
+              "of an expert-parallel layer, with the R ranks as logical buffers in its own HBM; "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__ as ge
+    ge.ensure_built()
+    import combine_topk_ids_02_amd as moe
+    import synth
+    from synth import staging
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
+    hid = synth.hidden(w)
+    ids, wts = synth.routing(w)
+    y = synth.expert_out_slots(w.seed, w.E, w.H, ids)
+
+    shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
+    buf = moe.Buffers(shape, dev)
+    hid_d = staging.rows_to_device(hid, dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    wts_d = torch.from_numpy(wts).to(dev)
+    moe.dispatch(buf, hid_d, ids_d)  # first layout gives pair_row for placing expert outputs
+    expert_out = staging.place_expert_outputs(staging.rows_to_device(y, dev), buf.pair_row,
+                                              shape.cap_expert)
+    torch.cuda.synchronize()
+    C = int(buf.rank_offsets[-1].item())
+    P = int(buf.expert_offsets[-1].item())
+    nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, C, P)
+    step_bytes = sum(nbytes.values())
+
+    stream = torch.cuda.current_stream(dev)
+    calls = ["layout", "pack", "permute", "combine"]
+
+    def step(ev=None):
+        s = shape
+        if ev is not None:
+            ev[0].record(stream)
+        moe.layout(ids_d, s.E, s.R, s.H, workspace=buf.workspace, err=buf.err,
+                   out=buf.layout_dict())
+        if ev is not None:
+            ev[1].record(stream)
+        moe.pack(hid_d, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token,
+                 err=buf.err)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, ids_d, buf.pair_row, s.E,
+                    buf.expert_buf, buf.expert_src_pair, err=buf.err)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.combine(expert_out, buf.pair_row, wts_d, s.E, s.R, buf.out, err=buf.err)
+        if ev is not None:
+            ev[4].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, events between the four calls of every step.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = {c: [] for c in calls}
+    for ev in evs:
+        for j, c in enumerate(calls):
+            per_call_ms[c].append(ev[j].elapsed_time(ev[j + 1]))
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][4])
+    ms_per_step = gpu_ms / args.steps
+    if int(buf.err.item()) != 0:
+        print(f"bench.py: device error word {int(buf.err.item())}", file=sys.stderr)
+        sys.exit(1)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    call_stats = {}
+    for c in calls:
+        ms = float(np.mean(per_call_ms[c]))
+        call_stats[c] = {"us": round(ms * 1e3, 2), "us_median": round(float(np.median(per_call_ms[c])) * 1e3, 2),
+                         "bytes": nbytes[c], "GB/s": round(nbytes[c] / (ms * 1e-3) / 1e9, 1)}
+    dom = "permute"
+    dom_us = call_stats[dom]["us"]
+    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "permute_rows",
+                "algorithmic_bytes_per_launch": nbytes[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, hid, ids, wts, y, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "T": w.T, "H": w.H, "E": w.E, "R": w.R, "k": w.k,
+                   "seed": w.seed, "copies_C": C, "pairs_P": P,
+                   "copies_per_token": round(C / max(w.T, 1), 4),
+                   "bytes_per_step": step_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "calls": call_stats,
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""Python binding of libmoe_dispatch.so (MoE token dispatch and combine on
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels on the
+caller's current torch stream. Torch tensors supply device memory; bf16 rows
+may be passed as torch.bfloat16, torch.int16 or torch.uint16 tensors (the bits
+are what matter). There is no CPU fallback: if the library is missing or the
+tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loads the HIP runtime the library binds to; must come first
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
+
+MOE_OK = 0
+MOE_ERR_ARG = -1
+MOE_ERR_HIP = -2
+MOE_ERR_WORKSPACE = -3
+ERRBIT_BAD_ID = 1
+ERRBIT_RANK_CAP = 2
+ERRBIT_EXPERT_CAP = 4
+ERRBIT_LAYOUT_TIMEOUT = 8
+
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_workspace_bytes",
+           "moe_dispatch_layout", "moe_dispatch_pack", "moe_permute_by_expert", "moe_combine")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MoeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    for name in EXPORTS:
+        if not hasattr(L, name):
+            raise MoeError(f"{LIB_PATH} does not export {name}")
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    shp = ctypes.POINTER(MoeShape)
+    L.moe_abi_version.restype = ctypes.c_int
+    L.moe_abi_version.argtypes = []
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_layout_workspace_bytes.restype = sz
+    L.moe_layout_workspace_bytes.argtypes = [shp]
+    L.moe_dispatch_layout.restype = ctypes.c_int
+    L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.moe_dispatch_pack.restype = ctypes.c_int
+    L.moe_dispatch_pack.argtypes = [shp, vp, vp, vp, vp, i64, vp, vp]
+    L.moe_permute_by_expert.restype = ctypes.c_int
+    L.moe_permute_by_expert.argtypes = [shp, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp, vp]
+    L.moe_combine.restype = ctypes.c_int
+    L.moe_combine.argtypes = [shp, vp, vp, vp, i64, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        msg = lib().moe_status_string(status).decode()
+        raise MoeError(f"{what} failed: {msg} ({status})")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoeError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise MoeError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _i32(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.int32:
+        raise MoeError(f"expected int32, got {t.dtype}")
+    return t
+
+
+def _rows16(t: torch.Tensor) -> torch.Tensor:
+    if t.element_size() != 2:
+        raise MoeError(f"expected a 16-bit row tensor, got {t.dtype}")
+    return t
+
+
+@dataclass
+class Shape:
+    T: int
+    H: int
+    E: int
+    R: int
+    k: int
+
+    def c(self) -> MoeShape:
+        return MoeShape(self.T, self.H, self.E, self.R, self.k)
+
+    @property
+    def cap_rank(self) -> int:
+        """Worst-case rank-buffer rows: T * min(k, R)."""
+        return self.T * min(self.k, self.R)
+
+    @property
+    def cap_expert(self) -> int:
+        """Worst-case expert-buffer rows: T * k."""
+        return self.T * self.k
+
+
+def workspace_bytes(shape: Shape) -> int:
+    n = lib().moe_layout_workspace_bytes(ctypes.byref(shape.c()))
+    if n == 0:
+        raise MoeError(f"invalid shape {shape}")
+    return n
+
+
+def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, workspace=None, err=None,
+           out: dict | None = None) -> dict:
+    """moe_dispatch_layout: counts, offsets, token_rank_slot [T,R], pair_row [T,k]."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    shape = Shape(T, H, E, R, k)
+    if out is None:
+        out = dict(
+            rank_counts=torch.empty(R, dtype=torch.int32, device=dev),
+            rank_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+            expert_counts=torch.empty(E, dtype=torch.int32, device=dev),
+            expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            token_rank_slot=torch.empty((T, R), dtype=torch.int32, device=dev),
+            pair_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+        )
+    if workspace is None:
+        workspace = torch.zeros(workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    st = lib().moe_dispatch_layout(
+        ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(out["rank_counts"]),
+        _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(err), _stream(dev))
+    _check(st, "moe_dispatch_layout")
+    return out
+
+
+def pack(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, rank_buf,
+         rank_src_token, *, err=None) -> None:
+    """moe_dispatch_pack into caller-provided rank_buf [cap_rank, H] and
+    rank_src_token [cap_rank]."""
+    T, H = hidden.shape
+    R = token_rank_slot.shape[1]
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_dispatch_pack(
+        ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
+        _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)), rank_buf.shape[0], _ptr(err),
+        _stream(hidden.device))
+    _check(st, "moe_dispatch_pack")
+
+
+def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, expert_buf,
+            expert_src_pair, *, err=None) -> None:
+    """moe_permute_by_expert into caller-provided expert_buf [cap_expert, H]."""
+    T, k = topk_ids.shape
+    H = rank_buf.shape[1]
+    R = rank_offsets.shape[0] - 1
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_permute_by_expert(
+        ctypes.byref(shape.c()), _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)),
+        _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)), _ptr(_i32(pair_row)),
+        rank_buf.shape[0], _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)),
+        expert_buf.shape[0], _ptr(err), _stream(rank_buf.device))
+    _check(st, "moe_permute_by_expert")
+
+
+def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=None,
+            err=None) -> None:
+    """moe_combine: out [T, H] bf16 (and optionally out_f32 [T, H] float32)."""
+    T, k = pair_row.shape
+    H = out.shape[1]
+    if topk_weights.dtype != torch.float32:
+        raise MoeError("topk_weights must be float32")
+    if out_f32 is not None and out_f32.dtype != torch.float32:
+        raise MoeError("out_f32 must be float32")
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_combine(
+        ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(pair_row)),
+        _ptr(topk_weights), expert_out.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err),
+        _stream(out.device))
+    _check(st, "moe_combine")
+
+
+class Buffers:
+    """Every buffer of one dispatch + combine pass, allocated once for a shape
+    at worst-case size (cap_rank = T*min(k,R), cap_expert = T*k rows)."""
+
+    def __init__(self, shape: Shape, device, row_dtype=torch.bfloat16, want_f32: bool = False):
+        T, H, E, R, k = shape.T, shape.H, shape.E, shape.R, shape.k
+        d = device
+        i32 = torch.int32
+        self.shape = shape
+        self.rank_counts = torch.empty(R, dtype=i32, device=d)
+        self.rank_offsets = torch.empty(R + 1, dtype=i32, device=d)
+        self.expert_counts = torch.empty(E, dtype=i32, device=d)
+        self.expert_offsets = torch.empty(E + 1, dtype=i32, device=d)
+        self.token_rank_slot = torch.empty((T, R), dtype=i32, device=d)
+        self.pair_row = torch.empty((T, k), dtype=i32, device=d)
+        self.workspace = torch.zeros(workspace_bytes(shape), dtype=torch.uint8, device=d)
+        self.rank_buf = torch.empty((shape.cap_rank, H), dtype=row_dtype, device=d)
+        self.rank_src_token = torch.empty(shape.cap_rank, dtype=i32, device=d)
+        self.expert_buf = torch.empty((shape.cap_expert, H), dtype=row_dtype, device=d)
+        self.expert_src_pair = torch.empty(shape.cap_expert, dtype=i32, device=d)
+        self.out = torch.empty((T, H), dtype=row_dtype, device=d)
+        self.out_f32 = torch.empty((T, H), dtype=torch.float32, device=d) if want_f32 else None
+        self.err = torch.zeros(1, dtype=i32, device=d)
+
+    def layout_dict(self) -> dict:
+        return dict(rank_counts=self.rank_counts, rank_offsets=self.rank_offsets,
+                    expert_counts=self.expert_counts, expert_offsets=self.expert_offsets,
+                    token_rank_slot=self.token_rank_slot, pair_row=self.pair_row)
+
+
+def dispatch(buf: Buffers, hidden, topk_ids) -> None:
+    """Layout, pack and permute into `buf` (three library calls, no host sync)."""
+    s = buf.shape
+    layout(topk_ids, s.E, s.R, s.H, workspace=buf.workspace, err=buf.err, out=buf.layout_dict())
+    pack(hidden, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token, err=buf.err)
+    permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, topk_ids, buf.pair_row, s.E,
+            buf.expert_buf, buf.expert_src_pair, err=buf.err)
+
+
+def combine_into(buf: Buffers, expert_out, topk_weights) -> None:
+    s = buf.shape
+    combine(expert_out, buf.pair_row, topk_weights, s.E, s.R, buf.out, out_f32=buf.out_f32,
+            err=buf.err)

@@ -1,0 +1,173 @@
+/*
+ * moe_dispatch.h — C ABI of libmoe_dispatch.so: MoE token dispatch and combine
+ * for one GPU's share of an expert-parallel layer, on AMD Instinct MI355X
+ * (gfx950). The R destination ranks are logical segments of one buffer in the
+ * GPU's own HBM.
+ *
+ * Pages cited (title, section):
+ *  [A2A]  "A2A backends" page, vincentzed.com/writing/a2a-backends
+ *  [GPUs] "How GPUs Talk to Each Other During LLM Inference"
+ *  [EP]   "Beyond One GPU: Tensor, Pipeline and Expert Parallelism, and Split
+ *         Prefill and Decode"
+ *
+ * Common conventions
+ *  - Every pointer argument except `shape` is a DEVICE pointer (hipMalloc'd or
+ *    a torch CUDA tensor). The caller owns every buffer; the library allocates
+ *    nothing, keeps no state between calls and is re-entrant for calls that
+ *    do not share output buffers or a workspace.
+ *  - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the null stream), never synchronise with the host and launch a
+ *    fixed number of kernels whose grids depend only on the shape and caps, so
+ *    they can be recorded in a HIP graph ([A2A] sec 1.4: fixed shapes, no CPU
+ *    wait for counts; sec 4.2 and 6.2: counts stay on the GPU).
+ *  - Return value: MOE_OK, or a negative moe_status_t for errors the host can
+ *    see (bad shape, NULL or misaligned pointer, workspace too small, launch
+ *    failure). On an argument error no kernel is launched.
+ *  - Data-dependent errors are OR-ed by the kernels into `*err_word` (a device
+ *    int32 the caller zeroes and reads when it chooses; may be NULL to ignore):
+ *    MOE_ERRBIT_BAD_ID, MOE_ERRBIT_RANK_CAP, MOE_ERRBIT_EXPERT_CAP,
+ *    MOE_ERRBIT_LAYOUT_TIMEOUT. Offending rows are dropped, never written out
+ *    of bounds ([A2A] sec 4.3: a batch larger than the cap fails).
+ *  - Types: expert ids int32; weights float32; hidden states and expert
+ *    outputs bf16 (passed as uint16_t bit patterns), row-major, row stride H.
+ *  - Ids: -1 means "no expert in this slot" and is skipped ([A2A] sec 2.1,
+ *    sec 6.3); any other id outside [0, E) is skipped and flagged. Duplicate
+ *    ids of one token each form their own (token, slot) pair and share the
+ *    token's single copy on that rank.
+ *  - Placement: expert e lives on rank e / (E/R) ([A2A] sec 1.1, 48 of 384
+ *    experts per GPU; sec 2.1, the local id range [first_local,
+ *    first_local + num_local); [EP] experts placed in order, E/G per GPU).
+ *  - Sizes: C = number of (token, rank) copies = rank_offsets[R];
+ *    P = number of valid (token, slot) pairs = expert_offsets[E]. Buffers sized
+ *    for the worst case, cap_rank = T*min(k,R) rows and cap_expert = T*k rows,
+ *    can never overflow ([A2A] sec 5.1: worst-case output plus an offsets list).
+ *  - Limits: 0 <= T, T*k < 2^30, T*R < 2^31; 1 <= R <= 64; E % R == 0;
+ *    1 <= E <= 1024; 1 <= k <= 32; H > 0 and H % 8 == 0; row buffers 16-byte
+ *    aligned.
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_DISPATCH_ABI_VERSION 1
+
+typedef struct moe_shape {
+  int32_t T; /* tokens on this GPU */
+  int32_t H; /* hidden size, bf16 elements per row */
+  int32_t E; /* experts */
+  int32_t R; /* ranks (logical destination GPUs) */
+  int32_t k; /* expert slots per token (top-k) */
+} moe_shape_t;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,       /* bad shape, NULL or misaligned pointer */
+  MOE_ERR_HIP = -2,       /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_WORKSPACE = -3  /* workspace missing or smaller than required */
+} moe_status_t;
+
+#define MOE_ERRBIT_BAD_ID 1         /* an id outside [-1, E) was skipped */
+#define MOE_ERRBIT_RANK_CAP 2       /* a copy at or past cap_rank was dropped */
+#define MOE_ERRBIT_EXPERT_CAP 4     /* a pair row at or past cap_expert was dropped or ignored */
+#define MOE_ERRBIT_LAYOUT_TIMEOUT 8 /* the layout scan gave up waiting for a tile (never expected) */
+
+/* ABI version of the loaded library (MOE_DISPATCH_ABI_VERSION at build time). */
+int moe_abi_version(void);
+
+/* Static text for a moe_status_t value. */
+const char* moe_status_string(int status);
+
+/* Bytes of device workspace moe_dispatch_layout needs for this shape (0 on a
+ * bad shape). The workspace must be zero-filled before its first use; every
+ * call that returns MOE_OK leaves it zero-filled again once its kernels have
+ * run. Two layout calls in flight at once must not share a workspace. */
+size_t moe_layout_workspace_bytes(const moe_shape_t* shape);
+
+/*
+ * Dispatch, step 1: layout ([A2A] sec 3.2 first step: per token, the set of
+ * ranks holding at least one of its experts, and how many rows each rank gets;
+ * sec 5.1: counts and offsets stay on the GPU, an offsets list says where each
+ * expert's rows begin; sec 1.3: one copy per distinct rank).
+ *   topk_ids         [T*k]   in:  router expert ids, row-major [T, k]
+ *   rank_counts      [R]     out: copies per rank, #{t : rank r holds an expert of t}
+ *   rank_offsets     [R+1]   out: exclusive prefix sum of rank_counts (rank_offsets[R] = C)
+ *   expert_counts    [E]     out: valid pairs per expert
+ *   expert_offsets   [E+1]   out: exclusive prefix sum of expert_counts (expert_offsets[E] = P)
+ *   token_rank_slot  [T*R]   out: row of token t's copy in rank r's segment, or -1;
+ *                                 rows of a segment ascend with t
+ *   pair_row         [T*k]   out: row of pair (t, j) in the expert-grouped buffer, or -1;
+ *                                 rows of an expert's run ascend with (t, j)
+ *   workspace, workspace_bytes: device scratch, see moe_layout_workspace_bytes
+ *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID, MOE_ERRBIT_LAYOUT_TIMEOUT)
+ * The result is a pure function of topk_ids: no order depends on timing.
+ */
+int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* rank_counts,
+                        int32_t* rank_offsets, int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* token_rank_slot, int32_t* pair_row, void* workspace,
+                        size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/*
+ * Dispatch, step 2: pack ([A2A] sec 1.3 third answer and sec 3.2: a token is
+ * sent once to each rank in its set, however many of its experts live there).
+ * Reads each hidden row once and writes it to every row token_rank_slot[t*R+r]
+ * >= 0 of the rank-major buffer; rank_src_token[row] = t.
+ *   hidden          [T*H]          in:  bf16
+ *   token_rank_slot [T*R]          in:  from moe_dispatch_layout
+ *   rank_buf        [cap_rank*H]   out: bf16 rows, segment r = rows
+ *                                       [rank_offsets[r], rank_offsets[r+1])
+ *   rank_src_token  [cap_rank]     out: source token of each written row
+ *   cap_rank: rows available; copies at or past it are dropped (MOE_ERRBIT_RANK_CAP)
+ * Rows past C are left untouched.
+ */
+int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
+                      const int32_t* token_rank_slot, uint16_t* rank_buf, int32_t* rank_src_token,
+                      int64_t cap_rank, int32_t* err_word, void* stream);
+
+/*
+ * Dispatch, step 3: permute by expert on the receiving side ([A2A] sec 3.3:
+ * each arrived row is copied once for each of its experts on this rank, into
+ * one run of rows per expert; sec 5.1: the copy epilogue with do_expand, one
+ * row per (token, local expert), grouped by expert).
+ * Every rank-buffer row i < min(rank_offsets[R], cap_rank), in the segment of
+ * rank r and holding token t = rank_src_token[i], is read once and written to
+ * pair_row[t*k+j] for every slot j of t whose expert lives on rank r;
+ * expert_src_pair[that row] = t*k + j.
+ *   rank_buf [cap_rank*H], rank_src_token [cap_rank], rank_offsets [R+1],
+ *   topk_ids [T*k], pair_row [T*k]                      in
+ *   expert_buf [cap_expert*H], expert_src_pair [cap_expert]   out
+ *   cap_rank: rows of rank_buf; cap_expert: rows of expert_buf (rows at or past
+ *   it are dropped, MOE_ERRBIT_EXPERT_CAP). Rows past P are left untouched.
+ */
+int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
+                          const int32_t* rank_src_token, const int32_t* rank_offsets,
+                          const int32_t* topk_ids, const int32_t* pair_row, int64_t cap_rank,
+                          uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
+                          int32_t* err_word, void* stream);
+
+/*
+ * Combine ([A2A] sec 1.1: the MoE output of a token is the sum of its chosen
+ * experts' outputs, each multiplied by its weight; sec 7.1: the sum is taken
+ * in 32-bit floats; [GPUs] sec 3.3: a fixed addition order makes the result
+ * reproducible).
+ *   out[t][h] = bf16_rne(acc), acc = +0.0f then, for j = 0..k-1 in order with
+ *   row = pair_row[t*k+j] >= 0: acc = fmaf(topk_weights[t*k+j],
+ *   float(expert_out[row][h]), acc). Rows at or past cap_expert are skipped
+ *   and flagged (MOE_ERRBIT_EXPERT_CAP).
+ *   expert_out [cap_expert*H] in: bf16 expert outputs in the expert-grouped order
+ *   pair_row [T*k], topk_weights [T*k] in
+ *   out [T*H] out: bf16; out_f32 [T*H] out: the float32 sums, or NULL
+ */
+int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int32_t* pair_row,
+                const float* topk_weights, int64_t cap_expert, uint16_t* out, float* out_f32,
+                int32_t* err_word, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

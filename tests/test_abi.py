@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments before launching anything (host-only checks; no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_topk_ids_02_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+
+
+def shape(T=64, H=512, E=16, R=4, k=2):
+    return moe.MoeShape(T, H, E, R, k)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(T=-1), dict(H=0), dict(H=12), dict(E=0), dict(R=0), dict(R=65, E=130), dict(E=10, R=4),
+    dict(k=0), dict(k=33, E=64), dict(E=2048, R=8), dict(T=1 << 28, k=8),
+])
+def test_workspace_query_rejects_bad_shapes(bad):
+    assert moe.lib().moe_layout_workspace_bytes(ctypes.byref(shape(**bad))) == 0
+
+
+def test_workspace_query_sizes():
+    L = moe.lib()
+    n = L.moe_layout_workspace_bytes(ctypes.byref(shape(T=4096, E=384, R=8, k=6)))
+    assert n == 16 * (384 + 8) * 4  # 16 tiles of 256 tokens, one int per column
+    n0 = L.moe_layout_workspace_bytes(ctypes.byref(shape(T=0)))
+    assert n0 > 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
+
+
+def test_calls_reject_bad_arguments_without_launching():
+    L = moe.lib()
+    s = shape()
+    sp = ctypes.byref(s)
+    bad = ctypes.byref(shape(E=10))
+    # layout: bad shape, NULL outputs, missing/small workspace
+    assert L.moe_dispatch_layout(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                 None, None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_layout(sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                 None, None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 20,
+                                 None, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                                 None, None) == moe.MOE_ERR_WORKSPACE
+    # pack: NULL hidden, misaligned rows, negative cap
+    assert L.moe_dispatch_pack(sp, None, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_pack(sp, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, 128, None,
+                               None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_pack(sp, FAKE, FAKE, FAKE, FAKE, -1, None, None) == moe.MOE_ERR_ARG
+    # permute / combine
+    assert L.moe_permute_by_expert(sp, FAKE, FAKE, None, FAKE, FAKE, 128, FAKE, FAKE, 128,
+                                   None, None) == moe.MOE_ERR_ARG
+    assert L.moe_permute_by_expert(sp, FAKE, FAKE, FAKE, FAKE, FAKE, 128, ctypes.c_void_p(0x10004),
+                                   FAKE, 128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine(sp, FAKE, None, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, ctypes.c_void_p(0x10002), None,
+                         None) == moe.MOE_ERR_ARG
+    assert L.moe_combine(bad, FAKE, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
+
+
+def test_empty_batches_are_no_ops():
+    L = moe.lib()
+    s0 = ctypes.byref(shape(T=0))
+    assert L.moe_dispatch_pack(s0, None, None, None, None, 0, None, None) == moe.MOE_OK
+    assert L.moe_combine(s0, None, None, None, 0, None, None, None, None) == moe.MOE_OK
+    assert L.moe_permute_by_expert(s0, None, None, FAKE, None, None, 0, None, None, 0, None,
+                                   None) == moe.MOE_OK
+
+
+def test_status_strings():
+    L = moe.lib()
+    assert L.moe_status_string(0) == b"ok"
+    assert b"workspace" in L.moe_status_string(-3)

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path, called through the C ABI, against the oracle on
+the same seeded inputs. Layout, offsets, indices and packed rows must match
+bit for bit; combine must be within 1 bf16 ulp (and 1e-6 relative in fp32) of
+the oracle — and is in fact bit-exact, since both take the same fused
+multiply-adds in the same slot order."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import pins
+import synth
+from gpu_path import compare, relative_error_vs_exact, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+FP32_REL_TOL = 1e-6   # relative to max(|exact|, sum_j |w_j y_j|)
+BF16_ULP_TOL = 1
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests must run on an MI355X")
+    import combine_topk_ids_02_amd as moe
+    moe.lib()
+
+
+def workload_inputs(name):
+    w = synth.WORKLOADS[name]
+    hid = synth.hidden(w)
+    ids, wts = synth.routing(w)
+    y = synth.expert_out_slots(w.seed, w.E, w.H, ids)
+    return w, hid, ids, wts, y
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
+def test_workload_parity(name):
+    w, hid, ids, wts, y = workload_inputs(name)
+    say(f"[parity] {w.describe()}")
+    gpu = run_gpu(hid, ids, wts, w.E, w.R, y)
+    ref = run_oracle(hid, ids, wts, w.E, w.R, y, gpu["cap_rank"], gpu["cap_expert"])
+    assert ref["err"] == 0
+    compare(gpu, ref, name)
+    if name in ("tiny", "decode", "prefill"):
+        rel = relative_error_vs_exact(gpu["out_f32"], ref["expert_out"], ref["layout"]["pair_row"],
+                                      wts)
+        assert rel <= FP32_REL_TOL, rel
+
+
+def test_identity_round_trip():
+    """Identity experts and renormalised weights: combine returns hidden."""
+    w, hid, ids, wts, _ = workload_inputs("prefill")
+    gpu = run_gpu(hid, ids, wts, w.E, w.R, None, want_f32=False)
+    a, b = gpu["out"], hid
+    zero = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+    assert np.all((a == b) | zero)
+
+
+EDGE = [
+    # (T, H, E, R, k, p_neg, p_dup, seed)
+    (1, 8, 2, 1, 1, 0.0, 0.0, 1),
+    (0, 512, 16, 4, 2, 0.0, 0.0, 2),
+    (3, 520, 8, 8, 3, 0.0, 0.0, 3),          # E = R; H not a multiple of 512 (tail columns)
+    (257, 512, 16, 4, 2, 0.1, 0.0, 4),       # ragged last tile
+    (1000, 1024, 64, 8, 4, 0.05, 0.1, 5),    # -1 slots and duplicate ids
+    (300, 16384, 32, 4, 4, 0.0, 0.0, 6),     # two register passes per row
+    (16385, 64, 16, 4, 2, 0.0, 0.0, 7),      # two sub-tiles per layout tile
+    (20000, 16, 256, 8, 8, 0.1, 0.0, 8),
+    (2000, 64, 1024, 64, 32, 0.02, 0.02, 9),  # largest E, R, k
+    (700, 256, 96, 1, 5, 0.0, 0.0, 10),      # one rank
+    (513, 2880, 384, 8, 6, 0.0, 0.0, 11),    # 360 uint4 per row: 5 full groups + tail
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_R{c[3]}_k{c[4]}" for c in EDGE])
+def test_edge_shapes(case):
+    T, H, E, R, k, pn, pd, seed = case
+    say(f"[edge] T={T} H={H} E={E} R={R} k={k}")
+    rng = np.random.default_rng(seed)
+    ids = pins.rand_ids(rng, T, E, k, p_neg=pn, p_dup=pd)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
+    y = synth.expert_out_slots(seed, E, H, ids)
+    gpu = run_gpu(hid, ids, wts, E, R, y)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    compare(gpu, ref, f"edge {case}")
+
+
+def test_all_tokens_on_one_rank():
+    T, H, E, R, k = 3000, 512, 64, 8, 6
+    rng = np.random.default_rng(12)
+    m = E // R
+    ids = np.stack([rng.permutation(m)[:k] + 3 * m for _ in range(T)]).astype(np.int32)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(12, 0, T * H).reshape(T, H)
+    y = synth.expert_out_slots(12, E, H, ids)
+    gpu = run_gpu(hid, ids, wts, E, R, y)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    assert int(ref["layout"]["rank_counts"][3]) == T
+    compare(gpu, ref, "one rank")
+
+
+def test_hot_expert_histogram():
+    """Every token picks expert 5 plus others: a single histogram bin gets T."""
+    T, H, E, R, k = 5000, 64, 32, 4, 4
+    rng = np.random.default_rng(13)
+    ids = pins.rand_ids(rng, T, E, k)
+    ids[:, 2] = np.where(ids[:, 0] == 5, ids[:, 2], 5)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(13, 0, T * H).reshape(T, H)
+    y = synth.expert_out_slots(13, E, H, ids)
+    gpu = run_gpu(hid, ids, wts, E, R, y)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    compare(gpu, ref, "hot expert")
+
+
+def test_bad_ids_are_flagged_and_skipped():
+    T, H, E, R, k = 600, 256, 32, 4, 4
+    rng = np.random.default_rng(14)
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1, p_bad=0.1)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(14, 0, T * H).reshape(T, H)
+    y = synth.expert_out_slots(14, E, H, ids)
+    gpu = run_gpu(hid, ids, wts, E, R, y)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    assert ref["err"] == 1
+    compare(gpu, ref, "bad ids")
+
+
+def test_undersized_buffers_drop_and_flag():
+    w, hid, ids, wts, y = workload_inputs("tiny")
+    lay = run_oracle(hid, ids, wts, w.E, w.R, None, w.T * 2, w.T * 2)["layout"]
+    C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
+    cap_rank, cap_expert = C - 37, P - 51
+    gpu = run_gpu(hid, ids, wts, w.E, w.R, y, cap_rank=cap_rank, cap_expert=cap_expert,
+                  spare_rows=64)
+    ref = run_oracle(hid, ids, wts, w.E, w.R, y, cap_rank, cap_expert)
+    assert ref["err"] == 2 | 4
+    compare(gpu, ref, "undersized")
+
+
+def test_deterministic_and_stream_independent():
+    w, hid, ids, wts, y = workload_inputs("decode")
+    a = run_gpu(hid, ids, wts, w.E, w.R, y)
+    b = run_gpu(hid, ids, wts, w.E, w.R, y, stream=torch.cuda.Stream())
+    for key in ("token_rank_slot", "pair_row", "rank_all", "expert_all", "out", "out_f32"):
+        assert np.array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8)), key
