@@ -146,8 +146,7 @@ def main():
         s = shape
         if ev is not None:
             ev[0].record(stream)
-        moe.layout(ids_d, s.E, s.R, s.H, workspace=buf.workspace, err=buf.err,
-                   out=buf.layout_dict())
+        moe.layout(ids_d, s.E, s.R, s.H, err=buf.err, out=buf.layout_dict())
         if ev is not None:
             ev[1].record(stream)
         moe.pack(hid_d, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token,
@@ -167,20 +166,31 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, events between the four calls of every step.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Timed region: K whole steps, bracketed by events on the stream the
+    # kernels run on (and a host clock around the synchronisations).
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_begin.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+
+    # Second timed pass with an event between every call, for per-kernel
+    # durations and the roofline of the dominant kernel.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_call_ms = {c: [] for c in calls}
     for ev in evs:
         for j, c in enumerate(calls):
             per_call_ms[c].append(ev[j].elapsed_time(ev[j + 1]))
-    gpu_ms = evs[0][0].elapsed_time(evs[-1][4])
-    ms_per_step = gpu_ms / args.steps
     if int(buf.err.item()) != 0:
         print(f"bench.py: device error word {int(buf.err.item())}", file=sys.stderr)
         sys.exit(1)

@@ -21,14 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe_dispatch.so")
 MOE_OK = 0
 MOE_ERR_ARG = -1
 MOE_ERR_HIP = -2
-MOE_ERR_WORKSPACE = -3
 ERRBIT_BAD_ID = 1
 ERRBIT_RANK_CAP = 2
 ERRBIT_EXPERT_CAP = 4
-ERRBIT_LAYOUT_TIMEOUT = 8
 
-EXPORTS = ("moe_abi_version", "moe_status_string", "moe_layout_workspace_bytes",
-           "moe_dispatch_layout", "moe_dispatch_pack", "moe_permute_by_expert", "moe_combine")
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout", "moe_dispatch_pack",
+           "moe_permute_by_expert", "moe_combine")
 
 
 class MoeShape(ctypes.Structure):
@@ -54,16 +52,14 @@ def lib():
     for name in EXPORTS:
         if not hasattr(L, name):
             raise MoeError(f"{LIB_PATH} does not export {name}")
-    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
     shp = ctypes.POINTER(MoeShape)
     L.moe_abi_version.restype = ctypes.c_int
     L.moe_abi_version.argtypes = []
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
-    L.moe_layout_workspace_bytes.restype = sz
-    L.moe_layout_workspace_bytes.argtypes = [shp]
     L.moe_dispatch_layout.restype = ctypes.c_int
-    L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_dispatch_pack.restype = ctypes.c_int
     L.moe_dispatch_pack.argtypes = [shp, vp, vp, vp, vp, i64, vp, vp]
     L.moe_permute_by_expert.restype = ctypes.c_int
@@ -128,14 +124,7 @@ class Shape:
         return self.T * self.k
 
 
-def workspace_bytes(shape: Shape) -> int:
-    n = lib().moe_layout_workspace_bytes(ctypes.byref(shape.c()))
-    if n == 0:
-        raise MoeError(f"invalid shape {shape}")
-    return n
-
-
-def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, workspace=None, err=None,
+def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, err=None,
            out: dict | None = None) -> dict:
     """moe_dispatch_layout: counts, offsets, token_rank_slot [T,R], pair_row [T,k]."""
     T, k = topk_ids.shape
@@ -150,13 +139,10 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, workspace=None
             token_rank_slot=torch.empty((T, R), dtype=torch.int32, device=dev),
             pair_row=torch.empty((T, k), dtype=torch.int32, device=dev),
         )
-    if workspace is None:
-        workspace = torch.zeros(workspace_bytes(shape), dtype=torch.uint8, device=dev)
     st = lib().moe_dispatch_layout(
         ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(out["rank_counts"]),
         _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
-        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(err), _stream(dev))
+        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(err), _stream(dev))
     _check(st, "moe_dispatch_layout")
     return out
 
@@ -222,7 +208,6 @@ class Buffers:
         self.expert_offsets = torch.empty(E + 1, dtype=i32, device=d)
         self.token_rank_slot = torch.empty((T, R), dtype=i32, device=d)
         self.pair_row = torch.empty((T, k), dtype=i32, device=d)
-        self.workspace = torch.zeros(workspace_bytes(shape), dtype=torch.uint8, device=d)
         self.rank_buf = torch.empty((shape.cap_rank, H), dtype=row_dtype, device=d)
         self.rank_src_token = torch.empty(shape.cap_rank, dtype=i32, device=d)
         self.expert_buf = torch.empty((shape.cap_expert, H), dtype=row_dtype, device=d)
@@ -240,7 +225,7 @@ class Buffers:
 def dispatch(buf: Buffers, hidden, topk_ids) -> None:
     """Layout, pack and permute into `buf` (three library calls, no host sync)."""
     s = buf.shape
-    layout(topk_ids, s.E, s.R, s.H, workspace=buf.workspace, err=buf.err, out=buf.layout_dict())
+    layout(topk_ids, s.E, s.R, s.H, err=buf.err, out=buf.layout_dict())
     pack(hidden, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token, err=buf.err)
     permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, topk_ids, buf.pair_row, s.E,
             buf.expert_buf, buf.expert_src_pair, err=buf.err)

@@ -7,20 +7,22 @@
 //  [GPUs] "How GPUs Talk to Each Other During LLM Inference"
 //
 // Kernels
-//  layout_tiles     per tile of tokens: wavefront-ballot stable ranks and LDS
-//                   histograms per expert and per rank ([A2A] sec 3.2 step 1)
-//  layout_finalize  per block: tile prefix from the per-tile histograms,
-//                   exclusive scans over experts and ranks, absolute rows
-//                   ([A2A] sec 5.1: offsets list on the GPU, no CPU wait)
-//  pack             one wave per token: read the row once, write one copy per
-//                   distinct rank ([A2A] sec 1.3 third answer)
-//  permute          one wave per rank-buffer row: read once, write once per
-//                   local expert ([A2A] sec 3.3, sec 5.1 do_expand)
-//  combine          one wave per token: k row gathers, fp32 FMA in slot
-//                   order, bf16 round-to-nearest-even ([A2A] sec 1.1, 7.1;
-//                   [GPUs] sec 3.3 fixed addition order)
-// Row copies move 16 bytes per lane (global_load/store_dwordx4), 1 KiB per
-// wave instruction; nothing here is a dense contraction, so no MFMA.
+//  layout_tiles  one launch. Every workgroup histograms all tokens (LDS
+//                atomics per expert, wavefront ballots per rank), scans the
+//                totals into expert and rank offsets, then ranks its own tile
+//                of tokens with wavefront ballots and writes absolute rows
+//                ([A2A] sec 3.2 step 1: per-token rank set and per-rank
+//                counts; sec 5.1: offsets stay on the GPU, no CPU wait)
+//  pack_rows     one wave per token: read the row once, write one copy per
+//                distinct rank ([A2A] sec 1.3 third answer)
+//  permute_rows  one wave per rank-buffer row: read once, write once per
+//                local expert ([A2A] sec 3.3, sec 5.1 do_expand)
+//  combine_rows  one wave per (token, column slice): k row gathers, fp32 FMA
+//                in slot order, bf16 round-to-nearest-even ([A2A] sec 1.1,
+//                7.1; [GPUs] sec 3.3 fixed addition order)
+// Rows move 16 bytes per lane (global_load/store_dwordx4), 1 KiB per wave
+// instruction; copies are stored non-temporally, since nothing re-reads them
+// inside the kernel. Nothing here is a dense contraction, so no MFMA.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,16 +33,16 @@
 
 namespace {
 
+typedef uint32_t vec4 __attribute__((ext_vector_type(4)));  // 8 bf16
+
 constexpr int kWave = 64;
-constexpr int kBlock = 256;                 // 4 waves per workgroup
+constexpr int kBlock = 256;                 // row movers: 4 waves per workgroup
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kSubTile = kBlock;            // tokens per layout sub-tile: one per thread
-constexpr int kMaxTiles = 64;               // layout tiles per call (tile size grows with T)
+constexpr int kMaxTiles = 64;               // layout workgroups per call
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxRanks = 64;
-constexpr int kMaxK = 32;
-constexpr int kExpertBits = 10;             // packed (wave rank << 10 | expert) in LDS
-constexpr int kMaxVec = 16;                 // uint4 per lane held in registers per pass
+constexpr int kMaxK = 16;
+constexpr int kMaxVec = 16;                 // vec4 per lane held in registers per pass
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -56,213 +58,317 @@ __device__ __forceinline__ void flag_error(int32_t* err_word, int bit) {
   if (err_word) atomicOr(err_word, bit);
 }
 
+__device__ __forceinline__ void store_stream(vec4* p, vec4 v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // ---------------------------------------------------------------------------
 // Layout
 
+constexpr int kLayoutWaves = 16;                 // 1024 threads per workgroup
+constexpr int kLayoutThreads = kLayoutWaves * kWave;
+constexpr int kOwnTokens = 256;                  // tokens ranked per sub-tile (waves 0..3)
+constexpr int kOwnWaves = kOwnTokens / kWave;
+constexpr int kBatchVecs = 8;                    // 16-byte id loads per thread per batch
+constexpr size_t kLayoutLdsLimit = 160 * 1024 - 1024;  // gfx950: 160 KiB of LDS per workgroup
+
 struct LayoutGeom {
-  int T, E, R, k, m;   // m = experts per rank
-  int ncols;           // E expert columns followed by R rank columns
-  int tile_tokens;     // multiple of kSubTile
+  int T, E, R, k, m;    // m = experts per rank
+  int ncols;            // E expert columns followed by R rank columns
+  int batch_tokens;     // tokens whose ids are staged in LDS at once (multiple of 1024)
+  int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
   int ntiles;
+  uint64_t rank_magic;  // ceil(2^32 / m)
 };
 
-// Per tile: for every valid pair, its rank among the tile's pairs of the same
-// expert (in (token, slot) order), and for every (token, rank) copy its rank
-// among the tile's tokens with a copy on that rank; both are written into the
-// output arrays, relative to the tile. The tile's per-column totals go to
-// tile_counts[tile][col].
-__global__ __launch_bounds__(kBlock) void layout_tiles(LayoutGeom g, const int32_t* __restrict__ ids,
-                                                       int32_t* __restrict__ pair_row,
-                                                       int32_t* __restrict__ token_rank_slot,
-                                                       int32_t* __restrict__ tile_counts,
-                                                       int32_t* err_word) {
+// rank(e) = e / m, as (e * ceil(2^32/m)) >> 32: exact for 0 <= e < 2^16 and
+// m <= 2^10 (the rounding error e*(ceil(2^32/m) - 2^32/m) / 2^32 < 2^-16
+// never reaches the next multiple of 1/m).
+__device__ __forceinline__ int rank_of(int e, uint64_t magic) {
+  return int((uint64_t(uint32_t(e)) * magic) >> 32);
+}
+
+// Inclusive prefix sum across a wave with DPP row shifts and broadcasts.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive scans of the expert columns s[0..E) (waves 0..7) and of the rank
+// columns s[E..E+R) (wave 8) in place, both at once. Returns nothing; the
+// totals are left in s_tmp[8] (experts) and s_tmp[9] (ranks).
+__device__ void scan_columns(int32_t* s, int E, int R, int32_t* s_tmp /* [16] */) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  constexpr int kScanThreads = 8 * kWave;
+  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= 2 for E <= 1024
+  int lo = 0, hi = 0, sum = 0, x = 0;
+  if (wave < 8) {
+    lo = min(E, tid * per);
+    hi = min(E, lo + per);
+    for (int i = lo; i < hi; ++i) sum += s[i];
+    x = wave_inclusive_scan(sum);
+    if (lane == kWave - 1) s_tmp[wave] = x;
+  } else if (wave == 8) {
+    const int v = lane < R ? s[E + lane] : 0;
+    const int inc = wave_inclusive_scan(v);
+    if (lane < R) s[E + lane] = inc - v;
+    if (lane == kWave - 1) s_tmp[9] = inc;
+  }
+  __syncthreads();
+  if (wave < 8) {
+    int base = 0, total = 0;
+    for (int w = 0; w < 8; ++w) {
+      const int t = s_tmp[w];
+      base += w < wave ? t : 0;
+      total += t;
+    }
+    int run = base + x - sum;
+    for (int i = lo; i < hi; ++i) {
+      const int v = s[i];
+      s[i] = run;
+      run += v;
+    }
+    if (tid == 0) s_tmp[8] = total;
+  }
+  __syncthreads();
+}
+
+// Loads ids [f0, f0 + 4*nvec) flat, 16 bytes per lane: slot q of thread i
+// holds ids f0 + 4*(q*1024 + i) .. +3 (past n_ids: -1).
+__device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int64_t n_ids,
+                                           int64_t f0, int nvec, vec4 (&r)[kBatchVecs]) {
+#pragma unroll
+  for (int q = 0; q < kBatchVecs; ++q) {
+    const int v = q * kLayoutThreads + threadIdx.x;
+    if (v < nvec) {
+      const int64_t f = f0 + 4 * int64_t(v);
+      if (f + 4 <= n_ids) {
+        r[q] = *reinterpret_cast<const vec4*>(ids + f);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) r[q][x] = f + x < n_ids ? uint32_t(ids[f + x]) : ~0u;
+      }
+    }
+  }
+}
+
+// One workgroup of 1024 threads per tile of g.tile_tokens tokens; K = k known
+// at compile time (0: any k up to kMaxK, read at run time). Writes:
+//   pair_row[t][j]        = expert_offsets[e] + #{pairs of e before (t, j)}
+//   token_rank_slot[t][r] = rank_offsets[r] + #{tokens before t with a copy on r}
+// Workgroup 0 also writes the counts and offsets.
+template <int K>
+__global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
+    LayoutGeom g, const int32_t* __restrict__ ids, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
+    int32_t* __restrict__ pair_row, int32_t* err_word) {
+  constexpr int KR = K > 0 ? K : kMaxK;
+  const int k = K > 0 ? K : g.k;
   extern __shared__ int32_t smem[];
-  int32_t* s_pack = smem;                              // [kSubTile * k]
-  int32_t* s_cnt = s_pack + kSubTile * g.k;            // [kWavesPerBlock][ncols]
-  int32_t* s_base = s_cnt + kWavesPerBlock * g.ncols;  // [ncols] running tile totals
+  int32_t* s_ids = smem;                          // [batch_tokens * k] staged ids
+  int32_t* s_pack = s_ids + g.batch_tokens * k + 4;  // [kOwnTokens * k] own sub-tile ids
+  int32_t* s_cnt = s_pack + kOwnTokens * k;       // [kOwnWaves][ncols] per-wave counts
+  int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols] before the tile -> running base
+  int32_t* s_tot = s_pre + g.ncols;               // [ncols] other tokens -> totals -> offsets
+  __shared__ int32_t s_tmp[kLayoutWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
-  const int tile = blockIdx.x;
-  const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);  // bits that tell experts apart
+  const int64_t n_ids = (int64_t)g.T * k;
+  const int tile_lo = blockIdx.x * g.tile_tokens;
+  const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
+  const bool one_sub = g.tile_tokens == kOwnTokens;  // own ids captured from the batch
+
+  for (int c = tid; c < g.ncols; c += kLayoutThreads) {
+    s_pre[c] = 0;
+    s_tot[c] = 0;
+  }
+
+  // 1. Histogram of every token, a batch of tokens at a time: all of a
+  //    batch's ids are requested at once (16 bytes per lane, coalesced) and
+  //    staged in LDS, the next batch's loads in flight while this one is
+  //    counted. Experts: one LDS atomic per pair. Ranks: one ballot per rank
+  //    per 64 tokens (a wave's 64 tokens sit on one side of the tile start).
+  const int batch_ids = g.batch_tokens * k;
+  vec4 nxt[kBatchVecs];
+  load_batch(ids, n_ids, 0, (int)((std::min<int64_t>(batch_ids, n_ids) + 3) / 4), nxt);
+  for (int b0 = 0; b0 < g.T; b0 += g.batch_tokens) {
+    const int nb = min(g.batch_tokens, g.T - b0);
+    const int nvec = (nb * k + 3) / 4;
+    __syncthreads();  // s_ids free; s_pre/s_tot zeroed
+#pragma unroll
+    for (int q = 0; q < kBatchVecs; ++q) {
+      const int v = q * kLayoutThreads + tid;
+      if (v < nvec) *reinterpret_cast<vec4*>(s_ids + 4 * v) = nxt[q];
+    }
+    const int b1 = b0 + g.batch_tokens;
+    if (b1 < g.T) {
+      const int nn = min(g.batch_tokens, g.T - b1);
+      load_batch(ids, n_ids, (int64_t)b1 * k, (nn * k + 3) / 4, nxt);
+    }
+    __syncthreads();
+    if (one_sub && b0 <= tile_lo && tile_lo < b0 + nb) {
+      const int base = (tile_lo - b0) * k;
+      const int n_own = min(kOwnTokens, tile_hi - tile_lo) * k;
+      for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads)
+        s_pack[f] = f < n_own ? s_ids[base + f] : -1;
+    }
+    for (int tl = tid; tl < ((nb + kWave - 1) & ~(kWave - 1)); tl += kLayoutThreads) {
+      int32_t* cnt = b0 + (tl & ~(kWave - 1)) < tile_lo ? s_pre : s_tot;
+      uint64_t mask = 0;
+      if (tl < nb) {
+        const int32_t* my = s_ids + tl * k;
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+          if (j < k) {
+            const int e = my[j];
+            if (e >= 0 && e < g.E) {
+              atomicAdd(&cnt[e], 1);
+              mask |= uint64_t(1) << rank_of(e, g.rank_magic);
+            }
+          }
+        }
+      }
+      for (int r = 0; r < g.R; ++r) {
+        const uint64_t on = __ballot((mask >> r) & 1);
+        if (lane == 0 && on) atomicAdd(&cnt[g.E + r], __popcll(on));
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < g.ncols; c += kLayoutThreads) s_tot[c] += s_pre[c];
+  __syncthreads();
+
+  // 2. Counts, then exclusive scans: experts in id order, ranks in rank order.
+  if (blockIdx.x == 0) {
+    for (int c = tid; c < g.E; c += kLayoutThreads) expert_counts[c] = s_tot[c];
+    for (int c = tid; c < g.R; c += kLayoutThreads) rank_counts[c] = s_tot[g.E + c];
+  }
+  __syncthreads();
+  scan_columns(s_tot, g.E, g.R, s_tmp);
+  if (blockIdx.x == 0) {
+    for (int c = tid; c < g.E; c += kLayoutThreads) expert_offsets[c] = s_tot[c];
+    for (int c = tid; c < g.R; c += kLayoutThreads) rank_offsets[c] = s_tot[g.E + c];
+    if (tid == 0) {
+      expert_offsets[g.E] = s_tmp[8];
+      rank_offsets[g.R] = s_tmp[9];
+    }
+  }
+  // 3. Absolute first row of this tile in every column.
+  for (int c = tid; c < g.ncols; c += kLayoutThreads) s_pre[c] += s_tot[c];
+
+  // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..3. Wave w
+  //    owns tokens [64w, 64w+64) of the sub-tile, i.e. the contiguous pairs
+  //    [64wk, 64(w+1)k), and walks them 64 at a time in order. Lanes holding
+  //    the same expert find each other with one ballot per id bit; the lowest
+  //    of them adds the group's size to the wave's running count for that
+  //    expert with an LDS atomic that returns the old count. A wave's atomics
+  //    complete in issue order, so the counts are exact without waiting
+  //    between chunks.
+  const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);
   bool bad_id = false;
-
-  for (int c = tid; c < g.ncols; c += kBlock) s_base[c] = 0;
-
-  const int tile_t0 = tile * g.tile_tokens;
-  const int tile_t1 = min(g.T, tile_t0 + g.tile_tokens);
-  for (int t0 = tile_t0; t0 < tile_t1; t0 += kSubTile) {
-    const int nt = min(kSubTile, tile_t1 - t0);
-    const int npairs = nt * g.k;
-    __syncthreads();  // previous sub-tile done with s_pack / s_cnt
-    for (int p = tid; p < kSubTile * g.k; p += kBlock)
-      s_pack[p] = p < npairs ? ids[(int64_t)t0 * g.k + p] : -1;
-    for (int c = tid; c < kWavesPerBlock * g.ncols; c += kBlock) s_cnt[c] = 0;
-    __syncthreads();
-
-    // Expert ranks. Wave w owns tokens [64w, 64w+64) of the sub-tile, i.e. the
-    // contiguous pairs [64wk, 64(w+1)k); it walks them 64 at a time in order.
-    // Lanes holding the same expert find each other with one ballot per id
-    // bit; the rank is the number of such lanes below plus the wave's running
-    // count for that expert.
-    int32_t* cnt_w = s_cnt + wave * g.ncols;
-    for (int ch = 0; ch < g.k; ++ch) {
-      const int pl = wave * kWave * g.k + ch * kWave + lane;
-      const int e = s_pack[pl];
-      const bool valid = e >= 0 && e < g.E;
-      bad_id |= (e != -1) && !valid;
-      uint64_t peers = __ballot(valid);
-      for (int b = 0; b < ebits; ++b) {
-        const uint64_t ones = __ballot(valid && ((e >> b) & 1));
-        peers &= ((e >> b) & 1) ? ones : ~ones;
-      }
-      if (valid) {
-        const int below = __popcll(peers & lanes_below());
-        const int base = cnt_w[e];
-        s_pack[pl] = ((base + below) << kExpertBits) | e;
-        if (below == 0) cnt_w[e] = base + __popcll(peers);
-      } else {
-        s_pack[pl] = -1;
+  const bool ranker = wave < kOwnWaves;
+  int32_t* cnt_w = s_cnt + (ranker ? wave : 0) * g.ncols;
+  for (int t0 = tile_lo; t0 < tile_hi; t0 += kOwnTokens) {
+    const int nt = min(kOwnTokens, tile_hi - t0);
+    const int npairs = nt * k;
+    __syncthreads();  // s_pack and s_cnt free; s_pre final
+    if (!one_sub) {
+      for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads) {
+        const int64_t gf = (int64_t)t0 * k + f;
+        s_pack[f] = f < npairs ? ids[gf] : -1;
       }
     }
+    for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
     __syncthreads();
 
-    // Rank masks: one token per thread.
-    const int tl = tid;
-    uint64_t mask = 0;
-    for (int j = 0; j < g.k; ++j) {
-      const int v = s_pack[tl * g.k + j];
-      if (v >= 0) mask |= uint64_t(1) << ((v & ((1 << kExpertBits) - 1)) / g.m);
-    }
-    for (int r = 0; r < g.R; ++r) {
-      const uint64_t on = __ballot((mask >> r) & 1);
-      if (lane == 0) cnt_w[g.E + r] = __popcll(on);
+    int ex[KR], rk[KR];  // per chunk: this lane's expert (or -1) and its rank in the wave
+    uint64_t mask = 0;   // rank set of token tid of the sub-tile
+    if (ranker) {
+      int lead[KR], cnt_old[KR];
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch) {
+        if (ch < k) {
+          const int pl = wave * kWave * k + ch * kWave + lane;
+          const int e = s_pack[pl];
+          const bool valid = e >= 0 && e < g.E;
+          bad_id |= (e != -1) && !valid;
+          uint64_t peers = __ballot(valid);
+          for (int b = 0; b < ebits; ++b) {
+            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+            peers &= ((e >> b) & 1) ? ones : ~ones;
+          }
+          ex[ch] = valid ? e : -1;
+          rk[ch] = __popcll(peers & lanes_below());
+          lead[ch] = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+          cnt_old[ch] = 0;
+          if (valid && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[e], __popcll(peers));
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch)
+        if (ch < k) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
+      if (tid < nt) {
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+          if (j < k) {
+            const int e = s_pack[tid * k + j];
+            if (e >= 0 && e < g.E) mask |= uint64_t(1) << rank_of(e, g.rank_magic);
+          }
+        }
+      }
+      for (int r = 0; r < g.R; ++r) {
+        const uint64_t on = __ballot((mask >> r) & 1);
+        if (lane == 0) cnt_w[g.E + r] = __popcll(on);
+      }
     }
     __syncthreads();
 
-    // Per column: wave bases inside this sub-tile, on top of the tile's
-    // running total; then advance the running total.
-    for (int c = tid; c < g.ncols; c += kBlock) {
-      int run = s_base[c];
-      for (int w = 0; w < kWavesPerBlock; ++w) {
+    // Per column: each ranking wave's first row, then advance the running base.
+    for (int c = tid; c < g.ncols; c += kLayoutThreads) {
+      int run = s_pre[c];
+#pragma unroll
+      for (int w = 0; w < kOwnWaves; ++w) {
         const int v = s_cnt[w * g.ncols + c];
         s_cnt[w * g.ncols + c] = run;
         run += v;
       }
-      s_base[c] = run;
+      s_pre[c] = run;
     }
     __syncthreads();
 
-    // Write tile-relative positions.
-    for (int ch = 0; ch < g.k; ++ch) {
-      const int pl = wave * kWave * g.k + ch * kWave + lane;
-      if (pl < npairs) {
-        const int v = s_pack[pl];
-        int out = -1;
-        if (v >= 0) out = cnt_w[v & ((1 << kExpertBits) - 1)] + (v >> kExpertBits);
-        pair_row[(int64_t)t0 * g.k + pl] = out;
+    if (ranker) {
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch) {
+        if (ch < k) {
+          const int pl = wave * kWave * k + ch * kWave + lane;
+          if (pl < npairs) pair_row[(int64_t)t0 * k + pl] = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
+        }
       }
-    }
-    for (int r = 0; r < g.R; ++r) {
-      const uint64_t on = __ballot((mask >> r) & 1);
-      if (tl < nt) {
-        const int out = ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
-        token_rank_slot[(int64_t)(t0 + tl) * g.R + r] = out;
+      for (int r = 0; r < g.R; ++r) {
+        const uint64_t on = __ballot((mask >> r) & 1);
+        if (tid < nt)
+          token_rank_slot[(int64_t)(t0 + tid) * g.R + r] =
+              ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
       }
     }
   }
-  __syncthreads();
-  for (int c = tid; c < g.ncols; c += kBlock) tile_counts[(int64_t)tile * g.ncols + c] = s_base[c];
   if (__ballot(bad_id) && lane == 0) flag_error(err_word, MOE_ERRBIT_BAD_ID);
 }
 
-// Exclusive scan of s[0..n) in place, by one workgroup; returns the total.
-__device__ int block_exclusive_scan(int32_t* s, int n, int32_t* s_tmp /* [kWavesPerBlock] */) {
-  const int tid = threadIdx.x;
-  const int per = (n + kBlock - 1) / kBlock;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += s[i];
-  // inclusive scan of per-thread sums across the wave
-  int x = sum;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane_id() >= d) x += y;
-  }
-  const int wave = tid / kWave;
-  if (lane_id() == kWave - 1) s_tmp[wave] = x;
-  __syncthreads();
-  int wave_base = 0, total = 0;
-  for (int w = 0; w < kWavesPerBlock; ++w) {
-    if (w < wave) wave_base += s_tmp[w];
-    total += s_tmp[w];
-  }
-  int run = wave_base + x - sum;
-  for (int i = lo; i < hi; ++i) {
-    const int v = s[i];
-    s[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
-}
-
-// Absolute rows: tile prefix (sum of the earlier tiles' counts) plus the
-// column's exclusive offset (experts scanned in id order, ranks in rank order).
-__global__ __launch_bounds__(kBlock) void layout_finalize(
-    LayoutGeom g, const int32_t* __restrict__ ids, const int32_t* __restrict__ tile_counts,
-    int32_t* __restrict__ pair_row, int32_t* __restrict__ token_rank_slot,
-    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets) {
-  __shared__ int32_t s_tot[kMaxExperts + kMaxRanks];
-  __shared__ int32_t s_pre[kMaxExperts + kMaxRanks];
-  __shared__ int32_t s_tmp[kWavesPerBlock];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kSubTile;
-  const int my_tile = t0 / g.tile_tokens;
-
-  for (int c = tid; c < g.ncols; c += kBlock) {
-    int tot = 0, pre = 0;
-    for (int i = 0; i < g.ntiles; ++i) {
-      const int v = tile_counts[(int64_t)i * g.ncols + c];
-      tot += v;
-      pre += (i < my_tile) ? v : 0;
-    }
-    s_tot[c] = tot;
-    s_pre[c] = pre;
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int c = tid; c < g.E; c += kBlock) expert_counts[c] = s_tot[c];
-    for (int c = tid; c < g.R; c += kBlock) rank_counts[c] = s_tot[g.E + c];
-  }
-  __syncthreads();
-  const int nexp = block_exclusive_scan(s_tot, g.E, s_tmp);
-  const int ncopy = block_exclusive_scan(s_tot + g.E, g.R, s_tmp);
-  if (blockIdx.x == 0) {
-    for (int c = tid; c < g.E; c += kBlock) expert_offsets[c] = s_tot[c];
-    for (int c = tid; c < g.R; c += kBlock) rank_offsets[c] = s_tot[g.E + c];
-    if (tid == 0) {
-      expert_offsets[g.E] = nexp;
-      rank_offsets[g.R] = ncopy;
-    }
-  }
-  for (int c = tid; c < g.ncols; c += kBlock) s_pre[c] += s_tot[c];
-  __syncthreads();
-
-  const int nt = min(kSubTile, g.T - t0);
-  if (nt <= 0) return;
-  const int64_t p0 = (int64_t)t0 * g.k;
-  for (int p = tid; p < nt * g.k; p += kBlock) {
-    const int v = pair_row[p0 + p];
-    if (v >= 0) pair_row[p0 + p] = v + s_pre[ids[p0 + p]];
-  }
-  const int64_t s0 = (int64_t)t0 * g.R;
-  for (int s = tid; s < nt * g.R; s += kBlock) {
-    const int v = token_rank_slot[s0 + s];
-    if (v >= 0) token_rank_slot[s0 + s] = v + s_pre[g.E + s % g.R];
-  }
+size_t layout_lds_bytes(int batch_tokens, int k, int ncols) {
+  // the staged ids get 4 ints of slack: a batch's last 16-byte load may run past its ids
+  return sizeof(int32_t) * (size_t(batch_tokens) * k + 4 + size_t(kOwnTokens) * k +
+                            size_t(kOwnWaves + 2) * ncols);
 }
 
 LayoutGeom layout_geometry(const moe_shape_t& sh) {
@@ -273,59 +379,90 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   g.k = sh.k;
   g.m = sh.E / sh.R;
   g.ncols = sh.E + sh.R;
-  const int64_t per_tile = (int64_t(sh.T) + kMaxTiles - 1) / kMaxTiles;
-  const int64_t subs = (per_tile + kSubTile - 1) / kSubTile;
-  g.tile_tokens = int(std::max<int64_t>(1, subs) * kSubTile);
-  g.ntiles = int((int64_t(sh.T) + g.tile_tokens - 1) / g.tile_tokens);
+  g.rank_magic = ((uint64_t(1) << 32) + uint64_t(g.m) - 1) / uint64_t(g.m);
+  // Largest batch (multiple of 1024 tokens) that the loads and LDS hold.
+  const int t_round = std::max(1, (sh.T + kLayoutThreads - 1) / kLayoutThreads) * kLayoutThreads;
+  g.batch_tokens = std::min(t_round, kLayoutThreads * std::max(1, (4 * kBatchVecs) / sh.k));
+  while (g.batch_tokens > kLayoutThreads &&
+         layout_lds_bytes(g.batch_tokens, g.k, g.ncols) > kLayoutLdsLimit)
+    g.batch_tokens -= kLayoutThreads;
+  const int64_t subs = (int64_t(sh.T) + kOwnTokens - 1) / kOwnTokens;
+  const int64_t per_tile = std::max<int64_t>(1, (subs + kMaxTiles - 1) / kMaxTiles);
+  g.tile_tokens = int(per_tile * kOwnTokens);
+  g.ntiles = int(std::max<int64_t>(1, (int64_t(sh.T) + g.tile_tokens - 1) / g.tile_tokens));
   return g;
 }
 
-size_t layout_smem_bytes(const LayoutGeom& g) {
-  return sizeof(int32_t) * (size_t(kSubTile) * g.k + size_t(kWavesPerBlock) * g.ncols + g.ncols);
+template <int K>
+void launch_layout_k(const LayoutGeom& g, size_t lds, hipStream_t st, const int32_t* ids,
+                     int32_t* rc, int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs,
+                     int32_t* pr, int32_t* err) {
+  // Allow this instantiation the LDS it may need (above the 64 KiB default);
+  // set once per process, the only thing the library ever caches.
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&layout_tiles<K>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
+  (void)attr;
+  hipLaunchKernelGGL((layout_tiles<K>), dim3(g.ntiles), dim3(kLayoutThreads), lds, st, g, ids,
+                     rc, ro, ec, eo, trs, pr, err);
+}
+
+void launch_layout(const LayoutGeom& g, hipStream_t st, const int32_t* ids, int32_t* rc,
+                   int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs, int32_t* pr,
+                   int32_t* err) {
+  const size_t lds = layout_lds_bytes(g.batch_tokens, g.k, g.ncols);
+  switch (g.k) {
+    case 1: launch_layout_k<1>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 2: launch_layout_k<2>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 4: launch_layout_k<4>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 6: launch_layout_k<6>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 8: launch_layout_k<8>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    default: launch_layout_k<0>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Row movers. A row is `nvec` uint4 (8 bf16 each). A wave moves a row in
-// passes of 64*V uint4: lane l holds columns c0 + l, c0 + 64 + l, ..., so each
-// wave instruction touches 1 KiB of contiguous bytes, and all V loads of a
-// pass are in flight before the first store. Columns past the last full pass
-// (only when H is not a multiple of 512*V) go one uint4 per lane at a time.
+// Row movers. A row is `nvec` vec4 (8 bf16 each). A wave moves a row in passes
+// of 64*V vec4: lane l holds columns c0 + l, c0 + 64 + l, ..., so each wave
+// instruction touches 1 KiB of contiguous bytes, and all V loads of a pass are
+// in flight before the first store. Columns past the last full pass (H not a
+// multiple of 512*V) go one vec4 per lane at a time.
 
-// Copies the row at `src` to every row dst_row(d) for d in the lane mask
-// `dests`, where dst_row(d) = readlane(row_of_lane, d).
+// Copies the row at `src` to every row dst_row(d), d in the lane mask `dests`,
+// dst_row(d) = readlane(row_of_lane, d).
 template <int V>
-__device__ __forceinline__ void fan_out_row(const uint4* src, uint4* dst_base,
-                                            int row_of_lane, uint64_t dests, int nvec) {
+__device__ __forceinline__ void fan_out_row(const vec4* src, vec4* dst_base, int row_of_lane,
+                                            uint64_t dests, int nvec) {
   const int lane = lane_id();
   int c0 = 0;
   for (; c0 + kWave * V <= nvec; c0 += kWave * V) {
-    uint4 v[V];
+    vec4 v[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) v[q] = src[c0 + q * kWave + lane];
     uint64_t d = dests;
     while (d) {
       const int which = __ffsll((unsigned long long)d) - 1;
       d &= d - 1;
-      uint4* dst = dst_base + (int64_t)read_lane(row_of_lane, which) * nvec;
+      vec4* dst = dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + c0 + lane;
 #pragma unroll
-      for (int q = 0; q < V; ++q) dst[c0 + q * kWave + lane] = v[q];
+      for (int q = 0; q < V; ++q) store_stream(dst + q * kWave, v[q]);
     }
   }
   for (int c = c0 + lane; c < nvec; c += kWave) {
-    const uint4 v = src[c];
+    const vec4 v = src[c];
     uint64_t d = dests;
     while (d) {
       const int which = __ffsll((unsigned long long)d) - 1;
       d &= d - 1;
-      dst_base[(int64_t)read_lane(row_of_lane, which) * nvec + c] = v;
+      store_stream(dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + c, v);
     }
   }
 }
 
 template <int V>
-__global__ __launch_bounds__(kBlock) void pack_rows(const uint4* hidden,
+__global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
                                                     const int32_t* __restrict__ token_rank_slot,
-                                                    uint4* rank_buf,
+                                                    vec4* rank_buf,
                                                     int32_t* __restrict__ rank_src_token, int T,
                                                     int R, int nvec, int64_t cap_rank,
                                                     int32_t* err_word) {
@@ -342,9 +479,9 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const uint4* hidden,
 
 template <int V>
 __global__ __launch_bounds__(kBlock) void permute_rows(
-    const uint4* rank_buf, const int32_t* __restrict__ rank_src_token,
+    const vec4* rank_buf, const int32_t* __restrict__ rank_src_token,
     const int32_t* __restrict__ rank_offsets, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ pair_row, uint4* expert_buf,
+    const int32_t* __restrict__ pair_row, vec4* expert_buf,
     int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int nvec,
     int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
   const int lane = lane_id();
@@ -372,67 +509,93 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ void fma_bf16x8(float (&acc)[8], float w, const uint4& y) {
-  const uint32_t h[4] = {y.x, y.y, y.z, y.w};
+__device__ __forceinline__ void fma_bf16x8(float (&acc)[8], float w, vec4 y) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    acc[2 * i] = __builtin_fmaf(w, __uint_as_float(h[i] << 16), acc[2 * i]);
-    acc[2 * i + 1] = __builtin_fmaf(w, __uint_as_float(h[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    acc[2 * i] = __builtin_fmaf(w, __uint_as_float(y[i] << 16), acc[2 * i]);
+    acc[2 * i + 1] = __builtin_fmaf(w, __uint_as_float(y[i] & 0xFFFF0000u), acc[2 * i + 1]);
   }
 }
 
-__device__ __forceinline__ void store_sum(const float (&acc)[8], uint4* __restrict__ out,
-                                          float4* __restrict__ out_f32, int64_t at) {
-  uint4 o;
-  o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-  o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-  o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-  o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-  out[at] = o;
+__device__ __forceinline__ void store_sum(const float (&acc)[8], vec4* out, vec4* out_f32,
+                                          int64_t at) {
+  vec4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  store_stream(out + at, o);
   if (out_f32) {
-    out_f32[2 * at] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    out_f32[2 * at + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    vec4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __float_as_uint(acc[i]);
+      b[i] = __float_as_uint(acc[4 + i]);
+    }
+    store_stream(out_f32 + 2 * at, a);
+    store_stream(out_f32 + 2 * at + 1, b);
   }
 }
 
+// One wave per (token, column slice of 64*V vec4). Slots are walked in
+// ascending order; the next slot's row is loaded while the current one is
+// accumulated.
 template <int V>
 __global__ __launch_bounds__(kBlock) void combine_rows(
-    const uint4* expert_out, const int32_t* __restrict__ pair_row,
-    const float* __restrict__ weights, uint4* __restrict__ out, float4* __restrict__ out_f32,
-    int T, int k, int nvec, int64_t cap_expert, int32_t* err_word) {
+    const vec4* expert_out, const int32_t* __restrict__ pair_row,
+    const float* __restrict__ weights, vec4* out, vec4* out_f32, int T, int k, int nvec,
+    int slices, int64_t cap_expert, int32_t* err_word) {
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = int(gw / slices);
+  const int slice = int(gw - (int64_t)t * slices);
   if (t >= T) return;
   const int p = lane < k ? pair_row[(int64_t)t * k + lane] : -1;
   const float wt = lane < k ? weights[(int64_t)t * k + lane] : 0.0f;
   const bool ok = p >= 0 && p < cap_expert;
-  if (__ballot(p >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+  if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
+    flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
   const uint64_t slots = __ballot(ok);
-  const int64_t row0 = (int64_t)t * nvec;
+  const int cb = slice * kWave * V;
+  const int64_t orow = (int64_t)t * nvec;
 
-  int c0 = 0;
-  for (; c0 + kWave * V <= nvec; c0 += kWave * V) {
+  if (cb + kWave * V <= nvec) {
     float acc[V][8];
 #pragma unroll
     for (int q = 0; q < V; ++q)
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc[q][x] = 0.0f;
     uint64_t s = slots;
-    while (s) {  // ascending slot order
-      const int j = __ffsll((unsigned long long)s) - 1;
+    if (s) {
+      int j = __ffsll((unsigned long long)s) - 1;
       s &= s - 1;
-      const uint4* src = expert_out + (int64_t)read_lane(p, j) * nvec + c0 + lane;
-      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
-      uint4 y[V];
+      vec4 y[V];
+      const vec4* src = expert_out + (int64_t)read_lane(p, j) * nvec + cb + lane;
 #pragma unroll
       for (int q = 0; q < V; ++q) y[q] = src[q * kWave];
+      while (s) {
+        const int jn = __ffsll((unsigned long long)s) - 1;
+        s &= s - 1;
+        vec4 yn[V];
+        const vec4* srcn = expert_out + (int64_t)read_lane(p, jn) * nvec + cb + lane;
+#pragma unroll
+        for (int q = 0; q < V; ++q) yn[q] = srcn[q * kWave];
+        const float w = __int_as_float(read_lane(__float_as_int(wt), j));
+#pragma unroll
+        for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
+#pragma unroll
+        for (int q = 0; q < V; ++q) y[q] = yn[q];
+        j = jn;
+      }
+      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
 #pragma unroll
       for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
     }
 #pragma unroll
-    for (int q = 0; q < V; ++q) store_sum(acc[q], out, out_f32, row0 + c0 + q * kWave + lane);
+    for (int q = 0; q < V; ++q) store_sum(acc[q], out, out_f32, orow + cb + q * kWave + lane);
+    return;
   }
-  for (int c = c0 + lane; c < nvec; c += kWave) {
+  // Partial slice at the end of the row: one vec4 per lane at a time.
+  for (int c = cb + lane; c < nvec; c += kWave) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     uint64_t s = slots;
     while (s) {
@@ -441,7 +604,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows(
       const float w = __int_as_float(read_lane(__float_as_int(wt), j));
       fma_bf16x8(acc, w, expert_out[(int64_t)read_lane(p, j) * nvec + c]);
     }
-    store_sum(acc, out, out_f32, row0 + c);
+    store_sum(acc, out, out_f32, orow + c);
   }
 }
 
@@ -456,6 +619,7 @@ bool shape_ok(const moe_shape_t* s) {
   if (s->k < 1 || s->k > kMaxK) return false;
   if (int64_t(s->T) * s->k >= (int64_t(1) << 30)) return false;
   if (int64_t(s->T) * s->R >= (int64_t(1) << 31)) return false;
+  if (layout_lds_bytes(kLayoutThreads, s->k, s->E + s->R) > kLayoutLdsLimit) return false;
   return true;
 }
 
@@ -463,10 +627,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Register tile V (uint4 per lane per pass): the whole row in one pass when
-// it has at most 16 groups of 64 uint4, else a divisor of the group count in
-// [8, 16] if there is one (no tail), else 16.
-int vec_per_lane(int nvec) {
+// Register tile V of pack and permute (vec4 per lane per pass): the whole row
+// in one pass when it has at most 16 groups of 64 vec4, else a divisor of the
+// group count in [8, 16] if there is one (no tail), else 16.
+int copy_vec(int nvec) {
   const int groups = nvec / kWave;
   if (groups <= 1) return 1;
   if (groups <= kMaxVec) return groups;
@@ -475,10 +639,16 @@ int vec_per_lane(int nvec) {
   return kMaxVec;
 }
 
+// Combine: slices of at most 8 groups (8 x 8 fp32 accumulators per lane),
+// as few slices as cover the row.
+void combine_tiling(int nvec, int* v, int* slices) {
+  const int groups = std::max(1, (nvec + kWave - 1) / kWave);
+  *slices = (groups + 7) / 8;
+  *v = (groups + *slices - 1) / *slices;
+}
+
 int blocks_for(int64_t waves) { return int((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
 
-// Picks the instantiation whose per-lane register tile V covers the row in
-// as few passes as possible.
 template <template <int> class K>
 struct ByVec {
   template <typename... Args>
@@ -499,7 +669,7 @@ struct ByVec {
 
 template <int V>
 struct PackLaunch {
-  static void go(dim3 grid, hipStream_t st, const uint4* hid, const int32_t* slots, uint4* rb,
+  static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots, vec4* rb,
                  int32_t* src, int T, int R, int nvec, int64_t cap, int32_t* err) {
     hipLaunchKernelGGL(pack_rows<V>, grid, dim3(kBlock), 0, st, hid, slots, rb, src, T, R, nvec,
                        cap, err);
@@ -508,8 +678,8 @@ struct PackLaunch {
 
 template <int V>
 struct PermuteLaunch {
-  static void go(dim3 grid, hipStream_t st, const uint4* rb, const int32_t* src,
-                 const int32_t* roff, const int32_t* ids, const int32_t* prow, uint4* eb,
+  static void go(dim3 grid, hipStream_t st, const vec4* rb, const int32_t* src,
+                 const int32_t* roff, const int32_t* ids, const int32_t* prow, vec4* eb,
                  int32_t* esrc, int T, int E, int R, int k, int m, int nvec, int64_t cap_rank,
                  int64_t cap_expert, int32_t* err) {
     hipLaunchKernelGGL(permute_rows<V>, grid, dim3(kBlock), 0, st, rb, src, roff, ids, prow, eb,
@@ -519,11 +689,11 @@ struct PermuteLaunch {
 
 template <int V>
 struct CombineLaunch {
-  static void go(dim3 grid, hipStream_t st, const uint4* eo, const int32_t* prow,
-                 const float* w, uint4* out, float4* out32, int T, int k, int nvec,
-                 int64_t cap_expert, int32_t* err) {
+  static void go(dim3 grid, hipStream_t st, const vec4* eo, const int32_t* prow, const float* w,
+                 vec4* out, vec4* out32, int T, int k, int nvec, int slices, int64_t cap_expert,
+                 int32_t* err) {
     hipLaunchKernelGGL(combine_rows<V>, grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T, k,
-                       nvec, cap_expert, err);
+                       nvec, slices, cap_expert, err);
   }
 };
 
@@ -538,38 +708,21 @@ const char* moe_status_string(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_ARG: return "invalid argument";
     case MOE_ERR_HIP: return "HIP launch failure";
-    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
   }
 }
 
-size_t moe_layout_workspace_bytes(const moe_shape_t* shape) {
-  if (!shape_ok(shape)) return 0;
-  const LayoutGeom g = layout_geometry(*shape);
-  return sizeof(int32_t) * size_t(std::max(g.ntiles, 1)) * size_t(g.ncols);
-}
-
 int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* expert_counts, int32_t* expert_offsets,
-                        int32_t* token_rank_slot, int32_t* pair_row, void* workspace,
-                        size_t workspace_bytes, int32_t* err_word, void* stream) {
+                        int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
+                        void* stream) {
   if (!shape_ok(shape)) return MOE_ERR_ARG;
   if (!rank_counts || !rank_offsets || !expert_counts || !expert_offsets) return MOE_ERR_ARG;
   if (shape->T > 0 && (!topk_ids || !token_rank_slot || !pair_row)) return MOE_ERR_ARG;
-  const size_t need = moe_layout_workspace_bytes(shape);
-  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (shape->T > 0 && !aligned16(topk_ids)) return MOE_ERR_ARG;
   const LayoutGeom g = layout_geometry(*shape);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* tile_counts = static_cast<int32_t*>(workspace);
-  if (g.ntiles > 0) {
-    hipLaunchKernelGGL(layout_tiles, dim3(g.ntiles), dim3(kBlock), layout_smem_bytes(g), st, g,
-                       topk_ids, pair_row, token_rank_slot, tile_counts, err_word);
-    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
-  }
-  const int fin_blocks = std::max(1, (g.T + kSubTile - 1) / kSubTile);
-  hipLaunchKernelGGL(layout_finalize, dim3(fin_blocks), dim3(kBlock), 0, st, g, topk_ids,
-                     tile_counts, pair_row, token_rank_slot, rank_counts, rank_offsets,
-                     expert_counts, expert_offsets);
+  launch_layout(g, static_cast<hipStream_t>(stream), topk_ids, rank_counts, rank_offsets,
+                expert_counts, expert_offsets, token_rank_slot, pair_row, err_word);
   return launch_status();
 }
 
@@ -582,11 +735,10 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
     return MOE_ERR_ARG;
   if (!aligned16(hidden) || !aligned16(rank_buf)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
-  ByVec<PackLaunch>::run(vec_per_lane(nvec), dim3(blocks_for(shape->T)),
-                         static_cast<hipStream_t>(stream),
-                         reinterpret_cast<const uint4*>(hidden), token_rank_slot,
-                         reinterpret_cast<uint4*>(rank_buf), rank_src_token, shape->T, shape->R,
-                         nvec, cap_rank, err_word);
+  ByVec<PackLaunch>::run(copy_vec(nvec), dim3(blocks_for(shape->T)),
+                         static_cast<hipStream_t>(stream), reinterpret_cast<const vec4*>(hidden),
+                         token_rank_slot, reinterpret_cast<vec4*>(rank_buf), rank_src_token,
+                         shape->T, shape->R, nvec, cap_rank, err_word);
   return launch_status();
 }
 
@@ -605,13 +757,12 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
     return MOE_ERR_ARG;
   if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
-  ByVec<PermuteLaunch>::run(vec_per_lane(nvec), dim3(blocks_for(max_rows)),
+  ByVec<PermuteLaunch>::run(copy_vec(nvec), dim3(blocks_for(max_rows)),
                             static_cast<hipStream_t>(stream),
-                            reinterpret_cast<const uint4*>(rank_buf), rank_src_token,
-                            rank_offsets, topk_ids, pair_row,
-                            reinterpret_cast<uint4*>(expert_buf), expert_src_pair, shape->T,
-                            shape->E, shape->R, shape->k, shape->E / shape->R, nvec, cap_rank,
-                            cap_expert, err_word);
+                            reinterpret_cast<const vec4*>(rank_buf), rank_src_token, rank_offsets,
+                            topk_ids, pair_row, reinterpret_cast<vec4*>(expert_buf),
+                            expert_src_pair, shape->T, shape->E, shape->R, shape->k,
+                            shape->E / shape->R, nvec, cap_rank, cap_expert, err_word);
   return launch_status();
 }
 
@@ -623,11 +774,13 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   if (!pair_row || !topk_weights || !out || (cap_expert > 0 && !expert_out)) return MOE_ERR_ARG;
   if (!aligned16(expert_out) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
-  ByVec<CombineLaunch>::run(vec_per_lane(nvec), dim3(blocks_for(shape->T)),
+  int v = 1, slices = 1;
+  combine_tiling(nvec, &v, &slices);
+  ByVec<CombineLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
-                            reinterpret_cast<const uint4*>(expert_out), pair_row, topk_weights,
-                            reinterpret_cast<uint4*>(out), reinterpret_cast<float4*>(out_f32),
-                            shape->T, shape->k, nvec, cap_expert, err_word);
+                            reinterpret_cast<const vec4*>(expert_out), pair_row, topk_weights,
+                            reinterpret_cast<vec4*>(out), reinterpret_cast<vec4*>(out_f32),
+                            shape->T, shape->k, nvec, slices, cap_expert, err_word);
   return launch_status();
 }
 

@@ -14,20 +14,20 @@
  *  - Every pointer argument except `shape` is a DEVICE pointer (hipMalloc'd or
  *    a torch CUDA tensor). The caller owns every buffer; the library allocates
  *    nothing, keeps no state between calls and is re-entrant for calls that
- *    do not share output buffers or a workspace.
+ *    do not share output buffers.
  *  - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL = the null stream), never synchronise with the host and launch a
  *    fixed number of kernels whose grids depend only on the shape and caps, so
  *    they can be recorded in a HIP graph ([A2A] sec 1.4: fixed shapes, no CPU
  *    wait for counts; sec 4.2 and 6.2: counts stay on the GPU).
  *  - Return value: MOE_OK, or a negative moe_status_t for errors the host can
- *    see (bad shape, NULL or misaligned pointer, workspace too small, launch
- *    failure). On an argument error no kernel is launched.
+ *    see (bad shape, NULL or misaligned pointer, launch failure). On an
+ *    argument error no kernel is launched.
  *  - Data-dependent errors are OR-ed by the kernels into `*err_word` (a device
  *    int32 the caller zeroes and reads when it chooses; may be NULL to ignore):
- *    MOE_ERRBIT_BAD_ID, MOE_ERRBIT_RANK_CAP, MOE_ERRBIT_EXPERT_CAP,
- *    MOE_ERRBIT_LAYOUT_TIMEOUT. Offending rows are dropped, never written out
- *    of bounds ([A2A] sec 4.3: a batch larger than the cap fails).
+ *    MOE_ERRBIT_BAD_ID, MOE_ERRBIT_RANK_CAP, MOE_ERRBIT_EXPERT_CAP. Offending
+ *    rows are dropped, never written out of bounds ([A2A] sec 4.3: a batch
+ *    larger than the cap fails).
  *  - Types: expert ids int32; weights float32; hidden states and expert
  *    outputs bf16 (passed as uint16_t bit patterns), row-major, row stride H.
  *  - Ids: -1 means "no expert in this slot" and is skipped ([A2A] sec 2.1,
@@ -42,8 +42,8 @@
  *    for the worst case, cap_rank = T*min(k,R) rows and cap_expert = T*k rows,
  *    can never overflow ([A2A] sec 5.1: worst-case output plus an offsets list).
  *  - Limits: 0 <= T, T*k < 2^30, T*R < 2^31; 1 <= R <= 64; E % R == 0;
- *    1 <= E <= 1024; 1 <= k <= 32; H > 0 and H % 8 == 0; row buffers 16-byte
- *    aligned.
+ *    1 <= E <= 1024; 1 <= k <= 16; H > 0 and H % 8 == 0; row buffers and
+ *    topk_ids 16-byte aligned.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
@@ -68,26 +68,18 @@ typedef struct moe_shape {
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_ARG = -1,       /* bad shape, NULL or misaligned pointer */
-  MOE_ERR_HIP = -2,       /* a kernel launch failed (hipGetLastError) */
-  MOE_ERR_WORKSPACE = -3  /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -2        /* a kernel launch failed (hipGetLastError) */
 } moe_status_t;
 
 #define MOE_ERRBIT_BAD_ID 1         /* an id outside [-1, E) was skipped */
 #define MOE_ERRBIT_RANK_CAP 2       /* a copy at or past cap_rank was dropped */
 #define MOE_ERRBIT_EXPERT_CAP 4     /* a pair row at or past cap_expert was dropped or ignored */
-#define MOE_ERRBIT_LAYOUT_TIMEOUT 8 /* the layout scan gave up waiting for a tile (never expected) */
 
 /* ABI version of the loaded library (MOE_DISPATCH_ABI_VERSION at build time). */
 int moe_abi_version(void);
 
 /* Static text for a moe_status_t value. */
 const char* moe_status_string(int status);
-
-/* Bytes of device workspace moe_dispatch_layout needs for this shape (0 on a
- * bad shape). The workspace must be zero-filled before its first use; every
- * call that returns MOE_OK leaves it zero-filled again once its kernels have
- * run. Two layout calls in flight at once must not share a workspace. */
-size_t moe_layout_workspace_bytes(const moe_shape_t* shape);
 
 /*
  * Dispatch, step 1: layout ([A2A] sec 3.2 first step: per token, the set of
@@ -103,14 +95,14 @@ size_t moe_layout_workspace_bytes(const moe_shape_t* shape);
  *                                 rows of a segment ascend with t
  *   pair_row         [T*k]   out: row of pair (t, j) in the expert-grouped buffer, or -1;
  *                                 rows of an expert's run ascend with (t, j)
- *   workspace, workspace_bytes: device scratch, see moe_layout_workspace_bytes
- *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID, MOE_ERRBIT_LAYOUT_TIMEOUT)
- * The result is a pure function of topk_ids: no order depends on timing.
+ *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID)
+ * One kernel launch, no scratch memory beyond LDS. The result is a pure
+ * function of topk_ids: no order depends on timing.
  */
 int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* expert_counts, int32_t* expert_offsets,
-                        int32_t* token_rank_slot, int32_t* pair_row, void* workspace,
-                        size_t workspace_bytes, int32_t* err_word, void* stream);
+                        int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
+                        void* stream);
 
 /*
  * Dispatch, step 2: pack ([A2A] sec 1.3 third answer and sec 3.2: a token is

@@ -50,7 +50,6 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
             pair_row=torch.full((T, k), -9, dtype=i32, device=dev),
         )
         err = torch.zeros(1, dtype=i32, device=dev)
-        ws = torch.zeros(moe.workspace_bytes(shape), dtype=torch.uint8, device=dev)
         canary = torch.tensor(CANARY_ROW, dtype=torch.int32).to(torch.int16).item()
         rank_all = torch.full((cap_rank + spare_rows, H), canary, dtype=torch.int16, device=dev)
         rsrc_all = torch.full((cap_rank + spare_rows,), CANARY_IDX, dtype=i32, device=dev)
@@ -59,7 +58,7 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
         rank_buf, rank_src = rank_all[:cap_rank], rsrc_all[:cap_rank]
         expert_buf, expert_src = exp_all[:cap_expert], esrc_all[:cap_expert]
 
-        moe.layout(ids_d, E, R, H, workspace=ws, err=err, out=lay)
+        moe.layout(ids_d, E, R, H, err=err, out=lay)
         moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
         moe.permute(rank_buf, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"], E,
                     expert_buf, expert_src, err=err)

@@ -29,27 +29,27 @@ def test_library_exports_every_declared_symbol():
     assert L.moe_abi_version() == 1
 
 
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
+
+
 def shape(T=64, H=512, E=16, R=4, k=2):
     return moe.MoeShape(T, H, E, R, k)
 
 
-@pytest.mark.parametrize("bad", [
+BAD_SHAPES = [
     dict(T=-1), dict(H=0), dict(H=12), dict(E=0), dict(R=0), dict(R=65, E=130), dict(E=10, R=4),
-    dict(k=0), dict(k=33, E=64), dict(E=2048, R=8), dict(T=1 << 28, k=8),
-])
-def test_workspace_query_rejects_bad_shapes(bad):
-    assert moe.lib().moe_layout_workspace_bytes(ctypes.byref(shape(**bad))) == 0
+    dict(k=0), dict(k=17, E=64), dict(E=2048, R=8), dict(T=1 << 28, k=8),
+]
 
 
-def test_workspace_query_sizes():
+@pytest.mark.parametrize("bad", BAD_SHAPES)
+def test_calls_reject_bad_shapes(bad):
     L = moe.lib()
-    n = L.moe_layout_workspace_bytes(ctypes.byref(shape(T=4096, E=384, R=8, k=6)))
-    assert n == 16 * (384 + 8) * 4  # 16 tiles of 256 tokens, one int per column
-    n0 = L.moe_layout_workspace_bytes(ctypes.byref(shape(T=0)))
-    assert n0 > 0
-
-
-FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
+    sp = ctypes.byref(shape(**bad))
+    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_pack(sp, FAKE, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
 
 
 def test_calls_reject_bad_arguments_without_launching():
@@ -57,15 +57,13 @@ def test_calls_reject_bad_arguments_without_launching():
     s = shape()
     sp = ctypes.byref(s)
     bad = ctypes.byref(shape(E=10))
-    # layout: bad shape, NULL outputs, missing/small workspace
-    assert L.moe_dispatch_layout(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
-                                 None, None) == moe.MOE_ERR_ARG
-    assert L.moe_dispatch_layout(sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
-                                 None, None) == moe.MOE_ERR_ARG
-    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 20,
-                                 None, None) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
-                                 None, None) == moe.MOE_ERR_WORKSPACE
+    # layout: bad shape, NULL inputs and outputs
+    assert L.moe_dispatch_layout(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_layout(sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_layout(sp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == moe.MOE_ERR_ARG
     # pack: NULL hidden, misaligned rows, negative cap
     assert L.moe_dispatch_pack(sp, None, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
     assert L.moe_dispatch_pack(sp, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, 128, None,
@@ -94,4 +92,4 @@ def test_empty_batches_are_no_ops():
 def test_status_strings():
     L = moe.lib()
     assert L.moe_status_string(0) == b"ok"
-    assert b"workspace" in L.moe_status_string(-3)
+    assert b"argument" in L.moe_status_string(-1)

@@ -73,7 +73,8 @@ EDGE = [
     (300, 16384, 32, 4, 4, 0.0, 0.0, 6),     # two register passes per row
     (16385, 64, 16, 4, 2, 0.0, 0.0, 7),      # two sub-tiles per layout tile
     (20000, 16, 256, 8, 8, 0.1, 0.0, 8),
-    (2000, 64, 1024, 64, 32, 0.02, 0.02, 9),  # largest E, R, k
+    (2000, 64, 1024, 64, 16, 0.02, 0.02, 9),  # largest E, R, k
+    (70000, 16, 64, 8, 5, 0.05, 0.0, 12),    # > 64 tiles: several sub-tiles per workgroup
     (700, 256, 96, 1, 5, 0.0, 0.0, 10),      # one rank
     (513, 2880, 384, 8, 6, 0.0, 0.0, 11),    # 360 uint4 per row: 5 full groups + tail
 ]
