@@ -21,8 +21,12 @@
 //                in slot order, bf16 round-to-nearest-even ([A2A] sec 1.1,
 //                7.1; [GPUs] sec 3.3 fixed addition order)
 // Rows move 16 bytes per lane (global_load/store_dwordx4), 1 KiB per wave
-// instruction; copies are stored non-temporally, since nothing re-reads them
-// inside the kernel. Nothing here is a dense contraction, so no MFMA.
+// instruction. Cache policy per stream, chosen by measurement of the whole
+// layout -> pack -> permute -> combine sequence: the packed rows are written
+// with ordinary stores, so the permute finds them in the 256 MB Infinity
+// Cache; every other row stream (hidden, packed rows on their second read,
+// expert rows, combine outputs) is non-temporal so it does not evict them.
+// Nothing here is a dense contraction, so no MFMA.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,8 +62,20 @@ __device__ __forceinline__ void flag_error(int32_t* err_word, int bit) {
   if (err_word) atomicOr(err_word, bit);
 }
 
-__device__ __forceinline__ void store_stream(vec4* p, vec4 v) {
-  __builtin_nontemporal_store(v, p);
+// Row loads and stores with a cache policy: non-temporal (streaming) or
+// ordinary (allocating in L2 and the Infinity Cache).
+template <bool kStream>
+__device__ __forceinline__ vec4 load_row(const vec4* p) {
+  if (kStream) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool kStream>
+__device__ __forceinline__ void store_row(vec4* p, vec4 v) {
+  if (kStream)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -199,6 +215,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   //    counted. Experts: one LDS atomic per pair. Ranks: one ballot per rank
   //    per 64 tokens (a wave's 64 tokens sit on one side of the tile start).
   const int batch_ids = g.batch_tokens * k;
+  int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
   vec4 nxt[kBatchVecs];
   load_batch(ids, n_ids, 0, (int)((std::min<int64_t>(batch_ids, n_ids) + 3) / 4), nxt);
   for (int b0 = 0; b0 < g.T; b0 += g.batch_tokens) {
@@ -223,26 +240,29 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
         s_pack[f] = f < n_own ? s_ids[base + f] : -1;
     }
     for (int tl = tid; tl < ((nb + kWave - 1) & ~(kWave - 1)); tl += kLayoutThreads) {
-      int32_t* cnt = b0 + (tl & ~(kWave - 1)) < tile_lo ? s_pre : s_tot;
-      uint64_t mask = 0;
-      if (tl < nb) {
-        const int32_t* my = s_ids + tl * k;
+      const bool early = b0 + (tl & ~(kWave - 1)) < tile_lo;  // the same for the whole wave
+      int32_t* cnt = early ? s_pre : s_tot;
+      int ev[KR];
 #pragma unroll
-        for (int j = 0; j < KR; ++j) {
-          if (j < k) {
-            const int e = my[j];
-            if (e >= 0 && e < g.E) {
-              atomicAdd(&cnt[e], 1);
-              mask |= uint64_t(1) << rank_of(e, g.rank_magic);
-            }
-          }
+      for (int j = 0; j < KR; ++j)
+        if (j < k) ev[j] = tl < nb ? s_ids[tl * k + j] : -1;
+      uint64_t mask = 0;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        if (j < k && ev[j] >= 0 && ev[j] < g.E) {
+          atomicAdd(&cnt[ev[j]], 1);
+          mask |= uint64_t(1) << rank_of(ev[j], g.rank_magic);
         }
       }
       for (int r = 0; r < g.R; ++r) {
-        const uint64_t on = __ballot((mask >> r) & 1);
-        if (lane == 0 && on) atomicAdd(&cnt[g.E + r], __popcll(on));
+        const int c = __popcll(__ballot((mask >> r) & 1));
+        if (lane == r) (early ? rc_pre : rc_tot) += c;
       }
     }
+  }
+  if (lane < g.R) {  // lane r holds this wave's copies on rank r
+    if (rc_pre) atomicAdd(&s_pre[g.E + lane], rc_pre);
+    if (rc_tot) atomicAdd(&s_tot[g.E + lane], rc_tot);
   }
   __syncthreads();
   for (int c = tid; c < g.ncols; c += kLayoutThreads) s_tot[c] += s_pre[c];
@@ -294,12 +314,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     int ex[KR], rk[KR];  // per chunk: this lane's expert (or -1) and its rank in the wave
     uint64_t mask = 0;   // rank set of token tid of the sub-tile
     if (ranker) {
-      int lead[KR], cnt_old[KR];
+      // All of the wave's ids first (one LDS wait), then the matches, then the
+      // running-count atomics in chunk order, then the leaders' old counts.
+      int own[KR];  // ids of token tid, for its rank set
 #pragma unroll
       for (int ch = 0; ch < KR; ++ch) {
         if (ch < k) {
-          const int pl = wave * kWave * k + ch * kWave + lane;
-          const int e = s_pack[pl];
+          ex[ch] = s_pack[wave * kWave * k + ch * kWave + lane];
+          own[ch] = tid < nt ? s_pack[tid * k + ch] : -1;
+        }
+      }
+      int lead[KR], grp[KR];
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch) {
+        if (ch < k) {
+          const int e = ex[ch];
           const bool valid = e >= 0 && e < g.E;
           bad_id |= (e != -1) && !valid;
           uint64_t peers = __ballot(valid);
@@ -310,26 +339,29 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
           ex[ch] = valid ? e : -1;
           rk[ch] = __popcll(peers & lanes_below());
           lead[ch] = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+          grp[ch] = __popcll(peers);
+        }
+      }
+      int cnt_old[KR];
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch) {
+        if (ch < k) {
           cnt_old[ch] = 0;
-          if (valid && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[e], __popcll(peers));
+          if (ex[ch] >= 0 && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[ex[ch]], grp[ch]);
         }
       }
 #pragma unroll
       for (int ch = 0; ch < KR; ++ch)
         if (ch < k) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
-      if (tid < nt) {
 #pragma unroll
-        for (int j = 0; j < KR; ++j) {
-          if (j < k) {
-            const int e = s_pack[tid * k + j];
-            if (e >= 0 && e < g.E) mask |= uint64_t(1) << rank_of(e, g.rank_magic);
-          }
-        }
-      }
+      for (int j = 0; j < KR; ++j)
+        if (j < k && own[j] >= 0 && own[j] < g.E) mask |= uint64_t(1) << rank_of(own[j], g.rank_magic);
+      int copies = 0;  // lane r: the wave's tokens with a copy on rank r
       for (int r = 0; r < g.R; ++r) {
-        const uint64_t on = __ballot((mask >> r) & 1);
-        if (lane == 0) cnt_w[g.E + r] = __popcll(on);
+        const int c = __popcll(__ballot((mask >> r) & 1));
+        if (lane == r) copies = c;
       }
+      if (lane < g.R) cnt_w[g.E + lane] = copies;
     }
     __syncthreads();
 
@@ -414,7 +446,9 @@ void launch_layout(const LayoutGeom& g, hipStream_t st, const int32_t* ids, int3
   switch (g.k) {
     case 1: launch_layout_k<1>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
     case 2: launch_layout_k<2>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 3: launch_layout_k<3>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
     case 4: launch_layout_k<4>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
+    case 5: launch_layout_k<5>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
     case 6: launch_layout_k<6>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
     case 8: launch_layout_k<8>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
     default: launch_layout_k<0>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
@@ -429,8 +463,9 @@ void launch_layout(const LayoutGeom& g, hipStream_t st, const int32_t* ids, int3
 // multiple of 512*V) go one vec4 per lane at a time.
 
 // Copies the row at `src` to every row dst_row(d), d in the lane mask `dests`,
-// dst_row(d) = readlane(row_of_lane, d).
-template <int V>
+// dst_row(d) = readlane(row_of_lane, d), loading and storing with the given
+// cache policies.
+template <int V, bool kStreamLoad, bool kStreamStore>
 __device__ __forceinline__ void fan_out_row(const vec4* src, vec4* dst_base, int row_of_lane,
                                             uint64_t dests, int nvec) {
   const int lane = lane_id();
@@ -438,23 +473,23 @@ __device__ __forceinline__ void fan_out_row(const vec4* src, vec4* dst_base, int
   for (; c0 + kWave * V <= nvec; c0 += kWave * V) {
     vec4 v[V];
 #pragma unroll
-    for (int q = 0; q < V; ++q) v[q] = src[c0 + q * kWave + lane];
+    for (int q = 0; q < V; ++q) v[q] = load_row<kStreamLoad>(src + c0 + q * kWave + lane);
     uint64_t d = dests;
     while (d) {
       const int which = __ffsll((unsigned long long)d) - 1;
       d &= d - 1;
       vec4* dst = dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + c0 + lane;
 #pragma unroll
-      for (int q = 0; q < V; ++q) store_stream(dst + q * kWave, v[q]);
+      for (int q = 0; q < V; ++q) store_row<kStreamStore>(dst + q * kWave, v[q]);
     }
   }
   for (int c = c0 + lane; c < nvec; c += kWave) {
-    const vec4 v = src[c];
+    const vec4 v = load_row<kStreamLoad>(src + c);
     uint64_t d = dests;
     while (d) {
       const int which = __ffsll((unsigned long long)d) - 1;
       d &= d - 1;
-      store_stream(dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + c, v);
+      store_row<kStreamStore>(dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + c, v);
     }
   }
 }
@@ -474,7 +509,9 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
   if (__ballot(slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
   if (ok) rank_src_token[slot] = t;
   const uint64_t dests = __ballot(ok);
-  if (dests) fan_out_row<V>(hidden + (int64_t)t * nvec, rank_buf, slot, dests, nvec);
+  // The hidden row is read once (streamed); the copies are stored with
+  // ordinary stores so that they stay in the Infinity Cache for the permute.
+  if (dests) fan_out_row<V, true, false>(hidden + (int64_t)t * nvec, rank_buf, slot, dests, nvec);
 }
 
 template <int V>
@@ -500,7 +537,9 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   if (__ballot(here && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
   if (ok) expert_src_pair[p] = t * k + lane;
   const uint64_t dests = __ballot(ok);
-  if (dests) fan_out_row<V>(rank_buf + i * nvec, expert_buf, p, dests, nvec);
+  // The packed row is read once and the expert rows are not read again here:
+  // both streamed.
+  if (dests) fan_out_row<V, true, true>(rank_buf + i * nvec, expert_buf, p, dests, nvec);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -523,7 +562,7 @@ __device__ __forceinline__ void store_sum(const float (&acc)[8], vec4* out, vec4
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  store_stream(out + at, o);
+  store_row<true>(out + at, o);
   if (out_f32) {
     vec4 a, b;
 #pragma unroll
@@ -531,8 +570,8 @@ __device__ __forceinline__ void store_sum(const float (&acc)[8], vec4* out, vec4
       a[i] = __float_as_uint(acc[i]);
       b[i] = __float_as_uint(acc[4 + i]);
     }
-    store_stream(out_f32 + 2 * at, a);
-    store_stream(out_f32 + 2 * at + 1, b);
+    store_row<true>(out_f32 + 2 * at, a);
+    store_row<true>(out_f32 + 2 * at + 1, b);
   }
 }
 
