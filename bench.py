@@ -59,6 +59,53 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+OUR_KERNELS = ("layout_tiles", "pack_rows", "permute_rows", "combine_rows")
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: float, workload: str) -> dict:
+    """Per-launch HBM traffic of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same
+    counter reads for the plain device copy of calib_mib MiB that
+    --copy-calibration runs first. Writes profiles/traffic.json."""
+    import csv
+
+    def per_kernel(path, counter):
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        # the calibration copies: the runtime's copy kernel at its largest grid
+        copies = [r for r in rows if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")]
+        big = max(int(r["Grid_Size"]) for r in copies)
+        acc = {"copy": [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == big]}
+        for r in rows:
+            key = next((k for k in OUR_KERNELS if k in r["Kernel_Name"]), None)
+            if key is not None:
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    nbytes = calib_mib * 2 ** 20
+    f_fetch = nbytes / (fetch["copy"] * 1024)
+    f_write = nbytes / (write["copy"] * 1024)
+    rec = {"copy_calibration": {"bytes_each_way": nbytes, "fetch_kib": fetch["copy"],
+                                "write_kib": write["copy"], "fetch_scale": f_fetch,
+                                "write_scale": f_write}}
+    out = {}
+    for k in OUR_KERNELS:
+        if k in fetch and k in write:
+            rd = fetch[k] * 1024 * f_fetch
+            wr = write[k] * 1024 * f_write
+            out[k.replace("_rows", "").replace("_tiles", "")] = {
+                "fetch_kib_per_launch": fetch[k], "write_kib_per_launch": write[k],
+                "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                "source_sha256_16": source_digest()}
+    rec[workload] = out
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    return rec
+
+
 def cpu_baseline(w, hid, ids, wts, y, budget_s: float):
     """The oracle as it stands, single-threaded, on the same workload: whole
     steps (layout, pack, permute, combine) repeated until `budget_s` is used."""
@@ -99,7 +146,15 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (for counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        rec = ingest_counters(*args.ingest_counters, args.copy_calibration or 512.0, args.workload)
+        print(json.dumps(rec, indent=1, sort_keys=True))
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this path runs one GPU's share "
               "of an expert-parallel layer, with the R ranks as logical buffers in its own HBM; "
@@ -124,6 +179,17 @@ def main():
     hid = synth.hidden(w)
     ids, wts = synth.routing(w)
     y = synth.expert_out_slots(w.seed, w.E, w.H, ids)
+
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 2 ** 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB", file=sys.stderr,
+              flush=True)
 
     shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
     buf = moe.Buffers(shape, dev)
