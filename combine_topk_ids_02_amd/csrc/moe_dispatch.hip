@@ -94,15 +94,21 @@ struct LayoutGeom {
   int batch_tokens;     // tokens whose ids are staged in LDS at once (multiple of 1024)
   int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
   int ntiles;
-  uint64_t rank_magic;  // ceil(2^32 / m)
+  float inv_m;          // 1/m rounded to float
 };
 
-// rank(e) = e / m, as (e * ceil(2^32/m)) >> 32: exact for 0 <= e < 2^16 and
-// m <= 2^10 (the rounding error e*(ceil(2^32/m) - 2^32/m) / 2^32 < 2^-16
-// never reaches the next multiple of 1/m).
-__device__ __forceinline__ int rank_of(int e, uint64_t magic) {
-  return int((uint64_t(uint32_t(e)) * magic) >> 32);
+// rank(e) = e / m, as floor(fl(e * c + c/2)) with c = fl(1/m) and one fused
+// multiply-add: the result lies within 2^-13 of (e + 1/2)/m for e < 2^10 and
+// m <= 2^10, which is at least 1/(2m) >= 2^-11 away from the integers around
+// it, so the truncation is exact. (Full-rate instructions, unlike the
+// quarter-rate 32-bit integer multiply-high.)
+__device__ __forceinline__ int rank_of(int e, float inv_m) {
+  return int(__builtin_fmaf(float(e), inv_m, 0.5f * inv_m));
 }
+
+// Rank sets of a token as bit masks: 32 bits when R <= 32, else 64.
+template <bool kWide> struct RankMask { using type = uint32_t; };
+template <> struct RankMask<true> { using type = uint64_t; };
 
 // Inclusive prefix sum across a wave with DPP row shifts and broadcasts.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
@@ -115,43 +121,65 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
-// Exclusive scans of the expert columns s[0..E) (waves 0..7) and of the rank
-// columns s[E..E+R) (wave 8) in place, both at once. Returns nothing; the
-// totals are left in s_tmp[8] (experts) and s_tmp[9] (ranks).
-__device__ void scan_columns(int32_t* s, int E, int R, int32_t* s_tmp /* [16] */) {
+// Column totals, exclusive scans and the tile's first rows, in one pass: for
+// every column c, count = s_tot[c] + s_pre[c] (tokens from the tile on, and
+// before it), offset = exclusive prefix of the counts (experts in id order
+// over waves 0..7, ranks in rank order in wave 8), and s_pre[c] becomes
+// offset + (count before the tile), the tile's first row in that column. The
+// workgroup that is `writer` also stores the counts and offsets.
+__device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
+                             int32_t* s_tmp /* [16] */, bool writer, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* rank_counts,
+                             int32_t* rank_offsets) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
   constexpr int kScanThreads = 8 * kWave;
-  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= 2 for E <= 1024
-  int lo = 0, hi = 0, sum = 0, x = 0;
+  constexpr int kPer = (kMaxExperts + kScanThreads - 1) / kScanThreads;
+  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kPer
+  int lo = 0, sum = 0, x = 0;
+  int cnt[kPer];
   if (wave < 8) {
     lo = min(E, tid * per);
-    hi = min(E, lo + per);
-    for (int i = lo; i < hi; ++i) sum += s[i];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = lo + q;
+      cnt[q] = (q < per && i < E) ? s_tot[i] + s_pre[i] : 0;
+      if (writer && q < per && i < E) expert_counts[i] = cnt[q];
+      sum += cnt[q];
+    }
     x = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s_tmp[wave] = x;
   } else if (wave == 8) {
-    const int v = lane < R ? s[E + lane] : 0;
+    const int v = lane < R ? s_tot[E + lane] + s_pre[E + lane] : 0;
     const int inc = wave_inclusive_scan(v);
-    if (lane < R) s[E + lane] = inc - v;
-    if (lane == kWave - 1) s_tmp[9] = inc;
+    if (lane < R) {
+      s_pre[E + lane] += inc - v;
+      if (writer) {
+        rank_counts[lane] = v;
+        rank_offsets[lane] = inc - v;
+      }
+    }
+    if (writer && lane == kWave - 1) rank_offsets[R] = inc;
   }
   __syncthreads();
   if (wave < 8) {
-    int base = 0, total = 0;
+    int run = x - sum, total = 0;
     for (int w = 0; w < 8; ++w) {
       const int t = s_tmp[w];
-      base += w < wave ? t : 0;
+      run += w < wave ? t : 0;
       total += t;
     }
-    int run = base + x - sum;
-    for (int i = lo; i < hi; ++i) {
-      const int v = s[i];
-      s[i] = run;
-      run += v;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = lo + q;
+      if (q < per && i < E) {
+        s_pre[i] += run;
+        if (writer) expert_offsets[i] = run;
+        run += cnt[q];
+      }
     }
-    if (tid == 0) s_tmp[8] = total;
+    if (writer && tid == 0) expert_offsets[E] = total;
   }
   __syncthreads();
 }
@@ -180,20 +208,22 @@ __device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int6
 //   pair_row[t][j]        = expert_offsets[e] + #{pairs of e before (t, j)}
 //   token_rank_slot[t][r] = rank_offsets[r] + #{tokens before t with a copy on r}
 // Workgroup 0 also writes the counts and offsets.
-template <int K>
+template <int K, bool kWide>
 __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     LayoutGeom g, const int32_t* __restrict__ ids, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
     int32_t* __restrict__ pair_row, int32_t* err_word) {
   constexpr int KR = K > 0 ? K : kMaxK;
+  using Mask = typename RankMask<kWide>::type;
   const int k = K > 0 ? K : g.k;
   extern __shared__ int32_t smem[];
   int32_t* s_ids = smem;                          // [batch_tokens * k] staged ids
   int32_t* s_pack = s_ids + g.batch_tokens * k + 4;  // [kOwnTokens * k] own sub-tile ids
   int32_t* s_cnt = s_pack + kOwnTokens * k;       // [kOwnWaves][ncols] per-wave counts
-  int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols] before the tile -> running base
-  int32_t* s_tot = s_pre + g.ncols;               // [ncols] other tokens -> totals -> offsets
+  int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols + 1] before the tile -> running base
+  int32_t* s_tot = s_pre + g.ncols + 1;           // [ncols + 1] other tokens -> totals -> offsets
+  // (the extra slot of each takes the counts of invalid ids, so counting needs no branch)
   __shared__ int32_t s_tmp[kLayoutWaves];
 
   const int tid = threadIdx.x;
@@ -246,12 +276,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 #pragma unroll
       for (int j = 0; j < KR; ++j)
         if (j < k) ev[j] = tl < nb ? s_ids[tl * k + j] : -1;
-      uint64_t mask = 0;
+      Mask mask = 0;
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
-        if (j < k && ev[j] >= 0 && ev[j] < g.E) {
-          atomicAdd(&cnt[ev[j]], 1);
-          mask |= uint64_t(1) << rank_of(ev[j], g.rank_magic);
+        if (j < k) {
+          const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
+          atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
+          mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
         }
       }
       for (int r = 0; r < g.R; ++r) {
@@ -265,26 +296,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     if (rc_tot) atomicAdd(&s_tot[g.E + lane], rc_tot);
   }
   __syncthreads();
-  for (int c = tid; c < g.ncols; c += kLayoutThreads) s_tot[c] += s_pre[c];
-  __syncthreads();
 
-  // 2. Counts, then exclusive scans: experts in id order, ranks in rank order.
-  if (blockIdx.x == 0) {
-    for (int c = tid; c < g.E; c += kLayoutThreads) expert_counts[c] = s_tot[c];
-    for (int c = tid; c < g.R; c += kLayoutThreads) rank_counts[c] = s_tot[g.E + c];
-  }
-  __syncthreads();
-  scan_columns(s_tot, g.E, g.R, s_tmp);
-  if (blockIdx.x == 0) {
-    for (int c = tid; c < g.E; c += kLayoutThreads) expert_offsets[c] = s_tot[c];
-    for (int c = tid; c < g.R; c += kLayoutThreads) rank_offsets[c] = s_tot[g.E + c];
-    if (tid == 0) {
-      expert_offsets[g.E] = s_tmp[8];
-      rank_offsets[g.R] = s_tmp[9];
-    }
-  }
-  // 3. Absolute first row of this tile in every column.
-  for (int c = tid; c < g.ncols; c += kLayoutThreads) s_pre[c] += s_tot[c];
+  // 2.-3. Counts, exclusive scans (experts in id order, ranks in rank order)
+  //    and the absolute first row of this tile in every column (in s_pre).
+  scan_columns(s_pre, s_tot, g.E, g.R, s_tmp, blockIdx.x == 0, expert_counts, expert_offsets,
+               rank_counts, rank_offsets);
 
   // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..3. Wave w
   //    owns tokens [64w, 64w+64) of the sub-tile, i.e. the contiguous pairs
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     __syncthreads();
 
     int ex[KR], rk[KR];  // per chunk: this lane's expert (or -1) and its rank in the wave
-    uint64_t mask = 0;   // rank set of token tid of the sub-tile
+    Mask mask = 0;       // rank set of token tid of the sub-tile
     if (ranker) {
       // All of the wave's ids first (one LDS wait), then the matches, then the
       // running-count atomics in chunk order, then the leaders' old counts.
@@ -325,21 +341,33 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
         }
       }
       int lead[KR], grp[KR];
+      uint64_t peers[KR];
 #pragma unroll
       for (int ch = 0; ch < KR; ++ch) {
         if (ch < k) {
-          const int e = ex[ch];
-          const bool valid = e >= 0 && e < g.E;
-          bad_id |= (e != -1) && !valid;
-          uint64_t peers = __ballot(valid);
-          for (int b = 0; b < ebits; ++b) {
-            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
-            peers &= ((e >> b) & 1) ? ones : ~ones;
+          const bool valid = uint32_t(ex[ch]) < uint32_t(g.E);
+          bad_id |= (ex[ch] != -1) && !valid;
+          ex[ch] = valid ? ex[ch] : -1;
+          peers[ch] = __ballot(valid);
+        }
+      }
+      // One ballot per id bit, all chunks side by side (independent chains).
+      for (int b = 0; b < ebits; ++b) {
+#pragma unroll
+        for (int ch = 0; ch < KR; ++ch) {
+          if (ch < k) {
+            const bool bit = (ex[ch] >> b) & 1;
+            const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
+            peers[ch] &= bit ? ones : ~ones;
           }
-          ex[ch] = valid ? e : -1;
-          rk[ch] = __popcll(peers & lanes_below());
-          lead[ch] = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
-          grp[ch] = __popcll(peers);
+        }
+      }
+#pragma unroll
+      for (int ch = 0; ch < KR; ++ch) {
+        if (ch < k) {
+          rk[ch] = __popcll(peers[ch] & lanes_below());
+          lead[ch] = ex[ch] >= 0 ? __ffsll((unsigned long long)peers[ch]) - 1 : lane;
+          grp[ch] = __popcll(peers[ch]);
         }
       }
       int cnt_old[KR];
@@ -355,7 +383,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
         if (ch < k) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
 #pragma unroll
       for (int j = 0; j < KR; ++j)
-        if (j < k && own[j] >= 0 && own[j] < g.E) mask |= uint64_t(1) << rank_of(own[j], g.rank_magic);
+        if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
       int copies = 0;  // lane r: the wave's tokens with a copy on rank r
       for (int r = 0; r < g.R; ++r) {
         const int c = __popcll(__ballot((mask >> r) & 1));
@@ -400,7 +428,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 size_t layout_lds_bytes(int batch_tokens, int k, int ncols) {
   // the staged ids get 4 ints of slack: a batch's last 16-byte load may run past its ids
   return sizeof(int32_t) * (size_t(batch_tokens) * k + 4 + size_t(kOwnTokens) * k +
-                            size_t(kOwnWaves + 2) * ncols);
+                            size_t(kOwnWaves + 2) * ncols + 2);
 }
 
 LayoutGeom layout_geometry(const moe_shape_t& sh) {
@@ -411,7 +439,7 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   g.k = sh.k;
   g.m = sh.E / sh.R;
   g.ncols = sh.E + sh.R;
-  g.rank_magic = ((uint64_t(1) << 32) + uint64_t(g.m) - 1) / uint64_t(g.m);
+  g.inv_m = float(1.0 / double(g.m));
   // Largest batch (multiple of 1024 tokens) that the loads and LDS hold.
   const int t_round = std::max(1, (sh.T + kLayoutThreads - 1) / kLayoutThreads) * kLayoutThreads;
   g.batch_tokens = std::min(t_round, kLayoutThreads * std::max(1, (4 * kBatchVecs) / sh.k));
@@ -425,18 +453,28 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   return g;
 }
 
+template <int K, bool kWide>
+void launch_layout_kw(const LayoutGeom& g, size_t lds, hipStream_t st, const int32_t* ids,
+                      int32_t* rc, int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs,
+                      int32_t* pr, int32_t* err) {
+  // Allow this instantiation the LDS it may need (above the 64 KiB default);
+  // set once per process, the only thing the library ever caches.
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&layout_tiles<K, kWide>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
+  (void)attr;
+  hipLaunchKernelGGL((layout_tiles<K, kWide>), dim3(g.ntiles), dim3(kLayoutThreads), lds, st, g,
+                     ids, rc, ro, ec, eo, trs, pr, err);
+}
+
 template <int K>
 void launch_layout_k(const LayoutGeom& g, size_t lds, hipStream_t st, const int32_t* ids,
                      int32_t* rc, int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs,
                      int32_t* pr, int32_t* err) {
-  // Allow this instantiation the LDS it may need (above the 64 KiB default);
-  // set once per process, the only thing the library ever caches.
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
-  (void)attr;
-  hipLaunchKernelGGL((layout_tiles<K>), dim3(g.ntiles), dim3(kLayoutThreads), lds, st, g, ids,
-                     rc, ro, ec, eo, trs, pr, err);
+  if (g.R > 32)
+    launch_layout_kw<K, true>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
+  else
+    launch_layout_kw<K, false>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
 }
 
 void launch_layout(const LayoutGeom& g, hipStream_t st, const int32_t* ids, int32_t* rc,
