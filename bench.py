@@ -3,12 +3,20 @@ permute, combine) over one batch of seeded synthetic input already resident in
 HBM, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py --sweep [tiny,decode,prefill,skew,adv]
 
-Prints ONE JSON line: dispatch+combine throughput in GB/s of algorithmic bytes
-(what the method must move, with the measured copy count C and pair count P),
-its fraction of the 8 TB/s HBM peak, per-call times, the roofline of the
-dominant kernel (permute) measured with HIP events on the stream it runs on,
-and the CPU oracle timed on a bounded sample of the same workload.
+The default mode prints ONE JSON line: dispatch+combine throughput in GB/s of
+algorithmic bytes (what the method must move, with the measured copy count C
+and pair count P), its fraction of the 8 TB/s HBM peak, per-call times, the
+roofline of the dominant kernel (permute) measured with HIP events on the
+stream it runs on, and the CPU oracle timed on a bounded sample of the same
+workload.
+
+--sweep measures every workload per call, warm (back to back) and cold (a
+1 GiB write evicts L2 and the Infinity Cache before each call): 5 warm-up
+steps, then the median of 30 calls, repeated 3 times; next to it a plain 1 GiB
+device copy as the achievable rate, and the oracle pinned to one core (median
+of 5 steps, 3 for the two large workloads).
 """
 from __future__ import annotations
 
@@ -26,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "dispatch+combine GB/s and % HBM peak, T=4096 H=5120 E=384 top-6 R=8"
 KERNEL_SOURCE = os.path.join(ROOT, "combine_topk_ids_02_amd", "csrc", "moe_dispatch.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CALLS = ("layout", "pack", "permute", "combine")
 
 
 def algorithmic_bytes(T, H, E, R, k, C, P):
@@ -106,36 +115,264 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: float, workload: 
     return rec
 
 
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class one_core:
+    """Pins the calling process to one host core for the duration."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(self.saved)})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+
+
+def host_description() -> str:
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"1 thread of {len(os.sched_getaffinity(0))} host cores ({model})"
+
+
+def oracle_step(w, hid, ids, wts, eo):
+    import oracle
+
+    T, k = ids.shape
+    lay = oracle.layout(ids, w.E, w.R)
+    rb, src, _ = oracle.pack(hid, lay["token_rank_slot"], T * min(k, w.R))
+    oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], w.E, T * k)
+    oracle.combine(eo, lay["pair_row"], wts, want_f32=False)
+    return int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
+
+
 def cpu_baseline(w, hid, ids, wts, y, budget_s: float):
-    """The oracle as it stands, single-threaded, on the same workload: whole
+    """The oracle as it stands, pinned to one core, on the same workload: whole
     steps (layout, pack, permute, combine) repeated until `budget_s` is used."""
+    import oracle
+
+    T, k = ids.shape
+    lay = oracle.layout(ids, w.E, w.R)
+    eo = oracle.place_slots(y, lay["pair_row"], T * k)
+    reps, t_total = 0, 0.0
+    C = P = 0
+    with one_core():
+        while t_total < budget_s or reps == 0:
+            t0 = time.perf_counter()
+            C, P = oracle_step(w, hid, ids, wts, eo)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    nbytes = sum(algorithmic_bytes(T, w.H, w.E, w.R, k, C, P).values())
+    return {
+        "value": round(nbytes * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
+        "kind": "oracle", "ms_per_step": round(1e3 * t_total / reps, 2),
+        "sample": f"{reps} whole {w.name} steps (layout+pack+permute+combine), "
+                  f"{t_total:.1f} s, {host_description()}",
+    }
+
+
+def oracle_median(w, hid, ids, wts, y, reps: int) -> dict:
+    """Median wall time of `reps` whole oracle steps, pinned to one core."""
     import numpy as np
 
     import oracle
 
     T, k = ids.shape
-    cap_rank, cap_expert = T * min(k, w.R), T * k
     lay = oracle.layout(ids, w.E, w.R)
-    eo = oracle.place_slots(y, lay["pair_row"], cap_expert)
-    reps, t_total = 0, 0.0
-    C = P = 0
-    while t_total < budget_s or reps == 0:
-        t0 = time.perf_counter()
-        lay = oracle.layout(ids, w.E, w.R)
-        rb, src, _ = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
-        oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], w.E, cap_expert)
-        oracle.combine(eo, lay["pair_row"], wts, want_f32=False)
-        t_total += time.perf_counter() - t0
-        reps += 1
-        C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
+    eo = oracle.place_slots(y, lay["pair_row"], T * k)
+    times = []
+    with one_core():
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            C, P = oracle_step(w, hid, ids, wts, eo)
+            times.append(time.perf_counter() - t0)
+    ms = float(np.median(times)) * 1e3
     nbytes = sum(algorithmic_bytes(T, w.H, w.E, w.R, k, C, P).values())
-    del np
-    return {
-        "value": round(nbytes * reps / t_total / 1e9, 3), "unit": "GB/s", "cores": 1,
-        "kind": "oracle", "ms_per_step": round(1e3 * t_total / reps, 2),
-        "sample": f"{reps} whole {w.name} steps (layout+pack+permute+combine), "
-                  f"single thread, {t_total:.1f} s",
-    }
+    return {"ms_per_step": round(ms, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 3),
+            "reps": reps, "host": host_description()}
+
+
+class Rig:
+    """One workload resident on the GPU with every buffer of a pass, and the
+    four library calls on the current stream."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import combine_topk_ids_02_amd as moe
+        import synth
+        from synth import staging
+
+        self.w, self.dev, self.moe = w, dev, moe
+        log(f"generating {w.describe()}")
+        self.hid = synth.hidden(w)
+        self.ids, self.wts = synth.routing(w)
+        self.y = synth.expert_out_slots(w.seed, w.E, w.H, self.ids)
+        self.shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
+        self.buf = moe.Buffers(self.shape, dev)
+        self.hid_d = staging.rows_to_device(self.hid, dev)
+        self.ids_d = torch.from_numpy(self.ids).to(dev)
+        self.wts_d = torch.from_numpy(self.wts).to(dev)
+        # a first layout gives pair_row for placing the expert outputs
+        moe.dispatch(self.buf, self.hid_d, self.ids_d)
+        self.expert_out = staging.place_expert_outputs(
+            staging.rows_to_device(self.y, dev), self.buf.pair_row, self.shape.cap_expert)
+        torch.cuda.synchronize()
+        self.C = int(self.buf.rank_offsets[-1].item())
+        self.P = int(self.buf.expert_offsets[-1].item())
+        self.nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def call(self, name: str) -> None:
+        moe, s, b = self.moe, self.shape, self.buf
+        if name == "layout":
+            moe.layout(self.ids_d, s.E, s.R, s.H, err=b.err, out=b.layout_dict())
+        elif name == "pack":
+            moe.pack(self.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
+                     err=b.err)
+        elif name == "permute":
+            moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
+                        s.E, b.expert_buf, b.expert_src_pair, err=b.err)
+        else:
+            moe.combine(self.expert_out, b.pair_row, self.wts_d, s.E, s.R, b.out, err=b.err)
+
+    def step(self, ev=None, flush=None) -> None:
+        """One pass; with `ev` (5 events) records between the calls; with
+        `flush` (a large tensor) overwrites it before every call, outside the
+        events."""
+        for i, c in enumerate(CALLS):
+            if flush is not None:
+                flush.fill_(i + 1)
+            if ev is not None:
+                ev[2 * i if flush is not None else i].record(self.stream)
+            self.call(c)
+            if ev is not None and flush is not None:
+                ev[2 * i + 1].record(self.stream)
+        if ev is not None and flush is None:
+            ev[len(CALLS)].record(self.stream)
+
+    def per_call_ms(self, n: int, flush=None) -> dict:
+        """Per-call durations (ms) over n steps."""
+        import torch
+
+        nev = 2 * len(CALLS) if flush is not None else len(CALLS) + 1
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            self.step(evs[i], flush)
+        torch.cuda.synchronize()
+        out = {c: [] for c in CALLS}
+        for ev in evs:
+            for j, c in enumerate(CALLS):
+                a, b = (ev[2 * j], ev[2 * j + 1]) if flush is not None else (ev[j], ev[j + 1])
+                out[c].append(a.elapsed_time(b))
+        return out
+
+    def check_err(self) -> None:
+        e = int(self.buf.err.item())
+        if e != 0:
+            print(f"bench.py: device error word {e} on {self.w.name}", file=sys.stderr)
+            sys.exit(1)
+
+
+def copy_reference(dev, gib: float = 1.0, reps: int = 10) -> dict:
+    """A plain device-to-device copy of `gib` GiB: the achievable rate."""
+    import numpy as np
+    import torch
+
+    n = int(gib * 2 ** 30)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    del src, dst
+    return {"bytes": 2 * n, "us": round(ms * 1e3, 1), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+def sweep(names, dev, with_oracle: bool) -> None:
+    import numpy as np
+    import torch
+
+    import synth
+
+    flush = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    copy = copy_reference(dev)
+    log(f"1 GiB device copy: {copy['GB/s']} GB/s")
+    print(json.dumps({"copy_1GiB": copy}), flush=True)
+    rows = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        rig = Rig(w, dev)
+        for _ in range(5):
+            rig.step()
+        res = {"workload": w.describe(), "C": rig.C, "P": rig.P,
+               "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
+        for mode, fl in (("warm", None), ("cold", flush)):
+            meds = {c: [] for c in CALLS}
+            for _ in range(3):
+                ms = rig.per_call_ms(30, fl)
+                for c in CALLS:
+                    meds[c].append(float(np.median(ms[c])))
+            for c in CALLS:
+                us = float(np.median(meds[c])) * 1e3
+                ent = res["calls"].setdefault(c, {"bytes": rig.nbytes[c]})
+                ent[mode] = {"us": round(us, 2),
+                             "us_spread": [round(min(meds[c]) * 1e3, 2),
+                                           round(max(meds[c]) * 1e3, 2)],
+                             "GB/s": round(rig.nbytes[c] / (us * 1e-6) / 1e9, 1)}
+                ent[mode]["pct_peak"] = round(100 * ent[mode]["GB/s"] / HBM_PEAK_GBS, 1)
+            log(f"{name} {mode}: " + ", ".join(
+                f"{c} {res['calls'][c][mode]['us']} us" for c in CALLS))
+        rig.check_err()
+        tot = sum(rig.nbytes.values())
+        for mode in ("warm", "cold"):
+            us = sum(res["calls"][c][mode]["us"] for c in CALLS)
+            res[mode] = {"us": round(us, 2), "GB/s": round(tot / (us * 1e-6) / 1e9, 1),
+                         "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        warm = res["calls"]
+        res["rows_per_s"] = {
+            "pack_copies": round(rig.C / (warm["pack"]["warm"]["us"] * 1e-6)),
+            "permute_pairs": round(rig.P / (warm["permute"]["warm"]["us"] * 1e-6)),
+            "combine_tokens": round(w.T / (warm["combine"]["warm"]["us"] * 1e-6)),
+            "combine_pairs": round(rig.P / (warm["combine"]["warm"]["us"] * 1e-6))}
+        res["bytes"] = tot
+        if with_oracle:
+            log(f"{name}: oracle")
+            res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
+                                          3 if w.T * w.H > 2 ** 25 else 5)
+        print(json.dumps(res), flush=True)
+        rows.append((name, res))
+        del rig
+        torch.cuda.empty_cache()
+    # human-readable table
+    print("\n| workload | mode | layout us | pack us | permute us | combine us | total us "
+          "| GB/s | % of 8 TB/s | oracle ms/step |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for name, r in rows:
+        for mode in ("warm", "cold"):
+            orc = r.get("oracle", {}).get("ms_per_step", "") if mode == "warm" else ""
+            print(f"| {name} | {mode} | " + " | ".join(
+                str(r["calls"][c][mode]["us"]) for c in CALLS) +
+                f" | {r[mode]['us']} | {r[mode]['GB/s']} | {r[mode]['pct_peak']} | {orc} |")
+    print(f"\n1 GiB device copy: {copy['us']} us, {copy['GB/s']} GB/s (read + write)")
 
 
 def main():
@@ -146,6 +383,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", nargs="?", const="tiny,decode,prefill,skew,adv", default=None,
+                    metavar="WORKLOADS", help="per-call warm/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (for counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -166,19 +405,16 @@ def main():
 
     import __graft_entry__ as ge
     ge.ensure_built()
-    import combine_topk_ids_02_amd as moe
     import synth
-    from synth import staging
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep(args.sweep.split(","), dev, not args.no_cpu_baseline)
+        return
     w = synth.WORKLOADS[args.workload]
-    print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
-    hid = synth.hidden(w)
-    ids, wts = synth.routing(w)
-    y = synth.expert_out_slots(w.seed, w.E, w.H, ids)
 
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * 2 ** 20) // 2
@@ -188,48 +424,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        print(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB", file=sys.stderr,
-              flush=True)
+        log(f"copy calibration: 3 x {args.copy_calibration} MiB")
 
-    shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
-    buf = moe.Buffers(shape, dev)
-    hid_d = staging.rows_to_device(hid, dev)
-    ids_d = torch.from_numpy(ids).to(dev)
-    wts_d = torch.from_numpy(wts).to(dev)
-    moe.dispatch(buf, hid_d, ids_d)  # first layout gives pair_row for placing expert outputs
-    expert_out = staging.place_expert_outputs(staging.rows_to_device(y, dev), buf.pair_row,
-                                              shape.cap_expert)
-    torch.cuda.synchronize()
-    C = int(buf.rank_offsets[-1].item())
-    P = int(buf.expert_offsets[-1].item())
-    nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, C, P)
-    step_bytes = sum(nbytes.values())
+    rig = Rig(w, dev)
+    step_bytes = sum(rig.nbytes.values())
+    stream = rig.stream
 
-    stream = torch.cuda.current_stream(dev)
-    calls = ["layout", "pack", "permute", "combine"]
-
-    def step(ev=None):
-        s = shape
-        if ev is not None:
-            ev[0].record(stream)
-        moe.layout(ids_d, s.E, s.R, s.H, err=buf.err, out=buf.layout_dict())
-        if ev is not None:
-            ev[1].record(stream)
-        moe.pack(hid_d, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token,
-                 err=buf.err)
-        if ev is not None:
-            ev[2].record(stream)
-        moe.permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, ids_d, buf.pair_row, s.E,
-                    buf.expert_buf, buf.expert_src_pair, err=buf.err)
-        if ev is not None:
-            ev[3].record(stream)
-        moe.combine(expert_out, buf.pair_row, wts_d, s.E, s.R, buf.out, err=buf.err)
-        if ev is not None:
-            ev[4].record(stream)
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        step()
+        rig.step()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, bracketed by events on the stream the
@@ -240,7 +443,7 @@ def main():
     t0 = time.perf_counter()
     t_begin.record(stream)
     for _ in range(args.steps):
-        step()
+        rig.step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -248,40 +451,31 @@ def main():
 
     # Second timed pass with an event between every call, for per-kernel
     # durations and the roofline of the dominant kernel.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    per_call_ms = {c: [] for c in calls}
-    for ev in evs:
-        for j, c in enumerate(calls):
-            per_call_ms[c].append(ev[j].elapsed_time(ev[j + 1]))
-    if int(buf.err.item()) != 0:
-        print(f"bench.py: device error word {int(buf.err.item())}", file=sys.stderr)
-        sys.exit(1)
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
-          flush=True)
+    per_call_ms = rig.per_call_ms(args.steps)
+    rig.check_err()
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     call_stats = {}
-    for c in calls:
+    for c in CALLS:
         ms = float(np.mean(per_call_ms[c]))
-        call_stats[c] = {"us": round(ms * 1e3, 2), "us_median": round(float(np.median(per_call_ms[c])) * 1e3, 2),
-                         "bytes": nbytes[c], "GB/s": round(nbytes[c] / (ms * 1e-3) / 1e9, 1)}
+        call_stats[c] = {"us": round(ms * 1e3, 2),
+                         "us_median": round(float(np.median(per_call_ms[c])) * 1e3, 2),
+                         "bytes": rig.nbytes[c],
+                         "GB/s": round(rig.nbytes[c] / (ms * 1e-3) / 1e9, 1)}
     dom = "permute"
     dom_us = call_stats[dom]["us"]
-    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
+    achieved = rig.nbytes[dom] / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(dom, w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "permute_rows",
-                "algorithmic_bytes_per_launch": nbytes[dom]}
+                "algorithmic_bytes_per_launch": rig.nbytes[dom]}
 
     cpu = None
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, hid, ids, wts, y, args.cpu_seconds)
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, rig.hid, rig.ids, rig.wts, rig.y, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -289,8 +483,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.describe(), "T": w.T, "H": w.H, "E": w.E, "R": w.R, "k": w.k,
-                   "seed": w.seed, "copies_C": C, "pairs_P": P,
-                   "copies_per_token": round(C / max(w.T, 1), 4),
+                   "seed": w.seed, "copies_C": rig.C, "pairs_P": rig.P,
+                   "copies_per_token": round(rig.C / max(w.T, 1), 4),
                    "bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "calls": call_stats,
