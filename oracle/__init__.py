@@ -39,6 +39,11 @@ class _Lib:
         lib.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, i64, vp, vp]
         lib.oracle_combine_f64.restype = ctypes.c_int
         lib.oracle_combine_f64.argtypes = [i32, i32, i32, vp, vp, vp, i64, vp]
+        lib.oracle_combine_rank_partial.restype = ctypes.c_int
+        lib.oracle_combine_rank_partial.argtypes = [i32, i32, i32, i32, i32, vp, i64, vp, vp, vp,
+                                                    vp, vp, i64, vp, vp]
+        lib.oracle_combine_ranks.restype = ctypes.c_int
+        lib.oracle_combine_ranks.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
         self.lib = lib
 
 
@@ -158,6 +163,39 @@ def combine_f64(expert_out, pair_row, topk_weights):
     out = np.zeros((T, H), np.float64)
     err = _load().oracle_combine_f64(T, H, k, _p(eo), _p(pr), _p(w), eo.shape[0], _p(out))
     return out, err
+
+
+def combine_rank_partial(expert_out, rank_src_token, rank_offsets, topk_ids, pair_row,
+                         topk_weights, E: int, cap_rank: int, want_f32: bool = True):
+    """First stage of the two-stage combine: one partial row per rank-buffer
+    row (bf16, and the float32 accumulator if want_f32). Rows past the last
+    segment stay zero."""
+    eo = _c(expert_out, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    R = len(rank_offsets) - 1
+    H = eo.shape[1]
+    part = np.zeros((cap_rank, H), np.uint16)
+    part32 = np.zeros((cap_rank, H), np.float32) if want_f32 else None
+    err = _load().oracle_combine_rank_partial(
+        T, H, E, R, k, _p(eo), eo.shape[0], _p(_c(rank_src_token, np.int32)),
+        _p(_c(rank_offsets, np.int32)), _p(ids), _p(_c(pair_row, np.int32)),
+        _p(_c(topk_weights, np.float32)), cap_rank, _p(part), _p(part32))
+    return part, part32, err
+
+
+def combine_ranks(partial, token_rank_slot, want_f32: bool = True):
+    """Second stage of the two-stage combine: per token, the sum over ranks of
+    its partial rows, in float32, rounded to bf16."""
+    part = _c(partial, np.uint16)
+    slots = _c(token_rank_slot, np.int32)
+    T, R = slots.shape
+    H = part.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    out32 = np.zeros((T, H), np.float32) if want_f32 else None
+    err = _load().oracle_combine_ranks(T, H, R, _p(part), part.shape[0], _p(slots), _p(out),
+                                       _p(out32))
+    return out, out32, err
 
 
 def place_slots(y_slots: np.ndarray, pair_row: np.ndarray, rows: int) -> np.ndarray:

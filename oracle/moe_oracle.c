@@ -180,3 +180,62 @@ int oracle_combine_f64(int32_t T, int32_t H, int32_t k, const uint16_t* expert_o
   }
   return err;
 }
+
+int oracle_combine_rank_partial(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+                                const uint16_t* expert_out, int64_t cap_expert,
+                                const int32_t* rank_src_token, const int32_t* rank_offsets,
+                                const int32_t* topk_ids, const int32_t* pair_row,
+                                const float* topk_weights, int64_t cap_rank, uint16_t* partial,
+                                float* partial_f32) {
+  (void)T;
+  const int32_t m = E / R;
+  int err = 0;
+  for (int32_t r = 0; r < R; ++r) {
+    /* the rows of rank r's segment that fit in the buffer */
+    int64_t lo = rank_offsets[r], hi = rank_offsets[r + 1];
+    if (hi > cap_rank) hi = cap_rank;
+    for (int64_t i = lo; i < hi; ++i) {
+      const int32_t t = rank_src_token[i];
+      for (int32_t h = 0; h < H; ++h) {
+        float acc = 0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+          const int32_t e = topk_ids[(int64_t)t * k + j];
+          if (!id_is_expert(e, E) || e / m != r) continue; /* not an expert of rank r */
+          const int64_t row = pair_row[(int64_t)t * k + j];
+          if (row < 0) continue;
+          if (row >= cap_expert) {
+            err |= ORACLE_ERR_EXPERT_CAP;
+            continue;
+          }
+          acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);
+        }
+        partial[i * H + h] = narrow_bf16_rne(acc);
+        if (partial_f32) partial_f32[i * H + h] = acc;
+      }
+    }
+  }
+  return err;
+}
+
+int oracle_combine_ranks(int32_t T, int32_t H, int32_t R, const uint16_t* partial,
+                         int64_t cap_rank, const int32_t* token_rank_slot, uint16_t* out,
+                         float* out_f32) {
+  int err = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      for (int32_t r = 0; r < R; ++r) {
+        const int64_t s = token_rank_slot[(int64_t)t * R + r];
+        if (s < 0) continue; /* no copy of t on rank r */
+        if (s >= cap_rank) {
+          err |= ORACLE_ERR_RANK_CAP;
+          continue;
+        }
+        acc = acc + widen_bf16(partial[s * H + h]);
+      }
+      out[(int64_t)t * H + h] = narrow_bf16_rne(acc);
+      if (out_f32) out_f32[(int64_t)t * H + h] = acc;
+    }
+  }
+  return err;
+}

@@ -25,7 +25,9 @@
  *
  * Parity status: every function below is pinned by the CPU tests (stable-sort
  * and brute-force equivalence, closed-form copy count, prose examples,
- * identity and one-hot combine, exact-rational error bound); none is unpinned.
+ * identity and one-hot combine, exact-rational error bound, hand-derived
+ * rounding and addition-order cases, exact integer sums for the two-stage
+ * combine); none is unpinned.
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -95,6 +97,37 @@ int oracle_combine(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
 int oracle_combine_f64(int32_t T, int32_t H, int32_t k, const uint16_t* expert_out,
                        const int32_t* pair_row, const float* topk_weights, int64_t cap_expert,
                        double* out_f64);
+
+/*
+ * Two-stage combine, first stage ([A2A] sec 7.1: a token's weighted sum splits
+ * into a sum over the experts that sit on one GPU and a sum over the GPUs;
+ * with the layout by expert the expert's GPU does the first stage, so one row
+ * per GPU travels back, and what travels back is 16-bit). For every
+ * rank-buffer row i below min(rank_offsets[R], cap_rank), in the segment of
+ * rank r and holding token t = rank_src_token[i]:
+ *   acc = +0.0f; for j = 0..k-1 whose expert lives on r and whose pair_row is valid:
+ *     acc = fmaf(w[t*k+j], float(expert_out[pair_row[t*k+j]][h]), acc)
+ *   partial[i][h] = bf16 round-to-nearest-even of acc; partial_f32 (if not NULL) = acc.
+ * A pair row at or past cap_expert is skipped and reported (ORACLE_ERR_EXPERT_CAP).
+ */
+int oracle_combine_rank_partial(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+                                const uint16_t* expert_out, int64_t cap_expert,
+                                const int32_t* rank_src_token, const int32_t* rank_offsets,
+                                const int32_t* topk_ids, const int32_t* pair_row,
+                                const float* topk_weights, int64_t cap_rank, uint16_t* partial,
+                                float* partial_f32);
+
+/*
+ * Two-stage combine, second stage at the token's home ([A2A] sec 7.1: the home
+ * GPU adds up the rows it receives, in 32-bit floats), ranks in ascending order:
+ *   acc = +0.0f; for r = 0..R-1 with s = token_rank_slot[t*R+r] a row in [0, cap_rank):
+ *     acc = acc + float(partial[s][h])
+ *   out[t][h] = bf16 round-to-nearest-even of acc; out_f32 (if not NULL) = acc.
+ * A slot at or past cap_rank is skipped and reported (ORACLE_ERR_RANK_CAP).
+ */
+int oracle_combine_ranks(int32_t T, int32_t H, int32_t R, const uint16_t* partial,
+                         int64_t cap_rank, const int32_t* token_rank_slot, uint16_t* out,
+                         float* out_f32);
 
 #ifdef __cplusplus
 }

@@ -530,6 +530,193 @@ def pin_combine_rounding_ties():
     assert list(out[:, 0]) == [0x3F80, 0x3F82, 0xBF80, 0x3F81], [hex(v) for v in out[:, 0]]
 
 
+def pin_combine_single_rounding():
+    """Each slot is one fused multiply-add (one rounding of w*y + acc), not a
+    rounded product added afterwards. Hand-derived: with y = 1 + 2^-7 (bf16
+    0x3F81) in both slots and w = -(1 + 2^-20), then 1 + 2^-20, the first
+    product -(1 + 2^-7 + 2^-20 + 2^-27) rounds to -(1 + 2^-7 + 2^-20); the
+    second fused step then leaves exactly 2^-27 (bf16 0x3200), where a
+    rounded product would cancel to 0."""
+    E, R, H = 4, 2, 8
+    ids = np.array([[0, 3]], np.int32)
+    y = np.full((1, 2, H), 0x3F81, np.uint16)
+    w = np.array([[-(1 + 2 ** -20), 1 + 2 ** -20]], np.float32)
+    lay = oracle.layout(ids, E, R)
+    eo = oracle.place_slots(y, lay["pair_row"], 2)
+    out, out32, _ = oracle.combine(eo, lay["pair_row"], w)
+    assert np.all(out32 == np.float32(2 ** -27)), out32
+    assert np.all(out == 0x3200)
+
+
+# ----------------------------------------------------------------------------
+# two-stage combine pins
+
+def _two_stage(ids, y, w, E, R, cap_rank=None, cap_expert=None):
+    T, k = ids.shape
+    lay = oracle.layout(ids, E, R)
+    cap_rank = T * min(k, R) if cap_rank is None else cap_rank
+    cap_expert = T * k if cap_expert is None else cap_expert
+    rb, src, _ = oracle.pack(np.zeros((T, 8), np.uint16), lay["token_rank_slot"], cap_rank)
+    eo = oracle.place_slots(y, lay["pair_row"], cap_expert)
+    part, part32, e1 = oracle.combine_rank_partial(eo, src, lay["rank_offsets"], ids,
+                                                   lay["pair_row"], w, E, cap_rank)
+    out, out32, e2 = oracle.combine_ranks(part, lay["token_rank_slot"])
+    return dict(lay=lay, src=src, eo=eo, part=part, part32=part32, out=out, out32=out32,
+                err=e1 | e2)
+
+
+def pin_two_stage_order():
+    """Hand-derived cases where the order of the float32 additions shows. Slot
+    order inside a rank: three experts of rank 0 in slots (e2, e0, e1) with
+    y = 2^-24, 2^-24, 1 (bf16 0x3380, 0x3380, 0x3F80) and w = 1 give
+    2^-24 -> 2^-23 -> 1 + 2^-23 in slot order (expert-id or reversed slot
+    order would give 1). Ascending rank order at home: partials 2^-24, 2^-24,
+    1 on ranks 0, 1, 2 reached in slot order (r2, r0, r1) give 1 + 2^-23
+    (slot order or descending ranks would give 1)."""
+    H = 8
+    tiny, one = 0x3380, 0x3F80
+    ids = np.array([[2, 0, 1]], np.int32)
+    y = np.array([[[tiny] * H, [tiny] * H, [one] * H]], np.uint16)
+    w = np.ones((1, 3), np.float32)
+    r = _two_stage(ids, y, w, E=6, R=2)
+    assert np.all(r["part32"][0] == np.float32(1 + 2 ** -23)), r["part32"][0]
+    y2 = np.array([[[one] * H, [tiny] * H, [tiny] * H]], np.uint16)
+    r2 = _two_stage(ids, y2, w, E=3, R=3)
+    assert np.all(r2["out32"][0] == np.float32(1 + 2 ** -23)), r2["out32"][0]
+    assert np.all(r2["out"][0] == one)  # 1 + 2^-23 rounds to bf16 1.0
+
+
+def pin_two_stage_single_rounding():
+    """The first stage is the same fused chain: the hand-derived case of
+    pin_combine_single_rounding with both experts on one rank leaves 2^-27
+    in the partial row, and the home sum of that single row is 2^-27."""
+    H = 8
+    ids = np.array([[0, 1]], np.int32)
+    y = np.full((1, 2, H), 0x3F81, np.uint16)
+    w = np.array([[-(1 + 2 ** -20), 1 + 2 ** -20]], np.float32)
+    r = _two_stage(ids, y, w, E=4, R=2)
+    assert np.all(r["part32"][0] == np.float32(2 ** -27))
+    assert np.all(r["part"][0] == 0x3200)
+    assert np.all(r["out"][0] == 0x3200)
+
+
+def pin_two_stage_exact_integers():
+    """Small integer outputs and weights in {-1, 1/2, 1, 2}: every partial and
+    every total is exact in float32 and in bf16, so each partial row must equal
+    the plain integer sum over its rank's slots and each output the sum over
+    all slots (checks which rows, slots and ranks take part)."""
+    rng = np.random.default_rng(91)
+    for T, E, R, k, H in [(40, 16, 4, 4, 8), (64, 64, 8, 8, 8), (30, 12, 2, 3, 16),
+                          (25, 8, 8, 5, 8)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.2)
+        yv = rng.integers(-4, 5, (T, k, H)).astype(np.float32)
+        y = (yv.view(np.uint32) >> 16).astype(np.uint16)  # small integers are exact bf16
+        w = rng.choice(np.array([-1, 0.5, 1, 2], np.float32), (T, k))
+        r = _two_stage(ids, y, w, E, R)
+        assert r["err"] == 0
+        m = E // R
+        ok = ids >= 0
+        want = np.einsum("tk,tkh->th", np.where(ok, w, 0).astype(np.float64), yv)
+        assert np.array_equal(r["out32"].astype(np.float64), want)
+        assert np.array_equal(bf16_bits_to_float(r["out"]).astype(np.float64), want)
+        slots = r["lay"]["token_rank_slot"]
+        for t in range(T):
+            for rk in range(R):
+                on = ok[t] & (ids[t] // m == rk)
+                if slots[t, rk] < 0:
+                    assert not on.any()
+                    continue
+                part = (w[t, on].astype(np.float64)[:, None] * yv[t, on]).sum(0)
+                assert np.array_equal(bf16_bits_to_float(r["part"][slots[t, rk]]), part)
+
+
+def pin_two_stage_one_expert_per_rank():
+    """With one expert per rank (E = R) each partial row is a single product:
+    bf16(fl32(w * y)), checked against numpy's float32 multiply and torch's
+    bfloat16 conversion (round to nearest even)."""
+    import torch
+
+    rng = np.random.default_rng(93)
+    for T, E, k, H in [(30, 8, 3, 16), (20, 4, 4, 8)]:
+        ids = rand_ids(rng, T, E, k)
+        y = synth.normal_bf16(13, 2, T * k * H).reshape(T, k, H)
+        w = (rng.standard_normal((T, k)) * 3).astype(np.float32)
+        r = _two_stage(ids, y, w, E, E)
+        prod = w[:, :, None] * bf16_bits_to_float(y)  # float32 * float32, one rounding
+        want = torch.from_numpy(np.ascontiguousarray(prod)).to(torch.bfloat16).view(
+            torch.int16).numpy().view(np.uint16)
+        slots = r["lay"]["token_rank_slot"]
+        for t in range(T):
+            for j in range(k):
+                s = slots[t, ids[t, j]]
+                assert np.array_equal(r["part32"][s], prod[t, j]), (t, j)
+                assert np.array_equal(r["part"][s], want[t, j]), (t, j)
+
+
+def pin_two_stage_one_rank():
+    """With a single rank the first stage is the whole fused chain in slot
+    order and the second stage adds one row to +0: the two-stage result equals
+    the one-stage combine bit for bit."""
+    rng = np.random.default_rng(95)
+    for T, E, k, H in [(50, 16, 4, 16), (37, 64, 8, 8)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1)
+        ids[:, 0] = rng.integers(0, E, T)
+        y = synth.normal_bf16(15, 2, T * k * H).reshape(T, k, H)
+        w = (rng.standard_normal((T, k))).astype(np.float32)
+        r = _two_stage(ids, y, w, E, 1)
+        out, out32, _ = oracle.combine(r["eo"], r["lay"]["pair_row"], w)
+        assert np.array_equal(r["src"], np.arange(T))
+        assert np.array_equal(r["part32"], out32)
+        assert np.array_equal(r["out"], out)
+
+
+def pin_two_stage_exact_bound():
+    """Against the exact rational sum: two-stage float32 result within
+    ((k + R) u + 2^-8) * 1.01 * sum|w*y| (u = 2^-24: a fused chain per rank, one
+    bf16 rounding of each partial, a chain of float32 adds over the ranks);
+    doubling every weight doubles every partial and output exactly."""
+    rng = np.random.default_rng(97)
+    for T, E, R, k, H in [(20, 16, 4, 6, 8), (16, 64, 8, 8, 8)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1)
+        y = synth.normal_bf16(17, 2, T * k * H).reshape(T, k, H)
+        w = (rng.standard_normal((T, k)) * 3).astype(np.float32)
+        r = _two_stage(ids, y, w, E, R)
+        yf = bf16_bits_to_float(y)
+        bound = ((k + R) * Fraction(1, 2 ** 24) + Fraction(1, 256)) * Fraction(101, 100)
+        for t in range(T):
+            for h in range(H):
+                terms = [Fraction(float(w[t, j])) * Fraction(float(yf[t, j, h]))
+                         for j in range(k) if ids[t, j] >= 0]
+                exact = sum(terms, Fraction(0))
+                mag = sum((abs(x) for x in terms), Fraction(0))
+                assert abs(Fraction(float(r["out32"][t, h])) - exact) <= bound * mag, (t, h)
+        r2 = _two_stage(ids, y, w * np.float32(2), E, R)
+        assert np.array_equal(r2["part32"], r["part32"] * np.float32(2))
+        assert np.array_equal(r2["out32"], r["out32"] * np.float32(2))
+
+
+def pin_two_stage_caps():
+    """Undersized buffers: a pair row past cap_expert contributes nothing (as a
+    zero weight would) and is reported; rank-buffer rows past cap_rank get no
+    partial and are reported by the home sum."""
+    rng = np.random.default_rng(99)
+    T, E, R, k, H = 40, 16, 4, 3, 8
+    ids = rand_ids(rng, T, E, k)
+    y = synth.normal_bf16(19, 2, T * k * H).reshape(T, k, H)
+    w = rng.random((T, k)).astype(np.float32)
+    full = _two_stage(ids, y, w, E, R)
+    P = T * k
+    r = _two_stage(ids, y, w, E, R, cap_expert=P - 4)
+    assert r["err"] == oracle.ERR_EXPERT_CAP
+    w0 = np.where(full["lay"]["pair_row"] >= P - 4, np.float32(0), w)
+    r0 = _two_stage(ids, y, w0, E, R)
+    assert np.array_equal(r["part32"], r0["part32"]) and np.array_equal(r["out"], r0["out"])
+    C = int(full["lay"]["rank_offsets"][-1])
+    rc = _two_stage(ids, y, w, E, R, cap_rank=C - 6)
+    assert rc["err"] == oracle.ERR_RANK_CAP
+    assert np.array_equal(rc["part32"], full["part32"][:C - 6])
+
+
 PINS = [
     pin_layout_stable_sort,
     pin_layout_brute_force,
@@ -549,4 +736,12 @@ PINS = [
     pin_combine_k1,
     pin_combine_exact_bound,
     pin_combine_rounding_ties,
+    pin_combine_single_rounding,
+    pin_two_stage_order,
+    pin_two_stage_single_rounding,
+    pin_two_stage_exact_integers,
+    pin_two_stage_one_expert_per_rank,
+    pin_two_stage_one_rank,
+    pin_two_stage_exact_bound,
+    pin_two_stage_caps,
 ]

@@ -42,14 +42,14 @@ MUTANTS = {
         "rank_src_token[row] = t;",
         "rank_src_token[row] = t + (r > 0);"),
     "permute wrong rank test": (
-        "if (!id_is_expert(e, E) || e / m != r) continue;",
-        "if (!id_is_expert(e, E)) continue;"),
+        "if (!id_is_expert(e, E) || e / m != r) continue;\n      const int64_t dst",
+        "if (!id_is_expert(e, E)) continue;\n      const int64_t dst"),
     "permute wrong pair id": (
         "expert_src_pair[dst] = t * k + j;",
         "expert_src_pair[dst] = t * k;"),
     "combine reversed weights": (
-        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);",
-        "acc = fmaf(topk_weights[(int64_t)t * k + (k - 1 - j)], widen_bf16(expert_out[row * H + h]), acc);"),
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);\n      }\n      out[",
+        "acc = fmaf(topk_weights[(int64_t)t * k + (k - 1 - j)], widen_bf16(expert_out[row * H + h]), acc);\n      }\n      out["),
     "combine drops last slot": (
         "      float acc = 0.0f;\n      for (int32_t j = 0; j < k; ++j) {",
         "      float acc = 0.0f;\n      for (int32_t j = 0; j < k - 1; ++j) {"),
@@ -63,8 +63,35 @@ MUTANTS = {
         "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;",
         "if (lower >= 0x8000u) upper += 1u;"),
     "combine squares weight": (
-        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);",
-        "acc = fmaf(topk_weights[(int64_t)t * k + j] * topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);"),
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);\n      }\n      out[",
+        "acc = fmaf(topk_weights[(int64_t)t * k + j] * topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);\n      }\n      out["),
+    "combine rounds the product first": (
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);\n      }\n      out[",
+        "acc = acc + topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]);\n      }\n      out["),
+    "partial ignores the rank": (
+        "if (!id_is_expert(e, E) || e / m != r) continue; /* not an expert of rank r */",
+        "if (!id_is_expert(e, E)) continue; /* not an expert of rank r */"),
+    "partial rounds the product first": (
+        "acc = fmaf(topk_weights[(int64_t)t * k + j], widen_bf16(expert_out[row * H + h]), acc);\n        }\n        partial",
+        "acc = acc + topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]);\n        }\n        partial"),
+    "partial walks slots backwards": (
+        "for (int32_t j = 0; j < k; ++j) {\n          const int32_t e = topk_ids[(int64_t)t * k + j];\n          if (!id_is_expert(e, E) || e / m != r) continue; /* not",
+        "for (int32_t j = k - 1; j >= 0; --j) {\n          const int32_t e = topk_ids[(int64_t)t * k + j];\n          if (!id_is_expert(e, E) || e / m != r) continue; /* not"),
+    "partial segment starts one late": (
+        "int64_t lo = rank_offsets[r], hi = rank_offsets[r + 1];",
+        "int64_t lo = rank_offsets[r] + 1, hi = rank_offsets[r + 1];"),
+    "partial ignores the expert cap": (
+        "          if (row >= cap_expert) {\n            err |= ORACLE_ERR_EXPERT_CAP;\n            continue;\n          }\n          acc = fmaf(",
+        "          if (row >= cap_expert + 1000000) {\n            err |= ORACLE_ERR_EXPERT_CAP;\n            continue;\n          }\n          acc = fmaf("),
+    "home sum walks ranks backwards": (
+        "for (int32_t r = 0; r < R; ++r) {\n        const int64_t s = token_rank_slot",
+        "for (int32_t r = R - 1; r >= 0; --r) {\n        const int64_t s = token_rank_slot"),
+    "home sum drops the last rank": (
+        "for (int32_t r = 0; r < R; ++r) {\n        const int64_t s = token_rank_slot",
+        "for (int32_t r = 0; r < R - 1; ++r) {\n        const int64_t s = token_rank_slot"),
+    "home sum ignores the rank cap": (
+        "        if (s >= cap_rank) {\n          err |= ORACLE_ERR_RANK_CAP;",
+        "        if (s >= cap_rank + 1000000) {\n          err |= ORACLE_ERR_RANK_CAP;"),
     "f64 combine rounds products to float": (
         "acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);",
         "acc += (double)(topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]));"),
