@@ -35,6 +35,7 @@ METRIC = "dispatch+combine GB/s and % HBM peak, T=4096 H=5120 E=384 top-6 R=8"
 KERNEL_SOURCE = os.path.join(ROOT, "combine_topk_ids_02_amd", "csrc", "moe_dispatch.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CALLS = ("layout", "pack", "permute", "combine")
+TWO_STAGE_CALLS = ("partial", "ranks")
 
 
 def algorithmic_bytes(T, H, E, R, k, C, P):
@@ -46,6 +47,18 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
         "pack": T * row + C * row + 4 * T * R + 4 * C,
         "permute": C * row + P * row + 4 * C + 8 * T * k + 4 * P,
         "combine": P * row + T * row + 8 * T * k,
+    }
+
+
+def two_stage_bytes(T, H, R, k, C, P):
+    """Bytes of the two-stage combine: the per-rank partial rows (each expert
+    row read once, each partial row written once, the token's ids, pair rows
+    and weights read once) and the home sum (each partial row read once, each
+    output row written once, the slots read once)."""
+    row = 2 * H
+    return {
+        "partial": P * row + C * row + 4 * C + 12 * T * k + 4 * (R + 1),
+        "ranks": C * row + T * row + 4 * T * R,
     }
 
 
@@ -205,7 +218,7 @@ class Rig:
     """One workload resident on the GPU with every buffer of a pass, and the
     four library calls on the current stream."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, two_stage: bool = False):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -231,6 +244,13 @@ class Rig:
         self.P = int(self.buf.expert_offsets[-1].item())
         self.nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P)
         self.stream = torch.cuda.current_stream(dev)
+        self.calls = CALLS
+        if two_stage:
+            self.partial = torch.empty((self.shape.cap_rank, w.H), dtype=torch.bfloat16,
+                                       device=dev)
+            self.out2 = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+            self.nbytes.update(two_stage_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
+            self.calls = CALLS + TWO_STAGE_CALLS
 
     def call(self, name: str) -> None:
         moe, s, b = self.moe, self.shape, self.buf
@@ -242,14 +262,20 @@ class Rig:
         elif name == "permute":
             moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
                         s.E, b.expert_buf, b.expert_src_pair, err=b.err)
-        else:
+        elif name == "combine":
             moe.combine(self.expert_out, b.pair_row, self.wts_d, s.E, s.R, b.out, err=b.err)
+        elif name == "partial":
+            moe.combine_rank_partial(self.expert_out, b.rank_src_token, b.rank_offsets,
+                                     self.ids_d, b.pair_row, self.wts_d, s.E, self.partial,
+                                     err=b.err)
+        else:
+            moe.combine_ranks(self.partial, b.token_rank_slot, s.E, s.k, self.out2, err=b.err)
 
     def step(self, ev=None, flush=None) -> None:
         """One pass; with `ev` (5 events) records between the calls; with
         `flush` (a large tensor) overwrites it before every call, outside the
         events."""
-        for i, c in enumerate(CALLS):
+        for i, c in enumerate(self.calls):
             if flush is not None:
                 flush.fill_(i + 1)
             if ev is not None:
@@ -258,21 +284,22 @@ class Rig:
             if ev is not None and flush is not None:
                 ev[2 * i + 1].record(self.stream)
         if ev is not None and flush is None:
-            ev[len(CALLS)].record(self.stream)
+            ev[len(self.calls)].record(self.stream)
 
     def per_call_ms(self, n: int, flush=None) -> dict:
         """Per-call durations (ms) over n steps."""
         import torch
 
-        nev = 2 * len(CALLS) if flush is not None else len(CALLS) + 1
+        nc = len(self.calls)
+        nev = 2 * nc if flush is not None else nc + 1
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
             self.step(evs[i], flush)
         torch.cuda.synchronize()
-        out = {c: [] for c in CALLS}
+        out = {c: [] for c in self.calls}
         for ev in evs:
-            for j, c in enumerate(CALLS):
+            for j, c in enumerate(self.calls):
                 a, b = (ev[2 * j], ev[2 * j + 1]) if flush is not None else (ev[j], ev[j + 1])
                 out[c].append(a.elapsed_time(b))
         return out
@@ -320,18 +347,18 @@ def sweep(names, dev, with_oracle: bool) -> None:
     rows = []
     for name in names:
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev)
+        rig = Rig(w, dev, two_stage=True)
         for _ in range(5):
             rig.step()
         res = {"workload": w.describe(), "C": rig.C, "P": rig.P,
                "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
         for mode, fl in (("warm", None), ("cold", flush)):
-            meds = {c: [] for c in CALLS}
+            meds = {c: [] for c in rig.calls}
             for _ in range(3):
                 ms = rig.per_call_ms(30, fl)
-                for c in CALLS:
+                for c in rig.calls:
                     meds[c].append(float(np.median(ms[c])))
-            for c in CALLS:
+            for c in rig.calls:
                 us = float(np.median(meds[c])) * 1e3
                 ent = res["calls"].setdefault(c, {"bytes": rig.nbytes[c]})
                 ent[mode] = {"us": round(us, 2),
@@ -340,13 +367,19 @@ def sweep(names, dev, with_oracle: bool) -> None:
                              "GB/s": round(rig.nbytes[c] / (us * 1e-6) / 1e9, 1)}
                 ent[mode]["pct_peak"] = round(100 * ent[mode]["GB/s"] / HBM_PEAK_GBS, 1)
             log(f"{name} {mode}: " + ", ".join(
-                f"{c} {res['calls'][c][mode]['us']} us" for c in CALLS))
+                f"{c} {res['calls'][c][mode]['us']} us" for c in rig.calls))
         rig.check_err()
-        tot = sum(rig.nbytes.values())
+        tot = sum(rig.nbytes[c] for c in CALLS)
+        path2 = ("layout", "pack", "permute") + TWO_STAGE_CALLS
+        tot2 = sum(rig.nbytes[c] for c in path2)
         for mode in ("warm", "cold"):
             us = sum(res["calls"][c][mode]["us"] for c in CALLS)
             res[mode] = {"us": round(us, 2), "GB/s": round(tot / (us * 1e-6) / 1e9, 1),
                          "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+            us2 = sum(res["calls"][c][mode]["us"] for c in path2)
+            res["two_stage_" + mode] = {
+                "us": round(us2, 2), "GB/s": round(tot2 / (us2 * 1e-6) / 1e9, 1),
+                "pct_peak": round(100 * tot2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
         warm = res["calls"]
         res["rows_per_s"] = {
             "pack_copies": round(rig.C / (warm["pack"]["warm"]["us"] * 1e-6)),
@@ -354,6 +387,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
             "combine_tokens": round(w.T / (warm["combine"]["warm"]["us"] * 1e-6)),
             "combine_pairs": round(rig.P / (warm["combine"]["warm"]["us"] * 1e-6))}
         res["bytes"] = tot
+        res["two_stage_bytes"] = tot2
         if with_oracle:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
@@ -372,6 +406,17 @@ def sweep(names, dev, with_oracle: bool) -> None:
             print(f"| {name} | {mode} | " + " | ".join(
                 str(r["calls"][c][mode]["us"]) for c in CALLS) +
                 f" | {r[mode]['us']} | {r[mode]['GB/s']} | {r[mode]['pct_peak']} | {orc} |")
+    print("\nTwo-stage combine (per-rank partial rows, then the home sum), and the whole path "
+          "with it in place of the one-stage combine:\n")
+    print("| workload | mode | partial us | partial GB/s | ranks us | ranks GB/s | path us "
+          "| path GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, r in rows:
+        for mode in ("warm", "cold"):
+            a, b, p = r["calls"]["partial"][mode], r["calls"]["ranks"][mode], \
+                r["two_stage_" + mode]
+            print(f"| {name} | {mode} | {a['us']} | {a['GB/s']} | {b['us']} | {b['GB/s']} "
+                  f"| {p['us']} | {p['GB/s']} | {p['pct_peak']} |")
     print(f"\n1 GiB device copy: {copy['us']} us, {copy['GB/s']} GB/s (read + write)")
 
 

@@ -26,7 +26,8 @@ ERRBIT_RANK_CAP = 2
 ERRBIT_EXPERT_CAP = 4
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout", "moe_dispatch_pack",
-           "moe_permute_by_expert", "moe_combine")
+           "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
+           "moe_combine_ranks")
 
 
 class MoeShape(ctypes.Structure):
@@ -66,6 +67,10 @@ def lib():
     L.moe_permute_by_expert.argtypes = [shp, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [shp, vp, vp, vp, i64, vp, vp, vp, vp]
+    L.moe_combine_rank_partial.restype = ctypes.c_int
+    L.moe_combine_rank_partial.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
+    L.moe_combine_ranks.restype = ctypes.c_int
+    L.moe_combine_ranks.argtypes = [shp, vp, vp, i64, vp, vp, vp, vp]
     _lib = L
     return L
 
@@ -191,6 +196,40 @@ def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=
         _ptr(topk_weights), expert_out.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err),
         _stream(out.device))
     _check(st, "moe_combine")
+
+
+def combine_rank_partial(expert_out, rank_src_token, rank_offsets, topk_ids, pair_row,
+                         topk_weights, E: int, partial, *, partial_f32=None, err=None) -> None:
+    """moe_combine_rank_partial: one bf16 partial row per rank-buffer row into
+    caller-provided partial [cap_rank, H] (and optionally partial_f32)."""
+    T, k = topk_ids.shape
+    H = partial.shape[1]
+    R = rank_offsets.shape[0] - 1
+    if topk_weights.dtype != torch.float32:
+        raise MoeError("topk_weights must be float32")
+    if partial_f32 is not None and partial_f32.dtype != torch.float32:
+        raise MoeError("partial_f32 must be float32")
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_combine_rank_partial(
+        ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(rank_src_token)),
+        _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)), _ptr(_i32(pair_row)),
+        _ptr(topk_weights), expert_out.shape[0], partial.shape[0], _ptr(_rows16(partial)),
+        _ptr(partial_f32), _ptr(err), _stream(partial.device))
+    _check(st, "moe_combine_rank_partial")
+
+
+def combine_ranks(partial, token_rank_slot, E: int, k: int, out, *, out_f32=None,
+                  err=None) -> None:
+    """moe_combine_ranks: out [T, H] = sum over ranks of the token's partial rows."""
+    T, R = token_rank_slot.shape
+    H = out.shape[1]
+    if out_f32 is not None and out_f32.dtype != torch.float32:
+        raise MoeError("out_f32 must be float32")
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_combine_ranks(
+        ctypes.byref(shape.c()), _ptr(_rows16(partial)), _ptr(_i32(token_rank_slot)),
+        partial.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err), _stream(out.device))
+    _check(st, "moe_combine_ranks")
 
 
 class Buffers:

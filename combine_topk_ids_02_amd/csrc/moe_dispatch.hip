@@ -20,6 +20,9 @@
 //  combine_rows  one wave per (token, column slice): k row gathers, fp32 FMA
 //                in slot order, bf16 round-to-nearest-even ([A2A] sec 1.1,
 //                7.1; [GPUs] sec 3.3 fixed addition order)
+//  rank_partial_rows / rank_sum_rows  the two-stage combine of [A2A] sec 7.1:
+//                one bf16 partial row per (token, rank) copy, then the sum of
+//                a token's partial rows at home in rank order
 // Rows move 16 bytes per lane (global_load/store_dwordx4), 1 KiB per wave
 // instruction. Cache policy per stream, chosen by measurement of the whole
 // layout -> pack -> permute -> combine sequence: the packed rows are written
@@ -594,13 +597,14 @@ __device__ __forceinline__ void fma_bf16x8(float (&acc)[8], float w, vec4 y) {
   }
 }
 
+template <bool kStream>
 __device__ __forceinline__ void store_sum(const float (&acc)[8], vec4* out, vec4* out_f32,
                                           int64_t at) {
   vec4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-  store_row<true>(out + at, o);
+  store_row<kStream>(out + at, o);
   if (out_f32) {
     vec4 a, b;
 #pragma unroll
@@ -608,14 +612,74 @@ __device__ __forceinline__ void store_sum(const float (&acc)[8], vec4* out, vec4
       a[i] = __float_as_uint(acc[i]);
       b[i] = __float_as_uint(acc[4 + i]);
     }
-    store_row<true>(out_f32 + 2 * at, a);
-    store_row<true>(out_f32 + 2 * at + 1, b);
+    store_row<kStream>(out_f32 + 2 * at, a);
+    store_row<kStream>(out_f32 + 2 * at + 1, b);
   }
 }
 
-// One wave per (token, column slice of 64*V vec4). Slots are walked in
-// ascending order; the next slot's row is loaded while the current one is
-// accumulated.
+// Weighted sum of rows for one column slice, in a fixed order. Lane j holds
+// term j: the row it reads (src_row) and its weight (wt); the terms taken are
+// the lanes in `terms`, in ascending lane order, each one fused multiply-add
+// into float32 accumulators that start at +0. Columns [cb, cb + 64*V) of the
+// sum go to row `orow` of out (bf16, round to nearest even) and of out_f32.
+// The next term's rows are loaded while the current one is accumulated.
+template <int V, bool kStreamLoad, bool kStreamStore>
+__device__ __forceinline__ void weighted_row_sum(const vec4* rows, int src_row, float wt,
+                                                 uint64_t terms, vec4* out, vec4* out_f32,
+                                                 int64_t orow, int cb, int nvec) {
+  const int lane = lane_id();
+  if (cb + kWave * V <= nvec) {
+    float acc[V][8];
+#pragma unroll
+    for (int q = 0; q < V; ++q)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[q][x] = 0.0f;
+    uint64_t s = terms;
+    if (s) {
+      int j = __ffsll((unsigned long long)s) - 1;
+      s &= s - 1;
+      vec4 y[V];
+      const vec4* src = rows + (int64_t)read_lane(src_row, j) * nvec + cb + lane;
+#pragma unroll
+      for (int q = 0; q < V; ++q) y[q] = load_row<kStreamLoad>(src + q * kWave);
+      while (s) {
+        const int jn = __ffsll((unsigned long long)s) - 1;
+        s &= s - 1;
+        vec4 yn[V];
+        const vec4* srcn = rows + (int64_t)read_lane(src_row, jn) * nvec + cb + lane;
+#pragma unroll
+        for (int q = 0; q < V; ++q) yn[q] = load_row<kStreamLoad>(srcn + q * kWave);
+        const float w = __int_as_float(read_lane(__float_as_int(wt), j));
+#pragma unroll
+        for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
+#pragma unroll
+        for (int q = 0; q < V; ++q) y[q] = yn[q];
+        j = jn;
+      }
+      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
+#pragma unroll
+      for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < V; ++q)
+      store_sum<kStreamStore>(acc[q], out, out_f32, orow + cb + q * kWave + lane);
+    return;
+  }
+  // Partial slice at the end of the row: one vec4 per lane at a time.
+  for (int c = cb + lane; c < nvec; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint64_t s = terms;
+    while (s) {
+      const int j = __ffsll((unsigned long long)s) - 1;
+      s &= s - 1;
+      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
+      fma_bf16x8(acc, w, load_row<kStreamLoad>(rows + (int64_t)read_lane(src_row, j) * nvec + c));
+    }
+    store_sum<kStreamStore>(acc, out, out_f32, orow + c);
+  }
+}
+
+// Combine: one wave per (token, column slice of 64*V vec4); term j is slot j.
 template <int V>
 __global__ __launch_bounds__(kBlock) void combine_rows(
     const vec4* expert_out, const int32_t* __restrict__ pair_row,
@@ -631,58 +695,60 @@ __global__ __launch_bounds__(kBlock) void combine_rows(
   const bool ok = p >= 0 && p < cap_expert;
   if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
     flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
-  const uint64_t slots = __ballot(ok);
-  const int cb = slice * kWave * V;
-  const int64_t orow = (int64_t)t * nvec;
+  weighted_row_sum<V, false, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
+                                   (int64_t)t * nvec, slice * kWave * V, nvec);
+}
 
-  if (cb + kWave * V <= nvec) {
-    float acc[V][8];
-#pragma unroll
-    for (int q = 0; q < V; ++q)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc[q][x] = 0.0f;
-    uint64_t s = slots;
-    if (s) {
-      int j = __ffsll((unsigned long long)s) - 1;
-      s &= s - 1;
-      vec4 y[V];
-      const vec4* src = expert_out + (int64_t)read_lane(p, j) * nvec + cb + lane;
-#pragma unroll
-      for (int q = 0; q < V; ++q) y[q] = src[q * kWave];
-      while (s) {
-        const int jn = __ffsll((unsigned long long)s) - 1;
-        s &= s - 1;
-        vec4 yn[V];
-        const vec4* srcn = expert_out + (int64_t)read_lane(p, jn) * nvec + cb + lane;
-#pragma unroll
-        for (int q = 0; q < V; ++q) yn[q] = srcn[q * kWave];
-        const float w = __int_as_float(read_lane(__float_as_int(wt), j));
-#pragma unroll
-        for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
-#pragma unroll
-        for (int q = 0; q < V; ++q) y[q] = yn[q];
-        j = jn;
-      }
-      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
-#pragma unroll
-      for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < V; ++q) store_sum(acc[q], out, out_f32, orow + cb + q * kWave + lane);
-    return;
-  }
-  // Partial slice at the end of the row: one vec4 per lane at a time.
-  for (int c = cb + lane; c < nvec; c += kWave) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    uint64_t s = slots;
-    while (s) {
-      const int j = __ffsll((unsigned long long)s) - 1;
-      s &= s - 1;
-      const float w = __int_as_float(read_lane(__float_as_int(wt), j));
-      fma_bf16x8(acc, w, expert_out[(int64_t)read_lane(p, j) * nvec + c]);
-    }
-    store_sum(acc, out, out_f32, orow + c);
-  }
+// Two-stage combine, first stage: one wave per (rank-buffer row, column
+// slice). Row i of rank r's segment holds token t; its terms are the slots j
+// of t whose expert lives on r. The partial rows are stored with ordinary
+// stores so that the home sum finds them in the Infinity Cache.
+template <int V>
+__global__ __launch_bounds__(kBlock) void rank_partial_rows(
+    const vec4* expert_out, const int32_t* __restrict__ rank_src_token,
+    const int32_t* __restrict__ rank_offsets, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ pair_row, const float* __restrict__ weights, vec4* partial,
+    vec4* partial_f32, int T, int E, int R, int k, int m, int nvec, int slices,
+    int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t i = gw / slices;
+  const int slice = int(gw - i * slices);
+  const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
+  if (i >= rows) return;
+  const int end = lane < R ? rank_offsets[lane + 1] : 0x7FFFFFFF;
+  const int r = __popcll(__ballot(lane < R && end <= i));
+  const int t = rank_src_token[i];
+  if (t < 0 || t >= T) return;
+  const int e = lane < k ? ids[(int64_t)t * k + lane] : -1;
+  const bool here = e >= 0 && e < E && e / m == r;
+  const int p = here ? pair_row[(int64_t)t * k + lane] : -1;
+  const float wt = here ? weights[(int64_t)t * k + lane] : 0.0f;
+  const bool ok = p >= 0 && p < cap_expert;
+  if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
+    flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+  weighted_row_sum<V, false, false>(expert_out, p, wt, __ballot(ok), partial, partial_f32,
+                                    i * nvec, slice * kWave * V, nvec);
+}
+
+// Two-stage combine, second stage: one wave per (token, column slice); term r
+// is the token's partial row on rank r, weight 1 (a fused multiply-add by 1 is
+// the plain float32 addition).
+template <int V>
+__global__ __launch_bounds__(kBlock) void rank_sum_rows(
+    const vec4* partial, const int32_t* __restrict__ token_rank_slot, vec4* out,
+    vec4* out_f32, int T, int R, int nvec, int slices, int64_t cap_rank, int32_t* err_word) {
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = int(gw / slices);
+  const int slice = int(gw - (int64_t)t * slices);
+  if (t >= T) return;
+  const int s = lane < R ? token_rank_slot[(int64_t)t * R + lane] : -1;
+  const bool ok = s >= 0 && s < cap_rank;
+  if (slice == 0 && __ballot(s >= 0 && !ok) && lane == 0)
+    flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+  weighted_row_sum<V, true, true>(partial, s, 1.0f, __ballot(ok), out, out_f32,
+                                  (int64_t)t * nvec, slice * kWave * V, nvec);
 }
 
 // ---------------------------------------------------------------------------
@@ -774,6 +840,27 @@ struct CombineLaunch {
   }
 };
 
+template <int V>
+struct RankPartialLaunch {
+  static void go(dim3 grid, hipStream_t st, const vec4* eo, const int32_t* src,
+                 const int32_t* roff, const int32_t* ids, const int32_t* prow, const float* w,
+                 vec4* part, vec4* part32, int T, int E, int R, int k, int m, int nvec,
+                 int slices, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
+    hipLaunchKernelGGL(rank_partial_rows<V>, grid, dim3(kBlock), 0, st, eo, src, roff, ids, prow,
+                       w, part, part32, T, E, R, k, m, nvec, slices, cap_rank, cap_expert, err);
+  }
+};
+
+template <int V>
+struct RankSumLaunch {
+  static void go(dim3 grid, hipStream_t st, const vec4* part, const int32_t* slots, vec4* out,
+                 vec4* out32, int T, int R, int nvec, int slices, int64_t cap_rank,
+                 int32_t* err) {
+    hipLaunchKernelGGL(rank_sum_rows<V>, grid, dim3(kBlock), 0, st, part, slots, out, out32, T,
+                       R, nvec, slices, cap_rank, err);
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -858,6 +945,52 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
                             reinterpret_cast<const vec4*>(expert_out), pair_row, topk_weights,
                             reinterpret_cast<vec4*>(out), reinterpret_cast<vec4*>(out_f32),
                             shape->T, shape->k, nvec, slices, cap_expert, err_word);
+  return launch_status();
+}
+
+int moe_combine_rank_partial(const moe_shape_t* shape, const uint16_t* expert_out,
+                             const int32_t* rank_src_token, const int32_t* rank_offsets,
+                             const int32_t* topk_ids, const int32_t* pair_row,
+                             const float* topk_weights, int64_t cap_expert, int64_t cap_rank,
+                             uint16_t* partial, float* partial_f32, int32_t* err_word,
+                             void* stream) {
+  if (!shape_ok(shape) || cap_rank < 0 || cap_expert < 0) return MOE_ERR_ARG;
+  if (!rank_offsets) return MOE_ERR_ARG;
+  const int64_t max_rows =
+      std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
+  if (shape->T == 0 || max_rows == 0) return MOE_OK;
+  if (!rank_src_token || !topk_ids || !pair_row || !topk_weights || !partial ||
+      (cap_expert > 0 && !expert_out))
+    return MOE_ERR_ARG;
+  if (!aligned16(expert_out) || !aligned16(partial) || !aligned16(partial_f32))
+    return MOE_ERR_ARG;
+  const int nvec = shape->H / 8;
+  int v = 1, slices = 1;
+  combine_tiling(nvec, &v, &slices);
+  ByVec<RankPartialLaunch>::run(
+      v, dim3(blocks_for(max_rows * slices)), static_cast<hipStream_t>(stream),
+      reinterpret_cast<const vec4*>(expert_out), rank_src_token, rank_offsets, topk_ids, pair_row,
+      topk_weights, reinterpret_cast<vec4*>(partial), reinterpret_cast<vec4*>(partial_f32),
+      shape->T, shape->E, shape->R, shape->k, shape->E / shape->R, nvec, slices, cap_rank,
+      cap_expert, err_word);
+  return launch_status();
+}
+
+int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
+                      const int32_t* token_rank_slot, int64_t cap_rank, uint16_t* out,
+                      float* out_f32, int32_t* err_word, void* stream) {
+  if (!shape_ok(shape) || cap_rank < 0) return MOE_ERR_ARG;
+  if (shape->T == 0) return MOE_OK;
+  if (!token_rank_slot || !out || (cap_rank > 0 && !partial)) return MOE_ERR_ARG;
+  if (!aligned16(partial) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
+  const int nvec = shape->H / 8;
+  int v = 1, slices = 1;
+  combine_tiling(nvec, &v, &slices);
+  ByVec<RankSumLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
+                            static_cast<hipStream_t>(stream),
+                            reinterpret_cast<const vec4*>(partial), token_rank_slot,
+                            reinterpret_cast<vec4*>(out), reinterpret_cast<vec4*>(out_f32),
+                            shape->T, shape->R, nvec, slices, cap_rank, err_word);
   return launch_status();
 }
 

@@ -159,6 +159,47 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
                 const float* topk_weights, int64_t cap_expert, uint16_t* out, float* out_f32,
                 int32_t* err_word, void* stream);
 
+/*
+ * Two-stage combine, first stage: per-rank pre-add ([A2A] sec 7.1: a token's
+ * weighted sum splits into a sum over the experts that sit on one GPU and a
+ * sum over the GPUs; with the layout by expert the first stage runs on the
+ * expert's GPU, so one row per GPU travels back instead of one per expert, and
+ * what travels back is 16-bit).
+ * For every rank-buffer row i < min(rank_offsets[R], cap_rank), in the segment
+ * of rank r and holding token t = rank_src_token[i]:
+ *   acc = +0.0f, then for j = 0..k-1 in order whose expert lives on rank r and
+ *   whose row = pair_row[t*k+j] is in [0, cap_expert):
+ *   acc = fmaf(topk_weights[t*k+j], float(expert_out[row][h]), acc);
+ *   partial[i][h] = bf16_rne(acc); partial_f32[i][h] = acc.
+ *   expert_out [cap_expert*H], rank_src_token [cap_rank], rank_offsets [R+1],
+ *   topk_ids [T*k], pair_row [T*k], topk_weights [T*k]       in
+ *   partial [cap_rank*H] out: bf16; partial_f32 [cap_rank*H] out: float32, or NULL
+ *   Pair rows at or past cap_expert are skipped and flagged (MOE_ERRBIT_EXPERT_CAP).
+ *   Rows past C are left untouched.
+ */
+int moe_combine_rank_partial(const moe_shape_t* shape, const uint16_t* expert_out,
+                             const int32_t* rank_src_token, const int32_t* rank_offsets,
+                             const int32_t* topk_ids, const int32_t* pair_row,
+                             const float* topk_weights, int64_t cap_expert, int64_t cap_rank,
+                             uint16_t* partial, float* partial_f32, int32_t* err_word,
+                             void* stream);
+
+/*
+ * Two-stage combine, second stage at the token's home ([A2A] sec 7.1: the home
+ * GPU adds up the one row per GPU that it receives, in 32-bit floats).
+ *   out[t][h] = bf16_rne(acc), acc = +0.0f then, for r = 0..R-1 in order with
+ *   s = token_rank_slot[t*R+r] in [0, cap_rank): acc = acc + float(partial[s][h]).
+ *   partial [cap_rank*H] in: bf16 rows from moe_combine_rank_partial
+ *   token_rank_slot [T*R] in: from moe_dispatch_layout
+ *   out [T*H] out: bf16; out_f32 [T*H] out: the float32 sums, or NULL
+ *   Slots at or past cap_rank are skipped and flagged (MOE_ERRBIT_RANK_CAP).
+ * The result differs from moe_combine's by the bf16 rounding of each partial
+ * row (relative 2^-8 of that row at most) and the changed addition order.
+ */
+int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
+                      const int32_t* token_rank_slot, int64_t cap_rank, uint16_t* out,
+                      float* out_f32, int32_t* err_word, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,3 +140,72 @@ def relative_error_vs_exact(out_f32, expert_out, pair_row, wts) -> float:
     with np.errstate(invalid="ignore", divide="ignore"):
         rel = np.where(den > 0, num / den, num)
     return float(rel.max(initial=0.0))
+
+
+def run_gpu_two_stage(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
+                      y_slots: np.ndarray, cap_rank: int | None = None,
+                      cap_expert: int | None = None, spare_rows: int = 4,
+                      device="cuda:0") -> dict:
+    """Layout and pack (for the rank-buffer bookkeeping), the expert outputs
+    placed at their pair rows, then the two-stage combine through the C ABI.
+    The partial buffers get `spare_rows` canary rows past cap_rank."""
+    T, H = hid.shape
+    k = ids.shape[1]
+    shape = moe.Shape(T, H, E, R, k)
+    cap_rank = shape.cap_rank if cap_rank is None else cap_rank
+    cap_expert = shape.cap_expert if cap_expert is None else cap_expert
+    dev = torch.device(device)
+    i32 = torch.int32
+    hid_d = staging.rows_to_device(hid, dev)
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+    wts_d = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).to(dev)
+    err = torch.zeros(1, dtype=i32, device=dev)
+    lay = moe.layout(ids_d, E, R, H, err=err)
+    rank_buf = torch.empty((cap_rank, H), dtype=torch.int16, device=dev)
+    rank_src = torch.full((cap_rank,), CANARY_IDX, dtype=i32, device=dev)
+    moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
+    expert_out = staging.place_expert_outputs(staging.rows_to_device(y_slots, dev),
+                                              lay["pair_row"], cap_expert)
+    canary = torch.tensor(CANARY_ROW, dtype=torch.int32).to(torch.int16).item()
+    part_all = torch.full((cap_rank + spare_rows, H), canary, dtype=torch.int16, device=dev)
+    part32_all = torch.full((cap_rank + spare_rows, H), float("nan"), dtype=torch.float32,
+                            device=dev)
+    moe.combine_rank_partial(expert_out, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"],
+                             wts_d, E, part_all[:cap_rank], partial_f32=part32_all[:cap_rank],
+                             err=err)
+    out = torch.full((T, H), canary, dtype=torch.int16, device=dev)
+    out32 = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    moe.combine_ranks(part_all[:cap_rank], lay["token_rank_slot"], E, k, out, out_f32=out32,
+                      err=err)
+    torch.cuda.synchronize(dev)
+    return dict(rank_offsets=lay["rank_offsets"].cpu().numpy(),
+                part_all=staging.rows_to_host(part_all), part32_all=part32_all.cpu().numpy(),
+                out=staging.rows_to_host(out), out_f32=out32.cpu().numpy(),
+                err=int(err.item()), cap_rank=cap_rank, cap_expert=cap_expert)
+
+
+def run_oracle_two_stage(hid, ids, wts, E, R, y_slots, cap_rank, cap_expert) -> dict:
+    lay = oracle.layout(ids, E, R)
+    _, src, e1 = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
+    eo = oracle.place_slots(y_slots, lay["pair_row"], cap_expert)
+    part, part32, e2 = oracle.combine_rank_partial(eo, src, lay["rank_offsets"], ids,
+                                                   lay["pair_row"], wts, E, cap_rank)
+    out, out32, e3 = oracle.combine_ranks(part, lay["token_rank_slot"])
+    return dict(layout=lay, expert_out=eo, part=part, part32=part32, out=out, out_f32=out32,
+                err=lay["err"] | e1 | e2 | e3)
+
+
+def compare_two_stage(gpu: dict, ref: dict, what: str) -> None:
+    assert gpu["err"] == ref["err"], f"{what}: error word {gpu['err']} vs oracle {ref['err']}"
+    C = int(ref["layout"]["rank_offsets"][-1])
+    wr = min(C, gpu["cap_rank"])
+    assert np.array_equal(gpu["part_all"][:wr], ref["part"][:wr]), f"{what}: partial rows"
+    assert np.array_equal(gpu["part32_all"][:wr].view(np.uint32),
+                          ref["part32"][:wr].view(np.uint32)), f"{what}: partial fp32 rows"
+    assert np.all(gpu["part_all"][wr:] == CANARY_ROW), f"{what}: partial rows past C written"
+    assert np.all(np.isnan(gpu["part32_all"][wr:])), f"{what}: fp32 partial rows past C written"
+    ulp = bf16_ulp_distance(gpu["out"], ref["out"])
+    assert ulp.max(initial=0) <= 1, f"{what}: two-stage bf16 differs by {ulp.max()} ulp"
+    assert np.array_equal(gpu["out"], ref["out"]), f"{what}: two-stage bf16 not bit-exact"
+    assert np.array_equal(gpu["out_f32"].view(np.uint32), ref["out_f32"].view(np.uint32)), \
+        f"{what}: two-stage fp32 not bit-exact"

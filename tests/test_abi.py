@@ -50,6 +50,9 @@ def test_calls_reject_bad_shapes(bad):
                                  None) == moe.MOE_ERR_ARG
     assert L.moe_dispatch_pack(sp, FAKE, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
     assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_rank_partial(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, FAKE,
+                                      None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_ranks(sp, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
 
 
 def test_calls_reject_bad_arguments_without_launching():
@@ -78,6 +81,19 @@ def test_calls_reject_bad_arguments_without_launching():
     assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, ctypes.c_void_p(0x10002), None,
                          None) == moe.MOE_ERR_ARG
     assert L.moe_combine(bad, FAKE, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
+    # two-stage combine: NULL offsets / partial / slots, misaligned rows, negative caps
+    assert L.moe_combine_rank_partial(sp, FAKE, FAKE, None, FAKE, FAKE, FAKE, 128, 128, FAKE,
+                                      None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_rank_partial(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, None,
+                                      None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_rank_partial(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, FAKE,
+                                      ctypes.c_void_p(0x10004), None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_rank_partial(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 128, FAKE,
+                                      None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_ranks(sp, FAKE, None, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_ranks(sp, ctypes.c_void_p(0x10008), FAKE, 128, FAKE, None, None,
+                               None) == moe.MOE_ERR_ARG
+    assert L.moe_combine_ranks(sp, FAKE, FAKE, -3, FAKE, None, None, None) == moe.MOE_ERR_ARG
 
 
 def test_empty_batches_are_no_ops():
@@ -87,6 +103,9 @@ def test_empty_batches_are_no_ops():
     assert L.moe_combine(s0, None, None, None, 0, None, None, None, None) == moe.MOE_OK
     assert L.moe_permute_by_expert(s0, None, None, FAKE, None, None, 0, None, None, 0, None,
                                    None) == moe.MOE_OK
+    assert L.moe_combine_rank_partial(s0, None, None, FAKE, None, None, None, 0, 0, None, None,
+                                      None, None) == moe.MOE_OK
+    assert L.moe_combine_ranks(s0, None, None, 0, None, None, None, None) == moe.MOE_OK
 
 
 def test_status_strings():
