@@ -163,7 +163,7 @@ def oracle_step(w, hid, ids, wts, eo):
     T, k = ids.shape
     lay = oracle.layout(ids, w.E, w.R)
     rb, src, _ = oracle.pack(hid, lay["token_rank_slot"], T * min(k, w.R))
-    oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], w.E, T * k)
+    oracle.permute(rb, src, lay, ids, w.E, T * k)
     oracle.combine(eo, lay["pair_row"], wts, want_f32=False)
     return int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
 

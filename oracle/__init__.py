@@ -29,12 +29,12 @@ class _Lib:
         lib = ctypes.CDLL(path)
         i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
         lib.oracle_layout.restype = ctypes.c_int
-        lib.oracle_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_layout.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_pack.restype = ctypes.c_int
         lib.oracle_pack.argtypes = [i32, i32, i32, vp, vp, vp, vp, i64]
         lib.oracle_permute.restype = ctypes.c_int
-        lib.oracle_permute.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64, vp, vp,
-                                       i64]
+        lib.oracle_permute.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                       i64, vp, vp, i64]
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, i64, vp, vp]
         lib.oracle_combine_f64.restype = ctypes.c_int
@@ -90,10 +90,13 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
-def layout(topk_ids: np.ndarray, E: int, R: int) -> dict:
+def layout(topk_ids: np.ndarray, E: int, R: int, align: int = 1, block: int = 0) -> dict:
+    """Counts, offsets and rows of the layout. align > 1 pads every expert's
+    run to a multiple of align rows; block > 0 gives every expert a fixed
+    block of rows instead (masked). The result records align and block."""
     ids = _c(topk_ids, np.int32)
     T, k = ids.shape
-    assert E % R == 0
+    assert E % R == 0 and align >= 1 and block >= 0 and (block == 0 or align == 1)
     res = dict(
         rank_counts=np.zeros(R, np.int32),
         rank_offsets=np.zeros(R + 1, np.int32),
@@ -103,9 +106,10 @@ def layout(topk_ids: np.ndarray, E: int, R: int) -> dict:
         pair_row=np.zeros((T, k), np.int32),
     )
     res["err"] = _load().oracle_layout(
-        T, E, R, k, _p(ids), _p(res["rank_counts"]), _p(res["rank_offsets"]),
+        T, E, R, k, align, block, _p(ids), _p(res["rank_counts"]), _p(res["rank_offsets"]),
         _p(res["expert_counts"]), _p(res["expert_offsets"]), _p(res["token_rank_slot"]),
         _p(res["pair_row"]))
+    res["align"], res["block"] = align, block
     return res
 
 
@@ -124,21 +128,24 @@ def pack(hidden: np.ndarray, token_rank_slot: np.ndarray, cap_rank: int,
     return rank_buf, rank_src_token, err
 
 
-def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int,
-            cap_expert: int, expert_buf=None, expert_src_pair=None):
+def permute(rank_buf, rank_src_token, lay: dict, topk_ids, E: int, cap_expert: int,
+            expert_buf=None, expert_src_pair=None):
+    """Regroup the rank-buffer rows by expert, at the rows the layout `lay`
+    (from layout()) assigned, and mark its padding rows -1."""
     rb = _c(rank_buf, np.uint16)
     ids = _c(topk_ids, np.int32)
     T, k = ids.shape
-    R = len(rank_offsets) - 1
+    R = len(lay["rank_offsets"]) - 1
     H = rb.shape[1]
     if expert_buf is None:
         expert_buf = np.zeros((cap_expert, H), np.uint16)
     if expert_src_pair is None:
-        expert_src_pair = np.full(cap_expert, -1, np.int32)
+        expert_src_pair = np.full(cap_expert, -2, np.int32)
     err = _load().oracle_permute(
-        T, H, E, R, k, _p(rb), _p(_c(rank_src_token, np.int32)), _p(_c(rank_offsets, np.int32)),
-        _p(ids), _p(_c(pair_row, np.int32)), rb.shape[0], _p(expert_buf), _p(expert_src_pair),
-        cap_expert)
+        T, H, E, R, k, lay.get("block", 0), _p(rb), _p(_c(rank_src_token, np.int32)),
+        _p(_c(lay["rank_offsets"], np.int32)), _p(ids), _p(_c(lay["pair_row"], np.int32)),
+        _p(_c(lay["expert_counts"], np.int32)), _p(_c(lay["expert_offsets"], np.int32)),
+        rb.shape[0], _p(expert_buf), _p(expert_src_pair), cap_expert)
     return expert_buf, expert_src_pair, err
 
 
@@ -217,8 +224,7 @@ def dispatch_combine(hidden, topk_ids, topk_weights, E: int, R: int, expert_out_
     cap_rank = T * min(k, R)
     cap_expert = T * k
     rank_buf, src, e1 = pack(hidden, lay["token_rank_slot"], cap_rank)
-    expert_buf, src_pair, e2 = permute(rank_buf, src, lay["rank_offsets"], topk_ids,
-                                       lay["pair_row"], E, cap_expert)
+    expert_buf, src_pair, e2 = permute(rank_buf, src, lay, topk_ids, E, cap_expert)
     if expert_out_slots is None:
         eo = expert_buf
     else:

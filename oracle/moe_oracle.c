@@ -30,9 +30,10 @@ static uint16_t narrow_bf16_rne(float f) {
   return (uint16_t)upper;
 }
 
-int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* topk_ids,
-                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
-                  int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row) {
+int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, int32_t align, int32_t block,
+                  const int32_t* topk_ids, int32_t* rank_counts, int32_t* rank_offsets,
+                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* token_rank_slot,
+                  int32_t* pair_row) {
   const int32_t m = E / R; /* experts per rank; expert e is on rank e / m */
   int err = 0;
   unsigned char* on_rank = (unsigned char*)malloc((size_t)R);
@@ -61,7 +62,16 @@ int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* top
   rank_offsets[0] = 0;
   for (int32_t r = 0; r < R; ++r) rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];
   expert_offsets[0] = 0;
-  for (int32_t e = 0; e < E; ++e) expert_offsets[e + 1] = expert_offsets[e] + expert_counts[e];
+  for (int32_t e = 0; e < E; ++e) {
+    if (block > 0) {
+      /* masked: a fixed block of rows per expert */
+      expert_offsets[e + 1] = (e + 1) * block;
+    } else {
+      /* contiguous: the expert's run, padded up to a multiple of align rows */
+      const int32_t run = (expert_counts[e] + align - 1) / align * align;
+      expert_offsets[e + 1] = expert_offsets[e] + run;
+    }
+  }
 
   /* Positions: walk the tokens in order and hand out the next free row of the
    * segment (rank) or run (expert), so rows ascend with the token index. */
@@ -75,7 +85,14 @@ int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* top
         pair_row[(int64_t)t * k + j] = -1;
         continue;
       }
-      pair_row[(int64_t)t * k + j] = next_expert[e]++;
+      const int32_t row = next_expert[e]++;
+      if (block > 0 && row >= (e + 1) * block) {
+        /* masked: the expert's block is full; the pair is dropped */
+        pair_row[(int64_t)t * k + j] = -1;
+        err |= ORACLE_ERR_EXPERT_CAP;
+      } else {
+        pair_row[(int64_t)t * k + j] = row;
+      }
       on_rank[e / m] = 1;
     }
     for (int32_t r = 0; r < R; ++r)
@@ -107,10 +124,11 @@ int oracle_pack(int32_t T, int32_t H, int32_t R, const uint16_t* hidden,
   return err;
 }
 
-int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k, int32_t block,
                    const uint16_t* rank_buf, const int32_t* rank_src_token,
                    const int32_t* rank_offsets, const int32_t* topk_ids,
-                   const int32_t* pair_row, int64_t cap_rank, uint16_t* expert_buf,
+                   const int32_t* pair_row, const int32_t* expert_counts,
+                   const int32_t* expert_offsets, int64_t cap_rank, uint16_t* expert_buf,
                    int32_t* expert_src_pair, int64_t cap_expert) {
   (void)T;
   const int32_t m = E / R;
@@ -125,13 +143,22 @@ int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
       const int32_t e = topk_ids[(int64_t)t * k + j];
       if (!id_is_expert(e, E) || e / m != r) continue;
       const int64_t dst = pair_row[(int64_t)t * k + j];
-      if (dst >= cap_expert) {
+      if (dst < 0 || dst >= cap_expert) { /* dropped by the layout (full block) or past the cap */
         err |= ORACLE_ERR_EXPERT_CAP;
         continue;
       }
       memcpy(expert_buf + dst * H, rank_buf + i * H, sizeof(uint16_t) * (size_t)H);
       expert_src_pair[dst] = t * k + j;
     }
+  }
+  /* Rows of an expert's run or block that no pair fills (padding) are marked
+   * -1 in expert_src_pair; their row data is left as it was. */
+  for (int32_t e = 0; e < E; ++e) {
+    int64_t used = expert_counts[e];
+    if (block > 0 && used > block) used = block;
+    const int64_t end = block > 0 ? (int64_t)(e + 1) * block : expert_offsets[e + 1];
+    for (int64_t row = expert_offsets[e] + used; row < end && row < cap_expert; ++row)
+      expert_src_pair[row] = -1;
   }
   return err;
 }

@@ -48,14 +48,23 @@ extern "C" {
  * Figure 1 and sec 1.3 third answer) and pairs per expert, takes exclusive
  * prefix sums, and numbers every (token, rank) copy and every (token, slot)
  * pair in ascending token order inside its segment.
+ * The expert-grouped rows come in one of three shapes ([A2A] sec 2.2,
+ * Figure 4): contiguous (align = 1, block = 0); contiguous with every expert's
+ * run padded to a multiple of `align` rows (the DeepGEMM contiguous kernel
+ * wants 128); masked (block > 0): a fixed block of `block` rows per expert,
+ * expert e's rows starting at e * block, pairs past a full block dropped
+ * (pair_row -1, ORACLE_ERR_EXPERT_CAP) while expert_counts keeps the full
+ * count ([A2A] sec 4.1 and 4.2: a region per expert of a fixed cap, the count
+ * per expert in a small tensor).
  *   rank_counts[R], rank_offsets[R+1], expert_counts[E], expert_offsets[E+1]
  *   token_rank_slot[T*R]: row of token t in rank r's segment, or -1
  *   pair_row[T*k]: row of pair (t, j) in the expert-grouped buffer, or -1
  * Returns the OR of ORACLE_ERR_* bits.
  */
-int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, const int32_t* topk_ids,
-                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
-                  int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row);
+int oracle_layout(int32_t T, int32_t E, int32_t R, int32_t k, int32_t align, int32_t block,
+                  const int32_t* topk_ids, int32_t* rank_counts, int32_t* rank_offsets,
+                  int32_t* expert_counts, int32_t* expert_offsets, int32_t* token_rank_slot,
+                  int32_t* pair_row);
 
 /*
  * Pack ([A2A] sec 1.3 third answer, sec 3.2 first step): copy token t's hidden
@@ -72,11 +81,14 @@ int oracle_pack(int32_t T, int32_t H, int32_t R, const uint16_t* hidden,
  * min(rank_offsets[R], cap_rank), sitting in the segment of rank r and holding
  * token t = rank_src_token[i], is copied once for each slot j of t whose expert
  * lives on r, to row pair_row[t*k + j]; expert_src_pair of that row is t*k + j.
+ * Padding rows (rows of an expert's padded run or block that no pair fills)
+ * get expert_src_pair -1; their row data is left as it was.
  */
-int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k,
+int oracle_permute(int32_t T, int32_t H, int32_t E, int32_t R, int32_t k, int32_t block,
                    const uint16_t* rank_buf, const int32_t* rank_src_token,
                    const int32_t* rank_offsets, const int32_t* topk_ids,
-                   const int32_t* pair_row, int64_t cap_rank, uint16_t* expert_buf,
+                   const int32_t* pair_row, const int32_t* expert_counts,
+                   const int32_t* expert_offsets, int64_t cap_rank, uint16_t* expert_buf,
                    int32_t* expert_src_pair, int64_t cap_expert);
 
 /*

@@ -85,7 +85,7 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
 def run_oracle(hid, ids, wts, E, R, y_slots, cap_rank, cap_expert) -> dict:
     lay = oracle.layout(ids, E, R)
     rb, rsrc, e1 = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
-    eb, esrc, e2 = oracle.permute(rb, rsrc, lay["rank_offsets"], ids, lay["pair_row"], E,
+    eb, esrc, e2 = oracle.permute(rb, rsrc, lay, ids, E,
                                   cap_expert)
     eo = eb if y_slots is None else oracle.place_slots(y_slots, lay["pair_row"], cap_expert)
     out, out32, e3 = oracle.combine(eo, lay["pair_row"], wts)

@@ -269,7 +269,7 @@ def pin_figure4():
     local = range(rank * m, (rank + 1) * m)
     assert int(sum(lay["expert_counts"][e] for e in local)) == int(kv["expert_rows"][0])
     rank_buf, src, _ = oracle.pack(hid, lay["token_rank_slot"], cap_rank=T * min(k, R))
-    ebuf, esrc, err = oracle.permute(rank_buf, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+    ebuf, esrc, err = oracle.permute(rank_buf, src, lay, ids, E,
                                      cap_expert=T * k)
     assert err == 0
     lo, hi = lay["expert_offsets"][rank * m], lay["expert_offsets"][(rank + 1) * m]
@@ -329,7 +329,7 @@ def pin_pack_permute_rows():
 
         eb = np.full((cap_expert, H), canary, np.uint16)
         es = np.full(cap_expert, -5, np.int32)
-        eb, es, e2 = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+        eb, es, e2 = oracle.permute(rb, src, lay, ids, E,
                                     cap_expert, eb, es)
         assert e2 == 0
         P = int(want["expert_offsets"][-1])
@@ -356,7 +356,7 @@ def pin_permute_reads_own_segment():
         src = np.full(C, -1, np.int32)
         ts, rs = np.nonzero(lay["token_rank_slot"] >= 0)
         src[lay["token_rank_slot"][ts, rs]] = ts
-        eb, es, err = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E,
+        eb, es, err = oracle.permute(rb, src, lay, ids, E,
                                      T * k)
         assert err == 0
         m = E // R
@@ -387,11 +387,94 @@ def pin_caps():
     P = int(lay["expert_offsets"][-1])
     eb = np.zeros((P - 5, H), np.uint16)
     es = np.full(P - 5, -1, np.int32)
-    eb, es, err2 = oracle.permute(rb, src, lay["rank_offsets"], ids, lay["pair_row"], E, P - 5,
+    eb, es, err2 = oracle.permute(rb, src, lay, ids, E, P - 5,
                                   eb, es)
     assert err2 & oracle.ERR_EXPERT_CAP
     out, _, err3 = oracle.combine(eb, lay["pair_row"], np.ones((T, k), np.float32))
     assert err3 & oracle.ERR_EXPERT_CAP
+
+
+def _padded_expected(ids, E, R, align=1, block=0):
+    """The padded or masked layout from the plain one (stable sort): every
+    pair keeps its index inside its expert's run; only where runs start
+    changes (numpy cumsum of the rounded-up counts, or e * block)."""
+    want = expected_layout_by_sorting(ids, E, R)
+    counts = want["expert_counts"]
+    base = want["expert_offsets"][:-1]
+    if block > 0:
+        offsets = np.arange(E + 1) * block
+    else:
+        offsets = np.concatenate([[0], np.cumsum(-(-counts // align) * align)])
+    pr = want["pair_row"]
+    e = np.where(pr >= 0, ids, 0)
+    idx = pr - base[e]
+    new_pr = np.where(pr >= 0, offsets[e] + idx, -1)
+    over = (pr >= 0) & (block > 0) & (idx >= block)
+    new_pr = np.where(over, -1, new_pr)
+    out = dict(want, expert_offsets=offsets, pair_row=new_pr)
+    return out, bool(over.any())
+
+
+def pin_layout_padded_and_masked():
+    """Runs padded to a multiple of `align` rows and fixed per-expert blocks:
+    against the stable-sort layout with the run starts moved (cumsum of the
+    rounded-up counts, or e * block) and pairs past a full block dropped
+    and reported. The worst-case padded size T*k + E*(align-1) is never
+    exceeded."""
+    for (T, E, R, k, pn, pd, seed) in LAYOUT_CASES:
+        rng = np.random.default_rng(seed + 100)
+        ids = rand_ids(rng, T, E, k, p_neg=pn, p_dup=pd)
+        for align in (1, 2, 8, 128):
+            got = oracle.layout(ids, E, R, align=align)
+            want, _ = _padded_expected(ids, E, R, align=align)
+            assert_layout_equal(got, want, f"align {align} T{T} E{E} R{R} k{k}")
+            assert got["err"] == 0
+            assert got["expert_offsets"][-1] <= T * k + E * (align - 1)
+        for block in (1, 3, 64):
+            got = oracle.layout(ids, E, R, block=block)
+            want, over = _padded_expected(ids, E, R, block=block)
+            assert_layout_equal(got, want, f"block {block} T{T} E{E} R{R} k{k}")
+            assert got["err"] == (oracle.ERR_EXPERT_CAP if over else 0), (block, got["err"])
+
+
+def pin_permute_padding_rows():
+    """After the permute of a padded or masked layout, every row that a pair
+    fills holds that token's hidden row with its (token, slot) id, every other
+    row of a run or block is marked -1, and rows past the last run are not
+    touched. The combine does not see the difference: it equals the combine
+    of the plain layout bit for bit (when no block overflows)."""
+    rng = np.random.default_rng(103)
+    for T, E, R, k, H, align, block in [(60, 16, 4, 3, 8, 8, 0), (40, 32, 8, 4, 16, 128, 0),
+                                        (50, 16, 4, 2, 8, 1, 40), (30, 8, 2, 4, 8, 1, 7)]:
+        ids = rand_ids(rng, T, E, k, p_neg=0.1)
+        hid = synth.normal_bf16(21, 0, T * H).reshape(T, H)
+        lay = oracle.layout(ids, E, R, align=align, block=block)
+        cap_rank = T * min(k, R)
+        cap_expert = E * block if block else T * k + E * (align - 1)
+        rb, src, _ = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
+        eb, es, _ = oracle.permute(rb, src, lay, ids, E, cap_expert)
+        filled = np.zeros(cap_expert, bool)
+        for t in range(T):
+            for j in range(k):
+                row = lay["pair_row"][t, j]
+                if row >= 0:
+                    filled[row] = True
+                    assert es[row] == t * k + j and np.array_equal(eb[row], hid[t])
+        offs, cnts = lay["expert_offsets"], lay["expert_counts"]
+        in_run = np.zeros(cap_expert, bool)
+        for e in range(E):
+            end = (e + 1) * block if block else offs[e + 1]
+            in_run[offs[e]:end] = True
+        assert np.all(es[in_run & ~filled] == -1)
+        assert np.all(es[~in_run] == -2)  # untouched
+        assert not np.any(filled & ~in_run)
+        if block == 0 or not (lay["err"] & oracle.ERR_EXPERT_CAP):
+            y = synth.normal_bf16(23, 2, T * k * H).reshape(T, k, H)
+            w = rng.random((T, k)).astype(np.float32)
+            plain = oracle.layout(ids, E, R)
+            a = oracle.combine(oracle.place_slots(y, plain["pair_row"], T * k), plain["pair_row"], w)
+            b = oracle.combine(oracle.place_slots(y, lay["pair_row"], cap_expert), lay["pair_row"], w)
+            assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
 
 
 # ----------------------------------------------------------------------------
@@ -730,6 +813,8 @@ PINS = [
     pin_pack_permute_rows,
     pin_permute_reads_own_segment,
     pin_caps,
+    pin_layout_padded_and_masked,
+    pin_permute_padding_rows,
     pin_roundtrip_identity,
     pin_combine_one_hot,
     pin_combine_scaling_and_skip,

@@ -92,6 +92,24 @@ MUTANTS = {
     "home sum ignores the rank cap": (
         "        if (s >= cap_rank) {\n          err |= ORACLE_ERR_RANK_CAP;",
         "        if (s >= cap_rank + 1000000) {\n          err |= ORACLE_ERR_RANK_CAP;"),
+    "padding rounds down": (
+        "const int32_t run = (expert_counts[e] + align - 1) / align * align;",
+        "const int32_t run = expert_counts[e] / align * align;"),
+    "padding one row short": (
+        "const int32_t run = (expert_counts[e] + align - 1) / align * align;",
+        "const int32_t run = (expert_counts[e] + align - 2) / align * align;"),
+    "masked blocks packed contiguously": (
+        "expert_offsets[e + 1] = (e + 1) * block;",
+        "expert_offsets[e + 1] = expert_offsets[e] + expert_counts[e];"),
+    "masked block overflow kept": (
+        "if (block > 0 && row >= (e + 1) * block) {",
+        "if (block > 0 && row > (e + 1) * block) {"),
+    "padding rows not marked": (
+        "      expert_src_pair[row] = -1;\n  }\n  return err;",
+        "      (void)0;\n  }\n  return err;"),
+    "padding marks one row too many": (
+        "row < end && row < cap_expert; ++row)",
+        "row <= end && row < cap_expert; ++row)"),
     "f64 combine rounds products to float": (
         "acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);",
         "acc += (double)(topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]));"),
