@@ -218,7 +218,7 @@ class Rig:
     """One workload resident on the GPU with every buffer of a pass, and the
     four library calls on the current stream."""
 
-    def __init__(self, w, dev, two_stage: bool = False):
+    def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -230,7 +230,7 @@ class Rig:
         self.hid = synth.hidden(w)
         self.ids, self.wts = synth.routing(w)
         self.y = synth.expert_out_slots(w.seed, w.E, w.H, self.ids)
-        self.shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
+        self.shape = moe.Shape(w.T, w.H, w.E, w.R, w.k, align, block)
         self.buf = moe.Buffers(self.shape, dev)
         self.hid_d = staging.rows_to_device(self.hid, dev)
         self.ids_d = torch.from_numpy(self.ids).to(dev)
@@ -241,8 +241,12 @@ class Rig:
             staging.rows_to_device(self.y, dev), self.buf.pair_row, self.shape.cap_expert)
         torch.cuda.synchronize()
         self.C = int(self.buf.rank_offsets[-1].item())
-        self.P = int(self.buf.expert_offsets[-1].item())
+        # pairs placed (a full block drops the rest) and padding rows marked
+        counts = self.buf.expert_counts.long()
+        self.P = int((counts.clamp(max=block) if block else counts).sum().item())
+        self.pad_rows = int(self.buf.expert_offsets[-1].item()) - self.P
         self.nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P)
+        self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         self.stream = torch.cuda.current_stream(dev)
         self.calls = CALLS
         if two_stage:
@@ -255,13 +259,16 @@ class Rig:
     def call(self, name: str) -> None:
         moe, s, b = self.moe, self.shape, self.buf
         if name == "layout":
-            moe.layout(self.ids_d, s.E, s.R, s.H, err=b.err, out=b.layout_dict())
+            moe.layout(self.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
+                       out=b.layout_dict())
         elif name == "pack":
             moe.pack(self.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
                      err=b.err)
         elif name == "permute":
             moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
-                        s.E, b.expert_buf, b.expert_src_pair, err=b.err)
+                        s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
+                        expert_offsets=b.expert_offsets, align=s.align, block=s.block,
+                        err=b.err)
         elif name == "combine":
             moe.combine(self.expert_out, b.pair_row, self.wts_d, s.E, s.R, b.out, err=b.err)
         elif name == "partial":
@@ -345,12 +352,17 @@ def sweep(names, dev, with_oracle: bool) -> None:
     log(f"1 GiB device copy: {copy['GB/s']} GB/s")
     print(json.dumps({"copy_1GiB": copy}), flush=True)
     rows = []
-    for name in names:
+    for spec in names:
+        # "name" or "name:align=128" / "name:block=128" (padded or masked expert layout)
+        name, _, opt = spec.partition(":")
+        opts = dict(kv.split("=") for kv in opt.split(",") if kv)
+        align, block = int(opts.get("align", 1)), int(opts.get("block", 0))
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev, two_stage=True)
+        rig = Rig(w, dev, two_stage=True, align=align, block=block)
         for _ in range(5):
             rig.step()
-        res = {"workload": w.describe(), "C": rig.C, "P": rig.P,
+        res = {"workload": w.describe(), "layout_shape": {"align": align, "block": block},
+               "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
                "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
         for mode, fl in (("warm", None), ("cold", flush)):
             meds = {c: [] for c in rig.calls}
@@ -388,12 +400,12 @@ def sweep(names, dev, with_oracle: bool) -> None:
             "combine_pairs": round(rig.P / (warm["combine"]["warm"]["us"] * 1e-6))}
         res["bytes"] = tot
         res["two_stage_bytes"] = tot2
-        if with_oracle:
+        if with_oracle and align == 1 and block == 0:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
                                           3 if w.T * w.H > 2 ** 25 else 5)
         print(json.dumps(res), flush=True)
-        rows.append((name, res))
+        rows.append((spec, res))
         del rig
         torch.cuda.empty_cache()
     # human-readable table
@@ -428,7 +440,9 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", nargs="?", const="tiny,decode,prefill,skew,adv", default=None,
+    ap.add_argument("--sweep", nargs="?",
+                    const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128",
+                    default=None,
                     metavar="WORKLOADS", help="per-call warm/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (for counter calibration)")

@@ -30,9 +30,16 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout", "moe_d
            "moe_combine_ranks")
 
 
+ABI_VERSION = 2
+
+
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("R", ctypes.c_int32), ("k", ctypes.c_int32)]
+                ("R", ctypes.c_int32), ("k", ctypes.c_int32), ("align", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
+
+    def __init__(self, T=0, H=8, E=1, R=1, k=1, align=1, block=0):
+        super().__init__(T, H, E, R, k, align, block)
 
 
 class MoeError(RuntimeError):
@@ -64,13 +71,17 @@ def lib():
     L.moe_dispatch_pack.restype = ctypes.c_int
     L.moe_dispatch_pack.argtypes = [shp, vp, vp, vp, vp, i64, vp, vp]
     L.moe_permute_by_expert.restype = ctypes.c_int
-    L.moe_permute_by_expert.argtypes = [shp, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp, vp]
+    L.moe_permute_by_expert.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp,
+                                        vp]
     L.moe_combine.restype = ctypes.c_int
     L.moe_combine.argtypes = [shp, vp, vp, vp, i64, vp, vp, vp, vp]
     L.moe_combine_rank_partial.restype = ctypes.c_int
     L.moe_combine_rank_partial.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
     L.moe_combine_ranks.restype = ctypes.c_int
     L.moe_combine_ranks.argtypes = [shp, vp, vp, i64, vp, vp, vp, vp]
+    if L.moe_abi_version() != ABI_VERSION:
+        raise MoeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, this binding "
+                       f"expects {ABI_VERSION}: rebuild with __graft_entry__.build()")
     _lib = L
     return L
 
@@ -114,9 +125,11 @@ class Shape:
     E: int
     R: int
     k: int
+    align: int = 1  # expert runs padded to a multiple of align rows
+    block: int = 0  # > 0: a fixed block of rows per expert (masked layout)
 
     def c(self) -> MoeShape:
-        return MoeShape(self.T, self.H, self.E, self.R, self.k)
+        return MoeShape(self.T, self.H, self.E, self.R, self.k, self.align, self.block)
 
     @property
     def cap_rank(self) -> int:
@@ -125,16 +138,18 @@ class Shape:
 
     @property
     def cap_expert(self) -> int:
-        """Worst-case expert-buffer rows: T * k."""
-        return self.T * self.k
+        """Worst-case expert-buffer rows: T*k + E*(align-1), or E*block."""
+        if self.block > 0:
+            return self.E * self.block
+        return self.T * self.k + self.E * (self.align - 1)
 
 
-def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, err=None,
-           out: dict | None = None) -> dict:
+def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1,
+           block: int = 0, err=None, out: dict | None = None) -> dict:
     """moe_dispatch_layout: counts, offsets, token_rank_slot [T,R], pair_row [T,k]."""
     T, k = topk_ids.shape
     dev = topk_ids.device
-    shape = Shape(T, H, E, R, k)
+    shape = Shape(T, H, E, R, k, align, block)
     if out is None:
         out = dict(
             rank_counts=torch.empty(R, dtype=torch.int32, device=dev),
@@ -167,15 +182,20 @@ def pack(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, ra
 
 
 def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, expert_buf,
-            expert_src_pair, *, err=None) -> None:
-    """moe_permute_by_expert into caller-provided expert_buf [cap_expert, H]."""
+            expert_src_pair, *, expert_counts=None, expert_offsets=None, align: int = 1,
+            block: int = 0, err=None) -> None:
+    """moe_permute_by_expert into caller-provided expert_buf [cap_expert, H].
+    A padded (align > 1) or blocked (block > 0) layout needs the layout's
+    expert_counts and expert_offsets, to mark its padding rows."""
     T, k = topk_ids.shape
     H = rank_buf.shape[1]
     R = rank_offsets.shape[0] - 1
-    shape = Shape(T, H, E, R, k)
+    shape = Shape(T, H, E, R, k, align, block)
     st = lib().moe_permute_by_expert(
         ctypes.byref(shape.c()), _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)),
         _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)), _ptr(_i32(pair_row)),
+        _ptr(None if expert_counts is None else _i32(expert_counts)),
+        _ptr(None if expert_offsets is None else _i32(expert_offsets)),
         rank_buf.shape[0], _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)),
         expert_buf.shape[0], _ptr(err), _stream(rank_buf.device))
     _check(st, "moe_permute_by_expert")
@@ -264,10 +284,12 @@ class Buffers:
 def dispatch(buf: Buffers, hidden, topk_ids) -> None:
     """Layout, pack and permute into `buf` (three library calls, no host sync)."""
     s = buf.shape
-    layout(topk_ids, s.E, s.R, s.H, err=buf.err, out=buf.layout_dict())
+    layout(topk_ids, s.E, s.R, s.H, align=s.align, block=s.block, err=buf.err,
+           out=buf.layout_dict())
     pack(hidden, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token, err=buf.err)
     permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, topk_ids, buf.pair_row, s.E,
-            buf.expert_buf, buf.expert_src_pair, err=buf.err)
+            buf.expert_buf, buf.expert_src_pair, expert_counts=buf.expert_counts,
+            expert_offsets=buf.expert_offsets, align=s.align, block=s.block, err=buf.err)
 
 
 def combine_into(buf: Buffers, expert_out, topk_weights) -> None:

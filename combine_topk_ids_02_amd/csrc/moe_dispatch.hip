@@ -50,6 +50,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxRanks = 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxVec = 16;                 // vec4 per lane held in registers per pass
+constexpr int kMaxAlign = 1 << 16;          // largest run padding
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -93,6 +94,7 @@ constexpr size_t kLayoutLdsLimit = 160 * 1024 - 1024;  // gfx950: 160 KiB of LDS
 
 struct LayoutGeom {
   int T, E, R, k, m;    // m = experts per rank
+  int align, block;     // expert runs padded to multiples of align; or fixed blocks (block > 0)
   int ncols;            // E expert columns followed by R rank columns
   int batch_tokens;     // tokens whose ids are staged in LDS at once (multiple of 1024)
   int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
@@ -126,14 +128,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 
 // Column totals, exclusive scans and the tile's first rows, in one pass: for
 // every column c, count = s_tot[c] + s_pre[c] (tokens from the tile on, and
-// before it), offset = exclusive prefix of the counts (experts in id order
-// over waves 0..7, ranks in rank order in wave 8), and s_pre[c] becomes
-// offset + (count before the tile), the tile's first row in that column. The
-// workgroup that is `writer` also stores the counts and offsets.
-__device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
-                             int32_t* s_tmp /* [16] */, bool writer, int32_t* expert_counts,
-                             int32_t* expert_offsets, int32_t* rank_counts,
-                             int32_t* rank_offsets) {
+// before it), offset = exclusive prefix of the run lengths (experts in id
+// order over waves 0..7, ranks in rank order in wave 8), and s_pre[c] becomes
+// offset + (count before the tile), the tile's first row in that column. An
+// expert's run length is its count, rounded up to a multiple of `align`, or
+// the fixed `block` when block > 0. The workgroup that is `writer` also
+// stores the counts and offsets.
+__device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R, int align,
+                             int block, int32_t* s_tmp /* [16] */, bool writer,
+                             int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* rank_counts, int32_t* rank_offsets) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
@@ -141,15 +145,17 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
   constexpr int kPer = (kMaxExperts + kScanThreads - 1) / kScanThreads;
   const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kPer
   int lo = 0, sum = 0, x = 0;
-  int cnt[kPer];
+  int run_len[kPer];  // rows of the expert's run: its count, padded, or the fixed block
   if (wave < 8) {
     lo = min(E, tid * per);
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int i = lo + q;
-      cnt[q] = (q < per && i < E) ? s_tot[i] + s_pre[i] : 0;
-      if (writer && q < per && i < E) expert_counts[i] = cnt[q];
-      sum += cnt[q];
+      const int cnt = (q < per && i < E) ? s_tot[i] + s_pre[i] : 0;
+      if (writer && q < per && i < E) expert_counts[i] = cnt;
+      run_len[q] = block > 0 ? ((q < per && i < E) ? block : 0)
+                             : (align == 1 ? cnt : (cnt + align - 1) / align * align);
+      sum += run_len[q];
     }
     x = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s_tmp[wave] = x;
@@ -179,7 +185,7 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
       if (q < per && i < E) {
         s_pre[i] += run;
         if (writer) expert_offsets[i] = run;
-        run += cnt[q];
+        run += run_len[q];
       }
     }
     if (writer && tid == 0) expert_offsets[E] = total;
@@ -209,6 +215,7 @@ __device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int6
 // One workgroup of 1024 threads per tile of g.tile_tokens tokens; K = k known
 // at compile time (0: any k up to kMaxK, read at run time). Writes:
 //   pair_row[t][j]        = expert_offsets[e] + #{pairs of e before (t, j)}
+//                           (-1 when that is past the end of a fixed block)
 //   token_rank_slot[t][r] = rank_offsets[r] + #{tokens before t with a copy on r}
 // Workgroup 0 also writes the counts and offsets.
 template <int K, bool kWide>
@@ -302,8 +309,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 
   // 2.-3. Counts, exclusive scans (experts in id order, ranks in rank order)
   //    and the absolute first row of this tile in every column (in s_pre).
-  scan_columns(s_pre, s_tot, g.E, g.R, s_tmp, blockIdx.x == 0, expert_counts, expert_offsets,
-               rank_counts, rank_offsets);
+  scan_columns(s_pre, s_tot, g.E, g.R, g.align, g.block, s_tmp, blockIdx.x == 0, expert_counts,
+               expert_offsets, rank_counts, rank_offsets);
 
   // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..3. Wave w
   //    owns tokens [64w, 64w+64) of the sub-tile, i.e. the contiguous pairs
@@ -315,6 +322,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   //    between chunks.
   const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);
   bool bad_id = false;
+  bool full_block = false;  // a pair found its expert's fixed block full
   const bool ranker = wave < kOwnWaves;
   int32_t* cnt_w = s_cnt + (ranker ? wave : 0) * g.ncols;
   for (int t0 = tile_lo; t0 < tile_hi; t0 += kOwnTokens) {
@@ -414,7 +422,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       for (int ch = 0; ch < KR; ++ch) {
         if (ch < k) {
           const int pl = wave * kWave * k + ch * kWave + lane;
-          if (pl < npairs) pair_row[(int64_t)t0 * k + pl] = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
+          if (pl < npairs) {
+            int row = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
+            if (g.block > 0 && row >= (ex[ch] + 1) * g.block) {
+              row = -1;
+              full_block = true;
+            }
+            pair_row[(int64_t)t0 * k + pl] = row;
+          }
         }
       }
       for (int r = 0; r < g.R; ++r) {
@@ -426,6 +441,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     }
   }
   if (__ballot(bad_id) && lane == 0) flag_error(err_word, MOE_ERRBIT_BAD_ID);
+  if (__ballot(full_block) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
 }
 
 size_t layout_lds_bytes(int batch_tokens, int k, int ncols) {
@@ -441,6 +457,8 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   g.R = sh.R;
   g.k = sh.k;
   g.m = sh.E / sh.R;
+  g.align = sh.align;
+  g.block = sh.block;
   g.ncols = sh.E + sh.R;
   g.inv_m = float(1.0 / double(g.m));
   // Largest batch (multiple of 1024 tokens) that the loads and LDS hold.
@@ -555,15 +573,36 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
   if (dests) fan_out_row<V, true, false>(hidden + (int64_t)t * nvec, rank_buf, slot, dests, nvec);
 }
 
+// Marks the padding rows of expert e (rows of its run or block that no pair
+// fills) with expert_src_pair -1.
+__device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts,
+                                             const int32_t* expert_offsets, int block,
+                                             int32_t* expert_src_pair, int64_t cap_expert) {
+  const int cnt = expert_counts[e];
+  const int64_t lo = (int64_t)expert_offsets[e] + (block > 0 ? min(cnt, block) : cnt);
+  const int64_t end = block > 0 ? (int64_t)(e + 1) * block : (int64_t)expert_offsets[e + 1];
+  const int64_t hi = min(end, cap_expert);
+  for (int64_t row = lo + lane_id(); row < hi; row += kWave) expert_src_pair[row] = -1;
+}
+
+// With a padded or blocked layout, the first pad_waves = E waves mark one
+// expert's padding rows each (first, so that their latency hides under the
+// row copies); then one wave per rank-buffer row.
 template <int V>
 __global__ __launch_bounds__(kBlock) void permute_rows(
     const vec4* rank_buf, const int32_t* __restrict__ rank_src_token,
     const int32_t* __restrict__ rank_offsets, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ pair_row, vec4* expert_buf,
-    int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int nvec,
-    int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
+    const int32_t* __restrict__ pair_row, const int32_t* __restrict__ expert_counts,
+    const int32_t* __restrict__ expert_offsets, vec4* expert_buf,
+    int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int block,
+    int nvec, int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (gw < pad_waves) {
+    mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
+    return;
+  }
+  const int64_t i = gw - pad_waves;
   const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
   if (i >= rows) return;
   // segment of row i: number of segment ends at or below i
@@ -760,6 +799,10 @@ bool shape_ok(const moe_shape_t* s) {
   if (s->R < 1 || s->R > kMaxRanks || s->E < 1 || s->E > kMaxExperts || s->E % s->R != 0)
     return false;
   if (s->k < 1 || s->k > kMaxK) return false;
+  if (s->align < 1 || s->align > kMaxAlign || s->block < 0) return false;
+  if (s->block > 0 && s->align != 1) return false;
+  if (int64_t(s->E) * s->block + int64_t(s->T) * s->k >= (int64_t(1) << 31)) return false;
+  if (int64_t(s->T) * s->k + int64_t(s->E) * (s->align - 1) >= (int64_t(1) << 31)) return false;
   if (int64_t(s->T) * s->k >= (int64_t(1) << 30)) return false;
   if (int64_t(s->T) * s->R >= (int64_t(1) << 31)) return false;
   if (layout_lds_bytes(kLayoutThreads, s->k, s->E + s->R) > kLayoutLdsLimit) return false;
@@ -822,11 +865,13 @@ struct PackLaunch {
 template <int V>
 struct PermuteLaunch {
   static void go(dim3 grid, hipStream_t st, const vec4* rb, const int32_t* src,
-                 const int32_t* roff, const int32_t* ids, const int32_t* prow, vec4* eb,
-                 int32_t* esrc, int T, int E, int R, int k, int m, int nvec, int64_t cap_rank,
+                 const int32_t* roff, const int32_t* ids, const int32_t* prow,
+                 const int32_t* ecnt, const int32_t* eoff, vec4* eb, int32_t* esrc, int T, int E,
+                 int R, int k, int m, int block, int nvec, int pad_waves, int64_t cap_rank,
                  int64_t cap_expert, int32_t* err) {
-    hipLaunchKernelGGL(permute_rows<V>, grid, dim3(kBlock), 0, st, rb, src, roff, ids, prow, eb,
-                       esrc, T, E, R, k, m, nvec, cap_rank, cap_expert, err);
+    hipLaunchKernelGGL(permute_rows<V>, grid, dim3(kBlock), 0, st, rb, src, roff, ids, prow,
+                       ecnt, eoff, eb, esrc, T, E, R, k, m, block, nvec, pad_waves, cap_rank,
+                       cap_expert, err);
   }
 };
 
@@ -908,25 +953,33 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
 
 int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
                           const int32_t* rank_src_token, const int32_t* rank_offsets,
-                          const int32_t* topk_ids, const int32_t* pair_row, int64_t cap_rank,
-                          uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
-                          int32_t* err_word, void* stream) {
+                          const int32_t* topk_ids, const int32_t* pair_row,
+                          const int32_t* expert_counts, const int32_t* expert_offsets,
+                          int64_t cap_rank, uint16_t* expert_buf, int32_t* expert_src_pair,
+                          int64_t cap_expert, int32_t* err_word, void* stream) {
   if (!shape_ok(shape) || cap_rank < 0 || cap_expert < 0) return MOE_ERR_ARG;
   if (!rank_offsets) return MOE_ERR_ARG;
+  const bool padded = shape->align > 1 || shape->block > 0;
+  if (padded && (!expert_counts || !expert_offsets)) return MOE_ERR_ARG;
   const int64_t max_rows =
       std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
-  if (shape->T == 0 || max_rows == 0) return MOE_OK;
-  if (!rank_buf || !rank_src_token || !topk_ids || !pair_row ||
-      (cap_expert > 0 && (!expert_buf || !expert_src_pair)))
+  const int pad_waves = padded && cap_expert > 0 ? shape->E : 0;
+  if (max_rows + pad_waves == 0) return MOE_OK;
+  // With no rows to move (T = 0) only the padding marks are written: the
+  // row buffers and token arrays are not touched and may be NULL.
+  if (max_rows > 0 && (!rank_buf || !rank_src_token || !topk_ids || !pair_row ||
+                       (cap_expert > 0 && !expert_buf)))
     return MOE_ERR_ARG;
+  if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
   if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
-  ByVec<PermuteLaunch>::run(copy_vec(nvec), dim3(blocks_for(max_rows)),
+  ByVec<PermuteLaunch>::run(copy_vec(nvec), dim3(blocks_for(max_rows + pad_waves)),
                             static_cast<hipStream_t>(stream),
                             reinterpret_cast<const vec4*>(rank_buf), rank_src_token, rank_offsets,
-                            topk_ids, pair_row, reinterpret_cast<vec4*>(expert_buf),
-                            expert_src_pair, shape->T, shape->E, shape->R, shape->k,
-                            shape->E / shape->R, nvec, cap_rank, cap_expert, err_word);
+                            topk_ids, pair_row, expert_counts, expert_offsets,
+                            reinterpret_cast<vec4*>(expert_buf), expert_src_pair, shape->T,
+                            shape->E, shape->R, shape->k, shape->E / shape->R, shape->block,
+                            nvec, pad_waves, cap_rank, cap_expert, err_word);
   return launch_status();
 }
 

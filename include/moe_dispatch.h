@@ -38,12 +38,15 @@
  *    experts per GPU; sec 2.1, the local id range [first_local,
  *    first_local + num_local); [EP] experts placed in order, E/G per GPU).
  *  - Sizes: C = number of (token, rank) copies = rank_offsets[R];
- *    P = number of valid (token, slot) pairs = expert_offsets[E]. Buffers sized
- *    for the worst case, cap_rank = T*min(k,R) rows and cap_expert = T*k rows,
- *    can never overflow ([A2A] sec 5.1: worst-case output plus an offsets list).
+ *    P = rows of the expert-grouped buffer in use = expert_offsets[E] (the
+ *    valid (token, slot) pairs, plus padding when align > 1; E*block when
+ *    block > 0). Buffers sized for the worst case, cap_rank = T*min(k,R) rows
+ *    and cap_expert = T*k + E*(align-1) rows (E*block when block > 0), can
+ *    never overflow ([A2A] sec 5.1: worst-case output plus an offsets list).
  *  - Limits: 0 <= T, T*k < 2^30, T*R < 2^31; 1 <= R <= 64; E % R == 0;
- *    1 <= E <= 1024; 1 <= k <= 16; H > 0 and H % 8 == 0; row buffers and
- *    topk_ids 16-byte aligned.
+ *    1 <= E <= 1024; 1 <= k <= 16; H > 0 and H % 8 == 0; 1 <= align <= 65536;
+ *    block >= 0, and align = 1 when block > 0; T*k + E*(align-1) < 2^31 and
+ *    T*k + E*block < 2^31; row buffers and topk_ids 16-byte aligned.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
@@ -55,14 +58,30 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 1
+#define MOE_DISPATCH_ABI_VERSION 2
 
+/*
+ * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
+ * Figure 4; sec 4.1-4.2):
+ *  - contiguous (align = 1, block = 0): expert e's rows are
+ *    [expert_offsets[e], expert_offsets[e] + expert_counts[e]);
+ *  - contiguous, padded (align > 1, block = 0): every expert's run is padded
+ *    up to a multiple of `align` rows (a contiguous grouped GEMM such as
+ *    DeepGEMM's wants 128); the padding rows are marked -1 in expert_src_pair;
+ *  - masked (block > 0, align = 1): expert e owns the fixed block of rows
+ *    [e*block, (e+1)*block) whatever the batch (a masked kernel reads
+ *    expert_counts to know how many rows of each block to use); pairs that
+ *    find their expert's block full are dropped (pair_row -1,
+ *    MOE_ERRBIT_EXPERT_CAP) while expert_counts keeps counting them.
+ */
 typedef struct moe_shape {
-  int32_t T; /* tokens on this GPU */
-  int32_t H; /* hidden size, bf16 elements per row */
-  int32_t E; /* experts */
-  int32_t R; /* ranks (logical destination GPUs) */
-  int32_t k; /* expert slots per token (top-k) */
+  int32_t T;     /* tokens on this GPU */
+  int32_t H;     /* hidden size, bf16 elements per row */
+  int32_t E;     /* experts */
+  int32_t R;     /* ranks (logical destination GPUs) */
+  int32_t k;     /* expert slots per token (top-k) */
+  int32_t align; /* expert runs padded to a multiple of align rows (1: no padding) */
+  int32_t block; /* 0: contiguous runs; > 0: fixed blocks of `block` rows per expert */
 } moe_shape_t;
 
 typedef enum moe_status {
@@ -90,12 +109,15 @@ const char* moe_status_string(int status);
  *   rank_counts      [R]     out: copies per rank, #{t : rank r holds an expert of t}
  *   rank_offsets     [R+1]   out: exclusive prefix sum of rank_counts (rank_offsets[R] = C)
  *   expert_counts    [E]     out: valid pairs per expert
- *   expert_offsets   [E+1]   out: exclusive prefix sum of expert_counts (expert_offsets[E] = P)
+ *   expert_offsets   [E+1]   out: first row of each expert's run: the exclusive prefix sum
+ *                                 of the run lengths (expert_counts, rounded up to a
+ *                                 multiple of align), or e*block (expert_offsets[E] = P)
  *   token_rank_slot  [T*R]   out: row of token t's copy in rank r's segment, or -1;
  *                                 rows of a segment ascend with t
  *   pair_row         [T*k]   out: row of pair (t, j) in the expert-grouped buffer, or -1;
  *                                 rows of an expert's run ascend with (t, j)
- *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID)
+ *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID; MOE_ERRBIT_EXPERT_CAP when a
+ *             pair finds its fixed block full)
  * One kernel launch, no scratch memory beyond LDS. The result is a pure
  * function of topk_ids: no order depends on timing.
  */
@@ -129,18 +151,25 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
  * Every rank-buffer row i < min(rank_offsets[R], cap_rank), in the segment of
  * rank r and holding token t = rank_src_token[i], is read once and written to
  * pair_row[t*k+j] for every slot j of t whose expert lives on rank r;
- * expert_src_pair[that row] = t*k + j.
+ * expert_src_pair[that row] = t*k + j. With a padded or blocked layout
+ * (align > 1 or block > 0), the rows of each run or block that no pair fills
+ * get expert_src_pair -1 (their row data is not written).
  *   rank_buf [cap_rank*H], rank_src_token [cap_rank], rank_offsets [R+1],
  *   topk_ids [T*k], pair_row [T*k]                      in
+ *   expert_counts [E], expert_offsets [E+1]             in: from moe_dispatch_layout; read
+ *                                                       only when align > 1 or block > 0
+ *                                                       (may be NULL otherwise)
  *   expert_buf [cap_expert*H], expert_src_pair [cap_expert]   out
  *   cap_rank: rows of rank_buf; cap_expert: rows of expert_buf (rows at or past
- *   it are dropped, MOE_ERRBIT_EXPERT_CAP). Rows past P are left untouched.
+ *   it are dropped, MOE_ERRBIT_EXPERT_CAP; so is a pair the layout dropped).
+ *   Rows past P are left untouched.
  */
 int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
                           const int32_t* rank_src_token, const int32_t* rank_offsets,
-                          const int32_t* topk_ids, const int32_t* pair_row, int64_t cap_rank,
-                          uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
-                          int32_t* err_word, void* stream);
+                          const int32_t* topk_ids, const int32_t* pair_row,
+                          const int32_t* expert_counts, const int32_t* expert_offsets,
+                          int64_t cap_rank, uint16_t* expert_buf, int32_t* expert_src_pair,
+                          int64_t cap_expert, int32_t* err_word, void* stream);
 
 /*
  * Combine ([A2A] sec 1.1: the MoE output of a token is the sum of its chosen

@@ -25,12 +25,13 @@ def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
             y_slots: np.ndarray | None, cap_rank: int | None = None,
             cap_expert: int | None = None, spare_rows: int = 4, want_f32: bool = True,
-            device="cuda:0", stream: torch.cuda.Stream | None = None) -> dict:
+            device="cuda:0", stream: torch.cuda.Stream | None = None, align: int = 1,
+            block: int = 0) -> dict:
     """One full pass through the library. Row buffers get `spare_rows` canary
     rows past their caps; the library is told only the caps."""
     T, H = hid.shape
     k = ids.shape[1]
-    shape = moe.Shape(T, H, E, R, k)
+    shape = moe.Shape(T, H, E, R, k, align, block)
     cap_rank = shape.cap_rank if cap_rank is None else cap_rank
     cap_expert = shape.cap_expert if cap_expert is None else cap_expert
     dev = torch.device(device)
@@ -58,10 +59,11 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
         rank_buf, rank_src = rank_all[:cap_rank], rsrc_all[:cap_rank]
         expert_buf, expert_src = exp_all[:cap_expert], esrc_all[:cap_expert]
 
-        moe.layout(ids_d, E, R, H, err=err, out=lay)
+        moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay)
         moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
         moe.permute(rank_buf, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"], E,
-                    expert_buf, expert_src, err=err)
+                    expert_buf, expert_src, expert_counts=lay["expert_counts"],
+                    expert_offsets=lay["expert_offsets"], align=align, block=block, err=err)
         if y_slots is None:
             expert_out = expert_buf
         else:
@@ -82,8 +84,8 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
     return res
 
 
-def run_oracle(hid, ids, wts, E, R, y_slots, cap_rank, cap_expert) -> dict:
-    lay = oracle.layout(ids, E, R)
+def run_oracle(hid, ids, wts, E, R, y_slots, cap_rank, cap_expert, align=1, block=0) -> dict:
+    lay = oracle.layout(ids, E, R, align=align, block=block)
     rb, rsrc, e1 = oracle.pack(hid, lay["token_rank_slot"], cap_rank)
     eb, esrc, e2 = oracle.permute(rb, rsrc, lay, ids, E,
                                   cap_expert)
@@ -110,8 +112,13 @@ def compare(gpu: dict, ref: dict, what: str, check_f32: bool = True) -> None:
     assert np.array_equal(gpu["rank_src_all"][:wr], ref["rank_src"][:wr]), f"{what}: rank_src"
     assert np.all(gpu["rank_all"][wr:] == CANARY_ROW), f"{what}: rank rows past C written"
     assert np.all(gpu["rank_src_all"][wr:] == CANARY_IDX), f"{what}: rank_src past C written"
-    # expert rows: every row the oracle wrote (rows of dropped rank copies stay unwritten)
+    # expert rows: every row the oracle wrote (rows of dropped rank copies stay unwritten);
+    # padding rows of padded runs or fixed blocks are marked -1, their data untouched
     written = ref["expert_src"][:we] >= 0
+    pad = ref["expert_src"][:we] == -1
+    assert np.all(gpu["expert_src_all"][:we][pad] == -1), f"{what}: padding rows not marked"
+    assert np.all(gpu["expert_src_all"][:we][~written & ~pad] == CANARY_IDX), \
+        f"{what}: expert_src written where the oracle writes nothing"
     assert np.array_equal(gpu["expert_all"][:we][written], ref["expert_buf"][:we][written]), \
         f"{what}: expert rows"
     assert np.array_equal(gpu["expert_src_all"][:we][written], ref["expert_src"][:we][written]), \

@@ -26,19 +26,20 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == moe.ABI_VERSION == 2
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
 
 
-def shape(T=64, H=512, E=16, R=4, k=2):
-    return moe.MoeShape(T, H, E, R, k)
+def shape(T=64, H=512, E=16, R=4, k=2, align=1, block=0):
+    return moe.MoeShape(T, H, E, R, k, align, block)
 
 
 BAD_SHAPES = [
     dict(T=-1), dict(H=0), dict(H=12), dict(E=0), dict(R=0), dict(R=65, E=130), dict(E=10, R=4),
-    dict(k=0), dict(k=17, E=64), dict(E=2048, R=8), dict(T=1 << 28, k=8),
+    dict(k=0), dict(k=17, E=64), dict(E=2048, R=8), dict(T=1 << 28, k=8), dict(align=0),
+    dict(align=1 << 17), dict(block=-1), dict(block=128, align=2), dict(E=1024, R=8, block=1 << 21),
 ]
 
 
@@ -73,10 +74,17 @@ def test_calls_reject_bad_arguments_without_launching():
                                None) == moe.MOE_ERR_ARG
     assert L.moe_dispatch_pack(sp, FAKE, FAKE, FAKE, FAKE, -1, None, None) == moe.MOE_ERR_ARG
     # permute / combine
-    assert L.moe_permute_by_expert(sp, FAKE, FAKE, None, FAKE, FAKE, 128, FAKE, FAKE, 128,
-                                   None, None) == moe.MOE_ERR_ARG
-    assert L.moe_permute_by_expert(sp, FAKE, FAKE, FAKE, FAKE, FAKE, 128, ctypes.c_void_p(0x10004),
-                                   FAKE, 128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_permute_by_expert(sp, FAKE, FAKE, None, FAKE, FAKE, None, None, 128, FAKE, FAKE,
+                                   128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_permute_by_expert(sp, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 128,
+                                   ctypes.c_void_p(0x10004), FAKE, 128, None,
+                                   None) == moe.MOE_ERR_ARG
+    # a padded or blocked layout needs the expert counts and offsets
+    for pad in (ctypes.byref(shape(align=128)), ctypes.byref(shape(block=64))):
+        assert L.moe_permute_by_expert(pad, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 128, FAKE,
+                                       FAKE, 128, None, None) == moe.MOE_ERR_ARG
+        assert L.moe_permute_by_expert(pad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 128, FAKE,
+                                       FAKE, 128, None, None) == moe.MOE_ERR_ARG
     assert L.moe_combine(sp, FAKE, None, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
     assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, ctypes.c_void_p(0x10002), None,
                          None) == moe.MOE_ERR_ARG
@@ -101,8 +109,8 @@ def test_empty_batches_are_no_ops():
     s0 = ctypes.byref(shape(T=0))
     assert L.moe_dispatch_pack(s0, None, None, None, None, 0, None, None) == moe.MOE_OK
     assert L.moe_combine(s0, None, None, None, 0, None, None, None, None) == moe.MOE_OK
-    assert L.moe_permute_by_expert(s0, None, None, FAKE, None, None, 0, None, None, 0, None,
-                                   None) == moe.MOE_OK
+    assert L.moe_permute_by_expert(s0, None, None, FAKE, None, None, None, None, 0, None, None,
+                                   0, None, None) == moe.MOE_OK
     assert L.moe_combine_rank_partial(s0, None, None, FAKE, None, None, None, 0, 0, None, None,
                                       None, None) == moe.MOE_OK
     assert L.moe_combine_ranks(s0, None, None, 0, None, None, None, None) == moe.MOE_OK
