@@ -44,6 +44,8 @@ class _Lib:
                                                     vp, vp, i64, vp, vp]
         lib.oracle_combine_ranks.restype = ctypes.c_int
         lib.oracle_combine_ranks.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
+        lib.oracle_quantize_mxfp8.restype = None
+        lib.oracle_quantize_mxfp8.argtypes = [i64, i32, vp, vp, vp]
         self.lib = lib
 
 
@@ -203,6 +205,39 @@ def combine_ranks(partial, token_rank_slot, want_f32: bool = True):
     err = _load().oracle_combine_ranks(T, H, R, _p(part), part.shape[0], _p(slots), _p(out),
                                        _p(out32))
     return out, out32, err
+
+
+def quantize_mxfp8(x):
+    """bf16 rows [rows, H] (H a multiple of 32) -> (q [rows, H] uint8 e4m3 codes,
+    scale [rows, H/32] uint8 E8M0 exponents)."""
+    xb = _c(x, np.uint16)
+    rows, H = xb.shape
+    assert H % 32 == 0
+    q = np.zeros((rows, H), np.uint8)
+    sc = np.zeros((rows, H // 32), np.uint8)
+    _load().oracle_quantize_mxfp8(rows, H, _p(xb), _p(q), _p(sc))
+    return q, sc
+
+
+def pack_mxfp8(hidden, token_rank_slot, cap_rank: int):
+    """Quantise every hidden row once, then pack the codes and the scales once
+    per distinct rank (the rows are plain byte copies, as in pack())."""
+    q, sc = quantize_mxfp8(hidden)
+    T, H = q.shape
+    rq, src, err = pack(q.view(np.uint16), token_rank_slot, cap_rank)
+    rs, _, _ = pack(sc.view(np.uint16), token_rank_slot, cap_rank)
+    return rq.view(np.uint8), rs.view(np.uint8), src, err
+
+
+def permute_mxfp8(rank_q, rank_scale, rank_src_token, lay: dict, topk_ids, E: int,
+                  cap_expert: int):
+    """Regroup quantised rows by expert: the codes and the scales each move as
+    permute() moves bf16 rows."""
+    eq, esrc, err = permute(np.ascontiguousarray(rank_q).view(np.uint16), rank_src_token, lay,
+                            topk_ids, E, cap_expert)
+    es, _, _ = permute(np.ascontiguousarray(rank_scale).view(np.uint16), rank_src_token, lay,
+                       topk_ids, E, cap_expert)
+    return eq.view(np.uint8), es.view(np.uint8), esrc, err
 
 
 def place_slots(y_slots: np.ndarray, pair_row: np.ndarray, rows: int) -> np.ndarray:

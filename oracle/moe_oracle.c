@@ -266,3 +266,58 @@ int oracle_combine_ranks(int32_t T, int32_t H, int32_t R, const uint16_t* partia
   }
   return err;
 }
+
+/* The value of a finite OCP FP8 E4M3 code (sign ignored): exponent bias 7,
+ * three mantissa bits, subnormals at exponent field 0. */
+static double e4m3_magnitude(int code) {
+  const int ef = (code >> 3) & 0xF, mf = code & 7;
+  if (ef == 0) return ldexp((double)mf, -9); /* mf/8 * 2^-6 */
+  return ldexp(1.0 + mf / 8.0, ef - 7);
+}
+
+void oracle_quantize_mxfp8(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale) {
+  const int32_t nblk = H / 32;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t b = 0; b < nblk; ++b) {
+      const uint16_t* v = x + r * H + (int64_t)b * 32;
+      uint8_t* out = q + r * H + (int64_t)b * 32;
+      double amax = 0.0;
+      int special = 0;
+      for (int i = 0; i < 32; ++i) {
+        const double a = fabs((double)widen_bf16(v[i]));
+        if (!isfinite(a)) special = 1;
+        else if (a > amax) amax = a;
+      }
+      if (special) {
+        scale[r * nblk + b] = 0xFF;
+        for (int i = 0; i < 32; ++i) out[i] = (uint8_t)(((v[i] >> 15) << 7) | 0x7F);
+        continue;
+      }
+      int e = -127;
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* amax = m * 2^ex with m in [0.5, 1): floor(log2(amax)) = ex - 1 */
+        e = ex - 1 - 8;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+      }
+      scale[r * nblk + b] = (uint8_t)(e + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double val = (double)widen_bf16(v[i]);
+        const double mag = fabs(ldexp(val, -e)); /* exact: a power-of-two scaling */
+        /* nearest of the 127 finite non-negative codes; on a tie, the even code */
+        int best = 0;
+        double best_d = fabs(mag - e4m3_magnitude(0));
+        for (int c = 1; c <= 0x7E; ++c) {
+          const double d = fabs(mag - e4m3_magnitude(c));
+          if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+          }
+        }
+        out[i] = (uint8_t)(((v[i] >> 15) << 7) | best);
+      }
+    }
+  }
+}

@@ -141,6 +141,25 @@ int oracle_combine_ranks(int32_t T, int32_t H, int32_t R, const uint16_t* partia
                          int64_t cap_rank, const int32_t* token_rank_slot, uint16_t* out,
                          float* out_f32);
 
+/*
+ * Quantised wire format for dispatch ([A2A] sec 7.2: a token can be sent as
+ * 8-bit values with a one-byte scale factor for every 32 values, 5,280 bytes
+ * for a 5,120-wide row instead of 10,240). The byte-per-32 scale is read as
+ * the OCP Microscaling (MX) format MXFP8: per block of 32 consecutive values
+ * of a row, with amax the largest magnitude in the block,
+ *   e     = floor(log2(amax)) - 8  (8 = exponent of the largest e4m3 normal, 448),
+ *           clamped to [-127, 127]; amax = 0 gives -127;
+ *   scale = e + 127 as one byte (E8M0, the value 2^e); 0xFF if the block holds
+ *           a NaN or an infinity;
+ *   q_i   = the OCP FP8 E4M3 value nearest to v_i / 2^e (ties to the even
+ *           mantissa; magnitudes past 448 saturate to 448; the sign is kept, so
+ *           a negative value that rounds to zero gives 0x80); in a NaN/Inf block
+ *           every q_i is the e4m3 NaN 0x7F with the value's sign.
+ * Rows of x are H bf16 values; q gets H bytes and scale H/32 bytes per row.
+ */
+void oracle_quantize_mxfp8(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale);
+
 #ifdef __cplusplus
 }
 #endif

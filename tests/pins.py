@@ -800,6 +800,130 @@ def pin_two_stage_caps():
     assert np.array_equal(rc["part32"], full["part32"][:C - 6])
 
 
+# ----------------------------------------------------------------------------
+# quantised dispatch (MXFP8) pins
+
+def _bf16(x) -> np.ndarray:
+    """float values exactly representable in bf16 -> bit patterns."""
+    a = np.asarray(x, np.float32)
+    bits = a.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def _e4m3_table():
+    """Magnitudes of the 127 finite non-negative OCP E4M3 codes, from the
+    format's definition (bias 7, 3 mantissa bits, subnormals at exponent 0)."""
+    vals = []
+    for c in range(0x7F):
+        ef, mf = c >> 3, c & 7
+        vals.append(mf * 2.0 ** -9 if ef == 0 else (1 + mf / 8) * 2.0 ** (ef - 7))
+    return np.array(vals)
+
+
+def pin_mxfp8_every_code_round_trips():
+    """A block whose largest magnitude is 448 (the largest e4m3 normal) has
+    scale 2^0; every finite e4m3 value, of either sign (-0 included), placed
+    in such blocks comes back as its own code."""
+    mags = _e4m3_table()
+    codes = np.concatenate([np.arange(0x7F), np.arange(0x7F) | 0x80])
+    blocks, want = [], []
+    for i in range(0, codes.size, 31):
+        chunk = list(codes[i:i + 31])
+        chunk += [0x7E] * (31 - len(chunk))
+        want.append([0x7E] + chunk)
+    want = np.array(want)
+    vals = np.where(want & 0x80, -1.0, 1.0) * mags[want & 0x7F]
+    x = _bf16(vals.astype(np.float32))
+    q, sc = oracle.quantize_mxfp8(x)
+    assert np.all(sc == 127), sc
+    assert np.array_equal(q, want), np.argwhere(q != want)[:5]
+
+
+def pin_mxfp8_hand_cases():
+    """Hand-derived cases of the OCP MX rule (scale 2^e, e = floor(log2 amax) - 8,
+    clamped to [-127, 127]; nearest e4m3, ties to even, saturating at 448)."""
+    H = 32
+
+    def one_block(values, pad=0.0):
+        v = list(values) + [pad] * (H - len(values))
+        return oracle.quantize_mxfp8(_bf16(np.array([v], np.float32)))
+
+    # amax 1 -> e = -8: 1 -> 256 = 2^8 (0x78); 0.5 -> 2^7 (0x70); -1.5 -> -384 (0xFC)
+    q, sc = one_block([1.0, 0.5, -1.5])
+    assert int(sc[0, 0]) == 127 - 8 and list(q[0, :3]) == [0x78, 0x70, 0xFC], (sc, q[0, :3])
+    # with 448 present e = 0: 1.0625 is halfway between 1 (0x38) and 1.125 (0x39) -> even 0x38;
+    # 1.1875 halfway between 1.125 and 1.25 -> 0x3A; 2^-9 -> 0x01; 2^-10 halfway between 0 and
+    # 2^-9 -> 0x00; 3*2^-10 halfway between 2^-9 and 2^-8 -> 0x02; -2^-11 -> -0 (0x80)
+    q, sc = one_block([448.0, 1.0625, 1.1875, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, -2.0 ** -11])
+    assert int(sc[0, 0]) == 127
+    assert list(q[0, :7]) == [0x7E, 0x38, 0x3A, 0x01, 0x00, 0x02, 0x80], [hex(c) for c in q[0, :7]]
+    # amax 510 -> e = 0 and 510 saturates to 448; 480 too
+    q, sc = one_block([510.0, -480.0, 464.0])
+    assert int(sc[0, 0]) == 127 and list(q[0, :3]) == [0x7E, 0xFE, 0x7E]
+    # smallest bf16 subnormal 2^-133: e = -141 clamps to -127, 2^-133 / 2^-127 = 2^-6 (0x08)
+    q, sc = oracle.quantize_mxfp8(np.array([[0x0001] + [0] * 31], np.uint16))
+    assert int(sc[0, 0]) == 0 and q[0, 0] == 0x08 and np.all(q[0, 1:] == 0)
+    # 1.5 * 2^127: e = 119, value / 2^119 = 384 (0x7C)
+    q, sc = oracle.quantize_mxfp8(np.array([[0x7F40] + [0] * 31], np.uint16))
+    assert int(sc[0, 0]) == 127 + 119 and q[0, 0] == 0x7C
+    # an all-zero block: scale 2^-127, codes 0 (and 0x80 for -0)
+    q, sc = oracle.quantize_mxfp8(np.array([[0x0000, 0x8000] + [0] * 30], np.uint16))
+    assert int(sc[0, 0]) == 0 and q[0, 0] == 0x00 and q[0, 1] == 0x80
+    # a NaN or an infinity makes the block's scale NaN (0xFF) and its codes NaN with their sign
+    for bad in (0x7FC0, 0x7F80, 0xFF80):
+        q, sc = oracle.quantize_mxfp8(np.array([[0x3F80, bad, 0xBF80] + [0] * 29], np.uint16))
+        assert int(sc[0, 0]) == 0xFF and q[0, 0] == 0x7F and q[0, 2] == 0xFF
+        assert q[0, 1] == (0xFF if bad & 0x8000 else 0x7F)
+
+
+def pin_mxfp8_error_bound():
+    """Random rows of several magnitudes: the block maximum lands in [256, 512)
+    after scaling (e is the largest exponent that does not push it to 512 or
+    past), and every element is within half an e4m3 step of its value
+    (2^-4 relative for normals, 2^-10 absolute below 2^-6), unless it
+    saturated at 448."""
+    rng = np.random.default_rng(107)
+    mags = _e4m3_table()
+    for spread in (1.0, 8.0, 30.0):
+        vals = rng.standard_normal((64, 256)) * np.exp2(rng.uniform(-spread, spread, (64, 256)))
+        x = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # truncate to bf16
+        q, sc = oracle.quantize_mxfp8(x)
+        xf = bf16_bits_to_float(x).astype(np.float64).reshape(64, 8, 32)
+        e = sc.astype(np.int64) - 127
+        scaled = np.abs(xf) / np.exp2(e)[:, :, None]
+        top = scaled.max(axis=2)
+        ok = (e > -127) & (e < 127)
+        assert np.all((top[ok] >= 256) & (top[ok] < 512))
+        deq = mags[(q & 0x7F).reshape(64, 8, 32)]
+        sat = scaled > 448
+        err = np.abs(deq - scaled)
+        lim = np.maximum(np.exp2(np.floor(np.log2(np.maximum(scaled, 2.0 ** -6))) - 4), 2.0 ** -10)
+        assert np.all((err <= lim) | sat)
+        assert np.all(deq[sat] == 448)
+        sign = (q.reshape(64, 8, 32) & 0x80) != 0
+        assert np.all(sign == (xf < 0) | ((xf == 0) & np.signbit(xf)))
+
+
+def pin_mxfp8_pack_and_permute():
+    """The quantised dispatch moves bytes only: every packed row holds the codes
+    and scales of its source token's quantised row, every expert row those of
+    its rank-buffer row."""
+    rng = np.random.default_rng(109)
+    T, E, R, k, H = 80, 32, 4, 4, 128
+    ids = rand_ids(rng, T, E, k, p_neg=0.1)
+    hid = synth.normal_bf16(25, 0, T * H).reshape(T, H)
+    lay = oracle.layout(ids, E, R)
+    q, sc = oracle.quantize_mxfp8(hid)
+    rq, rs, src, err = oracle.pack_mxfp8(hid, lay["token_rank_slot"], T * min(k, R))
+    C = int(lay["rank_offsets"][-1])
+    assert err == 0 and np.array_equal(rq[:C], q[src[:C]]) and np.array_equal(rs[:C], sc[src[:C]])
+    eq, es, esrc, err2 = oracle.permute_mxfp8(rq, rs, src, lay, ids, E, T * k)
+    P = int(lay["expert_offsets"][-1])
+    t_of = esrc[:P] // k
+    assert err2 == 0 and np.array_equal(eq[:P], q[t_of]) and np.array_equal(es[:P], sc[t_of])
+
+
 PINS = [
     pin_layout_stable_sort,
     pin_layout_brute_force,
@@ -829,4 +953,8 @@ PINS = [
     pin_two_stage_one_rank,
     pin_two_stage_exact_bound,
     pin_two_stage_caps,
+    pin_mxfp8_every_code_round_trips,
+    pin_mxfp8_hand_cases,
+    pin_mxfp8_error_bound,
+    pin_mxfp8_pack_and_permute,
 ]

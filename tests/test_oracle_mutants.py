@@ -110,6 +110,27 @@ MUTANTS = {
     "padding marks one row too many": (
         "row < end && row < cap_expert; ++row)",
         "row <= end && row < cap_expert; ++row)"),
+    "mx exponent off by one (emax 7)": (
+        "e = ex - 1 - 8;",
+        "e = ex - 1 - 7;"),
+    "mx ceiling of log2": (
+        "e = ex - 1 - 8;",
+        "e = ex - 8;"),
+    "mx scale not clamped below": (
+        "if (e < -127) e = -127;",
+        "if (e < -160) e = -160;"),
+    "mx ties away from zero": (
+        "if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {",
+        "if (d <= best_d) {"),
+    "mx drops the sign": (
+        "out[i] = (uint8_t)(((v[i] >> 15) << 7) | best);",
+        "out[i] = (uint8_t)best;"),
+    "mx ignores NaN blocks": (
+        "if (!isfinite(a)) special = 1;\n        else if (a > amax) amax = a;",
+        "if (!isfinite(a)) special = 0;\n        else if (a > amax) amax = a;"),
+    "e4m3 subnormals one binade low": (
+        "if (ef == 0) return ldexp((double)mf, -9);",
+        "if (ef == 0) return ldexp((double)mf, -10);"),
     "f64 combine rounds products to float": (
         "acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);",
         "acc += (double)(topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]));"),
