@@ -50,6 +50,17 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
     }
 
 
+def mxfp8_bytes(T, H, R, k, C, P):
+    """Bytes of the quantised dispatch: the fused quantise-and-pack reads each
+    bf16 hidden row once and writes H codes + H/32 scales per copy; the permute
+    reads each quantised rank row once and writes it once per pair."""
+    qrow = H + H // 32
+    return {
+        "pack": 2 * T * H + C * qrow + 4 * T * R + 4 * C,
+        "permute": C * qrow + P * qrow + 4 * C + 8 * T * k + 4 * P,
+    }
+
+
 def two_stage_bytes(T, H, R, k, C, P):
     """Bytes of the two-stage combine: the per-rank partial rows (each expert
     row read once, each partial row written once, the token's ids, pair rows
@@ -218,7 +229,8 @@ class Rig:
     """One workload resident on the GPU with every buffer of a pass, and the
     four library calls on the current stream."""
 
-    def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0):
+    def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0,
+                 mxfp8: bool = False):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -249,6 +261,18 @@ class Rig:
         self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         self.stream = torch.cuda.current_stream(dev)
         self.calls = CALLS
+        self.mxfp8 = mxfp8
+        if mxfp8:
+            # quantised dispatch: codes and scales replace the bf16 rank and expert rows
+            u8 = torch.uint8
+            self.rank_q = torch.empty((self.shape.cap_rank, w.H), dtype=u8, device=dev)
+            self.rank_s = torch.empty((self.shape.cap_rank, w.H // 32), dtype=u8, device=dev)
+            self.exp_q = torch.empty((self.shape.cap_expert, w.H), dtype=u8, device=dev)
+            self.exp_s = torch.empty((self.shape.cap_expert, w.H // 32), dtype=u8, device=dev)
+            self.buf.rank_buf = self.buf.expert_buf = None
+            torch.cuda.empty_cache()
+            self.nbytes.update(mxfp8_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
+            self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         if two_stage:
             self.partial = torch.empty((self.shape.cap_rank, w.H), dtype=torch.bfloat16,
                                        device=dev)
@@ -261,9 +285,18 @@ class Rig:
         if name == "layout":
             moe.layout(self.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
                        out=b.layout_dict())
+        elif name == "pack" and self.mxfp8:
+            moe.pack_mxfp8(self.hid_d, b.token_rank_slot, s.E, s.k, self.rank_q, self.rank_s,
+                           b.rank_src_token, err=b.err)
         elif name == "pack":
             moe.pack(self.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
                      err=b.err)
+        elif name == "permute" and self.mxfp8:
+            moe.permute_mxfp8(self.rank_q, self.rank_s, b.rank_src_token, b.rank_offsets,
+                              self.ids_d, b.pair_row, s.E, self.exp_q, self.exp_s,
+                              b.expert_src_pair, expert_counts=b.expert_counts,
+                              expert_offsets=b.expert_offsets, align=s.align, block=s.block,
+                              err=b.err)
         elif name == "permute":
             moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
                         s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
@@ -355,13 +388,15 @@ def sweep(names, dev, with_oracle: bool) -> None:
     for spec in names:
         # "name" or "name:align=128" / "name:block=128" (padded or masked expert layout)
         name, _, opt = spec.partition(":")
-        opts = dict(kv.split("=") for kv in opt.split(",") if kv)
+        opts = dict(kv.split("=") for kv in opt.split(",") if "=" in kv)
         align, block = int(opts.get("align", 1)), int(opts.get("block", 0))
+        mx = "mxfp8" in opt.split(",")
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev, two_stage=True, align=align, block=block)
+        rig = Rig(w, dev, two_stage=True, align=align, block=block, mxfp8=mx)
         for _ in range(5):
             rig.step()
         res = {"workload": w.describe(), "layout_shape": {"align": align, "block": block},
+               "dispatch_format": "mxfp8" if mx else "bf16",
                "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
                "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
         for mode, fl in (("warm", None), ("cold", flush)):
@@ -400,7 +435,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
             "combine_pairs": round(rig.P / (warm["combine"]["warm"]["us"] * 1e-6))}
         res["bytes"] = tot
         res["two_stage_bytes"] = tot2
-        if with_oracle and align == 1 and block == 0:
+        if with_oracle and align == 1 and block == 0 and not mx:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
                                           3 if w.T * w.H > 2 ** 25 else 5)
@@ -441,7 +476,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
-                    const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128",
+                    const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
+                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8",
                     default=None,
                     metavar="WORKLOADS", help="per-call warm/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",

@@ -27,7 +27,7 @@ ERRBIT_EXPERT_CAP = 4
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout", "moe_dispatch_pack",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
-           "moe_combine_ranks")
+           "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8")
 
 
 ABI_VERSION = 2
@@ -79,6 +79,11 @@ def lib():
     L.moe_combine_rank_partial.argtypes = [shp, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
     L.moe_combine_ranks.restype = ctypes.c_int
     L.moe_combine_ranks.argtypes = [shp, vp, vp, i64, vp, vp, vp, vp]
+    L.moe_dispatch_pack_mxfp8.restype = ctypes.c_int
+    L.moe_dispatch_pack_mxfp8.argtypes = [shp, vp, vp, vp, vp, vp, i64, vp, vp]
+    L.moe_permute_by_expert_mxfp8.restype = ctypes.c_int
+    L.moe_permute_by_expert_mxfp8.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp,
+                                              vp, i64, vp, vp]
     if L.moe_abi_version() != ABI_VERSION:
         raise MoeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, this binding "
                        f"expects {ABI_VERSION}: rebuild with __graft_entry__.build()")
@@ -199,6 +204,46 @@ def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, 
         rank_buf.shape[0], _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)),
         expert_buf.shape[0], _ptr(err), _stream(rank_buf.device))
     _check(st, "moe_permute_by_expert")
+
+
+def _bytes(t: torch.Tensor) -> torch.Tensor:
+    if t.element_size() != 1 or not t.is_contiguous():
+        raise MoeError(f"expected a contiguous 8-bit tensor, got {t.dtype}")
+    return t
+
+
+def pack_mxfp8(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, rank_q,
+               rank_scale, rank_src_token, *, err=None) -> None:
+    """moe_dispatch_pack_mxfp8: quantise each hidden row once to MXFP8 and pack
+    it once per distinct rank into rank_q [cap_rank, H] (uint8 e4m3 codes) and
+    rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
+    T, H = hidden.shape
+    R = token_rank_slot.shape[1]
+    shape = Shape(T, H, E, R, k)
+    st = lib().moe_dispatch_pack_mxfp8(
+        ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
+        _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
+        rank_q.shape[0], _ptr(err), _stream(hidden.device))
+    _check(st, "moe_dispatch_pack_mxfp8")
+
+
+def permute_mxfp8(rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids, pair_row, E: int,
+                  expert_q, expert_scale, expert_src_pair, *, expert_counts=None,
+                  expert_offsets=None, align: int = 1, block: int = 0, err=None) -> None:
+    """moe_permute_by_expert_mxfp8: the codes and scales of each rank-buffer row
+    to the rows of its token's experts on that rank."""
+    T, k = topk_ids.shape
+    H = rank_q.shape[1]
+    R = rank_offsets.shape[0] - 1
+    shape = Shape(T, H, E, R, k, align, block)
+    st = lib().moe_permute_by_expert_mxfp8(
+        ctypes.byref(shape.c()), _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)),
+        _ptr(_i32(rank_src_token)), _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)),
+        _ptr(_i32(pair_row)), _ptr(None if expert_counts is None else _i32(expert_counts)),
+        _ptr(None if expert_offsets is None else _i32(expert_offsets)), rank_q.shape[0],
+        _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)), _ptr(_i32(expert_src_pair)),
+        expert_q.shape[0], _ptr(err), _stream(rank_q.device))
+    _check(st, "moe_permute_by_expert_mxfp8")
 
 
 def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=None,

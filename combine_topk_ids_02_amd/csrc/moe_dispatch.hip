@@ -51,6 +51,7 @@ constexpr int kMaxRanks = 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxVec = 16;                 // vec4 per lane held in registers per pass
 constexpr int kMaxAlign = 1 << 16;          // largest run padding
+constexpr int kMxRowQuantum = 512;          // MXFP8 rows: H a multiple of 512 (whole vec4 of scales)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -588,14 +589,137 @@ __device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts
 // With a padded or blocked layout, the first pad_waves = E waves mark one
 // expert's padding rows each (first, so that their latency hides under the
 // row copies); then one wave per rank-buffer row.
+// ---------------------------------------------------------------------------
+// MXFP8 wire format: per block of 32 consecutive values of a row, one E8M0
+// scale byte (2^e, e = floor(log2 amax) - 8 clamped to [-127, 127]; 0xFF if the
+// block holds a NaN or an infinity) and 32 OCP e4m3 codes of v / 2^e, nearest
+// with ties to even, saturating at 448, sign kept.
+
+// e of a block from the largest magnitude's bf16 bits (0 < amax < 0x7F80).
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax) {
+  if (amax == 0) return -127;
+  const int eb = int(amax >> 7);
+  // floor(log2): a normal bf16 has it in its exponent field; a subnormal
+  // m * 2^-133 has it at the top set bit of m.
+  const int lg = eb > 0 ? eb - 127 : -133 + (31 - __clz(int(amax & 0x7F)));
+  return min(127, max(-127, lg - 8));
+}
+
+typedef short mx_short2 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four bf16 (two words) divided by the block scale and rounded to e4m3 by the
+// gfx950 scaled conversion (nearest, ties to even), bytes in element order.
+// The conversion turns a magnitude that rounds past 448 into NaN (0x7F with
+// the sign); in a block of finite values that can only be such an overflow,
+// so those bytes are lowered by one, to +-448: the saturation of the MX rule.
+__device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float scale) {
+  mx_short2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(mx_bf16x2, w0), scale,
+                                                false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(mx_bf16x2, w1), scale,
+                                                true);
+  const uint32_t x = __builtin_bit_cast(uint32_t, r);
+  const uint32_t nan_bytes = ((x & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+  return x - (nan_bytes >> 7);
+}
+
+// Quantises the 8 bf16 of `v` (one quarter of a 32-value block, the other
+// quarters in the neighbouring lanes of the same lane quad) to 8 e4m3 codes
+// (lo, hi: little-endian bytes) and returns the block's scale byte.
+__device__ __forceinline__ uint32_t mx_quantise(vec4 v, uint32_t& lo, uint32_t& hi) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    amax = max(amax, v[i] & 0x7FFFu);
+    amax = max(amax, (v[i] >> 16) & 0x7FFFu);
+  }
+  amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, kWave)));
+  amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
+  if (amax >= 0x7F80u) {  // NaN or infinity in the block
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[2 * i] = ((v[i] >> 8) & 0x80u) | 0x7Fu;
+      c[2 * i + 1] = ((v[i] >> 24) & 0x80u) | 0x7Fu;
+    }
+    lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    return 0xFFu;
+  }
+  const int e = mx_block_exponent(amax);
+  const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // the E8M0 byte as a float exponent
+  lo = e4m3x4(v[0], v[1], scale);
+  hi = e4m3x4(v[2], v[3], scale);
+  return uint32_t(e + 127);
+}
+
+// Fused quantise-and-pack: one wave per token, the row read once and
+// quantised once in registers, then written (codes and scales) to every rank
+// in the token's set. Passes of V groups of 64 vec4, V dividing the row's
+// group count (H is a multiple of 512). Codes and scales are stored with
+// ordinary stores, like the bf16 copies, for the permute to find in cache.
 template <int V>
+__global__ __launch_bounds__(kBlock) void pack_rows_mx(
+    const vec4* hidden, const int32_t* __restrict__ token_rank_slot, uint8_t* rank_q,
+    uint8_t* rank_scale, int32_t* __restrict__ rank_src_token, int T, int R, int nvec,
+    int64_t cap_rank, int32_t* err_word) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int slot = lane < R ? token_rank_slot[(int64_t)t * R + lane] : -1;
+  const bool ok = slot >= 0 && slot < cap_rank;
+  if (__ballot(slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+  if (ok) rank_src_token[slot] = t;
+  const uint64_t dests = __ballot(ok);
+  if (!dests) return;
+  const int64_t qrow = (int64_t)nvec * 8;  // bytes of codes per row (H)
+  const int64_t srow = nvec / 4;           // scale bytes per row (H / 32)
+  const vec4* src = hidden + (int64_t)t * nvec;
+  for (int c0 = 0; c0 < nvec; c0 += kWave * V) {
+    vec4 v[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) v[q] = load_row<true>(src + c0 + q * kWave + lane);
+    uint32_t lo[V], hi[V], sw[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const uint32_t sb = mx_quantise(v[q], lo[q], hi[q]);
+      // lanes 16w collect the scale bytes of blocks 4w..4w+3 (lanes 16w, +4, +8, +12)
+      sw[q] = sb | (uint32_t(__shfl(int(sb), lane + 4, kWave)) << 8) |
+              (uint32_t(__shfl(int(sb), lane + 8, kWave)) << 16) |
+              (uint32_t(__shfl(int(sb), lane + 12, kWave)) << 24);
+    }
+    uint64_t d = dests;
+    while (d) {
+      const int which = __ffsll((unsigned long long)d) - 1;
+      d &= d - 1;
+      const int64_t row = read_lane(slot, which);
+      uint8_t* qdst = rank_q + row * qrow;
+      uint8_t* sdst = rank_scale + row * srow;
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const int col = c0 + q * kWave + lane;
+        uint2 w;
+        w.x = lo[q];
+        w.y = hi[q];
+        *reinterpret_cast<uint2*>(qdst + (int64_t)col * 8) = w;
+        if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sdst + col / 4) = sw[q];
+      }
+    }
+  }
+}
+
+// kMx: the rows are MXFP8 codes, and each also has a row of nvec_s vec4 of
+// scales in rank_scale / expert_scale that moves with it.
+template <int V, bool kMx>
 __global__ __launch_bounds__(kBlock) void permute_rows(
-    const vec4* rank_buf, const int32_t* __restrict__ rank_src_token,
+    const vec4* rank_buf, const vec4* rank_scale, const int32_t* __restrict__ rank_src_token,
     const int32_t* __restrict__ rank_offsets, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ pair_row, const int32_t* __restrict__ expert_counts,
-    const int32_t* __restrict__ expert_offsets, vec4* expert_buf,
+    const int32_t* __restrict__ expert_offsets, vec4* expert_buf, vec4* expert_scale,
     int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int block,
-    int nvec, int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
+    int nvec, int nvec_s, int pad_waves, int64_t cap_rank, int64_t cap_expert,
+    int32_t* err_word) {
   const int lane = lane_id();
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (gw < pad_waves) {
@@ -619,7 +743,9 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   const uint64_t dests = __ballot(ok);
   // The packed row is read once and the expert rows are not read again here:
   // both streamed.
-  if (dests) fan_out_row<V, true, true>(rank_buf + i * nvec, expert_buf, p, dests, nvec);
+  if (!dests) return;
+  fan_out_row<V, true, true>(rank_buf + i * nvec, expert_buf, p, dests, nvec);
+  if (kMx) fan_out_row<1, true, true>(rank_scale + i * nvec_s, expert_scale, p, dests, nvec_s);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -825,6 +951,14 @@ int copy_vec(int nvec) {
   return kMaxVec;
 }
 
+// MXFP8 pack: passes of V groups of 64 vec4, V the largest divisor of the
+// group count that is at most 16 (so every pass is whole).
+int mx_vec(int groups) {
+  for (int v = std::min(groups, kMaxVec); v > 1; --v)
+    if (groups % v == 0) return v;
+  return 1;
+}
+
 // Combine: slices of at most 8 groups (8 x 8 fp32 accumulators per lane),
 // as few slices as cover the row.
 void combine_tiling(int nvec, int* v, int* slices) {
@@ -864,14 +998,28 @@ struct PackLaunch {
 
 template <int V>
 struct PermuteLaunch {
-  static void go(dim3 grid, hipStream_t st, const vec4* rb, const int32_t* src,
+  static void go(dim3 grid, hipStream_t st, const vec4* rb, const vec4* rs, const int32_t* src,
                  const int32_t* roff, const int32_t* ids, const int32_t* prow,
-                 const int32_t* ecnt, const int32_t* eoff, vec4* eb, int32_t* esrc, int T, int E,
-                 int R, int k, int m, int block, int nvec, int pad_waves, int64_t cap_rank,
-                 int64_t cap_expert, int32_t* err) {
-    hipLaunchKernelGGL(permute_rows<V>, grid, dim3(kBlock), 0, st, rb, src, roff, ids, prow,
-                       ecnt, eoff, eb, esrc, T, E, R, k, m, block, nvec, pad_waves, cap_rank,
-                       cap_expert, err);
+                 const int32_t* ecnt, const int32_t* eoff, vec4* eb, vec4* es, int32_t* esrc,
+                 int T, int E, int R, int k, int m, int block, int nvec, int nvec_s,
+                 int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
+    if (rs)
+      hipLaunchKernelGGL((permute_rows<V, true>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
+                         ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
+                         pad_waves, cap_rank, cap_expert, err);
+    else
+      hipLaunchKernelGGL((permute_rows<V, false>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
+                         ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
+                         pad_waves, cap_rank, cap_expert, err);
+  }
+};
+
+template <int V>
+struct PackMxLaunch {
+  static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots, uint8_t* rq,
+                 uint8_t* rs, int32_t* src, int T, int R, int nvec, int64_t cap, int32_t* err) {
+    hipLaunchKernelGGL(pack_rows_mx<V>, grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src, T, R,
+                       nvec, cap, err);
   }
 };
 
@@ -905,6 +1053,39 @@ struct RankSumLaunch {
                        R, nvec, slices, cap_rank, err);
   }
 };
+
+// The permute for bf16 rows (rank_scale == NULL) or MXFP8 rows (codes of
+// nvec vec4 plus scales of nvec_s vec4 per row).
+int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_scale,
+                 const int32_t* rank_src_token, const int32_t* rank_offsets,
+                 const int32_t* topk_ids, const int32_t* pair_row, const int32_t* expert_counts,
+                 const int32_t* expert_offsets, int64_t cap_rank, void* expert_rows,
+                 void* expert_scale, int32_t* expert_src_pair, int64_t cap_expert,
+                 int32_t* err_word, void* stream, int nvec, int nvec_s) {
+  if (cap_rank < 0 || cap_expert < 0) return MOE_ERR_ARG;
+  if (!rank_offsets) return MOE_ERR_ARG;
+  const bool padded = sh.align > 1 || sh.block > 0;
+  if (padded && (!expert_counts || !expert_offsets)) return MOE_ERR_ARG;
+  const int64_t max_rows = std::min<int64_t>(cap_rank, int64_t(sh.T) * std::min(sh.k, sh.R));
+  const int pad_waves = padded && cap_expert > 0 ? sh.E : 0;
+  if (max_rows + pad_waves == 0) return MOE_OK;
+  // With no rows to move (T = 0) only the padding marks are written: the
+  // row buffers and token arrays are not touched and may be NULL.
+  if (max_rows > 0 && (!rank_rows || !rank_src_token || !topk_ids || !pair_row ||
+                       (cap_expert > 0 && !expert_rows)))
+    return MOE_ERR_ARG;
+  if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
+  if (!aligned16(rank_rows) || !aligned16(expert_rows)) return MOE_ERR_ARG;
+  ByVec<PermuteLaunch>::run(copy_vec(nvec), dim3(blocks_for(max_rows + pad_waves)),
+                            static_cast<hipStream_t>(stream),
+                            static_cast<const vec4*>(rank_rows),
+                            static_cast<const vec4*>(rank_scale), rank_src_token, rank_offsets,
+                            topk_ids, pair_row, expert_counts, expert_offsets,
+                            static_cast<vec4*>(expert_rows), static_cast<vec4*>(expert_scale),
+                            expert_src_pair, sh.T, sh.E, sh.R, sh.k, sh.E / sh.R, sh.block, nvec,
+                            nvec_s, pad_waves, cap_rank, cap_expert, err_word);
+  return launch_status();
+}
 
 }  // namespace
 
@@ -957,30 +1138,50 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
                           const int32_t* expert_counts, const int32_t* expert_offsets,
                           int64_t cap_rank, uint16_t* expert_buf, int32_t* expert_src_pair,
                           int64_t cap_expert, int32_t* err_word, void* stream) {
-  if (!shape_ok(shape) || cap_rank < 0 || cap_expert < 0) return MOE_ERR_ARG;
-  if (!rank_offsets) return MOE_ERR_ARG;
-  const bool padded = shape->align > 1 || shape->block > 0;
-  if (padded && (!expert_counts || !expert_offsets)) return MOE_ERR_ARG;
+  if (!shape_ok(shape)) return MOE_ERR_ARG;
+  return permute_impl(*shape, rank_buf, nullptr, rank_src_token, rank_offsets, topk_ids,
+                      pair_row, expert_counts, expert_offsets, cap_rank, expert_buf, nullptr,
+                      expert_src_pair, cap_expert, err_word, stream, shape->H / 8, 0);
+}
+
+int moe_dispatch_pack_mxfp8(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream) {
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0 || cap_rank < 0) return MOE_ERR_ARG;
+  if (shape->T == 0) return MOE_OK;
+  if (!hidden || !token_rank_slot || (cap_rank > 0 && (!rank_q || !rank_scale || !rank_src_token)))
+    return MOE_ERR_ARG;
+  if (!aligned16(hidden) || !aligned16(rank_q) || !aligned16(rank_scale)) return MOE_ERR_ARG;
+  const int nvec = shape->H / 8;
+  ByVec<PackMxLaunch>::run(mx_vec(nvec / kWave), dim3(blocks_for(shape->T)),
+                           static_cast<hipStream_t>(stream),
+                           reinterpret_cast<const vec4*>(hidden), token_rank_slot, rank_q,
+                           rank_scale, rank_src_token, shape->T, shape->R, nvec, cap_rank,
+                           err_word);
+  return launch_status();
+}
+
+int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream) {
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0) return MOE_ERR_ARG;
   const int64_t max_rows =
       std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
-  const int pad_waves = padded && cap_expert > 0 ? shape->E : 0;
-  if (max_rows + pad_waves == 0) return MOE_OK;
-  // With no rows to move (T = 0) only the padding marks are written: the
-  // row buffers and token arrays are not touched and may be NULL.
-  if (max_rows > 0 && (!rank_buf || !rank_src_token || !topk_ids || !pair_row ||
-                       (cap_expert > 0 && !expert_buf)))
-    return MOE_ERR_ARG;
-  if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
-  if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
-  const int nvec = shape->H / 8;
-  ByVec<PermuteLaunch>::run(copy_vec(nvec), dim3(blocks_for(max_rows + pad_waves)),
-                            static_cast<hipStream_t>(stream),
-                            reinterpret_cast<const vec4*>(rank_buf), rank_src_token, rank_offsets,
-                            topk_ids, pair_row, expert_counts, expert_offsets,
-                            reinterpret_cast<vec4*>(expert_buf), expert_src_pair, shape->T,
-                            shape->E, shape->R, shape->k, shape->E / shape->R, shape->block,
-                            nvec, pad_waves, cap_rank, cap_expert, err_word);
-  return launch_status();
+  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
+  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
+  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
+  // a non-null marker selects the two-row kernel even when nothing is moved
+  const void* rs = rank_scale ? rank_scale : static_cast<const void*>(rank_q);
+  return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
+                      expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
+                      expert_src_pair, cap_expert, err_word, stream, shape->H / 16,
+                      shape->H / 512);
 }
 
 int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int32_t* pair_row,

@@ -172,6 +172,46 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
                           int64_t cap_expert, int32_t* err_word, void* stream);
 
 /*
+ * Quantised dispatch, step 2: fused quantise-and-pack to MXFP8 ([A2A] sec 7.2:
+ * a token can travel as 8-bit values with a one-byte scale for every 32
+ * values, 5,280 bytes for a 5,120-wide row instead of 10,240; the expert kernel
+ * takes that format as input). Each hidden row is read once and quantised once;
+ * its codes and scales are written to every row token_rank_slot[t*R+r] >= 0.
+ * The one-byte scale is read as OCP MX: per block of 32 consecutive values,
+ * scale byte = e + 127 with e = floor(log2(max |v|)) - 8 clamped to [-127, 127]
+ * (0xFF if the block holds a NaN or an infinity), and each code is the OCP FP8
+ * E4M3 value nearest to v / 2^e (ties to the even mantissa, magnitudes past 448
+ * saturate to 448, sign kept; NaN codes in a NaN/Inf block).
+ *   hidden [T*H] in: bf16; token_rank_slot [T*R] in
+ *   rank_q [cap_rank*H] out: e4m3 codes; rank_scale [cap_rank*H/32] out: E8M0 scales
+ *   rank_src_token [cap_rank] out; cap_rank as for moe_dispatch_pack
+ * Requires H % 512 == 0 (whole 16-byte groups of scales); rank_q and
+ * rank_scale 16-byte aligned.
+ */
+int moe_dispatch_pack_mxfp8(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream);
+
+/*
+ * Quantised dispatch, step 3: moe_permute_by_expert for MXFP8 rows. Each
+ * rank-buffer row's H codes and H/32 scales move together to the rows
+ * pair_row[t*k+j] of its token's experts on that rank, exactly as bf16 rows do
+ * (same grouping, padding marks and error handling).
+ *   rank_q [cap_rank*H], rank_scale [cap_rank*H/32] in
+ *   expert_q [cap_expert*H], expert_scale [cap_expert*H/32] out
+ *   other arguments as for moe_permute_by_expert. Requires H % 512 == 0.
+ */
+int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream);
+
+/*
  * Combine ([A2A] sec 1.1: the MoE output of a token is the sum of its chosen
  * experts' outputs, each multiplied by its weight; sec 7.1: the sum is taken
  * in 32-bit floats; [GPUs] sec 3.3: a fixed addition order makes the result

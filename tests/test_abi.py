@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "moe_dispatch.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -102,6 +102,26 @@ def test_calls_reject_bad_arguments_without_launching():
     assert L.moe_combine_ranks(sp, ctypes.c_void_p(0x10008), FAKE, 128, FAKE, None, None,
                                None) == moe.MOE_ERR_ARG
     assert L.moe_combine_ranks(sp, FAKE, FAKE, -3, FAKE, None, None, None) == moe.MOE_ERR_ARG
+
+
+def test_mxfp8_calls_reject_bad_arguments():
+    L = moe.lib()
+    ok = ctypes.byref(shape(H=1024))
+    for bad in (ctypes.byref(shape(H=520)), ctypes.byref(shape(H=1000)), ctypes.byref(shape(E=10))):
+        assert L.moe_dispatch_pack_mxfp8(bad, FAKE, FAKE, FAKE, FAKE, FAKE, 128, None,
+                                         None) == moe.MOE_ERR_ARG
+        assert L.moe_permute_by_expert_mxfp8(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                             128, FAKE, FAKE, FAKE, 128, None,
+                                             None) == moe.MOE_ERR_ARG
+    # NULL codes / scales, misaligned scales
+    assert L.moe_dispatch_pack_mxfp8(ok, FAKE, FAKE, None, FAKE, FAKE, 128, None,
+                                     None) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_pack_mxfp8(ok, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10001), FAKE, 128,
+                                     None, None) == moe.MOE_ERR_ARG
+    assert L.moe_permute_by_expert_mxfp8(ok, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, 128,
+                                         FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
+    assert L.moe_permute_by_expert_mxfp8(ok, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 128,
+                                         FAKE, None, FAKE, 128, None, None) == moe.MOE_ERR_ARG
 
 
 def test_empty_batches_are_no_ops():

@@ -1,0 +1,156 @@
+"""GPU parity of the quantised dispatch (fused MXFP8 quantise-and-pack, and the
+permute of quantised rows) against the oracle, through the C ABI: codes,
+scales, source ids and untouched canary rows, bit for bit. Integer work, so the
+bar is bit-exact."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_ids_02_amd as moe
+import oracle
+import pins
+import synth
+from synth import staging
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 0xA5
+CANARY_IDX = -5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests must run on an MI355X")
+    moe.lib()
+
+
+def run_gpu(hid, ids, E, R, align=1, block=0, cap_rank=None, cap_expert=None, spare=4):
+    T, H = hid.shape
+    k = ids.shape[1]
+    shape = moe.Shape(T, H, E, R, k, align, block)
+    cap_rank = shape.cap_rank if cap_rank is None else cap_rank
+    cap_expert = shape.cap_expert if cap_expert is None else cap_expert
+    dev = torch.device("cuda:0")
+    u8, i32 = torch.uint8, torch.int32
+    hid_d = staging.rows_to_device(hid, dev)
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
+    err = torch.zeros(1, dtype=i32, device=dev)
+    lay = moe.layout(ids_d, E, R, H, align=align, block=block, err=err)
+    rq = torch.full((cap_rank + spare, H), CANARY, dtype=u8, device=dev)
+    rs = torch.full((cap_rank + spare, H // 32), CANARY, dtype=u8, device=dev)
+    rsrc = torch.full((cap_rank + spare,), CANARY_IDX, dtype=i32, device=dev)
+    eq = torch.full((cap_expert + spare, H), CANARY, dtype=u8, device=dev)
+    es = torch.full((cap_expert + spare, H // 32), CANARY, dtype=u8, device=dev)
+    esrc = torch.full((cap_expert + spare,), CANARY_IDX, dtype=i32, device=dev)
+    moe.pack_mxfp8(hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
+                   rsrc[:cap_rank], err=err)
+    moe.permute_mxfp8(rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"], ids_d,
+                      lay["pair_row"], E, eq[:cap_expert], es[:cap_expert], esrc[:cap_expert],
+                      expert_counts=lay["expert_counts"], expert_offsets=lay["expert_offsets"],
+                      align=align, block=block, err=err)
+    torch.cuda.synchronize()
+    out = {key: v.cpu().numpy() for key, v in lay.items()}
+    out.update(rq=rq.cpu().numpy(), rs=rs.cpu().numpy(), rsrc=rsrc.cpu().numpy(),
+               eq=eq.cpu().numpy(), es=es.cpu().numpy(), esrc=esrc.cpu().numpy(),
+               err=int(err.item()), cap_rank=cap_rank, cap_expert=cap_expert)
+    return out
+
+
+def check(hid, ids, E, R, what, align=1, block=0, **kw):
+    g = run_gpu(hid, ids, E, R, align, block, **kw)
+    T, k = ids.shape
+    lay = oracle.layout(ids, E, R, align=align, block=block)
+    for key in ("token_rank_slot", "pair_row", "rank_offsets", "expert_offsets"):
+        assert np.array_equal(g[key], lay[key]), f"{what}: layout {key}"
+    cr, ce = g["cap_rank"], g["cap_expert"]
+    rq, rs, src, e1 = oracle.pack_mxfp8(hid, lay["token_rank_slot"], cr)
+    eq, es, esrc, e2 = oracle.permute_mxfp8(rq, rs, src, lay, ids, E, ce)
+    assert g["err"] == lay["err"] | e1 | e2, f"{what}: error word {g['err']}"
+    C = min(int(lay["rank_offsets"][-1]), cr)
+    assert np.array_equal(g["rq"][:C], rq[:C]), f"{what}: packed codes"
+    assert np.array_equal(g["rs"][:C], rs[:C]), f"{what}: packed scales"
+    assert np.array_equal(g["rsrc"][:C], src[:C]), f"{what}: rank_src_token"
+    assert np.all(g["rq"][C:] == CANARY) and np.all(g["rs"][C:] == CANARY), f"{what}: rank rows past C"
+    P = min(int(lay["expert_offsets"][-1]), ce)
+    written = esrc[:P] >= 0
+    assert np.array_equal(g["eq"][:P][written], eq[:P][written]), f"{what}: expert codes"
+    assert np.array_equal(g["es"][:P][written], es[:P][written]), f"{what}: expert scales"
+    assert np.array_equal(g["esrc"][:P][written], esrc[:P][written]), f"{what}: expert_src_pair"
+    assert np.all(g["esrc"][:P][esrc[:P] == -1] == -1), f"{what}: padding marks"
+    assert np.all(g["eq"][:P][~written] == CANARY) and np.all(g["eq"][P:] == CANARY)
+    assert np.all(g["es"][:P][~written] == CANARY) and np.all(g["esrc"][P:] == CANARY_IDX)
+    return lay
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
+def test_mxfp8_workload_parity(name):
+    w = synth.WORKLOADS[name]
+    say(f"[mxfp8] {w.describe()}")
+    hid = synth.hidden(w)
+    ids, _ = synth.routing(w)
+    lay = check(hid, ids, w.E, w.R, name)
+    assert lay["err"] == 0
+
+
+def test_mxfp8_every_bit_pattern():
+    """Hidden rows of random 16-bit patterns: NaNs, infinities, subnormals,
+    zeros of both signs and the whole exponent range, in every block."""
+    T, H, E, R, k = 300, 1024, 32, 4, 3
+    rng = np.random.default_rng(51)
+    hid = rng.integers(0, 65536, (T, H), dtype=np.uint16)
+    hid[::7] &= 0x80FF  # some rows of tiny and subnormal values only
+    hid[1::11, :64] = 0x7F80  # some blocks with an infinity
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
+    check(hid, ids, E, R, "bit patterns")
+
+
+EDGE = [
+    # (T, H, E, R, k, align, block, seed)
+    (0, 512, 16, 4, 2, 1, 0, 61),
+    (1, 512, 2, 1, 1, 1, 0, 62),
+    (257, 8704, 16, 4, 2, 1, 0, 63),      # 17 groups of 64 vec4: 17 passes of one group
+    (1000, 2048, 64, 8, 4, 128, 0, 64),   # padded runs
+    (500, 512, 64, 8, 6, 1, 32, 65),      # fixed blocks that overflow
+    (2000, 1536, 1024, 64, 16, 1, 0, 66),  # largest E, R, k
+    (700, 512, 96, 1, 5, 1, 0, 67),       # one rank
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_R{c[3]}_k{c[4]}_a{c[5]}_b{c[6]}" for c in EDGE])
+def test_mxfp8_edge_shapes(case):
+    T, H, E, R, k, align, block, seed = case
+    say(f"[mxfp8 edge] {case}")
+    rng = np.random.default_rng(seed)
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
+    hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
+    check(hid, ids, E, R, f"edge {case}", align=align, block=block)
+
+
+def test_mxfp8_undersized_buffers():
+    w = synth.WORKLOADS["tiny"]
+    hid = synth.hidden(w)
+    ids, _ = synth.routing(w)
+    lay = oracle.layout(ids, w.E, w.R)
+    C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
+    lay2 = check(hid, ids, w.E, w.R, "undersized", cap_rank=C - 37, cap_expert=P - 51, spare=64)
+    assert lay2["err"] == 0
+
+
+def test_mxfp8_rejects_rows_not_a_multiple_of_512():
+    dev = torch.device("cuda:0")
+    T, H, E, R, k = 4, 520, 8, 2, 2
+    hid = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
+    slots = torch.zeros((T, R), dtype=torch.int32, device=dev)
+    rq = torch.zeros((8, H), dtype=torch.uint8, device=dev)
+    rs = torch.zeros((8, 32), dtype=torch.uint8, device=dev)
+    src = torch.zeros(8, dtype=torch.int32, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.pack_mxfp8(hid, slots, E, k, rq, rs, src)
