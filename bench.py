@@ -284,7 +284,7 @@ class Rig:
         moe, s, b = self.moe, self.shape, self.buf
         if name == "layout":
             moe.layout(self.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
-                       out=b.layout_dict())
+                       out=b.layout_dict(), workspace=b.workspace)
         elif name == "pack" and self.mxfp8:
             moe.pack_mxfp8(self.hid_d, b.token_rank_slot, s.E, s.k, self.rank_q, self.rank_s,
                            b.rank_src_token, err=b.err)

@@ -25,12 +25,13 @@ ERRBIT_BAD_ID = 1
 ERRBIT_RANK_CAP = 2
 ERRBIT_EXPERT_CAP = 4
 
-EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout", "moe_dispatch_pack",
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
+           "moe_layout_workspace_bytes", "moe_dispatch_pack",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8")
 
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class MoeShape(ctypes.Structure):
@@ -67,7 +68,10 @@ def lib():
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_dispatch_layout.restype = ctypes.c_int
-    L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                      vp]
+    L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_layout_workspace_bytes.argtypes = [shp]
     L.moe_dispatch_pack.restype = ctypes.c_int
     L.moe_dispatch_pack.argtypes = [shp, vp, vp, vp, vp, i64, vp, vp]
     L.moe_permute_by_expert.restype = ctypes.c_int
@@ -149,9 +153,17 @@ class Shape:
         return self.T * self.k + self.E * (self.align - 1)
 
 
+def layout_workspace_bytes(shape: "Shape") -> int:
+    """moe_layout_workspace_bytes: scratch the two-launch layout needs (0: none)."""
+    return int(lib().moe_layout_workspace_bytes(ctypes.byref(shape.c())))
+
+
 def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1,
-           block: int = 0, err=None, out: dict | None = None) -> dict:
-    """moe_dispatch_layout: counts, offsets, token_rank_slot [T,R], pair_row [T,k]."""
+           block: int = 0, err=None, out: dict | None = None,
+           workspace: torch.Tensor | None = None) -> dict:
+    """moe_dispatch_layout: counts, offsets, token_rank_slot [T,R], pair_row [T,k].
+    `workspace` (a device tensor of at least layout_workspace_bytes bytes)
+    selects the two-launch layout; without it every workgroup counts all ids."""
     T, k = topk_ids.shape
     dev = topk_ids.device
     shape = Shape(T, H, E, R, k, align, block)
@@ -164,10 +176,12 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1
             token_rank_slot=torch.empty((T, R), dtype=torch.int32, device=dev),
             pair_row=torch.empty((T, k), dtype=torch.int32, device=dev),
         )
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().moe_dispatch_layout(
         ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(out["rank_counts"]),
         _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
-        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(err), _stream(dev))
+        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(workspace), ws_bytes,
+        _ptr(err), _stream(dev))
     _check(st, "moe_dispatch_layout")
     return out
 
@@ -319,6 +333,8 @@ class Buffers:
         self.out = torch.empty((T, H), dtype=row_dtype, device=d)
         self.out_f32 = torch.empty((T, H), dtype=torch.float32, device=d) if want_f32 else None
         self.err = torch.zeros(1, dtype=i32, device=d)
+        ws = layout_workspace_bytes(shape)
+        self.workspace = torch.empty(max(ws, 4) // 4, dtype=i32, device=d) if ws else None
 
     def layout_dict(self) -> dict:
         return dict(rank_counts=self.rank_counts, rank_offsets=self.rank_offsets,
@@ -330,7 +346,7 @@ def dispatch(buf: Buffers, hidden, topk_ids) -> None:
     """Layout, pack and permute into `buf` (three library calls, no host sync)."""
     s = buf.shape
     layout(topk_ids, s.E, s.R, s.H, align=s.align, block=s.block, err=buf.err,
-           out=buf.layout_dict())
+           out=buf.layout_dict(), workspace=buf.workspace)
     pack(hidden, buf.token_rank_slot, s.E, s.k, buf.rank_buf, buf.rank_src_token, err=buf.err)
     permute(buf.rank_buf, buf.rank_src_token, buf.rank_offsets, topk_ids, buf.pair_row, s.E,
             buf.expert_buf, buf.expert_src_pair, expert_counts=buf.expert_counts,

@@ -100,6 +100,7 @@ struct LayoutGeom {
   int batch_tokens;     // tokens whose ids are staged in LDS at once (multiple of 1024)
   int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
   int ntiles;
+  int tiles_pad;        // ntiles rounded up to a multiple of 4 (tile-count column stride)
   float inv_m;          // 1/m rounded to float
 };
 
@@ -213,15 +214,71 @@ __device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int6
   }
 }
 
+// Tile counts for the two-launch layout: one workgroup of 256 threads per
+// tile of g.tile_tokens tokens writes hist[c * g.tiles_pad + tile], the tile's
+// pairs per expert (c < E) and copies per rank (c = E + r). Column-major, so
+// that the ranking kernel reads a column's counts as whole 16-byte groups
+// (tiles_pad = ntiles rounded up to 4; the padding entries are never used).
+// Every entry a later read uses is written, so the workspace needs no
+// clearing between calls.
+constexpr int kCountThreads = 256;
+constexpr int64_t kTwoLaunchMinIds = 24576;  // ids above which the two-launch layout is used
+
+template <int K, bool kWide>
+__global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
+                                                              const int32_t* __restrict__ ids,
+                                                              int32_t* __restrict__ hist) {
+  using Mask = typename RankMask<kWide>::type;
+  constexpr int KR = K > 0 ? K : kMaxK;
+  const int k = K > 0 ? K : g.k;
+  __shared__ int32_t s_h[kMaxExperts + kMaxRanks + 1];  // + a slot for invalid ids
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  for (int c = tid; c <= g.ncols; c += kCountThreads) s_h[c] = 0;
+  __syncthreads();
+  const int tile_lo = blockIdx.x * g.tile_tokens;
+  const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
+  int rc = 0;  // lane r: this wave's copies on rank r
+  for (int t0 = tile_lo; t0 < tile_hi; t0 += kCountThreads) {
+    const int t = t0 + tid;
+    const bool in = t < tile_hi;
+    int ev[KR];
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+      if (j < k) ev[j] = in ? ids[(int64_t)t * k + j] : -1;
+    Mask mask = 0;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      if (j < k) {
+        const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
+        atomicAdd(&s_h[valid ? ev[j] : g.ncols], 1);
+        mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+      }
+    }
+    for (int r = 0; r < g.R; ++r) {
+      const int c = __popcll(__ballot((mask >> r) & 1));
+      if (lane == r) rc += c;
+    }
+  }
+  if (lane < g.R && rc) atomicAdd(&s_h[g.E + lane], rc);
+  __syncthreads();
+  for (int c = tid; c < g.ncols; c += kCountThreads)
+    hist[(int64_t)c * g.tiles_pad + blockIdx.x] = s_h[c];
+}
+
 // One workgroup of 1024 threads per tile of g.tile_tokens tokens; K = k known
-// at compile time (0: any k up to kMaxK, read at run time). Writes:
+// at compile time (0: any k up to kMaxK, read at run time). With kFromHist the
+// counts before and from the tile come from the tile counts in `hist`
+// (written by layout_count); otherwise every workgroup counts all tokens
+// itself. Writes:
 //   pair_row[t][j]        = expert_offsets[e] + #{pairs of e before (t, j)}
 //                           (-1 when that is past the end of a fixed block)
 //   token_rank_slot[t][r] = rank_offsets[r] + #{tokens before t with a copy on r}
 // Workgroup 0 also writes the counts and offsets.
-template <int K, bool kWide>
+template <int K, bool kWide, bool kFromHist>
 __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
-    LayoutGeom g, const int32_t* __restrict__ ids, int32_t* __restrict__ rank_counts,
+    LayoutGeom g, const int32_t* __restrict__ ids, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
     int32_t* __restrict__ pair_row, int32_t* err_word) {
@@ -230,7 +287,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int k = K > 0 ? K : g.k;
   extern __shared__ int32_t smem[];
   int32_t* s_ids = smem;                          // [batch_tokens * k] staged ids
-  int32_t* s_pack = s_ids + g.batch_tokens * k + 4;  // [kOwnTokens * k] own sub-tile ids
+  // [kOwnTokens * k] own sub-tile ids (no staged batch with kFromHist)
+  int32_t* s_pack = s_ids + (kFromHist ? 0 : g.batch_tokens * k) + 4;
   int32_t* s_cnt = s_pack + kOwnTokens * k;       // [kOwnWaves][ncols] per-wave counts
   int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols + 1] before the tile -> running base
   int32_t* s_tot = s_pre + g.ncols + 1;           // [ncols + 1] other tokens -> totals -> offsets
@@ -243,70 +301,103 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int64_t n_ids = (int64_t)g.T * k;
   const int tile_lo = blockIdx.x * g.tile_tokens;
   const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
-  const bool one_sub = g.tile_tokens == kOwnTokens;  // own ids captured from the batch
+  // own ids captured from the staged batch (only when the batch loop runs)
+  const bool one_sub = !kFromHist && g.tile_tokens == kOwnTokens;
 
   for (int c = tid; c < g.ncols; c += kLayoutThreads) {
     s_pre[c] = 0;
     s_tot[c] = 0;
   }
 
-  // 1. Histogram of every token, a batch of tokens at a time: all of a
-  //    batch's ids are requested at once (16 bytes per lane, coalesced) and
-  //    staged in LDS, the next batch's loads in flight while this one is
-  //    counted. Experts: one LDS atomic per pair. Ranks: one ballot per rank
-  //    per 64 tokens (a wave's 64 tokens sit on one side of the tile start).
-  const int batch_ids = g.batch_tokens * k;
-  int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
-  vec4 nxt[kBatchVecs];
-  load_batch(ids, n_ids, 0, (int)((std::min<int64_t>(batch_ids, n_ids) + 3) / 4), nxt);
-  for (int b0 = 0; b0 < g.T; b0 += g.batch_tokens) {
-    const int nb = min(g.batch_tokens, g.T - b0);
-    const int nvec = (nb * k + 3) / 4;
-    __syncthreads();  // s_ids free; s_pre/s_tot zeroed
+  if (kFromHist) {
+    // 1'. Counts before the tile and from it on, per column, from the tile
+    //     counts: a column's tiles_pad entries are contiguous, all of its
+    //     16-byte groups are requested at once.
+    constexpr int kMaxGroups = kMaxTiles / 4;
+    const int groups = g.tiles_pad / 4;
+    const int me = int(blockIdx.x);
+    for (int c = tid; c < g.ncols; c += kLayoutThreads) {
+      const vec4* col = reinterpret_cast<const vec4*>(hist + (int64_t)c * g.tiles_pad);
+      vec4 v[kMaxGroups];
 #pragma unroll
-    for (int q = 0; q < kBatchVecs; ++q) {
-      const int v = q * kLayoutThreads + tid;
-      if (v < nvec) *reinterpret_cast<vec4*>(s_ids + 4 * v) = nxt[q];
-    }
-    const int b1 = b0 + g.batch_tokens;
-    if (b1 < g.T) {
-      const int nn = min(g.batch_tokens, g.T - b1);
-      load_batch(ids, n_ids, (int64_t)b1 * k, (nn * k + 3) / 4, nxt);
-    }
-    __syncthreads();
-    if (one_sub && b0 <= tile_lo && tile_lo < b0 + nb) {
-      const int base = (tile_lo - b0) * k;
-      const int n_own = min(kOwnTokens, tile_hi - tile_lo) * k;
-      for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads)
-        s_pack[f] = f < n_own ? s_ids[base + f] : -1;
-    }
-    for (int tl = tid; tl < ((nb + kWave - 1) & ~(kWave - 1)); tl += kLayoutThreads) {
-      const bool early = b0 + (tl & ~(kWave - 1)) < tile_lo;  // the same for the whole wave
-      int32_t* cnt = early ? s_pre : s_tot;
-      int ev[KR];
+      for (int q = 0; q < kMaxGroups; ++q)
+        if (q < groups) v[q] = col[q];
+      int before = 0, total = 0;
 #pragma unroll
-      for (int j = 0; j < KR; ++j)
-        if (j < k) ev[j] = tl < nb ? s_ids[tl * k + j] : -1;
-      Mask mask = 0;
+      for (int q = 0; q < kMaxGroups; ++q) {
+        if (q < groups) {
 #pragma unroll
-      for (int j = 0; j < KR; ++j) {
-        if (j < k) {
-          const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
-          atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
-          mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+          for (int x = 0; x < 4; ++x) {
+            const int j = 4 * q + x;
+            const int cnt = j < g.ntiles ? int(v[q][x]) : 0;
+            before += j < me ? cnt : 0;
+            total += cnt;
+          }
         }
       }
-      for (int r = 0; r < g.R; ++r) {
-        const int c = __popcll(__ballot((mask >> r) & 1));
-        if (lane == r) (early ? rc_pre : rc_tot) += c;
+      s_pre[c] = before;
+      s_tot[c] = total - before;
+    }
+    __syncthreads();
+  } else {
+    // 1. Histogram of every token, a batch of tokens at a time: all of a
+    //    batch's ids are requested at once (16 bytes per lane, coalesced) and
+    //    staged in LDS, the next batch's loads in flight while this one is
+    //    counted. Experts: one LDS atomic per pair. Ranks: one ballot per rank
+    //    per 64 tokens (a wave's 64 tokens sit on one side of the tile start).
+    const int batch_ids = g.batch_tokens * k;
+    int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
+    vec4 nxt[kBatchVecs];
+    load_batch(ids, n_ids, 0, (int)((std::min<int64_t>(batch_ids, n_ids) + 3) / 4), nxt);
+    for (int b0 = 0; b0 < g.T; b0 += g.batch_tokens) {
+      const int nb = min(g.batch_tokens, g.T - b0);
+      const int nvec = (nb * k + 3) / 4;
+      __syncthreads();  // s_ids free; s_pre/s_tot zeroed
+#pragma unroll
+      for (int q = 0; q < kBatchVecs; ++q) {
+        const int v = q * kLayoutThreads + tid;
+        if (v < nvec) *reinterpret_cast<vec4*>(s_ids + 4 * v) = nxt[q];
+      }
+      const int b1 = b0 + g.batch_tokens;
+      if (b1 < g.T) {
+        const int nn = min(g.batch_tokens, g.T - b1);
+        load_batch(ids, n_ids, (int64_t)b1 * k, (nn * k + 3) / 4, nxt);
+      }
+      __syncthreads();
+      if (one_sub && b0 <= tile_lo && tile_lo < b0 + nb) {
+        const int base = (tile_lo - b0) * k;
+        const int n_own = min(kOwnTokens, tile_hi - tile_lo) * k;
+        for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads)
+          s_pack[f] = f < n_own ? s_ids[base + f] : -1;
+      }
+      for (int tl = tid; tl < ((nb + kWave - 1) & ~(kWave - 1)); tl += kLayoutThreads) {
+        const bool early = b0 + (tl & ~(kWave - 1)) < tile_lo;  // the same for the whole wave
+        int32_t* cnt = early ? s_pre : s_tot;
+        int ev[KR];
+#pragma unroll
+        for (int j = 0; j < KR; ++j)
+          if (j < k) ev[j] = tl < nb ? s_ids[tl * k + j] : -1;
+        Mask mask = 0;
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+          if (j < k) {
+            const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
+            atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
+            mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+          }
+        }
+        for (int r = 0; r < g.R; ++r) {
+          const int c = __popcll(__ballot((mask >> r) & 1));
+          if (lane == r) (early ? rc_pre : rc_tot) += c;
+        }
       }
     }
+    if (lane < g.R) {  // lane r holds this wave's copies on rank r
+      if (rc_pre) atomicAdd(&s_pre[g.E + lane], rc_pre);
+      if (rc_tot) atomicAdd(&s_tot[g.E + lane], rc_tot);
+    }
+    __syncthreads();
   }
-  if (lane < g.R) {  // lane r holds this wave's copies on rank r
-    if (rc_pre) atomicAdd(&s_pre[g.E + lane], rc_pre);
-    if (rc_tot) atomicAdd(&s_tot[g.E + lane], rc_tot);
-  }
-  __syncthreads();
 
   // 2.-3. Counts, exclusive scans (experts in id order, ranks in rank order)
   //    and the absolute first row of this tile in every column (in s_pre).
@@ -472,47 +563,65 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   const int64_t per_tile = std::max<int64_t>(1, (subs + kMaxTiles - 1) / kMaxTiles);
   g.tile_tokens = int(per_tile * kOwnTokens);
   g.ntiles = int(std::max<int64_t>(1, (int64_t(sh.T) + g.tile_tokens - 1) / g.tile_tokens));
+  g.tiles_pad = (g.ntiles + 3) / 4 * 4;
   return g;
 }
 
+struct LayoutArgs {
+  const int32_t* ids;
+  int32_t *rc, *ro, *ec, *eo, *trs, *pr, *err;
+  int32_t* hist;  // tile counts [ntiles][ncols], or NULL: one launch, every workgroup counts all
+};
+
 template <int K, bool kWide>
-void launch_layout_kw(const LayoutGeom& g, size_t lds, hipStream_t st, const int32_t* ids,
-                      int32_t* rc, int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs,
-                      int32_t* pr, int32_t* err) {
-  // Allow this instantiation the LDS it may need (above the 64 KiB default);
-  // set once per process, the only thing the library ever caches.
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K, kWide>),
+void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
+  // Allow these instantiations the LDS they may need (above the 64 KiB
+  // default); set once per process, the only thing the library ever caches.
+  static const hipError_t attr0 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&layout_tiles<K, kWide, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
-  (void)attr;
-  hipLaunchKernelGGL((layout_tiles<K, kWide>), dim3(g.ntiles), dim3(kLayoutThreads), lds, st, g,
-                     ids, rc, ro, ec, eo, trs, pr, err);
+  static const hipError_t attr1 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&layout_tiles<K, kWide, true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
+  (void)attr0;
+  (void)attr1;
+  if (a.hist) {
+    hipLaunchKernelGGL((layout_count<K, kWide>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
+                       a.ids, a.hist);
+    hipLaunchKernelGGL((layout_tiles<K, kWide, true>), dim3(g.ntiles), dim3(kLayoutThreads),
+                       layout_lds_bytes(0, g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
+                       a.eo, a.trs, a.pr, a.err);
+  } else {
+    hipLaunchKernelGGL((layout_tiles<K, kWide, false>), dim3(g.ntiles), dim3(kLayoutThreads),
+                       layout_lds_bytes(g.batch_tokens, g.k, g.ncols), st, g, a.ids, a.hist,
+                       a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.err);
+  }
 }
 
 template <int K>
-void launch_layout_k(const LayoutGeom& g, size_t lds, hipStream_t st, const int32_t* ids,
-                     int32_t* rc, int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs,
-                     int32_t* pr, int32_t* err) {
+void launch_layout_k(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
   if (g.R > 32)
-    launch_layout_kw<K, true>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
+    launch_layout_kw<K, true>(g, st, a);
   else
-    launch_layout_kw<K, false>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
+    launch_layout_kw<K, false>(g, st, a);
 }
 
-void launch_layout(const LayoutGeom& g, hipStream_t st, const int32_t* ids, int32_t* rc,
-                   int32_t* ro, int32_t* ec, int32_t* eo, int32_t* trs, int32_t* pr,
-                   int32_t* err) {
-  const size_t lds = layout_lds_bytes(g.batch_tokens, g.k, g.ncols);
+void launch_layout(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
   switch (g.k) {
-    case 1: launch_layout_k<1>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 2: launch_layout_k<2>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 3: launch_layout_k<3>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 4: launch_layout_k<4>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 5: launch_layout_k<5>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 6: launch_layout_k<6>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    case 8: launch_layout_k<8>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err); break;
-    default: launch_layout_k<0>(g, lds, st, ids, rc, ro, ec, eo, trs, pr, err);
+    case 1: launch_layout_k<1>(g, st, a); break;
+    case 2: launch_layout_k<2>(g, st, a); break;
+    case 3: launch_layout_k<3>(g, st, a); break;
+    case 4: launch_layout_k<4>(g, st, a); break;
+    case 5: launch_layout_k<5>(g, st, a); break;
+    case 6: launch_layout_k<6>(g, st, a); break;
+    case 8: launch_layout_k<8>(g, st, a); break;
+    default: launch_layout_k<0>(g, st, a);
   }
+}
+
+// Tile counts live in the caller's workspace: int32 [E + R][tiles_pad].
+size_t layout_workspace_bytes(const LayoutGeom& g) {
+  return g.ntiles > 1 ? sizeof(int32_t) * size_t(g.tiles_pad) * size_t(g.ncols) : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1102,17 +1211,30 @@ const char* moe_status_string(int status) {
   }
 }
 
+size_t moe_layout_workspace_bytes(const moe_shape_t* shape) {
+  if (!shape_ok(shape)) return 0;
+  return layout_workspace_bytes(layout_geometry(*shape));
+}
+
 int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* expert_counts, int32_t* expert_offsets,
-                        int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
-                        void* stream) {
+                        int32_t* token_rank_slot, int32_t* pair_row, void* workspace,
+                        size_t workspace_bytes, int32_t* err_word, void* stream) {
   if (!shape_ok(shape)) return MOE_ERR_ARG;
   if (!rank_counts || !rank_offsets || !expert_counts || !expert_offsets) return MOE_ERR_ARG;
   if (shape->T > 0 && (!topk_ids || !token_rank_slot || !pair_row)) return MOE_ERR_ARG;
   if (shape->T > 0 && !aligned16(topk_ids)) return MOE_ERR_ARG;
   const LayoutGeom g = layout_geometry(*shape);
-  launch_layout(g, static_cast<hipStream_t>(stream), topk_ids, rank_counts, rank_offsets,
-                expert_counts, expert_offsets, token_rank_slot, pair_row, err_word);
+  const size_t need = layout_workspace_bytes(g);
+  if (workspace && (workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_ARG;
+  // Two launches pay about 5 us more in fixed cost; one launch counts all
+  // T*k ids in every workgroup. Measured on MI355X, they break even near
+  // 24,576 ids (T = 4096, k = 6), so the tile counts are used above that.
+  const bool two = need > 0 && workspace && int64_t(shape->T) * shape->k > kTwoLaunchMinIds;
+  LayoutArgs a{topk_ids, rank_counts, rank_offsets, expert_counts, expert_offsets,
+               token_rank_slot, pair_row, err_word,
+               two ? static_cast<int32_t*>(workspace) : nullptr};
+  launch_layout(g, static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 

@@ -12,9 +12,10 @@
  *
  * Common conventions
  *  - Every pointer argument except `shape` is a DEVICE pointer (hipMalloc'd or
- *    a torch CUDA tensor). The caller owns every buffer; the library allocates
- *    nothing, keeps no state between calls and is re-entrant for calls that
- *    do not share output buffers.
+ *    a torch CUDA tensor). The caller owns every buffer, the layout's small
+ *    workspace included; the library allocates nothing, keeps no state between
+ *    calls and is re-entrant for calls that do not share output buffers or
+ *    workspaces.
  *  - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
  *    NULL = the null stream), never synchronise with the host and launch a
  *    fixed number of kernels whose grids depend only on the shape and caps, so
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 2
+#define MOE_DISPATCH_ABI_VERSION 3
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -116,15 +117,30 @@ const char* moe_status_string(int status);
  *                                 rows of a segment ascend with t
  *   pair_row         [T*k]   out: row of pair (t, j) in the expert-grouped buffer, or -1;
  *                                 rows of an expert's run ascend with (t, j)
+ *   workspace        [workspace_bytes] scratch: device memory of at least
+ *                    moe_layout_workspace_bytes(shape) bytes, 16-byte aligned (owned by
+ *                    the caller; no clearing needed: every call overwrites what it
+ *                    reads), or NULL
  *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID; MOE_ERRBIT_EXPERT_CAP when a
  *             pair finds its fixed block full)
- * One kernel launch, no scratch memory beyond LDS. The result is a pure
- * function of topk_ids: no order depends on timing.
+ * The tokens are cut into at most 64 tiles of a multiple of 256 tokens. With a
+ * workspace, more than one tile and more than 24,576 (token, slot) pairs, two
+ * kernel launches: per-tile counts into the workspace, then one workgroup per
+ * tile scans them and ranks its tile. Otherwise one launch in which every
+ * workgroup counts all tokens itself (cheaper for small T, slower for large). Either way the result is a
+ * pure function of topk_ids: no order depends on timing. Calls that run at
+ * the same time must not share a workspace. A workspace smaller than needed
+ * is an argument error.
  */
 int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* expert_counts, int32_t* expert_offsets,
-                        int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
-                        void* stream);
+                        int32_t* token_rank_slot, int32_t* pair_row, void* workspace,
+                        size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* Bytes of layout workspace for this shape: 4 * (tiles rounded up to a
+ * multiple of 4) * (E + R) when there is more than one tile (at most
+ * 64 * 1088 * 4 = 278,528), else 0. 0 for an invalid shape. */
+size_t moe_layout_workspace_bytes(const moe_shape_t* shape);
 
 /*
  * Dispatch, step 2: pack ([A2A] sec 1.3 third answer and sec 3.2: a token is

@@ -26,7 +26,7 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
             y_slots: np.ndarray | None, cap_rank: int | None = None,
             cap_expert: int | None = None, spare_rows: int = 4, want_f32: bool = True,
             device="cuda:0", stream: torch.cuda.Stream | None = None, align: int = 1,
-            block: int = 0) -> dict:
+            block: int = 0, use_workspace: bool = True) -> dict:
     """One full pass through the library. Row buffers get `spare_rows` canary
     rows past their caps; the library is told only the caps."""
     T, H = hid.shape
@@ -59,7 +59,11 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
         rank_buf, rank_src = rank_all[:cap_rank], rsrc_all[:cap_rank]
         expert_buf, expert_src = exp_all[:cap_expert], esrc_all[:cap_expert]
 
-        moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay)
+        ws = moe.layout_workspace_bytes(shape) if use_workspace else 0
+        # workspace filled with garbage: the layout must overwrite what it reads
+        workspace = torch.full((max(ws, 4) // 4,), 0x5A5A5A5A, dtype=i32, device=dev) if ws else None
+        moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay,
+                   workspace=workspace)
         moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
         moe.permute(rank_buf, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"], E,
                     expert_buf, expert_src, expert_counts=lay["expert_counts"],
@@ -167,7 +171,9 @@ def run_gpu_two_stage(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int,
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
     wts_d = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).to(dev)
     err = torch.zeros(1, dtype=i32, device=dev)
-    lay = moe.layout(ids_d, E, R, H, err=err)
+    ws = moe.layout_workspace_bytes(shape)
+    workspace = torch.empty((max(ws, 4) // 4,), dtype=i32, device=dev) if ws else None
+    lay = moe.layout(ids_d, E, R, H, err=err, workspace=workspace)
     rank_buf = torch.empty((cap_rank, H), dtype=torch.int16, device=dev)
     rank_src = torch.full((cap_rank,), CANARY_IDX, dtype=i32, device=dev)
     moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)

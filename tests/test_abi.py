@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 2
+    assert L.moe_abi_version() == moe.ABI_VERSION == 3
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first
@@ -47,7 +47,7 @@ BAD_SHAPES = [
 def test_calls_reject_bad_shapes(bad):
     L = moe.lib()
     sp = ctypes.byref(shape(**bad))
-    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+    assert L.moe_dispatch_layout(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
                                  None) == moe.MOE_ERR_ARG
     assert L.moe_dispatch_pack(sp, FAKE, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
     assert L.moe_combine(sp, FAKE, FAKE, FAKE, 128, FAKE, None, None, None) == moe.MOE_ERR_ARG
@@ -62,12 +62,17 @@ def test_calls_reject_bad_arguments_without_launching():
     sp = ctypes.byref(s)
     bad = ctypes.byref(shape(E=10))
     # layout: bad shape, NULL inputs and outputs
-    assert L.moe_dispatch_layout(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+    assert L.moe_dispatch_layout(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
                                  None) == moe.MOE_ERR_ARG
-    assert L.moe_dispatch_layout(sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+    assert L.moe_dispatch_layout(sp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
                                  None) == moe.MOE_ERR_ARG
-    assert L.moe_dispatch_layout(sp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+    assert L.moe_dispatch_layout(sp, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None,
                                  None) == moe.MOE_ERR_ARG
+    # a workspace smaller than moe_layout_workspace_bytes
+    big = ctypes.byref(shape(T=4096, H=512, E=384, R=8, k=6))
+    need = L.moe_layout_workspace_bytes(big)
+    assert L.moe_dispatch_layout(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+                                 None, None) == moe.MOE_ERR_ARG
     # pack: NULL hidden, misaligned rows, negative cap
     assert L.moe_dispatch_pack(sp, None, FAKE, FAKE, FAKE, 128, None, None) == moe.MOE_ERR_ARG
     assert L.moe_dispatch_pack(sp, ctypes.c_void_p(0x10008), FAKE, FAKE, FAKE, 128, None,
@@ -134,6 +139,18 @@ def test_empty_batches_are_no_ops():
     assert L.moe_combine_rank_partial(s0, None, None, FAKE, None, None, None, 0, 0, None, None,
                                       None, None) == moe.MOE_OK
     assert L.moe_combine_ranks(s0, None, None, 0, None, None, None, None) == moe.MOE_OK
+
+
+def test_layout_workspace_sizes():
+    L = moe.lib()
+    # one tile (T <= 256): no workspace; else 4 * (tiles rounded up to 4) * (E + R), tiles <= 64
+    assert L.moe_layout_workspace_bytes(ctypes.byref(shape(T=256))) == 0
+    assert L.moe_layout_workspace_bytes(ctypes.byref(shape(T=257))) == 4 * 4 * (16 + 4)
+    assert L.moe_layout_workspace_bytes(
+        ctypes.byref(shape(T=4096, E=384, R=8, k=6))) == 4 * 16 * (384 + 8)
+    assert L.moe_layout_workspace_bytes(
+        ctypes.byref(shape(T=16384, E=1024, R=64, k=4))) == 4 * 64 * (1024 + 64)
+    assert L.moe_layout_workspace_bytes(ctypes.byref(shape(E=10))) == 0  # invalid shape
 
 
 def test_status_strings():

@@ -153,3 +153,29 @@ def test_deterministic_and_stream_independent():
     b = run_gpu(hid, ids, wts, w.E, w.R, y, stream=torch.cuda.Stream())
     for key in ("token_rank_slot", "pair_row", "rank_all", "expert_all", "out", "out_f32"):
         assert np.array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8)), key
+
+
+NO_WORKSPACE = [
+    # the one-launch layout (no workspace): every workgroup counts all ids
+    ("prefill", None), ("adv", None), (None, (70000, 16, 64, 8, 5, 0.05, 0.0, 12)),
+    (None, (2000, 64, 1024, 64, 16, 0.02, 0.02, 9)), (None, (257, 512, 16, 4, 2, 0.1, 0.0, 4)),
+]
+
+
+@pytest.mark.parametrize("name,case", NO_WORKSPACE,
+                         ids=[n or f"T{c[0]}_E{c[2]}_R{c[3]}_k{c[4]}" for n, c in NO_WORKSPACE])
+def test_layout_without_workspace(name, case):
+    if name:
+        w, hid, ids, wts, y = workload_inputs(name)
+        E, R = w.E, w.R
+    else:
+        T, H, E, R, k, pn, pd, seed = case
+        rng = np.random.default_rng(seed)
+        ids = pins.rand_ids(rng, T, E, k, p_neg=pn, p_dup=pd)
+        wts = rng.random((T, k)).astype(np.float32)
+        hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
+        y = synth.expert_out_slots(seed, E, H, ids)
+    say(f"[no workspace] {name or case}")
+    gpu = run_gpu(hid, ids, wts, E, R, y, use_workspace=False)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    compare(gpu, ref, f"no workspace {name or case}")
