@@ -344,6 +344,28 @@ class Rig:
                 out[c].append(a.elapsed_time(b))
         return out
 
+    def graph_step_us(self, n: int = 50) -> float:
+        """One step recorded in a HIP graph, replayed n times back to back: the
+        step's GPU time without host launch gaps (what a decode loop that
+        replays a recorded step sees)."""
+        import torch
+
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in CALLS:  # the one-stage path: layout, pack, permute, combine
+                self.call(c)
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
     def check_err(self) -> None:
         e = int(self.buf.err.item())
         if e != 0:
@@ -435,6 +457,10 @@ def sweep(names, dev, with_oracle: bool) -> None:
             "combine_pairs": round(rig.P / (warm["combine"]["warm"]["us"] * 1e-6))}
         res["bytes"] = tot
         res["two_stage_bytes"] = tot2
+        us_g = rig.graph_step_us()
+        res["graph"] = {"us_per_step": round(us_g, 2),
+                        "note": "layout, pack, permute, combine replayed from one HIP graph"}
+        log(f"{name}: graph replay {us_g:.1f} us per step")
         if with_oracle and align == 1 and block == 0 and not mx:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
@@ -464,6 +490,12 @@ def sweep(names, dev, with_oracle: bool) -> None:
                 r["two_stage_" + mode]
             print(f"| {name} | {mode} | {a['us']} | {a['GB/s']} | {b['us']} | {b['GB/s']} "
                   f"| {p['us']} | {p['GB/s']} | {p['pct_peak']} |")
+    print("\nOne step (layout, pack, permute, combine) replayed from one HIP graph, back to "
+          "back (no host launch gaps), next to the sum of the per-call warm times:\n")
+    print("| workload | us per step (graph) | sum of per-call warm us |")
+    print("|---|---|---|")
+    for name, r in rows:
+        print(f"| {name} | {r['graph']['us_per_step']} | {r['warm']['us']} |")
     print(f"\n1 GiB device copy: {copy['us']} us, {copy['GB/s']} GB/s (read + write)")
 
 
