@@ -113,10 +113,6 @@ __device__ __forceinline__ int rank_of(int e, float inv_m) {
   return int(__builtin_fmaf(float(e), inv_m, 0.5f * inv_m));
 }
 
-// Rank sets of a token as bit masks: 32 bits when R <= 32, else 64.
-template <bool kWide> struct RankMask { using type = uint32_t; };
-template <> struct RankMask<true> { using type = uint64_t; };
-
 // Inclusive prefix sum across a wave with DPP row shifts and broadcasts.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
@@ -126,6 +122,31 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
   x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
+}
+
+// Rank sets of a token as bit masks. kRB is a compile-time bound on R (8, 32
+// or 64): 32-bit masks up to 32 ranks, 64-bit above; with kRB = 8 the loops
+// over ranks are unrolled.
+template <int kRB> struct RankMask { using type = uint32_t; };
+template <> struct RankMask<64> { using type = uint64_t; };
+
+// Copies per rank over the wave's 64 tokens (one rank set per lane), in lane r.
+template <int kRB, typename Mask>
+__device__ __forceinline__ int wave_rank_counts(Mask mask, int R) {
+  int mine = 0;
+  if (kRB == 8) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int c = __popcll(__ballot((mask >> r) & 1));
+      mine = lane_id() == r ? c : mine;
+    }
+  } else {
+    for (int r = 0; r < R; ++r) {
+      const int c = __popcll(__ballot((mask >> r) & 1));
+      mine = lane_id() == r ? c : mine;
+    }
+  }
+  return mine;
 }
 
 // Column totals, exclusive scans and the tile's first rows, in one pass: for
@@ -224,11 +245,11 @@ __device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int6
 constexpr int kCountThreads = 256;
 constexpr int64_t kTwoLaunchMinIds = 24576;  // ids above which the two-launch layout is used
 
-template <int K, bool kWide>
+template <int K, int kRB>
 __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
                                                               const int32_t* __restrict__ ids,
                                                               int32_t* __restrict__ hist) {
-  using Mask = typename RankMask<kWide>::type;
+  using Mask = typename RankMask<kRB>::type;
   constexpr int KR = K > 0 ? K : kMaxK;
   const int k = K > 0 ? K : g.k;
   __shared__ int32_t s_h[kMaxExperts + kMaxRanks + 1];  // + a slot for invalid ids
@@ -255,10 +276,7 @@ __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
         mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
       }
     }
-    for (int r = 0; r < g.R; ++r) {
-      const int c = __popcll(__ballot((mask >> r) & 1));
-      if (lane == r) rc += c;
-    }
+    rc += wave_rank_counts<kRB>(mask, g.R);
   }
   if (lane < g.R && rc) atomicAdd(&s_h[g.E + lane], rc);
   __syncthreads();
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
 //                           (-1 when that is past the end of a fixed block)
 //   token_rank_slot[t][r] = rank_offsets[r] + #{tokens before t with a copy on r}
 // Workgroup 0 also writes the counts and offsets.
-template <int K, bool kWide, bool kFromHist>
+template <int K, int kRB, bool kFromHist>
 __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     LayoutGeom g, const int32_t* __restrict__ ids, const int32_t* __restrict__ hist,
     int32_t* __restrict__ rank_counts,
@@ -283,7 +301,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
     int32_t* __restrict__ pair_row, int32_t* err_word) {
   constexpr int KR = K > 0 ? K : kMaxK;
-  using Mask = typename RankMask<kWide>::type;
+  using Mask = typename RankMask<kRB>::type;
   const int k = K > 0 ? K : g.k;
   extern __shared__ int32_t smem[];
   int32_t* s_ids = smem;                          // [batch_tokens * k] staged ids
@@ -308,6 +326,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     s_pre[c] = 0;
     s_tot[c] = 0;
   }
+  // The per-wave running counts of the first sub-tile start at zero (cleared
+  // here, under the id loads, rather than after the scan).
+  for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
 
   if (kFromHist) {
     // 1'. Counts before the tile and from it on, per column, from the tile
@@ -386,10 +407,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
             mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
           }
         }
-        for (int r = 0; r < g.R; ++r) {
-          const int c = __popcll(__ballot((mask >> r) & 1));
-          if (lane == r) (early ? rc_pre : rc_tot) += c;
-        }
+        const int c = wave_rank_counts<kRB>(mask, g.R);
+        (early ? rc_pre : rc_tot) += c;
       }
     }
     if (lane < g.R) {  // lane r holds this wave's copies on rank r
@@ -427,7 +446,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
         s_pack[f] = f < npairs ? ids[gf] : -1;
       }
     }
-    for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
+    if (t0 > tile_lo)  // the first sub-tile's counts were cleared at the start
+      for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
     __syncthreads();
 
     int ex[KR], rk[KR];  // per chunk: this lane's expert (or -1) and its rank in the wave
@@ -487,11 +507,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 #pragma unroll
       for (int j = 0; j < KR; ++j)
         if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
-      int copies = 0;  // lane r: the wave's tokens with a copy on rank r
-      for (int r = 0; r < g.R; ++r) {
-        const int c = __popcll(__ballot((mask >> r) & 1));
-        if (lane == r) copies = c;
-      }
+      const int copies = wave_rank_counts<kRB>(mask, g.R);  // lane r: tokens with a copy on r
       if (lane < g.R) cnt_w[g.E + lane] = copies;
     }
     __syncthreads();
@@ -524,11 +540,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
           }
         }
       }
-      for (int r = 0; r < g.R; ++r) {
+      auto write_slot = [&](int r) {
         const uint64_t on = __ballot((mask >> r) & 1);
         if (tid < nt)
           token_rank_slot[(int64_t)(t0 + tid) * g.R + r] =
               ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
+      };
+      if (kRB == 8) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (r < g.R) write_slot(r);
+      } else {
+        for (int r = 0; r < g.R; ++r) write_slot(r);
       }
     }
   }
@@ -573,26 +596,26 @@ struct LayoutArgs {
   int32_t* hist;  // tile counts [ntiles][ncols], or NULL: one launch, every workgroup counts all
 };
 
-template <int K, bool kWide>
+template <int K, int kRB>
 void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
   // Allow these instantiations the LDS they may need (above the 64 KiB
   // default); set once per process, the only thing the library ever caches.
   static const hipError_t attr0 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K, kWide, false>),
+      reinterpret_cast<const void*>(&layout_tiles<K, kRB, false>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
   static const hipError_t attr1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K, kWide, true>),
+      reinterpret_cast<const void*>(&layout_tiles<K, kRB, true>),
       hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
   (void)attr0;
   (void)attr1;
   if (a.hist) {
-    hipLaunchKernelGGL((layout_count<K, kWide>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
+    hipLaunchKernelGGL((layout_count<K, kRB>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
                        a.ids, a.hist);
-    hipLaunchKernelGGL((layout_tiles<K, kWide, true>), dim3(g.ntiles), dim3(kLayoutThreads),
+    hipLaunchKernelGGL((layout_tiles<K, kRB, true>), dim3(g.ntiles), dim3(kLayoutThreads),
                        layout_lds_bytes(0, g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
                        a.eo, a.trs, a.pr, a.err);
   } else {
-    hipLaunchKernelGGL((layout_tiles<K, kWide, false>), dim3(g.ntiles), dim3(kLayoutThreads),
+    hipLaunchKernelGGL((layout_tiles<K, kRB, false>), dim3(g.ntiles), dim3(kLayoutThreads),
                        layout_lds_bytes(g.batch_tokens, g.k, g.ncols), st, g, a.ids, a.hist,
                        a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.err);
   }
@@ -601,9 +624,11 @@ void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) 
 template <int K>
 void launch_layout_k(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
   if (g.R > 32)
-    launch_layout_kw<K, true>(g, st, a);
+    launch_layout_kw<K, 64>(g, st, a);
+  else if (g.R > 8)
+    launch_layout_kw<K, 32>(g, st, a);
   else
-    launch_layout_kw<K, false>(g, st, a);
+    launch_layout_kw<K, 8>(g, st, a);
 }
 
 void launch_layout(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
