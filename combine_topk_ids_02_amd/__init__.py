@@ -28,7 +28,8 @@ ERRBIT_EXPERT_CAP = 4
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_layout_workspace_bytes", "moe_dispatch_pack",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
-           "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8")
+           "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
+           "moe_testing_set_layout_form")
 
 
 ABI_VERSION = 3
@@ -88,6 +89,8 @@ def lib():
     L.moe_permute_by_expert_mxfp8.restype = ctypes.c_int
     L.moe_permute_by_expert_mxfp8.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp,
                                               vp, i64, vp, vp]
+    L.moe_testing_set_layout_form.restype = ctypes.c_int
+    L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
     if L.moe_abi_version() != ABI_VERSION:
         raise MoeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, this binding "
                        f"expects {ABI_VERSION}: rebuild with __graft_entry__.build()")

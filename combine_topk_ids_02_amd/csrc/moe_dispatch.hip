@@ -93,6 +93,11 @@ constexpr int kOwnWaves = kOwnTokens / kWave;
 constexpr int kBatchVecs = 8;                    // 16-byte id loads per thread per batch
 constexpr size_t kLayoutLdsLimit = 160 * 1024 - 1024;  // gfx950: 160 KiB of LDS per workgroup
 
+// Which form of the layout runs when a workspace is given: -1 by size (the
+// default), 0 every workgroup counts all ids, 1 two launches through tile
+// counts. Changed only by the testing hook.
+int g_layout_form = -1;
+
 struct LayoutGeom {
   int T, E, R, k, m;    // m = experts per rank
   int align, block;     // expert runs padded to multiples of align; or fixed blocks (block > 0)
@@ -1236,6 +1241,12 @@ const char* moe_status_string(int status) {
   }
 }
 
+int moe_testing_set_layout_form(int form) {
+  const int old = g_layout_form;
+  if (form >= -1 && form <= 1) g_layout_form = form;
+  return old;
+}
+
 size_t moe_layout_workspace_bytes(const moe_shape_t* shape) {
   if (!shape_ok(shape)) return 0;
   return layout_workspace_bytes(layout_geometry(*shape));
@@ -1255,7 +1266,8 @@ int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32
   // Two launches pay about 5 us more in fixed cost; one launch counts all
   // T*k ids in every workgroup. Measured on MI355X, they break even near
   // 24,576 ids (T = 4096, k = 6), so the tile counts are used above that.
-  const bool two = need > 0 && workspace && int64_t(shape->T) * shape->k > kTwoLaunchMinIds;
+  const bool big = int64_t(shape->T) * shape->k > kTwoLaunchMinIds;
+  const bool two = need > 0 && workspace && (g_layout_form < 0 ? big : g_layout_form == 1);
   LayoutArgs a{topk_ids, rank_counts, rank_offsets, expert_counts, expert_offsets,
                token_rank_slot, pair_row, err_word,
                two ? static_cast<int32_t*>(workspace) : nullptr};

@@ -285,6 +285,14 @@ int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
                       const int32_t* token_rank_slot, int64_t cap_rank, uint16_t* out,
                       float* out_f32, int32_t* err_word, void* stream);
 
+/*
+ * Testing hook (not for production callers; it changes a process-wide setting
+ * of this library and returns the previous value): which form of the layout
+ * runs when a workspace is given: -1 (default) by size as described at
+ * moe_dispatch_layout, 0 every workgroup counts all ids, 1 two launches.
+ */
+int moe_testing_set_layout_form(int form);
+
 #ifdef __cplusplus
 }
 #endif

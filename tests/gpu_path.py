@@ -61,7 +61,9 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
 
         ws = moe.layout_workspace_bytes(shape) if use_workspace else 0
         # workspace filled with garbage: the layout must overwrite what it reads
-        workspace = torch.full((max(ws, 4) // 4,), 0x5A5A5A5A, dtype=i32, device=dev) if ws else None
+        workspace = None
+        if ws:
+            workspace = torch.full(((ws + 15) // 16 * 4,), 0x5A5A5A5A, dtype=i32, device=dev)
         moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay,
                    workspace=workspace)
         moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
@@ -172,7 +174,7 @@ def run_gpu_two_stage(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int,
     wts_d = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).to(dev)
     err = torch.zeros(1, dtype=i32, device=dev)
     ws = moe.layout_workspace_bytes(shape)
-    workspace = torch.empty((max(ws, 4) // 4,), dtype=i32, device=dev) if ws else None
+    workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=i32, device=dev) if ws else None
     lay = moe.layout(ids_d, E, R, H, err=err, workspace=workspace)
     rank_buf = torch.empty((cap_rank, H), dtype=torch.int16, device=dev)
     rank_src = torch.full((cap_rank,), CANARY_IDX, dtype=i32, device=dev)

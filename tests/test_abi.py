@@ -143,7 +143,7 @@ def test_empty_batches_are_no_ops():
 
 def test_layout_workspace_sizes():
     L = moe.lib()
-    # one tile (T <= 256): no workspace; else 4 * (tiles rounded up to 4) * (E + R), tiles <= 64
+    # one tile (T <= 256): no workspace; else 4 * (tiles rounded up to 4) * (E + R)
     assert L.moe_layout_workspace_bytes(ctypes.byref(shape(T=256))) == 0
     assert L.moe_layout_workspace_bytes(ctypes.byref(shape(T=257))) == 4 * 4 * (16 + 4)
     assert L.moe_layout_workspace_bytes(

@@ -44,7 +44,7 @@ def run_gpu(hid, ids, E, R, align=1, block=0, cap_rank=None, cap_expert=None, sp
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(dev)
     err = torch.zeros(1, dtype=i32, device=dev)
     ws = moe.layout_workspace_bytes(shape)
-    workspace = torch.empty((max(ws, 4) // 4,), dtype=i32, device=dev) if ws else None
+    workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=i32, device=dev) if ws else None
     lay = moe.layout(ids_d, E, R, H, align=align, block=block, err=err, workspace=workspace)
     rq = torch.full((cap_rank + spare, H), CANARY, dtype=u8, device=dev)
     rs = torch.full((cap_rank + spare, H // 32), CANARY, dtype=u8, device=dev)

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import pins
 import synth
 from gpu_path import compare, relative_error_vs_exact, run_gpu, run_oracle
@@ -179,3 +180,36 @@ def test_layout_without_workspace(name, case):
     gpu = run_gpu(hid, ids, wts, E, R, y, use_workspace=False)
     ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
     compare(gpu, ref, f"no workspace {name or case}")
+
+
+LAYOUT_FORMS = [(0, "prefill"), (1, "prefill"), (1, "decode"), (0, "adv"), (1, "skew"),
+                (1, (70000, 16, 64, 8, 5, 0.05, 0.0, 12)), (1, (2000, 64, 1024, 64, 16, 0.02, 0.02, 9)),
+                (1, (257, 512, 16, 4, 2, 0.1, 0.0, 4))]
+
+
+@pytest.mark.parametrize("form,what", LAYOUT_FORMS,
+                         ids=[f"form{f}_{w if isinstance(w, str) else 'T%d' % w[0]}"
+                              for f, w in LAYOUT_FORMS])
+def test_layout_forms_with_workspace(form, what):
+    """Both forms of the layout with a workspace, forced whatever the size
+    (0: every workgroup counts all ids; 1: two launches through tile counts),
+    give the oracle's layout."""
+    import combine_topk_ids_02_amd as moe
+    if isinstance(what, str):
+        w, hid, ids, wts, y = workload_inputs(what)
+        E, R = w.E, w.R
+    else:
+        T, H, E, R, k, pn, pd, seed = what
+        rng = np.random.default_rng(seed)
+        ids = pins.rand_ids(rng, T, E, k, p_neg=pn, p_dup=pd)
+        wts = rng.random((T, k)).astype(np.float32)
+        hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
+        y = synth.expert_out_slots(seed, E, H, ids)
+    say(f"[layout form {form}] {what if isinstance(what, str) else what[:5]}")
+    old = moe.lib().moe_testing_set_layout_form(form)
+    try:
+        gpu = run_gpu(hid, ids, wts, E, R, y)
+    finally:
+        moe.lib().moe_testing_set_layout_form(old)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
+    compare(gpu, ref, f"layout form {form}")
