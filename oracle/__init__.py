@@ -46,6 +46,8 @@ class _Lib:
         lib.oracle_combine_ranks.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp]
         lib.oracle_quantize_mxfp8.restype = None
         lib.oracle_quantize_mxfp8.argtypes = [i64, i32, vp, vp, vp]
+        lib.oracle_quantize_mxfp4.restype = None
+        lib.oracle_quantize_mxfp4.argtypes = [i64, i32, vp, vp, vp]
         self.lib = lib
 
 
@@ -238,6 +240,34 @@ def permute_mxfp8(rank_q, rank_scale, rank_src_token, lay: dict, topk_ids, E: in
     es, _, _ = permute(np.ascontiguousarray(rank_scale).view(np.uint16), rank_src_token, lay,
                        topk_ids, E, cap_expert)
     return eq.view(np.uint8), es.view(np.uint8), esrc, err
+
+
+def quantize_mxfp4(x):
+    """bf16 rows [rows, H] (H a multiple of 32) -> (q [rows, H/2] uint8, two e2m1
+    codes per byte, even value in the low nibble; scale [rows, H/32] uint8)."""
+    xb = _c(x, np.uint16)
+    rows, H = xb.shape
+    assert H % 32 == 0
+    q = np.zeros((rows, H // 2), np.uint8)
+    sc = np.zeros((rows, H // 32), np.uint8)
+    _load().oracle_quantize_mxfp4(rows, H, _p(xb), _p(q), _p(sc))
+    return q, sc
+
+
+def pack_mxfp4(hidden, token_rank_slot, cap_rank: int):
+    """Quantise every hidden row once to MXFP4, then pack codes and scales once
+    per distinct rank (plain byte copies, as in pack())."""
+    q, sc = quantize_mxfp4(hidden)
+    rq, src, err = pack(q.view(np.uint16), token_rank_slot, cap_rank)
+    rs, _, _ = pack(sc.view(np.uint16), token_rank_slot, cap_rank)
+    return rq.view(np.uint8), rs.view(np.uint8), src, err
+
+
+def permute_mxfp4(rank_q, rank_scale, rank_src_token, lay: dict, topk_ids, E: int,
+                  cap_expert: int):
+    """Regroup MXFP4 rows by expert: codes and scales move as bytes, exactly as
+    permute_mxfp8 moves them."""
+    return permute_mxfp8(rank_q, rank_scale, rank_src_token, lay, topk_ids, E, cap_expert)
 
 
 def place_slots(y_slots: np.ndarray, pair_row: np.ndarray, rows: int) -> np.ndarray:

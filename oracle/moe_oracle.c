@@ -321,3 +321,62 @@ void oracle_quantize_mxfp8(int64_t rows, int32_t H, const uint16_t* x, uint8_t* 
     }
   }
 }
+
+/* The value of a non-negative OCP FP4 E2M1 code: exponent bias 1, one
+ * mantissa bit, a subnormal at exponent field 0. */
+static double e2m1_magnitude(int code) {
+  const int ef = (code >> 1) & 3, mf = code & 1;
+  if (ef == 0) return 0.5 * mf;
+  return ldexp(1.0 + mf / 2.0, ef - 1);
+}
+
+void oracle_quantize_mxfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale) {
+  const int32_t nblk = H / 32;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t b = 0; b < nblk; ++b) {
+      const uint16_t* v = x + r * H + (int64_t)b * 32;
+      uint8_t* out = q + r * (H / 2) + (int64_t)b * 16;
+      double amax = 0.0;
+      int special = 0;
+      for (int i = 0; i < 32; ++i) {
+        const double a = fabs((double)widen_bf16(v[i]));
+        if (!isfinite(a)) special = 1;
+        else if (a > amax) amax = a;
+      }
+      int e = -127;
+      if (!special && amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* floor(log2(amax)) = ex - 1 */
+        e = ex - 1 - 2;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+      }
+      scale[r * nblk + b] = special ? 0xFF : (uint8_t)(e + 127);
+      for (int i = 0; i < 32; ++i) {
+        int code;
+        if (special) {
+          code = 7;
+        } else {
+          const double mag = fabs(ldexp((double)widen_bf16(v[i]), -e));
+          /* nearest of the 8 non-negative codes; on a tie, the even code */
+          int best = 0;
+          double best_d = fabs(mag - e2m1_magnitude(0));
+          for (int c = 1; c < 8; ++c) {
+            const double d = fabs(mag - e2m1_magnitude(c));
+            if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+              best = c;
+              best_d = d;
+            }
+          }
+          code = best;
+        }
+        code |= (v[i] >> 15) << 3;
+        if (i % 2 == 0)
+          out[i / 2] = (uint8_t)code;
+        else
+          out[i / 2] = (uint8_t)(out[i / 2] | (code << 4));
+      }
+    }
+  }
+}

@@ -160,6 +160,24 @@ int oracle_combine_ranks(int32_t T, int32_t H, int32_t R, const uint16_t* partia
 void oracle_quantize_mxfp8(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
                            uint8_t* scale);
 
+/*
+ * The 4-bit variant of the quantised wire format ([A2A] sec 7.2 lists a 4-bit
+ * row beside the 8-bit one). Read as OCP MX MXFP4, the 4-bit MX format: per
+ * block of 32 consecutive values,
+ *   e     = floor(log2(amax)) - 2  (2 = exponent of the largest e2m1 value, 6),
+ *           clamped to [-127, 127]; amax = 0 gives -127;
+ *   scale = e + 127 as one byte (E8M0); 0xFF if the block holds a NaN or an
+ *           infinity;
+ *   q_i   = the OCP FP4 E2M1 value nearest to v_i / 2^e (values 0, 0.5, 1,
+ *           1.5, 2, 3, 4, 6; ties to the even code, magnitudes past 6 saturate
+ *           to 6, sign kept); in a NaN/Inf block every q_i is the largest
+ *           magnitude (code 7) with the value's sign.
+ * Two codes per byte, the even-indexed value in the low nibble. Rows of x are
+ * H bf16 values; q gets H/2 bytes and scale H/32 bytes per row.
+ */
+void oracle_quantize_mxfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale);
+
 #ifdef __cplusplus
 }
 #endif

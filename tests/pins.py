@@ -924,6 +924,103 @@ def pin_mxfp8_pack_and_permute():
     assert err2 == 0 and np.array_equal(eq[:P], q[t_of]) and np.array_equal(es[:P], sc[t_of])
 
 
+def _e2m1_table():
+    """Magnitudes of the 8 non-negative OCP E2M1 codes from the format's
+    definition (bias 1, one mantissa bit, a subnormal at exponent 0)."""
+    return np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _unpack_nibbles(q):
+    q = np.asarray(q, np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = q & 0xF
+    out[..., 1::2] = q >> 4
+    return out
+
+
+def pin_mxfp4_every_code_round_trips():
+    """A block whose largest magnitude is 6 (the largest e2m1 value) has scale
+    2^0; all 16 codes (both signs, -0 included) come back as themselves, the
+    even-indexed value in the low nibble."""
+    mags = _e2m1_table()
+    codes = np.array([7] + list(range(16)) + [7] * 15)
+    vals = np.where(codes & 8, -1.0, 1.0) * mags[codes & 7]
+    q, sc = oracle.quantize_mxfp4(_bf16(vals[None, :].astype(np.float32)))
+    assert int(sc[0, 0]) == 127
+    assert np.array_equal(_unpack_nibbles(q)[0], codes), _unpack_nibbles(q)[0]
+    assert q[0, 0] == 0x07 | (0x00 << 4) and q[0, 1] == 0x01 | (0x02 << 4)
+
+
+def pin_mxfp4_hand_cases():
+    """Hand-derived cases of the MX rule for e2m1 (e = floor(log2 amax) - 2):
+    ties go to the even code, magnitudes past 6 saturate, the scale clamps."""
+    H = 32
+
+    def block(values, pad=0.0):
+        v = list(values) + [pad] * (H - len(values))
+        q, sc = oracle.quantize_mxfp4(_bf16(np.array([v], np.float32)))
+        return _unpack_nibbles(q)[0], int(sc[0, 0])
+
+    # with 6 present e = 0: 0.25 -> 0 (tie 0 / 0.5), 0.75 -> 1.0 (tie 0.5 / 1), 1.25 -> 1.0,
+    # 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5.0 -> 4.0, -0.25 -> -0 (code 8)
+    c, s = block([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25])
+    assert s == 127 and list(c[:9]) == [7, 0, 2, 2, 4, 4, 6, 6, 8], list(c[:9])
+    # amax 7 -> e = 0, 7 saturates to 6; amax 1 -> e = -2: 1 -> 4 (code 6), 0.375 -> 1.5 (3)
+    c, s = block([7.0, -6.5])
+    assert s == 127 and list(c[:2]) == [7, 15]
+    c, s = block([1.0, 0.375, -0.0625])
+    assert s == 127 - 2 and list(c[:3]) == [6, 3, 8 | 0], list(c[:3])  # -0.25 ties to -0
+    # smallest bf16 subnormal: e = -135 clamps to -127, 2^-133 / 2^-127 = 2^-6 -> 0 (code 0)
+    q, sc = oracle.quantize_mxfp4(np.array([[0x0001] + [0] * 31], np.uint16))
+    assert int(sc[0, 0]) == 0 and np.all(q == 0)
+    # NaN / infinity: scale 0xFF, codes of the largest magnitude with their sign
+    q, sc = oracle.quantize_mxfp4(np.array([[0x3F80, 0x7FC0, 0xBF80, 0xFF80] + [0] * 28],
+                                           np.uint16))
+    assert int(sc[0, 0]) == 0xFF and list(_unpack_nibbles(q)[0, :4]) == [7, 7, 15, 15]
+
+
+def pin_mxfp4_error_bound():
+    """Random rows: after scaling the block maximum lies in [4, 8) and every
+    value is within half an e2m1 step of its code (a quarter below 2, a half
+    from 2 to 4, one from 4 to 6), unless it saturated at 6."""
+    rng = np.random.default_rng(111)
+    mags = _e2m1_table()
+    vals = rng.standard_normal((64, 256)) * np.exp2(rng.uniform(-20, 20, (64, 256)))
+    x = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q, sc = oracle.quantize_mxfp4(x)
+    xf = bf16_bits_to_float(x).astype(np.float64).reshape(64, 8, 32)
+    e = sc.astype(np.int64) - 127
+    scaled = np.abs(xf) / np.exp2(e)[:, :, None]
+    ok = (e > -127) & (e < 127)
+    top = scaled.max(axis=2)
+    assert np.all((top[ok] >= 4) & (top[ok] < 8))
+    codes = _unpack_nibbles(q).reshape(64, 8, 32)
+    deq = mags[codes & 7]
+    sat = scaled > 6
+    step = np.where(scaled < 2, 0.5, np.where(scaled < 4, 1.0, 2.0))
+    assert np.all((np.abs(deq - scaled) <= step / 2) | sat)
+    assert np.all(deq[sat] == 6)
+    assert np.all(((codes & 8) != 0) == np.signbit(xf))
+
+
+def pin_mxfp4_pack_and_permute():
+    """The 4-bit dispatch moves bytes only: packed and regrouped rows hold the
+    codes and scales of their source token's quantised row."""
+    rng = np.random.default_rng(113)
+    T, E, R, k, H = 70, 32, 4, 3, 128
+    ids = rand_ids(rng, T, E, k, p_neg=0.1)
+    hid = synth.normal_bf16(27, 0, T * H).reshape(T, H)
+    lay = oracle.layout(ids, E, R)
+    q, sc = oracle.quantize_mxfp4(hid)
+    rq, rs, src, err = oracle.pack_mxfp4(hid, lay["token_rank_slot"], T * min(k, R))
+    C = int(lay["rank_offsets"][-1])
+    assert err == 0 and np.array_equal(rq[:C], q[src[:C]]) and np.array_equal(rs[:C], sc[src[:C]])
+    eq, es, esrc, err2 = oracle.permute_mxfp4(rq, rs, src, lay, ids, E, T * k)
+    P = int(lay["expert_offsets"][-1])
+    t_of = esrc[:P] // k
+    assert err2 == 0 and np.array_equal(eq[:P], q[t_of]) and np.array_equal(es[:P], sc[t_of])
+
+
 PINS = [
     pin_layout_stable_sort,
     pin_layout_brute_force,
@@ -957,4 +1054,8 @@ PINS = [
     pin_mxfp8_hand_cases,
     pin_mxfp8_error_bound,
     pin_mxfp8_pack_and_permute,
+    pin_mxfp4_every_code_round_trips,
+    pin_mxfp4_hand_cases,
+    pin_mxfp4_error_bound,
+    pin_mxfp4_pack_and_permute,
 ]

@@ -117,17 +117,38 @@ MUTANTS = {
         "e = ex - 1 - 8;",
         "e = ex - 8;"),
     "mx scale not clamped below": (
-        "if (e < -127) e = -127;",
-        "if (e < -160) e = -160;"),
+        "e = ex - 1 - 8;\n        if (e < -127) e = -127;",
+        "e = ex - 1 - 8;\n        if (e < -160) e = -160;"),
+    "mx4 scale not clamped below": (
+        "e = ex - 1 - 2;\n        if (e < -127) e = -127;",
+        "e = ex - 1 - 2;\n        if (e < -160) e = -160;"),
     "mx ties away from zero": (
-        "if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {",
-        "if (d <= best_d) {"),
+        "e4m3_magnitude(c));\n          if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {",
+        "e4m3_magnitude(c));\n          if (d <= best_d) {"),
+    "mx4 ties away from zero": (
+        "e2m1_magnitude(c));\n            if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {",
+        "e2m1_magnitude(c));\n            if (d <= best_d) {"),
+    "mx4 exponent off by one (emax 3)": (
+        "e = ex - 1 - 2;",
+        "e = ex - 1 - 3;"),
+    "mx4 high nibble first": (
+        "        if (i % 2 == 0)\n          out[i / 2] = (uint8_t)code;\n        else\n          out[i / 2] = (uint8_t)(out[i / 2] | (code << 4));",
+        "        if (i % 2 == 0)\n          out[i / 2] = (uint8_t)(code << 4);\n        else\n          out[i / 2] = (uint8_t)(out[i / 2] | code);"),
+    "e2m1 subnormal halved": (
+        "if (ef == 0) return 0.5 * mf;",
+        "if (ef == 0) return 0.25 * mf;"),
+    "mx4 drops the sign": (
+        "        code |= (v[i] >> 15) << 3;",
+        "        code |= 0;"),
     "mx drops the sign": (
         "out[i] = (uint8_t)(((v[i] >> 15) << 7) | best);",
         "out[i] = (uint8_t)best;"),
     "mx ignores NaN blocks": (
-        "if (!isfinite(a)) special = 1;\n        else if (a > amax) amax = a;",
-        "if (!isfinite(a)) special = 0;\n        else if (a > amax) amax = a;"),
+        "if (!isfinite(a)) special = 1;\n        else if (a > amax) amax = a;\n      }\n      if (special) {",
+        "if (!isfinite(a)) special = 0;\n        else if (a > amax) amax = a;\n      }\n      if (special) {"),
+    "mx4 ignores NaN blocks": (
+        "if (!isfinite(a)) special = 1;\n        else if (a > amax) amax = a;\n      }\n      int e = -127;",
+        "if (!isfinite(a)) special = 0;\n        else if (a > amax) amax = a;\n      }\n      int e = -127;"),
     "e4m3 subnormals one binade low": (
         "if (ef == 0) return ldexp((double)mf, -9);",
         "if (ef == 0) return ldexp((double)mf, -10);"),
