@@ -50,11 +50,11 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
     }
 
 
-def mxfp8_bytes(T, H, R, k, C, P):
+def mx_bytes(T, H, R, k, C, P, bits=8):
     """Bytes of the quantised dispatch: the fused quantise-and-pack reads each
-    bf16 hidden row once and writes H codes + H/32 scales per copy; the permute
-    reads each quantised rank row once and writes it once per pair."""
-    qrow = H + H // 32
+    bf16 hidden row once and writes H*bits/8 code bytes + H/32 scales per copy;
+    the permute reads each quantised rank row once and writes it once per pair."""
+    qrow = H * bits // 8 + H // 32
     return {
         "pack": 2 * T * H + C * qrow + 4 * T * R + 4 * C,
         "permute": C * qrow + P * qrow + 4 * C + 8 * T * k + 4 * P,
@@ -230,7 +230,7 @@ class Rig:
     four library calls on the current stream."""
 
     def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0,
-                 mxfp8: bool = False):
+                 mx_bits: int = 0):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -261,17 +261,18 @@ class Rig:
         self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         self.stream = torch.cuda.current_stream(dev)
         self.calls = CALLS
-        self.mxfp8 = mxfp8
-        if mxfp8:
+        self.mx_bits = mx_bits
+        if mx_bits:
             # quantised dispatch: codes and scales replace the bf16 rank and expert rows
             u8 = torch.uint8
-            self.rank_q = torch.empty((self.shape.cap_rank, w.H), dtype=u8, device=dev)
+            qw = w.H * mx_bits // 8
+            self.rank_q = torch.empty((self.shape.cap_rank, qw), dtype=u8, device=dev)
             self.rank_s = torch.empty((self.shape.cap_rank, w.H // 32), dtype=u8, device=dev)
-            self.exp_q = torch.empty((self.shape.cap_expert, w.H), dtype=u8, device=dev)
+            self.exp_q = torch.empty((self.shape.cap_expert, qw), dtype=u8, device=dev)
             self.exp_s = torch.empty((self.shape.cap_expert, w.H // 32), dtype=u8, device=dev)
             self.buf.rank_buf = self.buf.expert_buf = None
             torch.cuda.empty_cache()
-            self.nbytes.update(mxfp8_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
+            self.nbytes.update(mx_bytes(w.T, w.H, w.R, w.k, self.C, self.P, mx_bits))
             self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         if two_stage:
             self.partial = torch.empty((self.shape.cap_rank, w.H), dtype=torch.bfloat16,
@@ -285,18 +286,18 @@ class Rig:
         if name == "layout":
             moe.layout(self.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
                        out=b.layout_dict(), workspace=b.workspace)
-        elif name == "pack" and self.mxfp8:
-            moe.pack_mxfp8(self.hid_d, b.token_rank_slot, s.E, s.k, self.rank_q, self.rank_s,
-                           b.rank_src_token, err=b.err)
+        elif name == "pack" and self.mx_bits:
+            moe.pack_mx(self.mx_bits, self.hid_d, b.token_rank_slot, s.E, s.k, self.rank_q,
+                        self.rank_s, b.rank_src_token, err=b.err)
         elif name == "pack":
             moe.pack(self.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
                      err=b.err)
-        elif name == "permute" and self.mxfp8:
-            moe.permute_mxfp8(self.rank_q, self.rank_s, b.rank_src_token, b.rank_offsets,
-                              self.ids_d, b.pair_row, s.E, self.exp_q, self.exp_s,
-                              b.expert_src_pair, expert_counts=b.expert_counts,
-                              expert_offsets=b.expert_offsets, align=s.align, block=s.block,
-                              err=b.err)
+        elif name == "permute" and self.mx_bits:
+            moe.permute_mx(self.mx_bits, self.rank_q, self.rank_s, b.rank_src_token,
+                           b.rank_offsets, self.ids_d, b.pair_row, s.E, self.exp_q, self.exp_s,
+                           b.expert_src_pair, expert_counts=b.expert_counts,
+                           expert_offsets=b.expert_offsets, align=s.align, block=s.block,
+                           err=b.err)
         elif name == "permute":
             moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
                         s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
@@ -412,13 +413,14 @@ def sweep(names, dev, with_oracle: bool) -> None:
         name, _, opt = spec.partition(":")
         opts = dict(kv.split("=") for kv in opt.split(",") if "=" in kv)
         align, block = int(opts.get("align", 1)), int(opts.get("block", 0))
-        mx = "mxfp8" in opt.split(",")
+        flags = opt.split(",")
+        mx = 8 if "mxfp8" in flags else 4 if "mxfp4" in flags else 0
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev, two_stage=True, align=align, block=block, mxfp8=mx)
+        rig = Rig(w, dev, two_stage=True, align=align, block=block, mx_bits=mx)
         for _ in range(5):
             rig.step()
         res = {"workload": w.describe(), "layout_shape": {"align": align, "block": block},
-               "dispatch_format": "mxfp8" if mx else "bf16",
+               "dispatch_format": f"mxfp{mx}" if mx else "bf16",
                "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
                "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
         for mode, fl in (("warm", None), ("cold", flush)):
@@ -509,7 +511,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
                     const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
-                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8",
+                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,adv:mxfp4",
                     default=None,
                     metavar="WORKLOADS", help="per-call warm/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",

@@ -29,6 +29,7 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_layout_workspace_bytes", "moe_dispatch_pack",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
+           "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
            "moe_testing_set_layout_form")
 
 
@@ -89,6 +90,10 @@ def lib():
     L.moe_permute_by_expert_mxfp8.restype = ctypes.c_int
     L.moe_permute_by_expert_mxfp8.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp,
                                               vp, i64, vp, vp]
+    L.moe_dispatch_pack_mxfp4.restype = ctypes.c_int
+    L.moe_dispatch_pack_mxfp4.argtypes = L.moe_dispatch_pack_mxfp8.argtypes
+    L.moe_permute_by_expert_mxfp4.restype = ctypes.c_int
+    L.moe_permute_by_expert_mxfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
     L.moe_testing_set_layout_form.restype = ctypes.c_int
     L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
     if L.moe_abi_version() != ABI_VERSION:
@@ -229,38 +234,54 @@ def _bytes(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def pack_mxfp8(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, rank_q,
-               rank_scale, rank_src_token, *, err=None) -> None:
-    """moe_dispatch_pack_mxfp8: quantise each hidden row once to MXFP8 and pack
-    it once per distinct rank into rank_q [cap_rank, H] (uint8 e4m3 codes) and
-    rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
+def pack_mx(bits: int, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int,
+            rank_q, rank_scale, rank_src_token, *, err=None) -> None:
+    """moe_dispatch_pack_mxfp8 (bits 8) or _mxfp4 (bits 4): quantise each hidden
+    row once and pack it once per distinct rank into rank_q [cap_rank, H*bits/8]
+    (uint8 codes) and rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
     shape = Shape(T, H, E, R, k)
-    st = lib().moe_dispatch_pack_mxfp8(
-        ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
-        _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
-        rank_q.shape[0], _ptr(err), _stream(hidden.device))
-    _check(st, "moe_dispatch_pack_mxfp8")
+    fn = lib().moe_dispatch_pack_mxfp8 if bits == 8 else lib().moe_dispatch_pack_mxfp4
+    st = fn(ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
+            _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
+            rank_q.shape[0], _ptr(err), _stream(hidden.device))
+    _check(st, f"moe_dispatch_pack_mxfp{bits}")
 
 
-def permute_mxfp8(rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids, pair_row, E: int,
-                  expert_q, expert_scale, expert_src_pair, *, expert_counts=None,
-                  expert_offsets=None, align: int = 1, block: int = 0, err=None) -> None:
-    """moe_permute_by_expert_mxfp8: the codes and scales of each rank-buffer row
-    to the rows of its token's experts on that rank."""
+def pack_mxfp8(*args, **kw) -> None:
+    pack_mx(8, *args, **kw)
+
+
+def pack_mxfp4(*args, **kw) -> None:
+    pack_mx(4, *args, **kw)
+
+
+def permute_mx(bits: int, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids, pair_row,
+               E: int, expert_q, expert_scale, expert_src_pair, *, expert_counts=None,
+               expert_offsets=None, align: int = 1, block: int = 0, err=None) -> None:
+    """moe_permute_by_expert_mxfp8 / _mxfp4: the codes and scales of each
+    rank-buffer row to the rows of its token's experts on that rank."""
     T, k = topk_ids.shape
-    H = rank_q.shape[1]
+    H = rank_q.shape[1] * 8 // bits
     R = rank_offsets.shape[0] - 1
     shape = Shape(T, H, E, R, k, align, block)
-    st = lib().moe_permute_by_expert_mxfp8(
-        ctypes.byref(shape.c()), _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)),
-        _ptr(_i32(rank_src_token)), _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)),
-        _ptr(_i32(pair_row)), _ptr(None if expert_counts is None else _i32(expert_counts)),
-        _ptr(None if expert_offsets is None else _i32(expert_offsets)), rank_q.shape[0],
-        _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)), _ptr(_i32(expert_src_pair)),
-        expert_q.shape[0], _ptr(err), _stream(rank_q.device))
-    _check(st, "moe_permute_by_expert_mxfp8")
+    fn = lib().moe_permute_by_expert_mxfp8 if bits == 8 else lib().moe_permute_by_expert_mxfp4
+    st = fn(ctypes.byref(shape.c()), _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)),
+            _ptr(_i32(rank_src_token)), _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)),
+            _ptr(_i32(pair_row)), _ptr(None if expert_counts is None else _i32(expert_counts)),
+            _ptr(None if expert_offsets is None else _i32(expert_offsets)), rank_q.shape[0],
+            _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)), _ptr(_i32(expert_src_pair)),
+            expert_q.shape[0], _ptr(err), _stream(rank_q.device))
+    _check(st, f"moe_permute_by_expert_mxfp{bits}")
+
+
+def permute_mxfp8(*args, **kw) -> None:
+    permute_mx(8, *args, **kw)
+
+
+def permute_mxfp4(*args, **kw) -> None:
+    permute_mx(4, *args, **kw)
 
 
 def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=None,

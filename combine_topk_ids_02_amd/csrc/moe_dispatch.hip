@@ -735,13 +735,15 @@ __device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts
 // with ties to even, saturating at 448, sign kept.
 
 // e of a block from the largest magnitude's bf16 bits (0 < amax < 0x7F80).
-__device__ __forceinline__ int mx_block_exponent(uint32_t amax) {
+// emax: exponent of the element format's largest value (8 for e4m3's 448, 2
+// for e2m1's 6).
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax, int emax) {
   if (amax == 0) return -127;
   const int eb = int(amax >> 7);
   // floor(log2): a normal bf16 has it in its exponent field; a subnormal
   // m * 2^-133 has it at the top set bit of m.
   const int lg = eb > 0 ? eb - 127 : -133 + (31 - __clz(int(amax & 0x7F)));
-  return min(127, max(-127, lg - 8));
+  return min(127, max(-127, lg - emax));
 }
 
 typedef short mx_short2 __attribute__((ext_vector_type(2)));
@@ -763,9 +765,29 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float scale
   return x - (nan_bytes >> 7);
 }
 
+// Eight bf16 divided by the block scale and rounded to e2m1 by the gfx950
+// scaled conversion, two codes per byte, the even value in the low nibble.
+// (It rounds to nearest even and saturates at 6 exactly as the MX rule does:
+// e2m1 has no NaN to overflow into.) The instruction is written out, one pair
+// into byte 0 of a fresh register, because this compiler mis-models which
+// source bits the fp4 conversion builtins read (it narrowed the loads feeding
+// them and merged conversions of different words).
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t two_bf16, float scale) {
+  uint32_t r;
+  asm("v_cvt_scalef32_pk_fp4_bf16 %0, %1, %2" : "=v"(r) : "v"(two_bf16), "v"(scale));
+  return r & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t e2m1x8(vec4 v, float scale) {
+  return e2m1_pair(v[0], scale) | (e2m1_pair(v[1], scale) << 8) |
+         (e2m1_pair(v[2], scale) << 16) | (e2m1_pair(v[3], scale) << 24);
+}
+
 // Quantises the 8 bf16 of `v` (one quarter of a 32-value block, the other
-// quarters in the neighbouring lanes of the same lane quad) to 8 e4m3 codes
-// (lo, hi: little-endian bytes) and returns the block's scale byte.
+// quarters in the neighbouring lanes of the same lane quad) and returns the
+// block's scale byte. kBits 8: 8 e4m3 codes in lo, hi (little-endian bytes);
+// kBits 4: 8 e2m1 codes in lo (hi unused).
+template <int kBits>
 __device__ __forceinline__ uint32_t mx_quantise(vec4 v, uint32_t& lo, uint32_t& hi) {
   uint32_t amax = 0;
 #pragma unroll
@@ -775,21 +797,38 @@ __device__ __forceinline__ uint32_t mx_quantise(vec4 v, uint32_t& lo, uint32_t& 
   }
   amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, kWave)));
   amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
-  if (amax >= 0x7F80u) {  // NaN or infinity in the block
+  if (amax >= 0x7F80u) {  // NaN or infinity in the block: NaN scale, marked codes
     uint32_t c[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      c[2 * i] = ((v[i] >> 8) & 0x80u) | 0x7Fu;
-      c[2 * i + 1] = ((v[i] >> 24) & 0x80u) | 0x7Fu;
+      if (kBits == 8) {  // e4m3 NaN with the value's sign
+        c[2 * i] = ((v[i] >> 8) & 0x80u) | 0x7Fu;
+        c[2 * i + 1] = ((v[i] >> 24) & 0x80u) | 0x7Fu;
+      } else {  // the largest e2m1 code with the value's sign
+        c[2 * i] = ((v[i] >> 12) & 0x8u) | 0x7u;
+        c[2 * i + 1] = ((v[i] >> 28) & 0x8u) | 0x7u;
+      }
     }
-    lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    if (kBits == 8) {
+      lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    } else {
+      lo = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lo |= c[j] << (4 * j);
+      hi = 0;
+    }
     return 0xFFu;
   }
-  const int e = mx_block_exponent(amax);
+  const int e = mx_block_exponent(amax, kBits == 8 ? 8 : 2);
   const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // the E8M0 byte as a float exponent
-  lo = e4m3x4(v[0], v[1], scale);
-  hi = e4m3x4(v[2], v[3], scale);
+  if (kBits == 8) {
+    lo = e4m3x4(v[0], v[1], scale);
+    hi = e4m3x4(v[2], v[3], scale);
+  } else {
+    lo = e2m1x8(v, scale);
+    hi = 0;
+  }
   return uint32_t(e + 127);
 }
 
@@ -798,7 +837,8 @@ __device__ __forceinline__ uint32_t mx_quantise(vec4 v, uint32_t& lo, uint32_t& 
 // in the token's set. Passes of V groups of 64 vec4, V dividing the row's
 // group count (H is a multiple of 512). Codes and scales are stored with
 // ordinary stores, like the bf16 copies, for the permute to find in cache.
-template <int V>
+// kBits 8: MXFP8, 8 code bytes per vec4 of input; 4: MXFP4, 4 code bytes.
+template <int V, int kBits>
 __global__ __launch_bounds__(kBlock) void pack_rows_mx(
     const vec4* hidden, const int32_t* __restrict__ token_rank_slot, uint8_t* rank_q,
     uint8_t* rank_scale, int32_t* __restrict__ rank_src_token, int T, int R, int nvec,
@@ -812,7 +852,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
   if (ok) rank_src_token[slot] = t;
   const uint64_t dests = __ballot(ok);
   if (!dests) return;
-  const int64_t qrow = (int64_t)nvec * 8;  // bytes of codes per row (H)
+  const int64_t qrow = (int64_t)nvec * kBits;  // bytes of codes per row (H or H/2)
   const int64_t srow = nvec / 4;           // scale bytes per row (H / 32)
   const vec4* src = hidden + (int64_t)t * nvec;
   for (int c0 = 0; c0 < nvec; c0 += kWave * V) {
@@ -822,7 +862,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
     uint32_t lo[V], hi[V], sw[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) {
-      const uint32_t sb = mx_quantise(v[q], lo[q], hi[q]);
+      const uint32_t sb = mx_quantise<kBits>(v[q], lo[q], hi[q]);
       // lanes 16w collect the scale bytes of blocks 4w..4w+3 (lanes 16w, +4, +8, +12)
       sw[q] = sb | (uint32_t(__shfl(int(sb), lane + 4, kWave)) << 8) |
               (uint32_t(__shfl(int(sb), lane + 8, kWave)) << 16) |
@@ -838,10 +878,14 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
 #pragma unroll
       for (int q = 0; q < V; ++q) {
         const int col = c0 + q * kWave + lane;
-        uint2 w;
-        w.x = lo[q];
-        w.y = hi[q];
-        *reinterpret_cast<uint2*>(qdst + (int64_t)col * 8) = w;
+        if (kBits == 8) {
+          uint2 w;
+          w.x = lo[q];
+          w.y = hi[q];
+          *reinterpret_cast<uint2*>(qdst + (int64_t)col * 8) = w;
+        } else {
+          *reinterpret_cast<uint32_t*>(qdst + (int64_t)col * 4) = lo[q];
+        }
         if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sdst + col / 4) = sw[q];
       }
     }
@@ -1155,10 +1199,15 @@ struct PermuteLaunch {
 
 template <int V>
 struct PackMxLaunch {
-  static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots, uint8_t* rq,
-                 uint8_t* rs, int32_t* src, int T, int R, int nvec, int64_t cap, int32_t* err) {
-    hipLaunchKernelGGL(pack_rows_mx<V>, grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src, T, R,
-                       nvec, cap, err);
+  static void go(int bits, dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots,
+                 uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R, int nvec, int64_t cap,
+                 int32_t* err) {
+    if (bits == 8)
+      hipLaunchKernelGGL((pack_rows_mx<V, 8>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src,
+                         T, R, nvec, cap, err);
+    else
+      hipLaunchKernelGGL((pack_rows_mx<V, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src,
+                         T, R, nvec, cap, err);
   }
 };
 
@@ -1223,6 +1272,23 @@ int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_
                             static_cast<vec4*>(expert_rows), static_cast<vec4*>(expert_scale),
                             expert_src_pair, sh.T, sh.E, sh.R, sh.k, sh.E / sh.R, sh.block, nvec,
                             nvec_s, pad_waves, cap_rank, cap_expert, err_word);
+  return launch_status();
+}
+
+int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
+                 const int32_t* token_rank_slot, uint8_t* rank_q, uint8_t* rank_scale,
+                 int32_t* rank_src_token, int64_t cap_rank, int32_t* err_word, void* stream) {
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0 || cap_rank < 0) return MOE_ERR_ARG;
+  if (shape->T == 0) return MOE_OK;
+  if (!hidden || !token_rank_slot || (cap_rank > 0 && (!rank_q || !rank_scale || !rank_src_token)))
+    return MOE_ERR_ARG;
+  if (!aligned16(hidden) || !aligned16(rank_q) || !aligned16(rank_scale)) return MOE_ERR_ARG;
+  const int nvec = shape->H / 8;
+  ByVec<PackMxLaunch>::run(mx_vec(nvec / kWave), bits, dim3(blocks_for(shape->T)),
+                           static_cast<hipStream_t>(stream),
+                           reinterpret_cast<const vec4*>(hidden), token_rank_slot, rank_q,
+                           rank_scale, rank_src_token, shape->T, shape->R, nvec, cap_rank,
+                           err_word);
   return launch_status();
 }
 
@@ -1307,18 +1373,16 @@ int moe_dispatch_pack_mxfp8(const moe_shape_t* shape, const uint16_t* hidden,
                             const int32_t* token_rank_slot, uint8_t* rank_q,
                             uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
                             int32_t* err_word, void* stream) {
-  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0 || cap_rank < 0) return MOE_ERR_ARG;
-  if (shape->T == 0) return MOE_OK;
-  if (!hidden || !token_rank_slot || (cap_rank > 0 && (!rank_q || !rank_scale || !rank_src_token)))
-    return MOE_ERR_ARG;
-  if (!aligned16(hidden) || !aligned16(rank_q) || !aligned16(rank_scale)) return MOE_ERR_ARG;
-  const int nvec = shape->H / 8;
-  ByVec<PackMxLaunch>::run(mx_vec(nvec / kWave), dim3(blocks_for(shape->T)),
-                           static_cast<hipStream_t>(stream),
-                           reinterpret_cast<const vec4*>(hidden), token_rank_slot, rank_q,
-                           rank_scale, rank_src_token, shape->T, shape->R, nvec, cap_rank,
-                           err_word);
-  return launch_status();
+  return pack_mx_impl(8, shape, hidden, token_rank_slot, rank_q, rank_scale, rank_src_token,
+                      cap_rank, err_word, stream);
+}
+
+int moe_dispatch_pack_mxfp4(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream) {
+  return pack_mx_impl(4, shape, hidden, token_rank_slot, rank_q, rank_scale, rank_src_token,
+                      cap_rank, err_word, stream);
 }
 
 int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
@@ -1340,6 +1404,28 @@ int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
   return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
                       expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
                       expert_src_pair, cap_expert, err_word, stream, shape->H / 16,
+                      shape->H / 512);
+}
+
+int moe_permute_by_expert_mxfp4(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream) {
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0) return MOE_ERR_ARG;
+  const int64_t max_rows =
+      std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
+  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
+  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
+  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
+  // a non-null marker selects the two-row kernel even when nothing is moved
+  const void* rs = rank_scale ? rank_scale : static_cast<const void*>(rank_q);
+  return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
+                      expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
+                      expert_src_pair, cap_expert, err_word, stream, shape->H / 32,
                       shape->H / 512);
 }
 

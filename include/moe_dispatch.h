@@ -228,6 +228,37 @@ int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
                                 void* stream);
 
 /*
+ * The 4-bit variant of the quantised dispatch ([A2A] sec 7.2 lists a 4-bit row
+ * beside the 8-bit one): MXFP4, OCP FP4 E2M1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * and their negatives) with one E8M0 scale byte per 32 values, e =
+ * floor(log2(max |v|)) - 2 clamped to [-127, 127] (0xFF for a block holding a
+ * NaN or an infinity, whose codes are then the largest magnitude with the
+ * value's sign); codes nearest to v / 2^e, ties to the even code, saturating at
+ * 6. Two codes per byte, the even-indexed value in the low nibble.
+ *   rank_q [cap_rank*H/2] out: codes; rank_scale [cap_rank*H/32] out: scales
+ *   other arguments and requirements as for moe_dispatch_pack_mxfp8.
+ */
+int moe_dispatch_pack_mxfp4(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream);
+
+/*
+ * moe_permute_by_expert for MXFP4 rows: each row's H/2 code bytes and H/32
+ * scales move together, as in moe_permute_by_expert_mxfp8.
+ *   rank_q [cap_rank*H/2], rank_scale [cap_rank*H/32] in
+ *   expert_q [cap_expert*H/2], expert_scale [cap_expert*H/32] out
+ */
+int moe_permute_by_expert_mxfp4(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream);
+
+/*
  * Combine ([A2A] sec 1.1: the MoE output of a token is the sum of its chosen
  * experts' outputs, each multiplied by its weight; sec 7.1: the sum is taken
  * in 32-bit floats; [GPUs] sec 3.3: a fixed addition order makes the result

@@ -1,7 +1,7 @@
-"""GPU parity of the quantised dispatch (fused MXFP8 quantise-and-pack, and the
-permute of quantised rows) against the oracle, through the C ABI: codes,
-scales, source ids and untouched canary rows, bit for bit. Integer work, so the
-bar is bit-exact."""
+"""GPU parity of the quantised dispatch (fused MXFP8 and MXFP4 quantise-and-
+pack, and the permute of quantised rows) against the oracle, through the C
+ABI: codes, scales, source ids and untouched canary rows, bit for bit. Integer
+work, so the bar is bit-exact."""
 import sys
 
 import numpy as np
@@ -32,7 +32,7 @@ def _gpu():
     moe.lib()
 
 
-def run_gpu(hid, ids, E, R, align=1, block=0, cap_rank=None, cap_expert=None, spare=4):
+def run_gpu(hid, ids, E, R, bits=8, align=1, block=0, cap_rank=None, cap_expert=None, spare=4):
     T, H = hid.shape
     k = ids.shape[1]
     shape = moe.Shape(T, H, E, R, k, align, block)
@@ -46,18 +46,19 @@ def run_gpu(hid, ids, E, R, align=1, block=0, cap_rank=None, cap_expert=None, sp
     ws = moe.layout_workspace_bytes(shape)
     workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=i32, device=dev) if ws else None
     lay = moe.layout(ids_d, E, R, H, align=align, block=block, err=err, workspace=workspace)
-    rq = torch.full((cap_rank + spare, H), CANARY, dtype=u8, device=dev)
+    qw = H * bits // 8  # code bytes per row
+    rq = torch.full((cap_rank + spare, qw), CANARY, dtype=u8, device=dev)
     rs = torch.full((cap_rank + spare, H // 32), CANARY, dtype=u8, device=dev)
     rsrc = torch.full((cap_rank + spare,), CANARY_IDX, dtype=i32, device=dev)
-    eq = torch.full((cap_expert + spare, H), CANARY, dtype=u8, device=dev)
+    eq = torch.full((cap_expert + spare, qw), CANARY, dtype=u8, device=dev)
     es = torch.full((cap_expert + spare, H // 32), CANARY, dtype=u8, device=dev)
     esrc = torch.full((cap_expert + spare,), CANARY_IDX, dtype=i32, device=dev)
-    moe.pack_mxfp8(hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
-                   rsrc[:cap_rank], err=err)
-    moe.permute_mxfp8(rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"], ids_d,
-                      lay["pair_row"], E, eq[:cap_expert], es[:cap_expert], esrc[:cap_expert],
-                      expert_counts=lay["expert_counts"], expert_offsets=lay["expert_offsets"],
-                      align=align, block=block, err=err)
+    moe.pack_mx(bits, hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
+                rsrc[:cap_rank], err=err)
+    moe.permute_mx(bits, rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"],
+                   ids_d, lay["pair_row"], E, eq[:cap_expert], es[:cap_expert],
+                   esrc[:cap_expert], expert_counts=lay["expert_counts"],
+                   expert_offsets=lay["expert_offsets"], align=align, block=block, err=err)
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in lay.items()}
     out.update(rq=rq.cpu().numpy(), rs=rs.cpu().numpy(), rsrc=rsrc.cpu().numpy(),
@@ -66,15 +67,17 @@ def run_gpu(hid, ids, E, R, align=1, block=0, cap_rank=None, cap_expert=None, sp
     return out
 
 
-def check(hid, ids, E, R, what, align=1, block=0, **kw):
-    g = run_gpu(hid, ids, E, R, align, block, **kw)
+def check(hid, ids, E, R, what, bits=8, align=1, block=0, **kw):
+    g = run_gpu(hid, ids, E, R, bits, align, block, **kw)
     T, k = ids.shape
     lay = oracle.layout(ids, E, R, align=align, block=block)
     for key in ("token_rank_slot", "pair_row", "rank_offsets", "expert_offsets"):
         assert np.array_equal(g[key], lay[key]), f"{what}: layout {key}"
     cr, ce = g["cap_rank"], g["cap_expert"]
-    rq, rs, src, e1 = oracle.pack_mxfp8(hid, lay["token_rank_slot"], cr)
-    eq, es, esrc, e2 = oracle.permute_mxfp8(rq, rs, src, lay, ids, E, ce)
+    pack = oracle.pack_mxfp8 if bits == 8 else oracle.pack_mxfp4
+    permute = oracle.permute_mxfp8 if bits == 8 else oracle.permute_mxfp4
+    rq, rs, src, e1 = pack(hid, lay["token_rank_slot"], cr)
+    eq, es, esrc, e2 = permute(rq, rs, src, lay, ids, E, ce)
     assert g["err"] == lay["err"] | e1 | e2, f"{what}: error word {g['err']}"
     C = min(int(lay["rank_offsets"][-1]), cr)
     assert np.array_equal(g["rq"][:C], rq[:C]), f"{what}: packed codes"
@@ -92,17 +95,19 @@ def check(hid, ids, E, R, what, align=1, block=0, **kw):
     return lay
 
 
+@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
-def test_mxfp8_workload_parity(name):
+def test_mx_workload_parity(name, bits):
     w = synth.WORKLOADS[name]
-    say(f"[mxfp8] {w.describe()}")
+    say(f"[mxfp{bits}] {w.describe()}")
     hid = synth.hidden(w)
     ids, _ = synth.routing(w)
-    lay = check(hid, ids, w.E, w.R, name)
+    lay = check(hid, ids, w.E, w.R, name, bits=bits)
     assert lay["err"] == 0
 
 
-def test_mxfp8_every_bit_pattern():
+@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
+def test_mx_every_bit_pattern(bits):
     """Hidden rows of random 16-bit patterns: NaNs, infinities, subnormals,
     zeros of both signs and the whole exponent range, in every block."""
     T, H, E, R, k = 300, 1024, 32, 4, 3
@@ -111,7 +116,7 @@ def test_mxfp8_every_bit_pattern():
     hid[::7] &= 0x80FF  # some rows of tiny and subnormal values only
     hid[1::11, :64] = 0x7F80  # some blocks with an infinity
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
-    check(hid, ids, E, R, "bit patterns")
+    check(hid, ids, E, R, "bit patterns", bits=bits)
 
 
 EDGE = [
@@ -126,27 +131,30 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_R{c[3]}_k{c[4]}_a{c[5]}_b{c[6]}" for c in EDGE])
-def test_mxfp8_edge_shapes(case):
+def test_mx_edge_shapes(case, bits):
     T, H, E, R, k, align, block, seed = case
-    say(f"[mxfp8 edge] {case}")
+    say(f"[mxfp{bits} edge] {case}")
     rng = np.random.default_rng(seed)
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
     hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
-    check(hid, ids, E, R, f"edge {case}", align=align, block=block)
+    check(hid, ids, E, R, f"edge {case}", bits=bits, align=align, block=block)
 
 
-def test_mxfp8_undersized_buffers():
+@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
+def test_mx_undersized_buffers(bits):
     w = synth.WORKLOADS["tiny"]
     hid = synth.hidden(w)
     ids, _ = synth.routing(w)
     lay = oracle.layout(ids, w.E, w.R)
     C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
-    lay2 = check(hid, ids, w.E, w.R, "undersized", cap_rank=C - 37, cap_expert=P - 51, spare=64)
+    lay2 = check(hid, ids, w.E, w.R, "undersized", bits=bits, cap_rank=C - 37, cap_expert=P - 51,
+                 spare=64)
     assert lay2["err"] == 0
 
 
-def test_mxfp8_rejects_rows_not_a_multiple_of_512():
+def test_mx_rejects_rows_not_a_multiple_of_512():
     dev = torch.device("cuda:0")
     T, H, E, R, k = 4, 520, 8, 2, 2
     hid = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
@@ -156,3 +164,5 @@ def test_mxfp8_rejects_rows_not_a_multiple_of_512():
     src = torch.zeros(8, dtype=torch.int32, device=dev)
     with pytest.raises(moe.MoeError):
         moe.pack_mxfp8(hid, slots, E, k, rq, rs, src)
+    with pytest.raises(moe.MoeError):
+        moe.pack_mxfp4(hid, slots, E, k, rq[:, :H // 2], rs, src)
