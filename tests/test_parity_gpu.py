@@ -78,6 +78,9 @@ EDGE = [
     (70000, 16, 64, 8, 5, 0.05, 0.0, 12),    # > 64 tiles: several sub-tiles per workgroup
     (700, 256, 96, 1, 5, 0.0, 0.0, 10),      # one rank
     (513, 2880, 384, 8, 6, 0.0, 0.0, 11),    # 360 uint4 per row: 5 full groups + tail
+    (3000, 512, 64, 16, 4, 0.05, 0.0, 13),   # 8 < R <= 32: 32-bit rank masks, rank loops not unrolled
+    (30000, 128, 96, 32, 6, 0.0, 0.05, 14),  # R = 32, two-launch layout
+    (9000, 64, 128, 64, 5, 0.0, 0.0, 15),    # R = 64: 64-bit rank masks, two-launch layout
 ]
 
 
