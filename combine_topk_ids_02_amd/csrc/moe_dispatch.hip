@@ -88,8 +88,9 @@ __device__ __forceinline__ void store_row(vec4* p, vec4 v) {
 
 constexpr int kLayoutWaves = 16;                 // 1024 threads per workgroup
 constexpr int kLayoutThreads = kLayoutWaves * kWave;
-constexpr int kOwnTokens = 256;                  // tokens ranked per sub-tile (waves 0..3)
-constexpr int kOwnWaves = kOwnTokens / kWave;
+constexpr int kOwnTokens = 256;                  // tokens ranked per sub-tile
+constexpr int kOwnWaves = 8;                     // waves 0..7 rank ...
+constexpr int kTokW = kOwnTokens / kOwnWaves;    // ... 32 tokens each
 constexpr int kBatchVecs = 8;                    // 16-byte id loads per thread per batch
 constexpr size_t kLayoutLdsLimit = 160 * 1024 - 1024;  // gfx950: 160 KiB of LDS per workgroup
 
@@ -428,15 +429,18 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   scan_columns(s_pre, s_tot, g.E, g.R, g.align, g.block, s_tmp, blockIdx.x == 0, expert_counts,
                expert_offsets, rank_counts, rank_offsets);
 
-  // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..3. Wave w
-  //    owns tokens [64w, 64w+64) of the sub-tile, i.e. the contiguous pairs
-  //    [64wk, 64(w+1)k), and walks them 64 at a time in order. Lanes holding
-  //    the same expert find each other with one ballot per id bit; the lowest
-  //    of them adds the group's size to the wave's running count for that
-  //    expert with an LDS atomic that returns the old count. A wave's atomics
-  //    complete in issue order, so the counts are exact without waiting
-  //    between chunks.
+  // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..7. Wave w
+  //    owns tokens [32w, 32w+32) of the sub-tile, i.e. the contiguous pairs
+  //    [32wk, 32(w+1)k), and walks them 64 at a time in order (chunks). Lanes
+  //    holding the same expert find each other with one ballot per id bit;
+  //    the lowest of them adds the group's size to the wave's running count
+  //    for that expert with an LDS atomic that returns the old count. A
+  //    wave's atomics complete in issue order, so the counts are exact
+  //    without waiting between chunks; the waves' counts are then chained in
+  //    wave order per column.
   const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);
+  constexpr int KC = (kTokW * KR + kWave - 1) / kWave;  // chunks of 64 pairs per wave (bound)
+  const int nch = (kTokW * k + kWave - 1) / kWave;
   bool bad_id = false;
   bool full_block = false;  // a pair found its expert's fixed block full
   const bool ranker = wave < kOwnWaves;
@@ -455,24 +459,29 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
     __syncthreads();
 
-    int ex[KR], rk[KR];  // per chunk: this lane's expert (or -1) and its rank in the wave
-    Mask mask = 0;       // rank set of token tid of the sub-tile
+    int ex[KC], rk[KC];  // per chunk: this lane's expert (or -1) and its rank in the wave
+    Mask mask = 0;       // rank set of token ti (lanes < kTokW)
+    const int ti = wave * kTokW + lane;  // this lane's token in the sub-tile (lanes < kTokW)
+    const bool tok_lane = lane < kTokW && ti < nt;
     if (ranker) {
       // All of the wave's ids first (one LDS wait), then the matches, then the
       // running-count atomics in chunk order, then the leaders' old counts.
-      int own[KR];  // ids of token tid, for its rank set
+      int own[KR];  // ids of token ti, for its rank set
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch) {
-        if (ch < k) {
-          ex[ch] = s_pack[wave * kWave * k + ch * kWave + lane];
-          own[ch] = tid < nt ? s_pack[tid * k + ch] : -1;
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
+          const bool mine = ch * kWave + lane < kTokW * k;  // past it: the next wave's pairs
+          ex[ch] = mine ? s_pack[wave * kTokW * k + ch * kWave + lane] : -1;
         }
       }
-      int lead[KR], grp[KR];
-      uint64_t peers[KR];
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch) {
-        if (ch < k) {
+      for (int j = 0; j < KR; ++j)
+        if (j < k) own[j] = tok_lane ? s_pack[ti * k + j] : -1;
+      int lead[KC], grp[KC];
+      uint64_t peers[KC];
+#pragma unroll
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
           const bool valid = uint32_t(ex[ch]) < uint32_t(g.E);
           bad_id |= (ex[ch] != -1) && !valid;
           ex[ch] = valid ? ex[ch] : -1;
@@ -482,8 +491,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       // One ballot per id bit, all chunks side by side (independent chains).
       for (int b = 0; b < ebits; ++b) {
 #pragma unroll
-        for (int ch = 0; ch < KR; ++ch) {
-          if (ch < k) {
+        for (int ch = 0; ch < KC; ++ch) {
+          if (ch < nch) {
             const bool bit = (ex[ch] >> b) & 1;
             const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
             peers[ch] &= bit ? ones : ~ones;
@@ -491,24 +500,24 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
         }
       }
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch) {
-        if (ch < k) {
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
           rk[ch] = __popcll(peers[ch] & lanes_below());
           lead[ch] = ex[ch] >= 0 ? __ffsll((unsigned long long)peers[ch]) - 1 : lane;
           grp[ch] = __popcll(peers[ch]);
         }
       }
-      int cnt_old[KR];
+      int cnt_old[KC];
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch) {
-        if (ch < k) {
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
           cnt_old[ch] = 0;
           if (ex[ch] >= 0 && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[ex[ch]], grp[ch]);
         }
       }
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch)
-        if (ch < k) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
+      for (int ch = 0; ch < KC; ++ch)
+        if (ch < nch) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
 #pragma unroll
       for (int j = 0; j < KR; ++j)
         if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
@@ -532,10 +541,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 
     if (ranker) {
 #pragma unroll
-      for (int ch = 0; ch < KR; ++ch) {
-        if (ch < k) {
-          const int pl = wave * kWave * k + ch * kWave + lane;
-          if (pl < npairs) {
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
+          const int pl = wave * kTokW * k + ch * kWave + lane;
+          if (ch * kWave + lane < kTokW * k && pl < npairs) {
             int row = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
             if (g.block > 0 && row >= (ex[ch] + 1) * g.block) {
               row = -1;
@@ -547,8 +556,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       }
       auto write_slot = [&](int r) {
         const uint64_t on = __ballot((mask >> r) & 1);
-        if (tid < nt)
-          token_rank_slot[(int64_t)(t0 + tid) * g.R + r] =
+        if (tok_lane)
+          token_rank_slot[(int64_t)(t0 + ti) * g.R + r] =
               ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
       };
       if (kRB == 8) {
