@@ -792,66 +792,29 @@ __device__ __forceinline__ uint32_t e2m1x8(vec4 v, float scale) {
          (e2m1_pair(v[2], scale) << 16) | (e2m1_pair(v[3], scale) << 24);
 }
 
-// Quantises the 8 bf16 of `v` (one quarter of a 32-value block, the other
-// quarters in the neighbouring lanes of the same lane quad) and returns the
-// block's scale byte. kBits 8: 8 e4m3 codes in lo, hi (little-endian bytes);
-// kBits 4: 8 e2m1 codes in lo (hi unused).
-template <int kBits>
-__device__ __forceinline__ uint32_t mx_quantise(vec4 v, uint32_t& lo, uint32_t& hi) {
-  uint32_t amax = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    amax = max(amax, v[i] & 0x7FFFu);
-    amax = max(amax, (v[i] >> 16) & 0x7FFFu);
-  }
-  amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, kWave)));
-  amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
-  if (amax >= 0x7F80u) {  // NaN or infinity in the block: NaN scale, marked codes
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kBits == 8) {  // e4m3 NaN with the value's sign
-        c[2 * i] = ((v[i] >> 8) & 0x80u) | 0x7Fu;
-        c[2 * i + 1] = ((v[i] >> 24) & 0x80u) | 0x7Fu;
-      } else {  // the largest e2m1 code with the value's sign
-        c[2 * i] = ((v[i] >> 12) & 0x8u) | 0x7u;
-        c[2 * i + 1] = ((v[i] >> 28) & 0x8u) | 0x7u;
-      }
-    }
-    if (kBits == 8) {
-      lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    } else {
-      lo = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lo |= c[j] << (4 * j);
-      hi = 0;
-    }
-    return 0xFFu;
-  }
-  const int e = mx_block_exponent(amax, kBits == 8 ? 8 : 2);
-  const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // the E8M0 byte as a float exponent
-  if (kBits == 8) {
-    lo = e4m3x4(v[0], v[1], scale);
-    hi = e4m3x4(v[2], v[3], scale);
-  } else {
-    lo = e2m1x8(v, scale);
-    hi = 0;
-  }
-  return uint32_t(e + 127);
-}
-
 // Fused quantise-and-pack: one wave per token, the row read once and
 // quantised once in registers, then written (codes and scales) to every rank
-// in the token's set. Passes of V groups of 64 vec4, V dividing the row's
-// group count (H is a multiple of 512). Codes and scales are stored with
-// ordinary stores, like the bf16 copies, for the permute to find in cache.
-// kBits 8: MXFP8, 8 code bytes per vec4 of input; 4: MXFP4, 4 code bytes.
-template <int V, int kBits>
+// in the token's set. Each lane takes NL consecutive vec4 of the row per pass
+// and produces NL * kBits bytes of codes (one store); a 32-value block is
+// 4/NL lanes (its maximum one or two lane-xors away, or in-lane). Measured:
+// MXFP8 is fastest with NL = 2 (16-byte stores), MXFP4 with NL = 1 (fully
+// coalesced loads; wider lanes made its loads stride). Passes cover 64 * NL
+// vec4; the last one may be partial (H is a multiple of 512, so whole blocks
+// and lane groups). NP passes are held in registers at once, NP dividing the
+// pass count. Codes and scales are stored with ordinary stores, like the bf16
+// copies, for the permute to find in cache.
+template <int kBits> struct MxLane { static constexpr int NL = 2; };
+template <> struct MxLane<4> { static constexpr int NL = 1; };
+
+template <int NP, int kBits>
 __global__ __launch_bounds__(kBlock) void pack_rows_mx(
     const vec4* hidden, const int32_t* __restrict__ token_rank_slot, uint8_t* rank_q,
     uint8_t* rank_scale, int32_t* __restrict__ rank_src_token, int T, int R, int nvec,
     int64_t cap_rank, int32_t* err_word) {
+  constexpr int NL = MxLane<kBits>::NL;  // vec4 per lane per pass
+  constexpr int NB = NL * kBits;      // code bytes per lane per pass
+  constexpr int LPB = 4 / NL;         // lanes per 32-value block
+  constexpr int kEmax = kBits == 8 ? 8 : 2;
   const int lane = lane_id();
   const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
@@ -861,21 +824,83 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
   if (ok) rank_src_token[slot] = t;
   const uint64_t dests = __ballot(ok);
   if (!dests) return;
-  const int64_t qrow = (int64_t)nvec * kBits;  // bytes of codes per row (H or H/2)
-  const int64_t srow = nvec / 4;           // scale bytes per row (H / 32)
+  const int64_t qrow = (int64_t)nvec * kBits;  // code bytes per row (H or H/2)
+  const int64_t srow = nvec / 4;               // scale bytes per row (H / 32)
+  const int npass = (nvec + kWave * NL - 1) / (kWave * NL);
   const vec4* src = hidden + (int64_t)t * nvec;
-  for (int c0 = 0; c0 < nvec; c0 += kWave * V) {
-    vec4 v[V];
+  for (int p0 = 0; p0 < npass; p0 += NP) {
+    vec4 v[NP][NL];
 #pragma unroll
-    for (int q = 0; q < V; ++q) v[q] = load_row<true>(src + c0 + q * kWave + lane);
-    uint32_t lo[V], hi[V], sw[V];
+    for (int q = 0; q < NP; ++q) {
+      const int col = (p0 + q) * kWave * NL + NL * lane;
+      const bool act = NL == 1 || col < nvec;
 #pragma unroll
-    for (int q = 0; q < V; ++q) {
-      const uint32_t sb = mx_quantise<kBits>(v[q], lo[q], hi[q]);
-      // lanes 16w collect the scale bytes of blocks 4w..4w+3 (lanes 16w, +4, +8, +12)
-      sw[q] = sb | (uint32_t(__shfl(int(sb), lane + 4, kWave)) << 8) |
-              (uint32_t(__shfl(int(sb), lane + 8, kWave)) << 16) |
-              (uint32_t(__shfl(int(sb), lane + 12, kWave)) << 24);
+      for (int i = 0; i < NL; ++i) {
+        if (act) {
+          v[q][i] = load_row<true>(src + col + i);
+        } else {
+          v[q][i] = vec4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    vec4 code[NP];
+    uint32_t sw[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          amax = max(amax, v[q][i][j] & 0x7FFFu);
+          amax = max(amax, (v[q][i][j] >> 16) & 0x7FFFu);
+        }
+      if (LPB >= 2) amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, kWave)));
+      if (LPB >= 4) amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
+      uint32_t sb;
+      if (amax >= 0x7F80u) {  // NaN or infinity in the block: NaN scale, marked codes
+        sb = 0xFFu;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          uint32_t c[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (kBits == 8) {  // e4m3 NaN with the value's sign
+              c[2 * j] = ((v[q][i][j] >> 8) & 0x80u) | 0x7Fu;
+              c[2 * j + 1] = ((v[q][i][j] >> 24) & 0x80u) | 0x7Fu;
+            } else {  // the largest e2m1 code with the value's sign
+              c[2 * j] = ((v[q][i][j] >> 12) & 0x8u) | 0x7u;
+              c[2 * j + 1] = ((v[q][i][j] >> 28) & 0x8u) | 0x7u;
+            }
+          }
+          if (kBits == 8) {
+            code[q][2 * i] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+            code[q][2 * i + 1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+          } else {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w |= c[j] << (4 * j);
+            code[q][i] = w;
+          }
+        }
+      } else {
+        const int e = mx_block_exponent(amax, kEmax);
+        const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // E8M0 byte as an exponent
+        sb = uint32_t(e + 127);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          if (kBits == 8) {
+            code[q][2 * i] = e4m3x4(v[q][i][0], v[q][i][1], scale);
+            code[q][2 * i + 1] = e4m3x4(v[q][i][2], v[q][i][3], scale);
+          } else {
+            code[q][i] = e2m1x8(v[q][i], scale);
+          }
+        }
+      }
+      // lanes 4*LPB*w collect the scale bytes of blocks 4w..4w+3
+      sw[q] = sb | (uint32_t(__shfl(int(sb), lane + LPB, kWave)) << 8) |
+              (uint32_t(__shfl(int(sb), lane + 2 * LPB, kWave)) << 16) |
+              (uint32_t(__shfl(int(sb), lane + 3 * LPB, kWave)) << 24);
     }
     uint64_t d = dests;
     while (d) {
@@ -885,17 +910,22 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
       uint8_t* qdst = rank_q + row * qrow;
       uint8_t* sdst = rank_scale + row * srow;
 #pragma unroll
-      for (int q = 0; q < V; ++q) {
-        const int col = c0 + q * kWave + lane;
-        if (kBits == 8) {
-          uint2 w;
-          w.x = lo[q];
-          w.y = hi[q];
-          *reinterpret_cast<uint2*>(qdst + (int64_t)col * 8) = w;
-        } else {
-          *reinterpret_cast<uint32_t*>(qdst + (int64_t)col * 4) = lo[q];
+      for (int q = 0; q < NP; ++q) {
+        const int col = (p0 + q) * kWave * NL + NL * lane;
+        if (NL == 1 || col < nvec) {
+          uint8_t* at = qdst + (int64_t)col * kBits;
+          if (NB == 16) {
+            *reinterpret_cast<vec4*>(at) = code[q];
+          } else if (NB == 8) {
+            uint2 w;
+            w.x = code[q][0];
+            w.y = code[q][1];
+            *reinterpret_cast<uint2*>(at) = w;
+          } else {
+            *reinterpret_cast<uint32_t*>(at) = code[q][0];
+          }
+          if (lane % (4 * LPB) == 0) *reinterpret_cast<uint32_t*>(sdst + col / 4) = sw[q];
         }
-        if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sdst + col / 4) = sw[q];
       }
     }
   }
@@ -1143,14 +1173,6 @@ int copy_vec(int nvec) {
   return kMaxVec;
 }
 
-// MXFP8 pack: passes of V groups of 64 vec4, V the largest divisor of the
-// group count that is at most 16 (so every pass is whole).
-int mx_vec(int groups) {
-  for (int v = std::min(groups, kMaxVec); v > 1; --v)
-    if (groups % v == 0) return v;
-  return 1;
-}
-
 // Combine: slices of at most 8 groups (8 x 8 fp32 accumulators per lane),
 // as few slices as cover the row.
 void combine_tiling(int nvec, int* v, int* slices) {
@@ -1206,19 +1228,6 @@ struct PermuteLaunch {
   }
 };
 
-template <int V>
-struct PackMxLaunch {
-  static void go(int bits, dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots,
-                 uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R, int nvec, int64_t cap,
-                 int32_t* err) {
-    if (bits == 8)
-      hipLaunchKernelGGL((pack_rows_mx<V, 8>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src,
-                         T, R, nvec, cap, err);
-    else
-      hipLaunchKernelGGL((pack_rows_mx<V, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs, src,
-                         T, R, nvec, cap, err);
-  }
-};
 
 template <int V>
 struct CombineLaunch {
@@ -1284,6 +1293,29 @@ int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_
   return launch_status();
 }
 
+// MX pack: NP passes in registers, the largest divisor of the pass count
+// that is at most `most` (so every register batch is whole).
+int mx_passes(int npass, int most) {
+  for (int v = std::min(npass, most); v > 1; --v)
+    if (npass % v == 0) return v;
+  return 1;
+}
+
+template <int NP>
+struct PackMxLaunch {
+  static void go(int bits, dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots,
+                 uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R, int nvec, int64_t cap,
+                 int32_t* err) {
+    if (bits == 4) {
+      hipLaunchKernelGGL((pack_rows_mx<NP, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
+                         src, T, R, nvec, cap, err);
+    } else if constexpr (NP * MxLane<8>::NL <= kMaxVec) {
+      hipLaunchKernelGGL((pack_rows_mx<NP, 8>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
+                         src, T, R, nvec, cap, err);
+    }
+  }
+};
+
 int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
                  const int32_t* token_rank_slot, uint8_t* rank_q, uint8_t* rank_scale,
                  int32_t* rank_src_token, int64_t cap_rank, int32_t* err_word, void* stream) {
@@ -1293,7 +1325,9 @@ int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
     return MOE_ERR_ARG;
   if (!aligned16(hidden) || !aligned16(rank_q) || !aligned16(rank_scale)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
-  ByVec<PackMxLaunch>::run(mx_vec(nvec / kWave), bits, dim3(blocks_for(shape->T)),
+  const int nl = bits == 8 ? MxLane<8>::NL : MxLane<4>::NL;
+  const int npass = (nvec + kWave * nl - 1) / (kWave * nl);
+  ByVec<PackMxLaunch>::run(mx_passes(npass, kMaxVec / nl), bits, dim3(blocks_for(shape->T)),
                            static_cast<hipStream_t>(stream),
                            reinterpret_cast<const vec4*>(hidden), token_rank_slot, rank_q,
                            rank_scale, rank_src_token, shape->T, shape->R, nvec, cap_rank,
