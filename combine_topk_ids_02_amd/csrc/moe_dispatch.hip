@@ -91,8 +91,8 @@ constexpr int kLayoutThreads = kLayoutWaves * kWave;
 constexpr int kOwnTokens = 256;                  // tokens ranked per sub-tile
 constexpr int kOwnWaves = 8;                     // waves 0..7 rank ...
 constexpr int kTokW = kOwnTokens / kOwnWaves;    // ... 32 tokens each
-constexpr int kBatchVecs = 8;                    // 16-byte id loads per thread per batch
-constexpr size_t kLayoutLdsLimit = 160 * 1024 - 1024;  // gfx950: 160 KiB of LDS per workgroup
+constexpr int kBatchVecs = 8;                    // 16-byte id loads per lane per batch
+constexpr size_t kLayoutLdsLimit = 64 * 1024 - 256;  // dynamic LDS without a launch attribute
 
 // Which form of the layout runs when a workspace is given: -1 by size (the
 // default), 0 every workgroup counts all ids, 1 two launches through tile
@@ -103,7 +103,6 @@ struct LayoutGeom {
   int T, E, R, k, m;    // m = experts per rank
   int align, block;     // expert runs padded to multiples of align; or fixed blocks (block > 0)
   int ncols;            // E expert columns followed by R rank columns
-  int batch_tokens;     // tokens whose ids are staged in LDS at once (multiple of 1024)
   int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
   int ntiles;
   int tiles_pad;        // ntiles rounded up to a multiple of 4 (tile-count column stride)
@@ -222,22 +221,50 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
   __syncthreads();
 }
 
-// Loads ids [f0, f0 + 4*nvec) flat, 16 bytes per lane: slot q of thread i
-// holds ids f0 + 4*(q*1024 + i) .. +3 (past n_ids: -1).
-__device__ __forceinline__ void load_batch(const int32_t* __restrict__ ids, int64_t n_ids,
-                                           int64_t f0, int nvec, vec4 (&r)[kBatchVecs]) {
+// Whole tokens per lane for the counting pass: each lane takes TPL tokens
+// (K * TPL ids, a multiple of 4, so 16-byte aligned loads) per pass and NQ
+// passes per batch (at most kBatchVecs loads per lane). A wave's tokens are
+// 64 * TPL consecutive ones, at most 256, so they never straddle a tile start
+// (a multiple of 256). K = 0 (k known only at run time): one token per lane,
+// its ids loaded one by one.
+template <int K>
+struct IdLanes {
+  static constexpr int TPL = K == 0 ? 1 : (K % 4 == 0 ? 1 : (K % 2 == 0 ? 2 : 4));
+  static constexpr int VPL = K == 0 ? 0 : K * TPL / 4;  // 16-byte loads per lane per pass
+  static constexpr int NQ = K == 0 ? 1 : (kBatchVecs / VPL > 0 ? kBatchVecs / VPL : 1);
+  static constexpr int NW = K == 0 ? kMaxK : NQ * VPL * 4;  // ids held per lane
+  static constexpr int BATCH = kLayoutThreads * TPL * NQ;  // tokens per batch
+};
+
+// Ids of this lane's tokens of the batch starting at token b0 (-1 past T):
+// pass q, token u of the lane holds w[q * VPL * 4 + u * K + j].
+template <int K>
+__device__ __forceinline__ void load_tokens(const int32_t* __restrict__ ids, int T, int k, int b0,
+                                            int32_t (&w)[IdLanes<K>::NW]) {
+  using L = IdLanes<K>;
+  const int64_t n_ids = (int64_t)T * k;
+  if (K > 0) {
 #pragma unroll
-  for (int q = 0; q < kBatchVecs; ++q) {
-    const int v = q * kLayoutThreads + threadIdx.x;
-    if (v < nvec) {
-      const int64_t f = f0 + 4 * int64_t(v);
-      if (f + 4 <= n_ids) {
-        r[q] = *reinterpret_cast<const vec4*>(ids + f);
-      } else {
+    for (int q = 0; q < L::NQ; ++q) {
+      const int64_t f0 = (b0 + int64_t(q * kLayoutThreads + threadIdx.x) * L::TPL) * K;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) r[q][x] = f + x < n_ids ? uint32_t(ids[f + x]) : ~0u;
+      for (int i = 0; i < L::VPL; ++i) {
+        const int64_t f = f0 + 4 * i;
+        int32_t* d = w + (q * L::VPL + i) * 4;
+        if (f + 4 <= n_ids) {
+          const vec4 v = *reinterpret_cast<const vec4*>(ids + f);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) d[x] = int32_t(v[x]);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) d[x] = f + x < n_ids ? ids[f + x] : -1;
+        }
       }
     }
+  } else {
+    const int t = b0 + int(threadIdx.x);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) w[j] = (j < k && t < T) ? ids[(int64_t)t * k + j] : -1;
   }
 }
 
@@ -310,9 +337,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   using Mask = typename RankMask<kRB>::type;
   const int k = K > 0 ? K : g.k;
   extern __shared__ int32_t smem[];
-  int32_t* s_ids = smem;                          // [batch_tokens * k] staged ids
-  // [kOwnTokens * k] own sub-tile ids (no staged batch with kFromHist)
-  int32_t* s_pack = s_ids + (kFromHist ? 0 : g.batch_tokens * k) + 4;
+  int32_t* s_pack = smem;                         // [kOwnTokens * k] own sub-tile ids
   int32_t* s_cnt = s_pack + kOwnTokens * k;       // [kOwnWaves][ncols] per-wave counts
   int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols + 1] before the tile -> running base
   int32_t* s_tot = s_pre + g.ncols + 1;           // [ncols + 1] other tokens -> totals -> offsets
@@ -322,19 +347,27 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = lane_id();
-  const int64_t n_ids = (int64_t)g.T * k;
   const int tile_lo = blockIdx.x * g.tile_tokens;
   const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
-  // own ids captured from the staged batch (only when the batch loop runs)
+  // own ids captured by the counting pass (only when it runs)
   const bool one_sub = !kFromHist && g.tile_tokens == kOwnTokens;
+
+  // The first batch of ids for the counting pass is requested before the
+  // LDS is cleared.
+  int32_t nxt[IdLanes<K>::NW];
+  if (!kFromHist) load_tokens<K>(ids, g.T, k, 0, nxt);
 
   for (int c = tid; c < g.ncols; c += kLayoutThreads) {
     s_pre[c] = 0;
     s_tot[c] = 0;
   }
   // The per-wave running counts of the first sub-tile start at zero (cleared
-  // here, under the id loads, rather than after the scan).
+  // here, while the ids load, rather than after the scan).
   for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
+  // Own ids past the last token read as -1 (the counting pass writes the rest).
+  if (one_sub)
+    for (int f = (tile_hi - tile_lo) * k + tid; f < kOwnTokens * k; f += kLayoutThreads)
+      s_pack[f] = -1;
 
   if (kFromHist) {
     // 1'. Counts before the tile and from it on, per column, from the tile
@@ -367,53 +400,44 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     }
     __syncthreads();
   } else {
-    // 1. Histogram of every token, a batch of tokens at a time: all of a
-    //    batch's ids are requested at once (16 bytes per lane, coalesced) and
-    //    staged in LDS, the next batch's loads in flight while this one is
-    //    counted. Experts: one LDS atomic per pair. Ranks: one ballot per rank
-    //    per 64 tokens (a wave's 64 tokens sit on one side of the tile start).
-    const int batch_ids = g.batch_tokens * k;
+    // 1. Histogram of every token, straight from registers: a batch of
+    //    whole tokens per lane is loaded (16 bytes per load, coalesced) while
+    //    the previous one is counted. Experts: one LDS atomic per pair. Ranks:
+    //    one ballot per rank per 64 tokens (a wave's tokens sit on one side of
+    //    the tile start). The tile's own ids go to s_pack on the way.
+    using L = IdLanes<K>;
     int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
-    vec4 nxt[kBatchVecs];
-    load_batch(ids, n_ids, 0, (int)((std::min<int64_t>(batch_ids, n_ids) + 3) / 4), nxt);
-    for (int b0 = 0; b0 < g.T; b0 += g.batch_tokens) {
-      const int nb = min(g.batch_tokens, g.T - b0);
-      const int nvec = (nb * k + 3) / 4;
-      __syncthreads();  // s_ids free; s_pre/s_tot zeroed
+    __syncthreads();  // s_pre / s_tot zeroed
+    for (int b0 = 0; b0 < g.T; b0 += L::BATCH) {
+      int32_t cur[L::NW];
 #pragma unroll
-      for (int q = 0; q < kBatchVecs; ++q) {
-        const int v = q * kLayoutThreads + tid;
-        if (v < nvec) *reinterpret_cast<vec4*>(s_ids + 4 * v) = nxt[q];
-      }
-      const int b1 = b0 + g.batch_tokens;
-      if (b1 < g.T) {
-        const int nn = min(g.batch_tokens, g.T - b1);
-        load_batch(ids, n_ids, (int64_t)b1 * k, (nn * k + 3) / 4, nxt);
-      }
-      __syncthreads();
-      if (one_sub && b0 <= tile_lo && tile_lo < b0 + nb) {
-        const int base = (tile_lo - b0) * k;
-        const int n_own = min(kOwnTokens, tile_hi - tile_lo) * k;
-        for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads)
-          s_pack[f] = f < n_own ? s_ids[base + f] : -1;
-      }
-      for (int tl = tid; tl < ((nb + kWave - 1) & ~(kWave - 1)); tl += kLayoutThreads) {
-        const bool early = b0 + (tl & ~(kWave - 1)) < tile_lo;  // the same for the whole wave
+      for (int x = 0; x < L::NW; ++x) cur[x] = nxt[x];
+      if (b0 + L::BATCH < g.T) load_tokens<K>(ids, g.T, k, b0 + L::BATCH, nxt);
+#pragma unroll
+      for (int q = 0; q < L::NQ; ++q) {
+        const int tq = b0 + (q * kLayoutThreads + tid) * L::TPL;   // this lane's first token
+        const int tw = b0 + (q * kLayoutThreads + wave * kWave) * L::TPL;  // the wave's first
+        if (tw >= g.T) continue;  // a wave past the last token counts nothing
+        const bool early = tw < tile_lo;
         int32_t* cnt = early ? s_pre : s_tot;
-        int ev[KR];
+        int c = 0;
 #pragma unroll
-        for (int j = 0; j < KR; ++j)
-          if (j < k) ev[j] = tl < nb ? s_ids[tl * k + j] : -1;
-        Mask mask = 0;
+        for (int u = 0; u < L::TPL; ++u) {
+          const int32_t* ev = cur + q * L::VPL * 4 + u * K;
+          const int t = tq + u;
+          const bool own = one_sub && t >= tile_lo && t < tile_hi;
+          Mask mask = 0;
 #pragma unroll
-        for (int j = 0; j < KR; ++j) {
-          if (j < k) {
-            const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
-            atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
-            mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+          for (int j = 0; j < KR; ++j) {
+            if (j < k) {
+              const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
+              atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
+              mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+              if (own) s_pack[(t - tile_lo) * k + j] = ev[j];
+            }
           }
+          c += wave_rank_counts<kRB>(mask, g.R);
         }
-        const int c = wave_rank_counts<kRB>(mask, g.R);
         (early ? rc_pre : rc_tot) += c;
       }
     }
@@ -573,11 +597,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   if (__ballot(full_block) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
 }
 
-size_t layout_lds_bytes(int batch_tokens, int k, int ncols) {
-  // the staged ids get 4 ints of slack: a batch's last 16-byte load may run past its ids
-  return sizeof(int32_t) * (size_t(batch_tokens) * k + 4 + size_t(kOwnTokens) * k +
-                            size_t(kOwnWaves + 2) * ncols + 2);
+constexpr size_t layout_lds_bytes(int k, int ncols) {
+  return sizeof(int32_t) * (size_t(kOwnTokens) * k + size_t(kOwnWaves + 2) * ncols + 2);
 }
+static_assert(layout_lds_bytes(kMaxK, kMaxExperts + kMaxRanks) <= kLayoutLdsLimit,
+              "the layout's LDS fits every shape");
 
 LayoutGeom layout_geometry(const moe_shape_t& sh) {
   LayoutGeom g;
@@ -590,12 +614,6 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   g.block = sh.block;
   g.ncols = sh.E + sh.R;
   g.inv_m = float(1.0 / double(g.m));
-  // Largest batch (multiple of 1024 tokens) that the loads and LDS hold.
-  const int t_round = std::max(1, (sh.T + kLayoutThreads - 1) / kLayoutThreads) * kLayoutThreads;
-  g.batch_tokens = std::min(t_round, kLayoutThreads * std::max(1, (4 * kBatchVecs) / sh.k));
-  while (g.batch_tokens > kLayoutThreads &&
-         layout_lds_bytes(g.batch_tokens, g.k, g.ncols) > kLayoutLdsLimit)
-    g.batch_tokens -= kLayoutThreads;
   const int64_t subs = (int64_t(sh.T) + kOwnTokens - 1) / kOwnTokens;
   const int64_t per_tile = std::max<int64_t>(1, (subs + kMaxTiles - 1) / kMaxTiles);
   g.tile_tokens = int(per_tile * kOwnTokens);
@@ -612,25 +630,15 @@ struct LayoutArgs {
 
 template <int K, int kRB>
 void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
-  // Allow these instantiations the LDS they may need (above the 64 KiB
-  // default); set once per process, the only thing the library ever caches.
-  static const hipError_t attr0 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K, kRB, false>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
-  static const hipError_t attr1 = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&layout_tiles<K, kRB, true>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(kLayoutLdsLimit));
-  (void)attr0;
-  (void)attr1;
   if (a.hist) {
     hipLaunchKernelGGL((layout_count<K, kRB>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
                        a.ids, a.hist);
     hipLaunchKernelGGL((layout_tiles<K, kRB, true>), dim3(g.ntiles), dim3(kLayoutThreads),
-                       layout_lds_bytes(0, g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
+                       layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
                        a.eo, a.trs, a.pr, a.err);
   } else {
     hipLaunchKernelGGL((layout_tiles<K, kRB, false>), dim3(g.ntiles), dim3(kLayoutThreads),
-                       layout_lds_bytes(g.batch_tokens, g.k, g.ncols), st, g, a.ids, a.hist,
+                       layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist,
                        a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.err);
   }
 }
@@ -1153,7 +1161,7 @@ bool shape_ok(const moe_shape_t* s) {
   if (int64_t(s->T) * s->k + int64_t(s->E) * (s->align - 1) >= (int64_t(1) << 31)) return false;
   if (int64_t(s->T) * s->k >= (int64_t(1) << 30)) return false;
   if (int64_t(s->T) * s->R >= (int64_t(1) << 31)) return false;
-  if (layout_lds_bytes(kLayoutThreads, s->k, s->E + s->R) > kLayoutLdsLimit) return false;
+  if (layout_lds_bytes(s->k, s->E + s->R) > kLayoutLdsLimit) return false;
   return true;
 }
 
