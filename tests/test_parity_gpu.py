@@ -81,6 +81,9 @@ EDGE = [
     (3000, 512, 64, 16, 4, 0.05, 0.0, 13),   # 8 < R <= 32: 32-bit rank masks, rank loops not unrolled
     (30000, 128, 96, 32, 6, 0.0, 0.05, 14),  # R = 32, two-launch layout
     (9000, 64, 128, 64, 5, 0.0, 0.0, 15),    # R = 64: 64-bit rank masks, two-launch layout
+    (5001, 512, 96, 8, 3, 0.05, 0.0, 16),    # k = 3: four whole tokens per lane when counting
+    (3001, 256, 64, 8, 7, 0.0, 0.05, 17),    # k = 7: k known only at run time
+    (4099, 128, 32, 4, 1, 0.05, 0.0, 18),    # top-1, ragged
 ]
 
 
@@ -163,6 +166,8 @@ NO_WORKSPACE = [
     # the one-launch layout (no workspace): every workgroup counts all ids
     ("prefill", None), ("adv", None), (None, (70000, 16, 64, 8, 5, 0.05, 0.0, 12)),
     (None, (2000, 64, 1024, 64, 16, 0.02, 0.02, 9)), (None, (257, 512, 16, 4, 2, 0.1, 0.0, 4)),
+    # several counting batches: run-time k (1024 tokens a batch), top-1 (32768 a batch)
+    (None, (2600, 128, 128, 8, 10, 0.0, 0.0, 20)), (None, (40000, 16, 32, 4, 1, 0.05, 0.0, 21)),
 ]
 
 
