@@ -13,7 +13,9 @@ stream it runs on, and the CPU oracle timed on a bounded sample of the same
 workload.
 
 --sweep measures every workload per call, warm (back to back) and cold (a
-1 GiB write evicts L2 and the Infinity Cache before each call): 5 warm-up
+1 GiB read evicts L2 and the Infinity Cache before each call; a read, not a
+write, so that no dirty lines of its own are written back inside the timed
+call): 5 warm-up
 steps, then the median of 30 calls, repeated 3 times; next to it a plain 1 GiB
 device copy as the achievable rate, and the oracle pinned to one core (median
 of 5 steps, 3 for the two large workloads).
@@ -312,36 +314,36 @@ class Rig:
         else:
             moe.combine_ranks(self.partial, b.token_rank_slot, s.E, s.k, self.out2, err=b.err)
 
-    def step(self, ev=None, flush=None) -> None:
+    def step(self, ev=None, evict=None) -> None:
         """One pass; with `ev` (5 events) records between the calls; with
-        `flush` (a large tensor) overwrites it before every call, outside the
-        events."""
+        `evict` (a callable that enqueues a cache-evicting read) runs it
+        before every call, outside the events."""
         for i, c in enumerate(self.calls):
-            if flush is not None:
-                flush.fill_(i + 1)
+            if evict is not None:
+                evict()
             if ev is not None:
-                ev[2 * i if flush is not None else i].record(self.stream)
+                ev[2 * i if evict is not None else i].record(self.stream)
             self.call(c)
-            if ev is not None and flush is not None:
+            if ev is not None and evict is not None:
                 ev[2 * i + 1].record(self.stream)
-        if ev is not None and flush is None:
+        if ev is not None and evict is None:
             ev[len(self.calls)].record(self.stream)
 
-    def per_call_ms(self, n: int, flush=None) -> dict:
+    def per_call_ms(self, n: int, evict=None) -> dict:
         """Per-call durations (ms) over n steps."""
         import torch
 
         nc = len(self.calls)
-        nev = 2 * nc if flush is not None else nc + 1
+        nev = 2 * nc if evict is not None else nc + 1
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
-            self.step(evs[i], flush)
+            self.step(evs[i], evict)
         torch.cuda.synchronize()
         out = {c: [] for c in self.calls}
         for ev in evs:
             for j, c in enumerate(self.calls):
-                a, b = (ev[2 * j], ev[2 * j + 1]) if flush is not None else (ev[j], ev[j + 1])
+                a, b = (ev[2 * j], ev[2 * j + 1]) if evict is not None else (ev[j], ev[j + 1])
                 out[c].append(a.elapsed_time(b))
         return out
 
@@ -403,7 +405,14 @@ def sweep(names, dev, with_oracle: bool) -> None:
 
     import synth
 
-    flush = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    # Cold calls: a 1 GiB read (a sum into a preallocated scalar) before each
+    # call replaces L2 and the 256 MB Infinity Cache with clean lines.
+    flush = torch.ones(2 ** 30, dtype=torch.uint8, device=dev)
+    acc = torch.zeros((), dtype=torch.int32, device=dev)
+
+    def evict() -> None:
+        torch.sum(flush, dim=0, dtype=torch.int32, out=acc)
+
     copy = copy_reference(dev)
     log(f"1 GiB device copy: {copy['GB/s']} GB/s")
     print(json.dumps({"copy_1GiB": copy}), flush=True)
@@ -423,7 +432,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
                "dispatch_format": f"mxfp{mx}" if mx else "bf16",
                "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
                "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
-        for mode, fl in (("warm", None), ("cold", flush)):
+        for mode, fl in (("warm", None), ("cold", evict)):
             meds = {c: [] for c in rig.calls}
             for _ in range(3):
                 ms = rig.per_call_ms(30, fl)
