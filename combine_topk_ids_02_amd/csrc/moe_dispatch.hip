@@ -678,14 +678,38 @@ size_t layout_workspace_bytes(const LayoutGeom& g) {
 // in flight before the first store. Columns past the last full pass (H not a
 // multiple of 512*V) go one vec4 per lane at a time.
 
+// The first pass of a row (columns [0, 64*V)) into registers: callers issue
+// it right behind the loads of the indices that say where the row goes, so
+// that the latencies overlap. The loads are unconditional (a row shorter than
+// one pass reads its last column instead, and fan_out_row does not use them),
+// which keeps the code straight so that the indices can be waited for alone.
+template <int V, bool kStreamLoad>
+__device__ __forceinline__ void load_first_pass(const vec4* src, int nvec, vec4 (&first)[V]) {
+#pragma unroll
+  for (int q = 0; q < V; ++q)
+    first[q] = load_row<kStreamLoad>(src + min(q * kWave + lane_id(), nvec - 1));
+}
+
 // Copies the row at `src` to every row dst_row(d), d in the lane mask `dests`,
 // dst_row(d) = readlane(row_of_lane, d), loading and storing with the given
-// cache policies.
+// cache policies; `first` holds the row's first pass (load_first_pass).
 template <int V, bool kStreamLoad, bool kStreamStore>
-__device__ __forceinline__ void fan_out_row(const vec4* src, vec4* dst_base, int row_of_lane,
-                                            uint64_t dests, int nvec) {
+__device__ __forceinline__ void fan_out_row(const vec4 (&first)[V], const vec4* src,
+                                            vec4* dst_base, int row_of_lane, uint64_t dests,
+                                            int nvec) {
   const int lane = lane_id();
   int c0 = 0;
+  if (kWave * V <= nvec) {
+    uint64_t d = dests;
+    while (d) {
+      const int which = __ffsll((unsigned long long)d) - 1;
+      d &= d - 1;
+      vec4* dst = dst_base + (int64_t)read_lane(row_of_lane, which) * nvec + lane;
+#pragma unroll
+      for (int q = 0; q < V; ++q) store_row<kStreamStore>(dst + q * kWave, first[q]);
+    }
+    c0 = kWave * V;
+  }
   for (; c0 + kWave * V <= nvec; c0 += kWave * V) {
     vec4 v[V];
 #pragma unroll
@@ -720,14 +744,20 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
   const int lane = lane_id();
   const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  const int slot = lane < R ? token_rank_slot[(int64_t)t * R + lane] : -1;
+  // The hidden row is read once (streamed), its first pass requested right
+  // behind the token's slots (loads return in order, so the slots can be
+  // used while the row is still arriving); the copies are stored with
+  // ordinary stores so that they stay in the Infinity Cache for the permute.
+  const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
+  const int slot = lane < R ? slot_any : -1;
+  const vec4* src = hidden + (int64_t)t * nvec;
+  vec4 first[V];
+  load_first_pass<V, true>(src, nvec, first);
   const bool ok = slot >= 0 && slot < cap_rank;
   if (__ballot(slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
   if (ok) rank_src_token[slot] = t;
   const uint64_t dests = __ballot(ok);
-  // The hidden row is read once (streamed); the copies are stored with
-  // ordinary stores so that they stay in the Infinity Cache for the permute.
-  if (dests) fan_out_row<V, true, false>(hidden + (int64_t)t * nvec, rank_buf, slot, dests, nvec);
+  if (dests) fan_out_row<V, true, false>(first, src, rank_buf, slot, dests, nvec);
 }
 
 // Marks the padding rows of expert e (rows of its run or block that no pair
@@ -956,26 +986,39 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
     mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
     return;
   }
-  const int64_t i = gw - pad_waves;
+  const int64_t i = gw - pad_waves;  // < cap_rank: rank_src_token[i] is in bounds
+  // Two rounds of loads: the offsets and the row's token, then the token's
+  // ids and pair rows with the row itself right behind them.
   const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
-  if (i >= rows) return;
-  // segment of row i: number of segment ends at or below i
-  const int end = lane < R ? rank_offsets[lane + 1] : 0x7FFFFFFF;
-  const int r = __popcll(__ballot(lane < R && end <= i));
+  const int end_any = rank_offsets[min(lane, R - 1) + 1];
   const int t = rank_src_token[i];
-  if (t < 0 || t >= T) return;
-  const int e = lane < k ? ids[(int64_t)t * k + lane] : -1;
+  const int end = lane < R ? end_any : 0x7FFFFFFF;
+  if (i >= rows || t < 0 || t >= T) return;
+  const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
+  const int pr_any = pair_row[(int64_t)t * k + min(lane, k - 1)];
+  const int e = lane < k ? e_any : -1;
+  const int pr = lane < k ? pr_any : -1;
+  // The packed row is read once and the expert rows are not read again here:
+  // both streamed.
+  const vec4* src = rank_buf + i * nvec;
+  vec4 first[V];
+  load_first_pass<V, true>(src, nvec, first);
+  // segment of row i: number of segment ends at or below i
+  const int r = __popcll(__ballot(lane < R && end <= i));
   const bool here = e >= 0 && e < E && e / m == r;
-  const int p = here ? pair_row[(int64_t)t * k + lane] : -1;
+  const int p = here ? pr : -1;
   const bool ok = here && p >= 0 && p < cap_expert;
   if (__ballot(here && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
   if (ok) expert_src_pair[p] = t * k + lane;
   const uint64_t dests = __ballot(ok);
-  // The packed row is read once and the expert rows are not read again here:
-  // both streamed.
   if (!dests) return;
-  fan_out_row<V, true, true>(rank_buf + i * nvec, expert_buf, p, dests, nvec);
-  if (kMx) fan_out_row<1, true, true>(rank_scale + i * nvec_s, expert_scale, p, dests, nvec_s);
+  fan_out_row<V, true, true>(first, src, expert_buf, p, dests, nvec);
+  if (kMx) {
+    const vec4* ssrc = rank_scale + i * nvec_s;
+    vec4 sfirst[1];
+    load_first_pass<1, true>(ssrc, nvec_s, sfirst);
+    fan_out_row<1, true, true>(sfirst, ssrc, expert_scale, p, dests, nvec_s);
+  }
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
