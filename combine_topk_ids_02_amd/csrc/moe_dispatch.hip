@@ -1224,11 +1224,22 @@ int copy_vec(int nvec) {
   return kMaxVec;
 }
 
-// Combine: slices of at most 8 groups (8 x 8 fp32 accumulators per lane),
-// as few slices as cover the row.
-void combine_tiling(int nvec, int* v, int* slices) {
+// Gathers (combine, partial rows, home sum): one wave per (row, column
+// slice), a slice being at most `most` groups of 64 vec4 (each group 8 fp32
+// accumulators per lane), as few slices as that allows; more groups per slice
+// (up to 8) only if the grid would otherwise pass 2^31 - 1 waves. Measured
+// best: one group per wave for the combine and the home sum (more waves in
+// flight, fewer registers), three for the partial rows, whose waves first
+// find their rank and terms.
+constexpr int kCombineGroups = 1;
+constexpr int kPartialGroups = 3;
+constexpr int kRankSumGroups = 1;
+
+void combine_tiling(int nvec, int64_t rows, int most, int* v, int* slices) {
   const int groups = std::max(1, (nvec + kWave - 1) / kWave);
-  *slices = (groups + 7) / 8;
+  int g = most;
+  while (g < 8 && rows * ((groups + g - 1) / g) > int64_t(INT32_MAX)) ++g;
+  *slices = (groups + g - 1) / g;
   *v = (groups + *slices - 1) / *slices;
 }
 
@@ -1532,7 +1543,7 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   if (!aligned16(expert_out) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
-  combine_tiling(nvec, &v, &slices);
+  combine_tiling(nvec, shape->T, kCombineGroups, &v, &slices);
   ByVec<CombineLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
                             reinterpret_cast<const vec4*>(expert_out), pair_row, topk_weights,
@@ -1559,7 +1570,7 @@ int moe_combine_rank_partial(const moe_shape_t* shape, const uint16_t* expert_ou
     return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
-  combine_tiling(nvec, &v, &slices);
+  combine_tiling(nvec, max_rows, kPartialGroups, &v, &slices);
   ByVec<RankPartialLaunch>::run(
       v, dim3(blocks_for(max_rows * slices)), static_cast<hipStream_t>(stream),
       reinterpret_cast<const vec4*>(expert_out), rank_src_token, rank_offsets, topk_ids, pair_row,
@@ -1578,7 +1589,7 @@ int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
   if (!aligned16(partial) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
-  combine_tiling(nvec, &v, &slices);
+  combine_tiling(nvec, shape->T, kRankSumGroups, &v, &slices);
   ByVec<RankSumLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
                             reinterpret_cast<const vec4*>(partial), token_rank_slot,
