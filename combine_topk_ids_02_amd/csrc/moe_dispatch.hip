@@ -1228,10 +1228,12 @@ int copy_vec(int nvec) {
 // slice), a slice being at most `most` groups of 64 vec4 (each group 8 fp32
 // accumulators per lane), as few slices as that allows; more groups per slice
 // (up to 8) only if the grid would otherwise pass 2^31 - 1 waves. Measured
-// best: one group per wave for the combine and the home sum (more waves in
-// flight, fewer registers), three for the partial rows, whose waves first
-// find their rank and terms.
-constexpr int kCombineGroups = 1;
+// (1, 2, 3, 5 and 10 groups at H=5120): the combine is fastest within the
+// whole prefill step with up to 8 (two slices of 5; one group per wave is
+// 4% faster at the adv size but 0.6 us slower in the prefill step), the
+// home sum with one group per wave, the partial rows with three (their waves
+// first find their rank and terms).
+constexpr int kCombineGroups = 8;
 constexpr int kPartialGroups = 3;
 constexpr int kRankSumGroups = 1;
 
