@@ -1003,6 +1003,11 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   const vec4* src = rank_buf + i * nvec;
   vec4 first[V];
   load_first_pass<V, true>(src, nvec, first);
+  // MX: a scale row of at most 64 vec4 (H <= 32768) is one partial pass,
+  // requested with the code row (clamped lanes; lanes >= nvec_s store nothing)
+  const bool short_scales = kMx && nvec_s <= kWave;
+  vec4 sv;
+  if (short_scales) sv = load_row<true>(rank_scale + i * nvec_s + min(lane, nvec_s - 1));
   // segment of row i: number of segment ends at or below i
   const int r = __popcll(__ballot(lane < R && end <= i));
   const bool here = e >= 0 && e < E && e / m == r;
@@ -1013,7 +1018,15 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   const uint64_t dests = __ballot(ok);
   if (!dests) return;
   fan_out_row<V, true, true>(first, src, expert_buf, p, dests, nvec);
-  if (kMx) {
+  if (short_scales) {
+    uint64_t d = dests;
+    while (d) {
+      const int which = __ffsll((unsigned long long)d) - 1;
+      d &= d - 1;
+      if (lane < nvec_s)
+        store_row<true>(expert_scale + (int64_t)read_lane(p, which) * nvec_s + lane, sv);
+    }
+  } else if (kMx) {
     const vec4* ssrc = rank_scale + i * nvec_s;
     vec4 sfirst[1];
     load_first_pass<1, true>(ssrc, nvec_s, sfirst);
