@@ -760,6 +760,37 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
   if (dests) fan_out_row<V, true, false>(first, src, rank_buf, slot, dests, nvec);
 }
 
+// The pack for small batches (fewer than kFillTokens tokens, where one wave
+// per token cannot fill the GPU): one wave per (token, group of 64 vec4), one
+// vec4 per lane, the group index fastest so that a row's groups run side by
+// side. The same copies, order and cache policy as pack_rows.
+__global__ __launch_bounds__(kBlock) void pack_rows_small(
+    const vec4* hidden, const int32_t* __restrict__ token_rank_slot, vec4* rank_buf,
+    int32_t* __restrict__ rank_src_token, int T, int R, int nvec, int groups, int64_t cap_rank,
+    int32_t* err_word) {
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = int(gw / groups);
+  const int g = int(gw - (int64_t)t * groups);
+  if (t >= T) return;
+  const int c = g * kWave + lane;
+  // the slots and the row's column requested together (clamped, unconditional)
+  const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
+  const vec4 v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
+  const int slot = lane < R ? slot_any : -1;
+  const bool ok = slot >= 0 && slot < cap_rank;
+  if (g == 0) {
+    if (__ballot(slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+    if (ok) rank_src_token[slot] = t;
+  }
+  uint64_t d = __ballot(ok);
+  while (d) {
+    const int which = __ffsll((unsigned long long)d) - 1;
+    d &= d - 1;
+    if (c < nvec) store_row<false>(rank_buf + (int64_t)read_lane(slot, which) * nvec + c, v);
+  }
+}
+
 // Marks the padding rows of expert e (rows of its run or block that no pair
 // fills) with expert_src_pair -1.
 __device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts,
@@ -1241,6 +1272,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Below this many tokens one wave per token leaves the GPU underfilled (fewer
+// than 4 waves per compute unit): the pack, the MX pack and the combine then
+// split rows across waves.
+constexpr int kFillTokens = 1024;
+
 // Register tile V of pack and permute (vec4 per lane per pass): the whole row
 // in one pass when it has at most 16 groups of 64 vec4, else a divisor of the
 // group count in [8, 16] if there is one (no tail), else 16.
@@ -1259,9 +1295,10 @@ int copy_vec(int nvec) {
 // (up to 8) only if the grid would otherwise pass 2^31 - 1 waves. Measured
 // (1, 2, 3, 5 and 10 groups at H=5120): the combine is fastest within the
 // whole prefill step with up to 8 (two slices of 5; one group per wave is
-// 4% faster at the adv size but 0.6 us slower in the prefill step), the
-// home sum with one group per wave, the partial rows with three (their waves
-// first find their rank and terms).
+// 4% faster at the adv size but 0.6 us slower in the prefill step) and with
+// one group per wave below kFillTokens tokens (decode step 23.0 vs 24.9 us),
+// the home sum with one group per wave, the partial rows with three (their
+// waves first find their rank and terms).
 constexpr int kCombineGroups = 8;
 
 // The combine and the partial rows read the expert rows non-temporally when
@@ -1408,7 +1445,6 @@ int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_
   return launch_status();
 }
 
-constexpr int kMxFillTokens = 1024;  // 4 waves per compute unit at one wave per token
 
 // MX pack: NP passes in registers, the largest divisor of the pass count
 // that is at most `most` (so every register batch is whole).
@@ -1450,7 +1486,7 @@ int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
   // wave: MXFP8 28.4 vs 29.6 us at prefill, 131 vs 141 at adv, 6.4 vs 8.6 at
   // decode; MXFP4 6.3 vs 8.7 us at decode but 24.7 vs 21.5 at prefill.
   int np = mx_passes(npass, kMaxVec / nl), slices = 1;
-  if ((bits == 8 || shape->T < kMxFillTokens) && int64_t(shape->T) * npass <= INT32_MAX) {
+  if ((bits == 8 || shape->T < kFillTokens) && int64_t(shape->T) * npass <= INT32_MAX) {
     np = 1;
     slices = npass;
   }
@@ -1520,6 +1556,17 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
     return MOE_ERR_ARG;
   if (!aligned16(hidden) || !aligned16(rank_buf)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
+  const int groups = (nvec + kWave - 1) / kWave;
+  if (shape->T < kFillTokens && groups > 1) {
+    // Small batch: one wave per (token, 1 KiB of the row) (decode step 21.9
+    // vs 23.0 us). At prefill one wave per token is faster.
+    hipLaunchKernelGGL(pack_rows_small, dim3(blocks_for(int64_t(shape->T) * groups)),
+                       dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<const vec4*>(hidden), token_rank_slot,
+                       reinterpret_cast<vec4*>(rank_buf), rank_src_token, shape->T, shape->R,
+                       nvec, groups, cap_rank, err_word);
+    return launch_status();
+  }
   ByVec<PackLaunch>::run(copy_vec(nvec), dim3(blocks_for(shape->T)),
                          static_cast<hipStream_t>(stream), reinterpret_cast<const vec4*>(hidden),
                          token_rank_slot, reinterpret_cast<vec4*>(rank_buf), rank_src_token,
@@ -1608,7 +1655,7 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   if (!aligned16(expert_out) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
-  combine_tiling(nvec, shape->T, kCombineGroups, &v, &slices);
+  combine_tiling(nvec, shape->T, shape->T < kFillTokens ? 1 : kCombineGroups, &v, &slices);
   ByVec<CombineLaunch>::run(v, stream_expert_rows(cap_expert, shape->H),
                             dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
