@@ -552,12 +552,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 
     // Per column: each ranking wave's first row, then advance the running base.
     for (int c = tid; c < g.ncols; c += kLayoutThreads) {
+      int v[kOwnWaves];  // all reads first: one LDS round trip, not one per wave
+#pragma unroll
+      for (int w = 0; w < kOwnWaves; ++w) v[w] = s_cnt[w * g.ncols + c];
       int run = s_pre[c];
 #pragma unroll
       for (int w = 0; w < kOwnWaves; ++w) {
-        const int v = s_cnt[w * g.ncols + c];
         s_cnt[w * g.ncols + c] = run;
-        run += v;
+        run += v[w];
       }
       s_pre[c] = run;
     }
