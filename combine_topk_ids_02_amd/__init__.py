@@ -30,10 +30,10 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
-           "moe_testing_set_layout_form")
+           "moe_testing_set_layout_form", "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeShape(ctypes.Structure):
@@ -96,6 +96,8 @@ def lib():
     L.moe_permute_by_expert_mxfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
     L.moe_testing_set_layout_form.restype = ctypes.c_int
     L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
+    L.moe_testing_time_next_launch.restype = ctypes.c_int
+    L.moe_testing_time_next_launch.argtypes = [vp, vp]
     if L.moe_abi_version() != ABI_VERSION:
         raise MoeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, this binding "
                        f"expects {ABI_VERSION}: rebuild with __graft_entry__.build()")
@@ -333,6 +335,20 @@ def combine_ranks(partial, token_rank_slot, E: int, k: int, out, *, out_f32=None
         ctypes.byref(shape.c()), _ptr(_rows16(partial)), _ptr(_i32(token_rank_slot)),
         partial.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err), _stream(out.device))
     _check(st, "moe_combine_ranks")
+
+
+def time_next_launch(start: "torch.cuda.Event | None", stop: "torch.cuda.Event | None") -> None:
+    """moe_testing_time_next_launch: the library's next kernel launch records
+    `start` as it begins and `stop` as it ends (a measurement hook; both events
+    must have been recorded once, so that they exist). None, None disarms."""
+    if (start is None) != (stop is None):
+        raise MoeError("give both events or neither")
+    if start is not None and not (start.cuda_event and stop.cuda_event):
+        raise MoeError("record both events once before arming them")
+    st = lib().moe_testing_time_next_launch(
+        None if start is None else ctypes.c_void_p(start.cuda_event),
+        None if stop is None else ctypes.c_void_p(stop.cuda_event))
+    _check(st, "moe_testing_time_next_launch")
 
 
 class Buffers:

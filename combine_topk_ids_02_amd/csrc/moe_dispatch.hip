@@ -31,6 +31,7 @@
 // expert rows, combine outputs) is non-temporal so it does not evict them.
 // Nothing here is a dense contraction, so no MFMA.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -98,6 +99,26 @@ constexpr size_t kLayoutLdsLimit = 64 * 1024 - 256;  // dynamic LDS without a la
 // default), 0 every workgroup counts all ids, 1 two launches through tile
 // counts. Changed only by the testing hook.
 int g_layout_form = -1;
+
+// Events armed by moe_testing_time_next_launch for the next kernel launch.
+hipEvent_t g_time_start = nullptr;
+hipEvent_t g_time_stop = nullptr;
+
+// Every kernel launch of the library: a plain launch, or, once after
+// moe_testing_time_next_launch, a launch that has the runtime record the armed
+// events as the kernel begins and ends (so the pair brackets that kernel
+// alone, without the gap a separately recorded event leaves before it).
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ...)                               \
+  do {                                                                                    \
+    if (g_time_start) {                                                                   \
+      const hipEvent_t start_ = g_time_start, stop_ = g_time_stop;                        \
+      g_time_start = g_time_stop = nullptr;                                               \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start_, stop_, 0,         \
+                            __VA_ARGS__);                                                 \
+    } else {                                                                              \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                \
+    }                                                                                     \
+  } while (0)
 
 struct LayoutGeom {
   int T, E, R, k, m;    // m = experts per rank
@@ -633,13 +654,13 @@ struct LayoutArgs {
 template <int K, int kRB>
 void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) {
   if (a.hist) {
-    hipLaunchKernelGGL((layout_count<K, kRB>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
+    MOE_LAUNCH((layout_count<K, kRB>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
                        a.ids, a.hist);
-    hipLaunchKernelGGL((layout_tiles<K, kRB, true>), dim3(g.ntiles), dim3(kLayoutThreads),
+    MOE_LAUNCH((layout_tiles<K, kRB, true>), dim3(g.ntiles), dim3(kLayoutThreads),
                        layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
                        a.eo, a.trs, a.pr, a.err);
   } else {
-    hipLaunchKernelGGL((layout_tiles<K, kRB, false>), dim3(g.ntiles), dim3(kLayoutThreads),
+    MOE_LAUNCH((layout_tiles<K, kRB, false>), dim3(g.ntiles), dim3(kLayoutThreads),
                        layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist,
                        a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.err);
   }
@@ -1348,7 +1369,7 @@ template <int V>
 struct PackLaunch {
   static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots, vec4* rb,
                  int32_t* src, int T, int R, int nvec, int64_t cap, int32_t* err) {
-    hipLaunchKernelGGL(pack_rows<V>, grid, dim3(kBlock), 0, st, hid, slots, rb, src, T, R, nvec,
+    MOE_LAUNCH(pack_rows<V>, grid, dim3(kBlock), 0, st, hid, slots, rb, src, T, R, nvec,
                        cap, err);
   }
 };
@@ -1361,11 +1382,11 @@ struct PermuteLaunch {
                  int T, int E, int R, int k, int m, int block, int nvec, int nvec_s,
                  int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
     if (rs)
-      hipLaunchKernelGGL((permute_rows<V, true>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
+      MOE_LAUNCH((permute_rows<V, true>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
                          ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
                          pad_waves, cap_rank, cap_expert, err);
     else
-      hipLaunchKernelGGL((permute_rows<V, false>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
+      MOE_LAUNCH((permute_rows<V, false>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
                          ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
                          pad_waves, cap_rank, cap_expert, err);
   }
@@ -1378,10 +1399,10 @@ struct CombineLaunch {
                  const int32_t* prow, const float* w, vec4* out, vec4* out32, int T, int k,
                  int nvec, int slices, int64_t cap_expert, int32_t* err) {
     if (stream_rows)
-      hipLaunchKernelGGL((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
+      MOE_LAUNCH((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
                          out32, T, k, nvec, slices, cap_expert, err);
     else
-      hipLaunchKernelGGL((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
+      MOE_LAUNCH((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
                          out32, T, k, nvec, slices, cap_expert, err);
   }
 };
@@ -1394,11 +1415,11 @@ struct RankPartialLaunch {
                  int R, int k, int m, int nvec, int slices, int64_t cap_rank, int64_t cap_expert,
                  int32_t* err) {
     if (stream_rows)
-      hipLaunchKernelGGL((rank_partial_rows<V, true>), grid, dim3(kBlock), 0, st, eo, src, roff,
+      MOE_LAUNCH((rank_partial_rows<V, true>), grid, dim3(kBlock), 0, st, eo, src, roff,
                          ids, prow, w, part, part32, T, E, R, k, m, nvec, slices, cap_rank,
                          cap_expert, err);
     else
-      hipLaunchKernelGGL((rank_partial_rows<V, false>), grid, dim3(kBlock), 0, st, eo, src, roff,
+      MOE_LAUNCH((rank_partial_rows<V, false>), grid, dim3(kBlock), 0, st, eo, src, roff,
                          ids, prow, w, part, part32, T, E, R, k, m, nvec, slices, cap_rank,
                          cap_expert, err);
   }
@@ -1409,7 +1430,7 @@ struct RankSumLaunch {
   static void go(dim3 grid, hipStream_t st, const vec4* part, const int32_t* slots, vec4* out,
                  vec4* out32, int T, int R, int nvec, int slices, int64_t cap_rank,
                  int32_t* err) {
-    hipLaunchKernelGGL(rank_sum_rows<V>, grid, dim3(kBlock), 0, st, part, slots, out, out32, T,
+    MOE_LAUNCH(rank_sum_rows<V>, grid, dim3(kBlock), 0, st, part, slots, out, out32, T,
                        R, nvec, slices, cap_rank, err);
   }
 };
@@ -1462,10 +1483,10 @@ struct PackMxLaunch {
                  uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R, int nvec, int slices,
                  int64_t cap, int32_t* err) {
     if (bits == 4) {
-      hipLaunchKernelGGL((pack_rows_mx<NP, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
+      MOE_LAUNCH((pack_rows_mx<NP, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
                          src, T, R, nvec, slices, cap, err);
     } else if constexpr (NP * MxLane<8>::NL <= kMaxVec) {
-      hipLaunchKernelGGL((pack_rows_mx<NP, 8>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
+      MOE_LAUNCH((pack_rows_mx<NP, 8>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
                          src, T, R, nvec, slices, cap, err);
     }
   }
@@ -1521,6 +1542,13 @@ int moe_testing_set_layout_form(int form) {
   return old;
 }
 
+int moe_testing_time_next_launch(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_ERR_ARG;
+  g_time_start = static_cast<hipEvent_t>(start_event);
+  g_time_stop = static_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
+}
+
 size_t moe_layout_workspace_bytes(const moe_shape_t* shape) {
   if (!shape_ok(shape)) return 0;
   return layout_workspace_bytes(layout_geometry(*shape));
@@ -1562,7 +1590,7 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
   if (shape->T < kFillTokens && groups > 1) {
     // Small batch: one wave per (token, 1 KiB of the row) (decode step 21.9
     // vs 23.0 us). At prefill one wave per token is faster.
-    hipLaunchKernelGGL(pack_rows_small, dim3(blocks_for(int64_t(shape->T) * groups)),
+    MOE_LAUNCH(pack_rows_small, dim3(blocks_for(int64_t(shape->T) * groups)),
                        dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                        reinterpret_cast<const vec4*>(hidden), token_rank_slot,
                        reinterpret_cast<vec4*>(rank_buf), rank_src_token, shape->T, shape->R,

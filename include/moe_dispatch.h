@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 3
+#define MOE_DISPATCH_ABI_VERSION 4
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -323,6 +323,18 @@ int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
  * moe_dispatch_layout, 0 every workgroup counts all ids, 1 two launches.
  */
 int moe_testing_set_layout_form(int form);
+
+/*
+ * Measurement hook (not for production callers; process-wide, not
+ * thread-safe): the next kernel this library launches, on any stream, has the
+ * runtime record start_event as it begins and stop_event as it ends, so that
+ * hipEventElapsedTime(start_event, stop_event) is that kernel's own duration.
+ * The events are the caller's (hipEvent_t as void*, created with timing
+ * enabled) and are used once; NULL, NULL disarms. Returns MOE_ERR_ARG if only
+ * one of them is NULL. A call that launches two kernels (the two-launch
+ * layout) times its first.
+ */
+int moe_testing_time_next_launch(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

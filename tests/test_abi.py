@@ -26,7 +26,14 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 3
+    assert L.moe_abi_version() == moe.ABI_VERSION == 4
+
+
+def test_timing_hook_takes_both_events_or_neither():
+    L = moe.lib()
+    assert L.moe_testing_time_next_launch(ctypes.c_void_p(0x10000), None) == moe.MOE_ERR_ARG
+    assert L.moe_testing_time_next_launch(None, ctypes.c_void_p(0x10000)) == moe.MOE_ERR_ARG
+    assert L.moe_testing_time_next_launch(None, None) == 0  # disarmed: nothing is recorded
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails its checks first

@@ -221,3 +221,25 @@ def test_layout_forms_with_workspace(form, what):
         moe.lib().moe_testing_set_layout_form(old)
     ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
     compare(gpu, ref, f"layout form {form}")
+
+
+def test_timing_hook_brackets_the_next_kernel():
+    """moe_testing_time_next_launch: the armed event pair is recorded by the
+    library's next kernel (here the layout, the first launch of the path) and
+    by nothing else, and the timed run gives the oracle's results."""
+    import combine_topk_ids_02_amd as moe
+    w, hid, ids, wts, y = workload_inputs("decode")
+    say("[timing hook] decode")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    moe.time_next_launch(a, b)
+    gpu = run_gpu(hid, ids, wts, w.E, w.R, y)
+    ref = run_oracle(hid, ids, wts, w.E, w.R, y, gpu["cap_rank"], gpu["cap_expert"])
+    compare(gpu, ref, "timed run")
+    first = a.elapsed_time(b)
+    assert 0.0 < first < 1.0, first  # one small kernel, in milliseconds
+    # used once: the next run records nothing into the pair
+    run_gpu(hid, ids, wts, w.E, w.R, y)
+    assert a.elapsed_time(b) == first
