@@ -30,10 +30,11 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
-           "moe_testing_set_layout_form", "moe_testing_time_next_launch")
+           "moe_testing_set_layout_form", "moe_testing_set_layout_match",
+           "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class MoeShape(ctypes.Structure):
@@ -96,6 +97,8 @@ def lib():
     L.moe_permute_by_expert_mxfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
     L.moe_testing_set_layout_form.restype = ctypes.c_int
     L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
+    L.moe_testing_set_layout_match.restype = ctypes.c_int
+    L.moe_testing_set_layout_match.argtypes = [ctypes.c_int]
     L.moe_testing_time_next_launch.restype = ctypes.c_int
     L.moe_testing_time_next_launch.argtypes = [vp, vp]
     if L.moe_abi_version() != ABI_VERSION:

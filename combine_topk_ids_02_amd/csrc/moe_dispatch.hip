@@ -99,6 +99,9 @@ constexpr size_t kLayoutLdsLimit = 64 * 1024 - 256;  // dynamic LDS without a la
 // default), 0 every workgroup counts all ids, 1 two launches through tile
 // counts. Changed only by the testing hook.
 int g_layout_form = -1;
+// 0: the layout matches equal experts with ballots even where the LDS tables
+// fit. Changed only by the testing hook.
+int g_layout_match = 1;
 
 // Events armed by moe_testing_time_next_launch for the next kernel launch.
 hipEvent_t g_time_start = nullptr;
@@ -127,6 +130,8 @@ struct LayoutGeom {
   int tile_tokens;      // tokens ranked per workgroup (multiple of kOwnTokens)
   int ntiles;
   int tiles_pad;        // ntiles rounded up to a multiple of 4 (tile-count column stride)
+  int lds_match;        // 1: equal experts of a chunk are matched through LDS tables
+  int e_pad;            // E rounded up to a multiple of 4 (byte-table stride)
   float inv_m;          // 1/m rounded to float
 };
 
@@ -357,11 +362,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   constexpr int KR = K > 0 ? K : kMaxK;
   using Mask = typename RankMask<kRB>::type;
   const int k = K > 0 ? K : g.k;
-  extern __shared__ int32_t smem[];
-  int32_t* s_pack = smem;                         // [kOwnTokens * k] own sub-tile ids
+  extern __shared__ __align__(16) int32_t smem[];
+  // With lds_match: per ranking wave a table of 64 lane masks (first, so
+  // 8-byte aligned) and a byte per expert (last).
+  uint64_t* s_peer = reinterpret_cast<uint64_t*>(smem);  // [kOwnWaves][64]
+  int32_t* s_pack = smem + (g.lds_match ? kOwnWaves * kWave * 2 : 0);  // [kOwnTokens * k] own ids
   int32_t* s_cnt = s_pack + kOwnTokens * k;       // [kOwnWaves][ncols] per-wave counts
   int32_t* s_pre = s_cnt + kOwnWaves * g.ncols;   // [ncols + 1] before the tile -> running base
   int32_t* s_tot = s_pre + g.ncols + 1;           // [ncols + 1] other tokens -> totals -> offsets
+  uint8_t* s_rep = reinterpret_cast<uint8_t*>(s_tot + g.ncols + 1);  // [kOwnWaves][e_pad]
   // (the extra slot of each takes the counts of invalid ids, so counting needs no branch)
   __shared__ int32_t s_tmp[kLayoutWaves];
 
@@ -523,7 +532,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       for (int j = 0; j < KR; ++j)
         if (j < k) own[j] = tok_lane ? s_pack[ti * k + j] : -1;
       int lead[KC], grp[KC];
-      uint64_t peers[KC];
+      uint64_t peers[KC];  // lanes of the chunk holding the same expert
 #pragma unroll
       for (int ch = 0; ch < KC; ++ch) {
         if (ch < nch) {
@@ -533,14 +542,46 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
           peers[ch] = __ballot(valid);
         }
       }
-      // One ballot per id bit, all chunks side by side (independent chains).
-      for (int b = 0; b < ebits; ++b) {
+      if (g.lds_match) {
+        // Through the wave's own LDS tables, one chunk after the other: each
+        // lane writes its lane number at its expert's byte and reads it back,
+        // which gives every lane of a group the same member of it (whichever
+        // write landed last); each lane then sets its bit in that member's
+        // mask and reads the mask. The wave's LDS operations take effect in
+        // issue order; atomic loads and stores keep the compiler from
+        // forwarding a lane's own write to its read.
+        uint8_t* rep_w = s_rep + wave * g.e_pad;
+        uint64_t* peer_w = s_peer + wave * kWave;
 #pragma unroll
         for (int ch = 0; ch < KC; ++ch) {
           if (ch < nch) {
-            const bool bit = (ex[ch] >> b) & 1;
-            const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
-            peers[ch] &= bit ? ones : ~ones;
+            const bool on = ex[ch] >= 0;
+            int rep = lane;
+            uint64_t pm = 0;
+            if (on) {
+              __hip_atomic_store(rep_w + ex[ch], uint8_t(lane), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+              rep = __hip_atomic_load(rep_w + ex[ch], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
+              __hip_atomic_store(peer_w + rep, uint64_t(0), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+              __hip_atomic_fetch_or(peer_w + rep, uint64_t(1) << lane, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WAVEFRONT);
+              pm = __hip_atomic_load(peer_w + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+            }
+            peers[ch] = pm;
+          }
+        }
+      } else {
+        // One ballot per id bit, all chunks side by side (independent chains).
+        for (int b = 0; b < ebits; ++b) {
+#pragma unroll
+          for (int ch = 0; ch < KC; ++ch) {
+            if (ch < nch) {
+              const bool bit = (ex[ch] >> b) & 1;
+              const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
+              peers[ch] &= bit ? ones : ~ones;
+            }
           }
         }
       }
@@ -623,6 +664,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 constexpr size_t layout_lds_bytes(int k, int ncols) {
   return sizeof(int32_t) * (size_t(kOwnTokens) * k + size_t(kOwnWaves + 2) * ncols + 2);
 }
+
+// LDS of the layout with the match tables (a lane mask per lane and a byte
+// per expert, per ranking wave); they are used when this fits.
+constexpr size_t layout_match_lds_bytes(int k, int E, int R) {
+  return layout_lds_bytes(k, E + R) +
+         size_t(kOwnWaves) * (sizeof(uint64_t) * kWave + size_t((E + 3) / 4 * 4));
+}
+
+size_t layout_launch_lds(const LayoutGeom& g) {
+  return g.lds_match ? layout_match_lds_bytes(g.k, g.E, g.R) : layout_lds_bytes(g.k, g.ncols);
+}
 static_assert(layout_lds_bytes(kMaxK, kMaxExperts + kMaxRanks) <= kLayoutLdsLimit,
               "the layout's LDS fits every shape");
 
@@ -637,6 +689,9 @@ LayoutGeom layout_geometry(const moe_shape_t& sh) {
   g.block = sh.block;
   g.ncols = sh.E + sh.R;
   g.inv_m = float(1.0 / double(g.m));
+  g.e_pad = (sh.E + 3) / 4 * 4;
+  g.lds_match = (g_layout_match != 0 && layout_match_lds_bytes(sh.k, sh.E, sh.R) <= kLayoutLdsLimit)
+                    ? 1 : 0;
   const int64_t subs = (int64_t(sh.T) + kOwnTokens - 1) / kOwnTokens;
   const int64_t per_tile = std::max<int64_t>(1, (subs + kMaxTiles - 1) / kMaxTiles);
   g.tile_tokens = int(per_tile * kOwnTokens);
@@ -657,11 +712,11 @@ void launch_layout_kw(const LayoutGeom& g, hipStream_t st, const LayoutArgs& a) 
     MOE_LAUNCH((layout_count<K, kRB>), dim3(g.ntiles), dim3(kCountThreads), 0, st, g,
                        a.ids, a.hist);
     MOE_LAUNCH((layout_tiles<K, kRB, true>), dim3(g.ntiles), dim3(kLayoutThreads),
-                       layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
+                       layout_launch_lds(g), st, g, a.ids, a.hist, a.rc, a.ro, a.ec,
                        a.eo, a.trs, a.pr, a.err);
   } else {
     MOE_LAUNCH((layout_tiles<K, kRB, false>), dim3(g.ntiles), dim3(kLayoutThreads),
-                       layout_lds_bytes(g.k, g.ncols), st, g, a.ids, a.hist,
+                       layout_launch_lds(g), st, g, a.ids, a.hist,
                        a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.err);
   }
 }
@@ -1539,6 +1594,12 @@ const char* moe_status_string(int status) {
 int moe_testing_set_layout_form(int form) {
   const int old = g_layout_form;
   if (form >= -1 && form <= 1) g_layout_form = form;
+  return old;
+}
+
+int moe_testing_set_layout_match(int match) {
+  const int old = g_layout_match;
+  if (match == 0 || match == 1) g_layout_match = match;
   return old;
 }
 

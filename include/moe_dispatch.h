@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 4
+#define MOE_DISPATCH_ABI_VERSION 5
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -323,6 +323,16 @@ int moe_combine_ranks(const moe_shape_t* shape, const uint16_t* partial,
  * moe_dispatch_layout, 0 every workgroup counts all ids, 1 two launches.
  */
 int moe_testing_set_layout_form(int form);
+
+/*
+ * Testing hook (not for production callers; process-wide; returns the
+ * previous value): how the layout finds the pairs of one expert among the 64
+ * pairs a wave ranks at once: 1 (default) through per-wave LDS tables where
+ * they fit (8 KiB plus E bytes beside the layout's other LDS, within 64 KiB),
+ * else with one wave ballot per bit of the expert id; 0 always with ballots.
+ * Both give the same results.
+ */
+int moe_testing_set_layout_match(int match);
 
 /*
  * Measurement hook (not for production callers; process-wide, not

@@ -195,13 +195,15 @@ LAYOUT_FORMS = [(0, "prefill"), (1, "prefill"), (1, "decode"), (0, "adv"), (1, "
                 (1, (257, 512, 16, 4, 2, 0.1, 0.0, 4))]
 
 
+@pytest.mark.parametrize("match", [1, 0], ids=["lds_match", "ballot_match"])
 @pytest.mark.parametrize("form,what", LAYOUT_FORMS,
                          ids=[f"form{f}_{w if isinstance(w, str) else 'T%d' % w[0]}"
                               for f, w in LAYOUT_FORMS])
-def test_layout_forms_with_workspace(form, what):
+def test_layout_forms_with_workspace(form, what, match):
     """Both forms of the layout with a workspace, forced whatever the size
     (0: every workgroup counts all ids; 1: two launches through tile counts),
-    give the oracle's layout."""
+    each with both ways of matching equal experts (LDS tables where they fit,
+    or ballots), give the oracle's layout."""
     import combine_topk_ids_02_amd as moe
     if isinstance(what, str):
         w, hid, ids, wts, y = workload_inputs(what)
@@ -213,12 +215,14 @@ def test_layout_forms_with_workspace(form, what):
         wts = rng.random((T, k)).astype(np.float32)
         hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
         y = synth.expert_out_slots(seed, E, H, ids)
-    say(f"[layout form {form}] {what if isinstance(what, str) else what[:5]}")
+    say(f"[layout form {form} match {match}] {what if isinstance(what, str) else what[:5]}")
     old = moe.lib().moe_testing_set_layout_form(form)
+    old_match = moe.lib().moe_testing_set_layout_match(match)
     try:
         gpu = run_gpu(hid, ids, wts, E, R, y)
     finally:
         moe.lib().moe_testing_set_layout_form(old)
+        moe.lib().moe_testing_set_layout_match(old_match)
     ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"])
     compare(gpu, ref, f"layout form {form}")
 

@@ -57,8 +57,9 @@ def draw(seed: int, mx: bool = False) -> dict:
     p_dup = float(rng.choice([0.0, 0.0, 0.1])) if k > 1 else 0.0
     p_bad = float(rng.choice([0.0, 0.0, 0.0, 0.02]))
     form = int(rng.choice([-1, 0, 1]))
+    match = int(rng.choice([0, 1, 1]))  # 0: the layout matches equal experts with ballots only
     return dict(seed=seed, T=T, H=H, E=E, R=R, k=k, align=align, block=block, p_neg=p_neg,
-                p_dup=p_dup, p_bad=p_bad, form=form)
+                p_dup=p_dup, p_bad=p_bad, form=form, match=match)
 
 
 def inputs(c: dict):
@@ -71,16 +72,20 @@ def inputs(c: dict):
 
 
 class layout_form:
-    """Forces the layout form for the duration (-1: chosen by size)."""
+    """Forces the layout form (-1: chosen by size) and its way of matching
+    equal experts (1: LDS tables where they fit, 0: ballots) for the duration."""
 
-    def __init__(self, form: int):
+    def __init__(self, form: int, match: int = 1):
         self.form = form
+        self.match = match
 
     def __enter__(self):
         self.old = moe.lib().moe_testing_set_layout_form(self.form)
+        self.old_match = moe.lib().moe_testing_set_layout_match(self.match)
 
     def __exit__(self, *exc):
         moe.lib().moe_testing_set_layout_form(self.old)
+        moe.lib().moe_testing_set_layout_match(self.old_match)
 
 
 CASES = [draw(s) for s in range(96)]
@@ -91,7 +96,7 @@ def test_random_shape_one_stage(c):
     say(f"[random] {c}")
     ids, wts, hid = inputs(c)
     y = synth.expert_out_slots(c["seed"], c["E"], c["H"], ids)
-    with layout_form(c["form"]):
+    with layout_form(c["form"], c["match"]):
         gpu = run_gpu(hid, ids, wts, c["E"], c["R"], y, align=c["align"], block=c["block"])
     ref = run_oracle(hid, ids, wts, c["E"], c["R"], y, gpu["cap_rank"], gpu["cap_expert"],
                      align=c["align"], block=c["block"])
@@ -107,7 +112,7 @@ def test_random_shape_two_stage(c):
     say(f"[random two-stage] {c}")
     ids, wts, hid = inputs(c)
     y = synth.expert_out_slots(c["seed"], c["E"], c["H"], ids)
-    with layout_form(c["form"]):
+    with layout_form(c["form"], c["match"]):
         check(hid, ids, wts, c["E"], c["R"], y, f"random two-stage {c}")
 
 
@@ -120,6 +125,6 @@ def test_random_shape_mx(c, bits):
     from test_mx_dispatch_gpu import check
     say(f"[random mxfp{bits}] {c}")
     ids, _, hid = inputs(c)
-    with layout_form(c["form"]):
+    with layout_form(c["form"], c["match"]):
         check(hid, ids, c["E"], c["R"], f"random mxfp{bits} {c}", bits=bits, align=c["align"],
               block=c["block"])
