@@ -379,8 +379,187 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int lane = lane_id();
   const int tile_lo = blockIdx.x * g.tile_tokens;
   const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
-  // own ids captured by the counting pass (only when it runs)
-  const bool one_sub = !kFromHist && g.tile_tokens == kOwnTokens;
+  // A tile of one sub-tile (every tile up to 64 * kOwnTokens tokens) is
+  // ranked before the counts are known: its ranking waves take their ids
+  // straight from memory and work out the ranks inside the tile while the
+  // counting runs; only the final rows wait for the scan. Larger tiles rank
+  // their sub-tiles one after the other, after the scan, through s_pack.
+  const bool early = g.tile_tokens == kOwnTokens;
+
+  // 4. (Ranking, used by both orders.) Wave w < kOwnWaves owns tokens
+  //    [32w, 32w+32) of a sub-tile, i.e. the contiguous pairs [32wk, 32(w+1)k),
+  //    and walks them 64 at a time in order (chunks). Lanes holding the same
+  //    expert find each other (the match); the lowest of them adds the
+  //    group's size to the wave's running count for that expert with an LDS
+  //    atomic that returns the old count. A wave's atomics complete in issue
+  //    order, so the counts are exact without waiting between chunks; the
+  //    waves' counts are then chained in wave order per column.
+  const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);
+  constexpr int KC = (kTokW * KR + kWave - 1) / kWave;  // chunks of 64 pairs per wave (bound)
+  const int nch = (kTokW * k + kWave - 1) / kWave;
+  bool bad_id = false;
+  bool full_block = false;  // a pair found its expert's fixed block full
+  const bool ranker = wave < kOwnWaves;
+  int32_t* cnt_w = s_cnt + (ranker ? wave : 0) * g.ncols;
+  const int ti = wave * kTokW + lane;  // this lane's token in the sub-tile (lanes < kTokW)
+  int ex[KC], rk[KC];  // per chunk: this lane's expert (or -1) and its rank in the wave
+  int own[KR];         // ids of token ti, for its rank set
+  Mask mask = 0;       // rank set of token ti (lanes < kTokW)
+
+  // Ranks inside the sub-tile from ex[] and own[]: rk[] relative to the
+  // wave's running counts, which it advances (cnt_w), and the wave's copies
+  // per rank (cnt_w[E + r]).
+  auto rank_in_wave = [&]() {
+    int lead[KC], grp[KC];
+    uint64_t peers[KC];  // lanes of the chunk holding the same expert
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch) {
+      if (ch < nch) {
+        const bool valid = uint32_t(ex[ch]) < uint32_t(g.E);
+        bad_id |= (ex[ch] != -1) && !valid;
+        ex[ch] = valid ? ex[ch] : -1;
+        peers[ch] = __ballot(valid);
+      }
+    }
+    if (g.lds_match) {
+      // Through the wave's own LDS tables, one chunk after the other: each
+      // lane writes its lane number at its expert's byte and reads it back,
+      // which gives every lane of a group the same member of it (whichever
+      // write landed last); each lane then sets its bit in that member's
+      // mask and reads the mask. The wave's LDS operations take effect in
+      // issue order; atomic loads and stores keep the compiler from
+      // forwarding a lane's own write to its read.
+      uint8_t* rep_w = s_rep + wave * g.e_pad;
+      uint64_t* peer_w = s_peer + wave * kWave;
+#pragma unroll
+      for (int ch = 0; ch < KC; ++ch) {
+        if (ch < nch) {
+          const bool on = ex[ch] >= 0;
+          int rep = lane;
+          uint64_t pm = 0;
+          if (on) {
+            __hip_atomic_store(rep_w + ex[ch], uint8_t(lane), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+            rep = __hip_atomic_load(rep_w + ex[ch], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WAVEFRONT);
+            __hip_atomic_store(peer_w + rep, uint64_t(0), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+            __hip_atomic_fetch_or(peer_w + rep, uint64_t(1) << lane, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WAVEFRONT);
+            pm = __hip_atomic_load(peer_w + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+          }
+          peers[ch] = pm;
+        }
+      }
+    } else {
+      // One ballot per id bit, all chunks side by side (independent chains).
+      for (int b = 0; b < ebits; ++b) {
+#pragma unroll
+        for (int ch = 0; ch < KC; ++ch) {
+          if (ch < nch) {
+            const bool bit = (ex[ch] >> b) & 1;
+            const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
+            peers[ch] &= bit ? ones : ~ones;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch) {
+      if (ch < nch) {
+        rk[ch] = __popcll(peers[ch] & lanes_below());
+        lead[ch] = ex[ch] >= 0 ? __ffsll((unsigned long long)peers[ch]) - 1 : lane;
+        grp[ch] = __popcll(peers[ch]);
+      }
+    }
+    int cnt_old[KC];
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch) {
+      if (ch < nch) {
+        cnt_old[ch] = 0;
+        if (ex[ch] >= 0 && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[ex[ch]], grp[ch]);
+      }
+    }
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch)
+      if (ch < nch) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
+    mask = 0;
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+      if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
+    const int copies = wave_rank_counts<kRB>(mask, g.R);  // lane r: tokens with a copy on r
+    if (lane < g.R) cnt_w[g.E + lane] = copies;
+  };
+
+  // Per column: each ranking wave's first row, then advance the running base
+  // (between barriers).
+  auto chain_columns = [&]() {
+    for (int c = tid; c < g.ncols; c += kLayoutThreads) {
+      int v[kOwnWaves];  // all reads first: one LDS round trip, not one per wave
+#pragma unroll
+      for (int w = 0; w < kOwnWaves; ++w) v[w] = s_cnt[w * g.ncols + c];
+      int run = s_pre[c];
+#pragma unroll
+      for (int w = 0; w < kOwnWaves; ++w) {
+        s_cnt[w * g.ncols + c] = run;
+        run += v[w];
+      }
+      s_pre[c] = run;
+    }
+  };
+
+  // The rows of the sub-tile starting at token t0 (nt tokens), from the
+  // chained bases (ranking waves).
+  auto write_rows = [&](int t0, int nt) {
+    const int npairs = nt * k;
+    const bool tok_lane = lane < kTokW && ti < nt;
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch) {
+      if (ch < nch) {
+        const int pl = wave * kTokW * k + ch * kWave + lane;
+        if (ch * kWave + lane < kTokW * k && pl < npairs) {
+          int row = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
+          if (g.block > 0 && row >= (ex[ch] + 1) * g.block) {
+            row = -1;
+            full_block = true;
+          }
+          pair_row[(int64_t)t0 * k + pl] = row;
+        }
+      }
+    }
+    auto write_slot = [&](int r) {
+      const uint64_t on = __ballot((mask >> r) & 1);
+      if (tok_lane)
+        token_rank_slot[(int64_t)(t0 + ti) * g.R + r] =
+            ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
+    };
+    if (kRB == 8) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < g.R) write_slot(r);
+    } else {
+      for (int r = 0; r < g.R; ++r) write_slot(r);
+    }
+  };
+
+  // Early order: the ranking waves request their ids before anything else
+  // (pairs past the tile's last token read as -1).
+  if (early && ranker) {
+    const int64_t pair0 = (int64_t)tile_lo * k;
+    const int npairs = max(0, tile_hi - tile_lo) * k;
+#pragma unroll
+    for (int ch = 0; ch < KC; ++ch) {
+      if (ch < nch) {
+        const int f = wave * kTokW * k + ch * kWave + lane;
+        const bool mine = ch * kWave + lane < kTokW * k && f < npairs;
+        ex[ch] = mine ? ids[pair0 + f] : -1;
+      }
+    }
+    const bool tok_lane = lane < kTokW && tile_lo + ti < tile_hi;
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+      if (j < k) own[j] = tok_lane ? ids[(int64_t)(tile_lo + ti) * k + j] : -1;
+  }
 
   // The first batch of ids for the counting pass is requested before the
   // LDS is cleared.
@@ -394,10 +573,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   // The per-wave running counts of the first sub-tile start at zero (cleared
   // here, while the ids load, rather than after the scan).
   for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
-  // Own ids past the last token read as -1 (the counting pass writes the rest).
-  if (one_sub)
-    for (int f = (tile_hi - tile_lo) * k + tid; f < kOwnTokens * k; f += kLayoutThreads)
-      s_pack[f] = -1;
 
   if (kFromHist) {
     // 1'. Counts before the tile and from it on, per column, from the tile
@@ -428,16 +603,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       s_pre[c] = before;
       s_tot[c] = total - before;
     }
-    __syncthreads();
+    __syncthreads();  // s_pre / s_tot final, s_cnt zeroed
+    if (early && ranker) rank_in_wave();  // before the scan, which needs no s_cnt
   } else {
     // 1. Histogram of every token, straight from registers: a batch of
     //    whole tokens per lane is loaded (16 bytes per load, coalesced) while
     //    the previous one is counted. Experts: one LDS atomic per pair. Ranks:
     //    one ballot per rank per 64 tokens (a wave's tokens sit on one side of
-    //    the tile start). The tile's own ids go to s_pack on the way.
+    //    the tile start). The ranking waves of the early order rank their
+    //    pairs first, so that their LDS work overlaps the others' counting.
     using L = IdLanes<K>;
     int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
-    __syncthreads();  // s_pre / s_tot zeroed
+    __syncthreads();  // s_pre / s_tot / s_cnt zeroed
+    if (early && ranker) rank_in_wave();
     for (int b0 = 0; b0 < g.T; b0 += L::BATCH) {
       int32_t cur[L::NW];
 #pragma unroll
@@ -445,30 +623,26 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       if (b0 + L::BATCH < g.T) load_tokens<K>(ids, g.T, k, b0 + L::BATCH, nxt);
 #pragma unroll
       for (int q = 0; q < L::NQ; ++q) {
-        const int tq = b0 + (q * kLayoutThreads + tid) * L::TPL;   // this lane's first token
         const int tw = b0 + (q * kLayoutThreads + wave * kWave) * L::TPL;  // the wave's first
         if (tw >= g.T) continue;  // a wave past the last token counts nothing
-        const bool early = tw < tile_lo;
-        int32_t* cnt = early ? s_pre : s_tot;
+        const bool before = tw < tile_lo;
+        int32_t* cnt = before ? s_pre : s_tot;
         int c = 0;
 #pragma unroll
         for (int u = 0; u < L::TPL; ++u) {
           const int32_t* ev = cur + q * L::VPL * 4 + u * K;
-          const int t = tq + u;
-          const bool own = one_sub && t >= tile_lo && t < tile_hi;
-          Mask mask = 0;
+          Mask tmask = 0;
 #pragma unroll
           for (int j = 0; j < KR; ++j) {
             if (j < k) {
               const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
               atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
-              mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
-              if (own) s_pack[(t - tile_lo) * k + j] = ev[j];
+              tmask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
             }
           }
-          c += wave_rank_counts<kRB>(mask, g.R);
+          c += wave_rank_counts<kRB>(tmask, g.R);
         }
-        (early ? rc_pre : rc_tot) += c;
+        (before ? rc_pre : rc_tot) += c;
       }
     }
     if (lane < g.R) {  // lane r holds this wave's copies on rank r
@@ -483,178 +657,41 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   scan_columns(s_pre, s_tot, g.E, g.R, g.align, g.block, s_tmp, blockIdx.x == 0, expert_counts,
                expert_offsets, rank_counts, rank_offsets);
 
-  // 4. Own tile, kOwnTokens tokens at a time, ranked by waves 0..7. Wave w
-  //    owns tokens [32w, 32w+32) of the sub-tile, i.e. the contiguous pairs
-  //    [32wk, 32(w+1)k), and walks them 64 at a time in order (chunks). Lanes
-  //    holding the same expert find each other with one ballot per id bit;
-  //    the lowest of them adds the group's size to the wave's running count
-  //    for that expert with an LDS atomic that returns the old count. A
-  //    wave's atomics complete in issue order, so the counts are exact
-  //    without waiting between chunks; the waves' counts are then chained in
-  //    wave order per column.
-  const int ebits = 32 - __clz(g.E > 1 ? g.E - 1 : 1);
-  constexpr int KC = (kTokW * KR + kWave - 1) / kWave;  // chunks of 64 pairs per wave (bound)
-  const int nch = (kTokW * k + kWave - 1) / kWave;
-  bool bad_id = false;
-  bool full_block = false;  // a pair found its expert's fixed block full
-  const bool ranker = wave < kOwnWaves;
-  int32_t* cnt_w = s_cnt + (ranker ? wave : 0) * g.ncols;
-  for (int t0 = tile_lo; t0 < tile_hi; t0 += kOwnTokens) {
-    const int nt = min(kOwnTokens, tile_hi - t0);
-    const int npairs = nt * k;
-    __syncthreads();  // s_pack and s_cnt free; s_pre final
-    if (!one_sub) {
+  if (early) {
+    chain_columns();
+    __syncthreads();
+    if (ranker) write_rows(tile_lo, max(0, tile_hi - tile_lo));
+  } else {
+    // Sub-tiles one after the other, their ids staged in LDS.
+    for (int t0 = tile_lo; t0 < tile_hi; t0 += kOwnTokens) {
+      const int nt = min(kOwnTokens, tile_hi - t0);
+      const int npairs = nt * k;
+      __syncthreads();  // s_pack and s_cnt free; s_pre final
       for (int f = tid; f < kOwnTokens * k; f += kLayoutThreads) {
         const int64_t gf = (int64_t)t0 * k + f;
         s_pack[f] = f < npairs ? ids[gf] : -1;
       }
-    }
-    if (t0 > tile_lo)  // the first sub-tile's counts were cleared at the start
-      for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
-    __syncthreads();
-
-    int ex[KC], rk[KC];  // per chunk: this lane's expert (or -1) and its rank in the wave
-    Mask mask = 0;       // rank set of token ti (lanes < kTokW)
-    const int ti = wave * kTokW + lane;  // this lane's token in the sub-tile (lanes < kTokW)
-    const bool tok_lane = lane < kTokW && ti < nt;
-    if (ranker) {
-      // All of the wave's ids first (one LDS wait), then the matches, then the
-      // running-count atomics in chunk order, then the leaders' old counts.
-      int own[KR];  // ids of token ti, for its rank set
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch) {
-        if (ch < nch) {
-          const bool mine = ch * kWave + lane < kTokW * k;  // past it: the next wave's pairs
-          ex[ch] = mine ? s_pack[wave * kTokW * k + ch * kWave + lane] : -1;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < KR; ++j)
-        if (j < k) own[j] = tok_lane ? s_pack[ti * k + j] : -1;
-      int lead[KC], grp[KC];
-      uint64_t peers[KC];  // lanes of the chunk holding the same expert
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch) {
-        if (ch < nch) {
-          const bool valid = uint32_t(ex[ch]) < uint32_t(g.E);
-          bad_id |= (ex[ch] != -1) && !valid;
-          ex[ch] = valid ? ex[ch] : -1;
-          peers[ch] = __ballot(valid);
-        }
-      }
-      if (g.lds_match) {
-        // Through the wave's own LDS tables, one chunk after the other: each
-        // lane writes its lane number at its expert's byte and reads it back,
-        // which gives every lane of a group the same member of it (whichever
-        // write landed last); each lane then sets its bit in that member's
-        // mask and reads the mask. The wave's LDS operations take effect in
-        // issue order; atomic loads and stores keep the compiler from
-        // forwarding a lane's own write to its read.
-        uint8_t* rep_w = s_rep + wave * g.e_pad;
-        uint64_t* peer_w = s_peer + wave * kWave;
+      if (t0 > tile_lo)  // the first sub-tile's counts were cleared at the start
+        for (int c = tid; c < kOwnWaves * g.ncols; c += kLayoutThreads) s_cnt[c] = 0;
+      __syncthreads();
+      if (ranker) {
+        const bool tok_lane = lane < kTokW && ti < nt;
 #pragma unroll
         for (int ch = 0; ch < KC; ++ch) {
           if (ch < nch) {
-            const bool on = ex[ch] >= 0;
-            int rep = lane;
-            uint64_t pm = 0;
-            if (on) {
-              __hip_atomic_store(rep_w + ex[ch], uint8_t(lane), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
-              rep = __hip_atomic_load(rep_w + ex[ch], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WAVEFRONT);
-              __hip_atomic_store(peer_w + rep, uint64_t(0), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
-              __hip_atomic_fetch_or(peer_w + rep, uint64_t(1) << lane, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_WAVEFRONT);
-              pm = __hip_atomic_load(peer_w + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-            }
-            peers[ch] = pm;
+            const bool mine = ch * kWave + lane < kTokW * k;  // past it: the next wave's pairs
+            ex[ch] = mine ? s_pack[wave * kTokW * k + ch * kWave + lane] : -1;
           }
         }
-      } else {
-        // One ballot per id bit, all chunks side by side (independent chains).
-        for (int b = 0; b < ebits; ++b) {
 #pragma unroll
-          for (int ch = 0; ch < KC; ++ch) {
-            if (ch < nch) {
-              const bool bit = (ex[ch] >> b) & 1;
-              const uint64_t ones = __ballot(ex[ch] >= 0 && bit);
-              peers[ch] &= bit ? ones : ~ones;
-            }
-          }
-        }
+        for (int j = 0; j < KR; ++j)
+          if (j < k) own[j] = tok_lane ? s_pack[ti * k + j] : -1;
+        rank_in_wave();
       }
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch) {
-        if (ch < nch) {
-          rk[ch] = __popcll(peers[ch] & lanes_below());
-          lead[ch] = ex[ch] >= 0 ? __ffsll((unsigned long long)peers[ch]) - 1 : lane;
-          grp[ch] = __popcll(peers[ch]);
-        }
-      }
-      int cnt_old[KC];
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch) {
-        if (ch < nch) {
-          cnt_old[ch] = 0;
-          if (ex[ch] >= 0 && rk[ch] == 0) cnt_old[ch] = atomicAdd(&cnt_w[ex[ch]], grp[ch]);
-        }
-      }
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch)
-        if (ch < nch) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
-#pragma unroll
-      for (int j = 0; j < KR; ++j)
-        if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
-      const int copies = wave_rank_counts<kRB>(mask, g.R);  // lane r: tokens with a copy on r
-      if (lane < g.R) cnt_w[g.E + lane] = copies;
-    }
-    __syncthreads();
-
-    // Per column: each ranking wave's first row, then advance the running base.
-    for (int c = tid; c < g.ncols; c += kLayoutThreads) {
-      int v[kOwnWaves];  // all reads first: one LDS round trip, not one per wave
-#pragma unroll
-      for (int w = 0; w < kOwnWaves; ++w) v[w] = s_cnt[w * g.ncols + c];
-      int run = s_pre[c];
-#pragma unroll
-      for (int w = 0; w < kOwnWaves; ++w) {
-        s_cnt[w * g.ncols + c] = run;
-        run += v[w];
-      }
-      s_pre[c] = run;
-    }
-    __syncthreads();
-
-    if (ranker) {
-#pragma unroll
-      for (int ch = 0; ch < KC; ++ch) {
-        if (ch < nch) {
-          const int pl = wave * kTokW * k + ch * kWave + lane;
-          if (ch * kWave + lane < kTokW * k && pl < npairs) {
-            int row = ex[ch] >= 0 ? cnt_w[ex[ch]] + rk[ch] : -1;
-            if (g.block > 0 && row >= (ex[ch] + 1) * g.block) {
-              row = -1;
-              full_block = true;
-            }
-            pair_row[(int64_t)t0 * k + pl] = row;
-          }
-        }
-      }
-      auto write_slot = [&](int r) {
-        const uint64_t on = __ballot((mask >> r) & 1);
-        if (tok_lane)
-          token_rank_slot[(int64_t)(t0 + ti) * g.R + r] =
-              ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
-      };
-      if (kRB == 8) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          if (r < g.R) write_slot(r);
-      } else {
-        for (int r = 0; r < g.R; ++r) write_slot(r);
-      }
+      __syncthreads();
+      chain_columns();
+      __syncthreads();
+      if (ranker) write_rows(t0, nt);
     }
   }
   if (__ballot(bad_id) && lane == 0) flag_error(err_word, MOE_ERRBIT_BAD_ID);
