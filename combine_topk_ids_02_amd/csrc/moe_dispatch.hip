@@ -302,7 +302,7 @@ __device__ __forceinline__ void load_tokens(const int32_t* __restrict__ ids, int
 // Every entry a later read uses is written, so the workspace needs no
 // clearing between calls.
 constexpr int kCountThreads = 256;
-constexpr int64_t kTwoLaunchMinIds = 24576;  // ids above which the two-launch layout is used
+constexpr int64_t kTwoLaunchMinIds = 65536;  // ids above which the two-launch layout is used
 
 template <int K, int kRB>
 __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
@@ -1663,9 +1663,10 @@ int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32
   const LayoutGeom g = layout_geometry(*shape);
   const size_t need = layout_workspace_bytes(g);
   if (workspace && (workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_ARG;
-  // Two launches pay about 5 us more in fixed cost; one launch counts all
-  // T*k ids in every workgroup. Measured on MI355X, they break even near
-  // 24,576 ids (T = 4096, k = 6), so the tile counts are used above that.
+  // Two launches pay about 3 us more in fixed cost; one launch counts all
+  // T*k ids in every workgroup. Measured on MI355X (calls back to back), they
+  // break even between 65,536 and 81,920 ids (k = 6 and k = 8), so the tile
+  // counts are used above 65,536.
   const bool big = int64_t(shape->T) * shape->k > kTwoLaunchMinIds;
   const bool two = need > 0 && workspace && (g_layout_form < 0 ? big : g_layout_form == 1);
   LayoutArgs a{topk_ids, rank_counts, rank_offsets, expert_counts, expert_offsets,
