@@ -302,7 +302,7 @@ __device__ __forceinline__ void load_tokens(const int32_t* __restrict__ ids, int
 // Every entry a later read uses is written, so the workspace needs no
 // clearing between calls.
 constexpr int kCountThreads = 256;
-constexpr int64_t kTwoLaunchMinIds = 65536;  // ids above which the two-launch layout is used
+constexpr int64_t kTwoLaunchMinIds = 49152;  // ids above which the two-launch layout is used
 
 template <int K, int kRB>
 __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
@@ -1665,8 +1665,10 @@ int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32
   if (workspace && (workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_ARG;
   // Two launches pay about 3 us more in fixed cost; one launch counts all
   // T*k ids in every workgroup. Measured on MI355X (calls back to back), they
-  // break even between 65,536 and 81,920 ids (k = 6 and k = 8), so the tile
-  // counts are used above 65,536.
+  // break even between 65,536 and 81,920 ids (k = 6 and k = 8) for uniform
+  // routing, but with a few hot experts (most lanes of a counting atomic on
+  // one address) one launch loses much earlier: 23.5 against 17.6 us at
+  // 65,536 ids. The tile counts are used above 49,152 ids.
   const bool big = int64_t(shape->T) * shape->k > kTwoLaunchMinIds;
   const bool two = need > 0 && workspace && (g_layout_form < 0 ? big : g_layout_form == 1);
   LayoutArgs a{topk_ids, rank_counts, rank_offsets, expert_counts, expert_offsets,

@@ -124,7 +124,7 @@ const char* moe_status_string(int status);
  *   err_word: device int32 or NULL (MOE_ERRBIT_BAD_ID; MOE_ERRBIT_EXPERT_CAP when a
  *             pair finds its fixed block full)
  * The tokens are cut into at most 64 tiles of a multiple of 256 tokens. With a
- * workspace, more than one tile and more than 65,536 (token, slot) pairs, two
+ * workspace, more than one tile and more than 49,152 (token, slot) pairs, two
  * kernel launches: per-tile counts into the workspace, then one workgroup per
  * tile scans them and ranks its tile. Otherwise one launch in which every
  * workgroup counts all tokens itself (cheaper for small T, slower for large). Either way the result is a
