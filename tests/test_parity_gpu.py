@@ -192,7 +192,10 @@ def test_layout_without_workspace(name, case):
 
 LAYOUT_FORMS = [(0, "prefill"), (1, "prefill"), (1, "decode"), (0, "adv"), (1, "skew"),
                 (1, (70000, 16, 64, 8, 5, 0.05, 0.0, 12)), (1, (2000, 64, 1024, 64, 16, 0.02, 0.02, 9)),
-                (1, (257, 512, 16, 4, 2, 0.1, 0.0, 4))]
+                (1, (257, 512, 16, 4, 2, 0.1, 0.0, 4)),
+                # one launch with several sub-tiles per workgroup (T above 64 tiles of 256),
+                # the last tile ragged
+                (0, (70000, 16, 64, 8, 5, 0.05, 0.0, 12)), (0, (20000, 8, 384, 8, 6, 0.0, 0.05, 14))]
 
 
 @pytest.mark.parametrize("match", [1, 0], ids=["lds_match", "ballot_match"])
