@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int lane = lane_id();
   const int tile_lo = blockIdx.x * g.tile_tokens;
   const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
-  // A tile of one sub-tile (every tile up to 64 * kOwnTokens tokens) is
+  // A tile of one sub-tile (every tile when T <= kMaxTiles * kOwnTokens) is
   // ranked before the counts are known: its ranking waves take their ids
   // straight from memory and work out the ranks inside the tile while the
   // counting runs; only the final rows wait for the scan. Larger tiles rank
