@@ -640,7 +640,22 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
               tmask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
             }
           }
-          c += wave_rank_counts<kRB>(tmask, g.R);
+          if (kRB == 8) {
+            c += wave_rank_counts<kRB>(tmask, g.R);
+          } else {
+            // Wider rank sets: one LDS atomic per rank of the token (at most
+            // k per token rather than R ballots per 64 tokens). The per-lane
+            // selection of ballot counts (wave_rank_counts) gave wrong copies
+            // per rank here for k = 4 with R > 32, reproducibly on MI355X
+            // though not on every call, while the same ballots added by one
+            // lane, or these atomics, gave the right ones.
+            Mask mm = tmask;
+            while (mm) {
+              const int r = __ffsll((unsigned long long)mm) - 1;
+              mm &= mm - 1;
+              atomicAdd(&cnt[g.E + r], 1);
+            }
+          }
         }
         (before ? rc_pre : rc_tot) += c;
       }

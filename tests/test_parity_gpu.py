@@ -250,3 +250,38 @@ def test_timing_hook_brackets_the_next_kernel():
     # used once: the next run records nothing into the pair
     run_gpu(hid, ids, wts, w.E, w.R, y)
     assert a.elapsed_time(b) == first
+
+
+WIDE_RANK_SETS = [(1024, 512, 64, 4), (4096, 480, 48, 4), (8192, 64, 64, 4), (12288, 1024, 64, 4),
+                  (3000, 640, 40, 5), (2048, 512, 64, 6)]
+
+
+@pytest.mark.parametrize("case", WIDE_RANK_SETS, ids=[f"T{c[0]}_E{c[1]}_R{c[2]}_k{c[3]}"
+                                                      for c in WIDE_RANK_SETS])
+def test_layout_wide_rank_sets_repeated(case):
+    """One-launch layout with more than 32 ranks (64-bit rank sets), forced
+    and chosen by size, three calls in a row on the same ids: every call gives
+    the oracle's counts, offsets and rows. (The copies per rank once came out
+    wrong for k = 4 with R > 32 in this form, on most calls but not all.)"""
+    import combine_topk_ids_02_amd as moe
+    T, E, R, k = case
+    say(f"[wide rank sets] T={T} E={E} R={R} k={k}")
+    rng = np.random.default_rng(T + E + R + k)
+    ids = pins.rand_ids(rng, T, E, k)
+    ref = oracle.layout(ids, E, R)
+    ids_d = torch.from_numpy(ids).to("cuda:0")
+    shape = moe.Shape(T, 8, E, R, k)
+    ws = moe.layout_workspace_bytes(shape)
+    workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=torch.int32, device="cuda:0") if ws else None
+    for form in (0, -1):
+        old = moe.lib().moe_testing_set_layout_form(form)
+        try:
+            for call in range(3):
+                got = moe.layout(ids_d, E, R, 8, workspace=workspace if form == 0 else None)
+                torch.cuda.synchronize()
+                for key in ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
+                            "token_rank_slot", "pair_row"):
+                    assert np.array_equal(got[key].cpu().numpy(), ref[key]), \
+                        f"{case} form {form} call {call}: {key} differs"
+        finally:
+            moe.lib().moe_testing_set_layout_form(old)
