@@ -656,6 +656,11 @@ def main():
                    "bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "calls": call_stats,
+        "rows_per_s": {
+            "step_tokens": round(w.T / (ms_per_step * 1e-3)),
+            "pack_copies": round(rig.C / (call_stats["pack"]["us"] * 1e-6)),
+            "permute_pairs": round(rig.P / (call_stats["permute"]["us"] * 1e-6)),
+            "combine_tokens": round(w.T / (call_stats["combine"]["us"] * 1e-6))},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
