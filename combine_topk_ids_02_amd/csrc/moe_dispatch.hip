@@ -1153,12 +1153,15 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
     mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
     return;
   }
-  const int64_t i = gw - pad_waves;  // < cap_rank: rank_src_token[i] is in bounds
+  const int64_t i = gw - pad_waves;
   // Two rounds of loads: the offsets and the row's token, then the token's
-  // ids and pair rows with the row itself right behind them.
+  // ids and pair rows with the row itself right behind them. The grid is
+  // rounded up to whole workgroups, so i can pass the last row: the token's
+  // load is clamped into the buffer and such waves return below.
   const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
   const int end_any = rank_offsets[min(lane, R - 1) + 1];
-  const int t = rank_src_token[i];
+  const int64_t ic = min(i, cap_rank - 1);
+  const int t = ic >= 0 ? rank_src_token[ic] : -1;
   const int end = lane < R ? end_any : 0x7FFFFFFF;
   if (i >= rows || t < 0 || t >= T) return;
   const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
@@ -1336,11 +1339,13 @@ __global__ __launch_bounds__(kBlock) void rank_partial_rows(
   const int64_t i = gw / slices;
   const int slice = int(gw - i * slices);
   // Two rounds of index loads, as in the permute: the offsets and the row's
-  // token (i < cap_rank, so rank_src_token[i] is in bounds), then the
-  // token's ids, pair rows and weights (unconditional, clamped lanes).
+  // token (clamped into the buffer: the rounded-up grid can pass the last
+  // row, and those waves return below), then the token's ids, pair rows and
+  // weights (unconditional, clamped lanes).
   const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
   const int end_any = rank_offsets[min(lane, R - 1) + 1];
-  const int t = rank_src_token[i];
+  const int64_t ic = min(i, cap_rank - 1);
+  const int t = ic >= 0 ? rank_src_token[ic] : -1;
   if (i >= rows || t < 0 || t >= T) return;
   const int64_t at = (int64_t)t * k + min(lane, k - 1);
   const int e_any = ids[at];
