@@ -124,6 +124,26 @@ def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: torch.Tensor | None, name: str, shape: tuple | None = None,
+          min_numel: int | None = None) -> None:
+    """Checks a tensor against the shape of the call before its pointer goes to
+    the library, which cannot see buffer lengths: `shape` exactly, or at least
+    `min_numel` elements. Raises MoeError."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{name} has shape {tuple(t.shape)}, the call needs {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise MoeError(f"{name} has {t.numel()} elements, the call needs at least {min_numel}")
+
+
+def _rows(t: torch.Tensor, name: str, width: int) -> int:
+    """Rows of a row buffer [rows, width]; raises MoeError on another width."""
+    if t.dim() != 2 or t.shape[1] != width:
+        raise MoeError(f"{name} has shape {tuple(t.shape)}, the call needs [rows, {width}]")
+    return t.shape[0]
+
+
 def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -180,6 +200,11 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1
     T, k = topk_ids.shape
     dev = topk_ids.device
     shape = Shape(T, H, E, R, k, align, block)
+    if out is not None:
+        for key, want in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
+                          ("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                          ("token_rank_slot", (T, R)), ("pair_row", (T, k))):
+            _need(out[key], key, want)
     if out is None:
         out = dict(
             rank_counts=torch.empty(R, dtype=torch.int32, device=dev),
@@ -205,6 +230,9 @@ def pack(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, ra
     rank_src_token [cap_rank]."""
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
+    _need(token_rank_slot, "token_rank_slot", (T, R))
+    cap = _rows(rank_buf, "rank_buf", H)
+    _need(rank_src_token, "rank_src_token", min_numel=cap)
     shape = Shape(T, H, E, R, k)
     st = lib().moe_dispatch_pack(
         ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
@@ -222,6 +250,13 @@ def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, 
     T, k = topk_ids.shape
     H = rank_buf.shape[1]
     R = rank_offsets.shape[0] - 1
+    _need(pair_row, "pair_row", (T, k))
+    cap_r = _rows(rank_buf, "rank_buf", H)
+    _need(rank_src_token, "rank_src_token", min_numel=cap_r)
+    cap_e = _rows(expert_buf, "expert_buf", H)
+    _need(expert_src_pair, "expert_src_pair", min_numel=cap_e)
+    _need(expert_counts, "expert_counts", (E,))
+    _need(expert_offsets, "expert_offsets", (E + 1,))
     shape = Shape(T, H, E, R, k, align, block)
     st = lib().moe_permute_by_expert(
         ctypes.byref(shape.c()), _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)),
@@ -246,6 +281,10 @@ def pack_mx(bits: int, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: i
     (uint8 codes) and rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
+    _need(token_rank_slot, "token_rank_slot", (T, R))
+    cap = _rows(rank_q, "rank_q", H * bits // 8)
+    _need(rank_scale, "rank_scale", (cap, H // 32))
+    _need(rank_src_token, "rank_src_token", min_numel=cap)
     shape = Shape(T, H, E, R, k)
     fn = lib().moe_dispatch_pack_mxfp8 if bits == 8 else lib().moe_dispatch_pack_mxfp4
     st = fn(ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
@@ -270,6 +309,15 @@ def permute_mx(bits: int, rank_q, rank_scale, rank_src_token, rank_offsets, topk
     T, k = topk_ids.shape
     H = rank_q.shape[1] * 8 // bits
     R = rank_offsets.shape[0] - 1
+    _need(pair_row, "pair_row", (T, k))
+    cap_r = rank_q.shape[0]
+    _need(rank_scale, "rank_scale", (cap_r, H // 32))
+    _need(rank_src_token, "rank_src_token", min_numel=cap_r)
+    cap_e = _rows(expert_q, "expert_q", rank_q.shape[1])
+    _need(expert_scale, "expert_scale", (cap_e, H // 32))
+    _need(expert_src_pair, "expert_src_pair", min_numel=cap_e)
+    _need(expert_counts, "expert_counts", (E,))
+    _need(expert_offsets, "expert_offsets", (E + 1,))
     shape = Shape(T, H, E, R, k, align, block)
     fn = lib().moe_permute_by_expert_mxfp8 if bits == 8 else lib().moe_permute_by_expert_mxfp4
     st = fn(ctypes.byref(shape.c()), _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)),
@@ -298,6 +346,10 @@ def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=
         raise MoeError("topk_weights must be float32")
     if out_f32 is not None and out_f32.dtype != torch.float32:
         raise MoeError("out_f32 must be float32")
+    _need(topk_weights, "topk_weights", (T, k))
+    _need(out, "out", (T, H))
+    _need(out_f32, "out_f32", (T, H))
+    _rows(expert_out, "expert_out", H)
     shape = Shape(T, H, E, R, k)
     st = lib().moe_combine(
         ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(pair_row)),
@@ -317,6 +369,12 @@ def combine_rank_partial(expert_out, rank_src_token, rank_offsets, topk_ids, pai
         raise MoeError("topk_weights must be float32")
     if partial_f32 is not None and partial_f32.dtype != torch.float32:
         raise MoeError("partial_f32 must be float32")
+    _need(pair_row, "pair_row", (T, k))
+    _need(topk_weights, "topk_weights", (T, k))
+    cap_r = _rows(partial, "partial", H)
+    _need(partial_f32, "partial_f32", (cap_r, H))
+    _need(rank_src_token, "rank_src_token", min_numel=cap_r)
+    _rows(expert_out, "expert_out", H)
     shape = Shape(T, H, E, R, k)
     st = lib().moe_combine_rank_partial(
         ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(rank_src_token)),
@@ -333,6 +391,9 @@ def combine_ranks(partial, token_rank_slot, E: int, k: int, out, *, out_f32=None
     H = out.shape[1]
     if out_f32 is not None and out_f32.dtype != torch.float32:
         raise MoeError("out_f32 must be float32")
+    _need(out, "out", (T, H))
+    _need(out_f32, "out_f32", (T, H))
+    _rows(partial, "partial", H)
     shape = Shape(T, H, E, R, k)
     st = lib().moe_combine_ranks(
         ctypes.byref(shape.c()), _ptr(_rows16(partial)), _ptr(_i32(token_rank_slot)),

@@ -164,3 +164,58 @@ def test_status_strings():
     L = moe.lib()
     assert L.moe_status_string(0) == b"ok"
     assert b"argument" in L.moe_status_string(-1)
+
+
+def _z(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rejects_tensors_that_do_not_fit_the_call():
+    """The library cannot see buffer lengths: the binding checks every tensor
+    against the call's shape and raises before any pointer reaches it (host
+    tensors here, so nothing could run even if a check were missing)."""
+    import torch
+    i32, i16, u8, f32 = torch.int32, torch.int16, torch.uint8, torch.float32
+    T, H, E, R, k, cap = 8, 16, 8, 2, 2, 16
+    hid = _z((T, H), torch.bfloat16)
+    slots = _z((T, R), i32)
+    ids = _z((T, k), i32)
+    offs = _z((R + 1,), i32)
+    cases = [
+        ("token_rank_slot", lambda: moe.pack(hid, _z((T - 1, R), i32), E, k, _z((cap, H), i16),
+                                             _z((cap,), i32))),
+        ("rank_buf", lambda: moe.pack(hid, slots, E, k, _z((cap, H // 2), i16), _z((cap,), i32))),
+        ("rank_src_token", lambda: moe.pack(hid, slots, E, k, _z((cap, H), i16),
+                                            _z((cap - 1,), i32))),
+        ("pair_row", lambda: moe.permute(_z((cap, H), i16), _z((cap,), i32), offs, ids,
+                                         _z((T, k + 1), i32), E, _z((cap, H), i16),
+                                         _z((cap,), i32))),
+        ("expert_src_pair", lambda: moe.permute(_z((cap, H), i16), _z((cap,), i32), offs, ids,
+                                                _z((T, k), i32), E, _z((cap, H), i16),
+                                                _z((cap - 3,), i32))),
+        ("expert_offsets", lambda: moe.permute(_z((cap, H), i16), _z((cap,), i32), offs, ids,
+                                               _z((T, k), i32), E, _z((cap, H), i16),
+                                               _z((cap,), i32), expert_counts=_z((E,), i32),
+                                               expert_offsets=_z((E,), i32), align=2)),
+        ("topk_weights", lambda: moe.combine(_z((cap, H), i16), ids, _z((T, k - 1), f32), E, R,
+                                             _z((T, H), i16))),
+        ("out_f32", lambda: moe.combine(_z((cap, H), i16), ids, _z((T, k), f32), E, R,
+                                        _z((T, H), i16), out_f32=_z((T, H // 2), f32))),
+        ("expert_out", lambda: moe.combine(_z((cap, H * 2), i16), ids, _z((T, k), f32), E, R,
+                                           _z((T, H), i16))),
+        ("partial_f32", lambda: moe.combine_rank_partial(
+            _z((cap, H), i16), _z((cap,), i32), offs, ids, _z((T, k), i32), _z((T, k), f32), E,
+            _z((cap, H), i16), partial_f32=_z((cap - 1, H), f32))),
+        ("out", lambda: moe.combine_ranks(_z((cap, H), i16), slots, E, k, _z((T + 1, H), i16))),
+        ("rank_scale", lambda: moe.pack_mxfp8(_z((T, 512), torch.bfloat16), slots, E, k,
+                                              _z((cap, 512), u8), _z((cap, 8), u8),
+                                              _z((cap,), i32))),
+        ("pair_row", lambda: moe.layout(ids, E, R, H, out=dict(
+            rank_counts=_z((R,), i32), rank_offsets=_z((R + 1,), i32),
+            expert_counts=_z((E,), i32), expert_offsets=_z((E + 1,), i32),
+            token_rank_slot=_z((T, R), i32), pair_row=_z((T - 2, k), i32)))),
+    ]
+    for name, call in cases:
+        with pytest.raises(moe.MoeError, match=name):
+            call()

@@ -160,8 +160,8 @@ def test_mx_rejects_rows_not_a_multiple_of_512():
     hid = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
     slots = torch.zeros((T, R), dtype=torch.int32, device=dev)
     rq = torch.zeros((8, H), dtype=torch.uint8, device=dev)
-    rs = torch.zeros((8, 32), dtype=torch.uint8, device=dev)
-    src = torch.zeros(8, dtype=torch.int32, device=dev)
+    rs = torch.zeros((8, H // 32), dtype=torch.uint8, device=dev)  # shapes consistent: the
+    src = torch.zeros(8, dtype=torch.int32, device=dev)              # library rejects H itself
     with pytest.raises(moe.MoeError):
         moe.pack_mxfp8(hid, slots, E, k, rq, rs, src)
     with pytest.raises(moe.MoeError):
