@@ -922,13 +922,24 @@ __global__ __launch_bounds__(kBlock) void pack_rows_small(
 }
 
 // Marks the padding rows of expert e (rows of its run or block that no pair
-// fills) with expert_src_pair -1.
+// fills) with expert_src_pair -1. A fixed block is [e*block, (e+1)*block)
+// whatever the offsets say; a padded run is [offsets[e], offsets[e+1]). The
+// counts and offsets are the caller's arguments, so the rows are clipped to
+// [0, cap_expert): a store stays inside the buffer even when they disagree.
 __device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts,
                                              const int32_t* expert_offsets, int block,
                                              int32_t* expert_src_pair, int64_t cap_expert) {
-  const int cnt = expert_counts[e];
-  const int64_t lo = (int64_t)expert_offsets[e] + (block > 0 ? min(cnt, block) : cnt);
-  const int64_t end = block > 0 ? (int64_t)(e + 1) * block : (int64_t)expert_offsets[e + 1];
+  const int64_t cnt = max(0, expert_counts[e]);  // a negative count fills nothing
+  int64_t first, end;
+  if (block > 0) {
+    first = (int64_t)e * block;
+    end = first + block;
+  } else {
+    first = expert_offsets[e];
+    end = expert_offsets[e + 1];
+  }
+  const int64_t filled = block > 0 ? min(cnt, (int64_t)block) : cnt;
+  const int64_t lo = max(first + filled, (int64_t)0);
   const int64_t hi = min(end, cap_expert);
   for (int64_t row = lo + lane_id(); row < hi; row += kWave) expert_src_pair[row] = -1;
 }

@@ -1,0 +1,693 @@
+"""Host-side model of the library's kernel launches, for bounds checking.
+
+For one call sequence (shape, caps, layout form and match), this replays on
+the CPU what the host code of combine_topk_ids_02_amd/csrc/moe_dispatch.hip
+chooses (grids, register tiles, column slices, layout tiles, one or two
+layout launches) and, for every workgroup, wave and lane of every launch, the
+global load and store indices the kernel computes. Indices that depend on
+data (slots, pair rows, source tokens, offsets, counts) are taken from the
+oracle's layout, which the GPU layout equals wherever parity holds. Every
+index is checked against the size of the buffer it addresses, as the C ABI
+states that size (cap_rank rows, cap_expert rows, T rows, the workspace size
+the library asks for): spare rows a test harness may add are not counted.
+
+The model is a transcription of the kernels' index arithmetic, kept beside
+them; loads that the kernels issue unconditionally (clamped addresses) are
+modelled unconditionally. It models global memory only. The layout's LDS
+regions are checked separately (layout_lds_regions): each region's largest
+index against the region's size, and the regions against the allocation.
+
+Test infrastructure: it never runs a kernel and shares no code with the
+library or the oracle; it only calls the oracle for the layout's values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+
+W = 64                  # lanes per wave
+BLOCK = 256             # row movers: threads per workgroup
+WPB = BLOCK // W
+MAX_TILES = 64
+OWN_TOKENS = 256
+OWN_WAVES = 8
+TOK_W = OWN_TOKENS // OWN_WAVES
+LAYOUT_THREADS = 1024
+BATCH_VECS = 8
+MAX_K = 16
+MAX_VEC = 16
+LDS_LIMIT = 64 * 1024 - 256
+TWO_LAUNCH_MIN_IDS = 49152
+COUNT_THREADS = 256
+FILL_TOKENS = 1024
+COMBINE_GROUPS = 8
+PARTIAL_GROUPS = 3
+RANK_SUM_GROUPS = 1
+INT32_MAX = 2 ** 31 - 1
+LANE = np.arange(W, dtype=np.int64)
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def blocks_for(waves: int) -> int:
+    return cdiv(waves, WPB)
+
+
+def copy_vec(nvec: int) -> int:
+    groups = nvec // W
+    if groups <= 1:
+        return 1
+    if groups <= MAX_VEC:
+        return groups
+    for v in range(MAX_VEC, 7, -1):
+        if groups % v == 0:
+            return v
+    return MAX_VEC
+
+
+def combine_tiling(nvec: int, rows: int, most: int):
+    groups = max(1, cdiv(nvec, W))
+    g = most
+    while g < 8 and rows * cdiv(groups, g) > INT32_MAX:
+        g += 1
+    slices = cdiv(groups, g)
+    return cdiv(groups, slices), slices  # (v, slices)
+
+
+def mx_passes(npass: int, most: int) -> int:
+    for v in range(min(npass, most), 1, -1):
+        if npass % v == 0:
+            return v
+    return 1
+
+
+def layout_lds_bytes(k, ncols):
+    return 4 * (OWN_TOKENS * k + (OWN_WAVES + 2) * ncols + 2)
+
+
+def layout_match_lds_bytes(k, E, R):
+    return layout_lds_bytes(k, E + R) + OWN_WAVES * (8 * W + cdiv(E, 4) * 4)
+
+
+@dataclass
+class Case:
+    T: int
+    H: int
+    E: int
+    R: int
+    k: int
+    align: int = 1
+    block: int = 0
+    form: int = -1          # layout form forced by the testing hook (-1: by size)
+    match: int = 1          # 0: ballot match forced
+    workspace: bool = True  # a workspace is passed to the layout
+    cap_rank: int | None = None
+    cap_expert: int | None = None
+
+    def __post_init__(self):
+        if self.cap_rank is None:
+            self.cap_rank = self.T * min(self.k, self.R)
+        if self.cap_expert is None:
+            self.cap_expert = (self.E * self.block if self.block > 0
+                               else self.T * self.k + self.E * (self.align - 1))
+
+    @property
+    def nvec(self):
+        return self.H // 8
+
+
+@dataclass
+class Report:
+    sizes: dict = field(default_factory=dict)
+    violations: list = field(default_factory=list)
+    counted: int = 0
+
+    def buf(self, name, n):
+        self.sizes[name] = int(n)
+
+    def access(self, kernel, name, idx, kind):
+        idx = np.asarray(idx, dtype=np.int64).ravel()
+        if idx.size == 0:
+            return
+        self.counted += idx.size
+        lo, hi = int(idx.min()), int(idx.max())
+        n = self.sizes[name]
+        if lo < 0 or hi >= n:
+            self.violations.append(f"{kernel}: {kind} {name}[{lo}..{hi}] outside [0, {n})")
+
+
+# ----------------------------------------------------------------------------
+# layout
+
+@dataclass
+class LayoutGeom:
+    T: int
+    E: int
+    R: int
+    k: int
+    align: int
+    block: int
+    ncols: int
+    tile_tokens: int
+    ntiles: int
+    tiles_pad: int
+    lds_match: int
+    e_pad: int
+    two: bool
+
+
+def layout_geometry(c: Case) -> LayoutGeom:
+    subs = cdiv(c.T, OWN_TOKENS)
+    per_tile = max(1, cdiv(subs, MAX_TILES))
+    tile_tokens = per_tile * OWN_TOKENS
+    ntiles = max(1, cdiv(c.T, tile_tokens))
+    tiles_pad = cdiv(ntiles, 4) * 4
+    ncols = c.E + c.R
+    lds_match = int(c.match != 0 and layout_match_lds_bytes(c.k, c.E, c.R) <= LDS_LIMIT)
+    need = 4 * tiles_pad * ncols if ntiles > 1 else 0
+    big = c.T * c.k > TWO_LAUNCH_MIN_IDS
+    two = need > 0 and c.workspace and (big if c.form < 0 else c.form == 1)
+    return LayoutGeom(c.T, c.E, c.R, c.k, c.align, c.block, ncols, tile_tokens, ntiles,
+                      tiles_pad, lds_match, cdiv(c.E, 4) * 4, two)
+
+
+def workspace_ints(g: LayoutGeom) -> int:
+    return g.tiles_pad * g.ncols if g.ntiles > 1 else 0
+
+
+def id_lanes(K: int):
+    """(TPL, VPL, NQ, NW, BATCH) of the counting pass for compile-time k = K."""
+    if K == 0:
+        return 1, 0, 1, MAX_K, LAYOUT_THREADS
+    tpl = 1 if K % 4 == 0 else (2 if K % 2 == 0 else 4)
+    vpl = K * tpl // 4
+    nq = BATCH_VECS // vpl if BATCH_VECS // vpl > 0 else 1
+    return tpl, vpl, nq, nq * vpl * 4, LAYOUT_THREADS * tpl * nq
+
+
+def compiled_k(k: int) -> int:
+    return k if k in (1, 2, 3, 4, 5, 6, 8) else 0
+
+
+def model_layout(c: Case, rep: Report) -> LayoutGeom:
+    g = layout_geometry(c)
+    T, k, R, E = c.T, c.k, c.R, c.E
+    K = compiled_k(k)
+    rep.buf("topk_ids", T * k)
+    rep.buf("rank_counts", R)
+    rep.buf("rank_offsets", R + 1)
+    rep.buf("expert_counts", E)
+    rep.buf("expert_offsets", E + 1)
+    rep.buf("token_rank_slot", T * R)
+    rep.buf("pair_row", T * k)
+    rep.buf("workspace", workspace_ints(g))
+    n_ids = T * k
+    tid = np.arange(LAYOUT_THREADS, dtype=np.int64)
+    wave, lane = tid // W, tid % W
+    ranker = wave < OWN_WAVES
+    ti = wave * TOK_W + lane
+    KR = K if K > 0 else MAX_K
+    KC = cdiv(TOK_W * KR, W)
+    nch = cdiv(TOK_W * k, W)
+    early = g.tile_tokens == OWN_TOKENS
+
+    if g.two:  # layout_count: one workgroup of 256 threads per tile
+        for b in range(g.ntiles):
+            tile_lo = b * g.tile_tokens
+            tile_hi = min(T, tile_lo + g.tile_tokens)
+            for t0 in range(tile_lo, tile_hi, COUNT_THREADS):
+                t = t0 + np.arange(COUNT_THREADS, dtype=np.int64)
+                t = t[t < tile_hi]
+                j = np.arange(k, dtype=np.int64)
+                rep.access("layout_count", "topk_ids", (t[:, None] * k + j[None, :]), "load")
+            col = np.arange(g.ncols, dtype=np.int64)
+            rep.access("layout_count", "workspace", col * g.tiles_pad + b, "store")
+
+    tpl, vpl, nq, nw, batch = id_lanes(K)
+    for b in range(g.ntiles):
+        tile_lo = b * g.tile_tokens
+        tile_hi = min(T, tile_lo + g.tile_tokens)
+        kname = "layout_tiles"
+        if early:
+            pair0 = tile_lo * k
+            npairs = max(0, tile_hi - tile_lo) * k
+            for ch in range(KC):
+                if ch >= nch:
+                    continue
+                f = wave * TOK_W * k + ch * W + lane
+                mine = ranker & (ch * W + lane < TOK_W * k) & (f < npairs)
+                rep.access(kname, "topk_ids", pair0 + f[mine], "load")
+            tok = ranker & (lane < TOK_W) & (tile_lo + ti < tile_hi)
+            for j in range(k):
+                rep.access(kname, "topk_ids", (tile_lo + ti[tok]) * k + j, "load")
+        if not g.two:
+            # counting pass: the first batch, then a prefetch of each next one
+            b0s = [0] + [b0 + batch for b0 in range(0, T, batch) if b0 + batch < T]
+            for b0 in b0s:
+                if K > 0:
+                    for q in range(nq):
+                        f0 = (b0 + (q * LAYOUT_THREADS + tid) * tpl) * K
+                        for i in range(vpl):
+                            f = f0 + 4 * i
+                            vec = f + 4 <= n_ids
+                            for x in range(4):
+                                rep.access(kname, "topk_ids", f[vec] + x, "load")
+                                sc = ~vec & (f + x < n_ids)
+                                rep.access(kname, "topk_ids", f[sc] + x, "load")
+                else:
+                    t = b0 + tid
+                    for j in range(k):
+                        rep.access(kname, "topk_ids", t[t < T] * k + j, "load")
+        else:
+            groups = g.tiles_pad // 4
+            col = np.arange(g.ncols, dtype=np.int64)
+            for q in range(groups):
+                for x in range(4):
+                    rep.access(kname, "workspace", col * g.tiles_pad + 4 * q + x, "load")
+        if b == 0:  # the writer workgroup
+            rep.access(kname, "expert_counts", np.arange(E), "store")
+            rep.access(kname, "expert_offsets", np.arange(E + 1), "store")
+            rep.access(kname, "rank_counts", LANE[LANE < R], "store")
+            rep.access(kname, "rank_offsets", LANE[LANE < R], "store")
+            rep.access(kname, "rank_offsets", [R], "store")
+        subtiles = [(tile_lo, max(0, tile_hi - tile_lo))] if early else \
+            [(t0, min(OWN_TOKENS, tile_hi - t0)) for t0 in range(tile_lo, tile_hi, OWN_TOKENS)]
+        for t0, nt in subtiles:
+            npairs = nt * k
+            if not early:
+                f = np.arange(OWN_TOKENS * k, dtype=np.int64)
+                rep.access(kname, "topk_ids", t0 * k + f[f < npairs], "load")
+            for ch in range(KC):
+                if ch >= nch:
+                    continue
+                pl = wave * TOK_W * k + ch * W + lane
+                wr = ranker & (ch * W + lane < TOK_W * k) & (pl < npairs)
+                rep.access(kname, "pair_row", t0 * k + pl[wr], "store")
+            tok = ranker & (lane < TOK_W) & (ti < nt)
+            for r in range(R):
+                rep.access(kname, "token_rank_slot", (t0 + ti[tok]) * R + r, "store")
+    return g
+
+
+def layout_lds_regions(c: Case) -> list[str]:
+    """The layout workgroup's LDS regions (int32 units, as the kernel carves
+    them out of its dynamic allocation) and the largest index each use takes.
+    Returns the problems found (empty: every use fits its region and every
+    region fits the allocation, which fits the 64 KiB a workgroup may have)."""
+    g = layout_geometry(c)
+    k = c.k
+    problems = []
+    alloc = layout_match_lds_bytes(k, c.E, c.R) if g.lds_match else layout_lds_bytes(k, g.ncols)
+    if alloc > LDS_LIMIT or alloc + 64 > 64 * 1024:
+        problems.append(f"allocation {alloc} B over the limit")
+    peer = OWN_WAVES * W * 2 if g.lds_match else 0          # u64 [8][64] as int32
+    regions = {
+        "s_pack": (peer, OWN_TOKENS * k),
+        "s_cnt": (peer + OWN_TOKENS * k, OWN_WAVES * g.ncols),
+        "s_pre": (peer + OWN_TOKENS * k + OWN_WAVES * g.ncols, g.ncols + 1),
+        "s_tot": (peer + OWN_TOKENS * k + (OWN_WAVES + 1) * g.ncols + 1, g.ncols + 1),
+    }
+    rep_base = 4 * (peer + OWN_TOKENS * k + (OWN_WAVES + 2) * g.ncols + 2)  # bytes
+    # largest index per use: s_cnt[wave * ncols + e or E + r], s_pre/s_tot[c <= ncols]
+    uses = {"s_pack": OWN_TOKENS * k - 1,
+            "s_cnt": (OWN_WAVES - 1) * g.ncols + g.ncols - 1,
+            "s_pre": g.ncols, "s_tot": g.ncols}
+    for name, (base, size) in regions.items():
+        if uses[name] >= size:
+            problems.append(f"{name}: index {uses[name]} past its {size} entries")
+        if 4 * (base + size) > alloc:
+            problems.append(f"{name} ends past the allocation")
+    if g.lds_match:
+        if rep_base + (OWN_WAVES - 1) * g.e_pad + (c.E - 1) >= alloc:
+            problems.append("s_rep byte table past the allocation")
+        if OWN_WAVES * W * 8 > 4 * regions["s_pack"][0]:
+            problems.append("s_peer overlaps s_pack")
+    return problems
+
+
+# ----------------------------------------------------------------------------
+# row movers (indices in 16-byte units unless stated)
+
+def fan_out_cols(V: int, nvec: int):
+    """Columns of fan_out_row<V>: (first-pass loads, later loads, stores)."""
+    first = np.minimum(np.arange(V)[:, None] * W + LANE[None, :], nvec - 1).ravel()
+    loads, stores = [], []
+    c0 = 0
+    if W * V <= nvec:
+        stores.append((np.arange(V)[:, None] * W + LANE[None, :]).ravel())
+        c0 = W * V
+    while c0 + W * V <= nvec:
+        cols = (c0 + np.arange(V)[:, None] * W + LANE[None, :]).ravel()
+        loads.append(cols)
+        stores.append(cols)
+        c0 += W * V
+    tail = np.arange(c0, nvec, dtype=np.int64)
+    loads.append(tail)
+    stores.append(tail)
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int64)
+    return first, cat(loads), cat(stores)
+
+
+def row_sum_cols(V: int, cb: int, nvec: int):
+    """Columns one wave of weighted_row_sum<V> reads and writes at slice start cb."""
+    if cb + W * V <= nvec:
+        return (cb + np.arange(V)[:, None] * W + LANE[None, :]).ravel()
+    return np.arange(cb, nvec, dtype=np.int64)
+
+
+def segment_of(rank_offsets, R, i):
+    """The permute's rank of row i: how many of the R segment ends (lanes < R
+    hold rank_offsets[lane + 1]) are at or below i."""
+    ends = np.asarray(rank_offsets, np.int64)[1:R + 1]
+    return (ends[None, :] <= np.asarray(i, np.int64)[:, None]).sum(axis=1)
+
+
+def rows_cols(rows, cols, nvec):
+    rows = np.asarray(rows, dtype=np.int64).ravel()
+    cols = np.asarray(cols, dtype=np.int64).ravel()
+    if rows.size == 0 or cols.size == 0:
+        return np.zeros(0, np.int64)
+    # the extremes suffice: the smallest and largest row with every column
+    ext = np.array([rows.min(), rows.max()])
+    return (ext[:, None] * nvec + cols[None, :]).ravel()
+
+
+def model_pack(c: Case, lay: dict, rep: Report):
+    T, R, nvec = c.T, c.R, c.nvec
+    rep.buf("hidden", T * nvec)
+    rep.buf("rank_buf", c.cap_rank * nvec)
+    rep.buf("rank_src_token", c.cap_rank)
+    if T == 0:
+        return
+    slots = lay["token_rank_slot"].astype(np.int64)  # [T, R]
+    lanes_r = np.minimum(LANE, R - 1)
+    t = np.arange(T, dtype=np.int64)
+    rep.access("pack", "token_rank_slot", (t[:, None] * R + lanes_r[None, :]), "load")
+    ok = (slots >= 0) & (slots < c.cap_rank)
+    rep.access("pack", "rank_src_token", slots[ok], "store")
+    groups = cdiv(nvec, W)
+    if T < FILL_TOKENS and groups > 1:
+        kname = "pack_rows_small"
+        # one wave per (token, group): loads min(g*64 + lane, nvec - 1), stores c < nvec
+        cols = np.arange(groups)[:, None] * W + LANE[None, :]
+        rep.access(kname, "hidden", rows_cols(t, np.minimum(cols, nvec - 1), nvec), "load")
+        rep.access(kname, "rank_buf", rows_cols(slots[ok], cols[cols < nvec], nvec), "store")
+        return
+    V = copy_vec(nvec)
+    first, loads, stores = fan_out_cols(V, nvec)
+    rep.access("pack_rows", "hidden", rows_cols(t, np.concatenate([first, loads]), nvec), "load")
+    rep.access("pack_rows", "rank_buf", rows_cols(slots[ok], stores, nvec), "store")
+
+
+def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep: Report,
+                  nvec=None, nvec_s=0, tag="permute", old_padding=False):
+    """permute_rows; nvec_s > 0: the MX form (scale rows of nvec_s vec4).
+    old_padding replays the padding marks before their rows were clipped."""
+    T, E, R, k = c.T, c.E, c.R, c.k
+    nvec = c.nvec if nvec is None else nvec
+    m = E // R
+    rep.buf("rank_buf", c.cap_rank * nvec)
+    rep.buf("rank_src_token", c.cap_rank)
+    rep.buf("expert_buf", c.cap_expert * nvec)
+    rep.buf("expert_src_pair", c.cap_expert)
+    if nvec_s:
+        rep.buf("rank_scale", c.cap_rank * nvec_s)
+        rep.buf("expert_scale", c.cap_expert * nvec_s)
+    padded = c.align > 1 or c.block > 0
+    max_rows = min(c.cap_rank, T * min(k, R))
+    pad_waves = E if padded and c.cap_expert > 0 else 0
+    if max_rows + pad_waves == 0:
+        return
+    nwaves = blocks_for(max_rows + pad_waves) * WPB
+    counts = lay["expert_counts"].astype(np.int64)
+    offs = lay["expert_offsets"].astype(np.int64)
+    if pad_waves:
+        e = np.arange(E, dtype=np.int64)
+        rep.access(tag, "expert_counts", e, "load")
+        if c.block > 0 and not old_padding:
+            first = e * c.block
+            end = first + c.block
+        else:
+            rep.access(tag, "expert_offsets", e, "load")
+            first = offs[:E]
+            end = (e + 1) * c.block if c.block > 0 else offs[1:]
+            if c.block <= 0:
+                rep.access(tag, "expert_offsets", e + 1, "load")
+        if old_padding:  # before the rows were clipped below
+            lo = first + (np.minimum(counts, c.block) if c.block > 0 else counts)
+        else:
+            cnt = np.maximum(counts, 0)
+            lo = np.maximum(first + (np.minimum(cnt, c.block) if c.block > 0 else cnt), 0)
+        hi = np.minimum(end, c.cap_expert)
+        for a, b in zip(lo, hi):
+            if b > a:
+                rep.access(tag, "expert_src_pair", [a, b - 1], "store")
+    i = np.arange(nwaves - pad_waves, dtype=np.int64)
+    rep.access(tag, "rank_offsets", np.minimum(LANE, R - 1) + 1, "load")
+    rep.access(tag, "rank_offsets", [R], "load")
+    ic = np.minimum(i, c.cap_rank - 1)
+    rep.access(tag, "rank_src_token", ic[ic >= 0], "load")
+    rows = min(int(lay["rank_offsets"][R]), c.cap_rank)
+    src = np.full(i.shape, -1, np.int64)
+    src[ic >= 0] = rank_src[ic[ic >= 0]]
+    live = (i < rows) & (src >= 0) & (src < T)
+    i, t = i[live], src[live]
+    if i.size == 0:
+        return
+    at = t[:, None] * k + np.minimum(LANE, k - 1)[None, :]
+    rep.access(tag, "topk_ids", at, "load")
+    rep.access(tag, "pair_row", at, "load")
+    V = copy_vec(nvec)
+    first, loads, stores = fan_out_cols(V, nvec)
+    rep.access(tag, "rank_buf", rows_cols(i, np.concatenate([first, loads]), nvec), "load")
+    if nvec_s and nvec_s <= W:
+        rep.access(tag, "rank_scale", rows_cols(i, np.minimum(LANE, nvec_s - 1), nvec_s), "load")
+    # destinations: the token's slots whose expert lives on row i's rank
+    r = segment_of(lay["rank_offsets"], R, i)
+    pr = lay["pair_row"].astype(np.int64)
+    e = np.asarray(ids, np.int64)[t]             # [n, k]
+    here = (e >= 0) & (e < E) & (e // m == r[:, None])
+    p = np.where(here, pr[t], -1)
+    ok = here & (p >= 0) & (p < c.cap_expert)
+    rep.access(tag, "expert_src_pair", p[ok], "store")
+    rep.access(tag, "expert_buf", rows_cols(p[ok], stores, nvec), "store")
+    if nvec_s:
+        if nvec_s <= W:
+            rep.access(tag, "expert_scale", rows_cols(p[ok], LANE[LANE < nvec_s], nvec_s),
+                       "store")
+        else:
+            f1, l1, s1 = fan_out_cols(1, nvec_s)
+            rep.access(tag, "rank_scale", rows_cols(i, np.concatenate([f1, l1]), nvec_s), "load")
+            rep.access(tag, "expert_scale", rows_cols(p[ok], s1, nvec_s), "store")
+
+
+def model_combine(c: Case, lay: dict, rep: Report):
+    T, k, nvec = c.T, c.k, c.nvec
+    rep.buf("expert_out", c.cap_expert * nvec)
+    rep.buf("weights", T * k)
+    rep.buf("out", T * nvec)
+    rep.buf("out_f32", T * nvec * 2)
+    if T == 0:
+        return
+    v, slices = combine_tiling(nvec, T, 1 if T < FILL_TOKENS else COMBINE_GROUPS)
+    t = np.arange(T, dtype=np.int64)
+    lanes_k = LANE[LANE < k]
+    rep.access("combine", "pair_row", t[:, None] * k + lanes_k[None, :], "load")
+    rep.access("combine", "weights", t[:, None] * k + lanes_k[None, :], "load")
+    pr = lay["pair_row"].astype(np.int64)
+    ok = (pr >= 0) & (pr < c.cap_expert)
+    for s in range(slices):
+        cols = row_sum_cols(v, s * W * v, nvec)
+        rep.access("combine", "expert_out", rows_cols(pr[ok], cols, nvec), "load")
+        rep.access("combine", "out", rows_cols(t, cols, nvec), "store")
+        f32 = np.concatenate([2 * cols, 2 * cols + 1])
+        rep.access("combine", "out_f32", rows_cols(t, f32, 2 * nvec), "store")
+
+
+def model_two_stage(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep: Report):
+    T, E, R, k, nvec = c.T, c.E, c.R, c.k, c.nvec
+    m = E // R
+    rep.buf("expert_out", c.cap_expert * nvec)
+    rep.buf("weights", T * k)
+    rep.buf("partial", c.cap_rank * nvec)
+    rep.buf("partial_f32", c.cap_rank * nvec * 2)
+    rep.buf("out", T * nvec)
+    rep.buf("out_f32", T * nvec * 2)
+    max_rows = min(c.cap_rank, T * min(k, R))
+    if T == 0 or max_rows == 0:
+        return
+    v, slices = combine_tiling(nvec, max_rows, PARTIAL_GROUPS)
+    nwaves = blocks_for(max_rows * slices) * WPB
+    gw = np.arange(nwaves, dtype=np.int64)
+    i_all = gw // slices
+    rep.access("rank_partial", "rank_offsets", np.minimum(LANE, R - 1) + 1, "load")
+    rep.access("rank_partial", "rank_offsets", [R], "load")
+    ic = np.minimum(i_all, c.cap_rank - 1)
+    rep.access("rank_partial", "rank_src_token", ic[ic >= 0], "load")
+    rows = min(int(lay["rank_offsets"][R]), c.cap_rank)
+    i = np.unique(i_all[i_all < rows])
+    t = rank_src[i].astype(np.int64)
+    live = (t >= 0) & (t < T)
+    i, t = i[live], t[live]
+    at = t[:, None] * k + np.minimum(LANE, k - 1)[None, :]
+    for name in ("topk_ids", "pair_row", "weights"):
+        rep.access("rank_partial", name, at, "load")
+    r = segment_of(lay["rank_offsets"], R, i)
+    e = np.asarray(ids, np.int64)[t]
+    here = (e >= 0) & (e < E) & (e // m == r[:, None])
+    pr = lay["pair_row"].astype(np.int64)
+    p = np.where(here, pr[t], -1)
+    ok = (p >= 0) & (p < c.cap_expert)
+    for s in range(slices):
+        cols = row_sum_cols(v, s * W * v, nvec)
+        rep.access("rank_partial", "expert_out", rows_cols(p[ok], cols, nvec), "load")
+        rep.access("rank_partial", "partial", rows_cols(i, cols, nvec), "store")
+        f32 = np.concatenate([2 * cols, 2 * cols + 1])
+        rep.access("rank_partial", "partial_f32", rows_cols(i, f32, 2 * nvec), "store")
+    # home sum
+    v, slices = combine_tiling(nvec, T, RANK_SUM_GROUPS)
+    tt = np.arange(T, dtype=np.int64)
+    lanes_r = LANE[LANE < R]
+    rep.access("rank_sum", "token_rank_slot", tt[:, None] * R + lanes_r[None, :], "load")
+    s_ = lay["token_rank_slot"].astype(np.int64)
+    ok = (s_ >= 0) & (s_ < c.cap_rank)
+    for sl in range(slices):
+        cols = row_sum_cols(v, sl * W * v, nvec)
+        rep.access("rank_sum", "partial", rows_cols(s_[ok], cols, nvec), "load")
+        rep.access("rank_sum", "out", rows_cols(tt, cols, nvec), "store")
+        f32 = np.concatenate([2 * cols, 2 * cols + 1])
+        rep.access("rank_sum", "out_f32", rows_cols(tt, f32, 2 * nvec), "store")
+
+
+def model_pack_mx(c: Case, lay: dict, bits: int, rep: Report):
+    """pack_rows_mx<NP, bits>: byte indices for codes and scales."""
+    T, R, nvec = c.T, c.R, c.nvec
+    rep.buf("hidden", T * nvec)
+    rep.buf("rank_q", c.cap_rank * nvec * bits)       # bytes
+    rep.buf("rank_scale_b", c.cap_rank * (nvec // 4))  # bytes
+    rep.buf("rank_src_token", c.cap_rank)
+    if T == 0:
+        return
+    nl = 2 if bits == 8 else 1
+    nb, lpb = nl * bits, 4 // nl
+    npass = cdiv(nvec, W * nl)
+    np_, slices = mx_passes(npass, MAX_VEC // nl), 1
+    if (bits == 8 or T < FILL_TOKENS) and T * npass <= INT32_MAX:
+        np_, slices = 1, npass
+    slots = lay["token_rank_slot"].astype(np.int64)
+    ok = (slots >= 0) & (slots < c.cap_rank)
+    t = np.arange(T, dtype=np.int64)
+    lanes_r = LANE[LANE < R]
+    rep.access("pack_mx", "token_rank_slot", t[:, None] * R + lanes_r[None, :], "load")
+    rep.access("pack_mx", "rank_src_token", slots[ok], "store")
+    cols, starts, scols = [], [], []
+    for sl in range(slices):
+        p_end = npass if slices == 1 else sl * np_ + np_
+        for p0 in range(sl * np_, p_end, np_):
+            for q in range(np_):
+                col = (p0 + q) * W * nl + nl * LANE
+                act = np.ones(W, bool) if nl == 1 else col < nvec
+                cols.append((col[act][:, None] + np.arange(nl)[None, :]).ravel())
+                starts.append(col[act])
+                scols.append(col[act & (LANE % (4 * lpb) == 0)])
+    rep.access("pack_mx", "hidden", rows_cols(t, np.concatenate(cols), nvec), "load")
+    st = np.concatenate(starts)
+    code_bytes = (st[:, None] * bits + np.arange(nb)[None, :]).ravel()
+    rep.access("pack_mx", "rank_q", rows_cols(slots[ok], code_bytes, nvec * bits), "store")
+    sb = np.concatenate(scols)
+    sb = (sb // 4)[:, None] + np.arange(4)[None, :]
+    rep.access("pack_mx", "rank_scale_b", rows_cols(slots[ok], sb, nvec // 4), "store")
+
+
+# ----------------------------------------------------------------------------
+# whole sequences
+
+def one_stage(c: Case, ids: np.ndarray, lay: dict | None = None,
+              rank_src: np.ndarray | None = None, unclamped_src: bool = False,
+              old_padding: bool = False) -> Report:
+    """Layout, pack, permute and combine of one call sequence. The index
+    arrays the later calls read are the oracle's layout and pack, or `lay` and
+    `rank_src` as given (any contents). unclamped_src and old_padding replay
+    two earlier forms of the permute (a load of rank_src_token[i] before i was
+    checked; padding marks not clipped below), kept to show the model finds
+    what they did."""
+    rep = Report()
+    if lay is None:
+        lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
+    if rank_src is None:
+        _, rank_src, _ = oracle.pack(np.zeros((c.T, 8), np.uint16), lay["token_rank_slot"],
+                                     c.cap_rank)
+    model_layout(c, rep)
+    model_pack(c, lay, rep)
+    if unclamped_src:
+        _model_unclamped_src(c, rep)
+    model_permute(c, lay, rank_src, ids, rep, old_padding=old_padding)
+    model_combine(c, lay, rep)
+    return rep
+
+
+def two_stage(c: Case, ids: np.ndarray, lay: dict | None = None,
+              rank_src: np.ndarray | None = None) -> Report:
+    rep = Report()
+    if lay is None:
+        lay = oracle.layout(ids, c.E, c.R)
+    if rank_src is None:
+        _, rank_src, _ = oracle.pack(np.zeros((c.T, 8), np.uint16), lay["token_rank_slot"],
+                                     c.cap_rank)
+    model_layout(c, rep)
+    model_pack(c, lay, rep)
+    model_two_stage(c, lay, rank_src, np.asarray(ids), rep)
+    return rep
+
+
+def mx(c: Case, ids: np.ndarray, bits: int, lay: dict | None = None,
+       rank_src: np.ndarray | None = None) -> Report:
+    rep = Report()
+    if lay is None:
+        lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
+    if rank_src is None:
+        _, rank_src, _ = oracle.pack(np.zeros((c.T, 8), np.uint16), lay["token_rank_slot"],
+                                     c.cap_rank)
+    model_layout(c, rep)
+    model_pack_mx(c, lay, bits, rep)
+    qrep = Report(sizes=dict(rep.sizes))  # code rows replace the bf16 rows' sizes
+    model_permute(c, lay, rank_src, ids, qrep, nvec=c.H * bits // 128, nvec_s=c.H // 512,
+                  tag=f"permute_mxfp{bits}")
+    rep.violations += qrep.violations
+    rep.counted += qrep.counted
+    return rep
+
+
+def _model_unclamped_src(c: Case, rep: Report):
+    padded = c.align > 1 or c.block > 0
+    max_rows = min(c.cap_rank, c.T * min(c.k, c.R))
+    pad_waves = c.E if padded and c.cap_expert > 0 else 0
+    if max_rows + pad_waves == 0:
+        return
+    nwaves = blocks_for(max_rows + pad_waves) * WPB
+    rep.access("permute (unclamped)", "rank_src_token", np.arange(nwaves - pad_waves), "load")
+
+
+def arbitrary_layout(rng, c: Case) -> tuple[dict, np.ndarray]:
+    """Index arrays of the layout's shapes with arbitrary contents: random
+    int32 values, half of them near the buffers' edges (-1, 0, the caps and
+    one past, huge positive and negative), for the later calls to read."""
+    edge = np.array([-2 ** 31, -100000, -2, -1, 0, 1, c.T - 1, c.T, c.cap_rank - 1, c.cap_rank,
+                     c.cap_rank + 1, c.cap_expert - 1, c.cap_expert, c.cap_expert + 1,
+                     2 ** 31 - 1], np.int64)
+
+    def arr(n):
+        a = rng.integers(-2 ** 31, 2 ** 31, size=n, dtype=np.int64)
+        pick = rng.random(n) < 0.5
+        a[pick] = rng.choice(edge, size=int(pick.sum()))
+        return np.clip(a, -2 ** 31, 2 ** 31 - 1).astype(np.int32)
+
+    lay = dict(rank_offsets=arr(c.R + 1), token_rank_slot=arr(c.T * c.R).reshape(c.T, c.R),
+               pair_row=arr(c.T * c.k).reshape(c.T, c.k), expert_counts=arr(c.E),
+               expert_offsets=arr(c.E + 1))
+    return lay, arr(c.cap_rank)

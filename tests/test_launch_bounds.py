@@ -1,0 +1,152 @@
+"""Every global load and store of every kernel launch stays inside the buffer
+it addresses, checked on the CPU with the host-side launch model
+(tests/launch_model.py), no GPU involved:
+
+* with the oracle's layout for the whole-path random shapes (the seeds the
+  GPU tests run, and further seeds that the GPU tests do not run), the
+  workloads, the edge shapes, the MX dispatch and the two-stage combine;
+* with index arrays of arbitrary contents (slots, pair rows, offsets, counts
+  and source tokens, the values the later calls take from the caller), for
+  which the C ABI still promises that nothing is written out of bounds;
+* the layout's LDS regions fit their allocation for every shape the library
+  accepts at the region sizes' extremes.
+
+Two earlier forms of the permute are replayed to show the model finds what
+they did: the load of rank_src_token[i] before i was checked, and padding
+marks that trusted the counts and offsets to keep their rows in the buffer.
+"""
+import numpy as np
+import pytest
+
+import launch_model as lm
+import pins
+import synth
+import test_random_shapes_gpu as rs
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def case_of(c: dict, plain: bool = False) -> lm.Case:
+    return lm.Case(c["T"], c["H"], c["E"], c["R"], c["k"], 1 if plain else c["align"],
+                   0 if plain else c["block"], c["form"], c["match"])
+
+
+def assert_clean(rep: lm.Report, what: str):
+    assert not rep.violations, f"{what}: {rep.violations[:4]}"
+
+
+@pytest.mark.parametrize("lo,hi", [(0, 96), (1000, 1100), (1100, 1400)])
+def test_whole_path_random_shapes(lo, hi):
+    """The whole-path random-shape generator of the GPU tests: seeds 0-95 (run
+    on the GPU) and 1000-1399 (not run there), one- and two-stage."""
+    for s in range(lo, hi):
+        c = rs.draw(s)
+        ids, _, _ = rs.inputs(c)
+        assert_clean(lm.one_stage(case_of(c), ids), f"seed {s} one-stage")
+        if c["align"] == 1 and c["block"] == 0:
+            assert_clean(lm.two_stage(case_of(c), ids), f"seed {s} two-stage")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_mx_random_shapes(bits):
+    for s in list(range(200, 216)) + list(range(10000, 10060)):
+        c = rs.draw(s, mx=True)
+        ids, _, _ = rs.inputs(c)
+        assert_clean(lm.mx(case_of(c), ids, bits), f"mx{bits} seed {s}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
+def test_workloads(name):
+    w = synth.WORKLOADS[name]
+    ids, _ = synth.routing(w)
+    for form in (-1, 0, 1):
+        c = lm.Case(w.T, w.H, w.E, w.R, w.k, form=form)
+        assert_clean(lm.one_stage(c, ids), f"{name} form {form}")
+    assert_clean(lm.two_stage(lm.Case(w.T, w.H, w.E, w.R, w.k), ids), f"{name} two-stage")
+    if w.H % 512 == 0:
+        for bits in (8, 4):
+            assert_clean(lm.mx(lm.Case(w.T, w.H, w.E, w.R, w.k), ids, bits), f"{name} mx{bits}")
+
+
+def test_undersized_caps():
+    """Caps below the worst case (rows dropped and flagged, never written past)."""
+    rng = np.random.default_rng(5)
+    for T, H, E, R, k in [(300, 64, 16, 4, 3), (1100, 520, 64, 8, 6), (257, 8, 8, 8, 8)]:
+        ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
+        for cr, ce in [(0, 0), (1, 1), (T // 3, T * k // 2), (T * min(k, R) - 1, T * k - 1)]:
+            c = lm.Case(T, H, E, R, k, cap_rank=cr, cap_expert=ce)
+            assert_clean(lm.one_stage(c, ids), f"T={T} caps {cr}/{ce}")
+            assert_clean(lm.two_stage(c, ids), f"T={T} caps {cr}/{ce} two-stage")
+
+
+def test_arbitrary_index_arrays():
+    """Whatever the slots, pair rows, offsets, counts and source tokens hold,
+    no kernel addresses outside its buffers."""
+    rng = np.random.default_rng(11)
+    for s in range(150):
+        c = rs.draw(3000 + s)
+        ids, _, _ = rs.inputs(c)
+        case = case_of(c)
+        lay, src = lm.arbitrary_layout(rng, case)
+        assert_clean(lm.one_stage(case, ids, lay=lay, rank_src=src), f"seed {3000 + s}")
+        plain = case_of(c, plain=True)
+        lay, src = lm.arbitrary_layout(rng, plain)
+        assert_clean(lm.two_stage(plain, ids, lay=lay, rank_src=src), f"seed {3000 + s} 2-st")
+    for s in range(40):
+        c = rs.draw(12000 + s, mx=True)
+        ids, _, _ = rs.inputs(c)
+        case = case_of(c)
+        lay, src = lm.arbitrary_layout(rng, case)
+        for bits in (8, 4):
+            assert_clean(lm.mx(case, ids, bits, lay=lay, rank_src=src), f"mx seed {12000 + s}")
+
+
+def test_model_finds_the_earlier_permute_reads():
+    """The unclamped source-token load of an earlier permute reads past
+    cap_rank for a grid rounded up past the last row; the model says so."""
+    hits = 0
+    for s in range(1000, 1040):
+        c = rs.draw(s)
+        ids, _, _ = rs.inputs(c)
+        rep = lm.one_stage(case_of(c), ids, unclamped_src=True)
+        hits += any("rank_src_token" in v for v in rep.violations)
+    assert hits >= 5
+
+
+def test_model_finds_unclipped_padding_marks():
+    """Padding marks that take their first row from the caller's offsets and
+    counts unclipped store below the buffer when those disagree; clipped, they
+    do not (masked and padded layouts, arbitrary counts and offsets)."""
+    rng = np.random.default_rng(3)
+    found = 0
+    for s in range(400):
+        c = rs.draw(5000 + s)
+        if c["align"] == 1 and c["block"] == 0 or c["T"] == 0:
+            continue
+        ids, _, _ = rs.inputs(c)
+        case = case_of(c)
+        lay, src = lm.arbitrary_layout(rng, case)
+        old = lm.one_stage(case, ids, lay=lay, rank_src=src, old_padding=True)
+        found += any("expert_src_pair" in v for v in old.violations)
+        assert_clean(lm.one_stage(case, ids, lay=lay, rank_src=src), f"seed {5000 + s}")
+    assert found >= 10
+
+
+def test_layout_lds_regions():
+    """The layout's LDS regions fit (largest index in each, and each region in
+    the allocation) at the extremes of every dimension the library accepts."""
+    for E in (1, 2, 255, 256, 257, 511, 512, 960, 1023, 1024):
+        for R in (1, 2, 3, 8, 32, 64):
+            if E % R:
+                continue
+            for k in (1, 2, 6, 8, 15, 16):
+                if k > E or pins_lds_too_big(k, E + R):
+                    continue
+                for match in (0, 1):
+                    c = lm.Case(4096, 8, E, R, k, match=match)
+                    assert not lm.layout_lds_regions(c), (E, R, k, match)
+
+
+def pins_lds_too_big(k, ncols):
+    """Shapes the library refuses (its LDS would not fit)."""
+    return lm.layout_lds_bytes(k, ncols) > lm.LDS_LIMIT
