@@ -154,6 +154,19 @@ def _i32(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
+def _check_err(t: torch.Tensor | None) -> None:
+    """The device error word: None, or an int32 tensor of at least one element
+    (the kernels OR 4 bytes into its first element)."""
+    if t is not None and (t.dtype != torch.int32 or t.numel() < 1):
+        raise MoeError(f"err must be an int32 tensor of at least 1 element, got {t.dtype} "
+                       f"with {t.numel()}")
+
+
+def _err(t: torch.Tensor | None):
+    _check_err(t)
+    return _ptr(t)
+
+
 def _rows16(t: torch.Tensor) -> torch.Tensor:
     if t.element_size() != 2:
         raise MoeError(f"expected a 16-bit row tensor, got {t.dtype}")
@@ -200,11 +213,14 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1
     T, k = topk_ids.shape
     dev = topk_ids.device
     shape = Shape(T, H, E, R, k, align, block)
+    _check_err(err)
     if out is not None:
         for key, want in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
                           ("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
                           ("token_rank_slot", (T, R)), ("pair_row", (T, k))):
             _need(out[key], key, want)
+            if out[key].dtype != torch.int32:
+                raise MoeError(f"{key} must be int32, got {out[key].dtype}")
     if out is None:
         out = dict(
             rank_counts=torch.empty(R, dtype=torch.int32, device=dev),
@@ -216,10 +232,11 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1
         )
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().moe_dispatch_layout(
-        ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(out["rank_counts"]),
-        _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
-        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _ptr(workspace), ws_bytes,
-        _ptr(err), _stream(dev))
+        ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(_i32(out["rank_counts"])),
+        _ptr(_i32(out["rank_offsets"])), _ptr(_i32(out["expert_counts"])),
+        _ptr(_i32(out["expert_offsets"])), _ptr(_i32(out["token_rank_slot"])),
+        _ptr(_i32(out["pair_row"])), _ptr(workspace), ws_bytes,
+        _err(err), _stream(dev))
     _check(st, "moe_dispatch_layout")
     return out
 
@@ -228,6 +245,7 @@ def pack(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, ra
          rank_src_token, *, err=None) -> None:
     """moe_dispatch_pack into caller-provided rank_buf [cap_rank, H] and
     rank_src_token [cap_rank]."""
+    _check_err(err)
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
     _need(token_rank_slot, "token_rank_slot", (T, R))
@@ -236,7 +254,7 @@ def pack(hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int, ra
     shape = Shape(T, H, E, R, k)
     st = lib().moe_dispatch_pack(
         ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
-        _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)), rank_buf.shape[0], _ptr(err),
+        _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)), rank_buf.shape[0], _err(err),
         _stream(hidden.device))
     _check(st, "moe_dispatch_pack")
 
@@ -247,6 +265,7 @@ def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, 
     """moe_permute_by_expert into caller-provided expert_buf [cap_expert, H].
     A padded (align > 1) or blocked (block > 0) layout needs the layout's
     expert_counts and expert_offsets, to mark its padding rows."""
+    _check_err(err)
     T, k = topk_ids.shape
     H = rank_buf.shape[1]
     R = rank_offsets.shape[0] - 1
@@ -264,7 +283,7 @@ def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, 
         _ptr(None if expert_counts is None else _i32(expert_counts)),
         _ptr(None if expert_offsets is None else _i32(expert_offsets)),
         rank_buf.shape[0], _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)),
-        expert_buf.shape[0], _ptr(err), _stream(rank_buf.device))
+        expert_buf.shape[0], _err(err), _stream(rank_buf.device))
     _check(st, "moe_permute_by_expert")
 
 
@@ -279,6 +298,7 @@ def pack_mx(bits: int, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: i
     """moe_dispatch_pack_mxfp8 (bits 8) or _mxfp4 (bits 4): quantise each hidden
     row once and pack it once per distinct rank into rank_q [cap_rank, H*bits/8]
     (uint8 codes) and rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
+    _check_err(err)
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
     _need(token_rank_slot, "token_rank_slot", (T, R))
@@ -289,7 +309,7 @@ def pack_mx(bits: int, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: i
     fn = lib().moe_dispatch_pack_mxfp8 if bits == 8 else lib().moe_dispatch_pack_mxfp4
     st = fn(ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
             _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
-            rank_q.shape[0], _ptr(err), _stream(hidden.device))
+            rank_q.shape[0], _err(err), _stream(hidden.device))
     _check(st, f"moe_dispatch_pack_mxfp{bits}")
 
 
@@ -306,6 +326,7 @@ def permute_mx(bits: int, rank_q, rank_scale, rank_src_token, rank_offsets, topk
                expert_offsets=None, align: int = 1, block: int = 0, err=None) -> None:
     """moe_permute_by_expert_mxfp8 / _mxfp4: the codes and scales of each
     rank-buffer row to the rows of its token's experts on that rank."""
+    _check_err(err)
     T, k = topk_ids.shape
     H = rank_q.shape[1] * 8 // bits
     R = rank_offsets.shape[0] - 1
@@ -325,7 +346,7 @@ def permute_mx(bits: int, rank_q, rank_scale, rank_src_token, rank_offsets, topk
             _ptr(_i32(pair_row)), _ptr(None if expert_counts is None else _i32(expert_counts)),
             _ptr(None if expert_offsets is None else _i32(expert_offsets)), rank_q.shape[0],
             _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)), _ptr(_i32(expert_src_pair)),
-            expert_q.shape[0], _ptr(err), _stream(rank_q.device))
+            expert_q.shape[0], _err(err), _stream(rank_q.device))
     _check(st, f"moe_permute_by_expert_mxfp{bits}")
 
 
@@ -340,6 +361,7 @@ def permute_mxfp4(*args, **kw) -> None:
 def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=None,
             err=None) -> None:
     """moe_combine: out [T, H] bf16 (and optionally out_f32 [T, H] float32)."""
+    _check_err(err)
     T, k = pair_row.shape
     H = out.shape[1]
     if topk_weights.dtype != torch.float32:
@@ -353,7 +375,7 @@ def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=
     shape = Shape(T, H, E, R, k)
     st = lib().moe_combine(
         ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(pair_row)),
-        _ptr(topk_weights), expert_out.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err),
+        _ptr(topk_weights), expert_out.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _err(err),
         _stream(out.device))
     _check(st, "moe_combine")
 
@@ -362,6 +384,7 @@ def combine_rank_partial(expert_out, rank_src_token, rank_offsets, topk_ids, pai
                          topk_weights, E: int, partial, *, partial_f32=None, err=None) -> None:
     """moe_combine_rank_partial: one bf16 partial row per rank-buffer row into
     caller-provided partial [cap_rank, H] (and optionally partial_f32)."""
+    _check_err(err)
     T, k = topk_ids.shape
     H = partial.shape[1]
     R = rank_offsets.shape[0] - 1
@@ -380,13 +403,14 @@ def combine_rank_partial(expert_out, rank_src_token, rank_offsets, topk_ids, pai
         ctypes.byref(shape.c()), _ptr(_rows16(expert_out)), _ptr(_i32(rank_src_token)),
         _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)), _ptr(_i32(pair_row)),
         _ptr(topk_weights), expert_out.shape[0], partial.shape[0], _ptr(_rows16(partial)),
-        _ptr(partial_f32), _ptr(err), _stream(partial.device))
+        _ptr(partial_f32), _err(err), _stream(partial.device))
     _check(st, "moe_combine_rank_partial")
 
 
 def combine_ranks(partial, token_rank_slot, E: int, k: int, out, *, out_f32=None,
                   err=None) -> None:
     """moe_combine_ranks: out [T, H] = sum over ranks of the token's partial rows."""
+    _check_err(err)
     T, R = token_rank_slot.shape
     H = out.shape[1]
     if out_f32 is not None and out_f32.dtype != torch.float32:
@@ -397,7 +421,7 @@ def combine_ranks(partial, token_rank_slot, E: int, k: int, out, *, out_f32=None
     shape = Shape(T, H, E, R, k)
     st = lib().moe_combine_ranks(
         ctypes.byref(shape.c()), _ptr(_rows16(partial)), _ptr(_i32(token_rank_slot)),
-        partial.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _ptr(err), _stream(out.device))
+        partial.shape[0], _ptr(_rows16(out)), _ptr(out_f32), _err(err), _stream(out.device))
     _check(st, "moe_combine_ranks")
 
 

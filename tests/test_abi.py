@@ -219,3 +219,31 @@ def test_binding_rejects_tensors_that_do_not_fit_the_call():
     for name, call in cases:
         with pytest.raises(moe.MoeError, match=name):
             call()
+
+
+def test_binding_rejects_wrong_dtypes_before_any_pointer():
+    """An int32 buffer of the right shape but another dtype (2 bytes an
+    element) would be written 4 bytes an element past its end: the layout's
+    outputs and the error word must be int32, and the error word must have an
+    element (host tensors, so nothing could run even if a check were missing)."""
+    import torch
+    i32, i16 = torch.int32, torch.int16
+    T, H, E, R, k, cap = 8, 16, 8, 2, 2, 16
+    ids = _z((T, k), i32)
+    good = dict(rank_counts=((R,), i32), rank_offsets=((R + 1,), i32),
+                expert_counts=((E,), i32), expert_offsets=((E + 1,), i32),
+                token_rank_slot=((T, R), i32), pair_row=((T, k), i32))
+    for key in good:
+        out = {name: _z(shape, i16 if name == key else dt) for name, (shape, dt) in good.items()}
+        with pytest.raises(moe.MoeError, match=f"{key} must be int32"):
+            moe.layout(ids, E, R, H, out=out)
+    hid = _z((T, H), torch.bfloat16)
+    slots = _z((T, R), i32)
+    for bad in (_z((1,), i16), _z((0,), i32), _z((2,), torch.float32)):
+        with pytest.raises(moe.MoeError, match="err must be an int32"):
+            moe.layout(ids, E, R, H, err=bad)
+        with pytest.raises(moe.MoeError, match="err must be an int32"):
+            moe.pack(hid, slots, E, k, _z((cap, H), i16), _z((cap,), i32), err=bad)
+        with pytest.raises(moe.MoeError, match="err must be an int32"):
+            moe.combine(_z((cap, H), i16), ids, _z((T, k), torch.float32), E, R,
+                        _z((T, H), i16), err=bad)

@@ -259,10 +259,12 @@ WIDE_RANK_SETS = [(1024, 512, 64, 4), (4096, 480, 48, 4), (8192, 64, 64, 4), (12
 @pytest.mark.parametrize("case", WIDE_RANK_SETS, ids=[f"T{c[0]}_E{c[1]}_R{c[2]}_k{c[3]}"
                                                       for c in WIDE_RANK_SETS])
 def test_layout_wide_rank_sets_repeated(case):
-    """One-launch layout with more than 32 ranks (64-bit rank sets), forced
-    and chosen by size, three calls in a row on the same ids: every call gives
-    the oracle's counts, offsets and rows. (The copies per rank once came out
-    wrong for k = 4 with R > 32 in this form, on most calls but not all.)"""
+    """Layout with more than 32 ranks (64-bit rank sets): the one-launch form
+    (forced with a workspace, and chosen without one) and the two-launch form
+    (forced, through the workspace), three calls in a row on the same ids:
+    every call gives the oracle's counts, offsets and rows. (The copies per
+    rank once came out wrong for k = 4 with R > 32 in the one-launch form, on
+    most calls but not all.)"""
     import combine_topk_ids_02_amd as moe
     T, E, R, k = case
     say(f"[wide rank sets] T={T} E={E} R={R} k={k}")
@@ -273,11 +275,11 @@ def test_layout_wide_rank_sets_repeated(case):
     shape = moe.Shape(T, 8, E, R, k)
     ws = moe.layout_workspace_bytes(shape)
     workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=torch.int32, device="cuda:0") if ws else None
-    for form in (0, -1):
+    for form in (0, -1, 1):
         old = moe.lib().moe_testing_set_layout_form(form)
         try:
             for call in range(3):
-                got = moe.layout(ids_d, E, R, 8, workspace=workspace if form == 0 else None)
+                got = moe.layout(ids_d, E, R, 8, workspace=workspace if form != -1 else None)
                 torch.cuda.synchronize()
                 for key in ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
                             "token_rank_slot", "pair_row"):
