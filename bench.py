@@ -2,24 +2,30 @@
 permute, combine) over one batch of seeded synthetic input already resident in
 HBM, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill] [--sets 3]
     python bench.py --sweep [tiny,decode,prefill,skew,adv]
 
 The default mode prints ONE JSON line: dispatch+combine throughput in GB/s of
 algorithmic bytes (what the method must move, with the measured copy count C
-and pair count P), its fraction of the 8 TB/s HBM peak, per-call times, the
-roofline of the dominant kernel (permute: its algorithmic bytes over its own
-duration, from a HIP event pair that the runtime records with the kernel's
-dispatch on the stream it runs on), and the CPU oracle timed on a bounded
-sample of the same workload.
+and pair count P) and its fraction of the 8 TB/s HBM peak. The value comes
+from steps that rotate through `--sets` complete buffer sets (inputs, expert
+outputs and every output buffer), so that no step finds in L2 or the Infinity
+Cache anything the step before it read or wrote, as consecutive layers or
+batches would not; within a step the calls hand their results on as they do
+in a layer. Beside it (`modes`): the same steps on one buffer set back to back
+(warm), and the sum of per-call times with L2 and the Infinity Cache evicted
+before every call (cold). Also: per-call times, the load per destination rank
+(max over mean), the roofline of the dominant kernel (permute: its algorithmic
+bytes over its own duration, from a HIP event pair that the runtime records
+with the kernel's dispatch on the stream it runs on), and the CPU oracle timed
+on a bounded sample of the same workload.
 
---sweep measures every workload per call, warm (back to back) and cold (a
-1 GiB read evicts L2 and the Infinity Cache before each call; a read, not a
-write, so that no dirty lines of its own are written back inside the timed
-call): 5 warm-up
-steps, then the median of 30 calls, repeated 3 times; next to it a plain 1 GiB
-device copy as the achievable rate, and the oracle pinned to one core (median
-of 5 steps, 3 for the two large workloads).
+--sweep measures every workload per call in the same three modes (warm,
+rotated, cold; the cold eviction is a 1 GiB read, not a write, so that no dirty
+lines of its own are written back inside the timed call): 5 warm-up steps,
+then the median of 30 calls, repeated 3 times; next to it a plain 1 GiB device
+copy as the achievable rate, and the oracle pinned to one core (median of 5
+steps, 3 for the two large workloads).
 """
 from __future__ import annotations
 
@@ -229,11 +235,15 @@ def oracle_median(w, hid, ids, wts, y, reps: int) -> dict:
 
 
 class Rig:
-    """One workload resident on the GPU with every buffer of a pass, and the
-    four library calls on the current stream."""
+    """One workload resident on the GPU with every buffer of a pass, in `sets`
+    complete copies (inputs, expert outputs and every output buffer), and the
+    four library calls on the current stream. Stepping through the copies in
+    turn (rotate) gives each step a batch at addresses the previous steps did
+    not touch, as consecutive layers or batches of a model would: nothing a
+    step reads is still in L2 or the Infinity Cache from the step before."""
 
     def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0,
-                 mx_bits: int = 0):
+                 mx_bits: int = 0, sets: int = 1):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -241,84 +251,125 @@ class Rig:
         from synth import staging
 
         self.w, self.dev, self.moe = w, dev, moe
-        log(f"generating {w.describe()}")
+        log(f"generating {w.describe()} ({sets} buffer set{'s' if sets > 1 else ''})")
         self.hid = synth.hidden(w)
         self.ids, self.wts = synth.routing(w)
         self.y = synth.expert_out_slots(w.seed, w.E, w.H, self.ids)
         self.shape = moe.Shape(w.T, w.H, w.E, w.R, w.k, align, block)
-        self.buf = moe.Buffers(self.shape, dev)
-        self.hid_d = staging.rows_to_device(self.hid, dev)
-        self.ids_d = torch.from_numpy(self.ids).to(dev)
-        self.wts_d = torch.from_numpy(self.wts).to(dev)
-        # a first layout gives pair_row for placing the expert outputs
-        moe.dispatch(self.buf, self.hid_d, self.ids_d)
-        self.expert_out = staging.place_expert_outputs(
-            staging.rows_to_device(self.y, dev), self.buf.pair_row, self.shape.cap_expert)
+        self.mx_bits = mx_bits
+        self.two_stage = two_stage
+        y_d = staging.rows_to_device(self.y, dev)
+        self.sets = [self._make_set(y_d) for _ in range(sets)]
+        del y_d
         torch.cuda.synchronize()
-        self.C = int(self.buf.rank_offsets[-1].item())
+        torch.cuda.empty_cache()
+        self.turn = 0
+        self.cur = self.sets[0]
+        b = self.cur.buf
+        self.C = int(b.rank_offsets[-1].item())
         # pairs placed (a full block drops the rest) and padding rows marked
-        counts = self.buf.expert_counts.long()
+        counts = b.expert_counts.long()
         self.P = int((counts.clamp(max=block) if block else counts).sum().item())
-        self.pad_rows = int(self.buf.expert_offsets[-1].item()) - self.P
+        self.pad_rows = int(b.expert_offsets[-1].item()) - self.P
         self.nbytes = algorithmic_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P)
         self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         self.stream = torch.cuda.current_stream(dev)
         self.calls = CALLS
-        self.mx_bits = mx_bits
         if mx_bits:
-            # quantised dispatch: codes and scales replace the bf16 rank and expert rows
-            u8 = torch.uint8
-            qw = w.H * mx_bits // 8
-            self.rank_q = torch.empty((self.shape.cap_rank, qw), dtype=u8, device=dev)
-            self.rank_s = torch.empty((self.shape.cap_rank, w.H // 32), dtype=u8, device=dev)
-            self.exp_q = torch.empty((self.shape.cap_expert, qw), dtype=u8, device=dev)
-            self.exp_s = torch.empty((self.shape.cap_expert, w.H // 32), dtype=u8, device=dev)
-            self.buf.rank_buf = self.buf.expert_buf = None
-            torch.cuda.empty_cache()
             self.nbytes.update(mx_bytes(w.T, w.H, w.R, w.k, self.C, self.P, mx_bits))
             self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         if two_stage:
-            self.partial = torch.empty((self.shape.cap_rank, w.H), dtype=torch.bfloat16,
-                                       device=dev)
-            self.out2 = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
             self.nbytes.update(two_stage_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
             self.calls = CALLS + TWO_STAGE_CALLS
 
+    def _make_set(self, y_d):
+        import types
+
+        import torch
+
+        from synth import staging
+
+        moe, w, dev, sh = self.moe, self.w, self.dev, self.shape
+        s = types.SimpleNamespace()
+        s.buf = moe.Buffers(sh, dev)
+        s.hid_d = staging.rows_to_device(self.hid, dev)
+        s.ids_d = torch.from_numpy(self.ids).to(dev)
+        s.wts_d = torch.from_numpy(self.wts).to(dev)
+        # a first layout gives pair_row for placing the expert outputs
+        moe.dispatch(s.buf, s.hid_d, s.ids_d)
+        s.expert_out = staging.place_expert_outputs(y_d, s.buf.pair_row, sh.cap_expert)
+        if self.mx_bits:
+            # quantised dispatch: codes and scales replace the bf16 rank and expert rows
+            u8 = torch.uint8
+            qw = w.H * self.mx_bits // 8
+            s.rank_q = torch.empty((sh.cap_rank, qw), dtype=u8, device=dev)
+            s.rank_s = torch.empty((sh.cap_rank, w.H // 32), dtype=u8, device=dev)
+            s.exp_q = torch.empty((sh.cap_expert, qw), dtype=u8, device=dev)
+            s.exp_s = torch.empty((sh.cap_expert, w.H // 32), dtype=u8, device=dev)
+            s.buf.rank_buf = s.buf.expert_buf = None
+        if self.two_stage:
+            s.partial = torch.empty((sh.cap_rank, w.H), dtype=torch.bfloat16, device=dev)
+            s.out2 = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+        return s
+
+    def rotate(self) -> None:
+        """Move on to the next buffer set (a no-op with one set)."""
+        self.turn = (self.turn + 1) % len(self.sets)
+        self.cur = self.sets[self.turn]
+
+    def imbalance(self) -> dict:
+        """Load per destination rank, max over mean: rank-buffer rows (token
+        copies) and pairs (expert rows), as the pages measure the busiest GPU
+        against the average ("A2A backends" page, section 1.3; "Beyond One
+        GPU", section 6)."""
+        b, R = self.cur.buf, self.w.R
+        rows = b.rank_counts.double()
+        pairs = b.expert_counts.double().reshape(R, -1).sum(dim=1)
+        ratio = lambda x: round(float(x.max() / x.mean()), 4) if float(x.mean()) > 0 else None
+        return {"rank_rows_max_over_mean": ratio(rows),
+                "rank_pairs_max_over_mean": ratio(pairs),
+                "rank_rows": [int(v) for v in b.rank_counts.tolist()],
+                "rank_pairs": [int(v) for v in pairs.tolist()]}
+
     def call(self, name: str) -> None:
-        moe, s, b = self.moe, self.shape, self.buf
+        moe, s, x = self.moe, self.shape, self.cur
+        b = x.buf
         if name == "layout":
-            moe.layout(self.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
+            moe.layout(x.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
                        out=b.layout_dict(), workspace=b.workspace)
         elif name == "pack" and self.mx_bits:
-            moe.pack_mx(self.mx_bits, self.hid_d, b.token_rank_slot, s.E, s.k, self.rank_q,
-                        self.rank_s, b.rank_src_token, err=b.err)
+            moe.pack_mx(self.mx_bits, x.hid_d, b.token_rank_slot, s.E, s.k, x.rank_q,
+                        x.rank_s, b.rank_src_token, err=b.err)
         elif name == "pack":
-            moe.pack(self.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
+            moe.pack(x.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
                      err=b.err)
         elif name == "permute" and self.mx_bits:
-            moe.permute_mx(self.mx_bits, self.rank_q, self.rank_s, b.rank_src_token,
-                           b.rank_offsets, self.ids_d, b.pair_row, s.E, self.exp_q, self.exp_s,
+            moe.permute_mx(self.mx_bits, x.rank_q, x.rank_s, b.rank_src_token,
+                           b.rank_offsets, x.ids_d, b.pair_row, s.E, x.exp_q, x.exp_s,
                            b.expert_src_pair, expert_counts=b.expert_counts,
                            expert_offsets=b.expert_offsets, align=s.align, block=s.block,
                            err=b.err)
         elif name == "permute":
-            moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, self.ids_d, b.pair_row,
+            moe.permute(b.rank_buf, b.rank_src_token, b.rank_offsets, x.ids_d, b.pair_row,
                         s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
                         expert_offsets=b.expert_offsets, align=s.align, block=s.block,
                         err=b.err)
         elif name == "combine":
-            moe.combine(self.expert_out, b.pair_row, self.wts_d, s.E, s.R, b.out, err=b.err)
+            moe.combine(x.expert_out, b.pair_row, x.wts_d, s.E, s.R, b.out, err=b.err)
         elif name == "partial":
-            moe.combine_rank_partial(self.expert_out, b.rank_src_token, b.rank_offsets,
-                                     self.ids_d, b.pair_row, self.wts_d, s.E, self.partial,
+            moe.combine_rank_partial(x.expert_out, b.rank_src_token, b.rank_offsets,
+                                     x.ids_d, b.pair_row, x.wts_d, s.E, x.partial,
                                      err=b.err)
         else:
-            moe.combine_ranks(self.partial, b.token_rank_slot, s.E, s.k, self.out2, err=b.err)
+            moe.combine_ranks(x.partial, b.token_rank_slot, s.E, s.k, x.out2, err=b.err)
 
-    def step(self, ev=None, evict=None) -> None:
-        """One pass; with `ev` (5 events) records between the calls; with
-        `evict` (a callable that enqueues a cache-evicting read) runs it
-        before every call, outside the events."""
+    def step(self, ev=None, evict=None, rotate: bool = True) -> None:
+        """One pass, on the next buffer set if `rotate` (else on the current
+        one again); with `ev` (events) records between the calls; with `evict`
+        (a callable that enqueues a cache-evicting read) runs it before every
+        call, outside the events."""
+        if rotate:
+            self.rotate()
         for i, c in enumerate(self.calls):
             if evict is not None:
                 evict()
@@ -330,7 +381,7 @@ class Rig:
         if ev is not None and evict is None:
             ev[len(self.calls)].record(self.stream)
 
-    def kernel_ms(self, call: str, n: int) -> list:
+    def kernel_ms(self, call: str, n: int, rotate: bool = True) -> list:
         """Durations (ms) of the kernel that `call` launches, inside n whole
         steps: the library has the runtime record an event pair with that
         kernel's dispatch (moe_testing_time_next_launch), so the pair brackets
@@ -348,6 +399,8 @@ class Rig:
             pairs.append((a, b))
         torch.cuda.synchronize()
         for a, b in pairs:
+            if rotate:
+                self.rotate()
             for c in self.calls:
                 if c == call:
                     moe.time_next_launch(a, b)
@@ -355,7 +408,7 @@ class Rig:
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in pairs]
 
-    def per_call_ms(self, n: int, evict=None) -> dict:
+    def per_call_ms(self, n: int, evict=None, rotate: bool = True) -> dict:
         """Per-call durations (ms) over n steps."""
         import torch
 
@@ -364,7 +417,7 @@ class Rig:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
-            self.step(evs[i], evict)
+            self.step(evs[i], evict, rotate)
         torch.cuda.synchronize()
         out = {c: [] for c in self.calls}
         for ev in evs:
@@ -396,10 +449,11 @@ class Rig:
         return a.elapsed_time(b) / n * 1e3
 
     def check_err(self) -> None:
-        e = int(self.buf.err.item())
-        if e != 0:
-            print(f"bench.py: device error word {e} on {self.w.name}", file=sys.stderr)
-            sys.exit(1)
+        for x in self.sets:
+            e = int(x.buf.err.item())
+            if e != 0:
+                print(f"bench.py: device error word {e} on {self.w.name}", file=sys.stderr)
+                sys.exit(1)
 
 
 def copy_reference(dev, gib: float = 1.0, reps: int = 10) -> dict:
@@ -425,6 +479,12 @@ def copy_reference(dev, gib: float = 1.0, reps: int = 10) -> dict:
     return {"bytes": 2 * n, "us": round(ms * 1e3, 1), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
+# Measurement modes: warm = the same buffers back to back; rotated = a
+# different complete buffer set each step; cold = a 1 GiB read evicts L2 and
+# the Infinity Cache before every call.
+MODE_NAMES = ("warm", "rotated", "cold")
+
+
 def sweep(names, dev, with_oracle: bool) -> None:
     import numpy as np
     import torch
@@ -439,6 +499,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
     def evict() -> None:
         torch.sum(flush, dim=0, dtype=torch.int32, out=acc)
 
+    modes = (("warm", None, False), ("rotated", None, True), ("cold", evict, False))
     copy = copy_reference(dev)
     log(f"1 GiB device copy: {copy['GB/s']} GB/s")
     print(json.dumps({"copy_1GiB": copy}), flush=True)
@@ -451,17 +512,18 @@ def sweep(names, dev, with_oracle: bool) -> None:
         flags = opt.split(",")
         mx = 8 if "mxfp8" in flags else 4 if "mxfp4" in flags else 0
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev, two_stage=True, align=align, block=block, mx_bits=mx)
+        rig = Rig(w, dev, two_stage=True, align=align, block=block, mx_bits=mx, sets=2)
         for _ in range(5):
             rig.step()
         res = {"workload": w.describe(), "layout_shape": {"align": align, "block": block},
                "dispatch_format": f"mxfp{mx}" if mx else "bf16",
                "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
-               "copies_per_token": round(rig.C / max(w.T, 1), 4), "calls": {}}
-        for mode, fl in (("warm", None), ("cold", evict)):
+               "copies_per_token": round(rig.C / max(w.T, 1), 4),
+               "imbalance": rig.imbalance(), "calls": {}}
+        for mode, fl, rot in modes:
             meds = {c: [] for c in rig.calls}
             for _ in range(3):
-                ms = rig.per_call_ms(30, fl)
+                ms = rig.per_call_ms(30, fl, rot)
                 for c in rig.calls:
                     meds[c].append(float(np.median(ms[c])))
             for c in rig.calls:
@@ -478,7 +540,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
         tot = sum(rig.nbytes[c] for c in CALLS)
         path2 = ("layout", "pack", "permute") + TWO_STAGE_CALLS
         tot2 = sum(rig.nbytes[c] for c in path2)
-        for mode in ("warm", "cold"):
+        for mode in MODE_NAMES:
             us = sum(res["calls"][c][mode]["us"] for c in CALLS)
             res[mode] = {"us": round(us, 2), "GB/s": round(tot / (us * 1e-6) / 1e9, 1),
                          "pct_peak": round(100 * tot / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
@@ -511,7 +573,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
           "| GB/s | % of 8 TB/s | oracle ms/step |")
     print("|---|---|---|---|---|---|---|---|---|---|")
     for name, r in rows:
-        for mode in ("warm", "cold"):
+        for mode in MODE_NAMES:
             orc = r.get("oracle", {}).get("ms_per_step", "") if mode == "warm" else ""
             print(f"| {name} | {mode} | " + " | ".join(
                 str(r["calls"][c][mode]["us"]) for c in CALLS) +
@@ -522,7 +584,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
           "| path GB/s | % of 8 TB/s |")
     print("|---|---|---|---|---|---|---|---|---|")
     for name, r in rows:
-        for mode in ("warm", "cold"):
+        for mode in MODE_NAMES:
             a, b, p = r["calls"]["partial"][mode], r["calls"]["ranks"][mode], \
                 r["two_stage_" + mode]
             print(f"| {name} | {mode} | {a['us']} | {a['GB/s']} | {b['us']} | {b['GB/s']} "
@@ -542,13 +604,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="complete buffer sets the timed steps rotate through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
                     const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
                           "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,adv:mxfp4",
                     default=None,
-                    metavar="WORKLOADS", help="per-call warm/cold table over workloads")
+                    metavar="WORKLOADS", help="per-call warm/rotated/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (for counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -590,7 +654,7 @@ def main():
         del src, dst
         log(f"copy calibration: 3 x {args.copy_calibration} MiB")
 
-    rig = Rig(w, dev)
+    rig = Rig(w, dev, sets=args.sets)
     step_bytes = sum(rig.nbytes.values())
     stream = rig.stream
 
@@ -599,36 +663,66 @@ def main():
         rig.step()
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps, bracketed by events on the stream the
-    # kernels run on (and a host clock around the synchronisations).
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_begin.record(stream)
-    for _ in range(args.steps):
-        rig.step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    def timed_steps(rotate: bool):
+        """K whole steps bracketed by events on the stream the kernels run on
+        (and a host clock around the synchronisations): ms per step, wall s."""
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        t_begin.record(stream)
+        for _ in range(args.steps):
+            rig.step(rotate=rotate)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_begin.elapsed_time(t_end) / args.steps, time.perf_counter() - t0
 
-    # Second timed pass with an event between every call, for per-kernel
-    # durations and the roofline of the dominant kernel.
+    # The timed region: every step on the next of the rotating buffer sets.
+    ms_per_step, wall = timed_steps(rotate=True)
+    log(f"timed {args.steps} steps (buffer sets rotating): {ms_per_step * 1e3:.1f} us/step")
+    # The same steps on one buffer set, back to back (its inputs partly cached
+    # by the step before).
+    warm_ms, _ = timed_steps(rotate=False)
+    log(f"timed {args.steps} steps (one buffer set): {warm_ms * 1e3:.1f} us/step")
+
+    # Per-call durations: events between the calls (rotating sets), and with a
+    # 1 GiB read that evicts L2 and the Infinity Cache before every call.
+    flush = torch.ones(2 ** 30, dtype=torch.uint8, device=dev)
+    acc = torch.zeros((), dtype=torch.int32, device=dev)
+
+    def evict() -> None:
+        torch.sum(flush, dim=0, dtype=torch.int32, out=acc)
+
     per_call_ms = rig.per_call_ms(args.steps)
+    cold_ms = rig.per_call_ms(args.steps, evict, rotate=False)
+    del flush
     rig.check_err()
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     call_stats = {}
     for c in CALLS:
         ms = float(np.mean(per_call_ms[c]))
+        cms = float(np.mean(cold_ms[c]))
         call_stats[c] = {"us": round(ms * 1e3, 2),
                          "us_median": round(float(np.median(per_call_ms[c])) * 1e3, 2),
                          "bytes": rig.nbytes[c],
-                         "GB/s": round(rig.nbytes[c] / (ms * 1e-3) / 1e9, 1)}
-    # The dominant kernel's own duration: a third pass of whole steps in which
-    # the library records an event pair with the permute's dispatch.
+                         "GB/s": round(rig.nbytes[c] / (ms * 1e-3) / 1e9, 1),
+                         "cold_us": round(cms * 1e3, 2)}
+    cold_step_ms = sum(float(np.mean(cold_ms[c])) for c in CALLS)
+
+    def mode(ms):
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        return {"us_per_step": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+    modes = {"rotated": dict(mode(ms_per_step), note="the value: a different buffer set each "
+                             "step, nothing read is cached from the step before"),
+             "warm": dict(mode(warm_ms), note="one buffer set back to back"),
+             "cold": dict(mode(cold_step_ms), note="sum of per-call means, L2 and Infinity "
+                          "Cache evicted by a 1 GiB read before every call")}
+    # The dominant kernel's own duration: a third pass of whole steps (rotating
+    # sets) in which the library records an event pair with the permute's
+    # dispatch.
     dom = "permute"
     dom_us = float(np.mean(rig.kernel_ms(dom, args.steps))) * 1e3
     rig.check_err()
@@ -653,8 +747,10 @@ def main():
         "config": {"workload": w.describe(), "T": w.T, "H": w.H, "E": w.E, "R": w.R, "k": w.k,
                    "seed": w.seed, "copies_C": rig.C, "pairs_P": rig.P,
                    "copies_per_token": round(rig.C / max(w.T, 1), 4),
-                   "bytes_per_step": step_bytes},
+                   "bytes_per_step": step_bytes, "buffer_sets": args.sets},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "modes": modes,
+        "imbalance": rig.imbalance(),
         "calls": call_stats,
         "rows_per_s": {
             "step_tokens": round(w.T / (ms_per_step * 1e-3)),
