@@ -1312,9 +1312,10 @@ __device__ __forceinline__ void weighted_row_sum(const vec4* rows, int src_row, 
 }
 
 // Combine: one wave per (token, column slice of 64*V vec4); term j is slot j.
-// kStreamLoad: the expert rows are read non-temporally (chosen when they are
-// far larger than the Infinity Cache, so that nothing can be reused from it).
-template <int V, bool kStreamLoad>
+// The expert rows are read non-temporally: an expert kernel writes them
+// between the dispatch and the combine, so nothing of them is left in the
+// caches to reuse, and streaming them keeps them from evicting other lines.
+template <int V>
 __global__ __launch_bounds__(kBlock) void combine_rows(
     const vec4* expert_out, const int32_t* __restrict__ pair_row,
     const float* __restrict__ weights, vec4* out, vec4* out_f32, int T, int k, int nvec,
@@ -1329,16 +1330,16 @@ __global__ __launch_bounds__(kBlock) void combine_rows(
   const bool ok = p >= 0 && p < cap_expert;
   if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
     flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
-  weighted_row_sum<V, kStreamLoad, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
+  weighted_row_sum<V, true, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
                                          (int64_t)t * nvec, slice * kWave * V, nvec);
 }
 
 // Two-stage combine, first stage: one wave per (rank-buffer row, column
 // slice). Row i of rank r's segment holds token t; its terms are the slots j
 // of t whose expert lives on r. The partial rows are stored with ordinary
-// stores so that the home sum finds them in the Infinity Cache; kStreamLoad as
-// in combine_rows.
-template <int V, bool kStreamLoad>
+// stores so that the home sum finds them in the Infinity Cache; the expert
+// rows are streamed as in combine_rows.
+template <int V>
 __global__ __launch_bounds__(kBlock) void rank_partial_rows(
     const vec4* expert_out, const int32_t* __restrict__ rank_src_token,
     const int32_t* __restrict__ rank_offsets, const int32_t* __restrict__ ids,
@@ -1371,7 +1372,7 @@ __global__ __launch_bounds__(kBlock) void rank_partial_rows(
   const bool ok = p >= 0 && p < cap_expert;
   if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
     flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
-  weighted_row_sum<V, kStreamLoad, false>(expert_out, p, wt, __ballot(ok), partial, partial_f32,
+  weighted_row_sum<V, true, false>(expert_out, p, wt, __ballot(ok), partial, partial_f32,
                                           i * nvec, slice * kWave * V, nvec);
 }
 
@@ -1447,16 +1448,6 @@ int copy_vec(int nvec) {
 // waves first find their rank and terms).
 constexpr int kCombineGroups = 8;
 
-// The combine and the partial rows read the expert rows non-temporally when
-// the expert buffer is over twice the 256 MiB Infinity Cache: measured, the
-// ordinary loads win at 240 MiB (prefill, 47.6 against 51.1 us: part of the
-// rows is still in the cache from the step before), non-temporal ones at
-// 768 MiB and 1.75 GiB (skew 158 against 170 us, adv 384 against 405 us).
-constexpr int64_t kStreamExpertRowsAbove = int64_t(512) << 20;
-
-bool stream_expert_rows(int64_t cap_expert, int H) {
-  return cap_expert * int64_t(H) * 2 > kStreamExpertRowsAbove;
-}
 constexpr int kPartialGroups = 3;
 constexpr int kRankSumGroups = 1;
 
@@ -1518,33 +1509,22 @@ struct PermuteLaunch {
 
 template <int V>
 struct CombineLaunch {
-  static void go(bool stream_rows, dim3 grid, hipStream_t st, const vec4* eo,
-                 const int32_t* prow, const float* w, vec4* out, vec4* out32, int T, int k,
-                 int nvec, int slices, int64_t cap_expert, int32_t* err) {
-    if (stream_rows)
-      MOE_LAUNCH((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
-                         out32, T, k, nvec, slices, cap_expert, err);
-    else
-      MOE_LAUNCH((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out,
-                         out32, T, k, nvec, slices, cap_expert, err);
+  static void go(dim3 grid, hipStream_t st, const vec4* eo, const int32_t* prow, const float* w,
+                 vec4* out, vec4* out32, int T, int k, int nvec, int slices, int64_t cap_expert,
+                 int32_t* err) {
+    MOE_LAUNCH(combine_rows<V>, grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T, k, nvec,
+               slices, cap_expert, err);
   }
 };
 
 template <int V>
 struct RankPartialLaunch {
-  static void go(bool stream_rows, dim3 grid, hipStream_t st, const vec4* eo,
-                 const int32_t* src, const int32_t* roff, const int32_t* ids,
-                 const int32_t* prow, const float* w, vec4* part, vec4* part32, int T, int E,
-                 int R, int k, int m, int nvec, int slices, int64_t cap_rank, int64_t cap_expert,
-                 int32_t* err) {
-    if (stream_rows)
-      MOE_LAUNCH((rank_partial_rows<V, true>), grid, dim3(kBlock), 0, st, eo, src, roff,
-                         ids, prow, w, part, part32, T, E, R, k, m, nvec, slices, cap_rank,
-                         cap_expert, err);
-    else
-      MOE_LAUNCH((rank_partial_rows<V, false>), grid, dim3(kBlock), 0, st, eo, src, roff,
-                         ids, prow, w, part, part32, T, E, R, k, m, nvec, slices, cap_rank,
-                         cap_expert, err);
+  static void go(dim3 grid, hipStream_t st, const vec4* eo, const int32_t* src,
+                 const int32_t* roff, const int32_t* ids, const int32_t* prow, const float* w,
+                 vec4* part, vec4* part32, int T, int E, int R, int k, int m, int nvec,
+                 int slices, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
+    MOE_LAUNCH(rank_partial_rows<V>, grid, dim3(kBlock), 0, st, eo, src, roff, ids, prow, w,
+               part, part32, T, E, R, k, m, nvec, slices, cap_rank, cap_expert, err);
   }
 };
 
@@ -1818,8 +1798,7 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
   combine_tiling(nvec, shape->T, shape->T < kFillTokens ? 1 : kCombineGroups, &v, &slices);
-  ByVec<CombineLaunch>::run(v, stream_expert_rows(cap_expert, shape->H),
-                            dim3(blocks_for(int64_t(shape->T) * slices)),
+  ByVec<CombineLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
                             reinterpret_cast<const vec4*>(expert_out), pair_row, topk_weights,
                             reinterpret_cast<vec4*>(out), reinterpret_cast<vec4*>(out_f32),
@@ -1847,7 +1826,7 @@ int moe_combine_rank_partial(const moe_shape_t* shape, const uint16_t* expert_ou
   int v = 1, slices = 1;
   combine_tiling(nvec, max_rows, kPartialGroups, &v, &slices);
   ByVec<RankPartialLaunch>::run(
-      v, stream_expert_rows(cap_expert, shape->H), dim3(blocks_for(max_rows * slices)),
+      v, dim3(blocks_for(max_rows * slices)),
       static_cast<hipStream_t>(stream),
       reinterpret_cast<const vec4*>(expert_out), rank_src_token, rank_offsets, topk_ids, pair_row,
       topk_weights, reinterpret_cast<vec4*>(partial), reinterpret_cast<vec4*>(partial_f32),
