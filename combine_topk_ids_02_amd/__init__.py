@@ -26,7 +26,7 @@ ERRBIT_RANK_CAP = 2
 ERRBIT_EXPERT_CAP = 4
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
-           "moe_layout_workspace_bytes", "moe_dispatch_pack",
+           "moe_dispatch_layout_noalloc", "moe_layout_workspace_bytes", "moe_dispatch_pack",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
@@ -34,7 +34,7 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class MoeShape(ctypes.Structure):
@@ -73,6 +73,8 @@ def lib():
     L.moe_dispatch_layout.restype = ctypes.c_int
     L.moe_dispatch_layout.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                       vp]
+    L.moe_dispatch_layout_noalloc.restype = ctypes.c_int
+    L.moe_dispatch_layout_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_layout_workspace_bytes.restype = ctypes.c_size_t
     L.moe_layout_workspace_bytes.argtypes = [shp]
     L.moe_dispatch_pack.restype = ctypes.c_int
@@ -238,6 +240,29 @@ def layout(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1
         _ptr(_i32(out["pair_row"])), _ptr(workspace), ws_bytes,
         _err(err), _stream(dev))
     _check(st, "moe_dispatch_layout")
+    return out
+
+
+def layout_noalloc(topk_ids: torch.Tensor, E: int, R: int, H: int = 8, *, align: int = 1,
+                   block: int = 0, err=None, out: dict) -> dict:
+    """moe_dispatch_layout_noalloc: the layout into caller-provided `out`
+    tensors (the same keys as layout()), its workspace the library's static
+    array on the current device; this call allocates nothing."""
+    T, k = topk_ids.shape
+    shape = Shape(T, H, E, R, k, align, block)
+    _check_err(err)
+    for key, want in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
+                      ("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                      ("token_rank_slot", (T, R)), ("pair_row", (T, k))):
+        _need(out[key], key, want)
+        if out[key].dtype != torch.int32:
+            raise MoeError(f"{key} must be int32, got {out[key].dtype}")
+    st = lib().moe_dispatch_layout_noalloc(
+        ctypes.byref(shape.c()), _ptr(_i32(topk_ids)), _ptr(out["rank_counts"]),
+        _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]), _err(err),
+        _stream(topk_ids.device))
+    _check(st, "moe_dispatch_layout_noalloc")
     return out
 
 

@@ -36,8 +36,17 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe_dispatch.h"
+
+// The layout workspace of moe_dispatch_layout_noalloc: a static device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes `scratch` itself (its host name is only a stand-in);
+// it passes the device address hipGetSymbolAddress returns for the current
+// device.
+static __device__ __align__(256) int32_t scratch[MOE_LAYOUT_STATIC_WORKSPACE_BYTES / 4];
 
 namespace {
 
@@ -1624,6 +1633,32 @@ int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
   return launch_status();
 }
 
+// Device address of `scratch` per device, looked up once per device with that
+// device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int static_workspace(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+static_assert(size_t(kMaxTiles) * (kMaxExperts + kMaxRanks) * 4 ==
+                  MOE_LAYOUT_STATIC_WORKSPACE_BYTES,
+              "the static workspace holds the largest tile counts");
+
 }  // namespace
 
 extern "C" {
@@ -1687,6 +1722,25 @@ int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32
                two ? static_cast<int32_t*>(workspace) : nullptr};
   launch_layout(g, static_cast<hipStream_t>(stream), a);
   return launch_status();
+}
+
+int moe_dispatch_layout_noalloc(const moe_shape_t* shape, const int32_t* topk_ids,
+                                int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* expert_counts, int32_t* expert_offsets,
+                                int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
+                                void* stream) {
+  if (!shape_ok(shape)) return MOE_ERR_ARG;
+  const size_t need = layout_workspace_bytes(layout_geometry(*shape));
+  if (need > MOE_LAYOUT_STATIC_WORKSPACE_BYTES) return MOE_ERR_ARG;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = static_workspace(&ws);
+    if (st != MOE_OK) return st;
+  }
+  return moe_dispatch_layout(shape, topk_ids, rank_counts, rank_offsets, expert_counts,
+                             expert_offsets, token_rank_slot, pair_row, ws,
+                             ws ? size_t(MOE_LAYOUT_STATIC_WORKSPACE_BYTES) : 0, err_word,
+                             stream);
 }
 
 int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,

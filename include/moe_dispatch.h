@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 5
+#define MOE_DISPATCH_ABI_VERSION 6
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -141,6 +141,34 @@ int moe_dispatch_layout(const moe_shape_t* shape, const int32_t* topk_ids, int32
  * multiple of 4) * (E + R) when there is more than one tile (at most
  * 64 * 1088 * 4 = 278,528), else 0. 0 for an invalid shape. */
 size_t moe_layout_workspace_bytes(const moe_shape_t* shape);
+
+/* Size of the library's static layout workspace (one per GPU): 64 tiles of
+ * (1024 + 64) int32 tile counts, the most any accepted shape needs. */
+#define MOE_LAYOUT_STATIC_WORKSPACE_BYTES 278528
+
+/*
+ * Dispatch, step 1, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It is moe_dispatch_layout with its workspace taken from a static device
+ * array inside the library instead of the caller's, and otherwise the same:
+ * the same arguments minus the workspace, the same kernels (one or two
+ * launches, chosen by size as with a workspace) and the same results.
+ *  - The array is MOE_LAYOUT_STATIC_WORKSPACE_BYTES per GPU, enough for every
+ *    shape the library accepts; a shape needing more is an argument error.
+ *  - The array of the current device is used (the stream's device must be
+ *    current). Its address is looked up on the first call on each device; the
+ *    array lives until the process ends.
+ *  - Every call on one GPU shares that GPU's array: calls that run at the same
+ *    time on one GPU (for instance on two streams) race and must not overlap.
+ *    Nothing in it needs clearing: a call writes every entry it reads.
+ *  - No memory is allocated (no hipMalloc, no allocating library call).
+ * Returns MOE_ERR_HIP if the array's address cannot be obtained.
+ */
+int moe_dispatch_layout_noalloc(const moe_shape_t* shape, const int32_t* topk_ids,
+                                int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* expert_counts, int32_t* expert_offsets,
+                                int32_t* token_rank_slot, int32_t* pair_row, int32_t* err_word,
+                                void* stream);
 
 /*
  * Dispatch, step 2: pack ([A2A] sec 1.3 third answer and sec 3.2: a token is

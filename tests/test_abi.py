@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 5
+    assert L.moe_abi_version() == moe.ABI_VERSION == 6
 
 
 def test_timing_hook_takes_both_events_or_neither():
@@ -247,3 +247,28 @@ def test_binding_rejects_wrong_dtypes_before_any_pointer():
         with pytest.raises(moe.MoeError, match="err must be an int32"):
             moe.combine(_z((cap, H), i16), ids, _z((T, k), torch.float32), E, R,
                         _z((T, H), i16), err=bad)
+
+
+def test_noalloc_layout_rejects_bad_shapes_before_anything():
+    """The allocation-free layout checks the shape before it looks up its static
+    workspace or launches anything (no GPU here)."""
+    L = moe.lib()
+    bad = moe.MoeShape(T=8, H=16, E=10, R=4, k=2)  # E % R != 0
+    args = [FAKE] * 7 + [None, None]
+    assert L.moe_dispatch_layout_noalloc(ctypes.byref(bad), *args) == moe.MOE_ERR_ARG
+    assert L.moe_dispatch_layout_noalloc(None, *args) == moe.MOE_ERR_ARG
+    too_many = moe.MoeShape(T=8, H=16, E=8, R=4, k=17)
+    assert L.moe_dispatch_layout_noalloc(ctypes.byref(too_many), *args) == moe.MOE_ERR_ARG
+
+
+def test_static_workspace_covers_every_accepted_shape():
+    """MOE_LAYOUT_STATIC_WORKSPACE_BYTES is the largest workspace any accepted
+    shape asks for (64 tiles of E + R = 1088 columns)."""
+    text = open(HEADER).read()
+    cap = int(re.search(r"MOE_LAYOUT_STATIC_WORKSPACE_BYTES (\d+)", text).group(1))
+    worst = moe.layout_workspace_bytes(moe.Shape(64 * 256 * 8, 8, 1024, 64, 1))
+    assert worst == cap == 278528
+    for T in (0, 256, 257, 16384, 16385, 70000, 2 ** 20):
+        for E, R, k in ((1024, 64, 1), (384, 8, 6), (1024, 1, 16)):
+            if moe.lib().moe_layout_workspace_bytes(ctypes.byref(moe.MoeShape(T, 8, E, R, k))):
+                assert moe.layout_workspace_bytes(moe.Shape(T, 8, E, R, k)) <= cap
