@@ -170,23 +170,30 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 template <int kRB> struct RankMask { using type = uint32_t; };
 template <> struct RankMask<64> { using type = uint64_t; };
 
-// Copies per rank over the wave's 64 tokens (one rank set per lane), in lane r.
-template <int kRB, typename Mask>
-__device__ __forceinline__ int wave_rank_counts(Mask mask, int R) {
+// Copies per rank over the wave's 64 tokens (one rank set of at most 8 ranks
+// per lane), in lane r: one ballot per rank.
+__device__ __forceinline__ int wave_rank_counts8(uint32_t mask) {
   int mine = 0;
-  if (kRB == 8) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int c = __popcll(__ballot((mask >> r) & 1));
-      mine = lane_id() == r ? c : mine;
-    }
-  } else {
-    for (int r = 0; r < R; ++r) {
-      const int c = __popcll(__ballot((mask >> r) & 1));
-      mine = lane_id() == r ? c : mine;
-    }
+  for (int r = 0; r < 8; ++r) {
+    const int c = __popcll(__ballot((mask >> r) & 1));
+    mine = lane_id() == r ? c : mine;
   }
   return mine;
+}
+
+// Adds one to counts[r] for every rank r in the lane's rank set (LDS
+// atomics). Used for more than 8 ranks, where a ballot per rank and a
+// per-lane pick of the counts gave wrong copies per rank on MI355X in one
+// form of the layout (64-bit rank sets, k = 4, the tile ranked before the
+// counting pass) for reasons not found in the generated code.
+template <typename Mask>
+__device__ __forceinline__ void count_rank_set(int32_t* counts, Mask mask) {
+  while (mask) {
+    const int r = __ffsll((unsigned long long)mask) - 1;
+    mask &= mask - 1;
+    atomicAdd(&counts[r], 1);
+  }
 }
 
 // Column totals, exclusive scans and the tile's first rows, in one pass: for
@@ -344,9 +351,12 @@ __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
         mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
       }
     }
-    rc += wave_rank_counts<kRB>(mask, g.R);
+    if (kRB == 8)
+      rc += wave_rank_counts8(uint32_t(mask));
+    else
+      count_rank_set(s_h + g.E, mask);
   }
-  if (lane < g.R && rc) atomicAdd(&s_h[g.E + lane], rc);
+  if (kRB == 8 && lane < g.R && rc) atomicAdd(&s_h[g.E + lane], rc);
   __syncthreads();
   for (int c = tid; c < g.ncols; c += kCountThreads)
     hist[(int64_t)c * g.tiles_pad + blockIdx.x] = s_h[c];
@@ -496,8 +506,12 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 #pragma unroll
     for (int j = 0; j < KR; ++j)
       if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
-    const int copies = wave_rank_counts<kRB>(mask, g.R);  // lane r: tokens with a copy on r
-    if (lane < g.R) cnt_w[g.E + lane] = copies;
+    if (kRB == 8) {
+      const int copies = wave_rank_counts8(uint32_t(mask));  // lane r: tokens with a copy on r
+      if (lane < g.R) cnt_w[g.E + lane] = copies;
+    } else {
+      count_rank_set(cnt_w + g.E, mask);  // the wave's rank columns start at zero
+    }
   };
 
   // Per column: each ranking wave's first row, then advance the running base
@@ -649,22 +663,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
               tmask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
             }
           }
-          if (kRB == 8) {
-            c += wave_rank_counts<kRB>(tmask, g.R);
-          } else {
-            // Wider rank sets: one LDS atomic per rank of the token (at most
-            // k per token rather than R ballots per 64 tokens). The per-lane
-            // selection of ballot counts (wave_rank_counts) gave wrong copies
-            // per rank here for k = 4 with R > 32, reproducibly on MI355X
-            // though not on every call, while the same ballots added by one
-            // lane, or these atomics, gave the right ones.
-            Mask mm = tmask;
-            while (mm) {
-              const int r = __ffsll((unsigned long long)mm) - 1;
-              mm &= mm - 1;
-              atomicAdd(&cnt[g.E + r], 1);
-            }
-          }
+          if (kRB == 8)
+            c += wave_rank_counts8(uint32_t(tmask));
+          else
+            count_rank_set(cnt + g.E, tmask);  // at most k atomics per token
         }
         (before ? rc_pre : rc_tot) += c;
       }

@@ -253,7 +253,8 @@ def test_timing_hook_brackets_the_next_kernel():
 
 
 WIDE_RANK_SETS = [(1024, 512, 64, 4), (4096, 480, 48, 4), (8192, 64, 64, 4), (12288, 1024, 64, 4),
-                  (3000, 640, 40, 5), (2048, 512, 64, 6)]
+                  (3000, 640, 40, 5), (2048, 512, 64, 6), (1024, 64, 64, 4), (1024, 480, 48, 4),
+                  (700, 96, 16, 4)]
 
 
 @pytest.mark.parametrize("case", WIDE_RANK_SETS, ids=[f"T{c[0]}_E{c[1]}_R{c[2]}_k{c[3]}"
