@@ -101,7 +101,7 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-OUR_KERNELS = ("layout_tiles", "pack_rows", "permute_rows", "combine_rows")
+OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "combine_rows")
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: float, workload: str) -> dict:
@@ -141,7 +141,14 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: float, workload: 
                 "fetch_kib_per_launch": fetch[k], "write_kib_per_launch": write[k],
                 "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
                 "source_sha256_16": source_digest()}
-    rec[workload] = out
+    try:  # other workloads' entries are kept
+        with open(TRAFFIC_FILE) as f:
+            prev = json.load(f)
+    except (OSError, ValueError):
+        prev = {}
+    prev.update(rec)
+    prev[workload] = out
+    rec = prev
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
