@@ -1168,7 +1168,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
     const int32_t* __restrict__ expert_offsets, vec4* expert_buf, vec4* expert_scale,
     int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int block,
     int nvec, int nvec_s, int pad_waves, int64_t cap_rank, int64_t cap_expert,
-    int32_t* err_word) {
+    int early_row, int32_t* err_word) {
   const int lane = lane_id();
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (gw < pad_waves) {
@@ -1179,11 +1179,16 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   // Two rounds of loads: the offsets and the row's token, then the token's
   // ids and pair rows with the row itself right behind them. The grid is
   // rounded up to whole workgroups, so i can pass the last row: the token's
-  // load is clamped into the buffer and such waves return below.
+  // load is clamped into the buffer and such waves return below. With
+  // early_row (small batches, where waiting for each round is most of the
+  // time and reading a row for nothing is cheap) the row is requested in the
+  // first round, clamped into the buffer, before it is known to be in use.
   const int64_t rows = min((int64_t)rank_offsets[R], cap_rank);
   const int end_any = rank_offsets[min(lane, R - 1) + 1];
   const int64_t ic = min(i, cap_rank - 1);
   const int t = ic >= 0 ? rank_src_token[ic] : -1;
+  vec4 first[V];
+  if (early_row) load_first_pass<V, true>(rank_buf + ic * nvec, nvec, first);
   const int end = lane < R ? end_any : 0x7FFFFFFF;
   if (i >= rows || t < 0 || t >= T) return;
   const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
@@ -1193,8 +1198,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   // The packed row is read once and the expert rows are not read again here:
   // both streamed.
   const vec4* src = rank_buf + i * nvec;
-  vec4 first[V];
-  load_first_pass<V, true>(src, nvec, first);
+  if (!early_row) load_first_pass<V, true>(src, nvec, first);
   // MX: a scale row of at most 64 vec4 (H <= 32768) is one partial pass,
   // requested with the code row (clamped lanes; lanes >= nvec_s store nothing)
   const bool short_scales = kMx && nvec_s <= kWave;
@@ -1322,11 +1326,60 @@ __device__ __forceinline__ void weighted_row_sum(const vec4* rows, int src_row, 
   }
 }
 
+// weighted_row_sum with the rows of up to KB terms requested at once, then
+// added in the same order (the same fused multiply-adds, so the same sums):
+// for small batches, where a wave's time is its rounds of loads.
+template <int V, int KB, bool kStreamLoad, bool kStreamStore>
+__device__ __forceinline__ void weighted_row_sum_batched(const vec4* rows, int src_row, float wt,
+                                                         uint64_t terms, vec4* out, vec4* out_f32,
+                                                         int64_t orow, int cb, int nvec) {
+  const int lane = lane_id();
+  if (cb + kWave * V > nvec) {
+    weighted_row_sum<V, kStreamLoad, kStreamStore>(rows, src_row, wt, terms, out, out_f32, orow,
+                                                   cb, nvec);
+    return;
+  }
+  float acc[V][8];
+#pragma unroll
+  for (int q = 0; q < V; ++q)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[q][x] = 0.0f;
+  uint64_t s = terms;
+  while (s) {
+    vec4 y[KB][V];
+    int js[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      js[b] = -1;
+      if (s) {
+        const int j = __ffsll((unsigned long long)s) - 1;
+        s &= s - 1;
+        js[b] = j;
+        const vec4* src = rows + (int64_t)read_lane(src_row, j) * nvec + cb + lane;
+#pragma unroll
+        for (int q = 0; q < V; ++q) y[b][q] = load_row<kStreamLoad>(src + q * kWave);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      if (js[b] >= 0) {
+        const float w = __int_as_float(read_lane(__float_as_int(wt), js[b]));
+#pragma unroll
+        for (int q = 0; q < V; ++q) fma_bf16x8(acc[q], w, y[b][q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < V; ++q)
+    store_sum<kStreamStore>(acc[q], out, out_f32, orow + cb + q * kWave + lane);
+}
+
 // Combine: one wave per (token, column slice of 64*V vec4); term j is slot j.
 // The expert rows are read non-temporally: an expert kernel writes them
 // between the dispatch and the combine, so nothing of them is left in the
 // caches to reuse, and streaming them keeps them from evicting other lines.
-template <int V>
+// kBatch: all of a token's slots are requested at once (small batches).
+template <int V, bool kBatch>
 __global__ __launch_bounds__(kBlock) void combine_rows(
     const vec4* expert_out, const int32_t* __restrict__ pair_row,
     const float* __restrict__ weights, vec4* out, vec4* out_f32, int T, int k, int nvec,
@@ -1341,8 +1394,12 @@ __global__ __launch_bounds__(kBlock) void combine_rows(
   const bool ok = p >= 0 && p < cap_expert;
   if (slice == 0 && __ballot(p >= 0 && !ok) && lane == 0)
     flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
-  weighted_row_sum<V, true, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
-                                         (int64_t)t * nvec, slice * kWave * V, nvec);
+  if (kBatch)
+    weighted_row_sum_batched<V, 8, true, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
+                                               (int64_t)t * nvec, slice * kWave * V, nvec);
+  else
+    weighted_row_sum<V, true, true>(expert_out, p, wt, __ballot(ok), out, out_f32,
+                                    (int64_t)t * nvec, slice * kWave * V, nvec);
 }
 
 // Two-stage combine, first stage: one wave per (rank-buffer row, column
@@ -1505,26 +1562,31 @@ struct PermuteLaunch {
                  const int32_t* roff, const int32_t* ids, const int32_t* prow,
                  const int32_t* ecnt, const int32_t* eoff, vec4* eb, vec4* es, int32_t* esrc,
                  int T, int E, int R, int k, int m, int block, int nvec, int nvec_s,
-                 int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
+                 int pad_waves, int64_t cap_rank, int64_t cap_expert, int early_row,
+                 int32_t* err) {
     if (rs)
       MOE_LAUNCH((permute_rows<V, true>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
                          ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
-                         pad_waves, cap_rank, cap_expert, err);
+                         pad_waves, cap_rank, cap_expert, early_row, err);
     else
       MOE_LAUNCH((permute_rows<V, false>), grid, dim3(kBlock), 0, st, rb, rs, src, roff,
                          ids, prow, ecnt, eoff, eb, es, esrc, T, E, R, k, m, block, nvec, nvec_s,
-                         pad_waves, cap_rank, cap_expert, err);
+                         pad_waves, cap_rank, cap_expert, early_row, err);
   }
 };
 
 
 template <int V>
 struct CombineLaunch {
-  static void go(dim3 grid, hipStream_t st, const vec4* eo, const int32_t* prow, const float* w,
-                 vec4* out, vec4* out32, int T, int k, int nvec, int slices, int64_t cap_expert,
-                 int32_t* err) {
-    MOE_LAUNCH(combine_rows<V>, grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T, k, nvec,
-               slices, cap_expert, err);
+  static void go(bool batch, dim3 grid, hipStream_t st, const vec4* eo, const int32_t* prow,
+                 const float* w, vec4* out, vec4* out32, int T, int k, int nvec, int slices,
+                 int64_t cap_expert, int32_t* err) {
+    if (batch)
+      MOE_LAUNCH((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T,
+                 k, nvec, slices, cap_expert, err);
+    else
+      MOE_LAUNCH((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32,
+                 T, k, nvec, slices, cap_expert, err);
   }
 };
 
@@ -1578,7 +1640,8 @@ int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_
                             topk_ids, pair_row, expert_counts, expert_offsets,
                             static_cast<vec4*>(expert_rows), static_cast<vec4*>(expert_scale),
                             expert_src_pair, sh.T, sh.E, sh.R, sh.k, sh.E / sh.R, sh.block, nvec,
-                            nvec_s, pad_waves, cap_rank, cap_expert, err_word);
+                            nvec_s, pad_waves, cap_rank, cap_expert,
+                            max_rows > 0 && sh.T < kFillTokens ? 1 : 0, err_word);
   return launch_status();
 }
 
@@ -1854,7 +1917,9 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
   combine_tiling(nvec, shape->T, shape->T < kFillTokens ? 1 : kCombineGroups, &v, &slices);
-  ByVec<CombineLaunch>::run(v, dim3(blocks_for(int64_t(shape->T) * slices)),
+  // Small batches: one 1 KiB group per wave and every slot requested at once.
+  ByVec<CombineLaunch>::run(v, shape->T < kFillTokens && v <= 2,
+                            dim3(blocks_for(int64_t(shape->T) * slices)),
                             static_cast<hipStream_t>(stream),
                             reinterpret_cast<const vec4*>(expert_out), pair_row, topk_weights,
                             reinterpret_cast<vec4*>(out), reinterpret_cast<vec4*>(out_f32),

@@ -452,6 +452,10 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
     rep.access(tag, "rank_offsets", [R], "load")
     ic = np.minimum(i, c.cap_rank - 1)
     rep.access(tag, "rank_src_token", ic[ic >= 0], "load")
+    V = copy_vec(nvec)
+    if max_rows > 0 and T < FILL_TOKENS:  # small batches: the row requested with the first round
+        first, _, _ = fan_out_cols(V, nvec)
+        rep.access(tag, "rank_buf", rows_cols(ic, first, nvec), "load")
     rows = min(int(lay["rank_offsets"][R]), c.cap_rank)
     src = np.full(i.shape, -1, np.int64)
     src[ic >= 0] = rank_src[ic[ic >= 0]]
@@ -462,7 +466,6 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
     at = t[:, None] * k + np.minimum(LANE, k - 1)[None, :]
     rep.access(tag, "topk_ids", at, "load")
     rep.access(tag, "pair_row", at, "load")
-    V = copy_vec(nvec)
     first, loads, stores = fan_out_cols(V, nvec)
     rep.access(tag, "rank_buf", rows_cols(i, np.concatenate([first, loads]), nvec), "load")
     if nvec_s and nvec_s <= W:
