@@ -35,9 +35,9 @@ def assert_clean(rep: lm.Report, what: str):
     assert not rep.violations, f"{what}: {rep.violations[:4]}"
 
 
-@pytest.mark.parametrize("lo,hi", [(0, 96), (1000, 1100), (1100, 1400)])
+@pytest.mark.parametrize("lo,hi", [(0, 192), (1000, 1100), (1100, 1400)])
 def test_whole_path_random_shapes(lo, hi):
-    """The whole-path random-shape generator of the GPU tests: seeds 0-95 (run
+    """The whole-path random-shape generator of the GPU tests: seeds 0-191 (run
     on the GPU) and 1000-1399 (not run there), one- and two-stage."""
     for s in range(lo, hi):
         c = rs.draw(s)
@@ -49,7 +49,7 @@ def test_whole_path_random_shapes(lo, hi):
 
 @pytest.mark.parametrize("bits", [8, 4])
 def test_mx_random_shapes(bits):
-    for s in list(range(200, 216)) + list(range(10000, 10060)):
+    for s in list(range(200, 224)) + list(range(10000, 10060)):
         c = rs.draw(s, mx=True)
         ids, _, _ = rs.inputs(c)
         assert_clean(lm.mx(case_of(c), ids, bits), f"mx{bits} seed {s}")

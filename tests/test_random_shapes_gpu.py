@@ -88,7 +88,7 @@ class layout_form:
         moe.lib().moe_testing_set_layout_match(self.old_match)
 
 
-CASES = [draw(s) for s in range(96)]
+CASES = [draw(s) for s in range(192)]
 
 
 @pytest.mark.parametrize("c", CASES, ids=[f"s{c['seed']}" for c in CASES])
@@ -103,7 +103,7 @@ def test_random_shape_one_stage(c):
     compare(gpu, ref, f"random {c}")
 
 
-TWO_STAGE = [c for c in CASES if c["align"] == 1 and c["block"] == 0][:24]
+TWO_STAGE = [c for c in CASES if c["align"] == 1 and c["block"] == 0][:48]
 
 
 @pytest.mark.parametrize("c", TWO_STAGE, ids=[f"s{c['seed']}" for c in TWO_STAGE])
@@ -116,7 +116,7 @@ def test_random_shape_two_stage(c):
         check(hid, ids, wts, c["E"], c["R"], y, f"random two-stage {c}")
 
 
-MX_CASES = [draw(200 + s, mx=True) for s in range(16)]
+MX_CASES = [draw(200 + s, mx=True) for s in range(24)]
 
 
 @pytest.mark.parametrize("c", MX_CASES, ids=[f"s{c['seed']}" for c in MX_CASES])
