@@ -165,10 +165,30 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 }
 
 // Rank sets of a token as bit masks. kRB is a compile-time bound on R (8, 32
-// or 64): 32-bit masks up to 32 ranks, 64-bit above; with kRB = 8 the loops
+// or 64): one 32-bit word up to 32 ranks, two above; with kRB = 8 the loops
 // over ranks are unrolled.
-template <int kRB> struct RankMask { using type = uint32_t; };
-template <> struct RankMask<64> { using type = uint64_t; };
+template <int kRB>
+struct RankSet {
+  static constexpr int NW = kRB > 32 ? 2 : 1;  // 32-bit words
+  uint32_t w[NW];
+  __device__ __forceinline__ RankSet() {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = 0;
+  }
+  // Adds rank r (< kRB) when `on`.
+  __device__ __forceinline__ void add(int r, bool on) {
+    const uint32_t bit = uint32_t(on) << (r & 31);
+    if (NW == 1) {
+      w[0] |= bit;
+    } else {
+      w[0] |= r < 32 ? bit : 0u;
+      w[NW - 1] |= r >= 32 ? bit : 0u;
+    }
+  }
+  __device__ __forceinline__ bool has(int r) const {
+    return (((NW == 1 || r < 32) ? w[0] : w[NW - 1]) >> (r & 31)) & 1;
+  }
+};
 
 // Copies per rank over the wave's 64 tokens (one rank set of at most 8 ranks
 // per lane), in lane r: one ballot per rank.
@@ -186,26 +206,46 @@ __device__ __forceinline__ int wave_rank_counts8(uint32_t mask) {
 // atomics). Used for more than 8 ranks, where a ballot per rank and a
 // per-lane pick of the counts gave wrong copies per rank on MI355X in one
 // form of the layout (64-bit rank sets, k = 4, the tile ranked before the
-// counting pass) for reasons not found in the generated code.
-template <typename Mask>
-__device__ __forceinline__ void count_rank_set(int32_t* counts, Mask mask) {
-  while (mask) {
-    const int r = __ffsll((unsigned long long)mask) - 1;
-    mask &= mask - 1;
-    atomicAdd(&counts[r], 1);
+// counting pass) for reasons not found in the generated code; a later form
+// with 64-bit masks and these atomics failed the same way after an unrelated
+// change, so rank sets are kept in 32-bit words throughout.
+template <int kRB>
+__device__ __forceinline__ void count_rank_set(int32_t* counts, RankSet<kRB> set) {
+#pragma unroll
+  for (int i = 0; i < RankSet<kRB>::NW; ++i) {
+    uint32_t m = set.w[i];
+    while (m) {
+      const int r = __ffs(m) - 1;
+      m &= m - 1;
+      atomicAdd(&counts[32 * i + r], 1);
+    }
   }
+}
+
+// Sum over the ranking waves of their counts in column c (0 without them).
+__device__ __forceinline__ int own_sum(const int32_t* s_own, int ncols, int c) {
+  if (!s_own) return 0;
+  int v[kOwnWaves];  // all reads first: one LDS round trip
+#pragma unroll
+  for (int w = 0; w < kOwnWaves; ++w) v[w] = s_own[w * ncols + c];
+  int sum = 0;
+#pragma unroll
+  for (int w = 0; w < kOwnWaves; ++w) sum += v[w];
+  return sum;
 }
 
 // Column totals, exclusive scans and the tile's first rows, in one pass: for
 // every column c, count = s_tot[c] + s_pre[c] (tokens from the tile on, and
-// before it), offset = exclusive prefix of the run lengths (experts in id
+// before it) + the ranking waves' counts s_own[w][c] when given (then the
+// tile's tokens were not counted into s_tot), offset = exclusive prefix of the run lengths (experts in id
 // order over waves 0..7, ranks in rank order in wave 8), and s_pre[c] becomes
 // offset + (count before the tile), the tile's first row in that column. An
 // expert's run length is its count, rounded up to a multiple of `align`, or
 // the fixed `block` when block > 0. The workgroup that is `writer` also
 // stores the counts and offsets.
-__device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R, int align,
-                             int block, int32_t* s_tmp /* [16] */, bool writer,
+__device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, const int32_t* s_own,
+                             int ncols, int E, int R, int align, int block,
+                             int32_t* s_tmp /* [16] */, bool writer,
                              int32_t* expert_counts, int32_t* expert_offsets,
                              int32_t* rank_counts, int32_t* rank_offsets) {
   const int tid = threadIdx.x;
@@ -221,7 +261,7 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int i = lo + q;
-      const int cnt = (q < per && i < E) ? s_tot[i] + s_pre[i] : 0;
+      const int cnt = (q < per && i < E) ? s_tot[i] + s_pre[i] + own_sum(s_own, ncols, i) : 0;
       if (writer && q < per && i < E) expert_counts[i] = cnt;
       run_len[q] = block > 0 ? ((q < per && i < E) ? block : 0)
                              : (align == 1 ? cnt : (cnt + align - 1) / align * align);
@@ -230,7 +270,7 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, int E, int R,
     x = wave_inclusive_scan(sum);
     if (lane == kWave - 1) s_tmp[wave] = x;
   } else if (wave == 8) {
-    const int v = lane < R ? s_tot[E + lane] + s_pre[E + lane] : 0;
+    const int v = lane < R ? s_tot[E + lane] + s_pre[E + lane] + own_sum(s_own, ncols, E + lane) : 0;
     const int inc = wave_inclusive_scan(v);
     if (lane < R) {
       s_pre[E + lane] += inc - v;
@@ -324,7 +364,6 @@ template <int K, int kRB>
 __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
                                                               const int32_t* __restrict__ ids,
                                                               int32_t* __restrict__ hist) {
-  using Mask = typename RankMask<kRB>::type;
   constexpr int KR = K > 0 ? K : kMaxK;
   const int k = K > 0 ? K : g.k;
   __shared__ int32_t s_h[kMaxExperts + kMaxRanks + 1];  // + a slot for invalid ids
@@ -342,19 +381,19 @@ __global__ __launch_bounds__(kCountThreads) void layout_count(LayoutGeom g,
 #pragma unroll
     for (int j = 0; j < KR; ++j)
       if (j < k) ev[j] = in ? ids[(int64_t)t * k + j] : -1;
-    Mask mask = 0;
+    RankSet<kRB> set;
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
       if (j < k) {
         const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
         atomicAdd(&s_h[valid ? ev[j] : g.ncols], 1);
-        mask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+        set.add(rank_of(valid ? ev[j] : 0, g.inv_m), valid);
       }
     }
     if (kRB == 8)
-      rc += wave_rank_counts8(uint32_t(mask));
+      rc += wave_rank_counts8(set.w[0]);
     else
-      count_rank_set(s_h + g.E, mask);
+      count_rank_set(s_h + g.E, set);
   }
   if (kRB == 8 && lane < g.R && rc) atomicAdd(&s_h[g.E + lane], rc);
   __syncthreads();
@@ -379,7 +418,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
     int32_t* __restrict__ pair_row, int32_t* err_word) {
   constexpr int KR = K > 0 ? K : kMaxK;
-  using Mask = typename RankMask<kRB>::type;
   const int k = K > 0 ? K : g.k;
   extern __shared__ __align__(16) int32_t smem[];
   // With lds_match: per ranking wave a table of 64 lane masks (first, so
@@ -423,7 +461,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   const int ti = wave * kTokW + lane;  // this lane's token in the sub-tile (lanes < kTokW)
   int ex[KC], rk[KC];  // per chunk: this lane's expert (or -1) and its rank in the wave
   int own[KR];         // ids of token ti, for its rank set
-  Mask mask = 0;       // rank set of token ti (lanes < kTokW)
+  RankSet<kRB> mask;   // rank set of token ti (lanes < kTokW)
 
   // Ranks inside the sub-tile from ex[] and own[]: rk[] relative to the
   // wave's running counts, which it advances (cnt_w), and the wave's copies
@@ -502,12 +540,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 #pragma unroll
     for (int ch = 0; ch < KC; ++ch)
       if (ch < nch) rk[ch] += __shfl(cnt_old[ch], lead[ch], kWave);
-    mask = 0;
+    mask = RankSet<kRB>();
 #pragma unroll
     for (int j = 0; j < KR; ++j)
-      if (j < k && own[j] >= 0 && own[j] < g.E) mask |= Mask(1) << rank_of(own[j], g.inv_m);
+      if (j < k) mask.add(rank_of(own[j] >= 0 && own[j] < g.E ? own[j] : 0, g.inv_m),
+                          own[j] >= 0 && own[j] < g.E);
     if (kRB == 8) {
-      const int copies = wave_rank_counts8(uint32_t(mask));  // lane r: tokens with a copy on r
+      const int copies = wave_rank_counts8(mask.w[0]);  // lane r: tokens with a copy on r
       if (lane < g.R) cnt_w[g.E + lane] = copies;
     } else {
       count_rank_set(cnt_w + g.E, mask);  // the wave's rank columns start at zero
@@ -551,10 +590,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       }
     }
     auto write_slot = [&](int r) {
-      const uint64_t on = __ballot((mask >> r) & 1);
+      const bool has = mask.has(r);
+      const uint64_t on = __ballot(has);
       if (tok_lane)
         token_rank_slot[(int64_t)(t0 + ti) * g.R + r] =
-            ((mask >> r) & 1) ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
+            has ? cnt_w[g.E + r] + __popcll(on & lanes_below()) : -1;
     };
     if (kRB == 8) {
 #pragma unroll
@@ -584,10 +624,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
       if (j < k) own[j] = tok_lane ? ids[(int64_t)(tile_lo + ti) * k + j] : -1;
   }
 
+  // One tile (T <= 256, one launch): the ranking waves' own counts are the
+  // totals, so there is no counting pass; the scan adds them up.
+  const bool own_counts = !kFromHist && g.ntiles == 1;
+
   // The first batch of ids for the counting pass is requested before the
   // LDS is cleared.
   int32_t nxt[IdLanes<K>::NW];
-  if (!kFromHist) load_tokens<K>(ids, g.T, k, 0, nxt);
+  if (!kFromHist && !own_counts) load_tokens<K>(ids, g.T, k, 0, nxt);
 
   for (int c = tid; c < g.ncols; c += kLayoutThreads) {
     s_pre[c] = 0;
@@ -639,7 +683,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
     int rc_pre = 0, rc_tot = 0;  // lane r: this wave's copies on rank r, before / from the tile
     __syncthreads();  // s_pre / s_tot / s_cnt zeroed
     if (early && ranker) rank_in_wave();
-    for (int b0 = 0; b0 < g.T; b0 += L::BATCH) {
+    for (int b0 = 0; !own_counts && b0 < g.T; b0 += L::BATCH) {
       int32_t cur[L::NW];
 #pragma unroll
       for (int x = 0; x < L::NW; ++x) cur[x] = nxt[x];
@@ -654,19 +698,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 #pragma unroll
         for (int u = 0; u < L::TPL; ++u) {
           const int32_t* ev = cur + q * L::VPL * 4 + u * K;
-          Mask tmask = 0;
+          RankSet<kRB> tset;
 #pragma unroll
           for (int j = 0; j < KR; ++j) {
             if (j < k) {
               const bool valid = uint32_t(ev[j]) < uint32_t(g.E);
               atomicAdd(&cnt[valid ? ev[j] : g.ncols], 1);
-              tmask |= Mask(valid) << rank_of(valid ? ev[j] : 0, g.inv_m);
+              tset.add(rank_of(valid ? ev[j] : 0, g.inv_m), valid);
             }
           }
           if (kRB == 8)
-            c += wave_rank_counts8(uint32_t(tmask));
+            c += wave_rank_counts8(tset.w[0]);
           else
-            count_rank_set(cnt + g.E, tmask);  // at most k atomics per token
+            count_rank_set(cnt + g.E, tset);  // at most k atomics per token
         }
         (before ? rc_pre : rc_tot) += c;
       }
@@ -680,8 +724,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
 
   // 2.-3. Counts, exclusive scans (experts in id order, ranks in rank order)
   //    and the absolute first row of this tile in every column (in s_pre).
-  scan_columns(s_pre, s_tot, g.E, g.R, g.align, g.block, s_tmp, blockIdx.x == 0, expert_counts,
-               expert_offsets, rank_counts, rank_offsets);
+  scan_columns(s_pre, s_tot, own_counts ? s_cnt : nullptr, g.ncols, g.E, g.R, g.align, g.block,
+               s_tmp, blockIdx.x == 0, expert_counts, expert_offsets, rank_counts, rank_offsets);
 
   if (early) {
     chain_columns();
@@ -1581,12 +1625,17 @@ struct CombineLaunch {
   static void go(bool batch, dim3 grid, hipStream_t st, const vec4* eo, const int32_t* prow,
                  const float* w, vec4* out, vec4* out32, int T, int k, int nvec, int slices,
                  int64_t cap_expert, int32_t* err) {
-    if (batch)
-      MOE_LAUNCH((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T,
-                 k, nvec, slices, cap_expert, err);
-    else
-      MOE_LAUNCH((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32,
-                 T, k, nvec, slices, cap_expert, err);
+    // The batched form holds all k slots' rows at once: small V only (the
+    // caller picks it for V <= 2), so it is not built for wider registers.
+    if constexpr (V <= 2) {
+      if (batch) {
+        MOE_LAUNCH((combine_rows<V, true>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32,
+                   T, k, nvec, slices, cap_expert, err);
+        return;
+      }
+    }
+    MOE_LAUNCH((combine_rows<V, false>), grid, dim3(kBlock), 0, st, eo, prow, w, out, out32, T,
+               k, nvec, slices, cap_expert, err);
   }
 };
 

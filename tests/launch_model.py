@@ -245,8 +245,9 @@ def model_layout(c: Case, rep: Report) -> LayoutGeom:
             tok = ranker & (lane < TOK_W) & (tile_lo + ti < tile_hi)
             for j in range(k):
                 rep.access(kname, "topk_ids", (tile_lo + ti[tok]) * k + j, "load")
-        if not g.two:
-            # counting pass: the first batch, then a prefetch of each next one
+        if not g.two and g.ntiles > 1:
+            # counting pass (none for one tile: the ranking waves' counts are
+            # the totals): the first batch, then a prefetch of each next one
             b0s = [0] + [b0 + batch for b0 in range(0, T, batch) if b0 + batch < T]
             for b0 in b0s:
                 if K > 0:
@@ -263,7 +264,7 @@ def model_layout(c: Case, rep: Report) -> LayoutGeom:
                     t = b0 + tid
                     for j in range(k):
                         rep.access(kname, "topk_ids", t[t < T] * k + j, "load")
-        else:
+        elif g.two:
             groups = g.tiles_pad // 4
             col = np.arange(g.ncols, dtype=np.int64)
             for q in range(groups):
