@@ -1552,13 +1552,22 @@ int copy_vec(int nvec) {
 // slice), a slice being at most `most` groups of 64 vec4 (each group 8 fp32
 // accumulators per lane), as few slices as that allows; more groups per slice
 // (up to 8) only if the grid would otherwise pass 2^31 - 1 waves. Measured
-// (1, 2, 3, 5 and 10 groups at H=5120): the combine is fastest within the
-// whole prefill step with up to 8 (two slices of 5; one group per wave is
-// 4% faster at the adv size but 0.6 us slower in the prefill step) and with
-// one group per wave below kFillTokens tokens (decode step 23.0 vs 24.9 us),
-// the home sum with one group per wave, the partial rows with three (their
-// waves first find their rank and terms).
+// (1, 2, 3, 4, 5 and 10 groups, each step on buffers no earlier step left in
+// the caches): the combine with up to 8 (two slices of 5 at H=5120) is as
+// fast as any within the prefill step, where the expert rows (240 MiB) fit
+// the 256 MiB Infinity Cache; with more expert rows than that one group per
+// wave is faster (T=8192 H=6144 k=8: 154 vs 159 us; T=16384 H=7168 k=8: 365
+// vs 385 us). Below kFillTokens tokens one group per wave too (decode step
+// 23.0 vs 24.9 us). The home sum takes one group per wave, the partial rows
+// three (their waves first find their rank and terms).
 constexpr int kCombineGroups = 8;
+constexpr int64_t kCombineOneGroupBytes = int64_t(256) << 20;  // T*k*H*2 above: one group
+
+int combine_groups(const moe_shape_t* sh) {
+  if (sh->T < kFillTokens) return 1;
+  const int64_t pair_bytes = int64_t(sh->T) * sh->k * sh->H * 2;
+  return pair_bytes > kCombineOneGroupBytes ? 1 : kCombineGroups;
+}
 
 constexpr int kPartialGroups = 3;
 constexpr int kRankSumGroups = 1;
@@ -1965,7 +1974,7 @@ int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int3
   if (!aligned16(expert_out) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   int v = 1, slices = 1;
-  combine_tiling(nvec, shape->T, shape->T < kFillTokens ? 1 : kCombineGroups, &v, &slices);
+  combine_tiling(nvec, shape->T, combine_groups(shape), &v, &slices);
   // Small batches: one 1 KiB group per wave and every slot requested at once.
   ByVec<CombineLaunch>::run(v, shape->T < kFillTokens && v <= 2,
                             dim3(blocks_for(int64_t(shape->T) * slices)),

@@ -44,6 +44,7 @@ TWO_LAUNCH_MIN_IDS = 49152
 COUNT_THREADS = 256
 FILL_TOKENS = 1024
 COMBINE_GROUPS = 8
+COMBINE_ONE_GROUP_BYTES = 256 << 20
 PARTIAL_GROUPS = 3
 RANK_SUM_GROUPS = 1
 INT32_MAX = 2 ** 31 - 1
@@ -498,7 +499,8 @@ def model_combine(c: Case, lay: dict, rep: Report):
     rep.buf("out_f32", T * nvec * 2)
     if T == 0:
         return
-    v, slices = combine_tiling(nvec, T, 1 if T < FILL_TOKENS else COMBINE_GROUPS)
+    most = 1 if T < FILL_TOKENS or T * c.k * c.H * 2 > COMBINE_ONE_GROUP_BYTES else COMBINE_GROUPS
+    v, slices = combine_tiling(nvec, T, most)
     t = np.arange(T, dtype=np.int64)
     lanes_k = LANE[LANE < k]
     rep.access("combine", "pair_row", t[:, None] * k + lanes_k[None, :], "load")

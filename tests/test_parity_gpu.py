@@ -254,11 +254,16 @@ def test_timing_hook_brackets_the_next_kernel():
 
 WIDE_RANK_SETS = [(1024, 512, 64, 4), (4096, 480, 48, 4), (8192, 64, 64, 4), (12288, 1024, 64, 4),
                   (3000, 640, 40, 5), (2048, 512, 64, 6), (1024, 64, 64, 4), (1024, 480, 48, 4),
-                  (700, 96, 16, 4)]
+                  (700, 96, 16, 4),
+                  # 30% of the ids -1 and 1% out of range, as in the random layout that
+                  # caught a second miscount: tiles of 512 tokens, 256, and one tile
+                  (16385, 512, 64, 4, 0.3, 0.01), (4096, 512, 64, 4, 0.3, 0.01),
+                  (256, 512, 64, 4, 0.3, 0.01), (200, 1024, 64, 16, 0.1, 0.0)]
 
 
-@pytest.mark.parametrize("case", WIDE_RANK_SETS, ids=[f"T{c[0]}_E{c[1]}_R{c[2]}_k{c[3]}"
-                                                      for c in WIDE_RANK_SETS])
+@pytest.mark.parametrize("case", WIDE_RANK_SETS, ids=[
+    f"T{c[0]}_E{c[1]}_R{c[2]}_k{c[3]}" + (f"_neg{c[4]}_bad{c[5]}" if len(c) > 4 else "")
+    for c in WIDE_RANK_SETS])
 def test_layout_wide_rank_sets_repeated(case):
     """Layout with more than 32 ranks (64-bit rank sets): the one-launch form
     (forced with a workspace, and chosen without one) and the two-launch form
@@ -267,10 +272,11 @@ def test_layout_wide_rank_sets_repeated(case):
     rank once came out wrong for k = 4 with R > 32 in the one-launch form, on
     most calls but not all.)"""
     import combine_topk_ids_02_amd as moe
-    T, E, R, k = case
-    say(f"[wide rank sets] T={T} E={E} R={R} k={k}")
+    T, E, R, k = case[:4]
+    p_neg, p_bad = case[4:] if len(case) > 4 else (0.0, 0.0)
+    say(f"[wide rank sets] T={T} E={E} R={R} k={k} p_neg={p_neg} p_bad={p_bad}")
     rng = np.random.default_rng(T + E + R + k)
-    ids = pins.rand_ids(rng, T, E, k)
+    ids = pins.rand_ids(rng, T, E, k, p_neg=p_neg, p_bad=p_bad)
     ref = oracle.layout(ids, E, R)
     ids_d = torch.from_numpy(ids).to("cuda:0")
     shape = moe.Shape(T, 8, E, R, k)
