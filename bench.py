@@ -13,8 +13,10 @@ outputs and every output buffer), so that no step finds in L2 or the Infinity
 Cache anything the step before it read or wrote, as consecutive layers or
 batches would not; within a step the calls hand their results on as they do
 in a layer. Beside it (`modes`): the same steps on one buffer set back to back
-(warm), and the sum of per-call times with L2 and the Infinity Cache evicted
-before every call (cold). Also: per-call times, the load per destination rank
+(warm), the rotated steps again right after a 1 GiB write by another kernel
+(after_write: a large write changes how the Infinity Cache keeps the pack's
+rows for the permute), and the sum of per-call times with L2 and the Infinity
+Cache evicted before every call (cold). Also: per-call times, the load per destination rank
 (max over mean), the roofline of the dominant kernel (permute: its algorithmic
 bytes over its own duration, from a HIP event pair that the runtime records
 with the kernel's dispatch on the stream it runs on), and the CPU oracle timed
@@ -433,7 +435,7 @@ class Rig:
                 out[c].append(a.elapsed_time(b))
         return out
 
-    def graph_step_us(self, n: int = 50) -> float:
+    def graph_step_us(self, n: int = 200) -> float:
         """One step recorded in a HIP graph, replayed n times back to back: the
         step's GPU time without host launch gaps (what a decode loop that
         replays a recorded step sees)."""
@@ -444,7 +446,7 @@ class Rig:
         with torch.cuda.graph(g):
             for c in CALLS:  # the one-stage path: layout, pack, permute, combine
                 self.call(c)
-        for _ in range(3):
+        for _ in range(20):  # the first replays of a new graph run slower
             g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -700,6 +702,12 @@ def main():
     def evict() -> None:
         torch.sum(flush, dim=0, dtype=torch.int32, out=acc)
 
+    # The rotated steps again, right after that 1 GiB write by another kernel
+    # (a large write changes how the Infinity Cache keeps the pack's rows for
+    # the permute; the step should not depend on it).
+    torch.cuda.synchronize()
+    after_write_ms, _ = timed_steps(rotate=True)
+    log(f"timed {args.steps} steps after a 1 GiB write: {after_write_ms * 1e3:.1f} us/step")
     per_call_ms = rig.per_call_ms(args.steps)
     cold_ms = rig.per_call_ms(args.steps, evict, rotate=False)
     del flush
@@ -725,6 +733,8 @@ def main():
     modes = {"rotated": dict(mode(ms_per_step), note="the value: a different buffer set each "
                              "step, nothing read is cached from the step before"),
              "warm": dict(mode(warm_ms), note="one buffer set back to back"),
+             "after_write": dict(mode(after_write_ms), note="the rotated steps right after a "
+                                 "1 GiB write by another kernel"),
              "cold": dict(mode(cold_step_ms), note="sum of per-call means, L2 and Infinity "
                           "Cache evicted by a 1 GiB read before every call")}
     # The dominant kernel's own duration: a third pass of whole steps (rotating

@@ -27,8 +27,10 @@
 // instruction. Cache policy per stream, chosen by measurement of the whole
 // layout -> pack -> permute -> combine sequence: the packed rows are written
 // with ordinary stores, so the permute finds them in the 256 MB Infinity
-// Cache; every other row stream (hidden, packed rows on their second read,
-// expert rows, combine outputs) is non-temporal so it does not evict them.
+// Cache; the hidden rows are read with ordinary loads (which keeps that
+// hand-off working whatever large writes other kernels made before); every
+// other row stream (packed rows on their second read, expert rows, combine
+// outputs) is non-temporal so it does not evict them.
 // Nothing here is a dense contraction, so no MFMA.
 
 #include <hip/hip_ext.h>
@@ -929,20 +931,24 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
   const int lane = lane_id();
   const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (t >= T) return;
-  // The hidden row is read once (streamed), its first pass requested right
-  // behind the token's slots (loads return in order, so the slots can be
-  // used while the row is still arriving); the copies are stored with
-  // ordinary stores so that they stay in the Infinity Cache for the permute.
+  // The hidden row is read once, its first pass requested right behind the
+  // token's slots (loads return in order, so the slots can be used while the
+  // row is still arriving); the copies are stored with ordinary stores so
+  // that they stay in the Infinity Cache for the permute. The row is read
+  // with ordinary loads, not streamed: with streamed loads the permute lost
+  // that cache hand-off (86 instead of 66 us at T=4096 H=5120) after any
+  // large write by another kernel, until a large read came along, while
+  // with ordinary loads the step takes the same time after either.
   const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
   const int slot = lane < R ? slot_any : -1;
   const vec4* src = hidden + (int64_t)t * nvec;
   vec4 first[V];
-  load_first_pass<V, true>(src, nvec, first);
+  load_first_pass<V, false>(src, nvec, first);
   const bool ok = slot >= 0 && slot < cap_rank;
   if (__ballot(slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
   if (ok) rank_src_token[slot] = t;
   const uint64_t dests = __ballot(ok);
-  if (dests) fan_out_row<V, true, false>(first, src, rank_buf, slot, dests, nvec);
+  if (dests) fan_out_row<V, false, false>(first, src, rank_buf, slot, dests, nvec);
 }
 
 // The pack for small batches (fewer than kFillTokens tokens, where one wave
@@ -961,7 +967,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_small(
   const int c = g * kWave + lane;
   // the slots and the row's column requested together (clamped, unconditional)
   const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
-  const vec4 v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
+  const vec4 v = load_row<false>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
   const int slot = lane < R ? slot_any : -1;
   const bool ok = slot >= 0 && slot < cap_rank;
   if (g == 0) {
@@ -1108,7 +1114,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         if (act) {
-          v[q][i] = load_row<true>(src + col + i);
+          v[q][i] = load_row<false>(src + col + i);
         } else {
           v[q][i] = vec4{0u, 0u, 0u, 0u};
         }
@@ -1204,6 +1210,13 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
 
 // kMx: the rows are MXFP8 codes, and each also has a row of nvec_s vec4 of
 // scales in rank_scale / expert_scale that moves with it.
+//
+// Packed bf16 rows are read non-temporally; packed MX codes and scales with
+// ordinary loads. With streamed loads the MX step lost the pack's cache
+// hand-off after any large write by another kernel (MXFP8 at T=4096 H=5120:
+// 130 instead of 120 us, until a large read came along); with ordinary loads
+// it takes 121-122 us after either. (For bf16 rows the pack's ordinary loads
+// of the hidden rows already keep the hand-off, and are the faster fix.)
 template <int V, bool kMx>
 __global__ __launch_bounds__(kBlock) void permute_rows(
     const vec4* rank_buf, const vec4* rank_scale, const int32_t* __restrict__ rank_src_token,
@@ -1213,6 +1226,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
     int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, int m, int block,
     int nvec, int nvec_s, int pad_waves, int64_t cap_rank, int64_t cap_expert,
     int early_row, int32_t* err_word) {
+  constexpr bool kStreamIn = !kMx;
   const int lane = lane_id();
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (gw < pad_waves) {
@@ -1232,7 +1246,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   const int64_t ic = min(i, cap_rank - 1);
   const int t = ic >= 0 ? rank_src_token[ic] : -1;
   vec4 first[V];
-  if (early_row) load_first_pass<V, true>(rank_buf + ic * nvec, nvec, first);
+  if (early_row) load_first_pass<V, kStreamIn>(rank_buf + ic * nvec, nvec, first);
   const int end = lane < R ? end_any : 0x7FFFFFFF;
   if (i >= rows || t < 0 || t >= T) return;
   const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
@@ -1240,14 +1254,14 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   const int e = lane < k ? e_any : -1;
   const int pr = lane < k ? pr_any : -1;
   // The packed row is read once and the expert rows are not read again here:
-  // both streamed.
+  // both streamed (but MX codes: see above).
   const vec4* src = rank_buf + i * nvec;
-  if (!early_row) load_first_pass<V, true>(src, nvec, first);
+  if (!early_row) load_first_pass<V, kStreamIn>(src, nvec, first);
   // MX: a scale row of at most 64 vec4 (H <= 32768) is one partial pass,
   // requested with the code row (clamped lanes; lanes >= nvec_s store nothing)
   const bool short_scales = kMx && nvec_s <= kWave;
   vec4 sv;
-  if (short_scales) sv = load_row<true>(rank_scale + i * nvec_s + min(lane, nvec_s - 1));
+  if (short_scales) sv = load_row<kStreamIn>(rank_scale + i * nvec_s + min(lane, nvec_s - 1));
   // segment of row i: number of segment ends at or below i
   const int r = __popcll(__ballot(lane < R && end <= i));
   const bool here = e >= 0 && e < E && e / m == r;
@@ -1257,7 +1271,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   if (ok) expert_src_pair[p] = t * k + lane;
   const uint64_t dests = __ballot(ok);
   if (!dests) return;
-  fan_out_row<V, true, true>(first, src, expert_buf, p, dests, nvec);
+  fan_out_row<V, kStreamIn, true>(first, src, expert_buf, p, dests, nvec);
   if (short_scales) {
     uint64_t d = dests;
     while (d) {
@@ -1269,8 +1283,8 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   } else if (kMx) {
     const vec4* ssrc = rank_scale + i * nvec_s;
     vec4 sfirst[1];
-    load_first_pass<1, true>(ssrc, nvec_s, sfirst);
-    fan_out_row<1, true, true>(sfirst, ssrc, expert_scale, p, dests, nvec_s);
+    load_first_pass<1, kStreamIn>(ssrc, nvec_s, sfirst);
+    fan_out_row<1, kStreamIn, true>(sfirst, ssrc, expert_scale, p, dests, nvec_s);
   }
 }
 
