@@ -48,6 +48,8 @@ class _Lib:
         lib.oracle_quantize_mxfp8.argtypes = [i64, i32, vp, vp, vp]
         lib.oracle_quantize_mxfp4.restype = None
         lib.oracle_quantize_mxfp4.argtypes = [i64, i32, vp, vp, vp]
+        lib.oracle_quantize_nvfp4.restype = None
+        lib.oracle_quantize_nvfp4.argtypes = [i64, i32, vp, vp, vp]
         self.lib = lib
 
 
@@ -267,6 +269,35 @@ def permute_mxfp4(rank_q, rank_scale, rank_src_token, lay: dict, topk_ids, E: in
                   cap_expert: int):
     """Regroup MXFP4 rows by expert: codes and scales move as bytes, exactly as
     permute_mxfp8 moves them."""
+    return permute_mxfp8(rank_q, rank_scale, rank_src_token, lay, topk_ids, E, cap_expert)
+
+
+def quantize_nvfp4(x):
+    """bf16 rows [rows, H] (H a multiple of 16) -> (q [rows, H/2] uint8, two
+    e2m1 codes per byte, even value in the low nibble; scale [rows, H/16] uint8
+    E4M3 codes): the pages' 4-bit row, one scale byte per 16 values."""
+    xb = _c(x, np.uint16)
+    rows, H = xb.shape
+    assert H % 16 == 0
+    q = np.zeros((rows, H // 2), np.uint8)
+    sc = np.zeros((rows, H // 16), np.uint8)
+    _load().oracle_quantize_nvfp4(rows, H, _p(xb), _p(q), _p(sc))
+    return q, sc
+
+
+def pack_nvfp4(hidden, token_rank_slot, cap_rank: int):
+    """Quantise every hidden row once to the 16-value-block 4-bit row, then
+    pack codes and scales once per distinct rank (plain byte copies)."""
+    q, sc = quantize_nvfp4(hidden)
+    rq, src, err = pack(q.view(np.uint16), token_rank_slot, cap_rank)
+    rs, _, _ = pack(sc.view(np.uint16), token_rank_slot, cap_rank)
+    return rq.view(np.uint8), rs.view(np.uint8), src, err
+
+
+def permute_nvfp4(rank_q, rank_scale, rank_src_token, lay: dict, topk_ids, E: int,
+                  cap_expert: int):
+    """Regroup 16-value-block 4-bit rows by expert: codes and scales move as
+    bytes, exactly as permute_mxfp8 moves them."""
     return permute_mxfp8(rank_q, rank_scale, rank_src_token, lay, topk_ids, E, cap_expert)
 
 

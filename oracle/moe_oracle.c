@@ -380,3 +380,48 @@ void oracle_quantize_mxfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* 
     }
   }
 }
+
+/* The nearest of the finite non-negative codes 0..last of a format (magnitude
+ * given by mag_of) to the non-negative value x; on a tie, the even code. */
+static int nearest_code(double x, int last, double (*mag_of)(int)) {
+  int best = 0;
+  for (int c = 1; c <= last; ++c) {
+    const double dc = fabs(x - mag_of(c)), db = fabs(x - mag_of(best));
+    if (dc < db || (dc == db && c % 2 == 0)) best = c;
+  }
+  return best;
+}
+
+void oracle_quantize_nvfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale) {
+  const int32_t nblk = H / 16;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t b = 0; b < nblk; ++b) {
+      const uint16_t* v = x + r * H + (int64_t)b * 16;
+      uint8_t* out = q + r * (H / 2) + (int64_t)b * 8;
+      double amax = 0.0;
+      int nonfinite = 0;
+      for (int i = 0; i < 16; ++i) {
+        const double a = fabs((double)widen_bf16(v[i]));
+        if (!isfinite(a)) nonfinite = 1;
+        else if (a > amax) amax = a;
+      }
+      /* the block scale: the E4M3 code nearest to amax / 6 */
+      const int sc = nonfinite ? 0x7F : nearest_code(amax / 6.0, 0x7E, e4m3_magnitude);
+      const double s = nonfinite ? 0.0 : e4m3_magnitude(sc);
+      scale[r * nblk + b] = (uint8_t)sc;
+      for (int i = 0; i < 16; ++i) {
+        int code = 0;
+        if (nonfinite)
+          code = 7;
+        else if (s > 0.0)
+          code = nearest_code(fabs((double)widen_bf16(v[i])) / s, 7, e2m1_magnitude);
+        code |= (int)(v[i] >> 15) << 3; /* the sign */
+        if ((i & 1) == 0)
+          out[i >> 1] = (uint8_t)code;
+        else
+          out[i >> 1] |= (uint8_t)(code << 4);
+      }
+    }
+  }
+}

@@ -178,6 +178,26 @@ void oracle_quantize_mxfp8(int64_t rows, int32_t H, const uint16_t* x, uint8_t* 
 void oracle_quantize_mxfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
                            uint8_t* scale);
 
+/*
+ * The pages' own 4-bit row ([A2A] sec 7.2: NVFP4, 2,880 bytes for a 5,120-wide
+ * row, a one-byte scale for every 16 values): per block of 16 consecutive
+ * values,
+ *   s     = the OCP FP8 E4M3 value nearest to amax / 6 (6 = the largest e2m1
+ *           value; ties to the even code, past 448 saturating to 448, small
+ *           enough quotients giving 0); the scale byte is its code; 0x7F (the
+ *           E4M3 NaN) if the block holds a NaN or an infinity;
+ *   q_i   = the OCP FP4 E2M1 value nearest to |v_i| / s (ties to the even code,
+ *           past 6 saturating to 6) with the sign of v_i; 0 with the sign when
+ *           s = 0; in a NaN/Inf block the largest magnitude (code 7) with the
+ *           value's sign.
+ * No second, per-tensor scale (the row size the pages give has no room for
+ * one): s scales the values themselves. Two codes per byte, the even-indexed
+ * value in the low nibble. Rows of x are H bf16 values; q gets H/2 bytes and
+ * scale H/16 bytes per row.
+ */
+void oracle_quantize_nvfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* q,
+                           uint8_t* scale);
+
 #ifdef __cplusplus
 }
 #endif

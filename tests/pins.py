@@ -1021,6 +1021,107 @@ def pin_mxfp4_pack_and_permute():
     assert err2 == 0 and np.array_equal(eq[:P], q[t_of]) and np.array_equal(es[:P], sc[t_of])
 
 
+def pin_nvfp4_row_bytes():
+    """The pages' 4-bit row: 2,880 bytes for a 5,120-wide row ("A2A backends"
+    page, section 7.2), 2,560 code bytes and one scale byte per 16 values."""
+    q, sc = oracle.quantize_nvfp4(np.zeros((1, 5120), np.uint16))
+    assert q.shape[1] + sc.shape[1] == 2880 and sc.shape[1] == 5120 // 16
+
+
+def pin_nvfp4_every_code_round_trips():
+    """A block whose largest magnitude is 6 has scale 1 (E4M3 code 0x38) and all
+    16 codes (both signs, -0 included) come back as themselves; the same block
+    times 1.5 has scale 1.5 (0x3C) and the same codes."""
+    mags = _e2m1_table()
+    codes = np.arange(16)
+    vals = np.where(codes & 8, -1.0, 1.0) * mags[codes & 7]
+    for factor, want in ((1.0, 0x38), (1.5, 0x3C)):
+        q, sc = oracle.quantize_nvfp4(_bf16((vals * factor)[None, :].astype(np.float32)))
+        assert int(sc[0, 0]) == want, hex(int(sc[0, 0]))
+        assert np.array_equal(_unpack_nibbles(q)[0], codes), _unpack_nibbles(q)[0]
+
+
+def pin_nvfp4_hand_cases():
+    """Hand-derived cases of the 16-value rule: s = E4M3 nearest to amax / 6 with
+    ties to the even code, codes = e2m1 nearest to |v| / s with ties to even."""
+    def block(values):
+        v = list(values) + [0.0] * (16 - len(values))
+        q, sc = oracle.quantize_nvfp4(_bf16(np.array([v], np.float32)))
+        return list(_unpack_nibbles(q)[0]), int(sc[0, 0])
+
+    # amax 6.375: amax/6 = 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39): 0x38
+    c, s = block([6.375, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25])
+    assert s == 0x38 and c[:9] == [7, 0, 2, 2, 4, 4, 6, 6, 8], (hex(s), c[:9])
+    # amax 6.75: amax/6 = 1.125 exactly (0x39); 6.75/1.125 = 6, 2.25/1.125 = 2
+    c, s = block([6.75, -2.25])
+    assert s == 0x39 and c[:2] == [7, 12], (hex(s), c[:2])
+    # amax 3072: 512 saturates to 448 (0x7E); 3072/448 = 6.9 saturates to 6
+    c, s = block([3072.0, -448.0])
+    assert s == 0x7E and c[:2] == [7, 8 | 2], (hex(s), c[:2])
+    # amax 6 * 2^-9: the smallest subnormal scale 2^-9 (0x01)
+    c, s = block([6 * 2.0 ** -9, -2.0 ** -9])
+    assert s == 0x01 and c[:2] == [7, 8 | 2], (hex(s), c[:2])
+    # amax 6 * 2^-10: amax/6 = 2^-10 ties between 0 and 2^-9, even code 0: a zero
+    # scale, and every code zero with its sign
+    c, s = block([6 * 2.0 ** -10, -2.0 ** -12])
+    assert s == 0x00 and c[:2] == [0, 8], (hex(s), c[:2])
+    # an all-zero block: scale 0, codes 0
+    c, s = block([])
+    assert s == 0 and c == [0] * 16
+    # NaN / infinity: the E4M3 NaN scale 0x7F, codes of the largest magnitude with signs
+    q, sc = oracle.quantize_nvfp4(np.array([[0x3F80, 0x7FC0, 0xBF80, 0xFF80] + [0] * 12],
+                                           np.uint16))
+    assert int(sc[0, 0]) == 0x7F and list(_unpack_nibbles(q)[0, :4]) == [7, 7, 15, 15]
+
+
+def pin_nvfp4_error_bound():
+    """Random rows over 24 binades: a block's scale is within half an E4M3 step
+    of amax / 6 (unless it saturated or went subnormal), and every value is
+    within half an e2m1 step (times the scale) of its code unless it saturated
+    at 6; signs are kept."""
+    rng = np.random.default_rng(117)
+    e4m3 = _e4m3_table()
+    mags = _e2m1_table()
+    binade = np.exp2(rng.uniform(-10, 14, (64, 16, 1))).repeat(16, axis=2).reshape(64, 256)
+    vals = rng.standard_normal((64, 256)) * binade
+    x = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    q, sc = oracle.quantize_nvfp4(x)
+    xf = bf16_bits_to_float(x).astype(np.float64).reshape(64, 16, 16)
+    s = e4m3[sc.astype(np.int64)]
+    t = np.abs(xf).max(axis=2) / 6
+    normal = (sc >= 8) & (sc < 0x7E)
+    assert normal.sum() > 400 and (sc == 0x7E).any() and (sc < 8).any()
+    half_step = np.exp2(np.floor(np.log2(s[normal]))) / 16
+    assert np.all(np.abs(s[normal] - t[normal]) <= half_step)
+    codes = _unpack_nibbles(q).reshape(64, 16, 16)
+    ok = s > 0
+    scaled = np.abs(xf[ok]) / s[ok][:, None]
+    deq = mags[codes[ok] & 7]
+    sat = scaled > 6
+    step = np.where(scaled < 2, 0.5, np.where(scaled < 4, 1.0, 2.0))
+    assert np.all((np.abs(deq - scaled) <= step / 2) | sat)
+    assert np.all(deq[sat] == 6)
+    assert np.all(((codes & 8) != 0) == np.signbit(xf))
+
+
+def pin_nvfp4_pack_and_permute():
+    """The 16-value-block 4-bit dispatch moves bytes only: packed and regrouped
+    rows hold the codes and scales of their source token's quantised row."""
+    rng = np.random.default_rng(119)
+    T, E, R, k, H = 70, 32, 4, 3, 128
+    ids = rand_ids(rng, T, E, k, p_neg=0.1)
+    hid = synth.normal_bf16(29, 0, T * H).reshape(T, H)
+    lay = oracle.layout(ids, E, R)
+    q, sc = oracle.quantize_nvfp4(hid)
+    rq, rs, src, err = oracle.pack_nvfp4(hid, lay["token_rank_slot"], T * min(k, R))
+    C = int(lay["rank_offsets"][-1])
+    assert err == 0 and np.array_equal(rq[:C], q[src[:C]]) and np.array_equal(rs[:C], sc[src[:C]])
+    eq, es, esrc, err2 = oracle.permute_nvfp4(rq, rs, src, lay, ids, E, T * k)
+    P = int(lay["expert_offsets"][-1])
+    t_of = esrc[:P] // k
+    assert err2 == 0 and np.array_equal(eq[:P], q[t_of]) and np.array_equal(es[:P], sc[t_of])
+
+
 PINS = [
     pin_layout_stable_sort,
     pin_layout_brute_force,
@@ -1058,4 +1159,9 @@ PINS = [
     pin_mxfp4_hand_cases,
     pin_mxfp4_error_bound,
     pin_mxfp4_pack_and_permute,
+    pin_nvfp4_row_bytes,
+    pin_nvfp4_every_code_round_trips,
+    pin_nvfp4_hand_cases,
+    pin_nvfp4_error_bound,
+    pin_nvfp4_pack_and_permute,
 ]

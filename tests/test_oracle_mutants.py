@@ -152,6 +152,27 @@ MUTANTS = {
     "e4m3 subnormals one binade low": (
         "if (ef == 0) return ldexp((double)mf, -9);",
         "if (ef == 0) return ldexp((double)mf, -10);"),
+    "nv4 scale from amax / 4": (
+        "nearest_code(amax / 6.0, 0x7E, e4m3_magnitude)",
+        "nearest_code(amax / 4.0, 0x7E, e4m3_magnitude)"),
+    "nv4 scale may reach the NaN code": (
+        "nearest_code(amax / 6.0, 0x7E, e4m3_magnitude)",
+        "nearest_code(amax / 6.0, 0x7F, e4m3_magnitude)"),
+    "nearest code ties to odd": (
+        "if (dc < db || (dc == db && c % 2 == 0)) best = c;",
+        "if (dc < db || (dc == db && c % 2 == 1)) best = c;"),
+    "nv4 zero scale not special": (
+        "else if (s > 0.0)\n          code = nearest_code",
+        "else\n          code = nearest_code"),
+    "nv4 high nibble first": (
+        "if ((i & 1) == 0)\n          out[i >> 1] = (uint8_t)code;\n        else\n          out[i >> 1] |= (uint8_t)(code << 4);",
+        "if ((i & 1) == 0)\n          out[i >> 1] = (uint8_t)(code << 4);\n        else\n          out[i >> 1] |= (uint8_t)code;"),
+    "nv4 drops the sign": (
+        "code |= (int)(v[i] >> 15) << 3; /* the sign */",
+        "code |= 0;"),
+    "nv4 ignores NaN blocks": (
+        "if (!isfinite(a)) nonfinite = 1;",
+        "if (!isfinite(a)) nonfinite = 0;"),
     "f64 combine rounds products to float": (
         "acc += (double)topk_weights[(int64_t)t * k + j] * (double)widen_bf16(expert_out[row * H + h]);",
         "acc += (double)(topk_weights[(int64_t)t * k + j] * widen_bf16(expert_out[row * H + h]));"),
