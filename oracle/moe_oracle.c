@@ -382,8 +382,12 @@ void oracle_quantize_mxfp4(int64_t rows, int32_t H, const uint16_t* x, uint8_t* 
 }
 
 /* The nearest of the finite non-negative codes 0..last of a format (magnitude
- * given by mag_of) to the non-negative value x; on a tie, the even code. */
+ * given by mag_of) to the non-negative value x; on a tie, the even code. At or
+ * past the largest magnitude that is the last code (saturation), decided
+ * before any distance is taken: far past it the distances to the two largest
+ * codes round to the same double. */
 static int nearest_code(double x, int last, double (*mag_of)(int)) {
+  if (x >= mag_of(last)) return last;
   int best = 0;
   for (int c = 1; c <= last; ++c) {
     const double dc = fabs(x - mag_of(c)), db = fabs(x - mag_of(best));

@@ -1065,6 +1065,12 @@ def pin_nvfp4_hand_cases():
     # scale, and every code zero with its sign
     c, s = block([6 * 2.0 ** -10, -2.0 ** -12])
     assert s == 0x00 and c[:2] == [0, 8], (hex(s), c[:2])
+    # values far past 6 * 448: the scale saturates at 448 and those codes at 6, however
+    # large the quotient (|v| / s up to 7.6e35)
+    q, sc = oracle.quantize_nvfp4(np.array([[0x7F7F, 0xFF00, 0x4780, 0x3F80] + [0] * 12],
+                                           np.uint16))
+    c = list(_unpack_nibbles(q)[0, :4])
+    assert int(sc[0, 0]) == 0x7E and c == [7, 15, 7, 0], (hex(int(sc[0, 0])), c)
     # an all-zero block: scale 0, codes 0
     c, s = block([])
     assert s == 0 and c == [0] * 16
