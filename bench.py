@@ -61,11 +61,17 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
     }
 
 
-def mx_bytes(T, H, R, k, C, P, bits=8):
+# Quantised wire formats: name -> (code bits per value, values per scale byte).
+WIRE = {"mxfp8": (8, 32), "mxfp4": (4, 32), "nvfp4": (4, 16)}
+
+
+def mx_bytes(T, H, R, k, C, P, fmt="mxfp8"):
     """Bytes of the quantised dispatch: the fused quantise-and-pack reads each
-    bf16 hidden row once and writes H*bits/8 code bytes + H/32 scales per copy;
-    the permute reads each quantised rank row once and writes it once per pair."""
-    qrow = H * bits // 8 + H // 32
+    bf16 hidden row once and writes H*bits/8 code bytes + H/block scales per
+    copy; the permute reads each quantised rank row once and writes it once
+    per pair."""
+    bits, blk = WIRE[fmt]
+    qrow = H * bits // 8 + H // blk
     return {
         "pack": 2 * T * H + C * qrow + 4 * T * R + 4 * C,
         "permute": C * qrow + P * qrow + 4 * C + 8 * T * k + 4 * P,
@@ -252,7 +258,7 @@ class Rig:
     step reads is still in L2 or the Infinity Cache from the step before."""
 
     def __init__(self, w, dev, two_stage: bool = False, align: int = 1, block: int = 0,
-                 mx_bits: int = 0, sets: int = 1):
+                 mx_bits=0, sets: int = 1):
         import torch
 
         import combine_topk_ids_02_amd as moe
@@ -265,7 +271,9 @@ class Rig:
         self.ids, self.wts = synth.routing(w)
         self.y = synth.expert_out_slots(w.seed, w.E, w.H, self.ids)
         self.shape = moe.Shape(w.T, w.H, w.E, w.R, w.k, align, block)
-        self.mx_bits = mx_bits
+        # quantised dispatch: a format name of WIRE, or the bits 8 / 4 of an MX one
+        self.wire = {8: "mxfp8", 4: "mxfp4", 0: None}.get(mx_bits, mx_bits)
+        self.mx_bits = WIRE[self.wire][0] if self.wire else 0
         self.two_stage = two_stage
         y_d = staging.rows_to_device(self.y, dev)
         self.sets = [self._make_set(y_d) for _ in range(sets)]
@@ -285,7 +293,7 @@ class Rig:
         self.stream = torch.cuda.current_stream(dev)
         self.calls = CALLS
         if mx_bits:
-            self.nbytes.update(mx_bytes(w.T, w.H, w.R, w.k, self.C, self.P, mx_bits))
+            self.nbytes.update(mx_bytes(w.T, w.H, w.R, w.k, self.C, self.P, self.wire))
             self.nbytes["permute"] += 4 * self.pad_rows + (8 * (w.E + 1) if self.pad_rows else 0)
         if two_stage:
             self.nbytes.update(two_stage_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
@@ -310,11 +318,12 @@ class Rig:
         if self.mx_bits:
             # quantised dispatch: codes and scales replace the bf16 rank and expert rows
             u8 = torch.uint8
-            qw = w.H * self.mx_bits // 8
+            bits, blk = WIRE[self.wire]
+            qw = w.H * bits // 8
             s.rank_q = torch.empty((sh.cap_rank, qw), dtype=u8, device=dev)
-            s.rank_s = torch.empty((sh.cap_rank, w.H // 32), dtype=u8, device=dev)
+            s.rank_s = torch.empty((sh.cap_rank, w.H // blk), dtype=u8, device=dev)
             s.exp_q = torch.empty((sh.cap_expert, qw), dtype=u8, device=dev)
-            s.exp_s = torch.empty((sh.cap_expert, w.H // 32), dtype=u8, device=dev)
+            s.exp_s = torch.empty((sh.cap_expert, w.H // blk), dtype=u8, device=dev)
             s.buf.rank_buf = s.buf.expert_buf = None
         if self.two_stage:
             s.partial = torch.empty((sh.cap_rank, w.H), dtype=torch.bfloat16, device=dev)
@@ -347,13 +356,13 @@ class Rig:
             moe.layout(x.ids_d, s.E, s.R, s.H, align=s.align, block=s.block, err=b.err,
                        out=b.layout_dict(), workspace=b.workspace)
         elif name == "pack" and self.mx_bits:
-            moe.pack_mx(self.mx_bits, x.hid_d, b.token_rank_slot, s.E, s.k, x.rank_q,
+            moe.pack_mx(self.wire, x.hid_d, b.token_rank_slot, s.E, s.k, x.rank_q,
                         x.rank_s, b.rank_src_token, err=b.err)
         elif name == "pack":
             moe.pack(x.hid_d, b.token_rank_slot, s.E, s.k, b.rank_buf, b.rank_src_token,
                      err=b.err)
         elif name == "permute" and self.mx_bits:
-            moe.permute_mx(self.mx_bits, x.rank_q, x.rank_s, b.rank_src_token,
+            moe.permute_mx(self.wire, x.rank_q, x.rank_s, b.rank_src_token,
                            b.rank_offsets, x.ids_d, b.pair_row, s.E, x.exp_q, x.exp_s,
                            b.expert_src_pair, expert_counts=b.expert_counts,
                            expert_offsets=b.expert_offsets, align=s.align, block=s.block,
@@ -519,13 +528,13 @@ def sweep(names, dev, with_oracle: bool) -> None:
         opts = dict(kv.split("=") for kv in opt.split(",") if "=" in kv)
         align, block = int(opts.get("align", 1)), int(opts.get("block", 0))
         flags = opt.split(",")
-        mx = 8 if "mxfp8" in flags else 4 if "mxfp4" in flags else 0
+        wire = next((f for f in flags if f in WIRE), 0)
         w = synth.WORKLOADS[name]
-        rig = Rig(w, dev, two_stage=True, align=align, block=block, mx_bits=mx, sets=2)
+        rig = Rig(w, dev, two_stage=True, align=align, block=block, mx_bits=wire, sets=2)
         for _ in range(5):
             rig.step()
         res = {"workload": w.describe(), "layout_shape": {"align": align, "block": block},
-               "dispatch_format": f"mxfp{mx}" if mx else "bf16",
+               "dispatch_format": wire or "bf16",
                "C": rig.C, "P": rig.P, "padding_rows": rig.pad_rows,
                "copies_per_token": round(rig.C / max(w.T, 1), 4),
                "imbalance": rig.imbalance(), "calls": {}}
@@ -619,7 +628,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
                     const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
-                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,adv:mxfp4",
+                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,adv:mxfp4,"
+                          "prefill:nvfp4,adv:nvfp4",
                     default=None,
                     metavar="WORKLOADS", help="per-call warm/rotated/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",

@@ -30,11 +30,15 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_permute_by_expert", "moe_combine", "moe_combine_rank_partial",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
+           "moe_dispatch_pack_nvfp4", "moe_permute_by_expert_nvfp4",
            "moe_testing_set_layout_form", "moe_testing_set_layout_match",
            "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 6
+ABI_VERSION = 7
+
+# Quantised wire formats: name -> (code bits per value, values per scale byte).
+WIRE_FORMATS = {"mxfp8": (8, 32), "mxfp4": (4, 32), "nvfp4": (4, 16)}
 
 
 class MoeShape(ctypes.Structure):
@@ -97,6 +101,10 @@ def lib():
     L.moe_dispatch_pack_mxfp4.argtypes = L.moe_dispatch_pack_mxfp8.argtypes
     L.moe_permute_by_expert_mxfp4.restype = ctypes.c_int
     L.moe_permute_by_expert_mxfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
+    L.moe_dispatch_pack_nvfp4.restype = ctypes.c_int
+    L.moe_dispatch_pack_nvfp4.argtypes = L.moe_dispatch_pack_mxfp8.argtypes
+    L.moe_permute_by_expert_nvfp4.restype = ctypes.c_int
+    L.moe_permute_by_expert_nvfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
     L.moe_testing_set_layout_form.restype = ctypes.c_int
     L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
     L.moe_testing_set_layout_match.restype = ctypes.c_int
@@ -318,69 +326,89 @@ def _bytes(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
-def pack_mx(bits: int, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int,
+def _wire(fmt) -> tuple:
+    """A wire format name (or the bits 8 / 4 of an MX format) -> (name, code
+    bits per value, values per scale byte)."""
+    name = {8: "mxfp8", 4: "mxfp4"}.get(fmt, fmt)
+    if name not in WIRE_FORMATS:
+        raise MoeError(f"unknown wire format {fmt!r}: one of {sorted(WIRE_FORMATS)}")
+    return (name,) + WIRE_FORMATS[name]
+
+
+def pack_mx(fmt, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k: int,
             rank_q, rank_scale, rank_src_token, *, err=None) -> None:
-    """moe_dispatch_pack_mxfp8 (bits 8) or _mxfp4 (bits 4): quantise each hidden
-    row once and pack it once per distinct rank into rank_q [cap_rank, H*bits/8]
-    (uint8 codes) and rank_scale [cap_rank, H/32] (uint8 E8M0 scales)."""
+    """moe_dispatch_pack_mxfp8 / _mxfp4 / _nvfp4 (fmt "mxfp8", "mxfp4",
+    "nvfp4", or the bits 8 / 4 of an MX format): quantise each hidden row once
+    and pack it once per distinct rank into rank_q [cap_rank, H*bits/8] (uint8
+    codes) and rank_scale [cap_rank, H/block] (uint8 scales)."""
+    name, bits, blk = _wire(fmt)
     _check_err(err)
     T, H = hidden.shape
     R = token_rank_slot.shape[1]
     _need(token_rank_slot, "token_rank_slot", (T, R))
     cap = _rows(rank_q, "rank_q", H * bits // 8)
-    _need(rank_scale, "rank_scale", (cap, H // 32))
+    _need(rank_scale, "rank_scale", (cap, H // blk))
     _need(rank_src_token, "rank_src_token", min_numel=cap)
     shape = Shape(T, H, E, R, k)
-    fn = lib().moe_dispatch_pack_mxfp8 if bits == 8 else lib().moe_dispatch_pack_mxfp4
+    fn = getattr(lib(), f"moe_dispatch_pack_{name}")
     st = fn(ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(token_rank_slot)),
             _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
             rank_q.shape[0], _err(err), _stream(hidden.device))
-    _check(st, f"moe_dispatch_pack_mxfp{bits}")
+    _check(st, f"moe_dispatch_pack_{name}")
 
 
 def pack_mxfp8(*args, **kw) -> None:
-    pack_mx(8, *args, **kw)
+    pack_mx("mxfp8", *args, **kw)
 
 
 def pack_mxfp4(*args, **kw) -> None:
-    pack_mx(4, *args, **kw)
+    pack_mx("mxfp4", *args, **kw)
 
 
-def permute_mx(bits: int, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids, pair_row,
+def pack_nvfp4(*args, **kw) -> None:
+    pack_mx("nvfp4", *args, **kw)
+
+
+def permute_mx(fmt, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids, pair_row,
                E: int, expert_q, expert_scale, expert_src_pair, *, expert_counts=None,
                expert_offsets=None, align: int = 1, block: int = 0, err=None) -> None:
-    """moe_permute_by_expert_mxfp8 / _mxfp4: the codes and scales of each
-    rank-buffer row to the rows of its token's experts on that rank."""
+    """moe_permute_by_expert_mxfp8 / _mxfp4 / _nvfp4: the codes and scales of
+    each rank-buffer row to the rows of its token's experts on that rank."""
+    name, bits, blk = _wire(fmt)
     _check_err(err)
     T, k = topk_ids.shape
     H = rank_q.shape[1] * 8 // bits
     R = rank_offsets.shape[0] - 1
     _need(pair_row, "pair_row", (T, k))
     cap_r = rank_q.shape[0]
-    _need(rank_scale, "rank_scale", (cap_r, H // 32))
+    _need(rank_scale, "rank_scale", (cap_r, H // blk))
     _need(rank_src_token, "rank_src_token", min_numel=cap_r)
     cap_e = _rows(expert_q, "expert_q", rank_q.shape[1])
-    _need(expert_scale, "expert_scale", (cap_e, H // 32))
+    _need(expert_scale, "expert_scale", (cap_e, H // blk))
     _need(expert_src_pair, "expert_src_pair", min_numel=cap_e)
     _need(expert_counts, "expert_counts", (E,))
     _need(expert_offsets, "expert_offsets", (E + 1,))
     shape = Shape(T, H, E, R, k, align, block)
-    fn = lib().moe_permute_by_expert_mxfp8 if bits == 8 else lib().moe_permute_by_expert_mxfp4
+    fn = getattr(lib(), f"moe_permute_by_expert_{name}")
     st = fn(ctypes.byref(shape.c()), _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)),
             _ptr(_i32(rank_src_token)), _ptr(_i32(rank_offsets)), _ptr(_i32(topk_ids)),
             _ptr(_i32(pair_row)), _ptr(None if expert_counts is None else _i32(expert_counts)),
             _ptr(None if expert_offsets is None else _i32(expert_offsets)), rank_q.shape[0],
             _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)), _ptr(_i32(expert_src_pair)),
             expert_q.shape[0], _err(err), _stream(rank_q.device))
-    _check(st, f"moe_permute_by_expert_mxfp{bits}")
+    _check(st, f"moe_permute_by_expert_{name}")
 
 
 def permute_mxfp8(*args, **kw) -> None:
-    permute_mx(8, *args, **kw)
+    permute_mx("mxfp8", *args, **kw)
 
 
 def permute_mxfp4(*args, **kw) -> None:
-    permute_mx(4, *args, **kw)
+    permute_mx("mxfp4", *args, **kw)
+
+
+def permute_nvfp4(*args, **kw) -> None:
+    permute_mx("nvfp4", *args, **kw)
 
 
 def combine(expert_out, pair_row, topk_weights, E: int, R: int, out, *, out_f32=None,

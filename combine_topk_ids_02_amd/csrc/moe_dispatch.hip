@@ -1063,6 +1063,54 @@ __device__ __forceinline__ uint32_t e2m1x8(vec4 v, float scale) {
          (e2m1_pair(v[2], scale) << 16) | (e2m1_pair(v[3], scale) << 24);
 }
 
+// The pages' 4-bit row ([A2A] sec 7.2: a one-byte scale for every 16 values):
+// the scale is an OCP E4M3 value s nearest to amax / 6 (6 = e2m1's largest
+// value), not a power of two, so the codes are found by exact comparisons
+// with the e2m1 midpoints times s (each product has at most 7 significant
+// bits, exact in float), not by the hardware's power-of-two scaled conversion.
+
+// E4M3 code of a non-negative float y: nearest, ties to the even code,
+// saturating at 448 (0x7E). Below 2^-6 the codes are multiples of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  if (!(y < 448.0f)) return 0x7Eu;
+  if (y < 0.015625f) return uint32_t(__builtin_rintf(y * 512.0f));
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // mantissa to 3 bits, ties to even
+  return (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t ef = c >> 3, mf = c & 7u;
+  return ef == 0 ? float(mf) * 0.001953125f : __uint_as_float(((ef + 120u) << 23) | (mf << 20));
+}
+
+// e2m1 code of |x| (bf16 bits in the low 16 bits of w) for scale s > 0: the
+// number of midpoints below it, a midpoint counting when |x| passes it or
+// meets it from the side of the even code (ties to even).
+__device__ __forceinline__ uint32_t e2m1_code_scaled(uint32_t w, const float (&mid)[7]) {
+  const float a = __uint_as_float((w & 0x7FFFu) << 16);
+  return uint32_t(a > mid[0]) + uint32_t(a >= mid[1]) + uint32_t(a > mid[2]) +
+         uint32_t(a >= mid[3]) + uint32_t(a > mid[4]) + uint32_t(a >= mid[5]) +
+         uint32_t(a > mid[6]);
+}
+
+// Eight bf16 (a vec4) to eight sign-and-magnitude e2m1 nibbles, the
+// even-indexed value in the low nibble; s = 0 gives zero codes with signs.
+__device__ __forceinline__ uint32_t e2m1x8_e4m3(vec4 v, float s) {
+  const float mid[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = v[i] >> (16 * h);
+      const uint32_t mag = s > 0.0f ? e2m1_code_scaled(w, mid) : 0u;
+      out |= (mag | ((w >> 12) & 0x8u)) << (8 * i + 4 * h);
+    }
+  }
+  return out;
+}
+
 // Fused quantise-and-pack: one wave per token, the row read once and
 // quantised once in registers, then written (codes and scales) to every rank
 // in the token's set. Each lane takes NL consecutive vec4 of the row per pass
@@ -1078,14 +1126,16 @@ __device__ __forceinline__ uint32_t e2m1x8(vec4 v, float scale) {
 template <int kBits> struct MxLane { static constexpr int NL = 2; };
 template <> struct MxLane<4> { static constexpr int NL = 1; };
 
-template <int NP, int kBits>
+template <int NP, int kBits, bool kE4M3 = false>
 __global__ __launch_bounds__(kBlock) void pack_rows_mx(
     const vec4* hidden, const int32_t* __restrict__ token_rank_slot, uint8_t* rank_q,
     uint8_t* rank_scale, int32_t* __restrict__ rank_src_token, int T, int R, int nvec,
     int slices, int64_t cap_rank, int32_t* err_word) {
+  static_assert(!kE4M3 || kBits == 4, "E4M3 scales per 16 values go with 4-bit codes");
   constexpr int NL = MxLane<kBits>::NL;  // vec4 per lane per pass
   constexpr int NB = NL * kBits;      // code bytes per lane per pass
-  constexpr int LPB = 4 / NL;         // lanes per 32-value block
+  constexpr int kBlockVecs = kE4M3 ? 2 : 4;  // vec4 per scale block (16 or 32 values)
+  constexpr int LPB = kBlockVecs / NL;       // lanes per scale block
   constexpr int kEmax = kBits == 8 ? 8 : 2;
   const int lane = lane_id();
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
@@ -1101,7 +1151,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
   const uint64_t dests = __ballot(ok);
   if (!dests) return;
   const int64_t qrow = (int64_t)nvec * kBits;  // code bytes per row (H or H/2)
-  const int64_t srow = nvec / 4;               // scale bytes per row (H / 32)
+  const int64_t srow = nvec / kBlockVecs;      // scale bytes per row (H / 32 or H / 16)
   const int npass = (nvec + kWave * NL - 1) / (kWave * NL);
   const vec4* src = hidden + (int64_t)t * nvec;
   const int p_end = slices == 1 ? npass : sl * NP + NP;
@@ -1136,7 +1186,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
       if (LPB >= 4) amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
       uint32_t sb;
       if (amax >= 0x7F80u) {  // NaN or infinity in the block: NaN scale, marked codes
-        sb = 0xFFu;
+        sb = kE4M3 ? 0x7Fu : 0xFFu;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           uint32_t c[8];
@@ -1160,6 +1210,11 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
             code[q][i] = w;
           }
         }
+      } else if (kE4M3) {
+        sb = e4m3_code(__uint_as_float(amax << 16) / 6.0f);
+        const float sv = e4m3_value(sb);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) code[q][i] = e2m1x8_e4m3(v[q][i], sv);
       } else {
         const int e = mx_block_exponent(amax, kEmax);
         const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // E8M0 byte as an exponent
@@ -1174,7 +1229,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
           }
         }
       }
-      // lanes 4*LPB*w collect the scale bytes of blocks 4w..4w+3
+      // lanes 4*LPB*w collect the scale bytes of blocks 4w..4w+3 (of this pass)
       sw[q] = sb | (uint32_t(__shfl(int(sb), lane + LPB, kWave)) << 8) |
               (uint32_t(__shfl(int(sb), lane + 2 * LPB, kWave)) << 16) |
               (uint32_t(__shfl(int(sb), lane + 3 * LPB, kWave)) << 24);
@@ -1201,7 +1256,8 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
           } else {
             *reinterpret_cast<uint32_t*>(at) = code[q][0];
           }
-          if (lane % (4 * LPB) == 0) *reinterpret_cast<uint32_t*>(sdst + col / 4) = sw[q];
+          if (lane % (4 * LPB) == 0)
+            *reinterpret_cast<uint32_t*>(sdst + col / kBlockVecs) = sw[q];
         }
       }
     }
@@ -1728,10 +1784,13 @@ int mx_passes(int npass, int most) {
 
 template <int NP>
 struct PackMxLaunch {
-  static void go(int bits, dim3 grid, hipStream_t st, const vec4* hid, const int32_t* slots,
-                 uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R, int nvec, int slices,
-                 int64_t cap, int32_t* err) {
-    if (bits == 4) {
+  static void go(int bits, bool e4m3, dim3 grid, hipStream_t st, const vec4* hid,
+                 const int32_t* slots, uint8_t* rq, uint8_t* rs, int32_t* src, int T, int R,
+                 int nvec, int slices, int64_t cap, int32_t* err) {
+    if (bits == 4 && e4m3) {
+      MOE_LAUNCH((pack_rows_mx<NP, 4, true>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
+                 src, T, R, nvec, slices, cap, err);
+    } else if (bits == 4) {
       MOE_LAUNCH((pack_rows_mx<NP, 4>), grid, dim3(kBlock), 0, st, hid, slots, rq, rs,
                          src, T, R, nvec, slices, cap, err);
     } else if constexpr (NP * MxLane<8>::NL <= kMaxVec) {
@@ -1741,7 +1800,8 @@ struct PackMxLaunch {
   }
 };
 
-int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
+// bits 8: MXFP8; bits 4: MXFP4, or with e4m3 the 16-value-block 4-bit row.
+int pack_mx_impl(int bits, bool e4m3, const moe_shape_t* shape, const uint16_t* hidden,
                  const int32_t* token_rank_slot, uint8_t* rank_q, uint8_t* rank_scale,
                  int32_t* rank_src_token, int64_t cap_rank, int32_t* err_word, void* stream) {
   if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0 || cap_rank < 0) return MOE_ERR_ARG;
@@ -1762,7 +1822,7 @@ int pack_mx_impl(int bits, const moe_shape_t* shape, const uint16_t* hidden,
     np = 1;
     slices = npass;
   }
-  ByVec<PackMxLaunch>::run(np, bits, dim3(blocks_for(int64_t(shape->T) * slices)),
+  ByVec<PackMxLaunch>::run(np, bits, e4m3, dim3(blocks_for(int64_t(shape->T) * slices)),
                            static_cast<hipStream_t>(stream),
                            reinterpret_cast<const vec4*>(hidden), token_rank_slot, rank_q,
                            rank_scale, rank_src_token, shape->T, shape->R, nvec, slices,
@@ -1923,16 +1983,46 @@ int moe_dispatch_pack_mxfp8(const moe_shape_t* shape, const uint16_t* hidden,
                             const int32_t* token_rank_slot, uint8_t* rank_q,
                             uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
                             int32_t* err_word, void* stream) {
-  return pack_mx_impl(8, shape, hidden, token_rank_slot, rank_q, rank_scale, rank_src_token,
-                      cap_rank, err_word, stream);
+  return pack_mx_impl(8, false, shape, hidden, token_rank_slot, rank_q, rank_scale,
+                      rank_src_token, cap_rank, err_word, stream);
 }
 
 int moe_dispatch_pack_mxfp4(const moe_shape_t* shape, const uint16_t* hidden,
                             const int32_t* token_rank_slot, uint8_t* rank_q,
                             uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
                             int32_t* err_word, void* stream) {
-  return pack_mx_impl(4, shape, hidden, token_rank_slot, rank_q, rank_scale, rank_src_token,
-                      cap_rank, err_word, stream);
+  return pack_mx_impl(4, false, shape, hidden, token_rank_slot, rank_q, rank_scale,
+                      rank_src_token, cap_rank, err_word, stream);
+}
+
+int moe_dispatch_pack_nvfp4(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream) {
+  return pack_mx_impl(4, true, shape, hidden, token_rank_slot, rank_q, rank_scale,
+                      rank_src_token, cap_rank, err_word, stream);
+}
+
+// The permute of quantised rows: codes of nvec vec4 and scales of nvec_s vec4
+// per row move together.
+int permute_q_impl(const moe_shape_t* shape, const uint8_t* rank_q, const uint8_t* rank_scale,
+                   const int32_t* rank_src_token, const int32_t* rank_offsets,
+                   const int32_t* topk_ids, const int32_t* pair_row,
+                   const int32_t* expert_counts, const int32_t* expert_offsets,
+                   int64_t cap_rank, uint8_t* expert_q, uint8_t* expert_scale,
+                   int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                   void* stream, int nvec, int nvec_s) {
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0) return MOE_ERR_ARG;
+  const int64_t max_rows =
+      std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
+  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
+  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
+  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
+  // a non-null marker selects the two-row kernel even when nothing is moved
+  const void* rs = rank_scale ? rank_scale : static_cast<const void*>(rank_q);
+  return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
+                      expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
+                      expert_src_pair, cap_expert, err_word, stream, nvec, nvec_s);
 }
 
 int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
@@ -1943,18 +2033,11 @@ int moe_permute_by_expert_mxfp8(const moe_shape_t* shape, const uint8_t* rank_q,
                                 uint8_t* expert_q, uint8_t* expert_scale,
                                 int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
                                 void* stream) {
-  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0) return MOE_ERR_ARG;
-  const int64_t max_rows =
-      std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
-  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
-  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
-  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
-  // a non-null marker selects the two-row kernel even when nothing is moved
-  const void* rs = rank_scale ? rank_scale : static_cast<const void*>(rank_q);
-  return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
-                      expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
-                      expert_src_pair, cap_expert, err_word, stream, shape->H / 16,
-                      shape->H / 512);
+  if (!shape) return MOE_ERR_ARG;
+  return permute_q_impl(shape, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids,
+                        pair_row, expert_counts, expert_offsets, cap_rank, expert_q,
+                        expert_scale, expert_src_pair, cap_expert, err_word, stream,
+                        shape->H / 16, shape->H / 512);
 }
 
 int moe_permute_by_expert_mxfp4(const moe_shape_t* shape, const uint8_t* rank_q,
@@ -1965,18 +2048,26 @@ int moe_permute_by_expert_mxfp4(const moe_shape_t* shape, const uint8_t* rank_q,
                                 uint8_t* expert_q, uint8_t* expert_scale,
                                 int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
                                 void* stream) {
-  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0) return MOE_ERR_ARG;
-  const int64_t max_rows =
-      std::min<int64_t>(cap_rank, int64_t(shape->T) * std::min(shape->k, shape->R));
-  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
-  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
-  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
-  // a non-null marker selects the two-row kernel even when nothing is moved
-  const void* rs = rank_scale ? rank_scale : static_cast<const void*>(rank_q);
-  return permute_impl(*shape, rank_q, rs, rank_src_token, rank_offsets, topk_ids, pair_row,
-                      expert_counts, expert_offsets, cap_rank, expert_q, expert_scale,
-                      expert_src_pair, cap_expert, err_word, stream, shape->H / 32,
-                      shape->H / 512);
+  if (!shape) return MOE_ERR_ARG;
+  return permute_q_impl(shape, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids,
+                        pair_row, expert_counts, expert_offsets, cap_rank, expert_q,
+                        expert_scale, expert_src_pair, cap_expert, err_word, stream,
+                        shape->H / 32, shape->H / 512);
+}
+
+int moe_permute_by_expert_nvfp4(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream) {
+  if (!shape) return MOE_ERR_ARG;
+  return permute_q_impl(shape, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids,
+                        pair_row, expert_counts, expert_offsets, cap_rank, expert_q,
+                        expert_scale, expert_src_pair, cap_expert, err_word, stream,
+                        shape->H / 32, shape->H / 256);
 }
 
 int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int32_t* pair_row,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 6
+#define MOE_DISPATCH_ABI_VERSION 7
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -278,6 +278,41 @@ int moe_dispatch_pack_mxfp4(const moe_shape_t* shape, const uint16_t* hidden,
  *   expert_q [cap_expert*H/2], expert_scale [cap_expert*H/32] out
  */
 int moe_permute_by_expert_mxfp4(const moe_shape_t* shape, const uint8_t* rank_q,
+                                const uint8_t* rank_scale, const int32_t* rank_src_token,
+                                const int32_t* rank_offsets, const int32_t* topk_ids,
+                                const int32_t* pair_row, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, int64_t cap_rank,
+                                uint8_t* expert_q, uint8_t* expert_scale,
+                                int32_t* expert_src_pair, int64_t cap_expert, int32_t* err_word,
+                                void* stream);
+
+/*
+ * The pages' own 4-bit row ([A2A] sec 7.2: 2,880 bytes for a 5,120-wide row,
+ * "NVFP4", with a one-byte scale for every 16 values): per block of 16
+ * consecutive values the scale byte is the OCP FP8 E4M3 code of s, the E4M3
+ * value nearest to max|v| / 6 (ties to the even code, saturating at 448, 0 for
+ * small enough blocks; 0x7F, the E4M3 NaN, if the block holds a NaN or an
+ * infinity), and each code is the OCP FP4 E2M1 value nearest to |v| / s (ties
+ * to the even code, saturating at 6) with the sign of v: 0 with the sign when
+ * s = 0, the largest magnitude with the sign in a NaN/Inf block. No second,
+ * per-tensor scale: s scales the values themselves. Two codes per byte, the
+ * even-indexed value in the low nibble.
+ *   rank_q [cap_rank*H/2] out: codes; rank_scale [cap_rank*H/16] out: scales
+ *   other arguments and requirements as for moe_dispatch_pack_mxfp8.
+ */
+int moe_dispatch_pack_nvfp4(const moe_shape_t* shape, const uint16_t* hidden,
+                            const int32_t* token_rank_slot, uint8_t* rank_q,
+                            uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                            int32_t* err_word, void* stream);
+
+/*
+ * moe_permute_by_expert for the 16-value-block 4-bit rows of
+ * moe_dispatch_pack_nvfp4: each row's H/2 code bytes and H/16 scales move
+ * together, as in moe_permute_by_expert_mxfp8.
+ *   rank_q [cap_rank*H/2], rank_scale [cap_rank*H/16] in
+ *   expert_q [cap_expert*H/2], expert_scale [cap_expert*H/16] out
+ */
+int moe_permute_by_expert_nvfp4(const moe_shape_t* shape, const uint8_t* rank_q,
                                 const uint8_t* rank_scale, const int32_t* rank_src_token,
                                 const int32_t* rank_offsets, const int32_t* topk_ids,
                                 const int32_t* pair_row, const int32_t* expert_counts,

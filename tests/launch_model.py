@@ -570,17 +570,19 @@ def model_two_stage(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, r
         rep.access("rank_sum", "out_f32", rows_cols(tt, f32, 2 * nvec), "store")
 
 
-def model_pack_mx(c: Case, lay: dict, bits: int, rep: Report):
-    """pack_rows_mx<NP, bits>: byte indices for codes and scales."""
+def model_pack_mx(c: Case, lay: dict, bits: int, rep: Report, e4m3: bool = False):
+    """pack_rows_mx<NP, bits, e4m3>: byte indices for codes and scales (a scale
+    byte per 32 values, or per 16 with e4m3)."""
     T, R, nvec = c.T, c.R, c.nvec
+    bv = 2 if e4m3 else 4  # vec4 per scale block
     rep.buf("hidden", T * nvec)
-    rep.buf("rank_q", c.cap_rank * nvec * bits)       # bytes
-    rep.buf("rank_scale_b", c.cap_rank * (nvec // 4))  # bytes
+    rep.buf("rank_q", c.cap_rank * nvec * bits)        # bytes
+    rep.buf("rank_scale_b", c.cap_rank * (nvec // bv))  # bytes
     rep.buf("rank_src_token", c.cap_rank)
     if T == 0:
         return
     nl = 2 if bits == 8 else 1
-    nb, lpb = nl * bits, 4 // nl
+    nb, lpb = nl * bits, bv // nl
     npass = cdiv(nvec, W * nl)
     np_, slices = mx_passes(npass, MAX_VEC // nl), 1
     if (bits == 8 or T < FILL_TOKENS) and T * npass <= INT32_MAX:
@@ -606,8 +608,8 @@ def model_pack_mx(c: Case, lay: dict, bits: int, rep: Report):
     code_bytes = (st[:, None] * bits + np.arange(nb)[None, :]).ravel()
     rep.access("pack_mx", "rank_q", rows_cols(slots[ok], code_bytes, nvec * bits), "store")
     sb = np.concatenate(scols)
-    sb = (sb // 4)[:, None] + np.arange(4)[None, :]
-    rep.access("pack_mx", "rank_scale_b", rows_cols(slots[ok], sb, nvec // 4), "store")
+    sb = (sb // bv)[:, None] + np.arange(4)[None, :]
+    rep.access("pack_mx", "rank_scale_b", rows_cols(slots[ok], sb, nvec // bv), "store")
 
 
 # ----------------------------------------------------------------------------
@@ -652,7 +654,9 @@ def two_stage(c: Case, ids: np.ndarray, lay: dict | None = None,
 
 
 def mx(c: Case, ids: np.ndarray, bits: int, lay: dict | None = None,
-       rank_src: np.ndarray | None = None) -> Report:
+       rank_src: np.ndarray | None = None, e4m3: bool = False) -> Report:
+    """The quantised dispatch: MXFP8 (bits 8), MXFP4 (bits 4), or with e4m3 the
+    4-bit row with a scale byte per 16 values."""
     rep = Report()
     if lay is None:
         lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
@@ -660,10 +664,11 @@ def mx(c: Case, ids: np.ndarray, bits: int, lay: dict | None = None,
         _, rank_src, _ = oracle.pack(np.zeros((c.T, 8), np.uint16), lay["token_rank_slot"],
                                      c.cap_rank)
     model_layout(c, rep)
-    model_pack_mx(c, lay, bits, rep)
+    model_pack_mx(c, lay, bits, rep, e4m3)
     qrep = Report(sizes=dict(rep.sizes))  # code rows replace the bf16 rows' sizes
-    model_permute(c, lay, rank_src, ids, qrep, nvec=c.H * bits // 128, nvec_s=c.H // 512,
-                  tag=f"permute_mxfp{bits}")
+    model_permute(c, lay, rank_src, ids, qrep, nvec=c.H * bits // 128,
+                  nvec_s=c.H // (256 if e4m3 else 512),
+                  tag="permute_nvfp4" if e4m3 else f"permute_mxfp{bits}")
     rep.violations += qrep.violations
     rep.counted += qrep.counted
     return rep

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 6
+    assert L.moe_abi_version() == moe.ABI_VERSION == 7
 
 
 def test_timing_hook_takes_both_events_or_neither():

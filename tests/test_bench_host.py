@@ -54,9 +54,9 @@ def test_algorithmic_bytes_are_the_arrays_each_call_touches():
     offsets_b = lay["rank_offsets"].nbytes
     assert ts["partial"] == P * row + C * row + src_b + ids_b + pair_b + weights_b + offsets_b
     assert ts["ranks"] == C * row + hidden + slots_b
-    for bits in (8, 4):
-        qrow = H * bits // 8 + H // 32  # codes + one E8M0 scale byte per 32 values
-        mx = bench.mx_bytes(T, H, R, k, C, P, bits)
+    for fmt, bits, per in (("mxfp8", 8, 32), ("mxfp4", 4, 32), ("nvfp4", 4, 16)):
+        qrow = H * bits // 8 + H // per  # codes + one scale byte per 32 (16) values
+        mx = bench.mx_bytes(T, H, R, k, C, P, fmt)
         assert mx["pack"] == hidden + C * qrow + slots_b + src_b
         assert mx["permute"] == C * qrow + P * qrow + src_b + ids_b + pair_b + esrc_b
 

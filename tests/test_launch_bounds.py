@@ -47,12 +47,16 @@ def test_whole_path_random_shapes(lo, hi):
             assert_clean(lm.two_stage(case_of(c), ids), f"seed {s} two-stage")
 
 
-@pytest.mark.parametrize("bits", [8, 4])
-def test_mx_random_shapes(bits):
+QFORMATS = {"mxfp8": (8, False), "mxfp4": (4, False), "nvfp4": (4, True)}
+
+
+@pytest.mark.parametrize("fmt", list(QFORMATS))
+def test_mx_random_shapes(fmt):
+    bits, e4m3 = QFORMATS[fmt]
     for s in list(range(200, 224)) + list(range(10000, 10060)):
         c = rs.draw(s, mx=True)
         ids, _, _ = rs.inputs(c)
-        assert_clean(lm.mx(case_of(c), ids, bits), f"mx{bits} seed {s}")
+        assert_clean(lm.mx(case_of(c), ids, bits, e4m3=e4m3), f"{fmt} seed {s}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
@@ -64,8 +68,9 @@ def test_workloads(name):
         assert_clean(lm.one_stage(c, ids), f"{name} form {form}")
     assert_clean(lm.two_stage(lm.Case(w.T, w.H, w.E, w.R, w.k), ids), f"{name} two-stage")
     if w.H % 512 == 0:
-        for bits in (8, 4):
-            assert_clean(lm.mx(lm.Case(w.T, w.H, w.E, w.R, w.k), ids, bits), f"{name} mx{bits}")
+        for fmt, (bits, e4m3) in QFORMATS.items():
+            assert_clean(lm.mx(lm.Case(w.T, w.H, w.E, w.R, w.k), ids, bits, e4m3=e4m3),
+                         f"{name} {fmt}")
 
 
 def test_undersized_caps():
@@ -97,8 +102,9 @@ def test_arbitrary_index_arrays():
         ids, _, _ = rs.inputs(c)
         case = case_of(c)
         lay, src = lm.arbitrary_layout(rng, case)
-        for bits in (8, 4):
-            assert_clean(lm.mx(case, ids, bits, lay=lay, rank_src=src), f"mx seed {12000 + s}")
+        for fmt, (bits, e4m3) in QFORMATS.items():
+            assert_clean(lm.mx(case, ids, bits, lay=lay, rank_src=src, e4m3=e4m3),
+                         f"{fmt} seed {12000 + s}")
 
 
 def test_model_finds_the_earlier_permute_reads():

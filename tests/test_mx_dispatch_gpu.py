@@ -1,7 +1,7 @@
-"""GPU parity of the quantised dispatch (fused MXFP8 and MXFP4 quantise-and-
-pack, and the permute of quantised rows) against the oracle, through the C
-ABI: codes, scales, source ids and untouched canary rows, bit for bit. Integer
-work, so the bar is bit-exact."""
+"""GPU parity of the quantised dispatch (fused MXFP8, MXFP4 and 16-value-block
+"NVFP4" quantise-and-pack, and the permute of quantised rows) against the
+oracle, through the C ABI: codes, scales, source ids and untouched canary rows,
+bit for bit. Integer work, so the bar is bit-exact."""
 import sys
 
 import numpy as np
@@ -32,7 +32,12 @@ def _gpu():
     moe.lib()
 
 
-def run_gpu(hid, ids, E, R, bits=8, align=1, block=0, cap_rank=None, cap_expert=None, spare=4):
+FORMATS = ["mxfp8", "mxfp4", "nvfp4"]
+
+
+def run_gpu(hid, ids, E, R, fmt="mxfp8", align=1, block=0, cap_rank=None, cap_expert=None,
+            spare=4):
+    bits, blk = moe.WIRE_FORMATS[fmt]
     T, H = hid.shape
     k = ids.shape[1]
     shape = moe.Shape(T, H, E, R, k, align, block)
@@ -48,14 +53,14 @@ def run_gpu(hid, ids, E, R, bits=8, align=1, block=0, cap_rank=None, cap_expert=
     lay = moe.layout(ids_d, E, R, H, align=align, block=block, err=err, workspace=workspace)
     qw = H * bits // 8  # code bytes per row
     rq = torch.full((cap_rank + spare, qw), CANARY, dtype=u8, device=dev)
-    rs = torch.full((cap_rank + spare, H // 32), CANARY, dtype=u8, device=dev)
+    rs = torch.full((cap_rank + spare, H // blk), CANARY, dtype=u8, device=dev)
     rsrc = torch.full((cap_rank + spare,), CANARY_IDX, dtype=i32, device=dev)
     eq = torch.full((cap_expert + spare, qw), CANARY, dtype=u8, device=dev)
-    es = torch.full((cap_expert + spare, H // 32), CANARY, dtype=u8, device=dev)
+    es = torch.full((cap_expert + spare, H // blk), CANARY, dtype=u8, device=dev)
     esrc = torch.full((cap_expert + spare,), CANARY_IDX, dtype=i32, device=dev)
-    moe.pack_mx(bits, hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
+    moe.pack_mx(fmt, hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
                 rsrc[:cap_rank], err=err)
-    moe.permute_mx(bits, rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"],
+    moe.permute_mx(fmt, rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"],
                    ids_d, lay["pair_row"], E, eq[:cap_expert], es[:cap_expert],
                    esrc[:cap_expert], expert_counts=lay["expert_counts"],
                    expert_offsets=lay["expert_offsets"], align=align, block=block, err=err)
@@ -67,15 +72,15 @@ def run_gpu(hid, ids, E, R, bits=8, align=1, block=0, cap_rank=None, cap_expert=
     return out
 
 
-def check(hid, ids, E, R, what, bits=8, align=1, block=0, **kw):
-    g = run_gpu(hid, ids, E, R, bits, align, block, **kw)
+def check(hid, ids, E, R, what, fmt="mxfp8", align=1, block=0, **kw):
+    g = run_gpu(hid, ids, E, R, fmt, align, block, **kw)
     T, k = ids.shape
     lay = oracle.layout(ids, E, R, align=align, block=block)
     for key in ("token_rank_slot", "pair_row", "rank_offsets", "expert_offsets"):
         assert np.array_equal(g[key], lay[key]), f"{what}: layout {key}"
     cr, ce = g["cap_rank"], g["cap_expert"]
-    pack = oracle.pack_mxfp8 if bits == 8 else oracle.pack_mxfp4
-    permute = oracle.permute_mxfp8 if bits == 8 else oracle.permute_mxfp4
+    pack = getattr(oracle, f"pack_{fmt}")
+    permute = getattr(oracle, f"permute_{fmt}")
     rq, rs, src, e1 = pack(hid, lay["token_rank_slot"], cr)
     eq, es, esrc, e2 = permute(rq, rs, src, lay, ids, E, ce)
     assert g["err"] == lay["err"] | e1 | e2, f"{what}: error word {g['err']}"
@@ -95,19 +100,19 @@ def check(hid, ids, E, R, what, bits=8, align=1, block=0, **kw):
     return lay
 
 
-@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
-def test_mx_workload_parity(name, bits):
+def test_mx_workload_parity(name, fmt):
     w = synth.WORKLOADS[name]
-    say(f"[mxfp{bits}] {w.describe()}")
+    say(f"[{fmt}] {w.describe()}")
     hid = synth.hidden(w)
     ids, _ = synth.routing(w)
-    lay = check(hid, ids, w.E, w.R, name, bits=bits)
+    lay = check(hid, ids, w.E, w.R, name, fmt=fmt)
     assert lay["err"] == 0
 
 
-@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
-def test_mx_every_bit_pattern(bits):
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_mx_every_bit_pattern(fmt):
     """Hidden rows of random 16-bit patterns: NaNs, infinities, subnormals,
     zeros of both signs and the whole exponent range, in every block."""
     T, H, E, R, k = 300, 1024, 32, 4, 3
@@ -116,7 +121,29 @@ def test_mx_every_bit_pattern(bits):
     hid[::7] &= 0x80FF  # some rows of tiny and subnormal values only
     hid[1::11, :64] = 0x7F80  # some blocks with an infinity
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
-    check(hid, ids, E, R, "bit patterns", bits=bits)
+    check(hid, ids, E, R, "bit patterns", fmt=fmt)
+
+
+def test_nvfp4_every_block_max():
+    """Every bf16 bit pattern as the largest magnitude of a 16-value block (both
+    signs, NaNs and infinities included), the other 15 values random below it:
+    the E4M3 scale of every possible block maximum, ties included, and the codes
+    around it."""
+    H, E, R, k = 1024, 16, 4, 1
+    pats = np.arange(65536, dtype=np.uint32)
+    T = 65536 // (H // 16)
+    rng = np.random.default_rng(53)
+    top = pats.astype(np.uint32) << 16
+    topf = top.view(np.float32)
+    frac = rng.uniform(-1.0, 1.0, (65536, 15)).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        rest = (frac * np.abs(topf)[:, None]).astype(np.float32)
+    rest = np.where(np.isfinite(rest), rest, np.float32(0.0))
+    rest_bits = (rest.view(np.uint32) >> 16).astype(np.uint16)  # truncated: at most |top|
+    blocks = np.concatenate([pats.astype(np.uint16)[:, None], rest_bits], axis=1)
+    hid = blocks.reshape(T, H)
+    ids = np.zeros((T, k), np.int32) + (np.arange(T, dtype=np.int32) % E)[:, None]
+    check(hid, ids, E, R, "every block max", fmt="nvfp4")
 
 
 EDGE = [
@@ -131,25 +158,25 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("case", EDGE, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_R{c[3]}_k{c[4]}_a{c[5]}_b{c[6]}" for c in EDGE])
-def test_mx_edge_shapes(case, bits):
+def test_mx_edge_shapes(case, fmt):
     T, H, E, R, k, align, block, seed = case
-    say(f"[mxfp{bits} edge] {case}")
+    say(f"[{fmt} edge] {case}")
     rng = np.random.default_rng(seed)
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
     hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
-    check(hid, ids, E, R, f"edge {case}", bits=bits, align=align, block=block)
+    check(hid, ids, E, R, f"edge {case}", fmt=fmt, align=align, block=block)
 
 
-@pytest.mark.parametrize("bits", [8, 4], ids=["mxfp8", "mxfp4"])
-def test_mx_undersized_buffers(bits):
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_mx_undersized_buffers(fmt):
     w = synth.WORKLOADS["tiny"]
     hid = synth.hidden(w)
     ids, _ = synth.routing(w)
     lay = oracle.layout(ids, w.E, w.R)
     C, P = int(lay["rank_offsets"][-1]), int(lay["expert_offsets"][-1])
-    lay2 = check(hid, ids, w.E, w.R, "undersized", bits=bits, cap_rank=C - 37, cap_expert=P - 51,
+    lay2 = check(hid, ids, w.E, w.R, "undersized", fmt=fmt, cap_rank=C - 37, cap_expert=P - 51,
                  spare=64)
     assert lay2["err"] == 0
 
@@ -166,3 +193,6 @@ def test_mx_rejects_rows_not_a_multiple_of_512():
         moe.pack_mxfp8(hid, slots, E, k, rq, rs, src)
     with pytest.raises(moe.MoeError):
         moe.pack_mxfp4(hid, slots, E, k, rq[:, :H // 2], rs, src)
+    rs16 = torch.zeros((8, H // 16), dtype=torch.uint8, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.pack_nvfp4(hid, slots, E, k, rq[:, :H // 2], rs16, src)

@@ -120,11 +120,11 @@ MX_CASES = [draw(200 + s, mx=True) for s in range(24)]
 
 
 @pytest.mark.parametrize("c", MX_CASES, ids=[f"s{c['seed']}" for c in MX_CASES])
-@pytest.mark.parametrize("bits", [8, 4])
-def test_random_shape_mx(c, bits):
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
+def test_random_shape_mx(c, fmt):
     from test_mx_dispatch_gpu import check
-    say(f"[random mxfp{bits}] {c}")
+    say(f"[random {fmt}] {c}")
     ids, _, hid = inputs(c)
     with layout_form(c["form"], c["match"]):
-        check(hid, ids, c["E"], c["R"], f"random mxfp{bits} {c}", bits=bits, align=c["align"],
+        check(hid, ids, c["E"], c["R"], f"random {fmt} {c}", fmt=fmt, align=c["align"],
               block=c["block"])
