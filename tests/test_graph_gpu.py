@@ -97,3 +97,105 @@ def test_graph_replays_match_eager(T, H, E, R, k, align):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), \
                 f"replay {i}: {key} differs from the eager run"
         assert int(got["err"].item()) == 0
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
+def test_graph_quantised_dispatch(fmt):
+    """Layout, quantise-and-pack and the permute of quantised rows recorded in
+    one graph: every replay's codes, scales and source ids equal an eager run's
+    on the same fresh inputs."""
+    T, H, E, R, k = 1500, 2048, 64, 8, 4
+    say(f"[graph {fmt}] T={T} H={H} E={E} R={R} k={k}")
+    dev = torch.device("cuda:0")
+    bits, blk = moe.WIRE_FORMATS[fmt]
+    shape = moe.Shape(T, H, E, R, k)
+    u8, i32 = torch.uint8, torch.int32
+
+    def buffers():
+        b = moe.Buffers(shape, dev)
+        b.rq = torch.zeros((shape.cap_rank, H * bits // 8), dtype=u8, device=dev)
+        b.rs = torch.zeros((shape.cap_rank, H // blk), dtype=u8, device=dev)
+        b.eq = torch.zeros((shape.cap_expert, H * bits // 8), dtype=u8, device=dev)
+        b.es = torch.zeros((shape.cap_expert, H // blk), dtype=u8, device=dev)
+        return b
+
+    def run(b, hid_d, ids_d):
+        lay = moe.layout(ids_d, E, R, H, err=b.err, out=b.layout_dict(), workspace=b.workspace)
+        moe.pack_mx(fmt, hid_d, lay["token_rank_slot"], E, k, b.rq, b.rs, b.rank_src_token,
+                    err=b.err)
+        moe.permute_mx(fmt, b.rq, b.rs, b.rank_src_token, lay["rank_offsets"], ids_d,
+                       lay["pair_row"], E, b.eq, b.es, b.expert_src_pair,
+                       expert_counts=lay["expert_counts"], expert_offsets=lay["expert_offsets"],
+                       err=b.err)
+
+    g, e = buffers(), buffers()
+    hid0, ids0, _ = inputs(T, H, E, k, 200)
+    s_hid = staging.rows_to_device(hid0, dev)
+    s_ids = torch.from_numpy(ids0).to(dev)
+    run(g, s_hid, s_ids)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g, s_hid, s_ids)
+    for i in range(4):
+        hid, ids, _ = inputs(T, H, E, k, 201 + i)
+        s_hid.copy_(staging.rows_to_device(hid, dev))
+        s_ids.copy_(torch.from_numpy(ids).to(dev))
+        g.err.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        e.err.zero_()
+        run(e, staging.rows_to_device(hid, dev), torch.from_numpy(ids).to(dev))
+        torch.cuda.synchronize()
+        C = int(e.rank_offsets[-1].item())
+        P = int(e.expert_offsets[-1].item())
+        assert torch.equal(g.rank_offsets, e.rank_offsets) and torch.equal(g.pair_row, e.pair_row)
+        for key in ("rq", "rs", "rank_src_token"):
+            assert torch.equal(getattr(g, key)[:C], getattr(e, key)[:C]), f"replay {i}: {key}"
+        for key in ("eq", "es", "expert_src_pair"):
+            assert torch.equal(getattr(g, key)[:P], getattr(e, key)[:P]), f"replay {i}: {key}"
+        assert int(g.err.item()) == 0 and int(e.err.item()) == 0
+
+
+def test_graph_layout_noalloc():
+    """The allocation-free layout recorded in a graph (the two-launch form,
+    its tile counts in the library's static array): every replay equals the
+    layout with a caller workspace, run eagerly on the same fresh ids."""
+    T, E, R, k = 20000, 256, 8, 8
+    say(f"[graph noalloc layout] T={T} E={E} R={R} k={k}")
+    dev = torch.device("cuda:0")
+    shape = moe.Shape(T, 8, E, R, k)
+    assert moe.layout_workspace_bytes(shape) > 0  # the two-launch form
+    i32 = torch.int32
+
+    def outs():
+        return dict(rank_counts=torch.zeros(R, dtype=i32, device=dev),
+                    rank_offsets=torch.zeros(R + 1, dtype=i32, device=dev),
+                    expert_counts=torch.zeros(E, dtype=i32, device=dev),
+                    expert_offsets=torch.zeros(E + 1, dtype=i32, device=dev),
+                    token_rank_slot=torch.zeros((T, R), dtype=i32, device=dev),
+                    pair_row=torch.zeros((T, k), dtype=i32, device=dev))
+
+    g_out, e_out = outs(), outs()
+    g_err = torch.zeros(1, dtype=i32, device=dev)
+    e_err = torch.zeros(1, dtype=i32, device=dev)
+    ws = moe.layout_workspace_bytes(shape)
+    workspace = torch.zeros((ws + 3) // 4, dtype=i32, device=dev)
+    _, ids0, _ = inputs(T, 8, E, k, 300)
+    s_ids = torch.from_numpy(ids0).to(dev)
+    moe.layout_noalloc(s_ids, E, R, err=g_err, out=g_out)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.layout_noalloc(s_ids, E, R, err=g_err, out=g_out)
+    for i in range(4):
+        _, ids, _ = inputs(T, 8, E, k, 301 + i)
+        s_ids.copy_(torch.from_numpy(ids).to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        moe.layout(torch.from_numpy(ids).to(dev), E, R, err=e_err, out=e_out,
+                   workspace=workspace)
+        torch.cuda.synchronize()
+        for key in e_out:
+            assert torch.equal(g_out[key], e_out[key]), f"replay {i}: {key}"
+        assert int(g_err.item()) == int(e_err.item())
