@@ -112,6 +112,52 @@ def measured_traffic(kernel: str, workload: str):
 OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "combine_rows")
 
 
+# The passes of a default bench run, in order, in units of steps: each step
+# launches every library kernel of the path once. `sets` steps come first
+# (one dispatch per buffer set to place the expert outputs), then the
+# warm-up and six passes of `steps` steps each.
+RUN_PASSES = ("placement", "warmup", "rotated", "warm", "after_write", "per_call", "cold",
+              "roofline")
+
+
+def trace_passes(trace_csv: str, steps: int, warmup: int, sets: int) -> dict:
+    """Per library kernel and per pass of a default bench run, the mean, min
+    and max duration (us) of its dispatches in a rocprofv3 kernel trace
+    (run_kernel_trace.csv of `rocprofv3 --kernel-trace -- python3 bench.py`),
+    so that the roofline pass can be compared with the bench line's own
+    kernel time."""
+    import csv
+    import re
+
+    durs = {}
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            name = re.sub(r"\(.*", "", row["Kernel_Name"].replace("void ", "").replace(
+                "(anonymous namespace)::", ""))
+            if not name.startswith(OUR_KERNELS):
+                continue
+            durs.setdefault(name, []).append(
+                (int(row["Dispatch_Id"]), (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3))
+    sizes = [sets, warmup] + [steps] * 6
+    out = {}
+    for name, d in durs.items():
+        d.sort()
+        # the combine does not run in the placement dispatches
+        sz = sizes if len(d) == sum(sizes) else [0] + sizes[1:]
+        if len(d) != sum(sz):
+            out[name] = {"error": f"{len(d)} dispatches, expected {sum(sizes)}"}
+            continue
+        res, i = {}, 0
+        for pas, n in zip(RUN_PASSES, sz):
+            v = [x for _, x in d[i:i + n]]
+            i += n
+            if v:
+                res[pas] = {"mean_us": round(sum(v) / len(v), 2), "min_us": round(min(v), 2),
+                            "max_us": round(max(v), 2), "n": len(v)}
+        out[name] = res
+    return out
+
+
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: float, workload: str) -> dict:
     """Per-launch HBM traffic of each kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), each scaled by what the same
@@ -642,7 +688,14 @@ def main():
                     help="first run a plain device copy of MIB MiB (for counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs into profiles/traffic.json")
+    ap.add_argument("--trace-passes", metavar="TRACE_CSV",
+                    help="per-pass kernel durations from the rocprofv3 kernel trace of a bench "
+                         "run with the same --steps, --warmup and --sets")
     args = ap.parse_args()
+    if args.trace_passes:
+        print(json.dumps(trace_passes(args.trace_passes, args.steps, args.warmup, args.sets),
+                         indent=1))
+        return
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters, args.copy_calibration or 512.0, args.workload)
         print(json.dumps(rec, indent=1, sort_keys=True))

@@ -104,3 +104,44 @@ def test_counter_ingestion_and_stale_source_guard(tmp_path, monkeypatch):
     stale["prefill"]["permute"]["source_sha256_16"] = "0" * 16
     (tmp_path / "traffic.json").write_text(json.dumps(stale))
     assert bench.measured_traffic("permute", "prefill") is None
+
+
+def test_trace_passes_split(tmp_path):
+    """The per-pass split of a kernel trace: every library kernel's dispatches,
+    in dispatch order, cut into the bench's passes (the combine has no
+    placement dispatches); a count that does not fit is reported, not split."""
+    steps, warmup, sets = 4, 2, 3
+    path = tmp_path / "run_kernel_trace.csv"
+    fields = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows, did, t = [], 0, 0
+
+    def add(name, us):
+        nonlocal did, t
+        did += 1
+        rows.append({"Kind": "KERNEL_DISPATCH", "Dispatch_Id": did, "Kernel_Name": name,
+                     "Start_Timestamp": t, "End_Timestamp": t + int(us * 1000)})
+        t += 10 ** 6
+
+    perm = "void (anonymous namespace)::permute_rows<10, false>(unsigned int const*, int)"
+    comb = "void (anonymous namespace)::combine_rows<5, false>(unsigned int const*)"
+    sizes = dict(zip(bench.RUN_PASSES, [sets, warmup] + [steps] * 6))
+    for p_i, (pas, n) in enumerate(sizes.items()):
+        for _ in range(n):
+            add(perm, 10 + p_i)
+            add("void at::native::fill_kernel<int>(int)", 1)
+            if pas != "placement":
+                add(comb, 100 + p_i)
+    add("void (anonymous namespace)::pack_rows<10>(unsigned int const*)", 5)  # one stray dispatch
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+    out = bench.trace_passes(str(path), steps, warmup, sets)
+    assert set(out) == {"permute_rows<10, false>", "combine_rows<5, false>", "pack_rows<10>"}
+    for p_i, pas in enumerate(bench.RUN_PASSES):
+        assert out["permute_rows<10, false>"][pas]["mean_us"] == 10 + p_i
+        if pas != "placement":
+            assert out["combine_rows<5, false>"][pas]["mean_us"] == 100 + p_i
+    assert "placement" not in out["combine_rows<5, false>"]
+    assert out["permute_rows<10, false>"]["roofline"]["n"] == steps
+    assert "error" in out["pack_rows<10>"]
