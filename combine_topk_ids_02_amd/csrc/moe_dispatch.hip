@@ -8,9 +8,10 @@
 //
 // Kernels
 //  layout_tiles  one launch. Every workgroup histograms all tokens (LDS
-//                atomics per expert, wavefront ballots per rank), scans the
-//                totals into expert and rank offsets, then ranks its own tile
-//                of tokens with wavefront ballots and writes absolute rows
+//                atomics per expert, wavefront ballots per rank; for one
+//                tile the ranking waves' own counts), scans the totals into
+//                expert and rank offsets, then ranks its own tile of tokens
+//                (an LDS match of equal experts) and writes absolute rows
 //                ([A2A] sec 3.2 step 1: per-token rank set and per-rank
 //                counts; sec 5.1: offsets stay on the GPU, no CPU wait)
 //  pack_rows     one wave per token: read the row once, write one copy per
@@ -23,6 +24,9 @@
 //  rank_partial_rows / rank_sum_rows  the two-stage combine of [A2A] sec 7.1:
 //                one bf16 partial row per (token, rank) copy, then the sum of
 //                a token's partial rows at home in rank order
+//  pack_rows_mx  fused quantise-and-pack to the [A2A] sec 7.2 wire formats:
+//                MXFP8, MXFP4, and the 4-bit row with an E4M3 scale per 16
+//                values; permute_rows moves their codes and scales
 // Rows move 16 bytes per lane (global_load/store_dwordx4), 1 KiB per wave
 // instruction. Cache policy per stream, chosen by measurement of the whole
 // layout -> pack -> permute -> combine sequence: the packed rows are written
@@ -63,7 +67,7 @@ constexpr int kMaxRanks = 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxVec = 16;                 // vec4 per lane held in registers per pass
 constexpr int kMaxAlign = 1 << 16;          // largest run padding
-constexpr int kMxRowQuantum = 512;          // MXFP8 rows: H a multiple of 512 (whole vec4 of scales)
+constexpr int kMxRowQuantum = 512;          // quantised rows: H a multiple of 512 (whole vec4 of scales)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -1739,7 +1743,7 @@ struct RankSumLaunch {
   }
 };
 
-// The permute for bf16 rows (rank_scale == NULL) or MXFP8 rows (codes of
+// The permute for bf16 rows (rank_scale == NULL) or quantised rows (codes of
 // nvec vec4 plus scales of nvec_s vec4 per row).
 int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_scale,
                  const int32_t* rank_src_token, const int32_t* rank_offsets,
