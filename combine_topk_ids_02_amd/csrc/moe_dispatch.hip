@@ -956,7 +956,8 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
 }
 
 // The pack for small batches (fewer than kFillTokens tokens, where one wave
-// per token cannot fill the GPU): one wave per (token, group of 64 vec4), one
+// per token cannot fill the GPU) and for copies beyond the Infinity Cache
+// (kPackSplitBytes): one wave per (token, group of 64 vec4), one
 // vec4 per lane, the group index fastest so that a row's groups run side by
 // side. The same copies, order and cache policy as pack_rows.
 __global__ __launch_bounds__(kBlock) void pack_rows_small(
@@ -1610,6 +1611,11 @@ int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_
 // split rows across waves.
 constexpr int kFillTokens = 1024;
 
+// T * min(k, R) * H * 2 (the most bytes the pack can copy) above which the
+// pack takes one wave per 1 KiB of the row at any batch size: the 256 MiB
+// Infinity Cache.
+constexpr int64_t kPackSplitBytes = int64_t(256) << 20;
+
 // Register tile V of pack and permute (vec4 per lane per pass): the whole row
 // in one pass when it has at most 16 groups of 64 vec4, else a divisor of the
 // group count in [8, 16] if there is one (no tail), else 16.
@@ -1954,9 +1960,14 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
   if (!aligned16(hidden) || !aligned16(rank_buf)) return MOE_ERR_ARG;
   const int nvec = shape->H / 8;
   const int groups = (nvec + kWave - 1) / kWave;
-  if (shape->T < kFillTokens && groups > 1) {
+  const int64_t copy_bytes = int64_t(shape->T) * std::min(shape->k, shape->R) * shape->H * 2;
+  if ((shape->T < kFillTokens || copy_bytes > kPackSplitBytes) && groups > 1) {
     // Small batch: one wave per (token, 1 KiB of the row) (decode step 21.9
-    // vs 23.0 us). At prefill one wave per token is faster.
+    // vs 23.0 us). So too when the copies can outgrow the Infinity Cache:
+    // their stores then go on to HBM, which takes them faster from one wave
+    // per 1 KiB (T=16384 H=7168 k=8: 234 vs 247 us). Below that one wave per
+    // token is faster (T=4096 H=5120 k=6, whose copies wait in the cache for
+    // the permute: +1.4 us per step with one wave per 1 KiB).
     MOE_LAUNCH(pack_rows_small, dim3(blocks_for(int64_t(shape->T) * groups)),
                        dim3(kBlock), 0, static_cast<hipStream_t>(stream),
                        reinterpret_cast<const vec4*>(hidden), token_rank_slot,

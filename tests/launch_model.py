@@ -45,6 +45,7 @@ COUNT_THREADS = 256
 FILL_TOKENS = 1024
 COMBINE_GROUPS = 8
 COMBINE_ONE_GROUP_BYTES = 256 << 20
+PACK_SPLIT_BYTES = 256 << 20
 PARTIAL_GROUPS = 3
 RANK_SUM_GROUPS = 1
 INT32_MAX = 2 ** 31 - 1
@@ -393,7 +394,8 @@ def model_pack(c: Case, lay: dict, rep: Report):
     ok = (slots >= 0) & (slots < c.cap_rank)
     rep.access("pack", "rank_src_token", slots[ok], "store")
     groups = cdiv(nvec, W)
-    if T < FILL_TOKENS and groups > 1:
+    split = T < FILL_TOKENS or T * min(c.k, R) * nvec * 16 > PACK_SPLIT_BYTES
+    if split and groups > 1:
         kname = "pack_rows_small"
         # one wave per (token, group): loads min(g*64 + lane, nvec - 1), stores c < nvec
         cols = np.arange(groups)[:, None] * W + LANE[None, :]
