@@ -1961,7 +1961,8 @@ int moe_dispatch_pack(const moe_shape_t* shape, const uint16_t* hidden,
   const int nvec = shape->H / 8;
   const int groups = (nvec + kWave - 1) / kWave;
   const int64_t copy_bytes = int64_t(shape->T) * std::min(shape->k, shape->R) * shape->H * 2;
-  if ((shape->T < kFillTokens || copy_bytes > kPackSplitBytes) && groups > 1) {
+  if ((shape->T < kFillTokens || copy_bytes > kPackSplitBytes) && groups > 1 &&
+      int64_t(shape->T) * groups <= INT32_MAX) {
     // Small batch: one wave per (token, 1 KiB of the row) (decode step 21.9
     // vs 23.0 us). So too when the copies can outgrow the Infinity Cache:
     // their stores then go on to HBM, which takes them faster from one wave

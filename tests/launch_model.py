@@ -395,7 +395,7 @@ def model_pack(c: Case, lay: dict, rep: Report):
     rep.access("pack", "rank_src_token", slots[ok], "store")
     groups = cdiv(nvec, W)
     split = T < FILL_TOKENS or T * min(c.k, R) * nvec * 16 > PACK_SPLIT_BYTES
-    if split and groups > 1:
+    if split and groups > 1 and T * groups <= INT32_MAX:
         kname = "pack_rows_small"
         # one wave per (token, group): loads min(g*64 + lane, nvec - 1), stores c < nvec
         cols = np.arange(groups)[:, None] * W + LANE[None, :]
