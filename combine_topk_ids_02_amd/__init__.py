@@ -494,7 +494,7 @@ def time_next_launch(start: "torch.cuda.Event | None", stop: "torch.cuda.Event |
 
 class Buffers:
     """Every buffer of one dispatch + combine pass, allocated once for a shape
-    at worst-case size (cap_rank = T*min(k,R), cap_expert = T*k rows)."""
+    at worst-case size (Shape.cap_rank and Shape.cap_expert rows)."""
 
     def __init__(self, shape: Shape, device, row_dtype=torch.bfloat16, want_f32: bool = False):
         T, H, E, R, k = shape.T, shape.H, shape.E, shape.R, shape.k

@@ -1010,9 +1010,6 @@ __device__ __forceinline__ void mark_padding(int e, const int32_t* expert_counts
   for (int64_t row = lo + lane_id(); row < hi; row += kWave) expert_src_pair[row] = -1;
 }
 
-// With a padded or blocked layout, the first pad_waves = E waves mark one
-// expert's padding rows each (first, so that their latency hides under the
-// row copies); then one wave per rank-buffer row.
 // ---------------------------------------------------------------------------
 // MXFP8 wire format: per block of 32 consecutive values of a row, one E8M0
 // scale byte (2^e, e = floor(log2 amax) - 8 clamped to [-127, 127]; 0xFF if the
@@ -1269,8 +1266,13 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
   }
 }
 
-// kMx: the rows are MXFP8 codes, and each also has a row of nvec_s vec4 of
-// scales in rank_scale / expert_scale that moves with it.
+// Permute: one wave per rank-buffer row, which it copies to the expert row of
+// every pair of its token on its rank. With a padded or blocked layout the
+// first pad_waves = E waves mark one expert's padding rows each (first, so
+// that their latency hides under the row copies).
+// kMx: the rows are quantised codes (MXFP8, MXFP4 or the 16-value 4-bit
+// row), and each also has a row of nvec_s vec4 of scales in rank_scale /
+// expert_scale that moves with it.
 //
 // Packed bf16 rows are read non-temporally; packed MX codes and scales with
 // ordinary loads. With streamed loads the MX step lost the pack's cache
