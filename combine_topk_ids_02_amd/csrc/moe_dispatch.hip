@@ -15,7 +15,9 @@
 //                ([A2A] sec 3.2 step 1: per-token rank set and per-rank
 //                counts; sec 5.1: offsets stay on the GPU, no CPU wait)
 //  pack_rows     one wave per token: read the row once, write one copy per
-//                distinct rank ([A2A] sec 1.3 third answer)
+//                distinct rank ([A2A] sec 1.3 third answer); pack_rows_small
+//                the same with one wave per 1 KiB of the row, for small
+//                batches and for copies larger than the Infinity Cache
 //  permute_rows  one wave per rank-buffer row: read once, write once per
 //                local expert ([A2A] sec 3.3, sec 5.1 do_expand)
 //  combine_rows  one wave per (token, column slice): k row gathers, fp32 FMA
