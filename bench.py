@@ -61,6 +61,16 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
     }
 
 
+def whole_dispatch_bytes(T, H, E, R, k, C, P):
+    """Bytes of moe_dispatch in its one-launch form: the layout's, each hidden
+    row read once, each copy and each expert row written once with its source
+    id (the packed rows are not read back, so this is less than the three
+    calls' sum and is reported on its own)."""
+    row = 2 * H
+    return {"dispatch": algorithmic_bytes(T, H, E, R, k, C, P)["layout"] + T * row
+            + C * row + 4 * C + P * row + 4 * P}
+
+
 # Quantised wire formats: name -> (code bits per value, values per scale byte).
 WIRE = {"mxfp8": (8, 32), "mxfp4": (4, 32), "nvfp4": (4, 16)}
 
@@ -109,7 +119,8 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "combine_rows")
+OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "combine_rows",
+               "dispatch_small")
 
 
 # The passes of a default bench run, in order, in units of steps: each step
@@ -344,6 +355,7 @@ class Rig:
         if two_stage:
             self.nbytes.update(two_stage_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
             self.calls = CALLS + TWO_STAGE_CALLS
+        self.nbytes.update(whole_dispatch_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P))
 
     def _make_set(self, y_d):
         import types
@@ -418,6 +430,10 @@ class Rig:
                         s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
                         expert_offsets=b.expert_offsets, align=s.align, block=s.block,
                         err=b.err)
+        elif name == "dispatch":
+            moe.dispatch_all(x.hid_d, x.ids_d, s.E, s.R, b.layout_dict(), b.rank_buf,
+                             b.rank_src_token, b.expert_buf, b.expert_src_pair,
+                             align=s.align, block=s.block, workspace=b.workspace, err=b.err)
         elif name == "combine":
             moe.combine(x.expert_out, b.pair_row, x.wts_d, s.E, s.R, b.out, err=b.err)
         elif name == "partial":
@@ -490,27 +506,32 @@ class Rig:
                 out[c].append(a.elapsed_time(b))
         return out
 
-    def graph_step_us(self, n: int = 200) -> float:
-        """One step recorded in a HIP graph, replayed n times back to back: the
-        step's GPU time without host launch gaps (what a decode loop that
-        replays a recorded step sees)."""
+    def graph_step_us(self, n: int = 200, calls=CALLS, per_graph: int = 20) -> float:
+        """`per_graph` steps recorded in one HIP graph (as a decode loop records
+        the MoE layers of a forward pass), replayed back to back: the step's GPU
+        time without host launch gaps and without the fixed cost of submitting
+        a graph, which for one short step alone is longer than the step (about
+        13 us per replay here). calls: the one-stage path, layout, pack,
+        permute and combine, or ("dispatch", "combine")."""
         import torch
 
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in CALLS:  # the one-stage path: layout, pack, permute, combine
-                self.call(c)
+            for _ in range(per_graph):
+                for c in calls:
+                    self.call(c)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-        def timed(reps: int) -> float:
+        def timed(steps: int) -> float:
+            reps = max(1, steps // per_graph)
             torch.cuda.synchronize()
             a.record()
             for _ in range(reps):
                 g.replay()
             b.record()
             torch.cuda.synchronize()
-            return a.elapsed_time(b) / reps * 1e3
+            return a.elapsed_time(b) / (reps * per_graph) * 1e3
 
         # The first replays of a new graph run slower, and an idle GPU takes a
         # while to raise its clocks: replay for about 30 ms before timing.
@@ -630,6 +651,14 @@ def sweep(names, dev, with_oracle: bool) -> None:
         res["graph"] = {"us_per_step": round(us_g, 2),
                         "note": "layout, pack, permute, combine replayed from one HIP graph"}
         log(f"{name}: graph replay {us_g:.1f} us per step")
+        if not wire:
+            us_d = rig.graph_step_us(calls=("dispatch", "combine"))
+            res["graph_whole_dispatch"] = {
+                "us_per_step": round(us_d, 2),
+                "one_launch": w.T <= 64 and align == 1,
+                "note": "moe_dispatch (one launch up to 64 tokens with align 1, else the three "
+                        "calls) and combine, replayed from one HIP graph"}
+            log(f"{name}: graph replay with moe_dispatch {us_d:.1f} us per step")
         if with_oracle and align == 1 and block == 0 and not wire:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
@@ -661,10 +690,13 @@ def sweep(names, dev, with_oracle: bool) -> None:
                   f"| {p['us']} | {p['GB/s']} | {p['pct_peak']} |")
     print("\nOne step (layout, pack, permute, combine) replayed from one HIP graph, back to "
           "back (no host launch gaps), next to the sum of the per-call warm times:\n")
-    print("| workload | us per step (graph) | sum of per-call warm us |")
-    print("|---|---|---|")
+    print("| workload | us per step (graph) | with moe_dispatch (graph) | sum of per-call warm us |")
+    print("|---|---|---|---|")
     for name, r in rows:
-        print(f"| {name} | {r['graph']['us_per_step']} | {r['warm']['us']} |")
+        wd = r.get("graph_whole_dispatch")
+        wds = "" if wd is None else f"{wd['us_per_step']}" + (" (one launch)" if wd["one_launch"]
+                                                               else "")
+        print(f"| {name} | {r['graph']['us_per_step']} | {wds} | {r['warm']['us']} |")
     print(f"\n1 GiB device copy: {copy['us']} us, {copy['GB/s']} GB/s (read + write)")
 
 

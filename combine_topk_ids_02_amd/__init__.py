@@ -31,11 +31,11 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
            "moe_dispatch_pack_nvfp4", "moe_permute_by_expert_nvfp4",
-           "moe_testing_set_layout_form", "moe_testing_set_layout_match",
-           "moe_testing_time_next_launch")
+           "moe_dispatch", "moe_testing_set_layout_form", "moe_testing_set_layout_match",
+           "moe_testing_set_dispatch_fused", "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # Quantised wire formats: name -> (code bits per value, values per scale byte).
 WIRE_FORMATS = {"mxfp8": (8, 32), "mxfp4": (4, 32), "nvfp4": (4, 16)}
@@ -105,6 +105,11 @@ def lib():
     L.moe_dispatch_pack_nvfp4.argtypes = L.moe_dispatch_pack_mxfp8.argtypes
     L.moe_permute_by_expert_nvfp4.restype = ctypes.c_int
     L.moe_permute_by_expert_nvfp4.argtypes = L.moe_permute_by_expert_mxfp8.argtypes
+    L.moe_dispatch.restype = ctypes.c_int
+    L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64,
+                               vp, ctypes.c_size_t, vp, vp]
+    L.moe_testing_set_dispatch_fused.restype = ctypes.c_int
+    L.moe_testing_set_dispatch_fused.argtypes = [ctypes.c_int]
     L.moe_testing_set_layout_form.restype = ctypes.c_int
     L.moe_testing_set_layout_form.argtypes = [ctypes.c_int]
     L.moe_testing_set_layout_match.restype = ctypes.c_int
@@ -318,6 +323,39 @@ def permute(rank_buf, rank_src_token, rank_offsets, topk_ids, pair_row, E: int, 
         rank_buf.shape[0], _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)),
         expert_buf.shape[0], _err(err), _stream(rank_buf.device))
     _check(st, "moe_permute_by_expert")
+
+
+def dispatch_all(hidden, topk_ids, E: int, R: int, out: dict, rank_buf, rank_src_token,
+                 expert_buf, expert_src_pair, *, align: int = 1, block: int = 0,
+                 workspace: torch.Tensor | None = None, err=None) -> None:
+    """moe_dispatch: layout, pack and permute in one call (one kernel launch
+    for up to 64 tokens with align = 1), into the caller's tensors: `out`
+    holds the layout's outputs (the keys of layout()), rank_buf [cap_rank, H],
+    rank_src_token [cap_rank], expert_buf [cap_expert, H], expert_src_pair
+    [cap_expert]."""
+    _check_err(err)
+    T, k = topk_ids.shape
+    H = hidden.shape[1]
+    _need(hidden, "hidden", (T, H))
+    for key, want in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
+                      ("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                      ("token_rank_slot", (T, R)), ("pair_row", (T, k))):
+        _need(out[key], key, want)
+        _i32(out[key])
+    cap_r = _rows(rank_buf, "rank_buf", H)
+    _need(rank_src_token, "rank_src_token", min_numel=cap_r)
+    cap_e = _rows(expert_buf, "expert_buf", H)
+    _need(expert_src_pair, "expert_src_pair", min_numel=cap_e)
+    shape = Shape(T, H, E, R, k, align, block)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().moe_dispatch(
+        ctypes.byref(shape.c()), _ptr(_rows16(hidden)), _ptr(_i32(topk_ids)),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]),
+        _ptr(out["expert_offsets"]), _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]),
+        _ptr(_rows16(rank_buf)), _ptr(_i32(rank_src_token)), rank_buf.shape[0],
+        _ptr(_rows16(expert_buf)), _ptr(_i32(expert_src_pair)), expert_buf.shape[0],
+        _ptr(workspace), ws_bytes, _err(err), _stream(hidden.device))
+    _check(st, "moe_dispatch")
 
 
 def _bytes(t: torch.Tensor) -> torch.Tensor:

@@ -119,6 +119,9 @@ int g_layout_form = -1;
 // 0: the layout matches equal experts with ballots even where the LDS tables
 // fit. Changed only by the testing hook.
 int g_layout_match = 1;
+// 0: moe_dispatch always makes the three calls, also where one launch would
+// do. Changed only by the testing hook.
+int g_dispatch_fused = 1;
 
 // Events armed by moe_testing_time_next_launch for the next kernel launch.
 hipEvent_t g_time_start = nullptr;
@@ -1353,6 +1356,198 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The whole dispatch of a small batch in one launch (moe_dispatch with at most
+// kSmallBatch tokens and unpadded runs): layout, pack and permute with no
+// kernel boundary between them, for the decode step, whose time is launches
+// and the waits between them. Every mover wave holds all T*k ids (lane u the
+// ids of token u) and works out from them, with wave ballots and wave sums,
+// the rows of its own token: as a low-latency sender decides where each row
+// goes without asking anyone ([A2A] sec 4.1), here for the rank segments and
+// the expert runs alike. Workgroup 0 writes the counts and offsets; with a
+// blocked layout the next pad_waves = E waves mark one expert's padding rows
+// each (its count is a wave sum over the ids); every other wave takes one
+// (token, 1 KiB of the row), reads that part of the hidden row once and
+// writes it to the token's copy on each of its ranks and to the row of each
+// of its pairs (the pair's row is written only if its rank copy was, as the
+// three calls do). The results are those of moe_dispatch_layout,
+// moe_dispatch_pack and moe_permute_by_expert, bit for bit.
+constexpr int kSmallBatch = kWave;
+
+// Sum over the wave, in every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(x), kWave - 1);
+}
+
+template <int K, int kRB>
+__global__ __launch_bounds__(kBlock) void dispatch_small(
+    const vec4* hidden, const int32_t* __restrict__ ids, int T, int E, int R, int k, int block,
+    float inv_m, int nvec, int groups, int pad_waves, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
+    int32_t* __restrict__ pair_row, vec4* rank_buf, int32_t* __restrict__ rank_src_token,
+    int64_t cap_rank, vec4* expert_buf, int32_t* __restrict__ expert_src_pair,
+    int64_t cap_expert, int32_t* err_word) {
+  constexpr int KR = K > 0 ? K : kMaxK;
+  const int kk = K > 0 ? K : k;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const bool counter = blockIdx.x == 0;
+  // Padding waves, then movers: a mover's token and 1 KiB group; its part of
+  // the hidden row is requested first (clamped into the row), the ids right
+  // behind it.
+  const int64_t gw = counter ? 0 : (int64_t)(blockIdx.x - 1) * kWavesPerBlock + wave;
+  const bool padder = !counter && gw < pad_waves;
+  const int64_t gm = padder ? 0 : gw - pad_waves;
+  const int t = int(gm / groups);
+  const int g = int(gm - (int64_t)t * groups);
+  if (!counter && !padder && t >= T) return;
+  const int c = g * kWave + lane;
+  vec4 v;
+  if (!counter && !padder) v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
+  int32_t idv[KR];  // lane u: the ids of token u (-1 past T)
+#pragma unroll
+  for (int j = 0; j < KR; ++j) idv[j] = (j < kk && lane < T) ? ids[lane * kk + j] : -1;
+  RankSet<kRB> set;  // lane u: the ranks of token u
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    if (j < kk) {
+      const bool valid = uint32_t(idv[j]) < uint32_t(E);
+      set.add(rank_of(valid ? idv[j] : 0, inv_m), valid);
+    }
+  }
+
+  if (counter) {
+    // Counts and offsets. Experts: an LDS histogram of all ids, then the
+    // exclusive scan of the run lengths (the counts, or `block` each).
+    __shared__ int32_t s_hist[kMaxExperts];
+    __shared__ int32_t s_part[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int f = tid; f < T * kk; f += kBlock) {
+      const int e = ids[f];
+      if (uint32_t(e) < uint32_t(E))
+        atomicAdd(&s_hist[e], 1);
+      else
+        bad |= e != -1;
+    }
+    if (__ballot(bad) && lane == 0) flag_error(err_word, MOE_ERRBIT_BAD_ID);
+    __syncthreads();
+    const int per = (E + kBlock - 1) / kBlock;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += block > 0 ? block : s_hist[e];
+    const int inc = wave_inclusive_scan(run);
+    if (lane == kWave - 1) s_part[wave] = inc;
+    __syncthreads();
+    int base = inc - run, total = 0;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      base += w < wave ? s_part[w] : 0;
+      total += s_part[w];
+    }
+    for (int e = lo; e < hi; ++e) {
+      expert_counts[e] = s_hist[e];
+      expert_offsets[e] = base;
+      base += block > 0 ? block : s_hist[e];
+    }
+    if (tid == 0) expert_offsets[E] = total;
+    // Copies per rank (wave 0, lane u = token u: one ballot per rank) and
+    // their offsets.
+    if (wave == 0) {
+      int mine = 0;
+      for (int r = 0; r < R; ++r) {
+        const int n = __popcll(__ballot(set.has(r)));
+        mine = lane == r ? n : mine;
+      }
+      const int rinc = wave_inclusive_scan(mine);
+      if (lane < R) {
+        rank_counts[lane] = mine;
+        rank_offsets[lane] = rinc - mine;
+      }
+      if (lane == kWave - 1) rank_offsets[R] = rinc;
+    }
+    return;
+  }
+
+  if (padder) {
+    // Expert e = gw of a blocked layout: the rows of its block past its pairs,
+    // within the buffer, get expert_src_pair -1.
+    const int e = int(gw);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+      if (j < kk) n += idv[j] == e ? 1 : 0;
+    const int filled = min(wave_sum(n), block);
+    const int64_t end = min((int64_t)(e + 1) * block, cap_expert);
+    for (int64_t row = (int64_t)e * block + filled + lane; row < end; row += kWave)
+      expert_src_pair[row] = -1;
+    return;
+  }
+
+  // The token's copies: ranks in order, its slot on rank r kept in lane r.
+  const uint64_t below = t == 0 ? 0ull : (~0ull >> (kWave - t));  // lanes (tokens) before t
+  int off = 0, my_slot = -1;
+  for (int r = 0; r < R; ++r) {
+    const uint64_t b = __ballot(set.has(r));
+    if ((b >> t) & 1) {
+      const int s = off + __popcll(b & below);
+      if (lane == r) my_slot = s;
+      if (s < cap_rank && c < nvec) store_row<true>(rank_buf + (int64_t)s * nvec + c, v);
+    }
+    off += __popcll(b);
+  }
+  if (g == 0) {
+    if (lane < R) token_rank_slot[(int64_t)t * R + lane] = my_slot;
+    const bool ok = my_slot >= 0 && my_slot < cap_rank;
+    if (__ballot(my_slot >= 0 && !ok) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+    if (ok) rank_src_token[my_slot] = t;
+  }
+
+  // The token's pairs, in slot order: the run's first row (the valid ids
+  // below e, or e*block) plus the pairs of e before (t, j), counted in one
+  // wave sum (below e in the low 16 bits, equal before (t, j) in the high).
+  bool full = false;
+  int my_row = -1;  // lane j: pair_row of slot j
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    if (j >= kk) break;
+    const int e = __builtin_amdgcn_readlane(idv[j], t);
+    if (uint32_t(e) >= uint32_t(E)) continue;
+    int n = 0;
+#pragma unroll
+    for (int jj = 0; jj < KR; ++jj) {
+      if (jj < kk) {
+        const int x = idv[jj];
+        n += uint32_t(x) < uint32_t(e) ? 1 : 0;
+        n += (x == e && (lane < t || (lane == t && jj < j))) ? (1 << 16) : 0;
+      }
+    }
+    const int sum = wave_sum(n);
+    const int rk = sum >> 16;
+    int p = (block > 0 ? e * block : (sum & 0xFFFF)) + rk;
+    if (block > 0 && rk >= block) {
+      p = -1;
+      full = true;
+    }
+    if (lane == j) my_row = p;
+    const int s = __builtin_amdgcn_readlane(my_slot, rank_of(e, inv_m));  // the copy it comes from
+    if (s < cap_rank) {
+      if (p >= 0 && p < cap_expert) {
+        if (c < nvec) store_row<true>(expert_buf + (int64_t)p * nvec + c, v);
+        if (g == 0 && lane == 0) expert_src_pair[p] = t * kk + j;
+      } else if (g == 0 && lane == 0) {
+        flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+      }
+    }
+  }
+  if (g == 0) {
+    if (lane < kk) pair_row[(int64_t)t * kk + lane] = my_row;
+    if (full && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+  }
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // NaN stays quiet NaN
@@ -1788,6 +1983,56 @@ int permute_impl(const moe_shape_t& sh, const void* rank_rows, const void* rank_
 }
 
 
+// The one-launch dispatch of a small batch: workgroup 0 for the counts, E
+// padding waves with a blocked layout, then one wave per (token, 1 KiB of the
+// row).
+struct DispatchSmallArgs {
+  const vec4* hidden;
+  const int32_t* ids;
+  int32_t *rc, *ro, *ec, *eo, *trs, *pr;
+  vec4* rank_buf;
+  int32_t* rank_src;
+  int64_t cap_rank;
+  vec4* expert_buf;
+  int32_t* expert_src;
+  int64_t cap_expert;
+  int32_t* err;
+};
+
+template <int K, int kRB>
+void launch_dispatch_small_kw(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {
+  const int nvec = sh.H / 8;
+  const int groups = (nvec + kWave - 1) / kWave;
+  const int pad_waves = sh.block > 0 && a.cap_expert > 0 ? sh.E : 0;
+  const int grid = 1 + blocks_for(pad_waves + int64_t(sh.T) * groups);
+  MOE_LAUNCH((dispatch_small<K, kRB>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids, sh.T,
+             sh.E, sh.R, sh.k, sh.block, float(1.0 / double(sh.E / sh.R)), nvec, groups,
+             pad_waves, a.rc,
+             a.ro, a.ec, a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
+             a.expert_src, a.cap_expert, a.err);
+}
+
+template <int K>
+void launch_dispatch_small_k(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {
+  if (sh.R > 32)
+    launch_dispatch_small_kw<K, 64>(sh, st, a);
+  else if (sh.R > 8)
+    launch_dispatch_small_kw<K, 32>(sh, st, a);
+  else
+    launch_dispatch_small_kw<K, 8>(sh, st, a);
+}
+
+void launch_dispatch_small(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {
+  switch (sh.k) {
+    case 1: launch_dispatch_small_k<1>(sh, st, a); break;
+    case 2: launch_dispatch_small_k<2>(sh, st, a); break;
+    case 4: launch_dispatch_small_k<4>(sh, st, a); break;
+    case 6: launch_dispatch_small_k<6>(sh, st, a); break;
+    case 8: launch_dispatch_small_k<8>(sh, st, a); break;
+    default: launch_dispatch_small_k<0>(sh, st, a);
+  }
+}
+
 // MX pack: NP passes in registers, the largest divisor of the pass count
 // that is at most `most` (so every register batch is whole).
 int mx_passes(int npass, int most) {
@@ -1897,6 +2142,12 @@ int moe_testing_set_layout_match(int match) {
   return old;
 }
 
+int moe_testing_set_dispatch_fused(int fused) {
+  const int old = g_dispatch_fused;
+  if (fused == 0 || fused == 1) g_dispatch_fused = fused;
+  return old;
+}
+
 int moe_testing_time_next_launch(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_ERR_ARG;
   g_time_start = static_cast<hipEvent_t>(start_event);
@@ -1997,6 +2248,55 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
   return permute_impl(*shape, rank_buf, nullptr, rank_src_token, rank_offsets, topk_ids,
                       pair_row, expert_counts, expert_offsets, cap_rank, expert_buf, nullptr,
                       expert_src_pair, cap_expert, err_word, stream, shape->H / 8, 0);
+}
+
+int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t* topk_ids,
+                 int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row,
+                 uint16_t* rank_buf, int32_t* rank_src_token, int64_t cap_rank,
+                 uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
+                 void* workspace, size_t workspace_bytes, int32_t* err_word, void* stream) {
+  // The checks of the three calls, all made before anything is launched.
+  if (!shape_ok(shape) || cap_rank < 0 || cap_expert < 0) return MOE_ERR_ARG;
+  const moe_shape_t& sh = *shape;
+  // layout
+  if (!rank_counts || !rank_offsets || !expert_counts || !expert_offsets) return MOE_ERR_ARG;
+  if (sh.T > 0 && (!topk_ids || !token_rank_slot || !pair_row || !aligned16(topk_ids)))
+    return MOE_ERR_ARG;
+  const size_t need = layout_workspace_bytes(layout_geometry(sh));
+  if (workspace && (workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_ARG;
+  // pack
+  if (sh.T > 0 && (!hidden || (cap_rank > 0 && (!rank_buf || !rank_src_token)) ||
+                   !aligned16(hidden) || !aligned16(rank_buf)))
+    return MOE_ERR_ARG;
+  // permute
+  const bool padded = sh.align > 1 || sh.block > 0;
+  const int64_t max_rows = std::min<int64_t>(cap_rank, int64_t(sh.T) * std::min(sh.k, sh.R));
+  if (max_rows > 0 || (padded && cap_expert > 0)) {
+    if (max_rows > 0 && cap_expert > 0 && !expert_buf) return MOE_ERR_ARG;
+    if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
+    if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
+  }
+  if (g_dispatch_fused && sh.T <= kSmallBatch && sh.align == 1) {
+    DispatchSmallArgs a{reinterpret_cast<const vec4*>(hidden), topk_ids, rank_counts,
+                        rank_offsets, expert_counts, expert_offsets, token_rank_slot, pair_row,
+                        reinterpret_cast<vec4*>(rank_buf), rank_src_token, cap_rank,
+                        reinterpret_cast<vec4*>(expert_buf), expert_src_pair, cap_expert,
+                        err_word};
+    launch_dispatch_small(sh, static_cast<hipStream_t>(stream), a);
+    return launch_status();
+  }
+  int st = moe_dispatch_layout(shape, topk_ids, rank_counts, rank_offsets, expert_counts,
+                               expert_offsets, token_rank_slot, pair_row, workspace,
+                               workspace_bytes, err_word, stream);
+  if (st == MOE_OK)
+    st = moe_dispatch_pack(shape, hidden, token_rank_slot, rank_buf, rank_src_token, cap_rank,
+                           err_word, stream);
+  if (st == MOE_OK)
+    st = moe_permute_by_expert(shape, rank_buf, rank_src_token, rank_offsets, topk_ids,
+                               pair_row, expert_counts, expert_offsets, cap_rank, expert_buf,
+                               expert_src_pair, cap_expert, err_word, stream);
+  return st;
 }
 
 int moe_dispatch_pack_mxfp8(const moe_shape_t* shape, const uint16_t* hidden,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 7
+#define MOE_DISPATCH_ABI_VERSION 8
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -214,6 +214,34 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
                           const int32_t* expert_counts, const int32_t* expert_offsets,
                           int64_t cap_rank, uint16_t* expert_buf, int32_t* expert_src_pair,
                           int64_t cap_expert, int32_t* err_word, void* stream);
+
+/*
+ * The whole dispatch in one call: moe_dispatch_layout, moe_dispatch_pack and
+ * moe_permute_by_expert on the same arguments, with the same results bit for
+ * bit and the same error bits. For a decode-sized batch (T <= 64 tokens) with
+ * unpadded runs (align = 1; block may be set) the three run as one kernel
+ * launch, because there the time is in launches and in each kernel waiting
+ * for the one before ([A2A] sec 8.1: a call that does nothing already costs
+ * about 10 microseconds; [GPUs] sec 7: DeepEP kept separate low-latency
+ * kernels for decoding). In that launch every wave works out the rows of its
+ * own token from the ids alone, as a low-latency sender places its rows
+ * without asking anyone ([A2A] sec 4.1), so nothing waits for the counts.
+ * Otherwise the three calls are made in turn on `stream`.
+ *   Arguments: those of the three calls (hidden, topk_ids, the layout's
+ *   outputs, rank_buf / rank_src_token / cap_rank, expert_buf /
+ *   expert_src_pair / cap_expert, the layout workspace), with the same
+ *   sizes, alignment and NULL rules; all are checked before anything is
+ *   launched, and an argument error launches nothing. The one-launch form
+ *   needs no workspace. rank_buf holds every copy as after
+ *   moe_dispatch_pack (the one-launch form streams it past the caches,
+ *   since nothing reads it back there).
+ */
+int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t* topk_ids,
+                 int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* token_rank_slot, int32_t* pair_row,
+                 uint16_t* rank_buf, int32_t* rank_src_token, int64_t cap_rank,
+                 uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
+                 void* workspace, size_t workspace_bytes, int32_t* err_word, void* stream);
 
 /*
  * Quantised dispatch, step 2: fused quantise-and-pack to MXFP8 ([A2A] sec 7.2:
@@ -396,6 +424,14 @@ int moe_testing_set_layout_form(int form);
  * Both give the same results.
  */
 int moe_testing_set_layout_match(int match);
+
+/*
+ * Testing hook (not for production callers; process-wide; returns the
+ * previous value): 1 (default) moe_dispatch runs a small batch as one launch
+ * as described there; 0 it always makes the three calls. Both give the same
+ * results.
+ */
+int moe_testing_set_dispatch_fused(int fused);
 
 /*
  * Measurement hook (not for production callers; process-wide, not

@@ -26,9 +26,10 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
             y_slots: np.ndarray | None, cap_rank: int | None = None,
             cap_expert: int | None = None, spare_rows: int = 4, want_f32: bool = True,
             device="cuda:0", stream: torch.cuda.Stream | None = None, align: int = 1,
-            block: int = 0, use_workspace: bool = True) -> dict:
+            block: int = 0, use_workspace: bool = True, whole_dispatch: bool = False) -> dict:
     """One full pass through the library. Row buffers get `spare_rows` canary
-    rows past their caps; the library is told only the caps."""
+    rows past their caps; the library is told only the caps. whole_dispatch:
+    layout, pack and permute through the one call moe_dispatch."""
     T, H = hid.shape
     k = ids.shape[1]
     shape = moe.Shape(T, H, E, R, k, align, block)
@@ -64,12 +65,18 @@ def run_gpu(hid: np.ndarray, ids: np.ndarray, wts: np.ndarray, E: int, R: int,
         workspace = None
         if ws:
             workspace = torch.full(((ws + 15) // 16 * 4,), 0x5A5A5A5A, dtype=i32, device=dev)
-        moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay,
-                   workspace=workspace)
-        moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
-        moe.permute(rank_buf, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"], E,
-                    expert_buf, expert_src, expert_counts=lay["expert_counts"],
-                    expert_offsets=lay["expert_offsets"], align=align, block=block, err=err)
+        if whole_dispatch:
+            moe.dispatch_all(hid_d, ids_d, E, R, lay, rank_buf, rank_src, expert_buf,
+                             expert_src, align=align, block=block, workspace=workspace,
+                             err=err)
+        else:
+            moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay,
+                       workspace=workspace)
+            moe.pack(hid_d, lay["token_rank_slot"], E, k, rank_buf, rank_src, err=err)
+            moe.permute(rank_buf, rank_src, lay["rank_offsets"], ids_d, lay["pair_row"], E,
+                        expert_buf, expert_src, expert_counts=lay["expert_counts"],
+                        expert_offsets=lay["expert_offsets"], align=align, block=block,
+                        err=err)
         if y_slots is None:
             expert_out = expert_buf
         else:

@@ -493,6 +493,83 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
             rep.access(tag, "expert_scale", rows_cols(p[ok], s1, nvec_s), "store")
 
 
+SMALL_BATCH = 64
+
+
+def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
+    """dispatch_small (moe_dispatch's one-launch form, T <= 64, align = 1):
+    workgroup 0 writes the counts and offsets; with a blocked layout one wave
+    per expert marks its padding rows; one wave per (token, group of 64 vec4)
+    moves that part of the row. The rows and slots
+    the waves compute from the ids are the layout's, so the oracle's layout
+    stands in for them; every store is guarded by the caps as in the kernel."""
+    T, E, R, k, nvec = c.T, c.E, c.R, c.k, c.nvec
+    m = E // R
+    for name, n in (("hidden", T * nvec), ("topk_ids", T * k), ("rank_counts", R),
+                    ("rank_offsets", R + 1), ("expert_counts", E), ("expert_offsets", E + 1),
+                    ("token_rank_slot", T * R), ("pair_row", T * k),
+                    ("rank_buf", c.cap_rank * nvec), ("rank_src_token", c.cap_rank),
+                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert)):
+        rep.buf(name, n)
+    tag = "dispatch_small"
+    groups = cdiv(nvec, W)
+    pad_waves = E if c.block > 0 and c.cap_expert > 0 else 0
+    nblocks = 1 + blocks_for(pad_waves + T * groups)
+    # every wave: lane u < T loads token u's ids
+    if T > 0:
+        u = np.arange(min(T, W), dtype=np.int64)
+        rep.access(tag, "topk_ids", u[:, None] * k + np.arange(k)[None, :], "load")
+    # workgroup 0
+    rep.access(tag, "topk_ids", np.arange(T * k), "load")
+    rep.access(tag, "expert_counts", np.arange(E), "store")
+    rep.access(tag, "expert_offsets", np.arange(E + 1), "store")
+    rep.access(tag, "rank_counts", np.arange(R), "store")
+    rep.access(tag, "rank_offsets", np.arange(R + 1), "store")
+    # padding waves: expert e's rows past its pairs, within the buffer
+    if pad_waves:
+        cnt = lay["expert_counts"].astype(np.int64)
+        for e in range(E):
+            lo = e * c.block + min(int(cnt[e]), c.block)
+            hi = min((e + 1) * c.block, c.cap_expert)
+            if hi > lo:
+                rep.access(tag, "expert_src_pair", [lo, hi - 1], "store")
+    # movers
+    gw = np.arange((nblocks - 1) * WPB - pad_waves, dtype=np.int64)
+    t = gw // groups
+    live = t < T
+    t, g = t[live], (gw % groups)[live]
+    if t.size == 0:
+        return
+    col = g[:, None] * W + LANE[None, :]
+    rep.access(tag, "hidden", t[:, None] * nvec + np.minimum(col, nvec - 1), "load")
+    slots = lay["token_rank_slot"].astype(np.int64)
+    pr = lay["pair_row"].astype(np.int64)
+    first = g == 0
+    tf = t[first]
+    rep.access(tag, "token_rank_slot", tf[:, None] * R + np.arange(R)[None, :], "store")
+    rep.access(tag, "pair_row", tf[:, None] * k + np.arange(k)[None, :], "store")
+    cols = np.arange(nvec, dtype=np.int64)
+    s_all = slots[:T]
+    ok_r = (s_all >= 0) & (s_all < c.cap_rank)
+    rep.access(tag, "rank_src_token", s_all[ok_r], "store")
+    rep.access(tag, "rank_buf", rows_cols(s_all[ok_r], cols, nvec), "store")
+    e = np.asarray(ids, np.int64)[:T]
+    valid = (e >= 0) & (e < E)
+    r = np.where(valid, e // m, 0)
+    copy = np.take_along_axis(s_all, r, axis=1)
+    ok_p = valid & (copy >= 0) & (copy < c.cap_rank) & (pr[:T] >= 0) & (pr[:T] < c.cap_expert)
+    rep.access(tag, "expert_src_pair", pr[:T][ok_p], "store")
+    rep.access(tag, "expert_buf", rows_cols(pr[:T][ok_p], cols, nvec), "store")
+
+
+def dispatch_one_launch(c: Case, ids: np.ndarray) -> Report:
+    """moe_dispatch's one-launch form on the oracle's layout."""
+    rep = Report()
+    lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
+    model_dispatch_small(c, lay, ids, rep)
+    return rep
+
+
 def model_combine(c: Case, lay: dict, rep: Report):
     T, k, nvec = c.T, c.k, c.nvec
     rep.buf("expert_out", c.cap_expert * nvec)

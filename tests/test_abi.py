@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 7
+    assert L.moe_abi_version() == moe.ABI_VERSION == 8
 
 
 def test_timing_hook_takes_both_events_or_neither():
@@ -114,6 +114,30 @@ def test_calls_reject_bad_arguments_without_launching():
     assert L.moe_combine_ranks(sp, ctypes.c_void_p(0x10008), FAKE, 128, FAKE, None, None,
                                None) == moe.MOE_ERR_ARG
     assert L.moe_combine_ranks(sp, FAKE, FAKE, -3, FAKE, None, None, None) == moe.MOE_ERR_ARG
+
+
+def test_dispatch_rejects_bad_arguments_without_launching():
+    """moe_dispatch checks what the three calls check before launching
+    anything, in both its forms (T <= 64 with align = 1: one launch)."""
+    L = moe.lib()
+    F = FAKE
+
+    def call(sp, hidden=F, ids=F, rc=F, ro=F, ec=F, eo=F, trs=F, pr=F, rb=F, rs=F, cr=128,
+             eb=F, es=F, ce=128, ws=None, wsb=0):
+        return L.moe_dispatch(sp, hidden, ids, rc, ro, ec, eo, trs, pr, rb, rs, cr, eb, es, ce,
+                              ws, wsb, None, None)
+
+    for s in (shape(), shape(T=4096, H=512, E=384, R=8, k=6), shape(align=16)):
+        sp = ctypes.byref(s)
+        for bad in (dict(ids=None), dict(rc=None), dict(eo=None), dict(trs=None), dict(pr=None),
+                    dict(hidden=None), dict(rb=None), dict(rs=None), dict(eb=None),
+                    dict(es=None), dict(cr=-1), dict(ce=-2), dict(hidden=ctypes.c_void_p(0x10008)),
+                    dict(ids=ctypes.c_void_p(0x10004)), dict(eb=ctypes.c_void_p(0x10002))):
+            assert call(sp, **bad) == moe.MOE_ERR_ARG, (s.T, s.align, bad)
+    assert call(ctypes.byref(shape(E=10))) == moe.MOE_ERR_ARG
+    big = ctypes.byref(shape(T=4096, H=512, E=384, R=8, k=6))
+    need = L.moe_layout_workspace_bytes(big)
+    assert call(big, ws=F, wsb=need - 4) == moe.MOE_ERR_ARG
 
 
 def test_mxfp8_calls_reject_bad_arguments():

@@ -1,0 +1,202 @@
+"""moe_dispatch, the whole dispatch in one call, against the oracle: its
+one-launch form (up to 64 tokens, unpadded runs) and the three calls it makes
+otherwise. The bar is the one of the three separate calls: bit-exact layout,
+rows, source ids and error words, canary rows past every cap untouched, and
+the combine on its pair rows bit-exact."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_ids_02_amd as moe
+import pins
+import synth
+from gpu_path import compare, run_gpu, run_oracle
+from synth import staging
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests must run on an MI355X")
+    moe.lib()
+
+
+def check(hid, ids, wts, E, R, y, what, **kw):
+    gpu = run_gpu(hid, ids, wts, E, R, y, whole_dispatch=True, **kw)
+    ref = run_oracle(hid, ids, wts, E, R, y, gpu["cap_rank"], gpu["cap_expert"],
+                     align=kw.get("align", 1), block=kw.get("block", 0))
+    compare(gpu, ref, what)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_workloads(name):
+    """decode (64 tokens) takes the one-launch form; tiny and prefill the three
+    calls."""
+    w = synth.WORKLOADS[name]
+    say(f"[dispatch] {w.describe()}")
+    ids, wts = synth.routing(w)
+    hid = synth.hidden(w)
+    y = synth.expert_out_slots(w.seed, w.E, w.H, ids)
+    check(hid, ids, wts, w.E, w.R, y, name)
+
+
+def small_case(s: int):
+    rng = np.random.default_rng(31000 + s)
+    R = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 33, 64]))
+    E = R * int(rng.integers(1, 1024 // R + 1))
+    k = int(rng.integers(1, min(16, E) + 1))
+    T = int(rng.choice([0, 1, 2, 31, 63, 64, int(rng.integers(3, 64))]))
+    H = 8 * int(rng.integers(1, 129))
+    block = int(rng.choice([0, 0, 0, 1, int(rng.integers(1, 6))]))
+    p_neg = float(rng.choice([0.0, 0.1, 0.5]))
+    p_dup = float(rng.choice([0.0, 0.15])) if k > 1 else 0.0
+    p_bad = float(rng.choice([0.0, 0.0, 0.05]))
+    ids = pins.rand_ids(rng, T, E, k, p_neg=p_neg, p_dup=p_dup, p_bad=p_bad)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(s, 0, T * H).reshape(T, H)
+    return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, wts=wts, hid=hid, rng=rng)
+
+
+SMALL = list(range(96))
+
+
+@pytest.mark.parametrize("s", SMALL)
+def test_small_batches(s):
+    """Random decode-sized shapes in the one-launch form: R up to 64, E up to
+    1024, k up to 16, masked blocks (one row, a few rows, overflowing), -1,
+    duplicate and out-of-range ids."""
+    c = small_case(s)
+    say(f"[dispatch small] s={s} T={c['T']} H={c['H']} E={c['E']} R={c['R']} k={c['k']} "
+        f"block={c['block']}")
+    y = synth.expert_out_slots(s, c["E"], c["H"], c["ids"])
+    check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small {s}", block=c["block"])
+
+
+@pytest.mark.parametrize("s", range(24))
+def test_small_batches_undersized(s):
+    """Caps below the worst case: copies and pairs past them dropped and
+    flagged exactly as the three calls do (a pair whose rank copy was dropped
+    is not written)."""
+    c = small_case(200 + s)
+    rng = c["rng"]
+    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], 1, c["block"])
+    cr = int(rng.integers(0, shape.cap_rank + 1))
+    ce = int(rng.integers(0, shape.cap_expert + 1))
+    say(f"[dispatch small caps] s={200 + s} T={c['T']} E={c['E']} R={c['R']} k={c['k']} "
+        f"block={c['block']} caps {cr}/{ce}")
+    y = synth.expert_out_slots(s, c["E"], c["H"], c["ids"])
+    check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small caps {200 + s}",
+          cap_rank=cr, cap_expert=ce, block=c["block"])
+
+
+@pytest.mark.parametrize("T,align", [(64, 16), (65, 1), (300, 1), (40, 128)])
+def test_three_call_form(T, align):
+    """Past the one-launch form (more than 64 tokens, or padded runs) the
+    three calls."""
+    rng = np.random.default_rng(T + align)
+    E, R, k, H = 64, 8, 4, 256
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(7, 0, T * H).reshape(T, H)
+    y = synth.expert_out_slots(7, E, H, ids)
+    say(f"[dispatch three calls] T={T} align={align}")
+    check(hid, ids, wts, E, R, y, f"T={T} align={align}", align=align)
+
+
+def test_one_launch_equals_three_calls():
+    """The same inputs through both forms (the testing hook switches the one
+    launch off): every output identical, repeated calls included."""
+    dev = torch.device("cuda:0")
+    for s in range(12):
+        c = small_case(500 + s)
+        T, H, E, R, k, block = c["T"], c["H"], c["E"], c["R"], c["k"], c["block"]
+        say(f"[dispatch forms] s={500 + s} T={T} E={E} R={R} k={k} block={block}")
+        hid_d = staging.rows_to_device(c["hid"], dev)
+        ids_d = torch.from_numpy(c["ids"]).to(dev)
+        res = []
+        for fused in (1, 0, 1):
+            old = moe.lib().moe_testing_set_dispatch_fused(fused)
+            try:
+                b = moe.Buffers(moe.Shape(T, H, E, R, k, 1, block), dev)
+                b.rank_buf.fill_(3)
+                b.expert_buf.fill_(3)
+                b.rank_src_token.fill_(-3)
+                b.expert_src_pair.fill_(-3)
+                moe.dispatch_all(hid_d, ids_d, E, R, b.layout_dict(), b.rank_buf,
+                                 b.rank_src_token, b.expert_buf, b.expert_src_pair,
+                                 block=block, workspace=b.workspace, err=b.err)
+                torch.cuda.synchronize()
+            finally:
+                moe.lib().moe_testing_set_dispatch_fused(old)
+            res.append({key: v.clone() for key, v in dict(
+                b.layout_dict(), rank_buf=b.rank_buf, rank_src=b.rank_src_token,
+                expert_buf=b.expert_buf, expert_src=b.expert_src_pair, err=b.err).items()})
+        for other in res[1:]:
+            for key, v in res[0].items():
+                a, w = v, other[key]
+                if a.dtype == torch.bfloat16:
+                    a, w = a.view(torch.int16), w.view(torch.int16)
+                assert torch.equal(a, w), f"s={500 + s}: {key} differs between the forms"
+
+
+def test_graph_decode_step():
+    """The decode step as two library calls (moe_dispatch, moe_combine)
+    recorded in a HIP graph: every replay equals an eager run on the same
+    fresh inputs."""
+    w = synth.WORKLOADS["decode"]
+    dev = torch.device("cuda:0")
+    shape = moe.Shape(w.T, w.H, w.E, w.R, w.k)
+    g, e = moe.Buffers(shape, dev), moe.Buffers(shape, dev)
+
+    def run(b, hid_d, ids_d, eo_d, wts_d):
+        moe.dispatch_all(hid_d, ids_d, w.E, w.R, b.layout_dict(), b.rank_buf,
+                         b.rank_src_token, b.expert_buf, b.expert_src_pair, err=b.err)
+        moe.combine(eo_d, b.pair_row, wts_d, w.E, w.R, b.out, err=b.err)
+
+    def inputs(seed):
+        rng = np.random.default_rng(seed)
+        ids = pins.rand_ids(rng, w.T, w.E, w.k, p_neg=0.05)
+        wts = rng.random((w.T, w.k)).astype(np.float32)
+        hid = synth.normal_bf16(seed, 0, w.T * w.H).reshape(w.T, w.H)
+        eo = synth.normal_bf16(seed, 1, shape.cap_expert * w.H).reshape(shape.cap_expert, w.H)
+        return hid, ids, wts, eo
+
+    hid, ids, wts, eo = inputs(40)
+    s_hid, s_ids = staging.rows_to_device(hid, dev), torch.from_numpy(ids).to(dev)
+    s_wts, s_eo = torch.from_numpy(wts).to(dev), staging.rows_to_device(eo, dev)
+    run(g, s_hid, s_ids, s_eo, s_wts)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g, s_hid, s_ids, s_eo, s_wts)
+    for i in range(4):
+        hid, ids, wts, eo = inputs(41 + i)
+        s_hid.copy_(staging.rows_to_device(hid, dev))
+        s_ids.copy_(torch.from_numpy(ids).to(dev))
+        s_wts.copy_(torch.from_numpy(wts).to(dev))
+        s_eo.copy_(staging.rows_to_device(eo, dev))
+        g.err.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        e.err.zero_()
+        run(e, staging.rows_to_device(hid, dev), torch.from_numpy(ids).to(dev),
+            staging.rows_to_device(eo, dev), torch.from_numpy(wts).to(dev))
+        torch.cuda.synchronize()
+        P = int(e.expert_offsets[-1].item())
+        C = int(e.rank_offsets[-1].item())
+        for key in ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
+                    "token_rank_slot", "pair_row", "err"):
+            assert torch.equal(getattr(g, key), getattr(e, key)), f"replay {i}: {key}"
+        assert torch.equal(g.out.view(torch.int16), e.out.view(torch.int16)), f"replay {i}: out"
+        assert torch.equal(g.rank_buf[:C].view(torch.int16), e.rank_buf[:C].view(torch.int16))
+        assert torch.equal(g.expert_buf[:P].view(torch.int16), e.expert_buf[:P].view(torch.int16))
+        assert torch.equal(g.expert_src_pair[:P], e.expert_src_pair[:P])

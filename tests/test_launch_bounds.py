@@ -107,6 +107,31 @@ def test_arbitrary_index_arrays():
                          f"{fmt} seed {12000 + s}")
 
 
+def small_batch(s: int):
+    """A random decode-sized case for moe_dispatch's one-launch form."""
+    rng = np.random.default_rng(20000 + s)
+    R = int(rng.choice([1, 2, 4, 8, 16, 33, 64]))
+    E = R * int(rng.integers(1, 1024 // R + 1))
+    k = int(rng.integers(1, min(16, E) + 1))
+    T = int(rng.choice([0, 1, 2, 63, 64, int(rng.integers(3, 63))]))
+    H = 8 * int(rng.integers(1, 1025))
+    block = int(rng.choice([0, 0, 1, int(rng.integers(1, 8))]))
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1, p_dup=0.1 if k > 1 else 0.0, p_bad=0.02)
+    return lm.Case(T, H, E, R, k, 1, block), ids, rng
+
+
+def test_dispatch_one_launch():
+    """moe_dispatch's one-launch form (T <= 64, align = 1), full and
+    undersized caps."""
+    for s in range(300):
+        c, ids, rng = small_batch(s)
+        assert_clean(lm.dispatch_one_launch(c, ids), f"small batch {s}")
+        cr = int(rng.integers(0, c.cap_rank + 1))
+        ce = int(rng.integers(0, c.cap_expert + 1))
+        c2 = lm.Case(c.T, c.H, c.E, c.R, c.k, 1, c.block, cap_rank=cr, cap_expert=ce)
+        assert_clean(lm.dispatch_one_launch(c2, ids), f"small batch {s} caps {cr}/{ce}")
+
+
 def test_model_finds_the_earlier_permute_reads():
     """The unclamped source-token load of an earlier permute reads past
     cap_rank for a grid rounded up past the last row; the model says so."""
