@@ -26,6 +26,9 @@
 //  rank_partial_rows / rank_sum_rows  the two-stage combine of [A2A] sec 7.1:
 //                one bf16 partial row per (token, rank) copy, then the sum of
 //                a token's partial rows at home in rank order
+//  dispatch_small  layout, pack and permute of a batch of at most 64 tokens
+//                in one launch (moe_dispatch): every wave finds its own
+//                token's rows from the ids ([A2A] sec 4.1, sec 8.1)
 //  pack_rows_mx  fused quantise-and-pack to the [A2A] sec 7.2 wire formats:
 //                MXFP8, MXFP4, and the 4-bit row with an E4M3 scale per 16
 //                values; permute_rows moves their codes and scales
