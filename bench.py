@@ -61,6 +61,13 @@ def algorithmic_bytes(T, H, E, R, k, C, P):
     }
 
 
+def path_bytes(nbytes: dict) -> int:
+    """Bytes of one step of the one-stage path: the four calls' algorithmic
+    bytes (other entries, such as the one-call dispatch's, are alternatives to
+    some of these calls and are not added)."""
+    return sum(nbytes[c] for c in CALLS)
+
+
 def whole_dispatch_bytes(T, H, E, R, k, C, P):
     """Bytes of moe_dispatch in its one-launch form: the layout's, each hidden
     row read once, each copy and each expert row written once with its source
@@ -765,7 +772,7 @@ def main():
         log(f"copy calibration: 3 x {args.copy_calibration} MiB")
 
     rig = Rig(w, dev, sets=args.sets)
-    step_bytes = sum(rig.nbytes.values())
+    step_bytes = path_bytes(rig.nbytes)
     stream = rig.stream
 
     log(f"warmup {args.warmup} steps")

@@ -71,6 +71,21 @@ def _counter_csv(path, counter, rows):
                         "Counter_Value": value})
 
 
+def test_step_bytes_are_the_four_calls():
+    """The bench line's bytes per step are the four calls' algorithmic bytes:
+    at the prefill shape with C = 18,016 copies and P = 24,576 pairs,
+    957,267,784 bytes (the one-call dispatch's own count, also kept by the
+    bench, is an alternative to three of them and is not added)."""
+    T, H, E, R, k, C, P = 4096, 5120, 384, 8, 6, 18016, 24576
+    nb = bench.algorithmic_bytes(T, H, E, R, k, C, P)
+    nb.update(bench.whole_dispatch_bytes(T, H, E, R, k, C, P))
+    assert bench.path_bytes(nb) == 957267784
+    # one launch: the layout's bytes, the hidden rows once, copies and expert rows once
+    row = 2 * H
+    assert nb["dispatch"] == nb["layout"] + T * row + C * row + 4 * C + P * row + 4 * P
+    assert nb["dispatch"] < nb["layout"] + nb["pack"] + nb["permute"]
+
+
 def test_counter_ingestion_and_stale_source_guard(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     mib = 512.0
