@@ -660,15 +660,15 @@ def sweep(names, dev, with_oracle: bool) -> None:
         log(f"{name}: graph replay {us_g:.1f} us per step")
         if not wire:
             us_d = rig.graph_step_us(calls=("dispatch", "combine"))
-            one = w.T <= 64 and align == 1
+            one = align == 1 and (w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8)))
             bytes_d = rig.nbytes["dispatch"] + rig.nbytes["combine"] if one else \
                 path_bytes(rig.nbytes)
             res["graph_whole_dispatch"] = {
                 "us_per_step": round(us_d, 2), "bytes": bytes_d,
                 "GB/s": round(bytes_d / (us_d * 1e-6) / 1e9, 1),
                 "one_launch": one,
-                "note": "moe_dispatch (one launch up to 64 tokens with align 1, else the three "
-                        "calls) and combine, replayed from one HIP graph"}
+                "note": "moe_dispatch (one launch for a decode-sized batch with align 1, else "
+                        "the three calls) and combine, replayed from a HIP graph"}
             log(f"{name}: graph replay with moe_dispatch {us_d:.1f} us per step")
         if with_oracle and align == 1 and block == 0 and not wire:
             log(f"{name}: oracle")

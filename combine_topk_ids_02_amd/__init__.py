@@ -329,7 +329,8 @@ def dispatch_all(hidden, topk_ids, E: int, R: int, out: dict, rank_buf, rank_src
                  expert_buf, expert_src_pair, *, align: int = 1, block: int = 0,
                  workspace: torch.Tensor | None = None, err=None) -> None:
     """moe_dispatch: layout, pack and permute in one call (one kernel launch
-    for up to 64 tokens with align = 1), into the caller's tensors: `out`
+    for up to 256 tokens with align = 1 and k in {1, 2, 4, 6, 8}, up to 64
+    for another k), into the caller's tensors: `out`
     holds the layout's outputs (the keys of layout()), rank_buf [cap_rank, H],
     rank_src_token [cap_rank], expert_buf [cap_expert, H], expert_src_pair
     [cap_expert]."""

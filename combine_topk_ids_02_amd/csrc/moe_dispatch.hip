@@ -26,7 +26,7 @@
 //  rank_partial_rows / rank_sum_rows  the two-stage combine of [A2A] sec 7.1:
 //                one bf16 partial row per (token, rank) copy, then the sum of
 //                a token's partial rows at home in rank order
-//  dispatch_small  layout, pack and permute of a batch of at most 64 tokens
+//  dispatch_small  layout, pack and permute of a batch of at most 256 tokens
 //                in one launch (moe_dispatch): every wave finds its own
 //                token's rows from the ids ([A2A] sec 4.1, sec 8.1)
 //  pack_rows_mx  fused quantise-and-pack to the [A2A] sec 7.2 wire formats:
@@ -1361,28 +1361,30 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
 
 // ---------------------------------------------------------------------------
 // The whole dispatch of a small batch in one launch (moe_dispatch with at most
-// kSmallBatch tokens and unpadded runs): layout, pack and permute with no
+// kSmallBatch tokens, 64 for a k read at run time, and unpadded runs):
+// layout, pack and permute with no
 // kernel boundary between them, for the decode step, whose time is launches
-// and the waits between them. Every mover wave holds all T*k ids (lane u the
-// ids of token u) and works out from them, with wave ballots and wave sums,
-// the rows of its own token: as a low-latency sender decides where each row
-// goes without asking anyone ([A2A] sec 4.1), here for the rank segments and
-// the expert runs alike. Workgroup 0 writes the counts and offsets; with a
-// blocked layout the next pad_waves = E waves mark one expert's padding rows
-// each (its count is a wave sum over the ids); every other wave takes one
-// (token, 1 KiB of the row), reads that part of the hidden row once and
-// writes it to the token's copy on each of its ranks and to the row of each
-// of its pairs (the pair's row is written only if its rank copy was, as the
-// three calls do). The results are those of moe_dispatch_layout,
-// moe_dispatch_pack and moe_permute_by_expert, bit for bit.
-constexpr int kSmallBatch = kWave;
+// and the waits between them. Every wave holds all T*k ids, TPL tokens per
+// lane (token u = 64q + lane in group q), and works out from them, with wave
+// ballots and wave sums, what it needs: as a low-latency sender decides where
+// each row goes without asking anyone ([A2A] sec 4.1), here for the rank
+// segments and the expert runs alike. Workgroup 0 writes the counts and
+// offsets; with a blocked layout the next pad_waves = E waves mark one
+// expert's padding rows each (its count is a wave sum over the ids); every
+// other wave takes one (token, 1 KiB of the row), reads that part of the
+// hidden row once and writes it to the token's copy on each of its ranks and
+// to the row of each of its pairs (the pair's row is written only if its rank
+// copy was, as the three calls do). The results are those of
+// moe_dispatch_layout, moe_dispatch_pack and moe_permute_by_expert, bit for
+// bit.
+constexpr int kSmallBatch = 4 * kWave;
 
 // Sum over the wave, in every lane.
 __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_inclusive_scan(x), kWave - 1);
 }
 
-template <int K, int kRB>
+template <int K, int kRB, int TPL>
 __global__ __launch_bounds__(kBlock) void dispatch_small(
     const vec4* hidden, const int32_t* __restrict__ ids, int T, int E, int R, int k, int block,
     float inv_m, int nvec, int groups, int pad_waves, int32_t* __restrict__ rank_counts,
@@ -1408,15 +1410,19 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   const int c = g * kWave + lane;
   vec4 v;
   if (!counter && !padder) v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
-  int32_t idv[KR];  // lane u: the ids of token u (-1 past T)
+  int32_t idv[TPL][KR];  // group q, lane u: the ids of token 64q + u (-1 past T)
+  RankSet<kRB> set[TPL];  // and its ranks
 #pragma unroll
-  for (int j = 0; j < KR; ++j) idv[j] = (j < kk && lane < T) ? ids[lane * kk + j] : -1;
-  RankSet<kRB> set;  // lane u: the ranks of token u
+  for (int q = 0; q < TPL; ++q) {
+    const int u = q * kWave + lane;
 #pragma unroll
-  for (int j = 0; j < KR; ++j) {
-    if (j < kk) {
-      const bool valid = uint32_t(idv[j]) < uint32_t(E);
-      set.add(rank_of(valid ? idv[j] : 0, inv_m), valid);
+    for (int j = 0; j < KR; ++j) idv[q][j] = (j < kk && u < T) ? ids[u * kk + j] : -1;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      if (j < kk) {
+        const bool valid = uint32_t(idv[q][j]) < uint32_t(E);
+        set[q].add(rank_of(valid ? idv[q][j] : 0, inv_m), valid);
+      }
     }
   }
 
@@ -1456,12 +1462,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
       base += block > 0 ? block : s_hist[e];
     }
     if (tid == 0) expert_offsets[E] = total;
-    // Copies per rank (wave 0, lane u = token u: one ballot per rank) and
+    // Copies per rank (wave 0: one ballot per rank and token group) and
     // their offsets.
     if (wave == 0) {
       int mine = 0;
       for (int r = 0; r < R; ++r) {
-        const int n = __popcll(__ballot(set.has(r)));
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < TPL; ++q) n += __popcll(__ballot(set[q].has(r)));
         mine = lane == r ? n : mine;
       }
       const int rinc = wave_inclusive_scan(mine);
@@ -1480,8 +1488,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     const int e = int(gw);
     int n = 0;
 #pragma unroll
-    for (int j = 0; j < KR; ++j)
-      if (j < kk) n += idv[j] == e ? 1 : 0;
+    for (int q = 0; q < TPL; ++q)
+#pragma unroll
+      for (int j = 0; j < KR; ++j)
+        if (j < kk) n += idv[q][j] == e ? 1 : 0;
     const int filled = min(wave_sum(n), block);
     const int64_t end = min((int64_t)(e + 1) * block, cap_expert);
     for (int64_t row = (int64_t)e * block + filled + lane; row < end; row += kWave)
@@ -1490,16 +1500,25 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   }
 
   // The token's copies: ranks in order, its slot on rank r kept in lane r.
-  const uint64_t below = t == 0 ? 0ull : (~0ull >> (kWave - t));  // lanes (tokens) before t
+  const int qt = t / kWave, lt = t - qt * kWave;  // token t is lane lt of group qt
+  const uint64_t below = lt == 0 ? 0ull : (~0ull >> (kWave - lt));  // lanes before lt
   int off = 0, my_slot = -1;
   for (int r = 0; r < R; ++r) {
-    const uint64_t b = __ballot(set.has(r));
-    if ((b >> t) & 1) {
-      const int s = off + __popcll(b & below);
+    int n = 0, before = 0;
+    bool mine = false;
+#pragma unroll
+    for (int q = 0; q < TPL; ++q) {
+      const uint64_t b = __ballot(set[q].has(r));
+      n += __popcll(b);
+      before += q < qt ? __popcll(b) : (q == qt ? __popcll(b & below) : 0);
+      mine = q == qt ? ((b >> lt) & 1) != 0 : mine;
+    }
+    if (mine) {
+      const int s = off + before;
       if (lane == r) my_slot = s;
       if (s < cap_rank && c < nvec) store_row<true>(rank_buf + (int64_t)s * nvec + c, v);
     }
-    off += __popcll(b);
+    off += n;
   }
   if (g == 0) {
     if (lane < R) token_rank_slot[(int64_t)t * R + lane] = my_slot;
@@ -1515,16 +1534,22 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   int my_row = -1;  // lane j: pair_row of slot j
 #pragma unroll
   for (int j = 0; j < KR; ++j) {
-    if (j >= kk) break;
-    const int e = __builtin_amdgcn_readlane(idv[j], t);
-    if (uint32_t(e) >= uint32_t(E)) continue;
+    int e = -1;
+#pragma unroll
+    for (int q = 0; q < TPL; ++q)
+      if (q == qt) e = __builtin_amdgcn_readlane(idv[q][j], lt);
+    if (j >= kk || uint32_t(e) >= uint32_t(E)) continue;  // (no break: keeps the loop unrolled)
     int n = 0;
 #pragma unroll
-    for (int jj = 0; jj < KR; ++jj) {
-      if (jj < kk) {
-        const int x = idv[jj];
-        n += uint32_t(x) < uint32_t(e) ? 1 : 0;
-        n += (x == e && (lane < t || (lane == t && jj < j))) ? (1 << 16) : 0;
+    for (int q = 0; q < TPL; ++q) {
+      const int u = q * kWave + lane;
+#pragma unroll
+      for (int jj = 0; jj < KR; ++jj) {
+        if (jj < kk) {
+          const int x = idv[q][jj];
+          n += uint32_t(x) < uint32_t(e) ? 1 : 0;
+          n += (x == e && (u < t || (u == t && jj < j))) ? (1 << 16) : 0;
+        }
       }
     }
     const int sum = wave_sum(n);
@@ -2008,11 +2033,20 @@ void launch_dispatch_small_kw(const moe_shape_t& sh, hipStream_t st, const Dispa
   const int groups = (nvec + kWave - 1) / kWave;
   const int pad_waves = sh.block > 0 && a.cap_expert > 0 ? sh.E : 0;
   const int grid = 1 + blocks_for(pad_waves + int64_t(sh.T) * groups);
-  MOE_LAUNCH((dispatch_small<K, kRB>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids, sh.T,
-             sh.E, sh.R, sh.k, sh.block, float(1.0 / double(sh.E / sh.R)), nvec, groups,
-             pad_waves, a.rc,
-             a.ro, a.ec, a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
-             a.expert_src, a.cap_expert, a.err);
+  const float inv_m = float(1.0 / double(sh.E / sh.R));
+  // one token per lane up to 64 tokens, else four (only for a k known at
+  // compile time: with k read at run time the four groups' ids do not stay in
+  // registers; moe_dispatch makes the three calls then)
+  if (K == 0 || sh.T <= kWave)
+    MOE_LAUNCH((dispatch_small<K, kRB, 1>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids,
+               sh.T, sh.E, sh.R, sh.k, sh.block, inv_m, nvec, groups, pad_waves, a.rc, a.ro, a.ec,
+               a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
+               a.expert_src, a.cap_expert, a.err);
+  else
+    MOE_LAUNCH((dispatch_small<K, kRB, K == 0 ? 1 : 4>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids,
+               sh.T, sh.E, sh.R, sh.k, sh.block, inv_m, nvec, groups, pad_waves, a.rc, a.ro, a.ec,
+               a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
+               a.expert_src, a.cap_expert, a.err);
 }
 
 template <int K>
@@ -2280,7 +2314,11 @@ int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t
     if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
     if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
   }
-  if (g_dispatch_fused && sh.T <= kSmallBatch && sh.align == 1) {
+  // the one-launch form: up to 64 tokens, or up to 256 with a k the kernels
+  // are compiled for, and unpadded runs
+  const bool compiled_k = sh.k == 1 || sh.k == 2 || sh.k == 4 || sh.k == 6 || sh.k == 8;
+  if (g_dispatch_fused && sh.align == 1 &&
+      (sh.T <= kWave || (sh.T <= kSmallBatch && compiled_k))) {
     DispatchSmallArgs a{reinterpret_cast<const vec4*>(hidden), topk_ids, rank_counts,
                         rank_offsets, expert_counts, expert_offsets, token_rank_slot, pair_row,
                         reinterpret_cast<vec4*>(rank_buf), rank_src_token, cap_rank,

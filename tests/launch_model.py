@@ -493,11 +493,11 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
             rep.access(tag, "expert_scale", rows_cols(p[ok], s1, nvec_s), "store")
 
 
-SMALL_BATCH = 64
+SMALL_BATCH = 256
 
 
 def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
-    """dispatch_small (moe_dispatch's one-launch form, T <= 64, align = 1):
+    """dispatch_small (moe_dispatch's one-launch form, T <= 256, align = 1):
     workgroup 0 writes the counts and offsets; with a blocked layout one wave
     per expert marks its padding rows; one wave per (token, group of 64 vec4)
     moves that part of the row. The rows and slots
@@ -515,9 +515,9 @@ def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
     groups = cdiv(nvec, W)
     pad_waves = E if c.block > 0 and c.cap_expert > 0 else 0
     nblocks = 1 + blocks_for(pad_waves + T * groups)
-    # every wave: lane u < T loads token u's ids
+    # every wave: lane u of group q loads the ids of token 64q + u (< T)
     if T > 0:
-        u = np.arange(min(T, W), dtype=np.int64)
+        u = np.arange(T, dtype=np.int64)
         rep.access(tag, "topk_ids", u[:, None] * k + np.arange(k)[None, :], "load")
     # workgroup 0
     rep.access(tag, "topk_ids", np.arange(T * k), "load")

@@ -1,6 +1,7 @@
 """moe_dispatch, the whole dispatch in one call, against the oracle: its
-one-launch form (up to 64 tokens, unpadded runs) and the three calls it makes
-otherwise. The bar is the one of the three separate calls: bit-exact layout,
+one-launch form (unpadded runs; up to 256 tokens with k in 1, 2, 4, 6, 8, up
+to 64 with another k; one or four tokens per lane) and the three calls it
+makes otherwise. The bar is the one of the three separate calls: bit-exact layout,
 rows, source ids and error words, canary rows past every cap untouched, and
 the combine on its pair rows bit-exact."""
 import sys
@@ -39,8 +40,8 @@ def check(hid, ids, wts, E, R, y, what, **kw):
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
 def test_workloads(name):
-    """decode (64 tokens) takes the one-launch form; tiny and prefill the three
-    calls."""
+    """decode (64 tokens) and tiny (256 tokens, k = 2) take the one-launch
+    form, prefill the three calls."""
     w = synth.WORKLOADS[name]
     say(f"[dispatch] {w.describe()}")
     ids, wts = synth.routing(w)
@@ -50,11 +51,17 @@ def test_workloads(name):
 
 
 def small_case(s: int):
+    """A random decode-sized case: T up to 256 (above 64 mostly with a k the
+    four-token form is compiled for)."""
     rng = np.random.default_rng(31000 + s)
     R = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 33, 64]))
     E = R * int(rng.integers(1, 1024 // R + 1))
-    k = int(rng.integers(1, min(16, E) + 1))
-    T = int(rng.choice([0, 1, 2, 31, 63, 64, int(rng.integers(3, 64))]))
+    T = int(rng.choice([0, 1, 2, 31, 63, 64, int(rng.integers(3, 64)), 65, 127, 128, 200, 255,
+                        256, int(rng.integers(65, 257))]))
+    if T > 64 and rng.random() < 0.85:
+        k = int(rng.choice([c for c in (1, 2, 4, 6, 8) if c <= E]))
+    else:
+        k = int(rng.integers(1, min(16, E) + 1))
     H = 8 * int(rng.integers(1, 129))
     block = int(rng.choice([0, 0, 0, 1, int(rng.integers(1, 6))]))
     p_neg = float(rng.choice([0.0, 0.1, 0.5]))
@@ -66,14 +73,14 @@ def small_case(s: int):
     return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, wts=wts, hid=hid, rng=rng)
 
 
-SMALL = list(range(96))
+SMALL = list(range(128))
 
 
 @pytest.mark.parametrize("s", SMALL)
 def test_small_batches(s):
-    """Random decode-sized shapes in the one-launch form: R up to 64, E up to
-    1024, k up to 16, masked blocks (one row, a few rows, overflowing), -1,
-    duplicate and out-of-range ids."""
+    """Random decode-sized shapes (T up to 256) in the one-launch form: R up
+    to 64, E up to 1024, k up to 16, masked blocks (one row, a few rows,
+    overflowing), -1, duplicate and out-of-range ids."""
     c = small_case(s)
     say(f"[dispatch small] s={s} T={c['T']} H={c['H']} E={c['E']} R={c['R']} k={c['k']} "
         f"block={c['block']}")
@@ -98,18 +105,19 @@ def test_small_batches_undersized(s):
           cap_rank=cr, cap_expert=ce, block=c["block"])
 
 
-@pytest.mark.parametrize("T,align", [(64, 16), (65, 1), (300, 1), (40, 128)])
-def test_three_call_form(T, align):
-    """Past the one-launch form (more than 64 tokens, or padded runs) the
-    three calls."""
+@pytest.mark.parametrize("T,k,align", [(64, 4, 16), (257, 4, 1), (300, 2, 1), (65, 3, 1),
+                                        (40, 4, 128)])
+def test_three_call_form(T, k, align):
+    """Past the one-launch form (more than 256 tokens, more than 64 with
+    another k, or padded runs) the three calls."""
     rng = np.random.default_rng(T + align)
-    E, R, k, H = 64, 8, 4, 256
+    E, R, H = 64, 8, 256
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
     wts = rng.random((T, k)).astype(np.float32)
     hid = synth.normal_bf16(7, 0, T * H).reshape(T, H)
     y = synth.expert_out_slots(7, E, H, ids)
-    say(f"[dispatch three calls] T={T} align={align}")
-    check(hid, ids, wts, E, R, y, f"T={T} align={align}", align=align)
+    say(f"[dispatch three calls] T={T} k={k} align={align}")
+    check(hid, ids, wts, E, R, y, f"T={T} k={k} align={align}", align=align)
 
 
 def test_one_launch_equals_three_calls():

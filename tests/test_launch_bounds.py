@@ -113,7 +113,8 @@ def small_batch(s: int):
     R = int(rng.choice([1, 2, 4, 8, 16, 33, 64]))
     E = R * int(rng.integers(1, 1024 // R + 1))
     k = int(rng.integers(1, min(16, E) + 1))
-    T = int(rng.choice([0, 1, 2, 63, 64, int(rng.integers(3, 63))]))
+    T = int(rng.choice([0, 1, 2, 63, 64, int(rng.integers(3, 63)), 65, 256,
+                        int(rng.integers(65, 257))]))
     H = 8 * int(rng.integers(1, 1025))
     block = int(rng.choice([0, 0, 1, int(rng.integers(1, 8))]))
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1, p_dup=0.1 if k > 1 else 0.0, p_bad=0.02)
@@ -121,7 +122,7 @@ def small_batch(s: int):
 
 
 def test_dispatch_one_launch():
-    """moe_dispatch's one-launch form (T <= 64, align = 1), full and
+    """moe_dispatch's one-launch form (T <= 256, align = 1), full and
     undersized caps."""
     for s in range(300):
         c, ids, rng = small_batch(s)
