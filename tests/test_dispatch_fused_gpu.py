@@ -73,7 +73,7 @@ def small_case(s: int):
     return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, wts=wts, hid=hid, rng=rng)
 
 
-SMALL = list(range(128))
+SMALL = list(range(384))
 
 
 @pytest.mark.parametrize("s", SMALL)
@@ -88,7 +88,7 @@ def test_small_batches(s):
     check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small {s}", block=c["block"])
 
 
-@pytest.mark.parametrize("s", range(24))
+@pytest.mark.parametrize("s", range(64))
 def test_small_batches_undersized(s):
     """Caps below the worst case: copies and pairs past them dropped and
     flagged exactly as the three calls do (a pair whose rank copy was dropped
