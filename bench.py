@@ -68,14 +68,19 @@ def path_bytes(nbytes: dict) -> int:
     return sum(nbytes[c] for c in CALLS)
 
 
-def whole_dispatch_bytes(T, H, E, R, k, C, P):
-    """Bytes of moe_dispatch in its one-launch form: the layout's, each hidden
-    row read once, each copy and each expert row written once with its source
-    id (the packed rows are not read back, so this is less than the three
-    calls' sum and is reported on its own)."""
-    row = 2 * H
-    return {"dispatch": algorithmic_bytes(T, H, E, R, k, C, P)["layout"] + T * row
-            + C * row + 4 * C + P * row + 4 * P}
+def whole_dispatch_bytes(T, H, E, R, k, C, P, fmt=None):
+    """Bytes of moe_dispatch (or with fmt moe_dispatch_quantised) in its
+    one-launch form: the layout's, each bf16 hidden row read once, each copy
+    and each expert row written once (bf16, or codes and scales) with its
+    source id (the packed rows are not read back, so this is less than the
+    three calls' sum and is reported on its own)."""
+    if fmt:
+        bits, blk = WIRE[fmt]
+        out_row = H * bits // 8 + H // blk
+    else:
+        out_row = 2 * H
+    return {"dispatch": algorithmic_bytes(T, H, E, R, k, C, P)["layout"] + T * 2 * H
+            + C * out_row + 4 * C + P * out_row + 4 * P}
 
 
 # Quantised wire formats: name -> (code bits per value, values per scale byte).
@@ -362,7 +367,8 @@ class Rig:
         if two_stage:
             self.nbytes.update(two_stage_bytes(w.T, w.H, w.R, w.k, self.C, self.P))
             self.calls = CALLS + TWO_STAGE_CALLS
-        self.nbytes.update(whole_dispatch_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P))
+        self.nbytes.update(whole_dispatch_bytes(w.T, w.H, w.E, w.R, w.k, self.C, self.P,
+                                                self.wire))
 
     def _make_set(self, y_d):
         import types
@@ -437,6 +443,11 @@ class Rig:
                         s.E, b.expert_buf, b.expert_src_pair, expert_counts=b.expert_counts,
                         expert_offsets=b.expert_offsets, align=s.align, block=s.block,
                         err=b.err)
+        elif name == "dispatch" and self.mx_bits:
+            moe.dispatch_all_mx(self.wire, x.hid_d, x.ids_d, s.E, s.R, b.layout_dict(),
+                                x.rank_q, x.rank_s, b.rank_src_token, x.exp_q, x.exp_s,
+                                b.expert_src_pair, align=s.align, block=s.block,
+                                workspace=b.workspace, err=b.err)
         elif name == "dispatch":
             moe.dispatch_all(x.hid_d, x.ids_d, s.E, s.R, b.layout_dict(), b.rank_buf,
                              b.rank_src_token, b.expert_buf, b.expert_src_pair,
@@ -658,18 +669,18 @@ def sweep(names, dev, with_oracle: bool) -> None:
         res["graph"] = {"us_per_step": round(us_g, 2),
                         "note": "layout, pack, permute, combine replayed from one HIP graph"}
         log(f"{name}: graph replay {us_g:.1f} us per step")
-        if not wire:
-            us_d = rig.graph_step_us(calls=("dispatch", "combine"))
-            one = align == 1 and (w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8)))
-            bytes_d = rig.nbytes["dispatch"] + rig.nbytes["combine"] if one else \
-                path_bytes(rig.nbytes)
-            res["graph_whole_dispatch"] = {
-                "us_per_step": round(us_d, 2), "bytes": bytes_d,
-                "GB/s": round(bytes_d / (us_d * 1e-6) / 1e9, 1),
-                "one_launch": one,
-                "note": "moe_dispatch (one launch for a decode-sized batch with align 1, else "
-                        "the three calls) and combine, replayed from a HIP graph"}
-            log(f"{name}: graph replay with moe_dispatch {us_d:.1f} us per step")
+        us_d = rig.graph_step_us(calls=("dispatch", "combine"))
+        one = align == 1 and (w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8)))
+        bytes_d = rig.nbytes["dispatch"] + rig.nbytes["combine"] if one else \
+            path_bytes(rig.nbytes)
+        res["graph_whole_dispatch"] = {
+            "us_per_step": round(us_d, 2), "bytes": bytes_d,
+            "GB/s": round(bytes_d / (us_d * 1e-6) / 1e9, 1),
+            "one_launch": one,
+            "note": ("moe_dispatch_quantised" if wire else "moe_dispatch") +
+                    " (one launch for a decode-sized batch with align 1, else the three "
+                    "calls) and combine, replayed from a HIP graph"}
+        log(f"{name}: graph replay with the one-call dispatch {us_d:.1f} us per step")
         if with_oracle and align == 1 and block == 0 and not wire:
             log(f"{name}: oracle")
             res["oracle"] = oracle_median(w, rig.hid, rig.ids, rig.wts, rig.y,
@@ -723,8 +734,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
                     const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
-                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,adv:mxfp4,"
-                          "prefill:nvfp4,adv:nvfp4",
+                          "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,decode:mxfp4,"
+                          "adv:mxfp4,prefill:nvfp4,decode:nvfp4,adv:nvfp4",
                     default=None,
                     metavar="WORKLOADS", help="per-call warm/rotated/cold table over workloads")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="MIB",

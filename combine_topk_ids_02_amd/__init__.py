@@ -31,14 +31,16 @@ EXPORTS = ("moe_abi_version", "moe_status_string", "moe_dispatch_layout",
            "moe_combine_ranks", "moe_dispatch_pack_mxfp8", "moe_permute_by_expert_mxfp8",
            "moe_dispatch_pack_mxfp4", "moe_permute_by_expert_mxfp4",
            "moe_dispatch_pack_nvfp4", "moe_permute_by_expert_nvfp4",
-           "moe_dispatch", "moe_testing_set_layout_form", "moe_testing_set_layout_match",
+           "moe_dispatch", "moe_dispatch_quantised", "moe_testing_set_layout_form",
+           "moe_testing_set_layout_match",
            "moe_testing_set_dispatch_fused", "moe_testing_time_next_launch")
 
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 # Quantised wire formats: name -> (code bits per value, values per scale byte).
 WIRE_FORMATS = {"mxfp8": (8, 32), "mxfp4": (4, 32), "nvfp4": (4, 16)}
+WIRE_CODES = {"mxfp8": 1, "mxfp4": 2, "nvfp4": 3}  # moe_dispatch_quantised's format
 
 
 class MoeShape(ctypes.Structure):
@@ -108,6 +110,10 @@ def lib():
     L.moe_dispatch.restype = ctypes.c_int
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64,
                                vp, ctypes.c_size_t, vp, vp]
+    L.moe_dispatch_quantised.restype = ctypes.c_int
+    L.moe_dispatch_quantised.argtypes = [shp, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, i64, vp, vp, vp, i64, vp, ctypes.c_size_t, vp,
+                                         vp]
     L.moe_testing_set_dispatch_fused.restype = ctypes.c_int
     L.moe_testing_set_dispatch_fused.argtypes = [ctypes.c_int]
     L.moe_testing_set_layout_form.restype = ctypes.c_int
@@ -394,6 +400,44 @@ def pack_mx(fmt, hidden: torch.Tensor, token_rank_slot: torch.Tensor, E: int, k:
             _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
             rank_q.shape[0], _err(err), _stream(hidden.device))
     _check(st, f"moe_dispatch_pack_{name}")
+
+
+def dispatch_all_mx(fmt, hidden, topk_ids, E: int, R: int, out: dict, rank_q, rank_scale,
+                    rank_src_token, expert_q, expert_scale, expert_src_pair, *, align: int = 1,
+                    block: int = 0, workspace: torch.Tensor | None = None, err=None) -> None:
+    """moe_dispatch_quantised: layout, quantise-and-pack and permute of the
+    quantised rows in one call (one kernel launch for a decode-sized batch, as
+    dispatch_all), into the caller's tensors: `out` holds the layout's outputs,
+    rank_q [cap_rank, H*bits/8] and rank_scale [cap_rank, H/block] (uint8),
+    rank_src_token [cap_rank], expert_q / expert_scale / expert_src_pair
+    likewise with cap_expert rows."""
+    name, bits, blk = _wire(fmt)
+    _check_err(err)
+    T, k = topk_ids.shape
+    H = hidden.shape[1]
+    _need(hidden, "hidden", (T, H))
+    for key, want in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
+                      ("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                      ("token_rank_slot", (T, R)), ("pair_row", (T, k))):
+        _need(out[key], key, want)
+        _i32(out[key])
+    cap_r = _rows(rank_q, "rank_q", H * bits // 8)
+    _need(rank_scale, "rank_scale", (cap_r, H // blk))
+    _need(rank_src_token, "rank_src_token", min_numel=cap_r)
+    cap_e = _rows(expert_q, "expert_q", H * bits // 8)
+    _need(expert_scale, "expert_scale", (cap_e, H // blk))
+    _need(expert_src_pair, "expert_src_pair", min_numel=cap_e)
+    shape = Shape(T, H, E, R, k, align, block)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().moe_dispatch_quantised(
+        ctypes.byref(shape.c()), WIRE_CODES[name], _ptr(_rows16(hidden)), _ptr(_i32(topk_ids)),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["expert_counts"]),
+        _ptr(out["expert_offsets"]), _ptr(out["token_rank_slot"]), _ptr(out["pair_row"]),
+        _ptr(_bytes(rank_q)), _ptr(_bytes(rank_scale)), _ptr(_i32(rank_src_token)),
+        rank_q.shape[0], _ptr(_bytes(expert_q)), _ptr(_bytes(expert_scale)),
+        _ptr(_i32(expert_src_pair)), expert_q.shape[0], _ptr(workspace), ws_bytes, _err(err),
+        _stream(hidden.device))
+    _check(st, "moe_dispatch_quantised")
 
 
 def pack_mxfp8(*args, **kw) -> None:

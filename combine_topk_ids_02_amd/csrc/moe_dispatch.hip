@@ -1384,15 +1384,94 @@ __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_inclusive_scan(x), kWave - 1);
 }
 
+// Row formats of the one-launch dispatch: bf16 rows, or a wire format of
+// pack_rows_mx (codes in one buffer, scale bytes in another).
+enum : int { kWireBf16 = 0, kWireMxfp8 = 1, kWireMxfp4 = 2, kWireNvfp4 = 3 };
+
+// One lane's vec4 (8 consecutive values, column c of the row) in a wire
+// format, by the rules of pack_rows_mx: `code` gets its 8 (MXFP8) or 4 code
+// bytes; a scale block is 4 lanes (32 values; 2 lanes, 16 values, for the
+// 16-value 4-bit row), and the first lane of every four blocks gets their
+// four scale bytes in `sw`. All lanes of the wave call it together (lane
+// shuffles).
+__device__ __forceinline__ void quantise_lane(int fmt, vec4 v, uint2& code, uint32_t& sw) {
+  const int lpb = fmt == kWireNvfp4 ? 2 : 4;
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = max(amax, v[j] & 0x7FFFu);
+    amax = max(amax, (v[j] >> 16) & 0x7FFFu);
+  }
+  amax = max(amax, uint32_t(__shfl_xor(int(amax), 1, kWave)));
+  if (lpb == 4) amax = max(amax, uint32_t(__shfl_xor(int(amax), 2, kWave)));
+  uint32_t sb;
+  code = uint2{0u, 0u};
+  if (amax >= 0x7F80u) {  // NaN or infinity in the block: NaN scale, marked codes
+    sb = fmt == kWireNvfp4 ? 0x7Fu : 0xFFu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (fmt == kWireMxfp8) {  // e4m3 NaN with the value's sign
+        const uint32_t two = (((v[j] >> 8) & 0x80u) | 0x7Fu) | ((((v[j] >> 24) & 0x80u) | 0x7Fu) << 8);
+        if (j < 2)
+          code.x |= two << (16 * j);
+        else
+          code.y |= two << (16 * (j - 2));
+      } else {  // the largest e2m1 code with the value's sign
+        code.x |= ((((v[j] >> 12) & 0x8u) | 0x7u) | ((((v[j] >> 28) & 0x8u) | 0x7u) << 4)) << (8 * j);
+      }
+    }
+  } else if (fmt == kWireNvfp4) {
+    sb = e4m3_code(__uint_as_float(amax << 16) / 6.0f);
+    code.x = e2m1x8_e4m3(v, e4m3_value(sb));
+  } else {
+    const int e = mx_block_exponent(amax, fmt == kWireMxfp8 ? 8 : 2);
+    const float scale = __uint_as_float(uint32_t(e + 127) << 23);  // E8M0 byte as an exponent
+    sb = uint32_t(e + 127);
+    if (fmt == kWireMxfp8) {
+      code.x = e4m3x4(v[0], v[1], scale);
+      code.y = e4m3x4(v[2], v[3], scale);
+    } else {
+      code.x = e2m1x8(v, scale);
+    }
+  }
+  const int lane = lane_id();
+  sw = sb | (uint32_t(__shfl(int(sb), lane + lpb, kWave)) << 8) |
+       (uint32_t(__shfl(int(sb), lane + 2 * lpb, kWave)) << 16) |
+       (uint32_t(__shfl(int(sb), lane + 3 * lpb, kWave)) << 24);
+}
+
+// Stores a wave's part of a row (column c of `nvec`, lane-wise) into row
+// `row` of a row buffer in format fmt: the bf16 vec4 v, or its codes and (in
+// the first lane of every four scale blocks) the four scale bytes.
+__device__ __forceinline__ void store_part(int fmt, void* rows, uint8_t* scales, int64_t row,
+                                           int c, int nvec, vec4 v, uint2 code, uint32_t sw) {
+  if (fmt == kWireBf16) {
+    if (c < nvec) store_row<true>(static_cast<vec4*>(rows) + row * nvec + c, v);
+    return;
+  }
+  // quantised rows: nvec is a multiple of 64, so every lane has a column
+  const int lane = lane_id();
+  uint8_t* q = static_cast<uint8_t*>(rows);
+  if (fmt == kWireMxfp8) {
+    *reinterpret_cast<uint2*>(q + row * (int64_t(nvec) * 8) + int64_t(c) * 8) = code;
+  } else {
+    *reinterpret_cast<uint32_t*>(q + row * (int64_t(nvec) * 4) + int64_t(c) * 4) = code.x;
+  }
+  const int lpb = fmt == kWireNvfp4 ? 2 : 4;
+  if (lane % (4 * lpb) == 0)
+    *reinterpret_cast<uint32_t*>(scales + row * (nvec / lpb) + c / lpb) = sw;
+}
+
 template <int K, int kRB, int TPL>
 __global__ __launch_bounds__(kBlock) void dispatch_small(
     const vec4* hidden, const int32_t* __restrict__ ids, int T, int E, int R, int k, int block,
     float inv_m, int nvec, int groups, int pad_waves, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
-    int32_t* __restrict__ pair_row, vec4* rank_buf, int32_t* __restrict__ rank_src_token,
-    int64_t cap_rank, vec4* expert_buf, int32_t* __restrict__ expert_src_pair,
-    int64_t cap_expert, int32_t* err_word) {
+    int32_t* __restrict__ pair_row, int fmt, void* rank_buf, uint8_t* rank_scale,
+    int32_t* __restrict__ rank_src_token, int64_t cap_rank, void* expert_buf,
+    uint8_t* expert_scale, int32_t* __restrict__ expert_src_pair, int64_t cap_expert,
+    int32_t* err_word) {
   constexpr int KR = K > 0 ? K : kMaxK;
   const int kk = K > 0 ? K : k;
   const int lane = lane_id();
@@ -1499,6 +1578,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     return;
   }
 
+  // A quantised format: the part's codes and scales, once for all its rows.
+  uint2 code = uint2{0u, 0u};
+  uint32_t sw = 0;
+  if (fmt != kWireBf16) quantise_lane(fmt, v, code, sw);
+
   // The token's copies: ranks in order, its slot on rank r kept in lane r.
   const int qt = t / kWave, lt = t - qt * kWave;  // token t is lane lt of group qt
   const uint64_t below = lt == 0 ? 0ull : (~0ull >> (kWave - lt));  // lanes before lt
@@ -1516,7 +1600,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     if (mine) {
       const int s = off + before;
       if (lane == r) my_slot = s;
-      if (s < cap_rank && c < nvec) store_row<true>(rank_buf + (int64_t)s * nvec + c, v);
+      if (s < cap_rank) store_part(fmt, rank_buf, rank_scale, s, c, nvec, v, code, sw);
     }
     off += n;
   }
@@ -1563,7 +1647,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     const int s = __builtin_amdgcn_readlane(my_slot, rank_of(e, inv_m));  // the copy it comes from
     if (s < cap_rank) {
       if (p >= 0 && p < cap_expert) {
-        if (c < nvec) store_row<true>(expert_buf + (int64_t)p * nvec + c, v);
+        store_part(fmt, expert_buf, expert_scale, p, c, nvec, v, code, sw);
         if (g == 0 && lane == 0) expert_src_pair[p] = t * kk + j;
       } else if (g == 0 && lane == 0) {
         flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
@@ -2018,10 +2102,13 @@ struct DispatchSmallArgs {
   const vec4* hidden;
   const int32_t* ids;
   int32_t *rc, *ro, *ec, *eo, *trs, *pr;
-  vec4* rank_buf;
+  int fmt;  // kWireBf16, or a wire format (rows of codes, scales beside them)
+  void* rank_buf;
+  uint8_t* rank_scale;
   int32_t* rank_src;
   int64_t cap_rank;
-  vec4* expert_buf;
+  void* expert_buf;
+  uint8_t* expert_scale;
   int32_t* expert_src;
   int64_t cap_expert;
   int32_t* err;
@@ -2040,13 +2127,13 @@ void launch_dispatch_small_kw(const moe_shape_t& sh, hipStream_t st, const Dispa
   if (K == 0 || sh.T <= kWave)
     MOE_LAUNCH((dispatch_small<K, kRB, 1>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids,
                sh.T, sh.E, sh.R, sh.k, sh.block, inv_m, nvec, groups, pad_waves, a.rc, a.ro, a.ec,
-               a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
-               a.expert_src, a.cap_expert, a.err);
+               a.eo, a.trs, a.pr, a.fmt, a.rank_buf, a.rank_scale, a.rank_src, a.cap_rank,
+               a.expert_buf, a.expert_scale, a.expert_src, a.cap_expert, a.err);
   else
     MOE_LAUNCH((dispatch_small<K, kRB, K == 0 ? 1 : 4>), dim3(grid), dim3(kBlock), 0, st, a.hidden, a.ids,
                sh.T, sh.E, sh.R, sh.k, sh.block, inv_m, nvec, groups, pad_waves, a.rc, a.ro, a.ec,
-               a.eo, a.trs, a.pr, a.rank_buf, a.rank_src, a.cap_rank, a.expert_buf,
-               a.expert_src, a.cap_expert, a.err);
+               a.eo, a.trs, a.pr, a.fmt, a.rank_buf, a.rank_scale, a.rank_src, a.cap_rank,
+               a.expert_buf, a.expert_scale, a.expert_src, a.cap_expert, a.err);
 }
 
 template <int K>
@@ -2057,6 +2144,14 @@ void launch_dispatch_small_k(const moe_shape_t& sh, hipStream_t st, const Dispat
     launch_dispatch_small_kw<K, 32>(sh, st, a);
   else
     launch_dispatch_small_kw<K, 8>(sh, st, a);
+}
+
+// Whether moe_dispatch runs as one launch: up to 64 tokens, or up to 256 with
+// a k the kernels are compiled for, and unpadded runs.
+bool dispatch_one_launch(const moe_shape_t& sh) {
+  const bool compiled_k = sh.k == 1 || sh.k == 2 || sh.k == 4 || sh.k == 6 || sh.k == 8;
+  return g_dispatch_fused && sh.align == 1 &&
+         (sh.T <= kWave || (sh.T <= kSmallBatch && compiled_k));
 }
 
 void launch_dispatch_small(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {
@@ -2314,16 +2409,11 @@ int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t
     if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
     if (!aligned16(rank_buf) || !aligned16(expert_buf)) return MOE_ERR_ARG;
   }
-  // the one-launch form: up to 64 tokens, or up to 256 with a k the kernels
-  // are compiled for, and unpadded runs
-  const bool compiled_k = sh.k == 1 || sh.k == 2 || sh.k == 4 || sh.k == 6 || sh.k == 8;
-  if (g_dispatch_fused && sh.align == 1 &&
-      (sh.T <= kWave || (sh.T <= kSmallBatch && compiled_k))) {
+  if (dispatch_one_launch(sh)) {
     DispatchSmallArgs a{reinterpret_cast<const vec4*>(hidden), topk_ids, rank_counts,
                         rank_offsets, expert_counts, expert_offsets, token_rank_slot, pair_row,
-                        reinterpret_cast<vec4*>(rank_buf), rank_src_token, cap_rank,
-                        reinterpret_cast<vec4*>(expert_buf), expert_src_pair, cap_expert,
-                        err_word};
+                        kWireBf16, rank_buf, nullptr, rank_src_token, cap_rank, expert_buf,
+                        nullptr, expert_src_pair, cap_expert, err_word};
     launch_dispatch_small(sh, static_cast<hipStream_t>(stream), a);
     return launch_status();
   }
@@ -2429,6 +2519,68 @@ int moe_permute_by_expert_nvfp4(const moe_shape_t* shape, const uint8_t* rank_q,
                         pair_row, expert_counts, expert_offsets, cap_rank, expert_q,
                         expert_scale, expert_src_pair, cap_expert, err_word, stream,
                         shape->H / 32, shape->H / 256);
+}
+
+int moe_dispatch_quantised(const moe_shape_t* shape, int format, const uint16_t* hidden,
+                           const int32_t* topk_ids, int32_t* rank_counts, int32_t* rank_offsets,
+                           int32_t* expert_counts, int32_t* expert_offsets,
+                           int32_t* token_rank_slot, int32_t* pair_row, uint8_t* rank_q,
+                           uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                           uint8_t* expert_q, uint8_t* expert_scale, int32_t* expert_src_pair,
+                           int64_t cap_expert, void* workspace, size_t workspace_bytes,
+                           int32_t* err_word, void* stream) {
+  // The checks of the three calls, all made before anything is launched.
+  if (format != MOE_WIRE_MXFP8 && format != MOE_WIRE_MXFP4 && format != MOE_WIRE_NVFP4)
+    return MOE_ERR_ARG;
+  if (!shape_ok(shape) || shape->H % kMxRowQuantum != 0 || cap_rank < 0 || cap_expert < 0)
+    return MOE_ERR_ARG;
+  const moe_shape_t& sh = *shape;
+  // layout
+  if (!rank_counts || !rank_offsets || !expert_counts || !expert_offsets) return MOE_ERR_ARG;
+  if (sh.T > 0 && (!topk_ids || !token_rank_slot || !pair_row || !aligned16(topk_ids)))
+    return MOE_ERR_ARG;
+  const size_t need = layout_workspace_bytes(layout_geometry(sh));
+  if (workspace && (workspace_bytes < need || !aligned16(workspace))) return MOE_ERR_ARG;
+  // quantise-and-pack
+  if (sh.T > 0 && (!hidden || (cap_rank > 0 && (!rank_q || !rank_scale || !rank_src_token)) ||
+                   !aligned16(hidden) || !aligned16(rank_q) || !aligned16(rank_scale)))
+    return MOE_ERR_ARG;
+  // permute of the codes and scales
+  const bool padded = sh.align > 1 || sh.block > 0;
+  const int64_t max_rows = std::min<int64_t>(cap_rank, int64_t(sh.T) * std::min(sh.k, sh.R));
+  if (max_rows > 0 && !rank_scale) return MOE_ERR_ARG;
+  if (cap_expert > 0 && max_rows > 0 && !expert_scale) return MOE_ERR_ARG;
+  if (!aligned16(rank_scale) || !aligned16(expert_scale)) return MOE_ERR_ARG;
+  if (max_rows > 0 || (padded && cap_expert > 0)) {
+    if (max_rows > 0 && cap_expert > 0 && !expert_q) return MOE_ERR_ARG;
+    if (cap_expert > 0 && !expert_src_pair) return MOE_ERR_ARG;
+    if (!aligned16(rank_q) || !aligned16(expert_q)) return MOE_ERR_ARG;
+  }
+  if (dispatch_one_launch(sh)) {
+    const int fmt = format == MOE_WIRE_MXFP8 ? kWireMxfp8
+                    : format == MOE_WIRE_MXFP4 ? kWireMxfp4 : kWireNvfp4;
+    DispatchSmallArgs a{reinterpret_cast<const vec4*>(hidden), topk_ids, rank_counts,
+                        rank_offsets, expert_counts, expert_offsets, token_rank_slot, pair_row,
+                        fmt, rank_q, rank_scale, rank_src_token, cap_rank, expert_q,
+                        expert_scale, expert_src_pair, cap_expert, err_word};
+    launch_dispatch_small(sh, static_cast<hipStream_t>(stream), a);
+    return launch_status();
+  }
+  int st = moe_dispatch_layout(shape, topk_ids, rank_counts, rank_offsets, expert_counts,
+                               expert_offsets, token_rank_slot, pair_row, workspace,
+                               workspace_bytes, err_word, stream);
+  if (st != MOE_OK) return st;
+  const int bits = format == MOE_WIRE_MXFP8 ? 8 : 4;
+  const bool e4m3 = format == MOE_WIRE_NVFP4;
+  st = pack_mx_impl(bits, e4m3, shape, hidden, token_rank_slot, rank_q, rank_scale,
+                    rank_src_token, cap_rank, err_word, stream);
+  if (st != MOE_OK) return st;
+  const int nvec = bits == 8 ? sh.H / 16 : sh.H / 32;
+  const int nvec_s = e4m3 ? sh.H / 256 : sh.H / 512;
+  return permute_q_impl(shape, rank_q, rank_scale, rank_src_token, rank_offsets, topk_ids,
+                        pair_row, expert_counts, expert_offsets, cap_rank, expert_q,
+                        expert_scale, expert_src_pair, cap_expert, err_word, stream, nvec,
+                        nvec_s);
 }
 
 int moe_combine(const moe_shape_t* shape, const uint16_t* expert_out, const int32_t* pair_row,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_DISPATCH_ABI_VERSION 8
+#define MOE_DISPATCH_ABI_VERSION 9
 
 /*
  * The expert-grouped buffer comes in one of three shapes ([A2A] sec 2.2,
@@ -243,6 +243,33 @@ int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t
                  uint16_t* rank_buf, int32_t* rank_src_token, int64_t cap_rank,
                  uint16_t* expert_buf, int32_t* expert_src_pair, int64_t cap_expert,
                  void* workspace, size_t workspace_bytes, int32_t* err_word, void* stream);
+
+/* Wire formats of moe_dispatch_quantised. */
+#define MOE_WIRE_MXFP8 1 /* moe_dispatch_pack_mxfp8 / moe_permute_by_expert_mxfp8 */
+#define MOE_WIRE_MXFP4 2 /* moe_dispatch_pack_mxfp4 / moe_permute_by_expert_mxfp4 */
+#define MOE_WIRE_NVFP4 3 /* moe_dispatch_pack_nvfp4 / moe_permute_by_expert_nvfp4 */
+
+/*
+ * The whole quantised dispatch in one call: moe_dispatch_layout, then the
+ * quantise-and-pack and the permute of the chosen wire format ([A2A] sec 7.2),
+ * on the same arguments, with the same results bit for bit and the same error
+ * bits; one kernel launch for a decode-sized batch exactly as moe_dispatch
+ * (the wave quantises its part of the row once and writes the codes and
+ * scales to every copy and every pair), otherwise the three calls in turn.
+ *   format: MOE_WIRE_MXFP8, MOE_WIRE_MXFP4 or MOE_WIRE_NVFP4 (anything else
+ *   is an argument error).
+ *   The other arguments: those of the three calls, with their sizes,
+ *   alignment and NULL rules (H a multiple of 512); all are checked before
+ *   anything is launched.
+ */
+int moe_dispatch_quantised(const moe_shape_t* shape, int format, const uint16_t* hidden,
+                           const int32_t* topk_ids, int32_t* rank_counts, int32_t* rank_offsets,
+                           int32_t* expert_counts, int32_t* expert_offsets,
+                           int32_t* token_rank_slot, int32_t* pair_row, uint8_t* rank_q,
+                           uint8_t* rank_scale, int32_t* rank_src_token, int64_t cap_rank,
+                           uint8_t* expert_q, uint8_t* expert_scale, int32_t* expert_src_pair,
+                           int64_t cap_expert, void* workspace, size_t workspace_bytes,
+                           int32_t* err_word, void* stream);
 
 /*
  * Quantised dispatch, step 2: fused quantise-and-pack to MXFP8 ([A2A] sec 7.2:

@@ -496,20 +496,31 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
 SMALL_BATCH = 256
 
 
-def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
+def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report, lpb: int = 0):
     """dispatch_small (moe_dispatch's one-launch form, T <= 256, align = 1):
     workgroup 0 writes the counts and offsets; with a blocked layout one wave
     per expert marks its padding rows; one wave per (token, group of 64 vec4)
     moves that part of the row. The rows and slots
     the waves compute from the ids are the layout's, so the oracle's layout
-    stands in for them; every store is guarded by the caps as in the kernel."""
+    stands in for them; every store is guarded by the caps as in the kernel.
+    lpb > 0 models the quantised form (moe_dispatch_quantised): lpb vec4 per
+    scale block (4 for MX, 2 for the 16-value rows), H a multiple of 512; a
+    row's codes are one element per vec4 (8 bytes for MXFP8, 4 for 4-bit), its
+    scales one 32-bit word per four blocks, stored by the lanes whose column
+    is a multiple of 4 * lpb."""
     T, E, R, k, nvec = c.T, c.E, c.R, c.k, c.nvec
     m = E // R
+    if lpb:
+        assert nvec % W == 0, "the quantised form takes rows of a multiple of 512 values"
+        sw = nvec // (4 * lpb)  # scale words per row
+    else:
+        sw = 0
     for name, n in (("hidden", T * nvec), ("topk_ids", T * k), ("rank_counts", R),
                     ("rank_offsets", R + 1), ("expert_counts", E), ("expert_offsets", E + 1),
                     ("token_rank_slot", T * R), ("pair_row", T * k),
                     ("rank_buf", c.cap_rank * nvec), ("rank_src_token", c.cap_rank),
-                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert)):
+                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert),
+                    ("rank_scale", c.cap_rank * sw), ("expert_scale", c.cap_expert * sw)):
         rep.buf(name, n)
     tag = "dispatch_small"
     groups = cdiv(nvec, W)
@@ -553,6 +564,9 @@ def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
     ok_r = (s_all >= 0) & (s_all < c.cap_rank)
     rep.access(tag, "rank_src_token", s_all[ok_r], "store")
     rep.access(tag, "rank_buf", rows_cols(s_all[ok_r], cols, nvec), "store")
+    if lpb:
+        scol = np.arange(0, nvec, 4 * lpb, dtype=np.int64) // (4 * lpb)
+        rep.access(tag, "rank_scale", rows_cols(s_all[ok_r], scol, sw), "store")
     e = np.asarray(ids, np.int64)[:T]
     valid = (e >= 0) & (e < E)
     r = np.where(valid, e // m, 0)
@@ -560,13 +574,16 @@ def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report):
     ok_p = valid & (copy >= 0) & (copy < c.cap_rank) & (pr[:T] >= 0) & (pr[:T] < c.cap_expert)
     rep.access(tag, "expert_src_pair", pr[:T][ok_p], "store")
     rep.access(tag, "expert_buf", rows_cols(pr[:T][ok_p], cols, nvec), "store")
+    if lpb:
+        rep.access(tag, "expert_scale", rows_cols(pr[:T][ok_p], scol, sw), "store")
 
 
-def dispatch_one_launch(c: Case, ids: np.ndarray) -> Report:
-    """moe_dispatch's one-launch form on the oracle's layout."""
+def dispatch_one_launch(c: Case, ids: np.ndarray, lpb: int = 0) -> Report:
+    """moe_dispatch's (lpb = 0) or moe_dispatch_quantised's one-launch form on
+    the oracle's layout."""
     rep = Report()
     lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
-    model_dispatch_small(c, lay, ids, rep)
+    model_dispatch_small(c, lay, ids, rep, lpb)
     return rep
 
 

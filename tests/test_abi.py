@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = moe.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == moe.ABI_VERSION == 8
+    assert L.moe_abi_version() == moe.ABI_VERSION == 9
 
 
 def test_timing_hook_takes_both_events_or_neither():
@@ -135,6 +135,39 @@ def test_dispatch_rejects_bad_arguments_without_launching():
                     dict(ids=ctypes.c_void_p(0x10004)), dict(eb=ctypes.c_void_p(0x10002))):
             assert call(sp, **bad) == moe.MOE_ERR_ARG, (s.T, s.align, bad)
     assert call(ctypes.byref(shape(E=10))) == moe.MOE_ERR_ARG
+    big = ctypes.byref(shape(T=4096, H=512, E=384, R=8, k=6))
+    need = L.moe_layout_workspace_bytes(big)
+    assert call(big, ws=F, wsb=need - 4) == moe.MOE_ERR_ARG
+
+
+def test_dispatch_quantised_rejects_bad_arguments_without_launching():
+    """moe_dispatch_quantised checks the format, rows of a multiple of 512
+    values and what its three calls check, before launching anything."""
+    L = moe.lib()
+    F = FAKE
+
+    def call(sp, fmt=1, hidden=F, ids=F, rc=F, ro=F, ec=F, eo=F, trs=F, pr=F, rq=F, rsc=F,
+             rs=F, cr=128, eq=F, esc=F, es=F, ce=128, ws=None, wsb=0):
+        return L.moe_dispatch_quantised(sp, fmt, hidden, ids, rc, ro, ec, eo, trs, pr, rq, rsc,
+                                        rs, cr, eq, esc, es, ce, ws, wsb, None, None)
+
+    for s in (shape(H=1024), shape(T=4096, H=512, E=384, R=8, k=6), shape(H=512, align=16),
+              shape(H=1536, block=4)):
+        sp = ctypes.byref(s)
+        for bad in (dict(fmt=0), dict(fmt=4), dict(fmt=-1), dict(ids=None), dict(rc=None),
+                    dict(eo=None), dict(trs=None), dict(pr=None), dict(hidden=None),
+                    dict(rq=None), dict(rsc=None), dict(rs=None), dict(eq=None),
+                    dict(esc=None), dict(es=None), dict(cr=-1), dict(ce=-2),
+                    dict(hidden=ctypes.c_void_p(0x10008)), dict(ids=ctypes.c_void_p(0x10004)),
+                    dict(rsc=ctypes.c_void_p(0x10004)), dict(esc=ctypes.c_void_p(0x10001)),
+                    dict(eq=ctypes.c_void_p(0x10008))):
+            for fmt in (1, 2, 3):
+                args = dict(dict(fmt=fmt), **bad)
+                assert call(sp, **args) == moe.MOE_ERR_ARG, (s.T, s.H, s.align, bad)
+    for H in (8, 520, 1000, 2560 + 8):
+        for fmt in (1, 2, 3):
+            assert call(ctypes.byref(shape(H=H)), fmt=fmt) == moe.MOE_ERR_ARG, (H, fmt)
+    assert call(ctypes.byref(shape(E=10, H=512))) == moe.MOE_ERR_ARG
     big = ctypes.byref(shape(T=4096, H=512, E=384, R=8, k=6))
     need = L.moe_layout_workspace_bytes(big)
     assert call(big, ws=F, wsb=need - 4) == moe.MOE_ERR_ARG

@@ -133,6 +133,23 @@ def test_dispatch_one_launch():
         assert_clean(lm.dispatch_one_launch(c2, ids), f"small batch {s} caps {cr}/{ce}")
 
 
+def test_dispatch_quantised_one_launch():
+    """moe_dispatch_quantised's one-launch form: codes and scale words of the
+    MX formats (4 vec4 per scale block) and the 16-value rows (2), full and
+    undersized caps, H a multiple of 512."""
+    for s in range(150):
+        c, ids, rng = small_batch(s)
+        H = 512 * int(rng.integers(1, 21))
+        for lpb in (4, 2):
+            c1 = lm.Case(c.T, H, c.E, c.R, c.k, 1, c.block)
+            assert_clean(lm.dispatch_one_launch(c1, ids, lpb), f"q small batch {s} lpb {lpb}")
+            cr = int(rng.integers(0, c1.cap_rank + 1))
+            ce = int(rng.integers(0, c1.cap_expert + 1))
+            c2 = lm.Case(c.T, H, c.E, c.R, c.k, 1, c.block, cap_rank=cr, cap_expert=ce)
+            assert_clean(lm.dispatch_one_launch(c2, ids, lpb),
+                         f"q small batch {s} lpb {lpb} caps {cr}/{ce}")
+
+
 def test_model_finds_the_earlier_permute_reads():
     """The unclamped source-token load of an earlier permute reads past
     cap_rank for a grid rounded up past the last row; the model says so."""

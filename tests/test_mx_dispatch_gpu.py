@@ -36,7 +36,11 @@ FORMATS = ["mxfp8", "mxfp4", "nvfp4"]
 
 
 def run_gpu(hid, ids, E, R, fmt="mxfp8", align=1, block=0, cap_rank=None, cap_expert=None,
-            spare=4):
+            spare=4, whole_dispatch=False):
+    """The quantised dispatch through the C ABI: the layout, quantise-and-pack
+    and permute calls, or with whole_dispatch the one call
+    moe_dispatch_quantised. Row buffers get `spare` canary rows past their
+    caps."""
     bits, blk = moe.WIRE_FORMATS[fmt]
     T, H = hid.shape
     k = ids.shape[1]
@@ -50,7 +54,12 @@ def run_gpu(hid, ids, E, R, fmt="mxfp8", align=1, block=0, cap_rank=None, cap_ex
     err = torch.zeros(1, dtype=i32, device=dev)
     ws = moe.layout_workspace_bytes(shape)
     workspace = torch.zeros(((ws + 15) // 16 * 4,), dtype=i32, device=dev) if ws else None
-    lay = moe.layout(ids_d, E, R, H, align=align, block=block, err=err, workspace=workspace)
+    lay = dict(rank_counts=torch.full((R,), -9, dtype=i32, device=dev),
+               rank_offsets=torch.full((R + 1,), -9, dtype=i32, device=dev),
+               expert_counts=torch.full((E,), -9, dtype=i32, device=dev),
+               expert_offsets=torch.full((E + 1,), -9, dtype=i32, device=dev),
+               token_rank_slot=torch.full((T, R), -9, dtype=i32, device=dev),
+               pair_row=torch.full((T, k), -9, dtype=i32, device=dev))
     qw = H * bits // 8  # code bytes per row
     rq = torch.full((cap_rank + spare, qw), CANARY, dtype=u8, device=dev)
     rs = torch.full((cap_rank + spare, H // blk), CANARY, dtype=u8, device=dev)
@@ -58,12 +67,21 @@ def run_gpu(hid, ids, E, R, fmt="mxfp8", align=1, block=0, cap_rank=None, cap_ex
     eq = torch.full((cap_expert + spare, qw), CANARY, dtype=u8, device=dev)
     es = torch.full((cap_expert + spare, H // blk), CANARY, dtype=u8, device=dev)
     esrc = torch.full((cap_expert + spare,), CANARY_IDX, dtype=i32, device=dev)
-    moe.pack_mx(fmt, hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
-                rsrc[:cap_rank], err=err)
-    moe.permute_mx(fmt, rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank], lay["rank_offsets"],
-                   ids_d, lay["pair_row"], E, eq[:cap_expert], es[:cap_expert],
-                   esrc[:cap_expert], expert_counts=lay["expert_counts"],
-                   expert_offsets=lay["expert_offsets"], align=align, block=block, err=err)
+    if whole_dispatch:
+        moe.dispatch_all_mx(fmt, hid_d, ids_d, E, R, lay, rq[:cap_rank], rs[:cap_rank],
+                            rsrc[:cap_rank], eq[:cap_expert], es[:cap_expert],
+                            esrc[:cap_expert], align=align, block=block, workspace=workspace,
+                            err=err)
+    else:
+        moe.layout(ids_d, E, R, H, align=align, block=block, err=err, out=lay,
+                   workspace=workspace)
+        moe.pack_mx(fmt, hid_d, lay["token_rank_slot"], E, k, rq[:cap_rank], rs[:cap_rank],
+                    rsrc[:cap_rank], err=err)
+        moe.permute_mx(fmt, rq[:cap_rank], rs[:cap_rank], rsrc[:cap_rank],
+                       lay["rank_offsets"], ids_d, lay["pair_row"], E, eq[:cap_expert],
+                       es[:cap_expert], esrc[:cap_expert], expert_counts=lay["expert_counts"],
+                       expert_offsets=lay["expert_offsets"], align=align, block=block,
+                       err=err)
     torch.cuda.synchronize()
     out = {key: v.cpu().numpy() for key, v in lay.items()}
     out.update(rq=rq.cpu().numpy(), rs=rs.cpu().numpy(), rsrc=rsrc.cpu().numpy(),
@@ -76,7 +94,8 @@ def check(hid, ids, E, R, what, fmt="mxfp8", align=1, block=0, **kw):
     g = run_gpu(hid, ids, E, R, fmt, align, block, **kw)
     T, k = ids.shape
     lay = oracle.layout(ids, E, R, align=align, block=block)
-    for key in ("token_rank_slot", "pair_row", "rank_offsets", "expert_offsets"):
+    for key in ("token_rank_slot", "pair_row", "rank_offsets", "expert_offsets",
+                "rank_counts", "expert_counts"):
         assert np.array_equal(g[key], lay[key]), f"{what}: layout {key}"
     cr, ce = g["cap_rank"], g["cap_expert"]
     pack = getattr(oracle, f"pack_{fmt}")
@@ -196,3 +215,153 @@ def test_mx_rejects_rows_not_a_multiple_of_512():
     rs16 = torch.zeros((8, H // 16), dtype=torch.uint8, device=dev)
     with pytest.raises(moe.MoeError):
         moe.pack_nvfp4(hid, slots, E, k, rq[:, :H // 2], rs16, src)
+
+
+# The quantised dispatch in one call (moe_dispatch_quantised): a decode-sized
+# unpadded batch takes the one-launch form (quantise in the mover waves), any
+# other batch the three calls above; both held to the same bar.
+
+def small_mx_case(s: int):
+    """A random decode-sized case for the quantised one-launch form: T up to 256
+    (above 64 mostly with a k the four-token form is compiled for), H a
+    multiple of 512, masked blocks, -1, duplicate and out-of-range ids, and
+    sometimes rows of raw 16-bit patterns (NaNs, infinities, subnormals)."""
+    rng = np.random.default_rng(71000 + s)
+    R = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 33, 64]))
+    E = R * int(rng.integers(1, 1024 // R + 1))
+    T = int(rng.choice([0, 1, 2, 31, 63, 64, int(rng.integers(3, 64)), 65, 128, 255, 256,
+                        int(rng.integers(65, 257))]))
+    if T > 64 and rng.random() < 0.85:
+        k = int(rng.choice([c for c in (1, 2, 4, 6, 8) if c <= E]))
+    else:
+        k = int(rng.integers(1, min(16, E) + 1))
+    H = 512 * int(rng.integers(1, 11))
+    block = int(rng.choice([0, 0, 0, 1, int(rng.integers(1, 6))]))
+    p_neg = float(rng.choice([0.0, 0.1, 0.5]))
+    p_dup = float(rng.choice([0.0, 0.15])) if k > 1 else 0.0
+    p_bad = float(rng.choice([0.0, 0.0, 0.05]))
+    ids = pins.rand_ids(rng, T, E, k, p_neg=p_neg, p_dup=p_dup, p_bad=p_bad)
+    if rng.random() < 0.25:
+        hid = rng.integers(0, 65536, (T, H), dtype=np.uint16)
+    else:
+        hid = synth.normal_bf16(s, 3, T * H).reshape(T, H)
+    fmt = FORMATS[s % 3]
+    return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, hid=hid, fmt=fmt, rng=rng)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_dispatch_quantised_workloads(name, fmt):
+    """decode (64 tokens) and tiny (256 tokens, k = 2) in one launch, prefill
+    through the three calls."""
+    w = synth.WORKLOADS[name]
+    say(f"[{fmt} dispatch] {w.describe()}")
+    hid = synth.hidden(w)
+    ids, _ = synth.routing(w)
+    lay = check(hid, ids, w.E, w.R, f"dispatch {name}", fmt=fmt, whole_dispatch=True)
+    assert lay["err"] == 0
+
+
+@pytest.mark.parametrize("s", range(192))
+def test_dispatch_quantised_small(s):
+    c = small_mx_case(s)
+    say(f"[dispatch q small] s={s} {c['fmt']} T={c['T']} H={c['H']} E={c['E']} R={c['R']} "
+        f"k={c['k']} block={c['block']}")
+    check(c["hid"], c["ids"], c["E"], c["R"], f"q small {s}", fmt=c["fmt"], block=c["block"],
+          whole_dispatch=True)
+
+
+@pytest.mark.parametrize("s", range(48))
+def test_dispatch_quantised_undersized(s):
+    """Caps below the worst case in the one-launch form: copies and pairs past
+    them dropped and flagged as the three calls do."""
+    c = small_mx_case(400 + s)
+    rng = c["rng"]
+    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], 1, c["block"])
+    cr = int(rng.integers(0, shape.cap_rank + 1))
+    ce = int(rng.integers(0, shape.cap_expert + 1))
+    say(f"[dispatch q caps] s={400 + s} {c['fmt']} T={c['T']} E={c['E']} R={c['R']} "
+        f"k={c['k']} block={c['block']} caps {cr}/{ce}")
+    check(c["hid"], c["ids"], c["E"], c["R"], f"q caps {400 + s}", fmt=c["fmt"],
+          block=c["block"], cap_rank=cr, cap_expert=ce, whole_dispatch=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_dispatch_quantised_every_bit_pattern(fmt):
+    """Random 16-bit patterns in one launch (64 tokens, four scale blocks per
+    1 KiB chunk for MX, eight for the 16-value rows)."""
+    T, H, E, R, k = 64, 1024, 32, 4, 3
+    rng = np.random.default_rng(52)
+    hid = rng.integers(0, 65536, (T, H), dtype=np.uint16)
+    hid[::7] &= 0x80FF
+    hid[1::11, :64] = 0x7F80
+    hid[2::13, 32:48] = 0xFFC1  # a NaN block
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
+    check(hid, ids, E, R, "q bit patterns", fmt=fmt, whole_dispatch=True)
+
+
+def test_dispatch_quantised_nvfp4_every_block_max():
+    """Every bf16 pattern as a 16-value block maximum, through the one-launch
+    form 64 tokens at a time."""
+    H, E, R, k = 1024, 16, 4, 1
+    pats = np.arange(65536, dtype=np.uint32)
+    rng = np.random.default_rng(54)
+    topf = (pats << 16).view(np.float32)
+    frac = rng.uniform(-1.0, 1.0, (65536, 15)).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        rest = (frac * np.abs(topf)[:, None]).astype(np.float32)
+    rest = np.where(np.isfinite(rest), rest, np.float32(0.0))
+    rest_bits = (rest.view(np.uint32) >> 16).astype(np.uint16)
+    rows = np.concatenate([pats.astype(np.uint16)[:, None], rest_bits], axis=1).reshape(-1, H)
+    for t0 in range(0, rows.shape[0], 64):
+        hid = rows[t0:t0 + 64]
+        T = hid.shape[0]
+        ids = (np.arange(T, dtype=np.int32) % E)[:, None].copy()
+        check(hid, ids, E, R, f"q block max {t0}", fmt="nvfp4", whole_dispatch=True)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("T,k,align", [(64, 4, 16), (257, 4, 1), (65, 3, 1), (40, 4, 128)])
+def test_dispatch_quantised_three_call_form(T, k, align, fmt):
+    rng = np.random.default_rng(T + align + 5)
+    E, R, H = 64, 8, 1024
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
+    hid = synth.normal_bf16(9, 0, T * H).reshape(T, H)
+    say(f"[{fmt} dispatch three calls] T={T} k={k} align={align}")
+    check(hid, ids, E, R, f"q T={T} k={k} align={align}", fmt=fmt, align=align,
+          whole_dispatch=True)
+
+
+def test_dispatch_quantised_one_launch_equals_three_calls():
+    """Both forms on the same inputs (the testing hook switches the one launch
+    off): every output byte identical."""
+    for s in range(12):
+        c = small_mx_case(800 + s)
+        say(f"[dispatch q forms] s={800 + s} {c['fmt']} T={c['T']} E={c['E']} R={c['R']} "
+            f"k={c['k']} block={c['block']}")
+        res = []
+        for fused in (1, 0):
+            old = moe.lib().moe_testing_set_dispatch_fused(fused)
+            try:
+                res.append(run_gpu(c["hid"], c["ids"], c["E"], c["R"], c["fmt"],
+                                   block=c["block"], whole_dispatch=True))
+            finally:
+                moe.lib().moe_testing_set_dispatch_fused(old)
+        for key, v in res[0].items():
+            assert np.array_equal(np.asarray(v), np.asarray(res[1][key])), \
+                f"s={800 + s}: {key} differs between the forms"
+
+
+def test_dispatch_quantised_rejects_bad_arguments():
+    dev = torch.device("cuda:0")
+    T, H, E, R, k = 4, 520, 8, 2, 2
+    hid = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
+    ids = torch.zeros((T, k), dtype=torch.int32, device=dev)
+    shape = moe.Shape(T, H, E, R, k)
+    b = moe.Buffers(shape, dev)
+    rq = torch.zeros((8, H), dtype=torch.uint8, device=dev)
+    rs = torch.zeros((8, H // 32), dtype=torch.uint8, device=dev)
+    src = torch.zeros(8, dtype=torch.int32, device=dev)
+    with pytest.raises(moe.MoeError):
+        moe.dispatch_all_mx("mxfp8", hid, ids, E, R, b.layout_dict(), rq, rs, src, rq, rs, src,
+                            err=b.err)
