@@ -671,15 +671,17 @@ def sweep(names, dev, with_oracle: bool) -> None:
         log(f"{name}: graph replay {us_g:.1f} us per step")
         us_d = rig.graph_step_us(calls=("dispatch", "combine"))
         one = align == 1 and (w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8)))
-        bytes_d = rig.nbytes["dispatch"] + rig.nbytes["combine"] if one else \
-            path_bytes(rig.nbytes)
+        form = "one launch" if one else "three calls" if wire else "pack+permute kernel"
+        bytes_d = path_bytes(rig.nbytes) if form == "three calls" else \
+            rig.nbytes["dispatch"] + rig.nbytes["combine"]
         res["graph_whole_dispatch"] = {
             "us_per_step": round(us_d, 2), "bytes": bytes_d,
             "GB/s": round(bytes_d / (us_d * 1e-6) / 1e9, 1),
-            "one_launch": one,
+            "one_launch": one, "form": form,
             "note": ("moe_dispatch_quantised" if wire else "moe_dispatch") +
-                    " (one launch for a decode-sized batch with align 1, else the three "
-                    "calls) and combine, replayed from a HIP graph"}
+                    " (one launch for a decode-sized batch with align 1; past it the layout "
+                    "and one pack-and-permute kernel, or the three calls for a wire format) "
+                    "and combine, replayed from a HIP graph"}
         log(f"{name}: graph replay with the one-call dispatch {us_d:.1f} us per step")
         if with_oracle and align == 1 and block == 0 and not wire:
             log(f"{name}: oracle")
@@ -716,8 +718,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
     print("|---|---|---|---|")
     for name, r in rows:
         wd = r.get("graph_whole_dispatch")
-        wds = "" if wd is None else f"{wd['us_per_step']}" + (" (one launch)" if wd["one_launch"]
-                                                               else "")
+        wds = "" if wd is None else f"{wd['us_per_step']} ({wd['form']})"
         print(f"| {name} | {r['graph']['us_per_step']} | {wds} | {r['warm']['us']} |")
     print(f"\n1 GiB device copy: {copy['us']} us, {copy['GB/s']} GB/s (read + write)")
 
@@ -836,6 +837,24 @@ def main():
     del flush
     rig.check_err()
 
+    # The same step with layout, pack and permute through the one call
+    # moe_dispatch (rotating sets): the same outputs from fewer bytes, since
+    # the packed rows are not read back.
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for _ in range(args.steps):
+        rig.rotate()
+        rig.call("dispatch")
+        rig.call("combine")
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    one_call_ms = t_begin.elapsed_time(t_end) / args.steps
+    rig.check_err()
+    one_call_bytes = rig.nbytes["dispatch"] + rig.nbytes["combine"]
+    log(f"timed {args.steps} steps through moe_dispatch: {one_call_ms * 1e3:.1f} us/step")
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     call_stats = {}
     for c in CALLS:
@@ -859,7 +878,13 @@ def main():
              "after_write": dict(mode(after_write_ms), note="the rotated steps right after a "
                                  "1 GiB write by another kernel"),
              "cold": dict(mode(cold_step_ms), note="sum of per-call means, L2 and Infinity "
-                          "Cache evicted by a 1 GiB read before every call")}
+                          "Cache evicted by a 1 GiB read before every call"),
+             "one_call_dispatch": {
+                 "us_per_step": round(one_call_ms * 1e3, 2), "bytes": one_call_bytes,
+                 "GB/s": round(one_call_bytes / (one_call_ms * 1e-3) / 1e9, 1),
+                 "note": "moe_dispatch (the layout, then pack and permute in one kernel) and "
+                         "moe_combine, rotating buffer sets: the same outputs, the packed rows "
+                         "not read back, so fewer algorithmic bytes (its own count)"}}
     # The dominant kernel's own duration: a third pass of whole steps (rotating
     # sets) in which the library records an event pair with the permute's
     # dispatch.

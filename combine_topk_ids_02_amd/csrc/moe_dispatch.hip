@@ -29,6 +29,11 @@
 //  dispatch_small  layout, pack and permute of a batch of at most 256 tokens
 //                in one launch (moe_dispatch): every wave finds its own
 //                token's rows from the ids ([A2A] sec 4.1, sec 8.1)
+//  pack_expand_rows  pack and permute in one kernel for moe_dispatch past
+//                dispatch_small's sizes, after the layout: one wave per
+//                (token, 1 KiB of the row) reads it once and writes it to
+//                every copy and every pair row, so the packed rows are not
+//                read back (ordinary loads and stores, chosen by measurement)
 //  pack_rows_mx  fused quantise-and-pack to the [A2A] sec 7.2 wire formats:
 //                MXFP8, MXFP4, and the 4-bit row with an E4M3 scale per 16
 //                values; permute_rows moves their codes and scales
@@ -1359,6 +1364,84 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
   }
 }
 
+// moe_dispatch past the one-launch form: once the layout is written, pack and
+// permute in one kernel. Each wave takes one (token, slice of V*64 vec4 of
+// its row), reads that part of the hidden row once and stores it to the
+// token's copy on each of its ranks and to the row of each of its pairs, so
+// the packed rows are not read back. A pair's row is written when the
+// permute would write it: its expert is valid, its rank copy is inside the
+// rank buffer (the permute reads only those), and its row is inside the
+// expert buffer; the cap errors are flagged as the pack and the permute
+// flag them. With padded or blocked runs the first pad_waves = E waves mark
+// the padding rows as the permute does.
+template <int V, bool kStreamLoad, bool kStreamStore>
+__global__ __launch_bounds__(kBlock) void pack_expand_rows(
+    const vec4* hidden, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ token_rank_slot, const int32_t* __restrict__ pair_row,
+    const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
+    vec4* rank_buf, int32_t* __restrict__ rank_src_token, vec4* expert_buf,
+    int32_t* __restrict__ expert_src_pair, int T, int E, int R, int k, float inv_m, int block,
+    int nvec, int slices, int pad_waves, int64_t cap_rank, int64_t cap_expert,
+    int32_t* err_word) {
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (gw < pad_waves) {
+    mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
+    return;
+  }
+  const int64_t w = gw - pad_waves;
+  const int t = int(w / slices);
+  const int sl = int(w - (int64_t)t * slices);
+  if (t >= T) return;
+  const int c0 = sl * (V * kWave);
+  // the token's slots, ids and pair rows, its part of the row right behind
+  // them (clamped into the row; columns past it are not stored)
+  const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
+  const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
+  const int pr_any = pair_row[(int64_t)t * k + min(lane, k - 1)];
+  const vec4* src = hidden + (int64_t)t * nvec;
+  vec4 v[V];
+#pragma unroll
+  for (int q = 0; q < V; ++q)
+    v[q] = load_row<kStreamLoad>(src + min(c0 + q * kWave + lane, nvec - 1));
+  const int slot = lane < R ? slot_any : -1;
+  const bool ok_r = slot >= 0 && slot < cap_rank;
+  const int e = lane < k ? e_any : -1;
+  const bool valid = uint32_t(e) < uint32_t(E);
+  const int copy = __shfl(slot, valid ? rank_of(e, inv_m) : 0, kWave);
+  const bool here = valid && copy >= 0 && copy < cap_rank;
+  const int p = here ? pr_any : -1;
+  const bool ok_p = here && p >= 0 && p < cap_expert;
+  if (sl == 0) {
+    if (__ballot(slot >= 0 && !ok_r) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+    if (__ballot(here && !ok_p) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+    if (ok_r) rank_src_token[slot] = t;
+    if (ok_p) expert_src_pair[p] = t * k + lane;
+  }
+  uint64_t d = __ballot(ok_r);
+  while (d) {
+    const int which = __ffsll((unsigned long long)d) - 1;
+    d &= d - 1;
+    vec4* dst = rank_buf + (int64_t)read_lane(slot, which) * nvec;
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const int c = c0 + q * kWave + lane;
+      if (c < nvec) store_row<kStreamStore>(dst + c, v[q]);
+    }
+  }
+  d = __ballot(ok_p);
+  while (d) {
+    const int which = __ffsll((unsigned long long)d) - 1;
+    d &= d - 1;
+    vec4* dst = expert_buf + (int64_t)read_lane(p, which) * nvec;
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const int c = c0 + q * kWave + lane;
+      if (c < nvec) store_row<kStreamStore>(dst + c, v[q]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The whole dispatch of a small batch in one launch (moe_dispatch with at most
 // kSmallBatch tokens, 64 for a k read at run time, and unpadded runs):
@@ -2004,6 +2087,27 @@ struct PackLaunch {
   }
 };
 
+// Pack and permute in one kernel: V vec4 per lane, `slices` waves per token.
+// One wave per (token, 1 KiB of the row) with ordinary loads and stores was
+// best or within 1% of the best of six forms measured (1 or 2 vec4 per lane
+// or the whole row per wave; streamed loads; streamed stores) over five
+// shapes; streamed stores were 1-6% slower everywhere.
+constexpr int kExpandVec = 1;
+constexpr bool kExpandStreamLoad = false;
+constexpr bool kExpandStreamStore = false;
+template <int V>
+struct PackExpandLaunch {
+  static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* ids,
+                 const int32_t* slots, const int32_t* prow, const int32_t* ecnt,
+                 const int32_t* eoff, vec4* rb, int32_t* rsrc, vec4* eb, int32_t* esrc, int T,
+                 int E, int R, int k, float inv_m, int block, int nvec, int slices,
+                 int pad_waves, int64_t cap_rank, int64_t cap_expert, int32_t* err) {
+    MOE_LAUNCH((pack_expand_rows<V, kExpandStreamLoad, kExpandStreamStore>), grid, dim3(kBlock),
+               0, st, hid, ids, slots, prow, ecnt, eoff, rb, rsrc, eb, esrc, T, E, R, k, inv_m,
+               block, nvec, slices, pad_waves, cap_rank, cap_expert, err);
+  }
+};
+
 template <int V>
 struct PermuteLaunch {
   static void go(dim3 grid, hipStream_t st, const vec4* rb, const vec4* rs, const int32_t* src,
@@ -2450,6 +2554,22 @@ int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t
   int st = moe_dispatch_layout(shape, topk_ids, rank_counts, rank_offsets, expert_counts,
                                expert_offsets, token_rank_slot, pair_row, workspace,
                                workspace_bytes, err_word, stream);
+  const int nvec = sh.H / 8;
+  const int V = std::min(kExpandVec, (nvec + kWave - 1) / kWave);
+  const int64_t slices = (nvec + V * kWave - 1) / (V * kWave);
+  const int pad_waves = padded && cap_expert > 0 ? sh.E : 0;
+  // (an empty batch takes the permute, for the padding marks alone)
+  if (st == MOE_OK && sh.T > 0 && g_dispatch_fused &&
+      pad_waves + int64_t(sh.T) * slices <= INT32_MAX) {
+    ByVec<PackExpandLaunch>::run(
+        V, dim3(blocks_for(pad_waves + int64_t(sh.T) * slices)),
+        static_cast<hipStream_t>(stream), reinterpret_cast<const vec4*>(hidden), topk_ids,
+        token_rank_slot, pair_row, expert_counts, expert_offsets,
+        reinterpret_cast<vec4*>(rank_buf), rank_src_token, reinterpret_cast<vec4*>(expert_buf),
+        expert_src_pair, sh.T, sh.E, sh.R, sh.k, float(1.0 / double(sh.E / sh.R)), sh.block,
+        nvec, int(slices), pad_waves, cap_rank, cap_expert, err_word);
+    return launch_status();
+  }
   if (st == MOE_OK)
     st = moe_dispatch_pack(shape, hidden, token_rank_slot, rank_buf, rank_src_token, cap_rank,
                            err_word, stream);

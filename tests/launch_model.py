@@ -408,6 +408,34 @@ def model_pack(c: Case, lay: dict, rep: Report):
     rep.access("pack_rows", "rank_buf", rows_cols(slots[ok], stores, nvec), "store")
 
 
+def model_mark_padding(tag: str, c: Case, lay: dict, rep: Report, old_padding: bool = False):
+    """mark_padding in waves 0..E-1: each expert's rows past its pairs (a
+    fixed block, or its run between the offsets), clipped to the buffer."""
+    E = c.E
+    counts = lay["expert_counts"].astype(np.int64)
+    offs = lay["expert_offsets"].astype(np.int64)
+    e = np.arange(E, dtype=np.int64)
+    rep.access(tag, "expert_counts", e, "load")
+    if c.block > 0 and not old_padding:
+        first = e * c.block
+        end = first + c.block
+    else:
+        rep.access(tag, "expert_offsets", e, "load")
+        first = offs[:E]
+        end = (e + 1) * c.block if c.block > 0 else offs[1:]
+        if c.block <= 0:
+            rep.access(tag, "expert_offsets", e + 1, "load")
+    if old_padding:  # before the rows were clipped below
+        lo = first + (np.minimum(counts, c.block) if c.block > 0 else counts)
+    else:
+        cnt = np.maximum(counts, 0)
+        lo = np.maximum(first + (np.minimum(cnt, c.block) if c.block > 0 else cnt), 0)
+    hi = np.minimum(end, c.cap_expert)
+    for a, b in zip(lo, hi):
+        if b > a:
+            rep.access(tag, "expert_src_pair", [a, b - 1], "store")
+
+
 def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep: Report,
                   nvec=None, nvec_s=0, tag="permute", old_padding=False):
     """permute_rows; nvec_s > 0: the MX form (scale rows of nvec_s vec4).
@@ -428,29 +456,8 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
     if max_rows + pad_waves == 0:
         return
     nwaves = blocks_for(max_rows + pad_waves) * WPB
-    counts = lay["expert_counts"].astype(np.int64)
-    offs = lay["expert_offsets"].astype(np.int64)
     if pad_waves:
-        e = np.arange(E, dtype=np.int64)
-        rep.access(tag, "expert_counts", e, "load")
-        if c.block > 0 and not old_padding:
-            first = e * c.block
-            end = first + c.block
-        else:
-            rep.access(tag, "expert_offsets", e, "load")
-            first = offs[:E]
-            end = (e + 1) * c.block if c.block > 0 else offs[1:]
-            if c.block <= 0:
-                rep.access(tag, "expert_offsets", e + 1, "load")
-        if old_padding:  # before the rows were clipped below
-            lo = first + (np.minimum(counts, c.block) if c.block > 0 else counts)
-        else:
-            cnt = np.maximum(counts, 0)
-            lo = np.maximum(first + (np.minimum(cnt, c.block) if c.block > 0 else cnt), 0)
-        hi = np.minimum(end, c.cap_expert)
-        for a, b in zip(lo, hi):
-            if b > a:
-                rep.access(tag, "expert_src_pair", [a, b - 1], "store")
+        model_mark_padding(tag, c, lay, rep, old_padding)
     i = np.arange(nwaves - pad_waves, dtype=np.int64)
     rep.access(tag, "rank_offsets", np.minimum(LANE, R - 1) + 1, "load")
     rep.access(tag, "rank_offsets", [R], "load")
@@ -491,6 +498,78 @@ def model_permute(c: Case, lay: dict, rank_src: np.ndarray, ids: np.ndarray, rep
             f1, l1, s1 = fan_out_cols(1, nvec_s)
             rep.access(tag, "rank_scale", rows_cols(i, np.concatenate([f1, l1]), nvec_s), "load")
             rep.access(tag, "expert_scale", rows_cols(p[ok], s1, nvec_s), "store")
+
+
+EXPAND_VEC = 1  # vec4 per lane of pack_expand_rows
+
+
+def expand_tiling(nvec: int):
+    """pack_expand_rows: V vec4 per lane, `slices` waves per token."""
+    V = min(EXPAND_VEC, cdiv(nvec, W))
+    return V, cdiv(nvec, V * W)
+
+
+def model_pack_expand(c: Case, lay: dict, ids: np.ndarray, rep: Report):
+    """pack_expand_rows (moe_dispatch past the one-launch form, after the
+    layout): padding waves, then one wave per (token, slice of V*64 vec4).
+    Every index array is read as the layout left it, whatever it holds: a
+    copy is stored when its slot is inside the rank buffer, a pair when its
+    expert is valid, the slot of its rank is inside the rank buffer and its
+    row inside the expert buffer."""
+    T, E, R, k, nvec = c.T, c.E, c.R, c.k, c.nvec
+    m = E // R
+    tag = "pack_expand_rows"
+    for name, n in (("hidden", T * nvec), ("topk_ids", T * k), ("token_rank_slot", T * R),
+                    ("pair_row", T * k), ("expert_counts", E), ("expert_offsets", E + 1),
+                    ("rank_buf", c.cap_rank * nvec), ("rank_src_token", c.cap_rank),
+                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert)):
+        rep.buf(name, n)
+    if T == 0:
+        return
+    V, slices = expand_tiling(nvec)
+    padded = c.align > 1 or c.block > 0
+    pad_waves = E if padded and c.cap_expert > 0 else 0
+    assert pad_waves + T * slices <= INT32_MAX
+    if pad_waves:
+        model_mark_padding(tag, c, lay, rep)
+    nwaves = blocks_for(pad_waves + T * slices) * WPB - pad_waves
+    w = np.arange(nwaves, dtype=np.int64)
+    t_all = w // slices
+    live = t_all < T
+    t, sl = t_all[live], (w % slices)[live]
+    rep.access(tag, "token_rank_slot", t[:, None] * R + np.minimum(LANE, R - 1)[None, :], "load")
+    at = t[:, None] * k + np.minimum(LANE, k - 1)[None, :]
+    rep.access(tag, "topk_ids", at, "load")
+    rep.access(tag, "pair_row", at, "load")
+    cols = sl[:, None] * (V * W) + np.arange(V * W)[None, :]
+    rep.access(tag, "hidden", (t[:, None] * nvec + np.minimum(cols, nvec - 1)).ravel(), "load")
+    stored = np.arange(nvec, dtype=np.int64)  # every column < nvec of some slice
+    tt = np.arange(T, dtype=np.int64)
+    slots = lay["token_rank_slot"].astype(np.int64)[:T]
+    ok_r = (slots >= 0) & (slots < c.cap_rank)
+    rep.access(tag, "rank_src_token", slots[ok_r], "store")
+    rep.access(tag, "rank_buf", rows_cols(slots[ok_r], stored, nvec), "store")
+    e = np.asarray(ids, np.int64)[:T]
+    valid = (e >= 0) & (e < E)
+    r = np.where(valid, e // m, 0)
+    copy = np.take_along_axis(slots, r, axis=1) if R > 0 else r
+    here = valid & (copy >= 0) & (copy < c.cap_rank)
+    p = np.where(here, lay["pair_row"].astype(np.int64)[:T], -1)
+    ok_p = here & (p >= 0) & (p < c.cap_expert)
+    rep.access(tag, "expert_src_pair", p[ok_p], "store")
+    rep.access(tag, "expert_buf", rows_cols(p[ok_p], stored, nvec), "store")
+    del tt
+
+
+def dispatch_rows(c: Case, ids: np.ndarray, lay: dict | None = None) -> Report:
+    """moe_dispatch past the one-launch form: the layout, then
+    pack_expand_rows on the oracle's layout (or `lay`, any contents)."""
+    rep = Report()
+    if lay is None:
+        lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
+    model_layout(c, rep)
+    model_pack_expand(c, lay, ids, rep)
+    return rep
 
 
 SMALL_BATCH = 256

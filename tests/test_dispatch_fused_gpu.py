@@ -1,9 +1,10 @@
 """moe_dispatch, the whole dispatch in one call, against the oracle: its
 one-launch form (unpadded runs; up to 256 tokens with k in 1, 2, 4, 6, 8, up
-to 64 with another k; one or four tokens per lane) and the three calls it
-makes otherwise. The bar is the one of the three separate calls: bit-exact layout,
-rows, source ids and error words, canary rows past every cap untouched, and
-the combine on its pair rows bit-exact."""
+to 64 with another k; one or four tokens per lane) and, past it, the layout
+followed by one pack-and-permute kernel (the testing hook switches both off,
+for the three calls). The bar is the one of the three separate calls:
+bit-exact layout, rows, source ids and error words, canary rows past every cap
+untouched, and the combine on its pair rows bit-exact."""
 import sys
 
 import numpy as np
@@ -38,10 +39,10 @@ def check(hid, ids, wts, E, R, y, what, **kw):
     compare(gpu, ref, what)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
 def test_workloads(name):
     """decode (64 tokens) and tiny (256 tokens, k = 2) take the one-launch
-    form, prefill the three calls."""
+    form, prefill, skew and adv the layout and the pack-and-permute kernel."""
     w = synth.WORKLOADS[name]
     say(f"[dispatch] {w.describe()}")
     ids, wts = synth.routing(w)
@@ -105,43 +106,85 @@ def test_small_batches_undersized(s):
           cap_rank=cr, cap_expert=ce, block=c["block"])
 
 
-@pytest.mark.parametrize("T,k,align", [(64, 4, 16), (257, 4, 1), (300, 2, 1), (65, 3, 1),
-                                        (40, 4, 128)])
-def test_three_call_form(T, k, align):
+@pytest.mark.parametrize("T,k,align,block", [
+    (64, 4, 16, 0), (257, 4, 1, 0), (300, 2, 1, 0), (65, 3, 1, 0), (40, 4, 128, 0),
+    (2000, 6, 1, 0), (1500, 16, 1, 0), (3000, 8, 128, 0), (1200, 5, 1, 24), (700, 2, 1, 1)])
+def test_pack_and_permute_form(T, k, align, block):
     """Past the one-launch form (more than 256 tokens, more than 64 with
-    another k, or padded runs) the three calls."""
-    rng = np.random.default_rng(T + align)
+    another k, or padded runs): the layout, then pack and permute in one
+    kernel, with plain, padded and blocked runs (a block of 24 rows
+    overflows at this size, one of 1 row always)."""
+    rng = np.random.default_rng(T + align + block)
     E, R, H = 64, 8, 256
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
     wts = rng.random((T, k)).astype(np.float32)
     hid = synth.normal_bf16(7, 0, T * H).reshape(T, H)
     y = synth.expert_out_slots(7, E, H, ids)
-    say(f"[dispatch three calls] T={T} k={k} align={align}")
-    check(hid, ids, wts, E, R, y, f"T={T} k={k} align={align}", align=align)
+    say(f"[dispatch pack+permute] T={T} k={k} align={align} block={block}")
+    check(hid, ids, wts, E, R, y, f"T={T} k={k} align={align} block={block}", align=align,
+          block=block)
+
+
+def large_case(s: int):
+    """A random batch past the one-launch form: T from 65 to 5000, R up to 64,
+    E up to 1024, k up to 16, plain, padded or blocked runs."""
+    rng = np.random.default_rng(41000 + s)
+    R = int(rng.choice([1, 2, 4, 8, 16, 33, 64]))
+    E = R * int(rng.integers(1, 1024 // R + 1))
+    k = int(rng.integers(1, min(16, E) + 1))
+    T = int(rng.choice([257, 1023, 1024, 1025, int(rng.integers(65, 5001))]))
+    H = 8 * int(rng.integers(1, 200))
+    kind = str(rng.choice(["plain", "plain", "align", "block"]))
+    align = int(rng.choice([2, 16, 128])) if kind == "align" else 1
+    block = int(rng.integers(1, 3 * max(1, T * k // E) + 2)) if kind == "block" else 0
+    ids = pins.rand_ids(rng, T, E, k, p_neg=float(rng.choice([0.0, 0.1])),
+                        p_dup=0.1 if k > 1 else 0.0, p_bad=float(rng.choice([0.0, 0.02])))
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(s, 5, T * H).reshape(T, H)
+    return dict(T=T, H=H, E=E, R=R, k=k, align=align, block=block, ids=ids, wts=wts, hid=hid,
+                rng=rng)
+
+
+@pytest.mark.parametrize("s", range(48))
+def test_large_batches(s):
+    """Random batches through the layout and the pack-and-permute kernel,
+    every third one with caps below the worst case."""
+    c = large_case(s)
+    kw = dict(align=c["align"], block=c["block"])
+    if s % 3 == 2:
+        shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], c["align"], c["block"])
+        kw.update(cap_rank=int(c["rng"].integers(0, shape.cap_rank + 1)),
+                  cap_expert=int(c["rng"].integers(0, shape.cap_expert + 1)))
+    say(f"[dispatch large] s={s} T={c['T']} H={c['H']} E={c['E']} R={c['R']} k={c['k']} "
+        f"align={c['align']} block={c['block']} caps {kw.get('cap_rank')}/{kw.get('cap_expert')}")
+    y = synth.expert_out_slots(s, c["E"], c["H"], c["ids"])
+    check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"large {s}", **kw)
 
 
 def test_one_launch_equals_three_calls():
     """The same inputs through both forms (the testing hook switches the one
-    launch off): every output identical, repeated calls included."""
+    launch and the pack-and-permute kernel off): every output identical,
+    repeated calls included."""
     dev = torch.device("cuda:0")
-    for s in range(12):
-        c = small_case(500 + s)
+    cases = [small_case(500 + s) for s in range(12)] + [large_case(600 + s) for s in range(8)]
+    for s, c in enumerate(cases):
         T, H, E, R, k, block = c["T"], c["H"], c["E"], c["R"], c["k"], c["block"]
-        say(f"[dispatch forms] s={500 + s} T={T} E={E} R={R} k={k} block={block}")
+        align = c.get("align", 1)
+        say(f"[dispatch forms] case {s} T={T} E={E} R={R} k={k} align={align} block={block}")
         hid_d = staging.rows_to_device(c["hid"], dev)
         ids_d = torch.from_numpy(c["ids"]).to(dev)
         res = []
         for fused in (1, 0, 1):
             old = moe.lib().moe_testing_set_dispatch_fused(fused)
             try:
-                b = moe.Buffers(moe.Shape(T, H, E, R, k, 1, block), dev)
+                b = moe.Buffers(moe.Shape(T, H, E, R, k, align, block), dev)
                 b.rank_buf.fill_(3)
                 b.expert_buf.fill_(3)
                 b.rank_src_token.fill_(-3)
                 b.expert_src_pair.fill_(-3)
                 moe.dispatch_all(hid_d, ids_d, E, R, b.layout_dict(), b.rank_buf,
                                  b.rank_src_token, b.expert_buf, b.expert_src_pair,
-                                 block=block, workspace=b.workspace, err=b.err)
+                                 align=align, block=block, workspace=b.workspace, err=b.err)
                 torch.cuda.synchronize()
             finally:
                 moe.lib().moe_testing_set_dispatch_fused(old)
@@ -153,7 +196,7 @@ def test_one_launch_equals_three_calls():
                 a, w = v, other[key]
                 if a.dtype == torch.bfloat16:
                     a, w = a.view(torch.int16), w.view(torch.int16)
-                assert torch.equal(a, w), f"s={500 + s}: {key} differs between the forms"
+                assert torch.equal(a, w), f"case {s}: {key} differs between the forms"
 
 
 def test_graph_decode_step():

@@ -150,6 +150,32 @@ def test_dispatch_quantised_one_launch():
                          f"q small batch {s} lpb {lpb} caps {cr}/{ce}")
 
 
+@pytest.mark.parametrize("vec", [1, 2, 16])
+def test_dispatch_pack_expand(vec, monkeypatch):
+    """moe_dispatch past the one-launch form (layout, then pack and permute in
+    one kernel): the whole-path random shapes (seeds run on the GPU and
+    beyond), the workloads, undersized caps and arbitrary index arrays, for
+    the kernel's vec4 per lane and two other widths."""
+    monkeypatch.setattr(lm, "EXPAND_VEC", vec)
+    rng = np.random.default_rng(13)
+    for s in list(range(0, 96)) + list(range(1000, 1100)):
+        c = rs.draw(s)
+        ids, _, _ = rs.inputs(c)
+        case = case_of(c)
+        assert_clean(lm.dispatch_rows(case, ids), f"seed {s}")
+        lay, _ = lm.arbitrary_layout(rng, case)
+        assert_clean(lm.dispatch_rows(case, ids, lay=lay), f"seed {s} arbitrary")
+        cr = int(rng.integers(0, case.cap_rank + 1))
+        ce = int(rng.integers(0, case.cap_expert + 1))
+        c2 = lm.Case(case.T, case.H, case.E, case.R, case.k, case.align, case.block,
+                     cap_rank=cr, cap_expert=ce)
+        assert_clean(lm.dispatch_rows(c2, ids), f"seed {s} caps {cr}/{ce}")
+    for name in ("prefill", "skew", "adv"):
+        w = synth.WORKLOADS[name]
+        ids, _ = synth.routing(w)
+        assert_clean(lm.dispatch_rows(lm.Case(w.T, w.H, w.E, w.R, w.k), ids), name)
+
+
 def test_model_finds_the_earlier_permute_reads():
     """The unclamped source-token load of an earlier permute reads past
     cap_rank for a grid rounded up past the last row; the model says so."""

@@ -1,7 +1,7 @@
 """Seeded random shapes through the whole path, against the oracle: the
 layout (in the form forced for the case), pack, permute and combine with plain,
 padded and masked expert layouts, the two-stage combine, and the MXFP8 / MXFP4
-dispatch. Every shape parameter is drawn (T around the 256-token tile size and
+dispatch, and the one-call moe_dispatch. Every shape parameter is drawn (T around the 256-token tile size and
 up to a few thousand, H any multiple of 8, R from 1 to 64, E up to 1024, k up
 to 16, -1 / duplicate / out-of-range ids), so the cases reach corners that
 the hand-picked shapes do not name. Sizes stay small enough for the oracle to
@@ -101,6 +101,22 @@ def test_random_shape_one_stage(c):
     ref = run_oracle(hid, ids, wts, c["E"], c["R"], y, gpu["cap_rank"], gpu["cap_expert"],
                      align=c["align"], block=c["block"])
     compare(gpu, ref, f"random {c}")
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"s{c['seed']}" for c in CASES])
+def test_random_shape_dispatch(c):
+    """The same cases with layout, pack and permute through the one call
+    moe_dispatch (one launch up to 256 tokens, else the layout and one
+    pack-and-permute kernel)."""
+    say(f"[random moe_dispatch] {c}")
+    ids, wts, hid = inputs(c)
+    y = synth.expert_out_slots(c["seed"], c["E"], c["H"], ids)
+    with layout_form(c["form"], c["match"]):
+        gpu = run_gpu(hid, ids, wts, c["E"], c["R"], y, align=c["align"], block=c["block"],
+                      whole_dispatch=True)
+    ref = run_oracle(hid, ids, wts, c["E"], c["R"], y, gpu["cap_rank"], gpu["cap_expert"],
+                     align=c["align"], block=c["block"])
+    compare(gpu, ref, f"random moe_dispatch {c}")
 
 
 TWO_STAGE = [c for c in CASES if c["align"] == 1 and c["block"] == 0][:48]
