@@ -1545,6 +1545,67 @@ __device__ __forceinline__ void store_part(int fmt, void* rows, uint8_t* scales,
     *reinterpret_cast<uint32_t*>(scales + row * (nvec / lpb) + c / lpb) = sw;
 }
 
+// pack_expand_rows for the wire formats (moe_dispatch_quantised past the
+// one-launch form): one wave per (token, 1 KiB of the row) quantises its part
+// once, by the rules of pack_rows_mx, and stores the codes and scales to every
+// copy and every pair row, under the same guards and error flags. Rows of a
+// multiple of 512 values: every lane has a column.
+template <int kFmt>
+__global__ __launch_bounds__(kBlock) void pack_expand_q(
+    const vec4* hidden, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ token_rank_slot, const int32_t* __restrict__ pair_row,
+    const int32_t* __restrict__ expert_counts, const int32_t* __restrict__ expert_offsets,
+    uint8_t* rank_q, uint8_t* rank_scale, int32_t* __restrict__ rank_src_token,
+    uint8_t* expert_q, uint8_t* expert_scale, int32_t* __restrict__ expert_src_pair, int T,
+    int E, int R, int k, float inv_m, int block, int nvec, int groups, int pad_waves,
+    int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
+  static_assert(kFmt != kWireBf16, "bf16 rows take pack_expand_rows");
+  const int lane = lane_id();
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (gw < pad_waves) {
+    mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
+    return;
+  }
+  const int64_t w = gw - pad_waves;
+  const int t = int(w / groups);
+  const int g = int(w - (int64_t)t * groups);
+  if (t >= T) return;
+  const int c = g * kWave + lane;
+  const int slot_any = token_rank_slot[(int64_t)t * R + min(lane, R - 1)];
+  const int e_any = ids[(int64_t)t * k + min(lane, k - 1)];
+  const int pr_any = pair_row[(int64_t)t * k + min(lane, k - 1)];
+  const vec4 v = load_row<false>(hidden + (int64_t)t * nvec + c);
+  const int slot = lane < R ? slot_any : -1;
+  const bool ok_r = slot >= 0 && slot < cap_rank;
+  const int e = lane < k ? e_any : -1;
+  const bool valid = uint32_t(e) < uint32_t(E);
+  const int copy = __shfl(slot, valid ? rank_of(e, inv_m) : 0, kWave);
+  const bool here = valid && copy >= 0 && copy < cap_rank;
+  const int p = here ? pr_any : -1;
+  const bool ok_p = here && p >= 0 && p < cap_expert;
+  if (g == 0) {
+    if (__ballot(slot >= 0 && !ok_r) && lane == 0) flag_error(err_word, MOE_ERRBIT_RANK_CAP);
+    if (__ballot(here && !ok_p) && lane == 0) flag_error(err_word, MOE_ERRBIT_EXPERT_CAP);
+    if (ok_r) rank_src_token[slot] = t;
+    if (ok_p) expert_src_pair[p] = t * k + lane;
+  }
+  uint2 code;
+  uint32_t sw;
+  quantise_lane(kFmt, v, code, sw);
+  uint64_t d = __ballot(ok_r);
+  while (d) {
+    const int which = __ffsll((unsigned long long)d) - 1;
+    d &= d - 1;
+    store_part(kFmt, rank_q, rank_scale, read_lane(slot, which), c, nvec, v, code, sw);
+  }
+  d = __ballot(ok_p);
+  while (d) {
+    const int which = __ffsll((unsigned long long)d) - 1;
+    d &= d - 1;
+    store_part(kFmt, expert_q, expert_scale, read_lane(p, which), c, nvec, v, code, sw);
+  }
+}
+
 template <int K, int kRB, int TPL, int kFmt>
 __global__ __launch_bounds__(kBlock) void dispatch_small(
     const vec4* hidden, const int32_t* __restrict__ ids, int T, int E, int R, int k, int block,
@@ -2720,6 +2781,28 @@ int moe_dispatch_quantised(const moe_shape_t* shape, int format, const uint16_t*
                                expert_offsets, token_rank_slot, pair_row, workspace,
                                workspace_bytes, err_word, stream);
   if (st != MOE_OK) return st;
+  const int groups = sh.H / 512;  // 1 KiB of bf16 per wave
+  const int pad_waves = padded && cap_expert > 0 ? sh.E : 0;
+  // (an empty batch takes the permute, for the padding marks alone)
+  if (sh.T > 0 && g_dispatch_fused && pad_waves + int64_t(sh.T) * groups <= INT32_MAX) {
+    const dim3 grid(blocks_for(pad_waves + int64_t(sh.T) * groups));
+    const float inv_m = float(1.0 / double(sh.E / sh.R));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const vec4* hid = reinterpret_cast<const vec4*>(hidden);
+#define MOE_EXPAND_Q(F)                                                                          \
+  MOE_LAUNCH((pack_expand_q<F>), grid, dim3(kBlock), 0, hs, hid, topk_ids, token_rank_slot,      \
+             pair_row, expert_counts, expert_offsets, rank_q, rank_scale, rank_src_token,         \
+             expert_q, expert_scale, expert_src_pair, sh.T, sh.E, sh.R, sh.k, inv_m, sh.block,    \
+             sh.H / 8, groups, pad_waves, cap_rank, cap_expert, err_word)
+    if (format == MOE_WIRE_MXFP8)
+      MOE_EXPAND_Q(kWireMxfp8);
+    else if (format == MOE_WIRE_MXFP4)
+      MOE_EXPAND_Q(kWireMxfp4);
+    else
+      MOE_EXPAND_Q(kWireNvfp4);
+#undef MOE_EXPAND_Q
+    return launch_status();
+  }
   const int bits = format == MOE_WIRE_MXFP8 ? 8 : 4;
   const bool e4m3 = format == MOE_WIRE_NVFP4;
   st = pack_mx_impl(bits, e4m3, shape, hidden, token_rank_slot, rank_q, rank_scale,

@@ -509,24 +509,32 @@ def expand_tiling(nvec: int):
     return V, cdiv(nvec, V * W)
 
 
-def model_pack_expand(c: Case, lay: dict, ids: np.ndarray, rep: Report):
+def model_pack_expand(c: Case, lay: dict, ids: np.ndarray, rep: Report, lpb: int = 0):
     """pack_expand_rows (moe_dispatch past the one-launch form, after the
     layout): padding waves, then one wave per (token, slice of V*64 vec4).
     Every index array is read as the layout left it, whatever it holds: a
     copy is stored when its slot is inside the rank buffer, a pair when its
     expert is valid, the slot of its rank is inside the rank buffer and its
-    row inside the expert buffer."""
+    row inside the expert buffer. lpb > 0: pack_expand_q (the wire formats,
+    one vec4 per lane, lpb vec4 per scale block): a row's codes are one
+    element per vec4, its scales one word per four blocks, as in
+    model_dispatch_small."""
     T, E, R, k, nvec = c.T, c.E, c.R, c.k, c.nvec
     m = E // R
-    tag = "pack_expand_rows"
+    tag = "pack_expand_q" if lpb else "pack_expand_rows"
+    sw = 0
+    if lpb:
+        assert nvec % W == 0, "the wire formats take rows of a multiple of 512 values"
+        sw = nvec // (4 * lpb)
     for name, n in (("hidden", T * nvec), ("topk_ids", T * k), ("token_rank_slot", T * R),
                     ("pair_row", T * k), ("expert_counts", E), ("expert_offsets", E + 1),
                     ("rank_buf", c.cap_rank * nvec), ("rank_src_token", c.cap_rank),
-                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert)):
+                    ("expert_buf", c.cap_expert * nvec), ("expert_src_pair", c.cap_expert),
+                    ("rank_scale", c.cap_rank * sw), ("expert_scale", c.cap_expert * sw)):
         rep.buf(name, n)
     if T == 0:
         return
-    V, slices = expand_tiling(nvec)
+    V, slices = (1, nvec // W) if lpb else expand_tiling(nvec)
     padded = c.align > 1 or c.block > 0
     pad_waves = E if padded and c.cap_expert > 0 else 0
     assert pad_waves + T * slices <= INT32_MAX
@@ -549,6 +557,9 @@ def model_pack_expand(c: Case, lay: dict, ids: np.ndarray, rep: Report):
     ok_r = (slots >= 0) & (slots < c.cap_rank)
     rep.access(tag, "rank_src_token", slots[ok_r], "store")
     rep.access(tag, "rank_buf", rows_cols(slots[ok_r], stored, nvec), "store")
+    scol = np.arange(0, nvec, 4 * lpb, dtype=np.int64) // (4 * lpb) if lpb else None
+    if lpb:
+        rep.access(tag, "rank_scale", rows_cols(slots[ok_r], scol, sw), "store")
     e = np.asarray(ids, np.int64)[:T]
     valid = (e >= 0) & (e < E)
     r = np.where(valid, e // m, 0)
@@ -558,17 +569,20 @@ def model_pack_expand(c: Case, lay: dict, ids: np.ndarray, rep: Report):
     ok_p = here & (p >= 0) & (p < c.cap_expert)
     rep.access(tag, "expert_src_pair", p[ok_p], "store")
     rep.access(tag, "expert_buf", rows_cols(p[ok_p], stored, nvec), "store")
+    if lpb:
+        rep.access(tag, "expert_scale", rows_cols(p[ok_p], scol, sw), "store")
     del tt
 
 
-def dispatch_rows(c: Case, ids: np.ndarray, lay: dict | None = None) -> Report:
-    """moe_dispatch past the one-launch form: the layout, then
-    pack_expand_rows on the oracle's layout (or `lay`, any contents)."""
+def dispatch_rows(c: Case, ids: np.ndarray, lay: dict | None = None, lpb: int = 0) -> Report:
+    """moe_dispatch (lpb = 0) or moe_dispatch_quantised past the one-launch
+    form: the layout, then pack_expand_rows / pack_expand_q on the oracle's
+    layout (or `lay`, any contents)."""
     rep = Report()
     if lay is None:
         lay = oracle.layout(ids, c.E, c.R, align=c.align, block=c.block)
     model_layout(c, rep)
-    model_pack_expand(c, lay, ids, rep)
+    model_pack_expand(c, lay, ids, rep, lpb)
     return rep
 
 

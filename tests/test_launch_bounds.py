@@ -176,6 +176,26 @@ def test_dispatch_pack_expand(vec, monkeypatch):
         assert_clean(lm.dispatch_rows(lm.Case(w.T, w.H, w.E, w.R, w.k), ids), name)
 
 
+def test_dispatch_quantised_pack_expand():
+    """moe_dispatch_quantised past the one-launch form: codes and scale words
+    of pack_expand_q for the MX formats (4 vec4 per block) and the 16-value
+    rows (2), on the MX random shapes, arbitrary index arrays and undersized
+    caps."""
+    rng = np.random.default_rng(17)
+    for s in list(range(200, 224)) + list(range(10000, 10060)):
+        c = rs.draw(s, mx=True)
+        ids, _, _ = rs.inputs(c)
+        case = case_of(c)
+        for lpb in (4, 2):
+            assert_clean(lm.dispatch_rows(case, ids, lpb=lpb), f"seed {s} lpb {lpb}")
+            lay, _ = lm.arbitrary_layout(rng, case)
+            assert_clean(lm.dispatch_rows(case, ids, lay=lay, lpb=lpb), f"seed {s} arbitrary")
+            c2 = lm.Case(case.T, case.H, case.E, case.R, case.k, case.align, case.block,
+                         cap_rank=int(rng.integers(0, case.cap_rank + 1)),
+                         cap_expert=int(rng.integers(0, case.cap_expert + 1)))
+            assert_clean(lm.dispatch_rows(c2, ids, lpb=lpb), f"seed {s} caps")
+
+
 def test_model_finds_the_earlier_permute_reads():
     """The unclamped source-token load of an earlier permute reads past
     cap_rank for a grid rounded up past the last row; the model says so."""

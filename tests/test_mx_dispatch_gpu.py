@@ -219,7 +219,8 @@ def test_mx_rejects_rows_not_a_multiple_of_512():
 
 # The quantised dispatch in one call (moe_dispatch_quantised): a decode-sized
 # unpadded batch takes the one-launch form (quantise in the mover waves), any
-# other batch the three calls above; both held to the same bar.
+# other batch the layout and one quantise-pack-and-permute kernel; the testing
+# hook switches both off for the three calls above. All held to the same bar.
 
 def small_mx_case(s: int):
     """A random decode-sized case for the quantised one-launch form: T up to 256
@@ -250,10 +251,11 @@ def small_mx_case(s: int):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "skew", "adv"])
 def test_dispatch_quantised_workloads(name, fmt):
-    """decode (64 tokens) and tiny (256 tokens, k = 2) in one launch, prefill
-    through the three calls."""
+    """decode (64 tokens) and tiny (256 tokens, k = 2) in one launch, prefill,
+    skew and adv through the layout and the quantise-pack-and-permute
+    kernel."""
     w = synth.WORKLOADS[name]
     say(f"[{fmt} dispatch] {w.describe()}")
     hid = synth.hidden(w)
@@ -321,22 +323,54 @@ def test_dispatch_quantised_nvfp4_every_block_max():
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("T,k,align", [(64, 4, 16), (257, 4, 1), (65, 3, 1), (40, 4, 128)])
-def test_dispatch_quantised_three_call_form(T, k, align, fmt):
-    rng = np.random.default_rng(T + align + 5)
+@pytest.mark.parametrize("T,k,align,block", [(64, 4, 16, 0), (257, 4, 1, 0), (65, 3, 1, 0),
+                                              (40, 4, 128, 0), (2000, 6, 1, 0),
+                                              (1500, 16, 1, 0), (1200, 5, 1, 24),
+                                              (700, 2, 1, 1)])
+def test_dispatch_quantised_pack_and_permute_form(T, k, align, block, fmt):
+    """Past the one-launch form: plain, padded and blocked runs (a block of
+    24 rows overflows at this size, one of 1 row always), random 16-bit
+    patterns in a third of the rows."""
+    rng = np.random.default_rng(T + align + block + 5)
     E, R, H = 64, 8, 1024
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1)
     hid = synth.normal_bf16(9, 0, T * H).reshape(T, H)
-    say(f"[{fmt} dispatch three calls] T={T} k={k} align={align}")
-    check(hid, ids, E, R, f"q T={T} k={k} align={align}", fmt=fmt, align=align,
+    hid[::3] = rng.integers(0, 65536, (len(hid[::3]), H), dtype=np.uint16)
+    say(f"[{fmt} dispatch pack+permute] T={T} k={k} align={align} block={block}")
+    check(hid, ids, E, R, f"q T={T} k={k} align={align} block={block}", fmt=fmt, align=align,
+          block=block, whole_dispatch=True)
+
+
+@pytest.mark.parametrize("s", range(24))
+def test_dispatch_quantised_large_undersized(s):
+    """Caps below the worst case past the one-launch form."""
+    rng = np.random.default_rng(73000 + s)
+    T = int(rng.integers(257, 3000))
+    R = int(rng.choice([1, 4, 8, 33, 64]))
+    E = R * int(rng.integers(1, 1024 // R + 1))
+    k = int(rng.integers(1, min(16, E) + 1))
+    H = 512 * int(rng.integers(1, 5))
+    fmt = FORMATS[s % 3]
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.1, p_dup=0.1 if k > 1 else 0.0, p_bad=0.02)
+    hid = synth.normal_bf16(s, 4, T * H).reshape(T, H)
+    shape = moe.Shape(T, H, E, R, k)
+    cr = int(rng.integers(0, shape.cap_rank + 1))
+    ce = int(rng.integers(0, shape.cap_expert + 1))
+    say(f"[{fmt} dispatch large caps] s={s} T={T} H={H} E={E} R={R} k={k} caps {cr}/{ce}")
+    check(hid, ids, E, R, f"q large caps {s}", fmt=fmt, cap_rank=cr, cap_expert=ce,
           whole_dispatch=True)
 
 
 def test_dispatch_quantised_one_launch_equals_three_calls():
     """Both forms on the same inputs (the testing hook switches the one launch
-    off): every output byte identical."""
-    for s in range(12):
+    and the quantise-pack-and-permute kernel off): every output byte
+    identical, small and larger batches."""
+    for s in range(16):
         c = small_mx_case(800 + s)
+        if s >= 12:  # larger batches: the pack-and-permute kernel against the three calls
+            c["T"] = T = 300 + 700 * (s - 12)
+            c["ids"] = pins.rand_ids(c["rng"], T, c["E"], c["k"], p_neg=0.1)
+            c["hid"] = synth.normal_bf16(s, 6, T * c["H"]).reshape(T, c["H"])
         say(f"[dispatch q forms] s={800 + s} {c['fmt']} T={c['T']} E={c['E']} R={c['R']} "
             f"k={c['k']} block={c['block']}")
         res = []

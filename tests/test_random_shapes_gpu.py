@@ -144,3 +144,15 @@ def test_random_shape_mx(c, fmt):
     with layout_form(c["form"], c["match"]):
         check(hid, ids, c["E"], c["R"], f"random {fmt} {c}", fmt=fmt, align=c["align"],
               block=c["block"])
+
+
+@pytest.mark.parametrize("c", MX_CASES, ids=[f"s{c['seed']}" for c in MX_CASES])
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
+def test_random_shape_mx_dispatch(c, fmt):
+    """The same cases through the one call moe_dispatch_quantised."""
+    from test_mx_dispatch_gpu import check
+    say(f"[random {fmt} moe_dispatch_quantised] {c}")
+    ids, _, hid = inputs(c)
+    with layout_form(c["form"], c["match"]):
+        check(hid, ids, c["E"], c["R"], f"random {fmt} one call {c}", fmt=fmt,
+              align=c["align"], block=c["block"], whole_dispatch=True)
