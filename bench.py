@@ -132,15 +132,28 @@ def measured_traffic(kernel: str, workload: str):
 
 
 OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "combine_rows",
-               "dispatch_small")
+               "dispatch_small", "pack_expand_rows", "pack_expand_q")
 
 
 # The passes of a default bench run, in order, in units of steps: each step
-# launches every library kernel of the path once. `sets` steps come first
-# (one dispatch per buffer set to place the expert outputs), then the
-# warm-up and six passes of `steps` steps each.
+# of the four calls launches every library kernel of the path once. `sets`
+# steps come first (layout, pack and permute once per buffer set, to place the
+# expert outputs), then the warm-up and five passes of `steps` steps each, a
+# pass of `steps` steps through moe_dispatch (layout, pack_expand_rows,
+# combine) and the roofline pass.
 RUN_PASSES = ("placement", "warmup", "rotated", "warm", "after_write", "per_call", "cold",
-              "roofline")
+              "one_call", "roofline")
+
+
+def passes_of(kernel: str) -> tuple:
+    """The passes of a default bench run in which `kernel` is launched."""
+    if kernel.startswith("pack_expand"):
+        return ("one_call",)
+    if kernel.startswith(("pack_rows", "permute_rows")):
+        return tuple(p for p in RUN_PASSES if p != "one_call")
+    if kernel.startswith("combine_rows"):
+        return RUN_PASSES[1:]
+    return RUN_PASSES
 
 
 def trace_passes(trace_csv: str, steps: int, warmup: int, sets: int) -> dict:
@@ -161,17 +174,17 @@ def trace_passes(trace_csv: str, steps: int, warmup: int, sets: int) -> dict:
                 continue
             durs.setdefault(name, []).append(
                 (int(row["Dispatch_Id"]), (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3))
-    sizes = [sets, warmup] + [steps] * 6
+    size = dict(placement=sets, warmup=warmup)
     out = {}
     for name, d in durs.items():
         d.sort()
-        # the combine does not run in the placement dispatches
-        sz = sizes if len(d) == sum(sizes) else [0] + sizes[1:]
+        passes = passes_of(name)
+        sz = [size.get(p, steps) for p in passes]
         if len(d) != sum(sz):
-            out[name] = {"error": f"{len(d)} dispatches, expected {sum(sizes)}"}
+            out[name] = {"error": f"{len(d)} dispatches, expected {sum(sz)}"}
             continue
         res, i = {}, 0
-        for pas, n in zip(RUN_PASSES, sz):
+        for pas, n in zip(passes, sz):
             v = [x for _, x in d[i:i + n]]
             i += n
             if v:

@@ -336,7 +336,8 @@ def dispatch_all(hidden, topk_ids, E: int, R: int, out: dict, rank_buf, rank_src
                  workspace: torch.Tensor | None = None, err=None) -> None:
     """moe_dispatch: layout, pack and permute in one call (one kernel launch
     for up to 256 tokens with align = 1 and k in {1, 2, 4, 6, 8}, up to 64
-    for another k), into the caller's tensors: `out`
+    for another k; else the layout and one pack-and-permute kernel), into
+    the caller's tensors: `out`
     holds the layout's outputs (the keys of layout()), rank_buf [cap_rank, H],
     rank_src_token [cap_rank], expert_buf [cap_expert, H], expert_src_pair
     [cap_expert]."""
@@ -406,8 +407,9 @@ def dispatch_all_mx(fmt, hidden, topk_ids, E: int, R: int, out: dict, rank_q, ra
                     rank_src_token, expert_q, expert_scale, expert_src_pair, *, align: int = 1,
                     block: int = 0, workspace: torch.Tensor | None = None, err=None) -> None:
     """moe_dispatch_quantised: layout, quantise-and-pack and permute of the
-    quantised rows in one call (one kernel launch for a decode-sized batch, as
-    dispatch_all), into the caller's tensors: `out` holds the layout's outputs,
+    quantised rows in one call (one kernel launch for a decode-sized batch, else
+    the layout and one quantise-pack-and-permute kernel, as dispatch_all), into
+    the caller's tensors: `out` holds the layout's outputs,
     rank_q [cap_rank, H*bits/8] and rank_scale [cap_rank, H/block] (uint8),
     rank_src_token [cap_rank], expert_q / expert_scale / expert_src_pair
     likewise with cap_expert rows."""

@@ -227,7 +227,10 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
  * kernels for decoding). In that launch every wave works out the rows of its
  * own token from the ids alone, as a low-latency sender places its rows
  * without asking anyone ([A2A] sec 4.1), so nothing waits for the counts.
- * Otherwise the three calls are made in turn on `stream`.
+ * Otherwise the layout runs as moe_dispatch_layout, then one kernel packs and
+ * permutes: each hidden row is read once and written to every copy and to
+ * every pair row the permute would write, so the packed rows are not read
+ * back (on one GPU nothing lies between the two, [A2A] sec 5.1 do_expand).
  *   Arguments: those of the three calls (hidden, topk_ids, the layout's
  *   outputs, rank_buf / rank_src_token / cap_rank, expert_buf /
  *   expert_src_pair / cap_expert, the layout workspace), with the same
@@ -235,7 +238,8 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
  *   launched, and an argument error launches nothing. The one-launch form
  *   needs no workspace. rank_buf holds every copy as after
  *   moe_dispatch_pack (the one-launch form streams it past the caches,
- *   since nothing reads it back there).
+ *   since nothing reads it back there). With padded or blocked runs the
+ *   padding rows of expert_src_pair are marked -1 as by the permute.
  */
 int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t* topk_ids,
                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
@@ -255,7 +259,9 @@ int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t
  * on the same arguments, with the same results bit for bit and the same error
  * bits; one kernel launch for a decode-sized batch exactly as moe_dispatch
  * (the wave quantises its part of the row once and writes the codes and
- * scales to every copy and every pair), otherwise the three calls in turn.
+ * scales to every copy and every pair), otherwise the layout and one kernel
+ * that quantises each part of a row once and writes its codes and scales to
+ * every copy and every pair row, the code rows not read back.
  *   format: MOE_WIRE_MXFP8, MOE_WIRE_MXFP4 or MOE_WIRE_NVFP4 (anything else
  *   is an argument error).
  *   The other arguments: those of the three calls, with their sizes,
@@ -455,9 +461,9 @@ int moe_testing_set_layout_match(int match);
 
 /*
  * Testing hook (not for production callers; process-wide; returns the
- * previous value): 1 (default) moe_dispatch runs a small batch as one launch
- * as described there; 0 it always makes the three calls. Both give the same
- * results.
+ * previous value): 1 (default) moe_dispatch and moe_dispatch_quantised run
+ * as described there (one launch, or the layout and one pack-and-permute
+ * kernel); 0 they always make the three calls. Both give the same results.
  */
 int moe_testing_set_dispatch_fused(int fused);
 

@@ -124,7 +124,9 @@ def test_counter_ingestion_and_stale_source_guard(tmp_path, monkeypatch):
 def test_trace_passes_split(tmp_path):
     """The per-pass split of a kernel trace: every library kernel's dispatches,
     in dispatch order, cut into the bench's passes (the combine has no
-    placement dispatches); a count that does not fit is reported, not split."""
+    placement dispatches, the permute none in the pass through moe_dispatch,
+    pack_expand_rows runs only there); a count that does not fit is reported,
+    not split."""
     steps, warmup, sets = 4, 2, 3
     path = tmp_path / "run_kernel_trace.csv"
     fields = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
@@ -139,10 +141,14 @@ def test_trace_passes_split(tmp_path):
 
     perm = "void (anonymous namespace)::permute_rows<10, false>(unsigned int const*, int)"
     comb = "void (anonymous namespace)::combine_rows<5, false>(unsigned int const*)"
-    sizes = dict(zip(bench.RUN_PASSES, [sets, warmup] + [steps] * 6))
-    for p_i, (pas, n) in enumerate(sizes.items()):
-        for _ in range(n):
-            add(perm, 10 + p_i)
+    expand = "void (anonymous namespace)::pack_expand_rows<1, false, false>(unsigned int const*)"
+    size = dict(placement=sets, warmup=warmup)
+    for p_i, pas in enumerate(bench.RUN_PASSES):
+        for _ in range(size.get(pas, steps)):
+            if pas == "one_call":
+                add(expand, 50)
+            else:
+                add(perm, 10 + p_i)
             add("void at::native::fill_kernel<int>(int)", 1)
             if pas != "placement":
                 add(comb, 100 + p_i)
@@ -152,11 +158,16 @@ def test_trace_passes_split(tmp_path):
         w.writeheader()
         w.writerows(rows)
     out = bench.trace_passes(str(path), steps, warmup, sets)
-    assert set(out) == {"permute_rows<10, false>", "combine_rows<5, false>", "pack_rows<10>"}
+    assert set(out) == {"permute_rows<10, false>", "combine_rows<5, false>", "pack_rows<10>",
+                        "pack_expand_rows<1, false, false>"}
     for p_i, pas in enumerate(bench.RUN_PASSES):
-        assert out["permute_rows<10, false>"][pas]["mean_us"] == 10 + p_i
+        if pas != "one_call":
+            assert out["permute_rows<10, false>"][pas]["mean_us"] == 10 + p_i
         if pas != "placement":
             assert out["combine_rows<5, false>"][pas]["mean_us"] == 100 + p_i
     assert "placement" not in out["combine_rows<5, false>"]
+    assert "one_call" not in out["permute_rows<10, false>"]
+    assert out["pack_expand_rows<1, false, false>"] == {
+        "one_call": {"mean_us": 50.0, "min_us": 50.0, "max_us": 50.0, "n": steps}}
     assert out["permute_rows<10, false>"]["roofline"]["n"] == steps
     assert "error" in out["pack_rows<10>"]
