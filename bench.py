@@ -138,19 +138,20 @@ OUR_KERNELS = ("layout_count", "layout_tiles", "pack_rows", "permute_rows", "com
 # The passes of a default bench run, in order, in units of steps: each step
 # of the four calls launches every library kernel of the path once. `sets`
 # steps come first (layout, pack and permute once per buffer set, to place the
-# expert outputs), then the warm-up and five passes of `steps` steps each, a
-# pass of `steps` steps through moe_dispatch (layout, pack_expand_rows,
-# combine) and the roofline pass.
+# expert outputs), then the warm-up and five passes of `steps` steps each, two
+# passes of `steps` steps through moe_dispatch (layout, pack_expand_rows,
+# combine; cold, then rotated) and the roofline pass.
 RUN_PASSES = ("placement", "warmup", "rotated", "warm", "after_write", "per_call", "cold",
-              "one_call", "roofline")
+              "one_call_cold", "one_call", "roofline")
+ONE_CALL_PASSES = ("one_call_cold", "one_call")
 
 
 def passes_of(kernel: str) -> tuple:
     """The passes of a default bench run in which `kernel` is launched."""
     if kernel.startswith("pack_expand"):
-        return ("one_call",)
+        return ONE_CALL_PASSES
     if kernel.startswith(("pack_rows", "permute_rows")):
-        return tuple(p for p in RUN_PASSES if p != "one_call")
+        return tuple(p for p in RUN_PASSES if p not in ONE_CALL_PASSES)
     if kernel.startswith("combine_rows"):
         return RUN_PASSES[1:]
     return RUN_PASSES
@@ -474,14 +475,15 @@ class Rig:
         else:
             moe.combine_ranks(x.partial, b.token_rank_slot, s.E, s.k, x.out2, err=b.err)
 
-    def step(self, ev=None, evict=None, rotate: bool = True) -> None:
+    def step(self, ev=None, evict=None, rotate: bool = True, calls=None) -> None:
         """One pass, on the next buffer set if `rotate` (else on the current
         one again); with `ev` (events) records between the calls; with `evict`
         (a callable that enqueues a cache-evicting read) runs it before every
-        call, outside the events."""
+        call, outside the events. calls: the rig's path, or those given."""
         if rotate:
             self.rotate()
-        for i, c in enumerate(self.calls):
+        calls = self.calls if calls is None else calls
+        for i, c in enumerate(calls):
             if evict is not None:
                 evict()
             if ev is not None:
@@ -490,7 +492,7 @@ class Rig:
             if ev is not None and evict is not None:
                 ev[2 * i + 1].record(self.stream)
         if ev is not None and evict is None:
-            ev[len(self.calls)].record(self.stream)
+            ev[len(calls)].record(self.stream)
 
     def kernel_ms(self, call: str, n: int, rotate: bool = True) -> list:
         """Durations (ms) of the kernel that `call` launches, inside n whole
@@ -519,20 +521,22 @@ class Rig:
         torch.cuda.synchronize()
         return [a.elapsed_time(b) for a, b in pairs]
 
-    def per_call_ms(self, n: int, evict=None, rotate: bool = True) -> dict:
-        """Per-call durations (ms) over n steps."""
+    def per_call_ms(self, n: int, evict=None, rotate: bool = True, calls=None) -> dict:
+        """Per-call durations (ms) over n steps (of the rig's path, or of
+        `calls`)."""
         import torch
 
-        nc = len(self.calls)
+        calls = self.calls if calls is None else calls
+        nc = len(calls)
         nev = 2 * nc if evict is not None else nc + 1
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
-            self.step(evs[i], evict, rotate)
+            self.step(evs[i], evict, rotate, calls)
         torch.cuda.synchronize()
-        out = {c: [] for c in self.calls}
+        out = {c: [] for c in calls}
         for ev in evs:
-            for j, c in enumerate(self.calls):
+            for j, c in enumerate(calls):
                 a, b = (ev[2 * j], ev[2 * j + 1]) if evict is not None else (ev[j], ev[j + 1])
                 out[c].append(a.elapsed_time(b))
         return out
@@ -847,6 +851,7 @@ def main():
     log(f"timed {args.steps} steps after a 1 GiB write: {after_write_ms * 1e3:.1f} us/step")
     per_call_ms = rig.per_call_ms(args.steps)
     cold_ms = rig.per_call_ms(args.steps, evict, rotate=False)
+    one_cold_ms = rig.per_call_ms(args.steps, evict, rotate=False, calls=("dispatch", "combine"))
     del flush
     rig.check_err()
 
@@ -866,6 +871,7 @@ def main():
     one_call_ms = t_begin.elapsed_time(t_end) / args.steps
     rig.check_err()
     one_call_bytes = rig.nbytes["dispatch"] + rig.nbytes["combine"]
+    one_cold_step_ms = sum(float(np.mean(v)) for v in one_cold_ms.values())
     log(f"timed {args.steps} steps through moe_dispatch: {one_call_ms * 1e3:.1f} us/step")
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -897,7 +903,12 @@ def main():
                  "GB/s": round(one_call_bytes / (one_call_ms * 1e-3) / 1e9, 1),
                  "note": "moe_dispatch (the layout, then pack and permute in one kernel) and "
                          "moe_combine, rotating buffer sets: the same outputs, the packed rows "
-                         "not read back, so fewer algorithmic bytes (its own count)"}}
+                         "not read back, so fewer algorithmic bytes (its own count)"},
+             "one_call_dispatch_cold": {
+                 "us_per_step": round(one_cold_step_ms * 1e3, 2), "bytes": one_call_bytes,
+                 "GB/s": round(one_call_bytes / (one_cold_step_ms * 1e-3) / 1e9, 1),
+                 "note": "the same two calls, L2 and Infinity Cache evicted by a 1 GiB read "
+                         "before each (sum of per-call means)"}}
     # The dominant kernel's own duration: a third pass of whole steps (rotating
     # sets) in which the library records an event pair with the permute's
     # dispatch.

@@ -145,7 +145,7 @@ def test_trace_passes_split(tmp_path):
     size = dict(placement=sets, warmup=warmup)
     for p_i, pas in enumerate(bench.RUN_PASSES):
         for _ in range(size.get(pas, steps)):
-            if pas == "one_call":
+            if pas in bench.ONE_CALL_PASSES:
                 add(expand, 50)
             else:
                 add(perm, 10 + p_i)
@@ -161,13 +161,14 @@ def test_trace_passes_split(tmp_path):
     assert set(out) == {"permute_rows<10, false>", "combine_rows<5, false>", "pack_rows<10>",
                         "pack_expand_rows<1, false, false>"}
     for p_i, pas in enumerate(bench.RUN_PASSES):
-        if pas != "one_call":
+        if pas not in bench.ONE_CALL_PASSES:
             assert out["permute_rows<10, false>"][pas]["mean_us"] == 10 + p_i
         if pas != "placement":
             assert out["combine_rows<5, false>"][pas]["mean_us"] == 100 + p_i
     assert "placement" not in out["combine_rows<5, false>"]
     assert "one_call" not in out["permute_rows<10, false>"]
     assert out["pack_expand_rows<1, false, false>"] == {
-        "one_call": {"mean_us": 50.0, "min_us": 50.0, "max_us": 50.0, "n": steps}}
+        p: {"mean_us": 50.0, "min_us": 50.0, "max_us": 50.0, "n": steps}
+        for p in bench.ONE_CALL_PASSES}
     assert out["permute_rows<10, false>"]["roofline"]["n"] == steps
     assert "error" in out["pack_rows<10>"]

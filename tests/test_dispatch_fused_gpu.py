@@ -251,3 +251,64 @@ def test_graph_decode_step():
         assert torch.equal(g.rank_buf[:C].view(torch.int16), e.rank_buf[:C].view(torch.int16))
         assert torch.equal(g.expert_buf[:P].view(torch.int16), e.expert_buf[:P].view(torch.int16))
         assert torch.equal(g.expert_src_pair[:P], e.expert_src_pair[:P])
+
+
+@pytest.mark.parametrize("T,H,E,R,k,align", [(2000, 512, 64, 8, 6, 16), (10000, 64, 128, 8, 6, 1)])
+def test_graph_large_step(T, H, E, R, k, align):
+    """A larger step as moe_dispatch (the layout, in its two-launch form with
+    a workspace for the second shape, then the pack-and-permute kernel) and
+    moe_combine recorded in a HIP graph: every replay, on fresh inputs copied
+    into the captured tensors, equals an eager run."""
+    dev = torch.device("cuda:0")
+    shape = moe.Shape(T, H, E, R, k, align)
+    g, e = moe.Buffers(shape, dev), moe.Buffers(shape, dev)
+
+    def run(b, hid_d, ids_d, eo_d, wts_d):
+        moe.dispatch_all(hid_d, ids_d, E, R, b.layout_dict(), b.rank_buf, b.rank_src_token,
+                         b.expert_buf, b.expert_src_pair, align=align, workspace=b.workspace,
+                         err=b.err)
+        moe.combine(eo_d, b.pair_row, wts_d, E, R, b.out, err=b.err)
+
+    def inputs(seed):
+        rng = np.random.default_rng(seed)
+        ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
+        wts = rng.random((T, k)).astype(np.float32)
+        hid = synth.normal_bf16(seed, 0, T * H).reshape(T, H)
+        eo = synth.normal_bf16(seed, 1, shape.cap_expert * H).reshape(shape.cap_expert, H)
+        return hid, ids, wts, eo
+
+    say(f"[dispatch graph] T={T} H={H} E={E} R={R} k={k} align={align}")
+    hid, ids, wts, eo = inputs(60)
+    s_hid, s_ids = staging.rows_to_device(hid, dev), torch.from_numpy(ids).to(dev)
+    s_wts, s_eo = torch.from_numpy(wts).to(dev), staging.rows_to_device(eo, dev)
+    run(g, s_hid, s_ids, s_eo, s_wts)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(g, s_hid, s_ids, s_eo, s_wts)
+    for i in range(3):
+        hid, ids, wts, eo = inputs(61 + i)
+        s_hid.copy_(staging.rows_to_device(hid, dev))
+        s_ids.copy_(torch.from_numpy(ids).to(dev))
+        s_wts.copy_(torch.from_numpy(wts).to(dev))
+        s_eo.copy_(staging.rows_to_device(eo, dev))
+        g.err.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        e.err.zero_()
+        run(e, staging.rows_to_device(hid, dev), torch.from_numpy(ids).to(dev),
+            staging.rows_to_device(eo, dev), torch.from_numpy(wts).to(dev))
+        torch.cuda.synchronize()
+        P = int(e.expert_offsets[-1].item())
+        C = int(e.rank_offsets[-1].item())
+        for key in ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
+                    "token_rank_slot", "pair_row", "err"):
+            assert torch.equal(getattr(g, key), getattr(e, key)), f"replay {i}: {key}"
+        assert torch.equal(g.out.view(torch.int16), e.out.view(torch.int16)), f"replay {i}: out"
+        assert torch.equal(g.rank_buf[:C].view(torch.int16), e.rank_buf[:C].view(torch.int16))
+        assert torch.equal(g.rank_src_token[:C], e.rank_src_token[:C])
+        assert torch.equal(g.expert_src_pair[:P], e.expert_src_pair[:P])
+        # padding rows (source -1) carry no row: their contents are not written
+        rows = e.expert_src_pair[:P] >= 0
+        assert torch.equal(g.expert_buf[:P][rows].view(torch.int16),
+                           e.expert_buf[:P][rows].view(torch.int16)), f"replay {i}: expert rows"
