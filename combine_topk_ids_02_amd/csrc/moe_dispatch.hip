@@ -1449,9 +1449,9 @@ __global__ __launch_bounds__(kBlock) void pack_expand_rows(
 // kernel boundary between them, for the decode step, whose time is launches
 // and the waits between them. Every wave holds all T*k ids, TPL tokens per
 // lane (token u = 64q + lane in group q), and works out from them, with wave
-// ballots and wave sums, what it needs: as a low-latency sender decides where
-// each row goes without asking anyone ([A2A] sec 4.1), here for the rank
-// segments and the expert runs alike. Workgroup 0 writes the counts and
+// ballots, scalar popcounts and wave sums, what it needs: as a low-latency
+// sender decides where each row goes without asking anyone ([A2A] sec 4.1),
+// here for the rank segments and the expert runs alike. Workgroup 0 writes the counts and
 // offsets; with a blocked layout the next pad_waves = E waves mark one
 // expert's padding rows each (its count is a wave sum over the ids); every
 // other wave takes one (token, 1 KiB of the row), reads that part of the
@@ -1623,7 +1623,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   constexpr int fmt = kFmt;
   const int kk = K > 0 ? K : k;
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  // (read through a scalar register: the compiler does not know that the
+  // wave index is the same in every lane, and would keep the token, its
+  // rank set masks and every row number derived from them per lane)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const bool counter = blockIdx.x == 0;
   // Padding waves, then movers: a mover's token and 1 KiB group; its part of
   // the hidden row is requested first (clamped into the row), the ids right
@@ -1760,8 +1763,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   }
 
   // The token's pairs, in slot order: the run's first row (the valid ids
-  // below e, or e*block) plus the pairs of e before (t, j), counted in one
-  // wave sum (below e in the low 16 bits, equal before (t, j) in the high).
+  // below e, or e*block) plus the pairs of e before (t, j), each counted
+  // with one ballot per (token group, slot) and a scalar popcount, so the
+  // expert and the row stay uniform (scalar registers, scalar branches).
+  const uint64_t upto = below | (1ull << lt);  // lanes up to and including lt
   bool full = false;
   int my_row = -1;  // lane j: pair_row of slot j
 #pragma unroll
@@ -1770,23 +1775,25 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
 #pragma unroll
     for (int q = 0; q < TPL; ++q)
       if (q == qt) e = __builtin_amdgcn_readlane(idv[q][j], lt);
+    e = __builtin_amdgcn_readfirstlane(e);
     if (j >= kk || uint32_t(e) >= uint32_t(E)) continue;  // (no break: keeps the loop unrolled)
-    int n = 0;
+    int n_below = 0, rk = 0;
 #pragma unroll
     for (int q = 0; q < TPL; ++q) {
-      const int u = q * kWave + lane;
+      // (t, j) comes after every pair of earlier tokens and of lanes before
+      // lt, and after the pairs of token t itself in slots below j
+      const uint64_t before_t = q < qt ? ~0ull : (q == qt ? below : 0ull);
+      const uint64_t upto_t = q < qt ? ~0ull : (q == qt ? upto : 0ull);
 #pragma unroll
       for (int jj = 0; jj < KR; ++jj) {
         if (jj < kk) {
           const int x = idv[q][jj];
-          n += uint32_t(x) < uint32_t(e) ? 1 : 0;
-          n += (x == e && (u < t || (u == t && jj < j))) ? (1 << 16) : 0;
+          n_below += __popcll(__ballot(uint32_t(x) < uint32_t(e)));
+          rk += __popcll(__ballot(x == e) & (jj < j ? upto_t : before_t));
         }
       }
     }
-    const int sum = wave_sum(n);
-    const int rk = sum >> 16;
-    int p = (block > 0 ? e * block : (sum & 0xFFFF)) + rk;
+    int p = (block > 0 ? e * block : n_below) + rk;
     if (block > 0 && rk >= block) {
       p = -1;
       full = true;
