@@ -85,6 +85,14 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return (uint64_t(1) << lane_id()) - 1;  // lane 63: 2^63 - 1
 }
 
+// The wave's index in its workgroup, through a scalar register: the compiler
+// does not know that threadIdx.x / 64 is the same in every lane of a wave,
+// and would otherwise keep the row or token a wave works on, and every row
+// number, mask and branch derived from it, per lane.
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
 __device__ __forceinline__ int read_lane(int v, int lane) {
   return __builtin_amdgcn_readlane(v, lane);
 }
@@ -268,7 +276,7 @@ __device__ void scan_columns(int32_t* s_pre, const int32_t* s_tot, const int32_t
                              int32_t* expert_counts, int32_t* expert_offsets,
                              int32_t* rank_counts, int32_t* rank_offsets) {
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = wave_in_block();
   const int lane = lane_id();
   constexpr int kScanThreads = 8 * kWave;
   constexpr int kPer = (kMaxExperts + kScanThreads - 1) / kScanThreads;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_tiles(
   __shared__ int32_t s_tmp[kLayoutWaves];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = wave_in_block();
   const int lane = lane_id();
   const int tile_lo = blockIdx.x * g.tile_tokens;
   const int tile_hi = min(g.T, tile_lo + g.tile_tokens);
@@ -946,7 +954,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows(const vec4* hidden,
                                                     int R, int nvec, int64_t cap_rank,
                                                     int32_t* err_word) {
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
   if (t >= T) return;
   // The hidden row is read once, its first pass requested right behind the
   // token's slots (loads return in order, so the slots can be used while the
@@ -978,7 +986,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_small(
     int32_t* __restrict__ rank_src_token, int T, int R, int nvec, int groups, int64_t cap_rank,
     int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   const int t = int(gw / groups);
   const int g = int(gw - (int64_t)t * groups);
   if (t >= T) return;
@@ -1153,7 +1161,7 @@ __global__ __launch_bounds__(kBlock) void pack_rows_mx(
   constexpr int LPB = kBlockVecs / NL;       // lanes per scale block
   constexpr int kEmax = kBits == 8 ? 8 : 2;
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   const int t = int(gw / slices);
   const int sl = int(gw - (int64_t)t * slices);  // this wave's NP passes: [sl*NP, sl*NP + NP)
   if (t >= T) return;
@@ -1304,7 +1312,7 @@ __global__ __launch_bounds__(kBlock) void permute_rows(
     int early_row, int32_t* err_word) {
   constexpr bool kStreamIn = !kMx;
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   if (gw < pad_waves) {
     mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
     return;
@@ -1384,7 +1392,7 @@ __global__ __launch_bounds__(kBlock) void pack_expand_rows(
     int nvec, int slices, int pad_waves, int64_t cap_rank, int64_t cap_expert,
     int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   if (gw < pad_waves) {
     mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
     return;
@@ -1561,7 +1569,7 @@ __global__ __launch_bounds__(kBlock) void pack_expand_q(
     int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
   static_assert(kFmt != kWireBf16, "bf16 rows take pack_expand_rows");
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   if (gw < pad_waves) {
     mark_padding(int(gw), expert_counts, expert_offsets, block, expert_src_pair, cap_expert);
     return;
@@ -1623,10 +1631,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   constexpr int fmt = kFmt;
   const int kk = K > 0 ? K : k;
   const int lane = lane_id();
-  // (read through a scalar register: the compiler does not know that the
-  // wave index is the same in every lane, and would keep the token, its
-  // rank set masks and every row number derived from them per lane)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wave = wave_in_block();
   const bool counter = blockIdx.x == 0;
   // Padding waves, then movers: a mover's token and 1 KiB group; its part of
   // the hidden row is requested first (clamped into the row), the ids right
@@ -1970,7 +1975,7 @@ __global__ __launch_bounds__(kBlock) void combine_rows(
     const float* __restrict__ weights, vec4* out, vec4* out_f32, int T, int k, int nvec,
     int slices, int64_t cap_expert, int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   const int t = int(gw / slices);
   const int slice = int(gw - (int64_t)t * slices);
   if (t >= T) return;
@@ -2000,7 +2005,7 @@ __global__ __launch_bounds__(kBlock) void rank_partial_rows(
     vec4* partial_f32, int T, int E, int R, int k, int m, int nvec, int slices,
     int64_t cap_rank, int64_t cap_expert, int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   const int64_t i = gw / slices;
   const int slice = int(gw - i * slices);
   // Two rounds of index loads, as in the permute: the offsets and the row's
@@ -2037,7 +2042,7 @@ __global__ __launch_bounds__(kBlock) void rank_sum_rows(
     const vec4* partial, const int32_t* __restrict__ token_rank_slot, vec4* out,
     vec4* out_f32, int T, int R, int nvec, int slices, int64_t cap_rank, int32_t* err_word) {
   const int lane = lane_id();
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
   const int t = int(gw / slices);
   const int slice = int(gw - (int64_t)t * slices);
   if (t >= T) return;
