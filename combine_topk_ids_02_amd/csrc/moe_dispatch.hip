@@ -2161,13 +2161,17 @@ struct PackLaunch {
 };
 
 // Pack and permute in one kernel: V vec4 per lane, `slices` waves per token.
-// One wave per (token, 1 KiB of the row) with ordinary loads and stores was
-// best or within 1% of the best of six forms measured (1 or 2 vec4 per lane
-// or the whole row per wave; streamed loads; streamed stores) over five
-// shapes; streamed stores were 1-6% slower everywhere.
+// One wave per (token, 1 KiB of the row) with ordinary loads was best or
+// within 1% of the best of six forms measured (1 or 2 vec4 per lane or the
+// whole row per wave; streamed or ordinary loads and stores) over five
+// shapes. The stores are streamed: on one buffer set replayed back to back
+// ordinary stores were 1-6% faster, but with three buffer sets in turn (as
+// layers and batches follow each other) streamed stores took the prefill
+// step (this call and the combine) from 153.9 to 143.2 us, and the ordinary
+// ones fell to 197 us when other work ran between the steps; skew the same.
 constexpr int kExpandVec = 1;
 constexpr bool kExpandStreamLoad = false;
-constexpr bool kExpandStreamStore = false;
+constexpr bool kExpandStreamStore = true;
 template <int V>
 struct PackExpandLaunch {
   static void go(dim3 grid, hipStream_t st, const vec4* hid, const int32_t* ids,
