@@ -33,7 +33,7 @@
 //                dispatch_small's sizes, after the layout: one wave per
 //                (token, 1 KiB of the row) reads it once and writes it to
 //                every copy and every pair row, so the packed rows are not
-//                read back (ordinary loads and stores, chosen by measurement)
+//                read back (ordinary loads, streamed stores: by measurement)
 //  pack_rows_mx  fused quantise-and-pack to the [A2A] sec 7.2 wire formats:
 //                MXFP8, MXFP4, and the 4-bit row with an E4M3 scale per 16
 //                values; permute_rows moves their codes and scales
@@ -44,7 +44,8 @@
 // Cache; the hidden rows are read with ordinary loads (which keeps that
 // hand-off working whatever large writes other kernels made before); every
 // other row stream (packed rows on their second read, expert rows, combine
-// outputs) is non-temporal so it does not evict them.
+// outputs, the rows of the one-call dispatch) is non-temporal so it does not
+// evict them.
 // Nothing here is a dense contraction, so no MFMA.
 
 #include <hip/hip_ext.h>

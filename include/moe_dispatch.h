@@ -237,8 +237,8 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
  *   sizes, alignment and NULL rules; all are checked before anything is
  *   launched, and an argument error launches nothing. The one-launch form
  *   needs no workspace. rank_buf holds every copy as after
- *   moe_dispatch_pack (the one-launch form streams it past the caches,
- *   since nothing reads it back there). With padded or blocked runs the
+ *   moe_dispatch_pack (both forms here store the bf16 rows non-temporally,
+ *   since nothing reads them back in this call). With padded or blocked runs the
  *   padding rows of expert_src_pair are marked -1 as by the permute.
  */
 int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t* topk_ids,
