@@ -312,3 +312,34 @@ def test_graph_large_step(T, H, E, R, k, align):
         rows = e.expert_src_pair[:P] >= 0
         assert torch.equal(g.expert_buf[:P][rows].view(torch.int16),
                            e.expert_buf[:P][rows].view(torch.int16)), f"replay {i}: expert rows"
+
+
+@pytest.mark.parametrize("T,k", [(64, 4), (300, 4)])
+def test_readme_flow(T, k):
+    """The usage shown in the README, step for step (identity experts: the
+    expert outputs are the dispatched rows themselves), at a size of each
+    form; the combined rows equal the oracle's bit for bit."""
+    H, E, R = 512, 64, 8
+    rng = np.random.default_rng(77 + T)
+    ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
+    wts = rng.random((T, k)).astype(np.float32)
+    hid = synth.normal_bf16(77, T, T * H).reshape(T, H)
+    dev = torch.device("cuda:0")
+    hidden = staging.rows_to_device(hid, dev)
+    topk_ids = torch.from_numpy(ids).to(dev)
+    topk_weights = torch.from_numpy(wts).to(dev)
+    say(f"[readme flow] T={T} k={k}")
+
+    shape = moe.Shape(T, H, E, R, k)
+    b = moe.Buffers(shape, dev)
+    moe.dispatch_all(hidden, topk_ids, E, R, b.layout_dict(), b.rank_buf, b.rank_src_token,
+                     b.expert_buf, b.expert_src_pair, workspace=b.workspace, err=b.err)
+    expert_out = b.expert_buf
+    moe.combine(expert_out, b.pair_row, topk_weights, E, R, b.out, err=b.err)
+    torch.cuda.synchronize()
+    assert int(b.err.item()) == 0
+
+    ref = run_oracle(hid, ids, wts, E, R, None, shape.cap_rank, shape.cap_expert)
+    assert ref["err"] == 0
+    got = b.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref["out"]), "combined rows differ from the oracle"
