@@ -687,7 +687,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
                         "note": "layout, pack, permute, combine replayed from one HIP graph"}
         log(f"{name}: graph replay {us_g:.1f} us per step")
         us_d = rig.graph_step_us(calls=("dispatch", "combine"))
-        one = align == 1 and (w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8)))
+        one = w.T <= 64 or (w.T <= 256 and w.k in (1, 2, 4, 6, 8))
         form = "one launch" if one else "three calls" if wire else "pack+permute kernel"
         bytes_d = path_bytes(rig.nbytes) if form == "three calls" else \
             rig.nbytes["dispatch"] + rig.nbytes["combine"]
@@ -696,7 +696,7 @@ def sweep(names, dev, with_oracle: bool) -> None:
             "GB/s": round(bytes_d / (us_d * 1e-6) / 1e9, 1),
             "one_launch": one, "form": form,
             "note": ("moe_dispatch_quantised" if wire else "moe_dispatch") +
-                    " (one launch for a decode-sized batch with align 1; past it the layout "
+                    " (one launch for a decode-sized batch; past it the layout "
                     "and one pack-and-permute kernel, or the three calls for a wire format) "
                     "and combine, replayed from a HIP graph"}
         log(f"{name}: graph replay with the one-call dispatch {us_d:.1f} us per step")

@@ -335,7 +335,7 @@ def dispatch_all(hidden, topk_ids, E: int, R: int, out: dict, rank_buf, rank_src
                  expert_buf, expert_src_pair, *, align: int = 1, block: int = 0,
                  workspace: torch.Tensor | None = None, err=None) -> None:
     """moe_dispatch: layout, pack and permute in one call (one kernel launch
-    for up to 256 tokens with align = 1 and k in {1, 2, 4, 6, 8}, up to 64
+    for up to 256 tokens with k in {1, 2, 4, 6, 8}, up to 64
     for another k; else the layout and one pack-and-permute kernel), into
     the caller's tensors: `out`
     holds the layout's outputs (the keys of layout()), rank_buf [cap_rank, H],

@@ -1453,7 +1453,8 @@ __global__ __launch_bounds__(kBlock) void pack_expand_rows(
 
 // ---------------------------------------------------------------------------
 // The whole dispatch of a small batch in one launch (moe_dispatch with at most
-// kSmallBatch tokens, 64 for a k read at run time, and unpadded runs):
+// kSmallBatch tokens, 64 for a k read at run time; plain, padded or blocked
+// runs):
 // layout, pack and permute with no
 // kernel boundary between them, for the decode step, whose time is launches
 // and the waits between them. Every wave holds all T*k ids, TPL tokens per
@@ -1470,6 +1471,9 @@ __global__ __launch_bounds__(kBlock) void pack_expand_rows(
 // moe_dispatch_layout, moe_dispatch_pack and moe_permute_by_expert, bit for
 // bit.
 constexpr int kSmallBatch = 4 * kWave;
+
+// x rounded up to a multiple of a (a >= 1): a padded run's rows.
+__device__ __forceinline__ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 // Sum over the wave, in every lane.
 __device__ __forceinline__ int wave_sum(int x) {
@@ -1618,7 +1622,7 @@ __global__ __launch_bounds__(kBlock) void pack_expand_q(
 template <int K, int kRB, int TPL, int kFmt>
 __global__ __launch_bounds__(kBlock) void dispatch_small(
     const vec4* hidden, const int32_t* __restrict__ ids, int T, int E, int R, int k, int block,
-    float inv_m, int nvec, int groups, int pad_waves, int32_t* __restrict__ rank_counts,
+    int align, float inv_m, int nvec, int groups, int pad_waves, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_offsets, int32_t* __restrict__ expert_counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ token_rank_slot,
     int32_t* __restrict__ pair_row, void* rank_buf, uint8_t* rank_scale,
@@ -1642,10 +1646,14 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
   const int64_t gm = padder ? 0 : gw - pad_waves;
   const int t = int(gm / groups);
   const int g = int(gm - (int64_t)t * groups);
-  if (!counter && !padder && t >= T) return;
+  // (with padded runs a wave past the last token still takes part in its
+  // workgroup's barriers below, and leaves after them)
+  const bool idle = !counter && !padder && t >= T;
+  if (idle && align == 1) return;
   const int c = g * kWave + lane;
   vec4 v;
-  if (!counter && !padder) v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
+  if (!counter && !padder && !idle)
+    v = load_row<true>(hidden + (int64_t)t * nvec + min(c, nvec - 1));
   int32_t idv[TPL][KR];  // group q, lane u: the ids of token 64q + u (-1 past T)
   RankSet<kRB> set[TPL];  // and its ranks
 #pragma unroll
@@ -1683,7 +1691,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     const int per = (E + kBlock - 1) / kBlock;
     const int lo = min(E, tid * per), hi = min(E, lo + per);
     int run = 0;
-    for (int e = lo; e < hi; ++e) run += block > 0 ? block : s_hist[e];
+    for (int e = lo; e < hi; ++e) run += block > 0 ? block : round_up(s_hist[e], align);
     const int inc = wave_inclusive_scan(run);
     if (lane == kWave - 1) s_part[wave] = inc;
     __syncthreads();
@@ -1695,7 +1703,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     for (int e = lo; e < hi; ++e) {
       expert_counts[e] = s_hist[e];
       expert_offsets[e] = base;
-      base += block > 0 ? block : s_hist[e];
+      base += block > 0 ? block : round_up(s_hist[e], align);
     }
     if (tid == 0) expert_offsets[E] = total;
     // Copies per rank (wave 0: one ballot per rank and token group) and
@@ -1718,6 +1726,51 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
     return;
   }
 
+  // Padded runs (align > 1): every workgroup histograms the ids in LDS (each
+  // wave a quarter of the slots, from its registers) and scans the padded
+  // run lengths into each expert's first row, as the counting workgroup
+  // does for the offsets it writes.
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_first[kMaxExperts];
+  __shared__ int32_t s_wsum[kWavesPerBlock];
+  if (align > 1) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kBlock) s_cnt[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TPL; ++q)
+#pragma unroll
+      for (int j = 0; j < KR; ++j)
+        if (j < kk && j % kWavesPerBlock == wave && uint32_t(idv[q][j]) < uint32_t(E))
+          atomicAdd(&s_cnt[idv[q][j]], 1);
+    __syncthreads();
+    const int per = (E + kBlock - 1) / kBlock;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += round_up(s_cnt[e], align);
+    const int inc = wave_inclusive_scan(run);
+    if (lane == kWave - 1) s_wsum[wave] = inc;
+    __syncthreads();
+    int base = inc - run;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    for (int e = lo; e < hi; ++e) {
+      s_first[e] = base;
+      base += round_up(s_cnt[e], align);
+    }
+    __syncthreads();
+    if (idle) return;
+  }
+
+  if (padder && align > 1) {
+    // Expert e = gw of a padded layout: the rows of its run past its pairs,
+    // within the buffer, get expert_src_pair -1.
+    const int e = int(gw);
+    const int64_t first = s_first[e];
+    const int64_t end = min(first + round_up(s_cnt[e], align), cap_expert);
+    for (int64_t row = first + s_cnt[e] + lane; row < end; row += kWave)
+      expert_src_pair[row] = -1;
+    return;
+  }
   if (padder) {
     // Expert e = gw of a blocked layout: the rows of its block past its pairs,
     // within the buffer, get expert_src_pair -1.
@@ -1799,7 +1852,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_small(
         }
       }
     }
-    int p = (block > 0 ? e * block : n_below) + rk;
+    int p = (block > 0 ? e * block : align > 1 ? s_first[e] : n_below) + rk;
     if (block > 0 && rk >= block) {
       p = -1;
       full = true;
@@ -2304,9 +2357,9 @@ template <int K, int kRB, int TPL, int kFmt>
 void launch_dispatch_small_f(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a,
                              int grid, float inv_m, int nvec, int groups, int pad_waves) {
   MOE_LAUNCH((dispatch_small<K, kRB, TPL, kFmt>), dim3(grid), dim3(kBlock), 0, st, a.hidden,
-             a.ids, sh.T, sh.E, sh.R, sh.k, sh.block, inv_m, nvec, groups, pad_waves, a.rc, a.ro,
-             a.ec, a.eo, a.trs, a.pr, a.rank_buf, a.rank_scale, a.rank_src, a.cap_rank,
-             a.expert_buf, a.expert_scale, a.expert_src, a.cap_expert, a.err);
+             a.ids, sh.T, sh.E, sh.R, sh.k, sh.block, sh.align, inv_m, nvec, groups, pad_waves,
+             a.rc, a.ro, a.ec, a.eo, a.trs, a.pr, a.rank_buf, a.rank_scale, a.rank_src,
+             a.cap_rank, a.expert_buf, a.expert_scale, a.expert_src, a.cap_expert, a.err);
 }
 
 template <int K, int kRB, int TPL>
@@ -2335,7 +2388,7 @@ template <int K, int kRB>
 void launch_dispatch_small_kw(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {
   const int nvec = sh.H / 8;
   const int groups = (nvec + kWave - 1) / kWave;
-  const int pad_waves = sh.block > 0 && a.cap_expert > 0 ? sh.E : 0;
+  const int pad_waves = (sh.block > 0 || sh.align > 1) && a.cap_expert > 0 ? sh.E : 0;
   const int grid = 1 + blocks_for(pad_waves + int64_t(sh.T) * groups);
   const float inv_m = float(1.0 / double(sh.E / sh.R));
   // one token per lane up to 64 tokens, else four (only for a k known at
@@ -2359,11 +2412,10 @@ void launch_dispatch_small_k(const moe_shape_t& sh, hipStream_t st, const Dispat
 }
 
 // Whether moe_dispatch runs as one launch: up to 64 tokens, or up to 256 with
-// a k the kernels are compiled for, and unpadded runs.
+// a k the kernels are compiled for (plain, padded or blocked runs).
 bool dispatch_one_launch(const moe_shape_t& sh) {
   const bool compiled_k = sh.k == 1 || sh.k == 2 || sh.k == 4 || sh.k == 6 || sh.k == 8;
-  return g_dispatch_fused && sh.align == 1 &&
-         (sh.T <= kWave || (sh.T <= kSmallBatch && compiled_k));
+  return g_dispatch_fused && (sh.T <= kWave || (sh.T <= kSmallBatch && compiled_k));
 }
 
 void launch_dispatch_small(const moe_shape_t& sh, hipStream_t st, const DispatchSmallArgs& a) {

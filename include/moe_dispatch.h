@@ -218,8 +218,8 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
 /*
  * The whole dispatch in one call: moe_dispatch_layout, moe_dispatch_pack and
  * moe_permute_by_expert on the same arguments, with the same results bit for
- * bit and the same error bits. For a decode-sized batch with unpadded runs
- * (align = 1; block may be set) the three run as one kernel launch: up to 256
+ * bit and the same error bits. For a decode-sized batch (any align or block)
+ * the three run as one kernel launch: up to 256
  * tokens when k is 1, 2, 4, 6 or 8, up to 64 for any other k. There the time
  * is in launches and in each kernel waiting
  * for the one before ([A2A] sec 8.1: a call that does nothing already costs

@@ -590,9 +590,11 @@ SMALL_BATCH = 256
 
 
 def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report, lpb: int = 0):
-    """dispatch_small (moe_dispatch's one-launch form, T <= 256, align = 1):
-    workgroup 0 writes the counts and offsets; with a blocked layout one wave
-    per expert marks its padding rows; one wave per (token, group of 64 vec4)
+    """dispatch_small (moe_dispatch's one-launch form, T <= 256): workgroup 0
+    writes the counts and offsets; with a blocked or padded layout one wave
+    per expert marks its padding rows (a padded run's first row from the
+    workgroup's LDS scan of the padded run lengths, held at the layout's
+    offsets here); one wave per (token, group of 64 vec4)
     moves that part of the row. The rows and slots
     the waves compute from the ids are the layout's, so the oracle's layout
     stands in for them; every store is guarded by the caps as in the kernel.
@@ -617,7 +619,7 @@ def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report, lpb: 
         rep.buf(name, n)
     tag = "dispatch_small"
     groups = cdiv(nvec, W)
-    pad_waves = E if c.block > 0 and c.cap_expert > 0 else 0
+    pad_waves = E if (c.block > 0 or c.align > 1) and c.cap_expert > 0 else 0
     nblocks = 1 + blocks_for(pad_waves + T * groups)
     # every wave: lane u of group q loads the ids of token 64q + u (< T)
     if T > 0:
@@ -632,9 +634,15 @@ def model_dispatch_small(c: Case, lay: dict, ids: np.ndarray, rep: Report, lpb: 
     # padding waves: expert e's rows past its pairs, within the buffer
     if pad_waves:
         cnt = lay["expert_counts"].astype(np.int64)
+        offs = lay["expert_offsets"].astype(np.int64)
         for e in range(E):
-            lo = e * c.block + min(int(cnt[e]), c.block)
-            hi = min((e + 1) * c.block, c.cap_expert)
+            if c.block > 0:
+                lo = e * c.block + min(int(cnt[e]), c.block)
+                hi = min((e + 1) * c.block, c.cap_expert)
+            else:  # padded run: [first + count, first + count rounded up to align)
+                first = int(offs[e])
+                lo = first + int(cnt[e])
+                hi = min(first + cdiv(int(cnt[e]), c.align) * c.align, c.cap_expert)
             if hi > lo:
                 rep.access(tag, "expert_src_pair", [lo, hi - 1], "store")
     # movers

@@ -1,6 +1,6 @@
 """moe_dispatch, the whole dispatch in one call, against the oracle: its
-one-launch form (unpadded runs; up to 256 tokens with k in 1, 2, 4, 6, 8, up
-to 64 with another k; one or four tokens per lane) and, past it, the layout
+one-launch form (plain, padded or blocked runs; up to 256 tokens with k in 1,
+2, 4, 6, 8, up to 64 with another k; one or four tokens per lane) and, past it, the layout
 followed by one pack-and-permute kernel (the testing hook switches both off,
 for the three calls). The bar is the one of the three separate calls:
 bit-exact layout, rows, source ids and error words, canary rows past every cap
@@ -65,13 +65,15 @@ def small_case(s: int):
         k = int(rng.integers(1, min(16, E) + 1))
     H = 8 * int(rng.integers(1, 129))
     block = int(rng.choice([0, 0, 0, 1, int(rng.integers(1, 6))]))
+    align = int(rng.choice([1, 1, 1, 2, 16, 128])) if block == 0 else 1
     p_neg = float(rng.choice([0.0, 0.1, 0.5]))
     p_dup = float(rng.choice([0.0, 0.15])) if k > 1 else 0.0
     p_bad = float(rng.choice([0.0, 0.0, 0.05]))
     ids = pins.rand_ids(rng, T, E, k, p_neg=p_neg, p_dup=p_dup, p_bad=p_bad)
     wts = rng.random((T, k)).astype(np.float32)
     hid = synth.normal_bf16(s, 0, T * H).reshape(T, H)
-    return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, wts=wts, hid=hid, rng=rng)
+    return dict(T=T, H=H, E=E, R=R, k=k, block=block, align=align, ids=ids, wts=wts, hid=hid,
+                rng=rng)
 
 
 SMALL = list(range(384))
@@ -81,12 +83,14 @@ SMALL = list(range(384))
 def test_small_batches(s):
     """Random decode-sized shapes (T up to 256) in the one-launch form: R up
     to 64, E up to 1024, k up to 16, masked blocks (one row, a few rows,
-    overflowing), -1, duplicate and out-of-range ids."""
+    overflowing), runs padded to 2, 16 or 128 rows, -1, duplicate and
+    out-of-range ids."""
     c = small_case(s)
     say(f"[dispatch small] s={s} T={c['T']} H={c['H']} E={c['E']} R={c['R']} k={c['k']} "
-        f"block={c['block']}")
+        f"block={c['block']} align={c['align']}")
     y = synth.expert_out_slots(s, c["E"], c["H"], c["ids"])
-    check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small {s}", block=c["block"])
+    check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small {s}", block=c["block"],
+          align=c["align"])
 
 
 @pytest.mark.parametrize("s", range(64))
@@ -96,14 +100,14 @@ def test_small_batches_undersized(s):
     is not written)."""
     c = small_case(200 + s)
     rng = c["rng"]
-    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], 1, c["block"])
+    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], c["align"], c["block"])
     cr = int(rng.integers(0, shape.cap_rank + 1))
     ce = int(rng.integers(0, shape.cap_expert + 1))
     say(f"[dispatch small caps] s={200 + s} T={c['T']} E={c['E']} R={c['R']} k={c['k']} "
-        f"block={c['block']} caps {cr}/{ce}")
+        f"block={c['block']} align={c['align']} caps {cr}/{ce}")
     y = synth.expert_out_slots(s, c["E"], c["H"], c["ids"])
     check(c["hid"], c["ids"], c["wts"], c["E"], c["R"], y, f"small caps {200 + s}",
-          cap_rank=cr, cap_expert=ce, block=c["block"])
+          cap_rank=cr, cap_expert=ce, block=c["block"], align=c["align"])
 
 
 @pytest.mark.parametrize("T,k,align,block", [

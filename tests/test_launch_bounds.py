@@ -117,19 +117,20 @@ def small_batch(s: int):
                         int(rng.integers(65, 257))]))
     H = 8 * int(rng.integers(1, 1025))
     block = int(rng.choice([0, 0, 1, int(rng.integers(1, 8))]))
+    align = int(rng.choice([1, 1, 2, 16, 128])) if block == 0 else 1
     ids = pins.rand_ids(rng, T, E, k, p_neg=0.1, p_dup=0.1 if k > 1 else 0.0, p_bad=0.02)
-    return lm.Case(T, H, E, R, k, 1, block), ids, rng
+    return lm.Case(T, H, E, R, k, align, block), ids, rng
 
 
 def test_dispatch_one_launch():
-    """moe_dispatch's one-launch form (T <= 256, align = 1), full and
-    undersized caps."""
+    """moe_dispatch's one-launch form (T <= 256; plain, padded or blocked
+    runs), full and undersized caps."""
     for s in range(300):
         c, ids, rng = small_batch(s)
         assert_clean(lm.dispatch_one_launch(c, ids), f"small batch {s}")
         cr = int(rng.integers(0, c.cap_rank + 1))
         ce = int(rng.integers(0, c.cap_expert + 1))
-        c2 = lm.Case(c.T, c.H, c.E, c.R, c.k, 1, c.block, cap_rank=cr, cap_expert=ce)
+        c2 = lm.Case(c.T, c.H, c.E, c.R, c.k, c.align, c.block, cap_rank=cr, cap_expert=ce)
         assert_clean(lm.dispatch_one_launch(c2, ids), f"small batch {s} caps {cr}/{ce}")
 
 
@@ -141,11 +142,11 @@ def test_dispatch_quantised_one_launch():
         c, ids, rng = small_batch(s)
         H = 512 * int(rng.integers(1, 21))
         for lpb in (4, 2):
-            c1 = lm.Case(c.T, H, c.E, c.R, c.k, 1, c.block)
+            c1 = lm.Case(c.T, H, c.E, c.R, c.k, c.align, c.block)
             assert_clean(lm.dispatch_one_launch(c1, ids, lpb), f"q small batch {s} lpb {lpb}")
             cr = int(rng.integers(0, c1.cap_rank + 1))
             ce = int(rng.integers(0, c1.cap_expert + 1))
-            c2 = lm.Case(c.T, H, c.E, c.R, c.k, 1, c.block, cap_rank=cr, cap_expert=ce)
+            c2 = lm.Case(c.T, H, c.E, c.R, c.k, c.align, c.block, cap_rank=cr, cap_expert=ce)
             assert_clean(lm.dispatch_one_launch(c2, ids, lpb),
                          f"q small batch {s} lpb {lpb} caps {cr}/{ce}")
 

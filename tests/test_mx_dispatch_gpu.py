@@ -218,7 +218,7 @@ def test_mx_rejects_rows_not_a_multiple_of_512():
 
 
 # The quantised dispatch in one call (moe_dispatch_quantised): a decode-sized
-# unpadded batch takes the one-launch form (quantise in the mover waves), any
+# batch takes the one-launch form (quantise in the mover waves), any
 # other batch the layout and one quantise-pack-and-permute kernel; the testing
 # hook switches both off for the three calls above. All held to the same bar.
 
@@ -238,6 +238,7 @@ def small_mx_case(s: int):
         k = int(rng.integers(1, min(16, E) + 1))
     H = 512 * int(rng.integers(1, 11))
     block = int(rng.choice([0, 0, 0, 1, int(rng.integers(1, 6))]))
+    align = int(rng.choice([1, 1, 1, 2, 16, 128])) if block == 0 else 1
     p_neg = float(rng.choice([0.0, 0.1, 0.5]))
     p_dup = float(rng.choice([0.0, 0.15])) if k > 1 else 0.0
     p_bad = float(rng.choice([0.0, 0.0, 0.05]))
@@ -247,7 +248,8 @@ def small_mx_case(s: int):
     else:
         hid = synth.normal_bf16(s, 3, T * H).reshape(T, H)
     fmt = FORMATS[s % 3]
-    return dict(T=T, H=H, E=E, R=R, k=k, block=block, ids=ids, hid=hid, fmt=fmt, rng=rng)
+    return dict(T=T, H=H, E=E, R=R, k=k, block=block, align=align, ids=ids, hid=hid, fmt=fmt,
+                rng=rng)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -268,9 +270,9 @@ def test_dispatch_quantised_workloads(name, fmt):
 def test_dispatch_quantised_small(s):
     c = small_mx_case(s)
     say(f"[dispatch q small] s={s} {c['fmt']} T={c['T']} H={c['H']} E={c['E']} R={c['R']} "
-        f"k={c['k']} block={c['block']}")
+        f"k={c['k']} block={c['block']} align={c['align']}")
     check(c["hid"], c["ids"], c["E"], c["R"], f"q small {s}", fmt=c["fmt"], block=c["block"],
-          whole_dispatch=True)
+          align=c["align"], whole_dispatch=True)
 
 
 @pytest.mark.parametrize("s", range(48))
@@ -279,13 +281,13 @@ def test_dispatch_quantised_undersized(s):
     them dropped and flagged as the three calls do."""
     c = small_mx_case(400 + s)
     rng = c["rng"]
-    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], 1, c["block"])
+    shape = moe.Shape(c["T"], c["H"], c["E"], c["R"], c["k"], c["align"], c["block"])
     cr = int(rng.integers(0, shape.cap_rank + 1))
     ce = int(rng.integers(0, shape.cap_expert + 1))
     say(f"[dispatch q caps] s={400 + s} {c['fmt']} T={c['T']} E={c['E']} R={c['R']} "
-        f"k={c['k']} block={c['block']} caps {cr}/{ce}")
+        f"k={c['k']} block={c['block']} align={c['align']} caps {cr}/{ce}")
     check(c["hid"], c["ids"], c["E"], c["R"], f"q caps {400 + s}", fmt=c["fmt"],
-          block=c["block"], cap_rank=cr, cap_expert=ce, whole_dispatch=True)
+          block=c["block"], align=c["align"], cap_rank=cr, cap_expert=ce, whole_dispatch=True)
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -378,7 +380,7 @@ def test_dispatch_quantised_one_launch_equals_three_calls():
             old = moe.lib().moe_testing_set_dispatch_fused(fused)
             try:
                 res.append(run_gpu(c["hid"], c["ids"], c["E"], c["R"], c["fmt"],
-                                   block=c["block"], whole_dispatch=True))
+                                   align=c["align"], block=c["block"], whole_dispatch=True))
             finally:
                 moe.lib().moe_testing_set_dispatch_fused(old)
         for key, v in res[0].items():
