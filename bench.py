@@ -751,7 +751,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", nargs="?",
-                    const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:block=128,"
+                    const="tiny,decode,prefill,skew,adv,prefill:align=128,decode:align=128,"
+                          "decode:block=128,"
                           "prefill:mxfp8,decode:mxfp8,adv:mxfp8,prefill:mxfp4,decode:mxfp4,"
                           "adv:mxfp4,prefill:nvfp4,decode:nvfp4,adv:nvfp4",
                     default=None,
