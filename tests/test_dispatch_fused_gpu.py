@@ -347,3 +347,58 @@ def test_readme_flow(T, k):
     assert ref["err"] == 0
     got = b.out.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, ref["out"]), "combined rows differ from the oracle"
+
+
+def test_two_streams_at_once():
+    """moe_dispatch + moe_combine on two streams at the same time, each with
+    its own buffers (one a decode-sized batch in one launch, one larger
+    through the layout and the pack-and-permute kernel): the library keeps no
+    state between calls, so each result equals the same call made alone."""
+    dev = torch.device("cuda:0")
+    cases = [(64, 5120, 384, 8, 6, 1), (2000, 1024, 128, 8, 4, 16)]
+    runs = []
+    for i, (T, H, E, R, k, align) in enumerate(cases):
+        rng = np.random.default_rng(90 + i)
+        ids = pins.rand_ids(rng, T, E, k, p_neg=0.05)
+        wts = rng.random((T, k)).astype(np.float32)
+        hid = synth.normal_bf16(90 + i, 0, T * H).reshape(T, H)
+        shape = moe.Shape(T, H, E, R, k, align)
+        eo = synth.normal_bf16(90 + i, 1, shape.cap_expert * H).reshape(shape.cap_expert, H)
+        runs.append(dict(E=E, R=R, align=align, shape=shape,
+                         hid=staging.rows_to_device(hid, dev), ids=torch.from_numpy(ids).to(dev),
+                         wts=torch.from_numpy(wts).to(dev), eo=staging.rows_to_device(eo, dev)))
+
+    def run(r, b):
+        moe.dispatch_all(r["hid"], r["ids"], r["E"], r["R"], b.layout_dict(), b.rank_buf,
+                         b.rank_src_token, b.expert_buf, b.expert_src_pair, align=r["align"],
+                         workspace=b.workspace, err=b.err)
+        moe.combine(r["eo"], b.pair_row, r["wts"], r["E"], r["R"], b.out, err=b.err)
+
+    alone = []
+    for r in runs:
+        b = moe.Buffers(r["shape"], dev)
+        run(r, b)
+        torch.cuda.synchronize()
+        alone.append(b)
+    say("[dispatch two streams]")
+    streams = [torch.cuda.Stream(dev) for _ in runs]
+    together = [moe.Buffers(r["shape"], dev) for r in runs]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for r, b, s in zip(runs, together, streams):
+            with torch.cuda.stream(s):
+                b.err.zero_()
+                run(r, b)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(alone, together)):
+            P = int(a.expert_offsets[-1].item())
+            C = int(a.rank_offsets[-1].item())
+            for key in ("rank_counts", "rank_offsets", "expert_counts", "expert_offsets",
+                        "token_rank_slot", "pair_row", "err"):
+                assert torch.equal(getattr(a, key), getattr(b, key)), f"case {i}: {key}"
+            assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), f"case {i}"
+            assert torch.equal(a.rank_buf[:C].view(torch.int16), b.rank_buf[:C].view(torch.int16))
+            rows = a.expert_src_pair[:P] >= 0
+            assert torch.equal(a.expert_src_pair[:P], b.expert_src_pair[:P])
+            assert torch.equal(a.expert_buf[:P][rows].view(torch.int16),
+                               b.expert_buf[:P][rows].view(torch.int16))
