@@ -219,12 +219,11 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
  * The whole dispatch in one call: moe_dispatch_layout, moe_dispatch_pack and
  * moe_permute_by_expert on the same arguments, with the same results bit for
  * bit and the same error bits. For a decode-sized batch (any align or block)
- * the three run as one kernel launch: up to 256
- * tokens when k is 1, 2, 4, 6 or 8, up to 64 for any other k. There the time
- * is in launches and in each kernel waiting
- * for the one before ([A2A] sec 8.1: a call that does nothing already costs
- * about 10 microseconds; [GPUs] sec 7: DeepEP kept separate low-latency
- * kernels for decoding). In that launch every wave works out the rows of its
+ * the three run as one kernel launch: up to 256 tokens when k is 1, 2, 4, 6
+ * or 8, up to 64 for any other k. There the time is in launches and in each
+ * kernel waiting for the one before ([A2A] sec 8.1: a call that does nothing
+ * already costs about 10 microseconds; [GPUs] sec 7: DeepEP kept separate
+ * low-latency kernels for decoding). In that launch every wave works out the rows of its
  * own token from the ids alone, as a low-latency sender places its rows
  * without asking anyone ([A2A] sec 4.1), so nothing waits for the counts.
  * Otherwise the layout runs as moe_dispatch_layout, then one kernel packs and
@@ -238,8 +237,8 @@ int moe_permute_by_expert(const moe_shape_t* shape, const uint16_t* rank_buf,
  *   launched, and an argument error launches nothing. The one-launch form
  *   needs no workspace. rank_buf holds every copy as after
  *   moe_dispatch_pack (both forms here store the bf16 rows non-temporally,
- *   since nothing reads them back in this call). With padded or blocked runs the
- *   padding rows of expert_src_pair are marked -1 as by the permute.
+ *   since nothing reads them back in this call). With padded or blocked
+ *   runs the padding rows of expert_src_pair are marked -1 as by the permute.
  */
 int moe_dispatch(const moe_shape_t* shape, const uint16_t* hidden, const int32_t* topk_ids,
                  int32_t* rank_counts, int32_t* rank_offsets, int32_t* expert_counts,
